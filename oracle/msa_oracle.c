@@ -1,0 +1,190 @@
+/*
+ * msa_oracle.c -- plain CPU oracle for MiniMax Sparse Attention (MSA).
+ *
+ * TEST INFRASTRUCTURE ONLY: called by the tests, by the smoke check and by the
+ * CPU-baseline leg of the benchmark, never by the product path.  It shares no
+ * code with the GPU library.  Every step is written out exactly as the method
+ * defines it, with no blocking, fusion or reordering; the only parallelism is
+ * an OpenMP loop over independent query rows.
+ *
+ * Sources (page title, section):
+ *   [P4] "MiniMax Sparse Attention: let each query pick its own blocks",
+ *        section "The mechanism, precisely" (index branch / main branch) and
+ *        the paper's Figure 1 caption reproduced there.
+ *   [P5] atlas record of MiniMax M3 (atlas.lewiswon.me), summary paragraph
+ *        ("max-pooled dot products", top-k = 16 of 128-token blocks, local
+ *        block forced, standard scaled dot-product softmax attention).
+ *   [P1] "llama.cpp Merges MiniMax M3's Sparse Attention ...", key facts:
+ *        16 blocks of 128 tokens, always including the block being written.
+ *
+ * Readings taken where the pages are silent are listed in msa_oracle.h.
+ */
+#include "msa_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+static float load_elem(const void* base, int dtype, int64_t i) {
+  if (dtype == 0) return ((const float*)base)[i];
+  uint32_t bits = ((uint32_t)((const uint16_t*)base)[i]) << 16; /* bf16 -> fp32, exact */
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return f;
+}
+
+static int64_t floor_div(int64_t a, int64_t b) {
+  int64_t q = a / b;
+  if ((a % b != 0) && ((a < 0) != (b < 0))) q -= 1;
+  return q;
+}
+
+typedef struct {
+  float score;
+  int32_t block;
+} scored_block;
+
+/* Total order of the selection: higher pooled score first; equal scores are
+ * broken towards the lower block id (the deterministic tie-break). */
+static int by_score_then_block(const void* pa, const void* pb) {
+  const scored_block* a = (const scored_block*)pa;
+  const scored_block* b = (const scored_block*)pb;
+  if (a->score > b->score) return -1;
+  if (a->score < b->score) return 1;
+  return (a->block > b->block) - (a->block < b->block);
+}
+
+static int ascending_int(const void* pa, const void* pb) {
+  int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+  return (a > b) - (a < b);
+}
+
+/* [P4] index branch: token score s_j = q_idx . k_idx[j] (raw dot product,
+ * no scale: selection is "exp-free", on raw scores [P5]); block score
+ * S_c = max of s_j over the Bk tokens of block c [P4 Figure 1 "block max
+ * pooling"]; keep the local block l = floor(p / Bk) and the best k-1 earlier
+ * blocks c < l [P4, P5]. */
+int oracle_index_topk(const void* q_idx, const void* k_idx, int dtype,
+                      const int64_t* kstart, const int64_t* pos, int64_t n,
+                      int G, int DI, int Bk, int topk, int32_t* sel,
+                      float* scores, int64_t nbmax) {
+  if (!q_idx || !k_idx || !kstart || !pos || !sel) return 1;
+  if (n < 0 || G <= 0 || DI <= 0 || Bk <= 0 || topk <= 0) return 1;
+  if (dtype != 0 && dtype != 1) return 1;
+
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t r = 0; r < n; ++r) {
+    const int64_t p = pos[r];
+    const int64_t local = floor_div(p, Bk);
+    const int64_t nearlier = local > 0 ? local : 0; /* blocks c < local */
+    if (scores && nearlier > nbmax) { bad = 1; continue; }
+    scored_block* cand = (scored_block*)malloc(sizeof(scored_block) * (size_t)(nearlier > 0 ? nearlier : 1));
+    int32_t* chosen = (int32_t*)malloc(sizeof(int32_t) * (size_t)topk);
+    if (!cand || !chosen) { bad = 1; free(cand); free(chosen); continue; }
+
+    for (int g = 0; g < G; ++g) {
+      int32_t* out = sel + (r * G + g) * (int64_t)topk;
+      for (int i = 0; i < topk; ++i) out[i] = -1;
+      if (scores)
+        for (int64_t c = 0; c < nbmax; ++c) scores[(r * G + g) * nbmax + c] = -INFINITY;
+      if (p < 0) continue; /* no key is visible */
+
+      const int64_t qoff = (r * G + g) * (int64_t)DI;
+      for (int64_t c = 0; c < nearlier; ++c) {
+        float best = -INFINITY;
+        for (int64_t j = c * Bk; j < (c + 1) * Bk; ++j) {
+          const int64_t koff = (kstart[r] + j) * (int64_t)DI;
+          float s = 0.0f; /* fp32, sequential over d */
+          for (int d = 0; d < DI; ++d)
+            s += load_elem(q_idx, dtype, qoff + d) * load_elem(k_idx, dtype, koff + d);
+          if (s > best) best = s;
+        }
+        cand[c].score = best;
+        cand[c].block = (int32_t)c;
+        if (scores) scores[(r * G + g) * nbmax + c] = best;
+      }
+
+      qsort(cand, (size_t)nearlier, sizeof(scored_block), by_score_then_block);
+      int64_t keep = nearlier < (int64_t)(topk - 1) ? nearlier : (int64_t)(topk - 1);
+      int cnt = 0;
+      for (int64_t i = 0; i < keep; ++i) chosen[cnt++] = cand[i].block;
+      chosen[cnt++] = (int32_t)local; /* the local block is always kept */
+      qsort(chosen, (size_t)cnt, sizeof(int32_t), ascending_int);
+      for (int i = 0; i < cnt; ++i) out[i] = chosen[i];
+    }
+    free(cand);
+    free(chosen);
+  }
+  return bad;
+}
+
+/* [P4] main branch: exact softmax attention over the keys of the selected
+ * blocks, for every head of the group, with the causal limit j <= p inside
+ * the local block.  z_j = scale * q . k_j; o = sum_j softmax(z)_j v_j;
+ * lse = log sum_j exp(z_j).  All in fp64. */
+int oracle_sparse_attn(const void* q, const void* k, const void* v, int dtype,
+                       const int64_t* kstart, const int64_t* pos, const int32_t* sel,
+                       int64_t n, int Hq, int Hkv, int D, int Bk, int topk,
+                       double scale, double* out, double* lse) {
+  if (!q || !k || !v || !kstart || !pos || !sel || !out || !lse) return 1;
+  if (n < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Bk <= 0 || topk <= 0) return 1;
+  if (Hq % Hkv != 0) return 1;
+  if (dtype != 0 && dtype != 1) return 1;
+  const int r_heads = Hq / Hkv;
+
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t r = 0; r < n; ++r) {
+    int32_t* blocks = (int32_t*)malloc(sizeof(int32_t) * (size_t)topk);
+    double* z = (double*)malloc(sizeof(double) * (size_t)topk * (size_t)Bk);
+    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)topk * (size_t)Bk);
+    if (!blocks || !z || !keys) { bad = 1; free(blocks); free(z); free(keys); continue; }
+    const int64_t p = pos[r];
+
+    for (int h = 0; h < Hq; ++h) {
+      const int g = h / r_heads; /* contiguous GQA grouping */
+      double* o = out + (r * Hq + h) * (int64_t)D;
+      for (int d = 0; d < D; ++d) o[d] = 0.0;
+
+      /* J = { j <= p : floor(j / Bk) in Sel }, Sel taken as a set. */
+      int nb = 0;
+      for (int i = 0; i < topk; ++i) {
+        int32_t c = sel[(r * Hkv + g) * (int64_t)topk + i];
+        if (c >= 0) blocks[nb++] = c;
+      }
+      qsort(blocks, (size_t)nb, sizeof(int32_t), ascending_int);
+      int64_t nk = 0;
+      for (int i = 0; i < nb; ++i) {
+        if (i > 0 && blocks[i] == blocks[i - 1]) continue;
+        for (int64_t j = (int64_t)blocks[i] * Bk; j < ((int64_t)blocks[i] + 1) * Bk; ++j)
+          if (j <= p) keys[nk++] = j;
+      }
+      if (nk == 0) { lse[r * Hq + h] = -INFINITY; continue; }
+
+      const int64_t qoff = (r * Hq + h) * (int64_t)D;
+      double m = -INFINITY;
+      for (int64_t a = 0; a < nk; ++a) {
+        const int64_t koff = ((kstart[r] + keys[a]) * Hkv + g) * (int64_t)D;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d)
+          dot += (double)load_elem(q, dtype, qoff + d) * (double)load_elem(k, dtype, koff + d);
+        z[a] = scale * dot;
+        if (z[a] > m) m = z[a];
+      }
+      double l = 0.0;
+      for (int64_t a = 0; a < nk; ++a) {
+        const double w = exp(z[a] - m);
+        l += w;
+        const int64_t voff = ((kstart[r] + keys[a]) * Hkv + g) * (int64_t)D;
+        for (int d = 0; d < D; ++d) o[d] += w * (double)load_elem(v, dtype, voff + d);
+      }
+      for (int d = 0; d < D; ++d) o[d] /= l;
+      lse[r * Hq + h] = m + log(l);
+    }
+    free(blocks);
+    free(z);
+    free(keys);
+  }
+  return bad;
+}

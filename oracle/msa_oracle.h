@@ -1,0 +1,68 @@
+/*
+ * msa_oracle.h -- plain CPU oracle for MiniMax Sparse Attention (MSA).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link or
+ * call this.  It is the slow, obviously correct definition that the GPU path
+ * is checked against; it shares no code, header or constant with the GPU
+ * library.
+ *
+ * What it computes (sources, by page title and section):
+ *   - "MiniMax Sparse Attention: let each query pick its own blocks"
+ *     (ai.thesatyajit.com), section "The mechanism, precisely", and the
+ *     paper's Figure 1 reproduced there: per GQA group one index-query head is
+ *     dotted with one shared index-key head, the token scores are max-pooled
+ *     into fixed key blocks, the top-k blocks are kept, the query's own
+ *     (local) block is always kept, and the main branch runs exact softmax
+ *     attention over the kept blocks for every head of the group.
+ *   - The atlas record of MiniMax M3 (atlas.lewiswon.me), summary paragraph:
+ *     standard scaled dot-product softmax attention; selection on raw
+ *     max-pooled dot products; block 128, k = 16, local block forced in.
+ *
+ * Conventions (readings where the pages are silent):
+ *   - k counts the forced local block: Sel = {local} + best (k-1) earlier blocks.
+ *   - Order for selection: block score descending, then block id ascending.
+ *   - Blocks are aligned to absolute position 0.  Query row t of a sequence
+ *     with q_len M and kv_len N sits at position p = N - M + t.
+ *   - Index scores: raw dot product accumulated in fp32, sequentially over d.
+ *   - Attention: fp64 throughout, natural-log LSE, no sink term.
+ *
+ * Element type codes for inputs: 0 = fp32, 1 = bf16 bit patterns (uint16),
+ * widened exactly to fp32 by a 16-bit left shift.
+ */
+#ifndef MSA_ORACLE_H
+#define MSA_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Block selection for n query rows.
+ *   q_idx  : [n][G][DI]        index queries of the n rows (compact)
+ *   k_idx  : [*][DI]           index keys; row r's sequence starts at kstart[r]
+ *   pos    : [n]               absolute position p of each row (p < 0: no keys)
+ *   sel    : [n][G][topk] out  ascending block ids, -1 padded
+ *   scores : [n][G][nbmax] out (nullable) pooled block scores for c < p/Bk,
+ *            -inf elsewhere; nbmax is the caller's row stride.
+ * Returns 0 on success, nonzero on bad arguments. */
+int oracle_index_topk(const void* q_idx, const void* k_idx, int dtype,
+                      const int64_t* kstart, const int64_t* pos, int64_t n,
+                      int G, int DI, int Bk, int topk, int32_t* sel,
+                      float* scores, int64_t nbmax);
+
+/* Exact sparse attention for n query rows.
+ *   q    : [n][Hq][D]          queries of the n rows (compact)
+ *   k, v : [*][Hkv][D]         keys / values; row r's sequence starts at kstart[r]
+ *   sel  : [n][Hkv][topk]      selected block ids (entries < 0 ignored)
+ *   out  : [n][Hq][D]  fp64 out
+ *   lse  : [n][Hq]     fp64 out (natural log; -inf when no key is attended)
+ * Head h uses KV head / group h / (Hq / Hkv). */
+int oracle_sparse_attn(const void* q, const void* k, const void* v, int dtype,
+                       const int64_t* kstart, const int64_t* pos, const int32_t* sel,
+                       int64_t n, int Hq, int Hkv, int D, int Bk, int topk,
+                       double scale, double* out, double* lse);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

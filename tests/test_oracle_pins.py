@@ -1,0 +1,298 @@
+"""Pins for the CPU oracle, independent of the oracle's own code.
+
+Each test checks the oracle against something the pages or the mathematics
+fix, chosen so that a plausible slip in the oracle (a wrong causal bound, a
+dropped local block, a reversed tie-break, a wrong head-to-group map, a
+transposed operand, a missing scale) fails at least one of them:
+
+* block selection vs brute force on integer-exact scores (tiny inputs, several
+  block sizes, k values, varlen and bottom-right-aligned chunks, tie-dense data);
+* a selection certificate on a medium input with the measured head config;
+* attention vs dense causal GQA attention (torch SDPA, fp64) when every causal
+  block fits in the budget: the pages' dense "escape hatch" equals MSA then;
+* attention vs a dense boolean-mask formulation for arbitrary selections;
+* closed forms: K == 0 gives the mean of V over the attended keys with
+  lse = ln |J|; a single dominant key gives that key's value row; per-group
+  constant values expose the head-to-group map.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+
+def _grid(rng, shape, lo=-16, hi=16):
+    """Integer grid values u (the data is u / 8)."""
+    return rng.integers(lo, hi + 1, size=shape).astype(np.int64)
+
+
+def _cu(lens):
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+
+
+def _brute_selection(uq, uk, cu_q, cu_k, bk, topk):
+    """Block selection from integer scores (64 x the real scores), by sorting."""
+    nrows, G, _ = uq.shape
+    out = np.full((nrows, G, topk), -1, dtype=np.int64)
+    pooled = {}
+    for b in range(len(cu_q) - 1):
+        m = cu_q[b + 1] - cu_q[b]
+        n = cu_k[b + 1] - cu_k[b]
+        keys = uk[cu_k[b]:cu_k[b + 1]]
+        for t in range(m):
+            row = cu_q[b] + t
+            p = n - m + t
+            local = p // bk
+            for g in range(G):
+                tok = keys[: local * bk] @ uq[row, g]          # all token scores
+                S = [int(tok[c * bk:(c + 1) * bk].max()) for c in range(local)]
+                order = sorted(range(local), key=lambda c: (-S[c], c))
+                chosen = sorted(order[: topk - 1] + [local])
+                out[row, g, :len(chosen)] = chosen
+                pooled[(row, g)] = S
+    return out, pooled
+
+
+CASES = [
+    # (seq kv lens, q lens, G, DI, Bk, topk, lo, hi)
+    ([37], [37], 1, 4, 4, 1, -16, 16),
+    ([64], [64], 2, 8, 8, 2, -16, 16),
+    ([130, 77], [130, 77], 2, 4, 8, 4, -16, 16),
+    ([300], [45], 2, 8, 8, 4, -16, 16),        # bottom-right aligned chunk
+    ([257, 100, 129], [1, 100, 2], 1, 4, 4, 4, -16, 16),
+    ([200], [200], 2, 4, 4, 4, -1, 1),        # tie-dense: values in {-1/8, 0, 1/8}
+    ([160], [160], 1, 2, 8, 3, 0, 0),         # all scores equal: pure tie-break
+    ([512], [512], 2, 8, 128, 4, -16, 16),    # production block size
+    ([383], [129], 2, 8, 128, 2, -1, 1),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_selection_matches_bruteforce(oracle_lib, case):
+    kv, ql, G, DI, bk, topk, lo, hi = case
+    rng = np.random.default_rng(len(kv) * 1000 + sum(kv) + topk)
+    cu_k, cu_q = _cu(kv), _cu(ql)
+    uq = _grid(rng, (cu_q[-1], G, DI), lo, hi)
+    uk = _grid(rng, (cu_k[-1], DI), lo, hi)
+    want, pooled = _brute_selection(uq, uk, cu_q, cu_k, bk, topk)
+
+    rows, kstart, pos = oracle_lib.rows_prefill(cu_q, cu_k)
+    sel, scores = oracle_lib.index_topk((uq / 8).astype(np.float32), (uk / 8).astype(np.float32),
+                                        kstart, pos, rows, bk, topk, return_scores=True)
+    np.testing.assert_array_equal(sel, want)
+    # the oracle's fp32 pooled scores are exact: 64 x score == integer score
+    for (row, g), S in pooled.items():
+        got = scores[row, g, :len(S)].astype(np.float64) * 64.0
+        np.testing.assert_array_equal(got, np.asarray(S, dtype=np.float64))
+        assert np.all(np.isneginf(scores[row, g, len(S):]))
+
+
+def test_selection_bf16_inputs_equal_fp32(oracle_lib):
+    """bf16 bit patterns widen exactly: same selection as the fp32 copy."""
+    rng = np.random.default_rng(7)
+    cu = _cu([700])
+    uq = _grid(rng, (700, 2, 16))
+    uk = _grid(rng, (700, 16))
+    qf = torch.from_numpy((uq / 8).astype(np.float32))
+    kf = torch.from_numpy((uk / 8).astype(np.float32))
+    rows, kstart, pos = oracle_lib.rows_prefill(cu, cu)
+    a = oracle_lib.index_topk(qf, kf, kstart, pos, rows, 8, 5)
+    b = oracle_lib.index_topk(qf.bfloat16(), kf.bfloat16(), kstart, pos, rows, 8, 5)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_selection_certificate_measured_config(oracle_lib):
+    """Certificate per (row, group) on 64/4 heads, d_idx 128, block 128, k 16.
+
+    Integer-valued fp64 matmul gives exact block scores independently of the
+    oracle; the certificate is: local block present, count = min(k, l + 1),
+    ids distinct, ascending and <= l, and the worst selected earlier block
+    precedes the best unselected one in the order (score desc, id asc)."""
+    from learned_block_sparse_amd import synth
+    wl = synth.WORKLOADS["prefill_32k"]
+    L, topk, bk = 4096 + 37, wl.topk, wl.block_size
+    inp = synth.prefill_inputs(wl, seq_lens=[L], with_main=False, seed=3)
+    cu = inp["cu_q_host"]
+    rows, kstart, pos = oracle_lib.rows_prefill(cu, cu)
+    sel = oracle_lib.index_topk(inp["q_idx"], inp["k_idx"], kstart, pos, rows, bk, topk)
+
+    qd = inp["q_idx"].double().numpy() * 8.0    # integer-valued
+    kd = inp["k_idx"].double().numpy() * 8.0
+    nb = (L + bk - 1) // bk
+    G = qd.shape[1]
+    ties = 0
+    for g in range(G):
+        tok = qd[:, g, :] @ kd.T                       # exact: integers < 2**53
+        full = tok[:, : (nb - 1) * bk].reshape(L, nb - 1, bk).max(axis=2)
+        for t in range(L):
+            local = t // bk
+            s = sel[t, g]
+            ids = s[s >= 0]
+            assert local in ids
+            assert len(ids) == min(topk, local + 1)
+            assert np.all(np.diff(ids) > 0) and ids.max() == local
+            assert np.all(s[len(ids):] == -1)
+            earlier = [c for c in ids if c != local]
+            rest = sorted(set(range(local)) - set(earlier))
+            if earlier and rest:
+                worst = min(earlier, key=lambda c: (full[t, c], -c))
+                best = max(rest, key=lambda c: (full[t, c], -c))
+                assert (full[t, worst], -worst) > (full[t, best], -best)
+                ties += full[t, worst] == full[t, best]
+    assert ties > 0, "expected ties at the selection boundary on grid data"
+
+
+def _dense_reference(q, k, v, cu_q, cu_k, scale):
+    """Dense causal GQA attention in fp64 with torch SDPA (bottom-right causal)."""
+    outs, lses = [], []
+    Hq, Hkv = q.shape[1], k.shape[1]
+    rep = Hq // Hkv
+    for b in range(len(cu_q) - 1):
+        m, n = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        qb = q[cu_q[b]:cu_q[b + 1]].double().permute(1, 0, 2)[None]
+        kb = k[cu_k[b]:cu_k[b + 1]].double().repeat_interleave(rep, dim=1).permute(1, 0, 2)[None]
+        vb = v[cu_k[b]:cu_k[b + 1]].double().repeat_interleave(rep, dim=1).permute(1, 0, 2)[None]
+        t = torch.arange(m)[:, None]
+        j = torch.arange(n)[None, :]
+        allow = j <= (n - m + t)
+        o = torch.nn.functional.scaled_dot_product_attention(qb, kb, vb, attn_mask=allow,
+                                                             scale=scale)
+        z = (qb @ kb.transpose(-1, -2)) * scale
+        z = z.masked_fill(~allow, float("-inf"))
+        outs.append(o[0].permute(1, 0, 2))
+        lses.append(torch.logsumexp(z, dim=-1)[0].permute(1, 0))
+    return torch.cat(outs).numpy(), torch.cat(lses).numpy()
+
+
+@pytest.mark.parametrize("kv,ql,Hq,Hkv,D,bk,topk", [
+    ([512], [512], 8, 2, 32, 128, 4),
+    ([300, 41], [300, 41], 4, 1, 16, 64, 5),
+    ([511], [77], 16, 4, 64, 128, 4),
+    ([96], [96], 6, 3, 8, 8, 12),
+])
+def test_attention_equals_dense_when_all_blocks_fit(oracle_lib, kv, ql, Hq, Hkv, D, bk, topk):
+    g = torch.Generator().manual_seed(11)
+    cu_k, cu_q = _cu(kv), _cu(ql)
+    assert max(kv) <= topk * bk
+    q = torch.randn(cu_q[-1], Hq, D, generator=g)
+    k = torch.randn(cu_k[-1], Hkv, D, generator=g)
+    v = torch.randn(cu_k[-1], Hkv, D, generator=g)
+    qi = torch.randint(-16, 17, (cu_q[-1], Hkv, 8), generator=g).float() / 8
+    ki = torch.randint(-16, 17, (cu_k[-1], 8), generator=g).float() / 8
+    scale = 1.0 / math.sqrt(D)
+    sel, out, lse = oracle_lib.prefill(qi, ki, q, k, v, cu_q, cu_k, bk, topk)
+    ref_o, ref_l = _dense_reference(q, k, v, cu_q, cu_k, scale)
+    np.testing.assert_allclose(out, ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-12)
+
+
+def test_attention_matches_mask_formulation(oracle_lib):
+    """Arbitrary selections (duplicates, future and missing local blocks
+    included) against a dense boolean-mask softmax written independently."""
+    rng = np.random.default_rng(5)
+    kv, ql, Hq, Hkv, D, bk, topk = [333, 200], [120, 200], 6, 2, 16, 16, 4
+    cu_k, cu_q = _cu(kv), _cu(ql)
+    q = rng.standard_normal((cu_q[-1], Hq, D)).astype(np.float32)
+    k = rng.standard_normal((cu_k[-1], Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((cu_k[-1], Hkv, D)).astype(np.float32)
+    rows, kstart, pos = oracle_lib.rows_prefill(cu_q, cu_k)
+    sel = rng.integers(-1, 25, size=(len(rows), Hkv, topk)).astype(np.int32)
+    for r in range(len(rows)):     # keep at least the local block in most rows
+        if r % 3:
+            sel[r, :, 0] = pos[r] // bk
+    out, lse = oracle_lib.sparse_attn(q, k, v, sel, kstart, pos, rows, bk, topk)
+    scale = 1.0 / math.sqrt(D)
+    for r in range(len(rows)):
+        b = int(np.searchsorted(cu_q, rows[r], side="right") - 1)
+        n = cu_k[b + 1] - cu_k[b]
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            j = np.arange(n)
+            mask = np.isin(j // bk, sel[r, g]) & (j <= pos[r])
+            kk = k[cu_k[b]:cu_k[b + 1], g].astype(np.float64)
+            vv = v[cu_k[b]:cu_k[b + 1], g].astype(np.float64)
+            z = kk @ q[rows[r], h].astype(np.float64) * scale
+            if not mask.any():
+                assert np.isneginf(lse[r, h]) and np.all(out[r, h] == 0)
+                continue
+            z = np.where(mask, z, -np.inf)
+            w = np.exp(z - z.max())
+            np.testing.assert_allclose(out[r, h], (w / w.sum()) @ vv, atol=1e-12, rtol=0)
+            np.testing.assert_allclose(lse[r, h], z.max() + np.log(w.sum()), atol=1e-12, rtol=0)
+
+
+def test_zero_keys_give_mean_of_values(oracle_lib):
+    """K == 0: every logit is 0, so o = mean of v over J and lse = ln |J|.
+    |J| is counted here from the selection and the causal bound alone."""
+    rng = np.random.default_rng(9)
+    kv, ql, Hq, Hkv, D, bk, topk = [1000], [390], 4, 2, 8, 32, 5
+    cu_k, cu_q = _cu(kv), _cu(ql)
+    q = rng.standard_normal((cu_q[-1], Hq, D)).astype(np.float32)
+    k = np.zeros((cu_k[-1], Hkv, D), dtype=np.float32)
+    v = rng.standard_normal((cu_k[-1], Hkv, D)).astype(np.float32)
+    qi = (_grid(rng, (cu_q[-1], Hkv, 4)) / 8).astype(np.float32)
+    ki = (_grid(rng, (cu_k[-1], 4)) / 8).astype(np.float32)
+    sel, out, lse = oracle_lib.prefill(qi, ki, q, k, v, cu_q, cu_k, bk, topk)
+    rows, kstart, pos = oracle_lib.rows_prefill(cu_q, cu_k)
+    for r in range(len(rows)):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            blocks = sel[r, g][sel[r, g] >= 0]
+            keys = [j for c in blocks for j in range(c * bk, (c + 1) * bk) if j <= pos[r]]
+            expect_n = sum(min(bk, pos[r] - c * bk + 1) for c in blocks)
+            assert len(keys) == expect_n
+            np.testing.assert_allclose(lse[r, h], math.log(expect_n), atol=1e-12, rtol=0)
+            np.testing.assert_allclose(out[r, h], v[keys, g].astype(np.float64).mean(0),
+                                       atol=1e-12, rtol=0)
+
+
+def test_dominant_key_selects_its_value_row(oracle_lib):
+    """One key aligned with the query dominates the softmax: o == v of that
+    key's row and KV head (pins the value gather and the head-to-group map)."""
+    rng = np.random.default_rng(13)
+    N, Hq, Hkv, D, bk, topk = 256, 4, 2, 16, 16, 3
+    cu = _cu([N])
+    q = (0.01 * rng.standard_normal((N, Hq, D))).astype(np.float32)
+    k = (0.01 * rng.standard_normal((N, Hkv, D))).astype(np.float32)
+    v = rng.standard_normal((N, Hkv, D)).astype(np.float32)
+    t = N - 1
+    q[t, :, 0] = 30.0
+    star = 250                                   # inside the local block of t
+    k[star, :, 0] = 30.0
+    qi = np.zeros((N, Hkv, 2), dtype=np.float32)
+    ki = np.zeros((N, 2), dtype=np.float32)
+    sel, out, lse = oracle_lib.prefill(qi, ki, q, k, v, cu, cu, bk, topk, rows=[t])
+    for h in range(Hq):
+        np.testing.assert_allclose(out[0, h], v[star, h // (Hq // Hkv)], atol=1e-9, rtol=0)
+
+
+def test_head_to_group_map(oracle_lib):
+    """Per-KV-head constant values: head h reads group h // (Hq / Hkv)."""
+    rng = np.random.default_rng(17)
+    N, Hq, Hkv, D, bk, topk = 64, 8, 4, 8, 8, 2
+    cu = _cu([N])
+    q = rng.standard_normal((N, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((N, Hkv, D)).astype(np.float32)
+    v = np.zeros((N, Hkv, D), dtype=np.float32)
+    for g in range(Hkv):
+        v[:, g, :] = g + 1.0
+    qi = (_grid(rng, (N, Hkv, 4)) / 8).astype(np.float32)
+    ki = (_grid(rng, (N, 4)) / 8).astype(np.float32)
+    _, out, _ = oracle_lib.prefill(qi, ki, q, k, v, cu, cu, bk, topk)
+    for h in range(Hq):
+        np.testing.assert_allclose(out[:, h], h // 2 + 1.0, atol=1e-12, rtol=0)
+
+
+def test_empty_rows_and_negative_positions(oracle_lib):
+    """q_len > kv_len leaves leading rows with p < 0: no keys, -1 ids, lse -inf."""
+    rng = np.random.default_rng(19)
+    cu_k, cu_q = _cu([3]), _cu([5])
+    q = rng.standard_normal((5, 2, 4)).astype(np.float32)
+    k = rng.standard_normal((3, 1, 4)).astype(np.float32)
+    v = rng.standard_normal((3, 1, 4)).astype(np.float32)
+    qi = np.ones((5, 1, 2), dtype=np.float32)
+    ki = np.ones((3, 2), dtype=np.float32)
+    sel, out, lse = oracle_lib.prefill(qi, ki, q, k, v, cu_q, cu_k, 2, 2)
+    assert np.all(sel[:2] == -1) and np.all(np.isneginf(lse[:2])) and np.all(out[:2] == 0)
+    assert np.all(np.isfinite(lse[2:]))
