@@ -1,0 +1,182 @@
+/*
+ * msa.h -- C ABI of the MI355X (gfx950) MiniMax Sparse Attention library.
+ *
+ * MiniMax Sparse Attention (MSA) adds, per GQA group, an index branch that
+ * scores every earlier key block with one index-query head against one shared
+ * index-key head, max-pools the token scores per block and keeps the top-k
+ * blocks, always including the query's own (local) block; the main branch
+ * then runs exact softmax attention over only those blocks for every head of
+ * the group.  Defined on "MiniMax Sparse Attention: let each query pick its
+ * own blocks" (ai.thesatyajit.com), section "The mechanism, precisely", and
+ * the paper's Figure 1 reproduced there; deployed as block 128, k = 16 (the
+ * atlas record of MiniMax M3, atlas.lewiswon.me, summary paragraph).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Sequences are packed token-major ("varlen"): a sequence b has q_len
+ *    M_b = cu_seqlens_q[b+1] - cu_seqlens_q[b] query rows and kv_len N_b key
+ *    rows.  Its query row t sits at absolute position p = N_b - M_b + t
+ *    (bottom-right aligned causal attention): M_b = N_b is a full prefill,
+ *    M_b < N_b a chunk of a longer prefill, M_b = 1 a decode step.  Rows with
+ *    p < 0 (only when M_b > N_b) attend to nothing: ids -1, output 0, lse -inf.
+ *  - Blocks are aligned to absolute position 0: block c holds positions
+ *    [c * block_size, (c + 1) * block_size).  The local block is
+ *    l = floor(p / block_size).
+ *  - topk counts the forced local block: the selection is {l} plus the best
+ *    min(topk - 1, l) earlier blocks c < l.  "Best" is the total order
+ *    (pooled score descending, block id ascending), so ties go to the lower id
+ *    and the result is unique.
+ *  - GQA: G = num_kv_heads groups, r = num_heads / G heads per group, query
+ *    head h belongs to group floor(h / r).
+ *  - All pointers to tensors are device pointers, except where stated.  The
+ *    caller owns every buffer and the stream; the library allocates no device
+ *    memory and keeps no state between calls.  Every call is asynchronous on
+ *    `stream` (0 = the null stream).
+ *  - Argument errors are returned before anything is launched.  Values held
+ *    in device arrays (sequence lengths, block ids) cannot be checked on the
+ *    host: lengths must not exceed max_q_len / max_kv_len and must match the
+ *    buffers; the kernels never read outside [row 0, last row of the
+ *    sequence], ignore block ids < 0 or > l, and never write outside the rows
+ *    the lengths describe.
+ *  - Results are deterministic: the same inputs give bit-identical outputs,
+ *    independent of how the work is split.
+ *
+ * Supported shapes: block_size 128; head_dim 128; index_dim 64 or 128;
+ * 1 <= topk <= 16; num_heads % num_kv_heads == 0 with at most 16 heads per
+ * group; 1 <= num_kv_heads <= 16.  Other values return MSA_ERR_UNSUPPORTED.
+ * Element types: MSA_F32 (fp32 in, fp32 out) and MSA_BF16 (bf16 in, bf16
+ * out); accumulation is fp32 in both.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad combination */
+  MSA_ERR_UNSUPPORTED = 2,  /* a shape or type this build does not implement */
+  MSA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+  MSA_ERR_HIP = 4           /* a HIP launch or runtime call failed */
+} msa_status_t;
+
+typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype_t;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* msa_status_string(msa_status_t status);
+
+/* Last HIP error recorded by a call that returned MSA_ERR_HIP on this host
+ * thread (hipSuccess if none). */
+int msa_last_hip_error(void);
+
+/* ------------------------------------------------------------------------
+ * Index branch: score, block max-pool, top-k with the forced local block.
+ *
+ * "MiniMax Sparse Attention: let each query pick its own blocks", section
+ * "The mechanism, precisely": for query row t and group g the token scores are
+ * s_j = q_idx[t, g, :] . k_idx[j, :] (raw dot product, no scale: selection is
+ * on raw scores, the "exp-free" top-k of the atlas record's kernel list), the
+ * block score is S_c = max over the block's tokens, and the block ids kept are
+ * {l} and the best min(topk - 1, l) blocks c < l.  The local block is never
+ * scored; every scored block is full.
+ *
+ *   q_idx        [Tq, G, index_dim]  index queries, Tq = cu_seqlens_q[batch]
+ *   k_idx        [Tk, index_dim]     index keys (one head shared by all groups)
+ *   dtype        element type of q_idx and k_idx
+ *   cu_seqlens_q [batch + 1] int32, device: query row offsets, cu[0] = 0
+ *   cu_seqlens_k [batch + 1] int32, device: key row offsets, cu[0] = 0
+ *   max_q_len, max_kv_len   host upper bounds of the per-sequence lengths
+ *   num_groups   G (= number of KV heads)
+ *   block_idx    [Tq, G, topk] int32 out: ascending ids, -1 padded
+ *   workspace    device scratch of at least msa_index_topk_workspace_size()
+ *                bytes (may be NULL when that size is 0)
+ *
+ * Scores accumulate in fp32.  With max_q_len == 1 (one new token per
+ * sequence) the call takes the decode path: the whole index-key cache is
+ * streamed once for all groups, then a per-(sequence, group) selection runs.
+ * Otherwise the prefill path scans key blocks per query block with an MFMA
+ * GEMM whose epilogue max-pools and keeps a per-lane register top-k, then
+ * merges the per-chunk candidates.  Both paths use the same total order and
+ * return identical ids on identical inputs.
+ * ---------------------------------------------------------------------- */
+size_t msa_index_topk_workspace_size(int batch, int max_q_len, int max_kv_len, int num_groups,
+                                     int block_size, int topk);
+
+msa_status_t msa_index_topk(const void* q_idx, const void* k_idx, msa_dtype_t dtype,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                            int max_q_len, int max_kv_len, int num_groups, int index_dim,
+                            int block_size, int topk, int32_t* block_idx, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Main branch, prefill: exact causal softmax attention over the selected
+ * blocks, for every head of each group.
+ *
+ * "MiniMax Sparse Attention: let each query pick its own blocks", section
+ * "The mechanism, precisely" (main branch) and the atlas record's summary
+ * ("standard scaled dot-product softmax attention"): for head h of group g,
+ * J = { j <= p : floor(j / block_size) in Sel(t, g) },
+ * z_j = softmax_scale * q[t, h, :] . k[j, g, :], out = softmax(z) V_J,
+ * lse = ln sum_j exp(z_j).  There is no sink term.
+ *
+ *   q            [Tq, num_heads, head_dim]
+ *   k, v         [Tk, num_kv_heads, head_dim]
+ *   block_idx    [Tq, num_kv_heads, topk] int32 (from msa_index_topk)
+ *   cu_seqlens_q, cu_seqlens_k, max_q_len, max_kv_len   as for msa_index_topk
+ *   softmax_scale  <= 0 selects 1 / sqrt(head_dim)
+ *   num_splits   split each selection into this many chunks of consecutive
+ *                ids, attended separately and merged by a log-sum-exp combine
+ *                in a fixed order (no atomics); 0 = choose automatically
+ *   out          [Tq, num_heads, head_dim], element type `dtype`
+ *   lse          [Tq, num_heads] fp32, natural log, or NULL
+ *   workspace    at least msa_sparse_attn_workspace_size() bytes
+ * ---------------------------------------------------------------------- */
+size_t msa_sparse_attn_workspace_size(int batch, int max_q_len, int num_heads, int num_kv_heads,
+                                      int head_dim, int topk, int num_splits);
+
+msa_status_t msa_sparse_attn_prefill(const void* q, const void* k, const void* v, msa_dtype_t dtype,
+                                     const int32_t* block_idx, const int32_t* cu_seqlens_q,
+                                     const int32_t* cu_seqlens_k, int batch, int max_q_len,
+                                     int max_kv_len, int num_heads, int num_kv_heads, int head_dim,
+                                     int block_size, int topk, float softmax_scale, int num_splits,
+                                     void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Main branch, decode: one new query token per sequence against its cache.
+ *
+ * Same definition as the prefill call with q_len = 1 and p = ctx_lens[b] - 1
+ * (the new token's K/V are already in the cache).  Per the pages
+ * ("llama.cpp Merges MiniMax M3's Sparse Attention", key facts) the main
+ * branch of a decode step reads about k * block_size = 2,048 tokens
+ * regardless of context; the selection is split over num_splits chunks
+ * (0 = automatic) so that the block gathers fill the GPU, then combined.
+ *
+ *   q             [batch, num_heads, head_dim]
+ *   k_cache, v_cache  token-major [*, num_kv_heads, head_dim]; sequence b's
+ *                 tokens are rows [cache_offsets[b], cache_offsets[b] + ctx_lens[b])
+ *   block_idx     [batch, num_kv_heads, topk] int32
+ *   cache_offsets [batch] int64, device, in tokens
+ *   ctx_lens      [batch] int32, device, >= 1, <= max_ctx
+ *   out           [batch, num_heads, head_dim]; lse [batch, num_heads] or NULL
+ *   workspace     at least msa_sparse_attn_workspace_size(batch, 1, ...) bytes
+ * ---------------------------------------------------------------------- */
+msa_status_t msa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                    msa_dtype_t dtype, const int32_t* block_idx,
+                                    const int64_t* cache_offsets, const int32_t* ctx_lens,
+                                    int batch, int max_ctx, int num_heads, int num_kv_heads,
+                                    int head_dim, int block_size, int topk, float softmax_scale,
+                                    int num_splits, void* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H */

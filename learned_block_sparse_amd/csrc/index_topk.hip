@@ -1,0 +1,378 @@
+// index_topk.hip -- MSA index branch on gfx950: score, block max-pool, top-k.
+//
+// Method: "MiniMax Sparse Attention: let each query pick its own blocks",
+// section "The mechanism, precisely" and the paper's Figure 1 there (index
+// query head per group, one shared index key head, Q_idx K_idx^T, block max
+// pooling, top-k blocks, local block always kept).  Selection is on raw
+// scores with no softmax ("exp-free" top-k in the atlas record's kernel list).
+//
+// Prefill path (two kernels):
+//   idx_scan_prefill  one workgroup per (sequence, query block, query slice,
+//                     key chunk).  Its columns are the (query, group) pairs of
+//                     one query block -- all queries of a block scan the same
+//                     earlier blocks, so no causal mask is ever needed.  Each
+//                     key block (128 x d_idx) is staged in LDS once and shared
+//                     by 8 waves; scores come from 32x32 MFMA tiles oriented
+//                     keys x columns, so a column's 128 scores sit in two lanes
+//                     (16 registers x 4 tiles each) and the block max is a
+//                     register max plus one lane swap.  Each lane then owns
+//                     one column and keeps a sorted top-15 list in registers.
+//   idx_merge_prefill one wave per (query, group): merges the per-chunk lists
+//                     under the same total order, adds the local block, writes
+//                     ids ascending.
+// Decode path (two kernels):
+//   idx_decode_scores streams the index-key cache once: each wave scores a run
+//                     of blocks for all groups of its sequence (16x16 MFMA,
+//                     keys x groups) and writes one fp32 per (group, block).
+//   idx_decode_select one workgroup per (sequence, group): per-thread register
+//                     lists, then two wave merges.
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+// --------------------------------------------------------------------------
+// Prefill scan
+// --------------------------------------------------------------------------
+constexpr int kScanThreads = 512;  // 8 waves; each owns 64 columns (two 32-wide tiles)
+
+template <typename T, int DI>
+struct ScanLds {
+  // One key block, rows padded by 16 bytes so 16-byte reads of 32 rows at the
+  // same column spread over the banks.
+  static constexpr int kRowBytes = DI * (int)sizeof(T) + 16;
+  static constexpr int kBufBytes = kBlock * kRowBytes;
+  static constexpr int kChunks = kBlock * DI * (int)sizeof(T) / 16;   // 16-byte pieces
+  static constexpr int kPerThread = kChunks / kScanThreads;
+  static constexpr int kChunksPerRow = DI * (int)sizeof(T) / 16;
+};
+
+template <typename T, int DI>
+__global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
+    const T* __restrict__ q_idx, const T* __restrict__ k_idx, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_k, int G, int qw, int nsub, int max_qblocks, int chunk,
+    int max_chunks, float* __restrict__ cand_s, int32_t* __restrict__ cand_i) {
+  using L = ScanLds<T, DI>;
+  static_assert(L::kChunks % kScanThreads == 0, "key block must split evenly over threads");
+  constexpr int KS = DI / 16;  // 16-wide contraction steps
+  __shared__ __attribute__((aligned(16))) char lds[2 * L::kBufBytes];
+
+  // Decode the workgroup: key chunk fastest, then query slice, then query block
+  // (heaviest query blocks first), then sequence.
+  int bid = blockIdx.x;
+  const int ch = bid % max_chunks;  bid /= max_chunks;
+  const int sub = bid % nsub;       bid /= nsub;
+  const int slot = max_qblocks - 1 - (bid % max_qblocks);
+  const int b = bid / max_qblocks;
+
+  const int q0 = cu_q[b], M = cu_q[b + 1] - q0;
+  const int k0 = cu_k[b], N = cu_k[b + 1] - k0;
+  if (M <= 0 || N <= 0) return;
+  const int pfirst = N - M > 0 ? N - M : 0;  // first position that has keys
+  const int c = pfirst / kBlock + slot;      // this workgroup's query block
+  if (c * kBlock >= N) return;
+  const int plo = max(c * kBlock, pfirst) + sub * qw;
+  const int phi = min(min((c + 1) * kBlock, N), plo + qw);
+  if (plo >= phi) return;
+  const int s_lo = ch * chunk;
+  const int s_hi = min(s_lo + chunk, c);  // scan earlier blocks only
+  if (s_lo >= s_hi) return;
+
+  const int ncols = (phi - plo) * G;
+  const int64_t row0 = (int64_t)(plo - (N - M)) + q0;  // first query row
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int col_base = wave * 64;
+  const bool active = col_base < ncols;
+
+  // B operand (Q^T): columns col_base + 32*j + lane%32, contraction slots
+  // 16*ks + 8*(lane/32) .. +7.
+  frag8<T> qf[2][KS];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = col_base + 32 * j + (lane & 31);
+    const bool ok = col < ncols;
+    const T* qp = q_idx + (row0 * G + (ok ? col : 0)) * DI + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[j][ks] = ok ? load8(qp + 16 * ks) : zero8<T>();
+  }
+
+  float ls[kList];
+  int li[kList];
+#pragma unroll
+  for (int j = 0; j < kList; ++j) { ls[j] = -__builtin_inff(); li[j] = -1; }
+
+  // Key blocks are staged into LDS in 16-byte pieces (coalesced global reads),
+  // double-buffered: block s+1 is fetched into registers while block s is used.
+  const char* kseq = reinterpret_cast<const char*>(k_idx + (int64_t)k0 * DI);
+  constexpr int64_t kBlockBytes = (int64_t)kBlock * DI * sizeof(T);
+  u32x4 stage[L::kPerThread];
+#pragma unroll
+  for (int u = 0; u < L::kPerThread; ++u)
+    stage[u] = *reinterpret_cast<const u32x4*>(kseq + s_lo * kBlockBytes + (threadIdx.x + u * kScanThreads) * 16);
+#pragma unroll
+  for (int u = 0; u < L::kPerThread; ++u) {
+    const int piece = threadIdx.x + u * kScanThreads;
+    *reinterpret_cast<u32x4*>(lds + (piece / L::kChunksPerRow) * L::kRowBytes + (piece % L::kChunksPerRow) * 16) =
+        stage[u];
+  }
+  __syncthreads();
+
+  for (int s = s_lo; s < s_hi; ++s) {
+    const int buf = (s - s_lo) & 1;
+    const bool more = s + 1 < s_hi;
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < L::kPerThread; ++u)
+        stage[u] = *reinterpret_cast<const u32x4*>(kseq + (s + 1) * kBlockBytes + (threadIdx.x + u * kScanThreads) * 16);
+    }
+    if (active) {
+      const char* kb = lds + buf * L::kBufBytes;
+      float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+#pragma unroll
+      for (int kt = 0; kt < kBlock / 32; ++kt) {
+        f32x16 acc0 = {}, acc1 = {};
+        const char* arow = kb + (32 * kt + (lane & 31)) * L::kRowBytes + 8 * (lane >> 5) * (int)sizeof(T);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const frag8<T> a = *reinterpret_cast<const frag8<T>*>(arow + 16 * ks * (int)sizeof(T));
+          acc0 = mma32(a, qf[0][ks], acc0);
+          acc1 = mma32(a, qf[1][ks], acc1);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { m0 = fmaxf(m0, acc0[r]); m1 = fmaxf(m1, acc1[r]); }
+      }
+      // Lane l < 32 owns column l of tile 0, lane l >= 32 column l-32 of tile 1;
+      // each needs the other half-wave's partial max of its own column.
+      const float send = lane < 32 ? m1 : m0;
+      const float recv = shfl_xor_f(send, 32);
+      const float v = fmaxf(lane < 32 ? m0 : m1, recv);
+      list_insert(ls, li, v, s);
+    }
+    if (more) {
+      char* dst = lds + (buf ^ 1) * L::kBufBytes;
+#pragma unroll
+      for (int u = 0; u < L::kPerThread; ++u) {
+        const int piece = threadIdx.x + u * kScanThreads;
+        *reinterpret_cast<u32x4*>(dst + (piece / L::kChunksPerRow) * L::kRowBytes + (piece % L::kChunksPerRow) * 16) =
+            stage[u];
+      }
+    }
+    __syncthreads();
+  }
+
+  const int col = col_base + lane;
+  if (active && col < ncols) {
+    const int64_t base = ((row0 * G + col) * max_chunks + ch) * kList;
+#pragma unroll
+    for (int j = 0; j < kList; ++j) { cand_s[base + j] = ls[j]; cand_i[base + j] = li[j]; }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Prefill merge: one wave per (query row, group)
+// --------------------------------------------------------------------------
+__device__ __forceinline__ int find_seq(const int32_t* cu, int batch, int64_t row) {
+  int lo = 0, hi = batch;  // invariant: cu[lo] <= row < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= row) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void idx_merge_prefill(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int64_t rows_bound,
+    int G, int topk, int chunk, int max_chunks, const float* __restrict__ cand_s,
+    const int32_t* __restrict__ cand_i, int32_t* __restrict__ block_idx) {
+  const int64_t item = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (item >= rows_bound * G) return;
+  const int64_t row = item / G;
+  const int g = (int)(item % G);
+  if (row >= cu_q[batch]) return;
+  const int lane = lane_id();
+  const int b = find_seq(cu_q, batch, row);
+  const int M = cu_q[b + 1] - cu_q[b], N = cu_k[b + 1] - cu_k[b];
+  const int64_t p = (int64_t)N - M + (row - cu_q[b]);
+  int32_t* out = block_idx + (row * G + g) * topk;
+  if (p < 0) {
+    if (lane < topk) out[lane] = -1;
+    return;
+  }
+  const int local = (int)(p / kBlock);
+  const int nch = (local + chunk - 1) / chunk;
+
+  float ls[kList];
+  int li[kList];
+  if (lane < nch) {
+    const int64_t base = ((row * G + g) * max_chunks + lane) * kList;
+#pragma unroll
+    for (int j = 0; j < kList; ++j) { ls[j] = cand_s[base + j]; li[j] = cand_i[base + j]; }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kList; ++j) { ls[j] = -__builtin_inff(); li[j] = -1; }
+  }
+  int mine;
+  const int found = wave_merge(ls, li, topk - 1, mine);
+  write_selection(mine, found, local, topk, out);
+}
+
+// --------------------------------------------------------------------------
+// Decode: stream the index-key cache once, one fp32 score per (group, block)
+// --------------------------------------------------------------------------
+template <typename T, int DI>
+__global__ __launch_bounds__(256) void idx_decode_scores(
+    const T* __restrict__ q_idx, const T* __restrict__ k_idx, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_k, int G, int nb_max, int blocks_per_wave, int wgs_per_seq,
+    float* __restrict__ scores) {
+  constexpr int DS = DI / 32;  // 32-wide contraction steps of the 16x16 MFMA
+  const int b = blockIdx.x / wgs_per_seq;
+  const int wchunk = (blockIdx.x % wgs_per_seq) * 4 + threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int q0 = cu_q[b];
+  if (cu_q[b + 1] - q0 != 1) return;
+  const int k0 = cu_k[b], N = cu_k[b + 1] - k0;
+  if (N <= 0) return;
+  const int local = (N - 1) / kBlock;
+  const int c_lo = wchunk * blocks_per_wave;
+  const int c_hi = min(c_lo + blocks_per_wave, local);
+  if (c_lo >= c_hi) return;
+
+  // B operand: columns are the groups (lane%16 < G), slots 32*ds + 8*(lane/16).
+  const int gcol = lane & 15;
+  frag8<T> qf[DS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds)
+    qf[ds] = gcol < G ? load8(q_idx + ((int64_t)q0 * G + gcol) * DI + 32 * ds + 8 * (lane >> 4))
+                      : zero8<T>();
+
+  const T* kbase = k_idx + ((int64_t)k0 + (lane & 15)) * DI + 8 * (lane >> 4);
+  for (int c = c_lo; c < c_hi; ++c) {
+    const T* kb = kbase + (int64_t)c * kBlock * DI;
+    frag8<T> a[kBlock / 16][DS];
+#pragma unroll
+    for (int kt = 0; kt < kBlock / 16; ++kt)
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) a[kt][ds] = load8(kb + (int64_t)kt * 16 * DI + 32 * ds);
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int kt = 0; kt < kBlock / 16; ++kt) {
+      f32x4 acc = {};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) acc = mma16(a[kt][ds], qf[ds], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[r]);
+    }
+    m = fmaxf(m, shfl_xor_f(m, 16));
+    m = fmaxf(m, shfl_xor_f(m, 32));
+    if (lane < G) scores[((int64_t)b * G + lane) * nb_max + c] = m;
+  }
+}
+
+constexpr int kSelThreads = 256;
+
+__global__ __launch_bounds__(kSelThreads) void idx_decode_select(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int G, int topk, int nb_max,
+    const float* __restrict__ scores, int32_t* __restrict__ block_idx) {
+  __shared__ float sh_s[kSelThreads / kWave][kList];
+  __shared__ int sh_i[kSelThreads / kWave][kList];
+  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  const int q0 = cu_q[b];
+  if (cu_q[b + 1] - q0 != 1) return;
+  const int N = cu_k[b + 1] - cu_k[b];
+  int32_t* out = block_idx + ((int64_t)q0 * G + g) * topk;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  if (N <= 0) {
+    if (wave == 0 && lane < topk) out[lane] = -1;
+    return;
+  }
+  const int local = (N - 1) / kBlock;
+  const float* sc = scores + ((int64_t)b * G + g) * nb_max;
+
+  float ls[kList];
+  int li[kList];
+#pragma unroll
+  for (int j = 0; j < kList; ++j) { ls[j] = -__builtin_inff(); li[j] = -1; }
+  for (int c = threadIdx.x; c < local; c += kSelThreads) list_insert(ls, li, sc[c], c);
+
+  int mine;
+  const int found = wave_merge(ls, li, kList, mine);
+  if (lane < kList) {
+    sh_s[wave][lane] = lane < found ? 0.0f : -__builtin_inff();
+    sh_i[wave][lane] = lane < found ? mine : -1;
+  }
+  // Scores of the winners, fetched back by id (exact copies).
+  if (lane < found) sh_s[wave][lane] = sc[mine];
+  __syncthreads();
+  if (wave != 0) return;
+  if (lane < kSelThreads / kWave) {
+#pragma unroll
+    for (int j = 0; j < kList; ++j) { ls[j] = sh_s[lane][j]; li[j] = sh_i[lane][j]; }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kList; ++j) { ls[j] = -__builtin_inff(); li[j] = -1; }
+  }
+  const int found2 = wave_merge(ls, li, topk - 1, mine);
+  write_selection(mine, found2, local, topk, out);
+}
+
+// --------------------------------------------------------------------------
+// Launchers
+// --------------------------------------------------------------------------
+template <typename T, int DI>
+static hipError_t launch_index_prefill(const IndexPlan& pl, const void* q_idx, const void* k_idx,
+                                       const int32_t* cu_q, const int32_t* cu_k, int batch, int G,
+                                       int topk, int32_t* block_idx, char* ws, hipStream_t st) {
+  float* cand_s = reinterpret_cast<float*>(ws);
+  int32_t* cand_i = reinterpret_cast<int32_t*>(ws + pl.cand_score_bytes);
+  if (pl.scan_wgs > 0) {
+    hipLaunchKernelGGL((idx_scan_prefill<T, DI>), dim3((unsigned)pl.scan_wgs), dim3(kScanThreads), 0, st,
+                       static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), cu_q, cu_k, G,
+                       pl.qw, pl.nsub, pl.max_qblocks, pl.chunk, pl.max_chunks, cand_s, cand_i);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t items = pl.rows_bound * G;
+  hipLaunchKernelGGL(idx_merge_prefill, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, cu_q, cu_k,
+                     batch, pl.rows_bound, G, topk, pl.chunk, pl.max_chunks, cand_s, cand_i, block_idx);
+  return hipGetLastError();
+}
+
+template <typename T, int DI>
+static hipError_t launch_index_decode(const IndexPlan& pl, const void* q_idx, const void* k_idx,
+                                      const int32_t* cu_q, const int32_t* cu_k, int batch, int G,
+                                      int topk, int32_t* block_idx, char* ws, hipStream_t st) {
+  float* scores = reinterpret_cast<float*>(ws);
+  if (pl.dec_wgs_per_seq > 0) {
+    hipLaunchKernelGGL((idx_decode_scores<T, DI>), dim3((unsigned)(batch * pl.dec_wgs_per_seq)), dim3(256), 0,
+                       st, static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), cu_q, cu_k, G,
+                       pl.nb_max, pl.dec_blocks_per_wave, pl.dec_wgs_per_seq, scores);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(idx_decode_select, dim3((unsigned)(batch * G)), dim3(kSelThreads), 0, st, cu_q, cu_k, G,
+                     topk, pl.nb_max, scores, block_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_topk(const IndexPlan& pl, int dtype, int DI, const void* q_idx, const void* k_idx,
+                             const int32_t* cu_q, const int32_t* cu_k, int batch, int G, int topk,
+                             int32_t* block_idx, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  if (pl.decode) {
+    if (dtype == 0) {
+      return DI == 64 ? launch_index_decode<float, 64>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st)
+                      : launch_index_decode<float, 128>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st);
+    }
+    return DI == 64 ? launch_index_decode<bf16, 64>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st)
+                    : launch_index_decode<bf16, 128>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st);
+  }
+  if (dtype == 0) {
+    return DI == 64 ? launch_index_prefill<float, 64>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st)
+                    : launch_index_prefill<float, 128>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st);
+  }
+  return DI == 64 ? launch_index_prefill<bf16, 64>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st)
+                  : launch_index_prefill<bf16, 128>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st);
+}
+
+}  // namespace msa

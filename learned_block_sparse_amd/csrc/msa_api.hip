@@ -1,0 +1,206 @@
+// msa_api.hip -- the C ABI declared in include/msa.h: argument checks, work
+// plans and dispatch to the HIP kernels.  The library allocates no device
+// memory; scratch comes from the caller's workspace.
+#include "../../include/msa.h"
+#include "msa_device.h"
+#include "msa_launch.h"
+
+#include <math.h>
+
+namespace msa {
+
+static constexpr size_t kAlign = 256;
+static size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Scan workgroups aimed at per launch: several per CU on 256 CUs, so the
+// triangular causal work spreads evenly.
+static constexpr int64_t kScanTargetWgs = 2048;
+// Decode scan: waves aimed at per launch.
+static constexpr int64_t kDecodeTargetWaves = 8192;
+// Attention: work items (waves) aimed at before splitting selections.
+static constexpr int64_t kAttnTargetWaves = 8192;
+
+IndexPlan plan_index(int batch, int max_q_len, int max_kv_len, int G) {
+  IndexPlan pl;
+  pl.nb_max = (int)ceil_div(max_kv_len, kBlock);
+  pl.rows_bound = (int64_t)batch * max_q_len;
+  pl.decode = (max_q_len == 1);
+  if (pl.decode) {
+    const int64_t total_blocks = (int64_t)batch * pl.nb_max;
+    int64_t bpw = ceil_div(total_blocks, kDecodeTargetWaves);
+    if (bpw < 1) bpw = 1;
+    if (bpw > 64) bpw = 64;
+    pl.dec_blocks_per_wave = (int)bpw;
+    const int64_t waves_per_seq = ceil_div(pl.nb_max, bpw);
+    pl.dec_wgs_per_seq = (int)ceil_div(waves_per_seq, 4);
+    pl.score_bytes = align_up((size_t)batch * G * pl.nb_max * sizeof(float));
+    pl.workspace_bytes = pl.score_bytes;
+    return pl;
+  }
+  pl.qw = 512 / G < kBlock ? 512 / G : kBlock;
+  pl.nsub = (int)ceil_div(kBlock, pl.qw);
+  int64_t qb = ceil_div(max_q_len, kBlock) + 1;
+  if (qb > pl.nb_max) qb = pl.nb_max;
+  pl.max_qblocks = (int)qb;
+  const int64_t c_max = pl.nb_max - 1;  // most earlier blocks any query scans
+  if (c_max <= 0) {
+    pl.chunk = 1;
+    pl.max_chunks = 1;
+    pl.scan_wgs = 0;
+  } else {
+    // Work estimate: query blocks c_max-qb+1 .. c_max, each scanning c blocks.
+    const int64_t c_first = c_max - qb + 1 > 0 ? c_max - qb + 1 : 0;
+    const int64_t work = (int64_t)batch * pl.nsub * (c_first + c_max) * (c_max - c_first + 1) / 2;
+    int64_t chunk = ceil_div(work, kScanTargetWgs);
+    const int64_t min_chunk = ceil_div(c_max, 64);  // merge wave holds <= 64 lists
+    if (chunk < min_chunk) chunk = min_chunk;
+    if (chunk < 1) chunk = 1;
+    pl.chunk = (int)chunk;
+    pl.max_chunks = (int)ceil_div(c_max, chunk);
+    pl.scan_wgs = (int64_t)batch * pl.max_qblocks * pl.nsub * pl.max_chunks;
+  }
+  const size_t nc = (size_t)pl.rows_bound * G * pl.max_chunks * kList;
+  pl.cand_score_bytes = align_up(nc * sizeof(float));
+  pl.cand_idx_bytes = align_up(nc * sizeof(int32_t));
+  pl.workspace_bytes = pl.scan_wgs > 0 ? pl.cand_score_bytes + pl.cand_idx_bytes : 0;
+  return pl;
+}
+
+AttnPlan plan_attn(int64_t rows, int Hq, int G, int D, int topk, int num_splits) {
+  AttnPlan pl;
+  pl.rows_bound = rows;
+  int ns = num_splits;
+  if (ns <= 0) {
+    const int64_t items = rows * G;
+    ns = (int)ceil_div(kAttnTargetWaves, items > 0 ? items : 1);
+  }
+  if (ns < 1) ns = 1;
+  if (ns > topk) ns = topk;
+  pl.bps = (int)ceil_div(topk, ns);
+  pl.nsplit = (int)ceil_div(topk, pl.bps);
+  if (pl.nsplit > 1) {
+    pl.part_o_bytes = align_up((size_t)rows * Hq * pl.nsplit * D * sizeof(float));
+    pl.part_lse_bytes = align_up((size_t)rows * Hq * pl.nsplit * sizeof(float));
+  }
+  pl.workspace_bytes = pl.part_o_bytes + pl.part_lse_bytes;
+  return pl;
+}
+
+}  // namespace msa
+
+using namespace msa;
+
+static thread_local int g_last_hip_error = 0;
+
+static msa_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return MSA_OK;
+  g_last_hip_error = (int)e;
+  return MSA_ERR_HIP;
+}
+
+static bool dtype_ok(msa_dtype_t d) { return d == MSA_F32 || d == MSA_BF16; }
+
+extern "C" {
+
+const char* msa_status_string(msa_status_t status) {
+  switch (status) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";
+    case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP";
+  }
+  return "MSA_ERR_UNKNOWN";
+}
+
+int msa_last_hip_error(void) { return g_last_hip_error; }
+
+size_t msa_index_topk_workspace_size(int batch, int max_q_len, int max_kv_len, int num_groups,
+                                     int block_size, int topk) {
+  if (batch <= 0 || max_q_len <= 0 || max_kv_len <= 0 || num_groups <= 0 || block_size != kBlock ||
+      topk <= 0)
+    return 0;
+  return plan_index(batch, max_q_len, max_kv_len, num_groups).workspace_bytes;
+}
+
+msa_status_t msa_index_topk(const void* q_idx, const void* k_idx, msa_dtype_t dtype,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                            int max_q_len, int max_kv_len, int num_groups, int index_dim,
+                            int block_size, int topk, int32_t* block_idx, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (!q_idx || !k_idx || !cu_seqlens_q || !cu_seqlens_k || !block_idx) return MSA_ERR_INVALID_ARG;
+  if (batch <= 0 || max_q_len <= 0 || max_kv_len <= 0 || num_groups <= 0 || index_dim <= 0 ||
+      block_size <= 0 || topk <= 0 || !dtype_ok(dtype))
+    return MSA_ERR_INVALID_ARG;
+  if (block_size != kBlock || (index_dim != 64 && index_dim != 128) || topk > 16 || num_groups > 16)
+    return MSA_ERR_UNSUPPORTED;
+  const IndexPlan pl = plan_index(batch, max_q_len, max_kv_len, num_groups);
+  if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes)) return MSA_ERR_WORKSPACE;
+  return hip_status(launch_index_topk(pl, (int)dtype, index_dim, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k,
+                                      batch, num_groups, topk, block_idx, workspace, stream));
+}
+
+size_t msa_sparse_attn_workspace_size(int batch, int max_q_len, int num_heads, int num_kv_heads,
+                                      int head_dim, int topk, int num_splits) {
+  if (batch <= 0 || max_q_len <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || topk <= 0)
+    return 0;
+  return plan_attn((int64_t)batch * max_q_len, num_heads, num_kv_heads, head_dim, topk, num_splits)
+      .workspace_bytes;
+}
+
+static msa_status_t check_attn(const void* q, const void* k, const void* v, msa_dtype_t dtype,
+                               const int32_t* block_idx, const void* out, int batch, int num_heads,
+                               int num_kv_heads, int head_dim, int block_size, int topk, int num_splits) {
+  if (!q || !k || !v || !block_idx || !out) return MSA_ERR_INVALID_ARG;
+  if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || topk <= 0 ||
+      num_splits < 0 || !dtype_ok(dtype))
+    return MSA_ERR_INVALID_ARG;
+  if (num_heads % num_kv_heads != 0) return MSA_ERR_INVALID_ARG;
+  if (block_size != kBlock || head_dim != kHeadDim || topk > 16 || num_heads / num_kv_heads > 16 ||
+      num_kv_heads > 16)
+    return MSA_ERR_UNSUPPORTED;
+  return MSA_OK;
+}
+
+static float resolve_scale(float s, int head_dim) {
+  return s > 0.f ? s : 1.0f / sqrtf((float)head_dim);
+}
+
+msa_status_t msa_sparse_attn_prefill(const void* q, const void* k, const void* v, msa_dtype_t dtype,
+                                     const int32_t* block_idx, const int32_t* cu_seqlens_q,
+                                     const int32_t* cu_seqlens_k, int batch, int max_q_len,
+                                     int max_kv_len, int num_heads, int num_kv_heads, int head_dim,
+                                     int block_size, int topk, float softmax_scale, int num_splits,
+                                     void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  msa_status_t st = check_attn(q, k, v, dtype, block_idx, out, batch, num_heads, num_kv_heads, head_dim,
+                               block_size, topk, num_splits);
+  if (st != MSA_OK) return st;
+  if (!cu_seqlens_q || !cu_seqlens_k || max_q_len <= 0 || max_kv_len <= 0) return MSA_ERR_INVALID_ARG;
+  const AttnPlan pl = plan_attn((int64_t)batch * max_q_len, num_heads, num_kv_heads, head_dim, topk, num_splits);
+  if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes)) return MSA_ERR_WORKSPACE;
+  AttnArgs a{q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, nullptr, nullptr, batch, num_heads, num_kv_heads,
+             topk, resolve_scale(softmax_scale, head_dim), out, lse};
+  return hip_status(launch_sparse_attn(pl, (int)dtype, a, workspace, stream));
+}
+
+msa_status_t msa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                    msa_dtype_t dtype, const int32_t* block_idx,
+                                    const int64_t* cache_offsets, const int32_t* ctx_lens,
+                                    int batch, int max_ctx, int num_heads, int num_kv_heads,
+                                    int head_dim, int block_size, int topk, float softmax_scale,
+                                    int num_splits, void* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  msa_status_t st = check_attn(q, k_cache, v_cache, dtype, block_idx, out, batch, num_heads, num_kv_heads,
+                               head_dim, block_size, topk, num_splits);
+  if (st != MSA_OK) return st;
+  if (!cache_offsets || !ctx_lens || max_ctx <= 0) return MSA_ERR_INVALID_ARG;
+  const AttnPlan pl = plan_attn(batch, num_heads, num_kv_heads, head_dim, topk, num_splits);
+  if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes)) return MSA_ERR_WORKSPACE;
+  AttnArgs a{q, k_cache, v_cache, block_idx, nullptr, nullptr, cache_offsets, ctx_lens, batch, num_heads,
+             num_kv_heads, topk, resolve_scale(softmax_scale, head_dim), out, lse};
+  return hip_status(launch_sparse_attn(pl, (int)dtype, a, workspace, stream));
+}
+
+}  // extern "C"

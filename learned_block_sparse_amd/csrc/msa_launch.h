@@ -1,0 +1,67 @@
+// msa_launch.h -- host-side work plans and kernel launchers (internal).
+//
+// A plan is a pure function of the host-visible sizes, so the workspace size
+// query and the launch always agree.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+struct IndexPlan {
+  bool decode = false;
+  int nb_max = 0;            // ceil(max_kv_len / 128)
+  int64_t rows_bound = 0;    // batch * max_q_len
+  // prefill scan
+  int qw = 0;                // queries per workgroup slice (columns = qw * G <= 512)
+  int nsub = 0;              // slices per query block
+  int max_qblocks = 0;       // query blocks per sequence (upper bound)
+  int chunk = 1;             // key blocks per scan workgroup
+  int max_chunks = 1;        // key chunks per query block (<= 64)
+  int64_t scan_wgs = 0;
+  size_t cand_score_bytes = 0;
+  size_t cand_idx_bytes = 0;
+  // decode scan
+  int dec_blocks_per_wave = 0;
+  int dec_wgs_per_seq = 0;
+  size_t score_bytes = 0;
+  size_t workspace_bytes = 0;
+};
+
+struct AttnPlan {
+  int nsplit = 1;            // chunks per selection
+  int bps = 16;              // selected blocks per chunk
+  int64_t rows_bound = 0;    // query rows (upper bound)
+  size_t part_o_bytes = 0;   // [rows, Hq, nsplit, D] fp32
+  size_t part_lse_bytes = 0; // [rows, Hq, nsplit] fp32
+  size_t workspace_bytes = 0;
+};
+
+IndexPlan plan_index(int batch, int max_q_len, int max_kv_len, int G);
+AttnPlan plan_attn(int64_t rows, int Hq, int G, int D, int topk, int num_splits);
+
+hipError_t launch_index_topk(const IndexPlan& pl, int dtype, int DI, const void* q_idx, const void* k_idx,
+                             const int32_t* cu_q, const int32_t* cu_k, int batch, int G, int topk,
+                             int32_t* block_idx, void* ws, hipStream_t st);
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_idx;
+  const int32_t* cu_q;        // prefill: query row offsets; null for decode (row b = sequence b)
+  const int32_t* cu_k;        // prefill: key row offsets; null for decode
+  const int64_t* k_offsets;   // decode: first cache row per sequence
+  const int32_t* k_lens;      // decode: context length per sequence
+  int batch;
+  int Hq, Hkv, topk;
+  float scale;
+  void* out;
+  float* lse;
+};
+
+hipError_t launch_sparse_attn(const AttnPlan& pl, int dtype, const AttnArgs& a, void* ws, hipStream_t st);
+
+}  // namespace msa

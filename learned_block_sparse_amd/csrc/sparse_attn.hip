@@ -1,0 +1,324 @@
+// sparse_attn.hip -- MSA main branch on gfx950: exact attention over the
+// selected key blocks, plus the log-sum-exp combine of split selections.
+//
+// Method: "MiniMax Sparse Attention: let each query pick its own blocks",
+// section "The mechanism, precisely" (main branch: exact attention over only
+// the selected blocks; every head of a group reuses the group's block set)
+// and the atlas record of MiniMax M3, summary and kernel list (standard
+// scaled dot-product softmax; a two-phase combine over per-partial LSE
+// buffers with no atomics; LSE produced by the forward pass).
+//
+// One wave owns one work item (query row, group, split) and all r <= 16 heads
+// of that group: the heads are the 16 columns of a 16x16 MFMA tile, so every
+// K/V element the wave gathers serves all heads of the group.  Scores are
+// computed transposed, S^T = K Q^T (keys x heads): a lane's 4 output registers
+// are 4 keys of one head, which makes the softmax row statistics a register
+// reduction plus two lane swaps, and the P^T fragment of the following
+// O^T += V^T P^T MFMA is exactly the registers the lane already holds.  V^T is
+// staged through a wave-private LDS tile, written transposed (keys
+// contiguous) so each MFMA operand is two 8-byte LDS reads.  Online softmax
+// (FlashAttention-style running max / sum) works in log2 units with exp2.
+// Waves never synchronise with each other.
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+constexpr int kAttnThreads = 256;  // 4 independent waves
+
+template <typename T>
+struct VtTile {
+  static constexpr int kStride = 32 + 4;  // 32 keys per d-row plus padding (elements)
+  static constexpr int kElems = kHeadDim * kStride;
+};
+
+struct AttnKernelArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_idx;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int64_t* k_offsets;
+  const int32_t* k_lens;
+  int batch;
+  int64_t rows_bound;
+  int Hq, Hkv, topk, nsplit, bps;
+  float scale_log2;  // softmax scale * log2(e)
+  void* out;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+};
+
+__device__ __forceinline__ int find_row_seq(const int32_t* cu, int batch, int64_t row) {
+  int lo = 0, hi = batch;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= row) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c, float d) {
+  bf16x4 v = {bf16(a), bf16(b), bf16(c), bf16(d)};
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  f32x4 v = {a, b, c, d};
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs args) {
+  using V = VtTile<T>;
+  __shared__ __attribute__((aligned(16))) T vt_all[kAttnThreads / kWave][V::kElems];
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  T* vt = vt_all[wave];
+
+  const int G = args.Hkv;
+  const int64_t item = (int64_t)blockIdx.x * (kAttnThreads / kWave) + wave;
+  if (item >= args.rows_bound * G * args.nsplit) return;
+  const int s = (int)(item % args.nsplit);
+  const int64_t rest = item / args.nsplit;
+  const int64_t t = rest % args.rows_bound;
+  const int g = (int)(rest / args.rows_bound);
+
+  int64_t q0, kb0;
+  int M, N;
+  if (args.cu_q) {
+    if (t >= args.cu_q[args.batch]) return;
+    const int b = find_row_seq(args.cu_q, args.batch, t);
+    q0 = args.cu_q[b];
+    M = args.cu_q[b + 1] - args.cu_q[b];
+    kb0 = args.cu_k[b];
+    N = args.cu_k[b + 1] - args.cu_k[b];
+  } else {
+    if (t >= args.batch) return;
+    q0 = t;
+    M = 1;
+    kb0 = args.k_offsets[t];
+    N = args.k_lens[t];
+  }
+  const int64_t p = (int64_t)N - M + (t - q0);
+
+  const T* __restrict__ qg = static_cast<const T*>(args.q);
+  const T* __restrict__ kg = static_cast<const T*>(args.k);
+  const T* __restrict__ vg = static_cast<const T*>(args.v);
+  const int R = args.Hq / G;
+  const int h = lane & 15;     // head column of the MFMA tile
+  const int a = lane >> 4;     // lane group: contraction slots 8a..8a+7
+  const int hq = g * R + h;
+  const bool head_ok = h < R;
+
+  // B operand of S^T = K Q^T: Q^T[d][h], slots d = 32*ds + 8a .. +7.
+  frag8<T> qf[kHeadDim / 32];
+#pragma unroll
+  for (int ds = 0; ds < kHeadDim / 32; ++ds)
+    qf[ds] = head_ok ? load8(qg + (t * args.Hq + (head_ok ? hq : g * R)) * kHeadDim + 32 * ds + 8 * a)
+                     : zero8<T>();
+
+  f32x4 o[kHeadDim / 16];
+#pragma unroll
+  for (int dt = 0; dt < kHeadDim / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+
+  if (p >= 0) {
+    const int64_t local = p / kBlock;
+    const int32_t* sel = args.block_idx + (t * G + g) * args.topk;
+    const int i_lo = s * args.bps;
+    const int i_hi = min(i_lo + args.bps, args.topk);
+    const int64_t row_stride = (int64_t)G * kHeadDim;   // elements between tokens
+    const T* kseq = kg + kb0 * row_stride + g * kHeadDim;
+    const T* vseq = vg + kb0 * row_stride + g * kHeadDim;
+
+    for (int i = i_lo; i < i_hi; ++i) {
+      const int c = sel[i];
+      if (c < 0 || c > local) continue;
+      const int64_t key0 = (int64_t)c * kBlock;
+      const bool causal = (c == local);
+
+      // ---- S^T[key][head] for the 128 keys of the block (8 tiles of 16 keys)
+      f32x4 st[kBlock / 16];
+#pragma unroll
+      for (int kt = 0; kt < kBlock / 16; ++kt) {
+        int64_t key = key0 + 16 * kt + h;   // A operand row = lane % 16
+        if (key > p) key = p;               // stay inside the sequence; masked below
+        const T* kp = kseq + key * row_stride + 8 * a;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < kHeadDim / 32; ++ds) acc = mma16(load8(kp + 32 * ds), qf[ds], acc);
+        st[kt] = acc;
+      }
+
+      // ---- online softmax (log2 units)
+      float mb = -__builtin_inff();
+#pragma unroll
+      for (int kt = 0; kt < kBlock / 16; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = st[kt][r] * args.scale_log2;
+          if (causal && key0 + 16 * kt + 4 * a + r > p) x = -__builtin_inff();
+          st[kt][r] = x;
+          mb = fmaxf(mb, x);
+        }
+      mb = fmaxf(mb, shfl_xor_f(mb, 16));
+      mb = fmaxf(mb, shfl_xor_f(mb, 32));
+      const float m_new = fmaxf(m_run, mb);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < kHeadDim / 16; ++dt) o[dt] *= alpha;
+#pragma unroll
+      for (int kt = 0; kt < kBlock / 16; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(st[kt][r] - m_new);
+          st[kt][r] = e;
+          l_run += e;
+        }
+
+      // ---- O^T[d][head] += V^T[d][key] P^T[key][head], 32 keys at a time
+#pragma unroll
+      for (int ks = 0; ks < kBlock / 32; ++ks) {
+        // Stage V rows key0+32ks .. +31 transposed: vt[d][key], keys contiguous.
+        // Unit u = (key quad u%8, d octet u/8); lane handles u = lane, lane+64.
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+          const int u = lane + 64 * uu;
+          const int kq = u & 7, o8 = u >> 3;
+          frag8<T> r4[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            int64_t key = key0 + 32 * ks + 4 * kq + jj;
+            if (key > p) key = p;
+            r4[jj] = load8(vseq + key * row_stride + 8 * o8);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            T* dst = vt + (8 * o8 + e) * V::kStride + 4 * kq;
+            if constexpr (sizeof(T) == 2) {
+              bf16x4 w = {r4[0][e], r4[1][e], r4[2][e], r4[3][e]};
+              *reinterpret_cast<bf16x4*>(dst) = w;
+            } else {
+              f32x4 w = {r4[0][e], r4[1][e], r4[2][e], r4[3][e]};
+              *reinterpret_cast<f32x4*>(dst) = w;
+            }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+
+        // B operand P^T: slots i<4 -> key 32ks+4a+i (tile 2ks), i>=4 -> 32ks+16+4a+i-4.
+        frag8<T> pb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pb[r] = T(st[2 * ks][r]);
+          pb[4 + r] = T(st[2 * ks + 1][r]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < kHeadDim / 16; ++dt) {
+          const T* src = vt + (16 * dt + h) * V::kStride + 4 * a;
+          frag8<T> va;
+          if constexpr (sizeof(T) == 2) {
+            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src);
+            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src + 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) { va[r] = lo[r]; va[4 + r] = hi[r]; }
+          } else {
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) { va[r] = lo[r]; va[4 + r] = hi[r]; }
+          }
+          o[dt] = mma16(va, pb, o[dt]);
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+  }
+
+  // ---- finalize: l is lane-partial over the 4 lane groups of a head
+  float l_tot = l_run + shfl_xor_f(l_run, 16);
+  l_tot += shfl_xor_f(l_tot, 32);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  const float lse_val = l_tot > 0.f ? m_run * 0.69314718055994530942f + logf(l_tot) : -__builtin_inff();
+  if (!head_ok) return;
+  const int64_t rh = t * args.Hq + hq;
+  if (args.nsplit == 1) {
+    T* out = static_cast<T*>(args.out) + rh * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < kHeadDim / 16; ++dt)
+      store4<T>(out + 16 * dt + 4 * a, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+    if (args.lse && a == 0) args.lse[rh] = lse_val;
+  } else {
+    float* po = args.part_o + (rh * args.nsplit + s) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < kHeadDim / 16; ++dt)
+      store4<float>(po + 16 * dt + 4 * a, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+    if (a == 0) args.part_lse[rh * args.nsplit + s] = lse_val;
+  }
+}
+
+// Two-phase combine: lse = ln sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s,
+// summed in split order (deterministic, no atomics).  One thread per (row, head, d).
+template <typename T>
+__global__ __launch_bounds__(256) void attn_combine(const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_lse,
+                                                    const int32_t* __restrict__ cu_q, int batch,
+                                                    int64_t rows_bound, int Hq, int nsplit, T* __restrict__ out,
+                                                    float* __restrict__ lse) {
+  const int64_t rh = (int64_t)blockIdx.x * 2 + threadIdx.x / kHeadDim;
+  const int d = threadIdx.x % kHeadDim;
+  if (rh >= rows_bound * Hq) return;
+  const int64_t t = rh / Hq;
+  const int64_t nrows = cu_q ? cu_q[batch] : batch;
+  if (t >= nrows) return;
+  const float* pl = part_lse + rh * nsplit;
+  float mx = -__builtin_inff();
+  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, pl[s]);
+  float res = 0.f, L = -__builtin_inff();
+  if (mx != -__builtin_inff()) {
+    float sum = 0.f;
+    for (int s = 0; s < nsplit; ++s) sum += expf(pl[s] - mx);
+    L = mx + logf(sum);
+    for (int s = 0; s < nsplit; ++s) res += expf(pl[s] - L) * part_o[(rh * nsplit + s) * kHeadDim + d];
+  }
+  out[rh * kHeadDim + d] = T(res);
+  if (lse && d == 0) lse[rh] = L;
+}
+
+template <typename T>
+static hipError_t launch_attn_t(const AttnPlan& pl, const AttnArgs& a, void* ws, hipStream_t st) {
+  AttnKernelArgs k;
+  k.q = a.q; k.k = a.k; k.v = a.v; k.block_idx = a.block_idx;
+  k.cu_q = a.cu_q; k.cu_k = a.cu_k; k.k_offsets = a.k_offsets; k.k_lens = a.k_lens;
+  k.batch = a.batch; k.rows_bound = pl.rows_bound;
+  k.Hq = a.Hq; k.Hkv = a.Hkv; k.topk = a.topk; k.nsplit = pl.nsplit; k.bps = pl.bps;
+  k.scale_log2 = a.scale * 1.4426950408889634f;
+  k.out = a.out; k.lse = a.lse;
+  char* w = static_cast<char*>(ws);
+  k.part_o = pl.nsplit > 1 ? reinterpret_cast<float*>(w) : nullptr;
+  k.part_lse = pl.nsplit > 1 ? reinterpret_cast<float*>(w + pl.part_o_bytes) : nullptr;
+  const int64_t items = pl.rows_bound * a.Hkv * pl.nsplit;
+  const int64_t wgs = (items + 3) / 4;
+  hipLaunchKernelGGL(sparse_attn_fwd<T>, dim3((unsigned)wgs), dim3(kAttnThreads), 0, st, k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.nsplit == 1) return e;
+  const int64_t rh = pl.rows_bound * a.Hq;
+  hipLaunchKernelGGL(attn_combine<T>, dim3((unsigned)((rh + 1) / 2)), dim3(256), 0, st, k.part_o, k.part_lse,
+                     a.cu_q, a.batch, pl.rows_bound, a.Hq, pl.nsplit, static_cast<T*>(a.out), a.lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn(const AttnPlan& pl, int dtype, const AttnArgs& a, void* ws, hipStream_t st) {
+  return dtype == 0 ? launch_attn_t<float>(pl, a, ws, st) : launch_attn_t<bf16>(pl, a, ws, st);
+}
+
+}  // namespace msa

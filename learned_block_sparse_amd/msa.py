@@ -1,0 +1,187 @@
+"""Thin Python binding of the C ABI in ``include/msa.h`` (``libmsa.so``).
+
+Argument marshalling only: every step of the MSA hot path runs in the HIP
+kernels of the library.  PyTorch provides device memory (tensors, and the
+workspace when the caller passes none) and the current stream.  There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+
+The functions carry the C names.  Tensor layouts are those of the header:
+
+* ``q_idx [Tq, G, d_idx]``, ``k_idx [Tk, d_idx]``
+* ``q [Tq, Hq, D]``, ``k, v [Tk, Hkv, D]``
+* ``block_idx [Tq, G, topk]`` int32, ``cu_seqlens_q/k [B + 1]`` int32
+* decode: ``q [B, Hq, D]``, ``cache_offsets [B]`` int64, ``ctx_lens [B]`` int32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmsa.so")
+
+MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = range(5)
+MSA_F32, MSA_BF16 = 0, 1
+
+_lib = None
+
+
+class MSAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        name = lib().msa_status_string(status).decode()
+        extra = ""
+        if status == MSA_ERR_HIP:
+            extra = f" (hipError {lib().msa_last_hip_error()})"
+        super().__init__(f"{where}: {name}{extra}")
+        self.status = status
+
+
+def lib():
+    """The loaded ``libmsa.so`` (ctypes); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m learned_block_sparse_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.msa_status_string.restype = ctypes.c_char_p
+        L.msa_status_string.argtypes = [i32]
+        L.msa_last_hip_error.restype = i32
+        L.msa_last_hip_error.argtypes = []
+        L.msa_index_topk_workspace_size.restype = sz
+        L.msa_index_topk_workspace_size.argtypes = [i32] * 6
+        L.msa_index_topk.restype = i32
+        L.msa_index_topk.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, sz, vp]
+        L.msa_sparse_attn_workspace_size.restype = sz
+        L.msa_sparse_attn_workspace_size.argtypes = [i32] * 7
+        L.msa_sparse_attn_prefill.restype = i32
+        L.msa_sparse_attn_prefill.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                              i32, ctypes.c_float, i32, vp, vp, vp, sz, vp]
+        L.msa_sparse_attn_decode.restype = i32
+        L.msa_sparse_attn_decode.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                             ctypes.c_float, i32, vp, vp, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MSA_F32
+    if t.dtype == torch.bfloat16:
+        return MSA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int, where: str):
+    if status != MSA_OK:
+        raise MSAError(status, where)
+
+
+def _workspace(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace smaller than the {nbytes} bytes required")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def msa_index_topk_workspace_size(batch, max_q_len, max_kv_len, num_groups, block_size, topk) -> int:
+    return lib().msa_index_topk_workspace_size(batch, max_q_len, max_kv_len, num_groups, block_size, topk)
+
+
+def msa_sparse_attn_workspace_size(batch, max_q_len, num_heads, num_kv_heads, head_dim, topk,
+                                   num_splits=0) -> int:
+    return lib().msa_sparse_attn_workspace_size(batch, max_q_len, num_heads, num_kv_heads, head_dim,
+                                                topk, num_splits)
+
+
+def msa_index_topk(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, max_q_len: int, max_kv_len: int,
+                   block_size: int = 128, topk: int = 16, block_idx=None, workspace=None, stream=None):
+    """Selected block ids ``[Tq, G, topk]`` (int32, ascending, -1 padded)."""
+    if q_idx.dim() != 3 or k_idx.dim() != 2 or q_idx.shape[2] != k_idx.shape[1]:
+        raise ValueError("q_idx must be [Tq, G, d_idx] and k_idx [Tk, d_idx]")
+    if q_idx.dtype != k_idx.dtype:
+        raise TypeError("q_idx and k_idx must share a dtype")
+    tq, G, di = q_idx.shape
+    batch = cu_seqlens_q.numel() - 1
+    if block_idx is None:
+        block_idx = torch.empty((tq, G, topk), dtype=torch.int32, device=q_idx.device)
+    need = msa_index_topk_workspace_size(batch, max_q_len, max_kv_len, G, block_size, topk)
+    ws, ws_bytes = _workspace(need, q_idx.device, workspace)
+    st = lib().msa_index_topk(_dev(q_idx, "q_idx"), _dev(k_idx, "k_idx"), _dtype_code(q_idx),
+                              _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+                              _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32), batch, max_q_len, max_kv_len,
+                              G, di, block_size, topk, _dev(block_idx, "block_idx", torch.int32),
+                              ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
+    _check(st, "msa_index_topk")
+    return block_idx
+
+
+def msa_sparse_attn_prefill(q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_q_len: int,
+                            max_kv_len: int, block_size: int = 128, topk: int = 16,
+                            softmax_scale: float = 0.0, num_splits: int = 0, out=None, lse=None,
+                            return_lse: bool = True, workspace=None, stream=None):
+    """``(out [Tq, Hq, D], lse [Tq, Hq] fp32 or None)``."""
+    tq, hq, d = q.shape
+    hkv = k.shape[1]
+    batch = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
+    need = msa_sparse_attn_workspace_size(batch, max_q_len, hq, hkv, d, topk, num_splits)
+    ws, ws_bytes = _workspace(need, q.device, workspace)
+    st = lib().msa_sparse_attn_prefill(
+        _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dtype_code(q),
+        _dev(block_idx, "block_idx", torch.int32), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32), batch, max_q_len, max_kv_len, hq, hkv, d,
+        block_size, topk, float(softmax_scale), num_splits, _dev(out, "out", q.dtype),
+        _dev(lse, "lse", torch.float32) if lse is not None else None,
+        ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
+    _check(st, "msa_sparse_attn_prefill")
+    return out, lse
+
+
+def msa_sparse_attn_decode(q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx: int,
+                           block_size: int = 128, topk: int = 16, softmax_scale: float = 0.0,
+                           num_splits: int = 0, out=None, lse=None, return_lse: bool = True,
+                           workspace=None, stream=None):
+    """``(out [B, Hq, D], lse [B, Hq] fp32 or None)`` for one decode step."""
+    batch, hq, d = q.shape
+    hkv = k_cache.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
+    need = msa_sparse_attn_workspace_size(batch, 1, hq, hkv, d, topk, num_splits)
+    ws, ws_bytes = _workspace(need, q.device, workspace)
+    st = lib().msa_sparse_attn_decode(
+        _dev(q, "q"), _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype), _dtype_code(q),
+        _dev(block_idx, "block_idx", torch.int32), _dev(cache_offsets, "cache_offsets", torch.int64),
+        _dev(ctx_lens, "ctx_lens", torch.int32), batch, max_ctx, hq, hkv, d, block_size, topk,
+        float(softmax_scale), num_splits, _dev(out, "out", q.dtype),
+        _dev(lse, "lse", torch.float32) if lse is not None else None,
+        ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
+    _check(st, "msa_sparse_attn_decode")
+    return out, lse

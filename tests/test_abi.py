@@ -1,0 +1,125 @@
+"""The C ABI library: it loads, exports what include/msa.h declares, and rejects
+bad arguments before launching anything (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from learned_block_sparse_amd import msa
+    if not os.path.exists(msa.LIB_PATH):
+        from learned_block_sparse_amd import build
+        build.build()
+    return msa.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = _declared_functions()
+    for n in ("msa_index_topk", "msa_sparse_attn_prefill", "msa_sparse_attn_decode"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(L, n), f"libmsa.so does not export {n}"
+
+
+def test_no_torch_or_oracle_symbols_in_library():
+    """The product library links neither torch nor the oracle."""
+    from learned_block_sparse_amd import msa
+    data = open(msa.LIB_PATH, "rb").read()
+    assert b"oracle_index_topk" not in data and b"oracle_sparse_attn" not in data
+    assert b"libtorch" not in data and b"libc10" not in data
+
+
+def test_status_strings(L):
+    for code, name in enumerate(["MSA_OK", "MSA_ERR_INVALID_ARG", "MSA_ERR_UNSUPPORTED",
+                                 "MSA_ERR_WORKSPACE", "MSA_ERR_HIP"]):
+        assert L.msa_status_string(code).decode() == name
+    assert L.msa_status_string(99).decode() == "MSA_ERR_UNKNOWN"
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def _index(L, **kw):
+    a = dict(q=FAKE, k=FAKE, dtype=1, cuq=FAKE, cuk=FAKE, batch=1, mq=256, mk=256, G=4, DI=128,
+             bk=128, topk=16, out=FAKE, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return L.msa_index_topk(a["q"], a["k"], a["dtype"], a["cuq"], a["cuk"], a["batch"], a["mq"], a["mk"],
+                            a["G"], a["DI"], a["bk"], a["topk"], a["out"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_index_topk_argument_errors(L):
+    assert _index(L, q=None) == 1
+    assert _index(L, batch=0) == 1
+    assert _index(L, dtype=7) == 1
+    assert _index(L, topk=0) == 1
+    assert _index(L, bk=64) == 2
+    assert _index(L, DI=96) == 2
+    assert _index(L, topk=17) == 2
+    assert _index(L, G=17) == 2
+    # prefill with more than one block needs a workspace
+    assert L.msa_index_topk_workspace_size(1, 256, 256, 4, 128, 16) > 0
+    assert _index(L) == 3
+    assert _index(L, ws=FAKE, wsb=16) == 3
+
+
+def test_workspace_sizes(L):
+    # a single block per sequence needs no candidate buffer
+    assert L.msa_index_topk_workspace_size(1, 100, 100, 4, 128, 16) == 0
+    # decode: one fp32 score per (sequence, group, block)
+    assert L.msa_index_topk_workspace_size(3, 1, 1000, 4, 128, 16) >= 3 * 4 * 8 * 4
+    # unsupported block size reports 0
+    assert L.msa_index_topk_workspace_size(1, 256, 256, 4, 64, 16) == 0
+    # one split: no workspace; more splits: partial outputs
+    assert L.msa_sparse_attn_workspace_size(1, 8192, 64, 4, 128, 16, 1) == 0
+    ws = L.msa_sparse_attn_workspace_size(2, 1, 64, 4, 128, 16, 4)
+    assert ws >= 2 * 64 * 4 * (128 + 1) * 4
+
+
+def _prefill(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, bi=FAKE, cuq=FAKE, cuk=FAKE, batch=1, mq=256, mk=256,
+             Hq=64, Hkv=4, D=128, bk=128, topk=16, scale=0.0, ns=0, out=FAKE, lse=None, ws=None,
+             wsb=0, stream=None)
+    a.update(kw)
+    return L.msa_sparse_attn_prefill(a["q"], a["k"], a["v"], a["dtype"], a["bi"], a["cuq"], a["cuk"],
+                                     a["batch"], a["mq"], a["mk"], a["Hq"], a["Hkv"], a["D"], a["bk"],
+                                     a["topk"], a["scale"], a["ns"], a["out"], a["lse"], a["ws"],
+                                     a["wsb"], a["stream"])
+
+
+def test_prefill_argument_errors(L):
+    assert _prefill(L, out=None) == 1
+    assert _prefill(L, Hq=63) == 1           # not a multiple of Hkv
+    assert _prefill(L, ns=-1) == 1
+    assert _prefill(L, D=64) == 2
+    assert _prefill(L, Hq=68, Hkv=4) == 2    # 17 heads per group
+    assert _prefill(L, bk=256) == 2
+    assert _prefill(L, ns=4) == 3            # split partials need a workspace
+
+
+def test_decode_argument_errors(L):
+    args = [FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 32, 1 << 20, 64, 4, 128, 128, 16, 0.0, 0, FAKE,
+            None, None, 0, None]
+    assert L.msa_sparse_attn_decode(*args) == 3      # automatic splits need a workspace
+    bad = list(args)
+    bad[5] = None                                    # cache_offsets
+    assert L.msa_sparse_attn_decode(*bad) == 1
+    bad = list(args)
+    bad[11] = 96                                     # head_dim
+    assert L.msa_sparse_attn_decode(*bad) == 2
