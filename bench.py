@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of the MSA hot path on one MI355X.
+
+A step is one pass of the whole prefill hot path over a synthetic 128K-token
+sequence (batch 1, 64 Q / 4 KV heads, head dim 128, index dim 128, block 128,
+k 16, 32 planted blocks), run as 16 calls of 8192 queries against the growing
+causal prefix: per call, index scoring + block max-pool + top-k
+(msa_index_topk) and block-sparse attention (msa_sparse_attn_prefill).  The
+headline value is prefill tokens/s.  The same JSON line also carries one
+decode step (32 sequences, contexts uniform in [64K, 1M]: msa_index_topk on
+the decode path + msa_sparse_attn_decode) in microseconds per step.
+
+Inputs are resident in HBM before the timed region starts.  Kernel durations
+come from HIP events recorded on the stream the calls are launched on
+(torch's current stream, passed to the library).
+
+Roofline: algorithmic FLOPs (index: 2 * d_idx * G * Bk * l(p) per query;
+attention: 4 * D * Hq * |J| per query) per call divided by the call's mean
+duration, against MI355X's dense bf16 MFMA peak (2.5 PFLOP/s); decode against
+HBM (8 TB/s) with the index-key scan plus selected K/V bytes.
+
+cpu_baseline: the CPU oracle (unchanged, as the tests use it) on a stratified
+sample of query rows of the same 128K workload, on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MSA prefill tokens/s @128K + decode µs/step @1M ctx, % of roofline (1 GPU)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    return ap.parse_args()
+
+
+def traffic_record(kernel_key):
+    """HBM bytes per launch measured with rocprofv3 counters, if the kernel
+    source is unchanged since they were taken (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    from learned_block_sparse_amd import build
+    if rec.get("source_sha") != build.source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the MSA path here is a "
+              "single-GPU library and no multi-GPU figure is produced", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from learned_block_sparse_amd import msa, synth, workmodel
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    msa.lib()
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------------ prefill
+    wl = synth.WORKLOADS["prefill_128k"]
+    L, T = wl.seq_len, wl.q_tile
+    inp = synth.prefill_inputs(wl, device=dev, seed=0)
+    G, DI, Hq, D = wl.num_kv_heads, wl.index_dim, wl.num_heads, wl.head_dim
+    tiles = [(lo, min(lo + T, L)) for lo in range(0, L, T)]
+    calls = []
+    for lo, hi in tiles:
+        m = hi - lo
+        cu_q = torch.tensor([0, m], dtype=torch.int32, device=dev)
+        cu_k = torch.tensor([0, hi], dtype=torch.int32, device=dev)
+        ws_i = torch.empty(max(1, msa.msa_index_topk_workspace_size(1, m, hi, G, wl.block_size, wl.topk)),
+                           dtype=torch.uint8, device=dev)
+        ws_a = torch.empty(max(1, msa.msa_sparse_attn_workspace_size(1, m, Hq, G, D, wl.topk, 0)),
+                           dtype=torch.uint8, device=dev)
+        ids = torch.empty((m, G, wl.topk), dtype=torch.int32, device=dev)
+        out = torch.empty((m, Hq, D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((m, Hq), dtype=torch.float32, device=dev)
+        calls.append(dict(lo=lo, hi=hi, m=m, cu_q=cu_q, cu_k=cu_k, ws_i=ws_i, ws_a=ws_a, ids=ids, out=out,
+                          lse=lse, q_idx=inp["q_idx"][lo:hi], q=inp["q"][lo:hi]))
+
+    def run_step(events=None):
+        for j, c in enumerate(calls):
+            if events is not None:
+                events[j][0].record(stream)
+            msa.msa_index_topk(c["q_idx"], inp["k_idx"], c["cu_q"], c["cu_k"], c["m"], c["hi"], wl.block_size,
+                               wl.topk, block_idx=c["ids"], workspace=c["ws_i"], stream=stream)
+            if events is not None:
+                events[j][1].record(stream)
+            msa.msa_sparse_attn_prefill(c["q"], inp["k"], inp["v"], c["ids"], c["cu_q"], c["cu_k"], c["m"], c["hi"],
+                                        wl.block_size, wl.topk, out=c["out"], lse=c["lse"], workspace=c["ws_a"],
+                                        stream=stream)
+            if events is not None:
+                events[j][2].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in calls] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run_step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    idx_ms = np.mean([sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for j in range(len(calls)))
+                      for s in range(args.steps)])
+    att_ms = np.mean([sum(ev[s][j][1].elapsed_time(ev[s][j][2]) for j in range(len(calls)))
+                      for s in range(args.steps)])
+    per_call_idx = [np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)])
+                    for j in range(len(calls))]
+    per_call_att = [np.mean([ev[s][j][1].elapsed_time(ev[s][j][2]) for s in range(args.steps)])
+                    for j in range(len(calls))]
+
+    idx_flops = att_flops = 0.0
+    for c in calls:
+        pos = np.arange(c["lo"], c["hi"])
+        idx_flops += workmodel.index_flops(pos, G, DI, wl.block_size)
+        att_flops += workmodel.attn_flops(pos, Hq, D, wl.block_size, wl.topk)
+    tokens_s = L / (ms_step / 1e3)
+    idx_tflops = idx_flops / (idx_ms / 1e3) / 1e12
+    att_tflops = att_flops / (att_ms / 1e3) / 1e12
+    tot_tflops = (idx_flops + att_flops) / (ms_step / 1e3) / 1e12
+
+    # planted-block share of the selections (workload skew), last tile
+    last = calls[-1]
+    planted = set(inp["planted"][0]) if inp["planted"] else set()
+    sel = last["ids"].cpu().numpy()
+    local = (np.arange(last["lo"], last["hi"]) // wl.block_size)[:, None, None]
+    nonlocal_sel = sel[(sel >= 0) & (sel != local)]
+    planted_share = float(np.isin(nonlocal_sel, list(planted)).mean()) if planted else 0.0
+
+    dominant = "index" if idx_ms >= att_ms else "attention"
+    if dominant == "index":
+        dom_ms = float(np.mean(per_call_idx))
+        dom_flops = idx_flops / len(calls)
+        kernel = "idx_scan_prefill<bf16,128> + idx_merge_prefill (one msa_index_topk call)"
+        traffic = traffic_record("idx_scan_prefill_128k")
+    else:
+        dom_ms = float(np.mean(per_call_att))
+        dom_flops = att_flops / len(calls)
+        kernel = "sparse_attn_fwd<bf16> (one msa_sparse_attn_prefill call)"
+        traffic = traffic_record("sparse_attn_fwd_128k")
+    achieved = dom_flops / (dom_ms / 1e3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": kernel, "launch_ms": round(dom_ms, 4),
+                "per_launch_flops": dom_flops}
+
+    result = {
+        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_128k", "batch": 1, "seq_len": L, "q_tile": T, "num_heads": Hq,
+                   "num_kv_heads": G, "head_dim": D, "index_dim": DI, "block_size": wl.block_size,
+                   "topk": wl.topk, "planted_blocks": wl.planted},
+        "roofline": roofline,
+        "prefill": {"index_ms": round(float(idx_ms), 3), "attention_ms": round(float(att_ms), 3),
+                    "index_tflops": round(idx_tflops, 1), "attention_tflops": round(att_tflops, 1),
+                    "total_tflops": round(tot_tflops, 1),
+                    "index_frac_mfma": round(idx_tflops / PEAK_BF16_TFLOPS, 4),
+                    "attention_frac_mfma": round(att_tflops / PEAK_BF16_TFLOPS, 4),
+                    "algorithmic_flops": idx_flops + att_flops,
+                    "planted_share_last_tile": round(planted_share, 3)},
+    }
+    del inp, calls
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------ decode
+    if not args.no_decode:
+        wd = synth.WORKLOADS["decode_1m"]
+        ctx = synth.decode_ctx_lens(wd, 0)
+        d = synth.decode_inputs(wd, device=dev, seed=0, ctx_lens=ctx)
+        B = len(ctx)
+        ws_i = torch.empty(max(1, msa.msa_index_topk_workspace_size(B, 1, max(ctx), G, wd.block_size, wd.topk)),
+                           dtype=torch.uint8, device=dev)
+        ws_a = torch.empty(max(1, msa.msa_sparse_attn_workspace_size(B, 1, Hq, G, D, wd.topk, 0)),
+                           dtype=torch.uint8, device=dev)
+        ids = torch.empty((B, G, wd.topk), dtype=torch.int32, device=dev)
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+
+        def dstep(e=None):
+            if e is not None:
+                e[0].record(stream)
+            msa.msa_index_topk(d["q_idx"], d["k_idx"], d["cu_seqlens_q"], d["cu_seqlens_k"], 1, max(ctx),
+                               wd.block_size, wd.topk, block_idx=ids, workspace=ws_i, stream=stream)
+            if e is not None:
+                e[1].record(stream)
+            msa.msa_sparse_attn_decode(d["q"], d["k"], d["v"], ids, d["k_offsets"], d["ctx_lens"], max(ctx),
+                                       wd.block_size, wd.topk, out=out, lse=lse, workspace=ws_a, stream=stream)
+            if e is not None:
+                e[2].record(stream)
+
+        for _ in range(5):
+            dstep()
+        torch.cuda.synchronize()
+        dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.decode_steps)]
+        t0 = time.perf_counter()
+        for s in range(args.decode_steps):
+            dstep(dev_ev[s])
+        torch.cuda.synchronize()
+        dwall = (time.perf_counter() - t0) / args.decode_steps
+        d_idx_us = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_ev])) * 1e3
+        d_att_us = float(np.mean([e[1].elapsed_time(e[2]) for e in dev_ev])) * 1e3
+        d_step_us = float(np.mean([e[0].elapsed_time(e[2]) for e in dev_ev])) * 1e3
+        idx_b, att_b = workmodel.decode_bytes(ctx, Hq, G, D, DI, wd.block_size, wd.topk)
+        gbs = (idx_b + att_b) / (d_step_us * 1e-6) / 1e9
+        idx_gbs = idx_b / (d_idx_us * 1e-6) / 1e9
+        result["decode"] = {
+            "workload": "decode_1m", "batch": B, "ctx_sum": int(sum(ctx)), "us_per_step": round(d_step_us, 1),
+            "wall_us_per_step": round(dwall * 1e6, 1), "index_us": round(d_idx_us, 1),
+            "attention_us": round(d_att_us, 1), "bytes_per_step": idx_b + att_b,
+            "achieved_GBs": round(gbs, 1), "peak_GBs": PEAK_HBM_GBS, "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+            "index_scan_GBs": round(idx_gbs, 1), "index_scan_frac_hbm": round(idx_gbs / PEAK_HBM_GBS, 4),
+            "index_scan_traffic": traffic_record("idx_decode_scores_1m"),
+        }
+        del d
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ CPU baseline
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(target_s: float):
+    """The oracle on a stratified sample of query rows of the 128K workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from learned_block_sparse_amd import synth
+
+    wl = synth.WORKLOADS["prefill_128k"]
+    inp = synth.prefill_inputs(wl, device="cpu", seed=0)
+    cores = os.cpu_count() or 1
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        pass
+    omp = os.environ.get("OMP_NUM_THREADS")
+    threads = int(omp) if omp and omp.isdigit() else cores
+
+    def run(n):
+        rows = np.linspace(0, wl.seq_len - 1, n).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.prefill(inp["q_idx"], inp["k_idx"], inp["q"], inp["k"], inp["v"], inp["cu_q_host"],
+                       inp["cu_k_host"], wl.block_size, wl.topk, rows=rows)
+        return time.perf_counter() - t0
+
+    n0 = max(8, threads)
+    t_cal = run(n0)
+    n = int(max(n0, min(8192, n0 * target_s / max(t_cal, 1e-3))))
+    t = run(n)
+    del inp
+    torch.set_num_threads(torch.get_num_threads())
+    return {"value": round(n / t, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} query rows evenly spaced over positions 0..131071 of the 128K prefill "
+                      f"(index scan + top-k + attention per row), {t:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

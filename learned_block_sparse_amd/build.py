@@ -53,5 +53,20 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+
+def source_digest() -> str:
+    """SHA-256 over the kernel sources and the ABI header (identifies which
+    build a set of hardware-counter measurements belongs to)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "msa.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 if __name__ == "__main__":
     build(verbose=True)
