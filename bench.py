@@ -96,15 +96,17 @@ def main():
     inp = synth.prefill_inputs(wl, device=dev, seed=0)
     G, DI, Hq, D = wl.num_kv_heads, wl.index_dim, wl.num_heads, wl.head_dim
     tiles = [(lo, min(lo + T, L)) for lo in range(0, L, T)]
+    # one workspace per kind, sized for the largest call (calls run in order on one stream)
+    ws_i_bytes = max(msa.msa_index_topk_workspace_size(1, hi - lo, hi, G, wl.block_size, wl.topk)
+                     for lo, hi in tiles)
+    ws_a_bytes = max(msa.msa_sparse_attn_workspace_size(1, hi - lo, hi, Hq, G, D, wl.topk, 0) for lo, hi in tiles)
+    ws_i = torch.empty(max(1, ws_i_bytes), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(1, ws_a_bytes), dtype=torch.uint8, device=dev)
     calls = []
     for lo, hi in tiles:
         m = hi - lo
         cu_q = torch.tensor([0, m], dtype=torch.int32, device=dev)
         cu_k = torch.tensor([0, hi], dtype=torch.int32, device=dev)
-        ws_i = torch.empty(max(1, msa.msa_index_topk_workspace_size(1, m, hi, G, wl.block_size, wl.topk)),
-                           dtype=torch.uint8, device=dev)
-        ws_a = torch.empty(max(1, msa.msa_sparse_attn_workspace_size(1, m, Hq, G, D, wl.topk, 0)),
-                           dtype=torch.uint8, device=dev)
         ids = torch.empty((m, G, wl.topk), dtype=torch.int32, device=dev)
         out = torch.empty((m, Hq, D), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((m, Hq), dtype=torch.float32, device=dev)
@@ -171,7 +173,7 @@ def main():
     else:
         dom_ms = float(np.mean(per_call_att))
         dom_flops = att_flops / len(calls)
-        kernel = "sparse_attn_fwd<bf16> (one msa_sparse_attn_prefill call)"
+        kernel = "kvo_attn + kvo_combine + edge-list kernels (one msa_sparse_attn_prefill call)"
         traffic = traffic_record("sparse_attn_fwd_128k")
     achieved = dom_flops / (dom_ms / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -207,7 +209,7 @@ def main():
         B = len(ctx)
         ws_i = torch.empty(max(1, msa.msa_index_topk_workspace_size(B, 1, max(ctx), G, wd.block_size, wd.topk)),
                            dtype=torch.uint8, device=dev)
-        ws_a = torch.empty(max(1, msa.msa_sparse_attn_workspace_size(B, 1, Hq, G, D, wd.topk, 0)),
+        ws_a = torch.empty(max(1, msa.msa_sparse_attn_workspace_size(B, 1, max(ctx), Hq, G, D, wd.topk, 0)),
                            dtype=torch.uint8, device=dev)
         ids = torch.empty((B, G, wd.topk), dtype=torch.int32, device=dev)
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)

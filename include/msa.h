@@ -131,15 +131,24 @@ msa_status_t msa_index_topk(const void* q_idx, const void* k_idx, msa_dtype_t dt
  *   block_idx    [Tq, num_kv_heads, topk] int32 (from msa_index_topk)
  *   cu_seqlens_q, cu_seqlens_k, max_q_len, max_kv_len   as for msa_index_topk
  *   softmax_scale  <= 0 selects 1 / sqrt(head_dim)
- *   num_splits   split each selection into this many chunks of consecutive
- *                ids, attended separately and merged by a log-sum-exp combine
- *                in a fixed order (no atomics); 0 = choose automatically
+ *   num_splits   0 = choose the schedule automatically.  For large prefills
+ *                (bf16, q_len > 1, at least 4096 (query, group) items) that
+ *                is the KV-outer schedule of the atlas record's kernel list:
+ *                the selection is inverted into per-block query lists, each
+ *                selected K/V block is staged on chip once for every query
+ *                that picked it, and the per-block partial results are merged
+ *                by a log-sum-exp combine in selection order (no atomics in
+ *                any arithmetic).  num_splits >= 1 forces the query-outer
+ *                schedule: each selection is split into that many chunks of
+ *                consecutive ids, attended separately and merged the same way.
  *   out          [Tq, num_heads, head_dim], element type `dtype`
  *   lse          [Tq, num_heads] fp32, natural log, or NULL
- *   workspace    at least msa_sparse_attn_workspace_size() bytes
+ *   workspace    at least msa_sparse_attn_workspace_size() bytes (the
+ *                KV-outer schedule needs about 266 KB per query row of a
+ *                window of at most 8192 rows, i.e. up to 2.2 GB)
  * ---------------------------------------------------------------------- */
-size_t msa_sparse_attn_workspace_size(int batch, int max_q_len, int num_heads, int num_kv_heads,
-                                      int head_dim, int topk, int num_splits);
+size_t msa_sparse_attn_workspace_size(int batch, int max_q_len, int max_kv_len, int num_heads,
+                                      int num_kv_heads, int head_dim, int topk, int num_splits);
 
 msa_status_t msa_sparse_attn_prefill(const void* q, const void* k, const void* v, msa_dtype_t dtype,
                                      const int32_t* block_idx, const int32_t* cu_seqlens_q,
@@ -166,7 +175,7 @@ msa_status_t msa_sparse_attn_prefill(const void* q, const void* k, const void* v
  *   cache_offsets [batch] int64, device, in tokens
  *   ctx_lens      [batch] int32, device, >= 1, <= max_ctx
  *   out           [batch, num_heads, head_dim]; lse [batch, num_heads] or NULL
- *   workspace     at least msa_sparse_attn_workspace_size(batch, 1, ...) bytes
+ *   workspace     at least msa_sparse_attn_workspace_size(batch, 1, max_ctx, ...) bytes
  * ---------------------------------------------------------------------- */
 msa_status_t msa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                                     msa_dtype_t dtype, const int32_t* block_idx,

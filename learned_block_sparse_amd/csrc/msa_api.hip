@@ -20,6 +20,8 @@ static constexpr int64_t kScanTargetWgs = 2048;
 static constexpr int64_t kDecodeTargetWaves = 8192;
 // Attention: work items (waves) aimed at before splitting selections.
 static constexpr int64_t kAttnTargetWaves = 8192;
+// Attention: (query, group) items from which the KV-outer schedule is used.
+static constexpr int64_t kKvoMinItems = 4096;
 
 IndexPlan plan_index(int batch, int max_q_len, int max_kv_len, int G) {
   IndexPlan pl;
@@ -67,9 +69,30 @@ IndexPlan plan_index(int batch, int max_q_len, int max_kv_len, int G) {
   return pl;
 }
 
-AttnPlan plan_attn(int64_t rows, int Hq, int G, int D, int topk, int num_splits) {
+AttnPlan plan_attn(int batch, int max_q_len, int max_kv_len, int Hq, int G, int D, int topk, int num_splits) {
   AttnPlan pl;
+  const int64_t rows = (int64_t)batch * max_q_len;
   pl.rows_bound = rows;
+  pl.nb_max = (int)ceil_div(max_kv_len, kBlock);
+  if (max_q_len > 1 && num_splits == 0 && rows * G >= kKvoMinItems) {
+    // KV-outer: each selected K/V block is staged once and shared by every
+    // query that picked it; partial outputs per selection slot.
+    pl.kvouter = true;
+    pl.kvo_window = rows < kvo_window_rows() ? rows : kvo_window_rows();
+    pl.kvo_nbuckets = (int)((int64_t)batch * G * pl.nb_max);
+    const size_t nbk = (size_t)pl.kvo_nbuckets;
+    const size_t slots = (size_t)pl.kvo_window * G * topk;
+    size_t off = 0;
+    pl.kvo_counts_off = off;  off += align_up(nbk * 4);
+    pl.kvo_offsets_off = off; off += align_up((nbk + 1) * 4);
+    pl.kvo_chunks_off = off;  off += align_up((nbk + 1) * 4);
+    pl.kvo_cursor_off = off;  off += align_up(nbk * 4);
+    pl.kvo_edges_off = off;   off += align_up(slots * 4);
+    pl.kvo_part_o_off = off;  off += align_up(slots * kvo_part_slot_bytes());
+    pl.kvo_part_lse_off = off; off += align_up(slots * 16 * sizeof(float));
+    pl.workspace_bytes = off;
+    return pl;
+  }
   int ns = num_splits;
   if (ns <= 0) {
     const int64_t items = rows * G;
@@ -141,11 +164,12 @@ msa_status_t msa_index_topk(const void* q_idx, const void* k_idx, msa_dtype_t dt
                                       batch, num_groups, topk, block_idx, workspace, stream));
 }
 
-size_t msa_sparse_attn_workspace_size(int batch, int max_q_len, int num_heads, int num_kv_heads,
-                                      int head_dim, int topk, int num_splits) {
-  if (batch <= 0 || max_q_len <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || topk <= 0)
+size_t msa_sparse_attn_workspace_size(int batch, int max_q_len, int max_kv_len, int num_heads,
+                                      int num_kv_heads, int head_dim, int topk, int num_splits) {
+  if (batch <= 0 || max_q_len <= 0 || max_kv_len <= 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || topk <= 0 || num_splits < 0)
     return 0;
-  return plan_attn((int64_t)batch * max_q_len, num_heads, num_kv_heads, head_dim, topk, num_splits)
+  return plan_attn(batch, max_q_len, max_kv_len, num_heads, num_kv_heads, head_dim, topk, num_splits)
       .workspace_bytes;
 }
 
@@ -178,7 +202,7 @@ msa_status_t msa_sparse_attn_prefill(const void* q, const void* k, const void* v
                                block_size, topk, num_splits);
   if (st != MSA_OK) return st;
   if (!cu_seqlens_q || !cu_seqlens_k || max_q_len <= 0 || max_kv_len <= 0) return MSA_ERR_INVALID_ARG;
-  const AttnPlan pl = plan_attn((int64_t)batch * max_q_len, num_heads, num_kv_heads, head_dim, topk, num_splits);
+  const AttnPlan pl = plan_attn(batch, max_q_len, max_kv_len, num_heads, num_kv_heads, head_dim, topk, num_splits);
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes)) return MSA_ERR_WORKSPACE;
   AttnArgs a{q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, nullptr, nullptr, batch, num_heads, num_kv_heads,
              topk, resolve_scale(softmax_scale, head_dim), out, lse};
@@ -196,7 +220,7 @@ msa_status_t msa_sparse_attn_decode(const void* q, const void* k_cache, const vo
                                head_dim, block_size, topk, num_splits);
   if (st != MSA_OK) return st;
   if (!cache_offsets || !ctx_lens || max_ctx <= 0) return MSA_ERR_INVALID_ARG;
-  const AttnPlan pl = plan_attn(batch, num_heads, num_kv_heads, head_dim, topk, num_splits);
+  const AttnPlan pl = plan_attn(batch, 1, max_ctx, num_heads, num_kv_heads, head_dim, topk, num_splits);
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes)) return MSA_ERR_WORKSPACE;
   AttnArgs a{q, k_cache, v_cache, block_idx, nullptr, nullptr, cache_offsets, ctx_lens, batch, num_heads,
              num_kv_heads, topk, resolve_scale(softmax_scale, head_dim), out, lse};

@@ -31,16 +31,23 @@ struct IndexPlan {
 };
 
 struct AttnPlan {
-  int nsplit = 1;            // chunks per selection
+  int nsplit = 1;            // chunks per selection (query-outer schedule)
   int bps = 16;              // selected blocks per chunk
   int64_t rows_bound = 0;    // query rows (upper bound)
   size_t part_o_bytes = 0;   // [rows, Hq, nsplit, D] fp32
   size_t part_lse_bytes = 0; // [rows, Hq, nsplit] fp32
+  // KV-outer schedule (prefill, bf16): per-block edge lists and per-slot partials
+  bool kvouter = false;
+  int nb_max = 0;
+  int64_t kvo_window = 0;    // query rows per window
+  int kvo_nbuckets = 0;      // batch * G * nb_max
+  size_t kvo_counts_off = 0, kvo_offsets_off = 0, kvo_chunks_off = 0, kvo_cursor_off = 0;
+  size_t kvo_edges_off = 0, kvo_part_o_off = 0, kvo_part_lse_off = 0;
   size_t workspace_bytes = 0;
 };
 
 IndexPlan plan_index(int batch, int max_q_len, int max_kv_len, int G);
-AttnPlan plan_attn(int64_t rows, int Hq, int G, int D, int topk, int num_splits);
+AttnPlan plan_attn(int batch, int max_q_len, int max_kv_len, int Hq, int G, int D, int topk, int num_splits);
 
 hipError_t launch_index_topk(const IndexPlan& pl, int dtype, int DI, const void* q_idx, const void* k_idx,
                              const int32_t* cu_q, const int32_t* cu_k, int batch, int G, int topk,
@@ -63,5 +70,8 @@ struct AttnArgs {
 };
 
 hipError_t launch_sparse_attn(const AttnPlan& pl, int dtype, const AttnArgs& a, void* ws, hipStream_t st);
+hipError_t launch_attn_kvouter(const AttnPlan& pl, const AttnArgs& a, void* ws, hipStream_t st);
+size_t kvo_part_slot_bytes();
+int kvo_window_rows();
 
 }  // namespace msa

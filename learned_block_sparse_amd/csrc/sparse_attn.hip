@@ -318,6 +318,15 @@ static hipError_t launch_attn_t(const AttnPlan& pl, const AttnArgs& a, void* ws,
 }
 
 hipError_t launch_sparse_attn(const AttnPlan& pl, int dtype, const AttnArgs& a, void* ws, hipStream_t st) {
+  if (pl.kvouter) {
+    if (dtype != 0) return launch_attn_kvouter(pl, a, ws, st);
+    // fp32 inputs: the query-outer schedule with one chunk (needs no workspace)
+    AttnPlan q1 = pl;
+    q1.kvouter = false;
+    q1.nsplit = 1;
+    q1.bps = a.topk;
+    return launch_attn_t<float>(q1, a, ws, st);
+  }
   return dtype == 0 ? launch_attn_t<float>(pl, a, ws, st) : launch_attn_t<bf16>(pl, a, ws, st);
 }
 

@@ -1,0 +1,427 @@
+// sparse_attn_kvouter.hip -- KV-outer schedule of the MSA main branch (prefill).
+//
+// Method: "MiniMax Sparse Attention: let each query pick its own blocks",
+// section "The mechanism, precisely" (exact attention over the selected
+// blocks; all heads of a group share the group's blocks).  Schedule: the
+// atlas record of MiniMax M3, kernel list (KV-outer sparse attention with
+// query gathering, pre-scheduled chunking of hot blocks, a two-phase combine
+// over per-partial LSE buffers with no atomics, LSE fused into the forward).
+//
+// Why KV-outer on gfx950: each (query, group, block) edge needs a 64 KB K/V
+// block.  Gathering it per query costs 64 KB of cache traffic per 1 MFLOP of
+// MFMA work; staging each block in LDS once and running every query that
+// selected it costs ~12 KB per edge instead (the query's 4 KB Q and a 4 KB
+// bf16 partial written and read back).
+//
+// Steps for one window of query rows (the host loops over windows so the
+// partial buffer stays bounded):
+//   kvo_zero / kvo_count / kvo_scan / kvo_scatter
+//       invert the selection into per-(sequence, group, block) edge lists and
+//       cut each list into chunks of kKvoChunk edges (the pre-scheduled
+//       chunking: hot blocks get several workgroups).  Atomics only count and
+//       place edges; every result lands in a slot fixed by (row, group,
+//       position in the selection), so outputs do not depend on the order.
+//   kvo_attn
+//       one workgroup per chunk: the K and V blocks (32 KB each) are staged in
+//       LDS once; each wave runs two queries at a time through 32x32x16 MFMAs
+//       (2 queries x 16 heads = 32 columns): S^T = K Q^T (keys x columns), a
+//       softmax over the block per column, O^T = V^T P^T with V staged
+//       transposed (keys contiguous) once per workgroup, so each operand is
+//       two 8-byte LDS reads.  Each edge writes its normalised partial output
+//       (bf16) and its LSE (fp32).
+//   kvo_combine
+//       per (row, group): lse = ln sum_i exp(lse_i), o = sum_i exp(lse_i - lse) o_i
+//       over the selection slots in order.
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+constexpr int kKvoThreads = 256;
+constexpr int kKvoChunk = 64;   // edges per attention workgroup
+constexpr int kKStride = 136;   // LDS row of K: 128 bf16 + 8 pad (272 B: 16-byte reads of 16 rows hit distinct banks)
+constexpr int kVtStride = 132;  // LDS row of V^T (one dim, 128 keys): 264 B, so 32 rows read at one key offset hit distinct banks
+constexpr int kRmax = 16;       // heads per group held by one partial slot
+
+struct KvoArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const int32_t* block_idx;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int batch, G, Hq, topk, nb_max;
+  int64_t row_lo, row_hi;
+  float scale_log2;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* chunk_start;
+  int32_t* cursor;
+  int32_t* edges;
+  bf16* part_o;
+  float* part_lse;
+  bf16* out;
+  float* lse;
+};
+
+__device__ __forceinline__ int kvo_find(const int32_t* cu, int n, int64_t x) {
+  int lo = 0, hi = n;  // cu[lo] <= x < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// A selection entry is attended when it names a block at or before the local
+// block and does not repeat an earlier entry of the same row (Sel is a set).
+__device__ __forceinline__ bool kvo_entry_valid(const int32_t* sel, int i, int c, int64_t local, int nb_max) {
+  if (c < 0 || c > local || c >= nb_max) return false;
+  for (int j = 0; j < i; ++j)
+    if (sel[j] == c) return false;
+  return true;
+}
+
+struct RowInfo {
+  int b;
+  int64_t p;
+};
+
+__device__ __forceinline__ RowInfo kvo_row(const KvoArgs& a, int64_t t) {
+  RowInfo r;
+  r.b = kvo_find(a.cu_q, a.batch, t);
+  const int M = a.cu_q[r.b + 1] - a.cu_q[r.b];
+  const int N = a.cu_k[r.b + 1] - a.cu_k[r.b];
+  r.p = (int64_t)N - M + (t - a.cu_q[r.b]);
+  return r;
+}
+
+__global__ __launch_bounds__(256) void kvo_zero(int32_t* counts, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) counts[i] = 0;
+}
+
+template <bool kScatter>
+__global__ __launch_bounds__(256) void kvo_bucket(KvoArgs a) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = a.G * a.topk;
+  if (e >= (a.row_hi - a.row_lo) * per_row) return;
+  const int64_t t = a.row_lo + e / per_row;
+  if (t >= a.cu_q[a.batch]) return;
+  const int g = (int)((e / a.topk) % a.G);
+  const int i = (int)(e % a.topk);
+  const int32_t* sel = a.block_idx + (t * a.G + g) * a.topk;
+  const int c = sel[i];
+  const RowInfo ri = kvo_row(a, t);
+  if (ri.p < 0 || !kvo_entry_valid(sel, i, c, ri.p / kBlock, a.nb_max)) return;
+  const int bucket = (ri.b * a.G + g) * a.nb_max + c;
+  if (kScatter) {
+    const int pos = atomicAdd(&a.cursor[bucket], 1);
+    a.edges[pos] = (int32_t)(((t - a.row_lo) << 4) | i);
+  } else {
+    atomicAdd(&a.counts[bucket], 1);
+  }
+}
+
+// Exclusive scans of the edge counts and of the chunk counts, one workgroup.
+__global__ __launch_bounds__(1024) void kvo_scan(KvoArgs a, int nbk) {
+  __shared__ int s_e[1024];
+  __shared__ int s_c[1024];
+  const int tid = threadIdx.x;
+  const int seg = (nbk + 1023) / 1024;
+  const int lo = min(tid * seg, nbk), hi = min(lo + seg, nbk);
+  int se = 0, sc = 0;
+  for (int j = lo; j < hi; ++j) {
+    const int n = a.counts[j];
+    se += n;
+    sc += (n + kKvoChunk - 1) / kKvoChunk;
+  }
+  s_e[tid] = se;
+  s_c[tid] = sc;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int ve = tid >= off ? s_e[tid - off] : 0;
+    const int vc = tid >= off ? s_c[tid - off] : 0;
+    __syncthreads();
+    s_e[tid] += ve;
+    s_c[tid] += vc;
+    __syncthreads();
+  }
+  int oe = s_e[tid] - se, oc = s_c[tid] - sc;  // exclusive prefix of this thread's range
+  for (int j = lo; j < hi; ++j) {
+    const int n = a.counts[j];
+    a.offsets[j] = oe;
+    a.cursor[j] = oe;
+    a.chunk_start[j] = oc;
+    oe += n;
+    oc += (n + kKvoChunk - 1) / kKvoChunk;
+  }
+  if (tid == 1023) {
+    a.offsets[nbk] = s_e[1023];
+    a.chunk_start[nbk] = s_c[1023];
+  }
+}
+
+__global__ __launch_bounds__(kKvoThreads, 2) void kvo_attn(KvoArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 k_lds[kBlock * kKStride];
+  __shared__ __attribute__((aligned(16))) bf16 vt_lds[kHeadDim * kVtStride];
+  const int nbk = a.batch * a.G * a.nb_max;
+  const int w = blockIdx.x;
+  if (w >= a.chunk_start[nbk]) return;
+  const int bucket = kvo_find(a.chunk_start, nbk, w);
+  const int chunk = w - a.chunk_start[bucket];
+  const int c = bucket % a.nb_max;
+  const int g = (bucket / a.nb_max) % a.G;
+  const int b = bucket / (a.nb_max * a.G);
+  const int e_lo = a.offsets[bucket] + chunk * kKvoChunk;
+  const int e_hi = min(e_lo + kKvoChunk, a.offsets[bucket + 1]);
+  const int64_t kb0 = a.cu_k[b];
+  const int N = a.cu_k[b + 1] - a.cu_k[b];
+  const int64_t q0 = a.cu_q[b];
+  const int M = a.cu_q[b + 1] - a.cu_q[b];
+  const int64_t rs = (int64_t)a.G * kHeadDim;
+
+  // ---- stage K row-major and V transposed (rows past the sequence end clamp
+  // to its last row; their scores are masked)
+  {
+    u32x4 kr[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int piece = threadIdx.x + u * kKvoThreads;
+      const int row = piece >> 4, col = (piece & 15) * 8;
+      const int64_t key = min(c * kBlock + row, N - 1);
+      kr[u] = *reinterpret_cast<const u32x4*>(a.k + (kb0 + key) * rs + g * kHeadDim + col);
+    }
+    // V unit = (key quad kq, dim octet o8): 4 rows x 8 dims, written as 8 runs of 4 keys
+    bf16x8 vr[2][4];
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) {
+      const int u = threadIdx.x + uu * kKvoThreads;
+      const int kq = u & 31, o8 = u >> 5;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int64_t key = min(c * kBlock + 4 * kq + jj, N - 1);
+        vr[uu][jj] = load8(a.v + (kb0 + key) * rs + g * kHeadDim + 8 * o8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int piece = threadIdx.x + u * kKvoThreads;
+      const int row = piece >> 4, col = (piece & 15) * 8;
+      *reinterpret_cast<u32x4*>(k_lds + row * kKStride + col) = kr[u];
+    }
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) {
+      const int u = threadIdx.x + uu * kKvoThreads;
+      const int kq = u & 31, o8 = u >> 5;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16x4 w4 = {vr[uu][0][e], vr[uu][1][e], vr[uu][2][e], vr[uu][3][e]};
+        *reinterpret_cast<bf16x4*>(vt_lds + (8 * o8 + e) * kVtStride + 4 * kq) = w4;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int col = lane & 31;   // MFMA column (query jq, head h); also the A-operand row
+  const int a32 = lane >> 5;   // contraction slots 8*a32 .. 8*a32+7
+  const int jq = col >> 4, h = col & 15;
+  const int R = a.Hq / a.G;
+
+  for (int e = e_lo + 2 * wave; e < e_hi; e += 2 * (kKvoThreads / kWave)) {
+    const bool has = e + jq < e_hi;
+    const int code = a.edges[has ? e + jq : e];
+    const int64_t trel = code >> 4;
+    const int slot_i = code & 15;
+    const int64_t t = a.row_lo + trel;
+    const int64_t p = (int64_t)N - M + (t - q0);
+    const bool colok = has && h < R;
+
+    // B operand Q^T: column (jq, h), slots d = 16*ks + 8*a32 .. +7
+    bf16x8 qf[kHeadDim / 16];
+    const bf16* qp = a.q + (t * a.Hq + g * R + (colok ? h : 0)) * kHeadDim + 8 * a32;
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 16; ++ks) qf[ks] = colok ? load8(qp + 16 * ks) : zero8<bf16>();
+
+    // S^T[key][col] for the 128 keys: 4 tiles of 32 keys
+    f32x16 st[kBlock / 32];
+#pragma unroll
+    for (int kt = 0; kt < kBlock / 32; ++kt) {
+      st[kt] = f32x16{};
+      const bf16* arow = k_lds + (32 * kt + col) * kKStride + 8 * a32;
+#pragma unroll
+      for (int ks = 0; ks < kHeadDim / 16; ++ks)
+        st[kt] = mma32(*reinterpret_cast<const bf16x8*>(arow + 16 * ks), qf[ks], st[kt]);
+      __builtin_amdgcn_sched_barrier(0);  // keep each tile's LDS reads next to its MFMAs
+    }
+
+    // softmax over the block, per column (the other half of the keys sits in lane ^ 32)
+    const int64_t key0 = (int64_t)c * kBlock;
+    const bool causal = key0 + kBlock - 1 > p;
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kt = 0; kt < kBlock / 32; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = st[kt][r] * a.scale_log2;
+        if (causal && key0 + 32 * kt + 8 * (r >> 2) + 4 * a32 + (r & 3) > p) x = -__builtin_inff();
+        st[kt][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    float sum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < kBlock / 32; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float ex = __builtin_amdgcn_exp2f(st[kt][r] - mx);
+        st[kt][r] = ex;
+        sum += ex;
+      }
+    sum += shfl_xor_f(sum, 32);
+
+    // P^T as bf16 B operands: k-step kk covers keys 32*kt + 16*m + 8*(i/4) + 4*a32 + i%4
+    // (kt = kk/2, m = kk%2), which are exactly this lane's S^T registers 8m .. 8m+7.
+    bf16x8 pb[kBlock / 16];
+#pragma unroll
+    for (int kk = 0; kk < kBlock / 16; ++kk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[kk][i] = bf16(st[kk >> 1][8 * (kk & 1) + i]);
+
+    const float inv = 1.0f / sum;
+    const int64_t slot = (trel * a.G + g) * a.topk + slot_i;
+    bf16* po = a.part_o + (slot * kRmax + h) * kHeadDim;
+    // O^T[d][col] = V^T[d][key] P^T[key][col], 32 dims at a time
+#pragma unroll
+    for (int dt = 0; dt < kHeadDim / 32; ++dt) {
+      f32x16 o = {};
+#pragma unroll
+      for (int kk = 0; kk < kBlock / 16; ++kk) {
+        const int kb1 = 32 * (kk >> 1) + 16 * (kk & 1) + 4 * a32;
+        // A operand V^T: row d = 32*dt + lane%32, keys kb1 .. kb1+3 and kb1+8 .. kb1+11
+        const bf16* src = vt_lds + (32 * dt + col) * kVtStride + kb1;
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src + 8);
+        bf16x8 va;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          va[i] = lo[i];
+          va[4 + i] = hi[i];
+        }
+        o = mma32(va, pb[kk], o);
+        if (kk & 1) __builtin_amdgcn_sched_barrier(0);
+      }
+      if (colok) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          bf16x4 wv = {bf16(o[4 * qd] * inv), bf16(o[4 * qd + 1] * inv), bf16(o[4 * qd + 2] * inv),
+                       bf16(o[4 * qd + 3] * inv)};
+          *reinterpret_cast<bf16x4*>(po + 32 * dt + 8 * qd + 4 * a32) = wv;
+        }
+      }
+    }
+    if (colok && a32 == 0) a.part_lse[slot * kRmax + h] = mx * 0.69314718055994530942f + logf(sum);
+  }
+}
+
+// Fixed-order LSE combine of the selection slots: one wave per (row, group);
+// lane = (head lane/4, 32 dims at 32*(lane%4)).
+__global__ __launch_bounds__(256) void kvo_combine(KvoArgs a) {
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= (a.row_hi - a.row_lo) * a.G) return;
+  const int64_t trel = item / a.G;
+  const int g = (int)(item % a.G);
+  const int64_t t = a.row_lo + trel;
+  if (t >= a.cu_q[a.batch]) return;
+  const int lane = lane_id();
+  const int h = lane >> 2, d0 = 32 * (lane & 3);
+  const int R = a.Hq / a.G;
+  if (h >= R) return;
+  const RowInfo ri = kvo_row(a, t);
+  const int32_t* sel = a.block_idx + (t * a.G + g) * a.topk;
+  const int64_t local = ri.p >= 0 ? ri.p / kBlock : -1;
+  const int64_t slot0 = (trel * a.G + g) * a.topk;
+  float mx = -__builtin_inff();
+  for (int i = 0; i < a.topk; ++i)
+    if (kvo_entry_valid(sel, i, sel[i], local, a.nb_max)) mx = fmaxf(mx, a.part_lse[(slot0 + i) * kRmax + h]);
+  bf16* out = a.out + (t * a.Hq + g * R + h) * kHeadDim + d0;
+  if (mx == -__builtin_inff()) {
+#pragma unroll
+    for (int j = 0; j < 32; j += 4) *reinterpret_cast<bf16x4*>(out + j) = bf16x4{bf16(0.f), bf16(0.f), bf16(0.f), bf16(0.f)};
+    if (a.lse && (lane & 3) == 0) a.lse[t * a.Hq + g * R + h] = -__builtin_inff();
+    return;
+  }
+  float sum = 0.f;
+  for (int i = 0; i < a.topk; ++i)
+    if (kvo_entry_valid(sel, i, sel[i], local, a.nb_max)) sum += expf(a.part_lse[(slot0 + i) * kRmax + h] - mx);
+  const float L = mx + logf(sum);
+  float acc[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) acc[j] = 0.f;
+  for (int i = 0; i < a.topk; ++i) {
+    if (!kvo_entry_valid(sel, i, sel[i], local, a.nb_max)) continue;
+    const float wgt = expf(a.part_lse[(slot0 + i) * kRmax + h] - L);
+    const bf16* src = a.part_o + ((slot0 + i) * kRmax + h) * kHeadDim + d0;
+#pragma unroll
+    for (int j = 0; j < 32; j += 8) {
+      const bf16x8 v8 = load8(src + j);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[j + u] += wgt * (float)v8[u];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 32; j += 4)
+    *reinterpret_cast<bf16x4*>(out + j) = bf16x4{bf16(acc[j]), bf16(acc[j + 1]), bf16(acc[j + 2]), bf16(acc[j + 3])};
+  if (a.lse && (lane & 3) == 0) a.lse[t * a.Hq + g * R + h] = L;
+}
+
+hipError_t launch_attn_kvouter(const AttnPlan& pl, const AttnArgs& x, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  KvoArgs a;
+  a.q = static_cast<const bf16*>(x.q);
+  a.k = static_cast<const bf16*>(x.k);
+  a.v = static_cast<const bf16*>(x.v);
+  a.block_idx = x.block_idx;
+  a.cu_q = x.cu_q;
+  a.cu_k = x.cu_k;
+  a.batch = x.batch;
+  a.G = x.Hkv;
+  a.Hq = x.Hq;
+  a.topk = x.topk;
+  a.nb_max = pl.nb_max;
+  a.scale_log2 = x.scale * 1.4426950408889634f;
+  a.counts = reinterpret_cast<int32_t*>(w + pl.kvo_counts_off);
+  a.offsets = reinterpret_cast<int32_t*>(w + pl.kvo_offsets_off);
+  a.chunk_start = reinterpret_cast<int32_t*>(w + pl.kvo_chunks_off);
+  a.cursor = reinterpret_cast<int32_t*>(w + pl.kvo_cursor_off);
+  a.edges = reinterpret_cast<int32_t*>(w + pl.kvo_edges_off);
+  a.part_o = reinterpret_cast<bf16*>(w + pl.kvo_part_o_off);
+  a.part_lse = reinterpret_cast<float*>(w + pl.kvo_part_lse_off);
+  a.out = static_cast<bf16*>(x.out);
+  a.lse = x.lse;
+  const int nbk = pl.kvo_nbuckets;
+  for (int64_t r0 = 0; r0 < pl.rows_bound; r0 += pl.kvo_window) {
+    a.row_lo = r0;
+    a.row_hi = r0 + pl.kvo_window < pl.rows_bound ? r0 + pl.kvo_window : pl.rows_bound;
+    const int64_t entries = (a.row_hi - a.row_lo) * a.G * a.topk;
+    const unsigned eg = (unsigned)((entries + 255) / 256);
+    hipLaunchKernelGGL(kvo_zero, dim3((unsigned)((nbk + 255) / 256)), dim3(256), 0, st, a.counts, nbk);
+    hipLaunchKernelGGL(kvo_bucket<false>, dim3(eg), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(kvo_scan, dim3(1), dim3(1024), 0, st, a, nbk);
+    hipLaunchKernelGGL(kvo_bucket<true>, dim3(eg), dim3(256), 0, st, a);
+    const int64_t ub = entries / kKvoChunk + (entries < nbk ? entries : nbk) + 1;
+    hipLaunchKernelGGL(kvo_attn, dim3((unsigned)ub), dim3(kKvoThreads), 0, st, a);
+    const int64_t items = (a.row_hi - a.row_lo) * a.G;
+    hipLaunchKernelGGL(kvo_combine, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+size_t kvo_part_slot_bytes() { return (size_t)kRmax * kHeadDim * sizeof(bf16); }
+int kvo_window_rows() { return 8192; }
+
+}  // namespace msa

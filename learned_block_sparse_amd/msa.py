@@ -56,7 +56,7 @@ def lib():
         L.msa_index_topk.restype = i32
         L.msa_index_topk.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, sz, vp]
         L.msa_sparse_attn_workspace_size.restype = sz
-        L.msa_sparse_attn_workspace_size.argtypes = [i32] * 7
+        L.msa_sparse_attn_workspace_size.argtypes = [i32] * 8
         L.msa_sparse_attn_prefill.restype = i32
         L.msa_sparse_attn_prefill.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                               i32, ctypes.c_float, i32, vp, vp, vp, sz, vp]
@@ -110,10 +110,10 @@ def msa_index_topk_workspace_size(batch, max_q_len, max_kv_len, num_groups, bloc
     return lib().msa_index_topk_workspace_size(batch, max_q_len, max_kv_len, num_groups, block_size, topk)
 
 
-def msa_sparse_attn_workspace_size(batch, max_q_len, num_heads, num_kv_heads, head_dim, topk,
-                                   num_splits=0) -> int:
-    return lib().msa_sparse_attn_workspace_size(batch, max_q_len, num_heads, num_kv_heads, head_dim,
-                                                topk, num_splits)
+def msa_sparse_attn_workspace_size(batch, max_q_len, max_kv_len, num_heads, num_kv_heads, head_dim,
+                                   topk, num_splits=0) -> int:
+    return lib().msa_sparse_attn_workspace_size(batch, max_q_len, max_kv_len, num_heads, num_kv_heads,
+                                                head_dim, topk, num_splits)
 
 
 def msa_index_topk(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, max_q_len: int, max_kv_len: int,
@@ -150,7 +150,7 @@ def msa_sparse_attn_prefill(q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_
         out = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
-    need = msa_sparse_attn_workspace_size(batch, max_q_len, hq, hkv, d, topk, num_splits)
+    need = msa_sparse_attn_workspace_size(batch, max_q_len, max_kv_len, hq, hkv, d, topk, num_splits)
     ws, ws_bytes = _workspace(need, q.device, workspace)
     st = lib().msa_sparse_attn_prefill(
         _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dtype_code(q),
@@ -174,7 +174,7 @@ def msa_sparse_attn_decode(q, k_cache, v_cache, block_idx, cache_offsets, ctx_le
         out = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
-    need = msa_sparse_attn_workspace_size(batch, 1, hq, hkv, d, topk, num_splits)
+    need = msa_sparse_attn_workspace_size(batch, 1, max_ctx, hq, hkv, d, topk, num_splits)
     ws, ws_bytes = _workspace(need, q.device, workspace)
     st = lib().msa_sparse_attn_decode(
         _dev(q, "q"), _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype), _dtype_code(q),

@@ -87,9 +87,12 @@ def test_workspace_sizes(L):
     # unsupported block size reports 0
     assert L.msa_index_topk_workspace_size(1, 256, 256, 4, 64, 16) == 0
     # one split: no workspace; more splits: partial outputs
-    assert L.msa_sparse_attn_workspace_size(1, 8192, 64, 4, 128, 16, 1) == 0
-    ws = L.msa_sparse_attn_workspace_size(2, 1, 64, 4, 128, 16, 4)
+    assert L.msa_sparse_attn_workspace_size(1, 8192, 8192, 64, 4, 128, 16, 1) == 0
+    ws = L.msa_sparse_attn_workspace_size(2, 1, 4096, 64, 4, 128, 16, 4)
     assert ws >= 2 * 64 * 4 * (128 + 1) * 4
+    # automatic schedule of a large prefill: KV-outer edge lists + bf16 partial slots
+    kvo = L.msa_sparse_attn_workspace_size(1, 8192, 131072, 64, 4, 128, 16, 0)
+    assert kvo >= 8192 * 4 * 16 * (16 * 128 * 2 + 16 * 4)
 
 
 def _prefill(L, **kw):

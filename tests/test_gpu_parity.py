@@ -58,24 +58,40 @@ def test_bf16_prefill_small_ragged(msa, synth, oracle_lib, L):
     _full_prefill_check(msa, oracle_lib, inp, wl, f"bf16 L={L}")
 
 
-def test_bf16_prefill_varlen_chunks(msa, synth, oracle_lib):
+@pytest.mark.parametrize("num_splits", [0, 1])
+def test_bf16_prefill_varlen_chunks(msa, synth, oracle_lib, num_splits):
     """Several sequences in one call, with q_len < kv_len (chunks of longer
-    prefills, bottom-right aligned) including a single-query sequence."""
+    prefills, bottom-right aligned) including a single-query sequence; both
+    the automatic (KV-outer) and the query-outer schedule."""
     wl = synth.WORKLOADS["prefill_32k"]
-    kv, ql = [3000, 1000, 300, 700], [517, 1000, 1, 129]
-    say(f"[parity] varlen kv={kv} q={ql}")
+    kv, ql = [3000, 1000, 300, 700], [1517, 1000, 1, 129]
+    say(f"[parity] varlen kv={kv} q={ql} splits={num_splits}")
     inp = synth.prefill_inputs(wl, device="cuda", seed=2, seq_lens=kv, q_lens=ql)
     cu_q, cu_k = inp["cu_q_host"], inp["cu_k_host"]
     ids = msa.msa_index_topk(inp["q_idx"], inp["k_idx"], inp["cu_seqlens_q"], inp["cu_seqlens_k"], max(ql),
                              max(kv), wl.block_size, wl.topk)
     out, lse = msa.msa_sparse_attn_prefill(inp["q"], inp["k"], inp["v"], ids, inp["cu_seqlens_q"],
-                                           inp["cu_seqlens_k"], max(ql), max(kv), wl.block_size, wl.topk)
+                                           inp["cu_seqlens_k"], max(ql), max(kv), wl.block_size, wl.topk,
+                                           num_splits=num_splits)
     torch.cuda.synchronize()
     ref_ids, ref_out, ref_lse = oracle_lib.prefill(host(inp["q_idx"]), host(inp["k_idx"]), host(inp["q"]),
                                                    host(inp["k"]), host(inp["v"]), cu_q, cu_k, wl.block_size,
                                                    wl.topk)
     compare_ids(ids, ref_ids, "varlen")
     compare_outputs(out, lse, ref_out, ref_lse, "bf16", "varlen")
+
+
+def test_kvouter_matches_query_outer(msa, synth):
+    """The KV-outer schedule (automatic for large prefills) and the query-outer
+    schedule agree to bf16 rounding on the same selection."""
+    wl = synth.WORKLOADS["prefill_32k"]
+    inp = synth.prefill_inputs(wl, device="cuda", seed=9, seq_lens=[5000])
+    say("[parity] kv-outer vs query-outer")
+    ids, out_kv, lse_kv = gpu_prefill(msa, inp, wl, num_splits=0)
+    _, out_q, lse_q = gpu_prefill(msa, inp, wl, num_splits=1)
+    torch.cuda.synchronize()
+    assert (out_kv.float() - out_q.float()).abs().max().item() <= 2 * 2.0 ** -8
+    assert (lse_kv - lse_q).abs().max().item() <= 1e-4
 
 
 @pytest.mark.parametrize("topk", [1, 2, 5, 16])
