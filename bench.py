@@ -50,6 +50,12 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--profile", choices=["prefill_tile", "decode", "copy"],
+                    help="run one workload a few times for hardware-counter collection and exit "
+                         "(prefill_tile: the last 8192-query call of the 128K prefill; decode: one "
+                         "decode step of the 1M-context batch; copy: a 1 GiB device-to-device copy "
+                         "that calibrates the byte counters)")
+    ap.add_argument("--profile-reps", type=int, default=3)
     return ap.parse_args()
 
 
@@ -89,6 +95,9 @@ def main():
     msa.lib()
     dev = "cuda"
     stream = torch.cuda.current_stream()
+    if args.profile:
+        profile_run(args, msa, synth, torch)
+        return
 
     # ------------------------------------------------------------------ prefill
     wl = synth.WORKLOADS["prefill_128k"]
@@ -258,6 +267,43 @@ def main():
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+def profile_run(args, msa, synth, torch):
+    """One workload, repeated, for rocprofv3 counter passes (no JSON line)."""
+    if args.profile == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.profile_reps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"profile copy: {args.profile_reps} x {n} bytes read + written", flush=True)
+        return
+    if args.profile == "prefill_tile":
+        wl = synth.WORKLOADS["prefill_128k"]
+        inp = synth.prefill_inputs(wl, device="cuda", seed=0)
+        lo, hi = wl.seq_len - wl.q_tile, wl.seq_len
+        cu_q = torch.tensor([0, hi - lo], dtype=torch.int32, device="cuda")
+        cu_k = torch.tensor([0, hi], dtype=torch.int32, device="cuda")
+        for _ in range(args.profile_reps):
+            ids = msa.msa_index_topk(inp["q_idx"][lo:hi], inp["k_idx"], cu_q, cu_k, hi - lo, hi, wl.block_size,
+                                     wl.topk)
+            msa.msa_sparse_attn_prefill(inp["q"][lo:hi], inp["k"], inp["v"], ids, cu_q, cu_k, hi - lo, hi,
+                                        wl.block_size, wl.topk)
+        torch.cuda.synchronize()
+        print(f"profile prefill_tile: rows [{lo}, {hi}) x {args.profile_reps}", flush=True)
+        return
+    wd = synth.WORKLOADS["decode_1m"]
+    ctx = synth.decode_ctx_lens(wd, 0)
+    d = synth.decode_inputs(wd, device="cuda", seed=0, ctx_lens=ctx)
+    for _ in range(args.profile_reps):
+        ids = msa.msa_index_topk(d["q_idx"], d["k_idx"], d["cu_seqlens_q"], d["cu_seqlens_k"], 1, max(ctx),
+                                 wd.block_size, wd.topk)
+        msa.msa_sparse_attn_decode(d["q"], d["k"], d["v"], ids, d["k_offsets"], d["ctx_lens"], max(ctx),
+                                   wd.block_size, wd.topk)
+    torch.cuda.synchronize()
+    print(f"profile decode: {len(ctx)} sequences, sum ctx {sum(ctx)} x {args.profile_reps}", flush=True)
 
 
 def cpu_baseline(target_s: float):

@@ -17,7 +17,7 @@
 //                     (16 registers x 4 tiles each) and the block max is a
 //                     register max plus one lane swap.  Each lane then owns
 //                     one column and keeps a sorted top-15 list in registers.
-//   idx_merge_prefill one wave per (query, group): merges the per-chunk lists
+//   idx_merge_prefill 8 lanes per (query, group): merge the per-chunk lists
 //                     under the same total order, adds the local block, writes
 //                     ids ascending.
 // Decode path (two kernels):
@@ -51,7 +51,7 @@ template <typename T, int DI>
 __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, int G, int qw, int nsub, int max_qblocks, int chunk,
-    int max_chunks, float* __restrict__ cand_s, int32_t* __restrict__ cand_i) {
+    int max_chunks, int64_t cand_stride, uint64_t* __restrict__ cand) {
   using L = ScanLds<T, DI>;
   static_assert(L::kChunks % kScanThreads == 0, "key block must split evenly over threads");
   constexpr int KS = DI / 16;  // 16-wide contraction steps
@@ -161,11 +161,14 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
     __syncthreads();
   }
 
+  // Candidates are stored as selection keys [chunk][list position][row * G +
+  // group]: lanes write consecutive columns, and the merge reads them the same way.
   const int col = col_base + lane;
   if (active && col < ncols) {
-    const int64_t base = ((row0 * G + col) * max_chunks + ch) * kList;
+    const int64_t rg = row0 * G + col;
 #pragma unroll
-    for (int j = 0; j < kList; ++j) { cand_s[base + j] = ls[j]; cand_i[base + j] = li[j]; }
+    for (int j = 0; j < kList; ++j)
+      cand[(int64_t)(ch * kList + j) * cand_stride + rg] = li[j] >= 0 ? sel_key(ls[j], li[j]) : 0ull;
   }
 }
 
@@ -181,40 +184,69 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int batch, int64_t ro
   return lo;
 }
 
+constexpr int kMergeLanes = 8;  // lanes sharing one (row, group)
+
 __global__ __launch_bounds__(256) void idx_merge_prefill(
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int64_t rows_bound,
-    int G, int topk, int chunk, int max_chunks, const float* __restrict__ cand_s,
-    const int32_t* __restrict__ cand_i, int32_t* __restrict__ block_idx) {
-  const int64_t item = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-  if (item >= rows_bound * G) return;
-  const int64_t row = item / G;
-  const int g = (int)(item % G);
-  if (row >= cu_q[batch]) return;
-  const int lane = lane_id();
-  const int b = find_seq(cu_q, batch, row);
-  const int M = cu_q[b + 1] - cu_q[b], N = cu_k[b + 1] - cu_k[b];
-  const int64_t p = (int64_t)N - M + (row - cu_q[b]);
-  int32_t* out = block_idx + (row * G + g) * topk;
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int64_t rows_bound, int G,
+    int topk, int chunk, const uint64_t* __restrict__ cand, int32_t* __restrict__ block_idx) {
+  // kMergeLanes lanes per (query row, group): lane part keeps the best 16 keys
+  // of chunks part, part + kMergeLanes, ...; three butterfly merges give every
+  // lane of the group the best 16 of all chunks; the best topk-1 plus the local
+  // block are written ascending.
+  const int64_t stride = rows_bound * G;
+  const int part = threadIdx.x % kMergeLanes;
+  const int64_t rg = ((int64_t)blockIdx.x * 256 + threadIdx.x) / kMergeLanes;
+  uint64_t kl[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) kl[j] = 0;
+  bool live = rg < stride;
+  const int64_t row = live ? rg / G : 0;
+  live = live && row < cu_q[batch];
+  int64_t p = -1;
+  if (live) {
+    const int b = find_seq(cu_q, batch, row);
+    const int M = cu_q[b + 1] - cu_q[b], N = cu_k[b + 1] - cu_k[b];
+    p = (int64_t)N - M + (row - cu_q[b]);
+  }
+  const int local = p >= 0 ? (int)(p / kBlock) : 0;
+  const int nch = p >= 0 ? (local + chunk - 1) / chunk : 0;
+  for (int ch = part; ch < nch; ch += kMergeLanes) {
+    uint64_t ck[kList];
+#pragma unroll
+    for (int j = 0; j < kList; ++j) ck[j] = cand[(int64_t)(ch * kList + j) * stride + rg];
+#pragma unroll
+    for (int j = 0; j < kList; ++j) {
+      if (!(ck[j] > kl[15])) break;  // lists are sorted: the rest of this one misses too
+      key_insert(kl, ck[j]);
+    }
+  }
+  key_merge_xor(kl, 1);
+  key_merge_xor(kl, 2);
+  key_merge_xor(kl, 4);
+  if (!live) return;
+  int32_t* out = block_idx + rg * topk;
   if (p < 0) {
-    if (lane < topk) out[lane] = -1;
+    if (part == 0)
+      for (int i = 0; i < topk; ++i) out[i] = -1;
     return;
   }
-  const int local = (int)(p / kBlock);
-  const int nch = (local + chunk - 1) / chunk;
-
-  float ls[kList];
-  int li[kList];
-  if (lane < nch) {
-    const int64_t base = ((row * G + g) * max_chunks + lane) * kList;
+  int m = 0;  // earlier blocks kept: the first min(valid, topk - 1) keys
 #pragma unroll
-    for (int j = 0; j < kList; ++j) { ls[j] = cand_s[base + j]; li[j] = cand_i[base + j]; }
-  } else {
+  for (int j = 0; j < kList; ++j) m += (j < topk - 1 && kl[j] != 0) ? 1 : 0;
+  // lane `part` writes list entries part and part + 8 at their ascending rank
 #pragma unroll
-    for (int j = 0; j < kList; ++j) { ls[j] = -__builtin_inff(); li[j] = -1; }
+  for (int j = 0; j < kList; ++j) {
+    if (j >= m || (j & (kMergeLanes - 1)) != part) continue;
+    const int id = sel_key_id(kl[j]);
+    int r = 0;
+#pragma unroll
+    for (int jj = 0; jj < kList; ++jj) r += (jj < m && sel_key_id(kl[jj]) < id) ? 1 : 0;
+    out[r] = id;
   }
-  int mine;
-  const int found = wave_merge(ls, li, topk - 1, mine);
-  write_selection(mine, found, local, topk, out);
+  if (part == 0) {
+    out[m] = local;  // every earlier id is below the local block
+    for (int i = m + 1; i < topk; ++i) out[i] = -1;
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -323,18 +355,17 @@ template <typename T, int DI>
 static hipError_t launch_index_prefill(const IndexPlan& pl, const void* q_idx, const void* k_idx,
                                        const int32_t* cu_q, const int32_t* cu_k, int batch, int G,
                                        int topk, int32_t* block_idx, char* ws, hipStream_t st) {
-  float* cand_s = reinterpret_cast<float*>(ws);
-  int32_t* cand_i = reinterpret_cast<int32_t*>(ws + pl.cand_score_bytes);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(ws);
   if (pl.scan_wgs > 0) {
     hipLaunchKernelGGL((idx_scan_prefill<T, DI>), dim3((unsigned)pl.scan_wgs), dim3(kScanThreads), 0, st,
                        static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), cu_q, cu_k, G,
-                       pl.qw, pl.nsub, pl.max_qblocks, pl.chunk, pl.max_chunks, cand_s, cand_i);
+                       pl.qw, pl.nsub, pl.max_qblocks, pl.chunk, pl.max_chunks, pl.rows_bound * G, cand);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t items = pl.rows_bound * G;
-  hipLaunchKernelGGL(idx_merge_prefill, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, cu_q, cu_k,
-                     batch, pl.rows_bound, G, topk, pl.chunk, pl.max_chunks, cand_s, cand_i, block_idx);
+  const int64_t items = pl.rows_bound * G * kMergeLanes;
+  hipLaunchKernelGGL(idx_merge_prefill, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, cu_q, cu_k,
+                     batch, pl.rows_bound, G, topk, pl.chunk, cand, block_idx);
   return hipGetLastError();
 }
 

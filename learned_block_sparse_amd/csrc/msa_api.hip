@@ -1,7 +1,7 @@
 // msa_api.hip -- the C ABI declared in include/msa.h: argument checks, work
 // plans and dispatch to the HIP kernels.  The library allocates no device
 // memory; scratch comes from the caller's workspace.
-#include "../../include/msa.h"
+#include "msa.h"
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -63,9 +63,8 @@ IndexPlan plan_index(int batch, int max_q_len, int max_kv_len, int G) {
     pl.scan_wgs = (int64_t)batch * pl.max_qblocks * pl.nsub * pl.max_chunks;
   }
   const size_t nc = (size_t)pl.rows_bound * G * pl.max_chunks * kList;
-  pl.cand_score_bytes = align_up(nc * sizeof(float));
-  pl.cand_idx_bytes = align_up(nc * sizeof(int32_t));
-  pl.workspace_bytes = pl.scan_wgs > 0 ? pl.cand_score_bytes + pl.cand_idx_bytes : 0;
+  pl.cand_bytes = align_up(nc * sizeof(uint64_t));
+  pl.workspace_bytes = pl.scan_wgs > 0 ? pl.cand_bytes : 0;
   return pl;
 }
 

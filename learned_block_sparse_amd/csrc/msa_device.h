@@ -26,6 +26,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kBlock = 128;    // key block size (tokens)
@@ -115,6 +116,72 @@ __device__ __forceinline__ void list_insert(float (&ls)[kList], int (&li)[kList]
     li[j] = ni;
   }
   if (gt[0]) { ls[0] = v; li[0] = c; }
+}
+
+// Insert (v, c) into a list kept sorted by `precedes` when it precedes the
+// last entry (for candidates arriving in any order).
+__device__ __forceinline__ void list_insert_ordered(float (&ls)[kList], int (&li)[kList], float v, int c) {
+  if (!precedes(v, c, ls[kList - 1], li[kList - 1])) return;
+  bool pr[kList];
+#pragma unroll
+  for (int j = 0; j < kList; ++j) pr[j] = precedes(v, c, ls[j], li[j]);
+#pragma unroll
+  for (int j = kList - 1; j > 0; --j) {
+    float ns = pr[j - 1] ? ls[j - 1] : (pr[j] ? v : ls[j]);
+    int ni = pr[j - 1] ? li[j - 1] : (pr[j] ? c : li[j]);
+    ls[j] = ns;
+    li[j] = ni;
+  }
+  if (pr[0]) { ls[0] = v; li[0] = c; }
+}
+
+// 64-bit selection key: the score's bits mapped to an order-preserving
+// unsigned integer in the high word, the inverted block id in the low word, so
+// a larger key precedes in the selection order (higher score, then lower id).
+// Every finite score maps to a non-zero high word; 0 is "no entry".
+__device__ __forceinline__ uint64_t sel_key(float s, int id) {
+  const uint32_t b = __float_as_uint(s);
+  const uint32_t hi = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)hi << 32) | (uint32_t)(0xffffffffu - (uint32_t)id);
+}
+__device__ __forceinline__ int sel_key_id(uint64_t k) { return (int)(0xffffffffu - (uint32_t)k); }
+
+// Insert a key into a descending list of 16 keys when it beats the last one.
+__device__ __forceinline__ void key_insert(uint64_t (&kl)[16], uint64_t v) {
+  if (!(v > kl[15])) return;
+  bool gt[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) gt[j] = v > kl[j];
+#pragma unroll
+  for (int j = 15; j > 0; --j) kl[j] = gt[j - 1] ? kl[j - 1] : (gt[j] ? v : kl[j]);
+  if (gt[0]) kl[0] = v;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, kWave);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Merge the descending 16-key lists of lanes l and l ^ m: every lane ends
+// with the top 16 of the union, descending.  Elementwise max against the
+// partner's reversed list keeps the top half (a bitonic sequence), which a
+// 4-stage bitonic half-cleaner network sorts.
+__device__ __forceinline__ void key_merge_xor(uint64_t (&kl)[16], int m) {
+  uint64_t other[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) other[j] = shfl_xor_u64(kl[j], m);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) kl[j] = kl[j] > other[15 - j] ? kl[j] : other[15 - j];
+#pragma unroll
+  for (int d = 8; d >= 1; d >>= 1)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if ((j & d) == 0) {
+        const uint64_t x = kl[j], y = kl[j + d];
+        kl[j] = x > y ? x : y;
+        kl[j + d] = x > y ? y : x;
+      }
 }
 
 // Remove the head of a list (shift left), padding with an invalid entry.

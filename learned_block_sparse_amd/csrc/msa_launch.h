@@ -21,8 +21,7 @@ struct IndexPlan {
   int chunk = 1;             // key blocks per scan workgroup
   int max_chunks = 1;        // key chunks per query block (<= 64)
   int64_t scan_wgs = 0;
-  size_t cand_score_bytes = 0;
-  size_t cand_idx_bytes = 0;
+  size_t cand_bytes = 0;     // [chunks][15][rows * G] 64-bit selection keys
   // decode scan
   int dec_blocks_per_wave = 0;
   int dec_wgs_per_seq = 0;

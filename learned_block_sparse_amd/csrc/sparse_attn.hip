@@ -158,13 +158,16 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs a
       }
 
       // ---- online softmax (log2 units)
+      // causal limit inside the block: key offsets above `lim` are masked
+      const int64_t rel = p - key0 - 4 * a;
+      const int lim = (!causal || rel > kBlock) ? kBlock : (int)rel;
       float mb = -__builtin_inff();
 #pragma unroll
       for (int kt = 0; kt < kBlock / 16; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float x = st[kt][r] * args.scale_log2;
-          if (causal && key0 + 16 * kt + 4 * a + r > p) x = -__builtin_inff();
+          if (16 * kt + r > lim) x = -__builtin_inff();
           st[kt][r] = x;
           mb = fmaxf(mb, x);
         }

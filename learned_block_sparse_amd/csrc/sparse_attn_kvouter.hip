@@ -73,15 +73,6 @@ __device__ __forceinline__ int kvo_find(const int32_t* cu, int n, int64_t x) {
   return lo;
 }
 
-// A selection entry is attended when it names a block at or before the local
-// block and does not repeat an earlier entry of the same row (Sel is a set).
-__device__ __forceinline__ bool kvo_entry_valid(const int32_t* sel, int i, int c, int64_t local, int nb_max) {
-  if (c < 0 || c > local || c >= nb_max) return false;
-  for (int j = 0; j < i; ++j)
-    if (sel[j] == c) return false;
-  return true;
-}
-
 struct RowInfo {
   int b;
   int64_t p;
@@ -101,26 +92,77 @@ __global__ __launch_bounds__(256) void kvo_zero(int32_t* counts, int n) {
   if (i < n) counts[i] = 0;
 }
 
-template <bool kScatter>
-__global__ __launch_bounds__(256) void kvo_bucket(KvoArgs a) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int per_row = a.G * a.topk;
-  if (e >= (a.row_hi - a.row_lo) * per_row) return;
-  const int64_t t = a.row_lo + e / per_row;
-  if (t >= a.cu_q[a.batch]) return;
-  const int g = (int)((e / a.topk) % a.G);
-  const int i = (int)(e % a.topk);
-  const int32_t* sel = a.block_idx + (t * a.G + g) * a.topk;
-  const int c = sel[i];
-  const RowInfo ri = kvo_row(a, t);
-  if (ri.p < 0 || !kvo_entry_valid(sel, i, c, ri.p / kBlock, a.nb_max)) return;
-  const int bucket = (ri.b * a.G + g) * a.nb_max + c;
-  if (kScatter) {
-    const int pos = atomicAdd(&a.cursor[bucket], 1);
-    a.edges[pos] = (int32_t)(((t - a.row_lo) << 4) | i);
-  } else {
-    atomicAdd(&a.counts[bucket], 1);
+// Validity of the (up to 16) entries of one selection row, as a bit mask: an
+// entry is attended when it names a block at or before the local block and
+// does not repeat an earlier entry of the row (Sel is a set).
+__device__ __forceinline__ unsigned kvo_row_mask(const int32_t* sel, int topk, int64_t local, int nb_max,
+                                                 int (&c)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c[i] = i < topk ? sel[i] : -1;
+  unsigned mask = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    bool ok = c[i] >= 0 && c[i] <= local && c[i] < nb_max;
+#pragma unroll
+    for (int j = 0; j < i; ++j) ok = ok && (c[j] != c[i]);
+    mask |= ok ? (1u << i) : 0u;
   }
+  return mask;
+}
+
+// Count the edges per (sequence, group, block) bucket, or place them.  One
+// thread per (row, group).  When the buckets fit in LDS, a workgroup first
+// aggregates its 256 rows' edges there (the 64 rows of a query block share
+// their local block, so this removes most same-address global atomics), then
+// issues one global atomic per non-empty bucket; in the placing pass that
+// atomic reserves the workgroup's range of the bucket's list.
+constexpr int kLdsBuckets = 8192;
+
+template <bool kScatter>
+__global__ __launch_bounds__(256) void kvo_bucket(KvoArgs a, int nbk) {
+  __shared__ int s_cnt[kLdsBuckets];
+  __shared__ int s_base[kScatter ? kLdsBuckets : 1];
+  const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t t = a.row_lo + item / a.G;
+  const int g = (int)(item % a.G);
+  bool live = item < (a.row_hi - a.row_lo) * a.G && t < a.cu_q[a.batch];
+  unsigned mask = 0;
+  int c[16];
+  int base = 0;
+  if (live) {
+    const RowInfo ri = kvo_row(a, t);
+    if (ri.p >= 0) {
+      mask = kvo_row_mask(a.block_idx + (t * a.G + g) * a.topk, a.topk, ri.p / kBlock, a.nb_max, c);
+      base = (ri.b * a.G + g) * a.nb_max;
+    }
+  }
+  const int32_t code0 = (int32_t)((t - a.row_lo) << 4);
+  if (nbk > kLdsBuckets) {  // too many buckets for LDS: global atomics per edge
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (!(mask & (1u << i))) continue;
+      if (kScatter) a.edges[atomicAdd(&a.cursor[base + c[i]], 1)] = code0 | i;
+      else atomicAdd(&a.counts[base + c[i]], 1);
+    }
+    return;
+  }
+  for (int j = threadIdx.x; j < nbk; j += 256) s_cnt[j] = 0;
+  __syncthreads();
+  int rk[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) rk[i] = (mask & (1u << i)) ? atomicAdd(&s_cnt[base + c[i]], 1) : 0;
+  __syncthreads();
+  for (int j = threadIdx.x; j < nbk; j += 256) {
+    const int n = s_cnt[j];
+    if (n == 0) continue;
+    if (kScatter) s_base[j] = atomicAdd(&a.cursor[j], n);
+    else atomicAdd(&a.counts[j], n);
+  }
+  if (!kScatter) return;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (mask & (1u << i)) a.edges[s_base[base + c[i]] + rk[i]] = code0 | i;
 }
 
 // Exclusive scans of the edge counts and of the chunk counts, one workgroup.
@@ -230,20 +272,28 @@ __global__ __launch_bounds__(kKvoThreads, 2) void kvo_attn(KvoArgs a) {
   const int jq = col >> 4, h = col & 15;
   const int R = a.Hq / a.G;
 
-  for (int e = e_lo + 2 * wave; e < e_hi; e += 2 * (kKvoThreads / kWave)) {
-    const bool has = e + jq < e_hi;
-    const int code = a.edges[has ? e + jq : e];
+  // Pairs of edges per wave; the next pair's edge codes and Q fragments are
+  // fetched while the current pair's PV MFMAs run.
+  constexpr int kPairStride = 2 * (kKvoThreads / kWave);
+  int e = e_lo + 2 * wave;
+  // B operand Q^T: column (jq, h), slots d = 16*ks + 8*a32 .. +7
+  bf16x8 qf[kHeadDim / 16];
+  int code = 0;
+  bool has = false;
+  if (e < e_hi) {
+    has = e + jq < e_hi;
+    code = a.edges[has ? e + jq : e];
+    const bool ok = has && h < R;
+    const bf16* qp = a.q + ((a.row_lo + (code >> 4)) * a.Hq + g * R + (ok ? h : 0)) * kHeadDim + 8 * a32;
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 16; ++ks) qf[ks] = ok ? load8(qp + 16 * ks) : zero8<bf16>();
+  }
+  for (; e < e_hi; e += kPairStride) {
     const int64_t trel = code >> 4;
     const int slot_i = code & 15;
     const int64_t t = a.row_lo + trel;
     const int64_t p = (int64_t)N - M + (t - q0);
     const bool colok = has && h < R;
-
-    // B operand Q^T: column (jq, h), slots d = 16*ks + 8*a32 .. +7
-    bf16x8 qf[kHeadDim / 16];
-    const bf16* qp = a.q + (t * a.Hq + g * R + (colok ? h : 0)) * kHeadDim + 8 * a32;
-#pragma unroll
-    for (int ks = 0; ks < kHeadDim / 16; ++ks) qf[ks] = colok ? load8(qp + 16 * ks) : zero8<bf16>();
 
     // S^T[key][col] for the 128 keys: 4 tiles of 32 keys
     f32x16 st[kBlock / 32];
@@ -258,15 +308,17 @@ __global__ __launch_bounds__(kKvoThreads, 2) void kvo_attn(KvoArgs a) {
     }
 
     // softmax over the block, per column (the other half of the keys sits in lane ^ 32)
-    const int64_t key0 = (int64_t)c * kBlock;
-    const bool causal = key0 + kBlock - 1 > p;
+    // causal limit inside the block: key offsets above `lim` are masked
+    // (lim >= 127 - 4*a32 means nothing in this lane is masked)
+    const int64_t rel = p - (int64_t)c * kBlock - 4 * a32;
+    const int lim = rel > kBlock ? kBlock : (int)rel;
     float mx = -__builtin_inff();
 #pragma unroll
     for (int kt = 0; kt < kBlock / 32; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float x = st[kt][r] * a.scale_log2;
-        if (causal && key0 + 32 * kt + 8 * (r >> 2) + 4 * a32 + (r & 3) > p) x = -__builtin_inff();
+        if (32 * kt + 8 * (r >> 2) + (r & 3) > lim) x = -__builtin_inff();
         st[kt][r] = x;
         mx = fmaxf(mx, x);
       }
@@ -289,6 +341,21 @@ __global__ __launch_bounds__(kKvoThreads, 2) void kvo_attn(KvoArgs a) {
     for (int kk = 0; kk < kBlock / 16; ++kk)
 #pragma unroll
       for (int i = 0; i < 8; ++i) pb[kk][i] = bf16(st[kk >> 1][8 * (kk & 1) + i]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // prefetch the next pair (qf is free once S^T is done)
+    const int en = e + kPairStride;
+    bool has_n = false;
+    int code_n = 0;
+    if (en < e_hi) {
+      has_n = en + jq < e_hi;
+      code_n = a.edges[has_n ? en + jq : en];
+      const bool ok = has_n && h < R;
+      const bf16* qp = a.q + ((a.row_lo + (code_n >> 4)) * a.Hq + g * R + (ok ? h : 0)) * kHeadDim + 8 * a32;
+#pragma unroll
+      for (int ks = 0; ks < kHeadDim / 16; ++ks) qf[ks] = ok ? load8(qp + 16 * ks) : zero8<bf16>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     const float inv = 1.0f / sum;
     const int64_t slot = (trel * a.G + g) * a.topk + slot_i;
@@ -323,11 +390,14 @@ __global__ __launch_bounds__(kKvoThreads, 2) void kvo_attn(KvoArgs a) {
       }
     }
     if (colok && a32 == 0) a.part_lse[slot * kRmax + h] = mx * 0.69314718055994530942f + logf(sum);
+    code = code_n;
+    has = has_n;
   }
 }
 
 // Fixed-order LSE combine of the selection slots: one wave per (row, group);
-// lane = (head lane/4, 32 dims at 32*(lane%4)).
+// lane = (head lane/4, 32 dims at 32*(lane%4)).  The row's selection and slot
+// LSEs are read once; the partial loads of all slots are independent.
 __global__ __launch_bounds__(256) void kvo_combine(KvoArgs a) {
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= (a.row_hi - a.row_lo) * a.G) return;
@@ -340,36 +410,45 @@ __global__ __launch_bounds__(256) void kvo_combine(KvoArgs a) {
   const int R = a.Hq / a.G;
   if (h >= R) return;
   const RowInfo ri = kvo_row(a, t);
-  const int32_t* sel = a.block_idx + (t * a.G + g) * a.topk;
-  const int64_t local = ri.p >= 0 ? ri.p / kBlock : -1;
+  int c[16];
+  const unsigned mask = ri.p >= 0 ? kvo_row_mask(a.block_idx + (t * a.G + g) * a.topk, a.topk, ri.p / kBlock,
+                                                 a.nb_max, c)
+                                  : 0u;
   const int64_t slot0 = (trel * a.G + g) * a.topk;
-  float mx = -__builtin_inff();
-  for (int i = 0; i < a.topk; ++i)
-    if (kvo_entry_valid(sel, i, sel[i], local, a.nb_max)) mx = fmaxf(mx, a.part_lse[(slot0 + i) * kRmax + h]);
   bf16* out = a.out + (t * a.Hq + g * R + h) * kHeadDim + d0;
-  if (mx == -__builtin_inff()) {
+  float ls[16];
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    ls[i] = (mask & (1u << i)) ? a.part_lse[(slot0 + i) * kRmax + h] : -__builtin_inff();
+    mx = fmaxf(mx, ls[i]);
+  }
+  if (mask == 0u) {
 #pragma unroll
     for (int j = 0; j < 32; j += 4) *reinterpret_cast<bf16x4*>(out + j) = bf16x4{bf16(0.f), bf16(0.f), bf16(0.f), bf16(0.f)};
     if (a.lse && (lane & 3) == 0) a.lse[t * a.Hq + g * R + h] = -__builtin_inff();
     return;
   }
   float sum = 0.f;
-  for (int i = 0; i < a.topk; ++i)
-    if (kvo_entry_valid(sel, i, sel[i], local, a.nb_max)) sum += expf(a.part_lse[(slot0 + i) * kRmax + h] - mx);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sum += (mask & (1u << i)) ? expf(ls[i] - mx) : 0.f;
   const float L = mx + logf(sum);
   float acc[32];
 #pragma unroll
   for (int j = 0; j < 32; ++j) acc[j] = 0.f;
-  for (int i = 0; i < a.topk; ++i) {
-    if (!kvo_entry_valid(sel, i, sel[i], local, a.nb_max)) continue;
-    const float wgt = expf(a.part_lse[(slot0 + i) * kRmax + h] - L);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (!(mask & (1u << i))) continue;
+    const float wgt = expf(ls[i] - L);
     const bf16* src = a.part_o + ((slot0 + i) * kRmax + h) * kHeadDim + d0;
+    bf16x8 v8[4];
 #pragma unroll
-    for (int j = 0; j < 32; j += 8) {
-      const bf16x8 v8 = load8(src + j);
+    for (int j = 0; j < 4; ++j)
+      v8[j] = load8(src + 8 * j);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc[j + u] += wgt * (float)v8[u];
-    }
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[8 * j + u] += wgt * (float)v8[j][u];
   }
 #pragma unroll
   for (int j = 0; j < 32; j += 4)
@@ -406,11 +485,11 @@ hipError_t launch_attn_kvouter(const AttnPlan& pl, const AttnArgs& x, void* ws, 
     a.row_lo = r0;
     a.row_hi = r0 + pl.kvo_window < pl.rows_bound ? r0 + pl.kvo_window : pl.rows_bound;
     const int64_t entries = (a.row_hi - a.row_lo) * a.G * a.topk;
-    const unsigned eg = (unsigned)((entries + 255) / 256);
+    const unsigned eg = (unsigned)(((a.row_hi - a.row_lo) * a.G + 255) / 256);
     hipLaunchKernelGGL(kvo_zero, dim3((unsigned)((nbk + 255) / 256)), dim3(256), 0, st, a.counts, nbk);
-    hipLaunchKernelGGL(kvo_bucket<false>, dim3(eg), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(kvo_bucket<false>, dim3(eg), dim3(256), 0, st, a, nbk);
     hipLaunchKernelGGL(kvo_scan, dim3(1), dim3(1024), 0, st, a, nbk);
-    hipLaunchKernelGGL(kvo_bucket<true>, dim3(eg), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(kvo_bucket<true>, dim3(eg), dim3(256), 0, st, a, nbk);
     const int64_t ub = entries / kKvoChunk + (entries < nbk ? entries : nbk) + 1;
     hipLaunchKernelGGL(kvo_attn, dim3((unsigned)ub), dim3(kKvoThreads), 0, st, a);
     const int64_t items = (a.row_hi - a.row_lo) * a.G;
