@@ -178,12 +178,12 @@ def main():
         dom_ms = float(np.mean(per_call_idx))
         dom_flops = idx_flops / len(calls)
         kernel = "idx_scan_prefill<bf16,128> + idx_merge_prefill (one msa_index_topk call)"
-        traffic = traffic_record("idx_scan_prefill_128k")
+        traffic = traffic_record("index_prefill_128k")
     else:
         dom_ms = float(np.mean(per_call_att))
         dom_flops = att_flops / len(calls)
         kernel = "kvo_attn + kvo_combine + edge-list kernels (one msa_sparse_attn_prefill call)"
-        traffic = traffic_record("sparse_attn_fwd_128k")
+        traffic = traffic_record("attention_prefill_128k")
     achieved = dom_flops / (dom_ms / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
@@ -257,7 +257,7 @@ def main():
             "attention_us": round(d_att_us, 1), "bytes_per_step": idx_b + att_b,
             "achieved_GBs": round(gbs, 1), "peak_GBs": PEAK_HBM_GBS, "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
             "index_scan_GBs": round(idx_gbs, 1), "index_scan_frac_hbm": round(idx_gbs / PEAK_HBM_GBS, 4),
-            "index_scan_traffic": traffic_record("idx_decode_scores_1m"),
+            "index_scan_traffic": traffic_record("index_decode_1m"),
         }
         del d
         torch.cuda.empty_cache()

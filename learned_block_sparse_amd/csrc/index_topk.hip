@@ -21,9 +21,10 @@
 //                     under the same total order, adds the local block, writes
 //                     ids ascending.
 // Decode path (two kernels):
-//   idx_decode_scores streams the index-key cache once: each wave scores a run
-//                     of blocks for all groups of its sequence (16x16 MFMA,
-//                     keys x groups) and writes one fp32 per (group, block).
+//   idx_decode_scores streams the index-key cache once: the earlier blocks of
+//                     all sequences are one flat range scored grid-stride by
+//                     waves (16x16 MFMA, keys x groups), one fp32 per (group,
+//                     block).
 //   idx_decode_select one workgroup per (sequence, group): per-thread register
 //                     lists, then two wave merges.
 #include "msa_device.h"
@@ -252,40 +253,53 @@ __global__ __launch_bounds__(256) void idx_merge_prefill(
 // --------------------------------------------------------------------------
 // Decode: stream the index-key cache once, one fp32 score per (group, block)
 // --------------------------------------------------------------------------
+// Earlier-block counts per sequence, as exclusive prefix sums (one workgroup).
+__global__ __launch_bounds__(256) void idx_decode_prefix(const int32_t* __restrict__ cu_q,
+                                                         const int32_t* __restrict__ cu_k, int batch,
+                                                         int32_t* __restrict__ blk_off) {
+  if (threadIdx.x != 0) return;
+  int acc = 0;
+  for (int b = 0; b < batch; ++b) {
+    blk_off[b] = acc;
+    const int N = cu_k[b + 1] - cu_k[b];
+    if (cu_q[b + 1] - cu_q[b] == 1 && N > 0) acc += (N - 1) / kBlock;
+  }
+  blk_off[batch] = acc;
+}
+
+// The earlier blocks of all sequences form one flat range; wave w scores
+// blocks w, w + W, w + 2W, ... so the waves running at any moment read
+// neighbouring 32 KB runs of the cache (copy-like DRAM locality).  Each block
+// is scored for all groups at once: 16x16 MFMA, keys x groups.
 template <typename T, int DI>
 __global__ __launch_bounds__(256) void idx_decode_scores(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ cu_k, int G, int nb_max, int blocks_per_wave, int wgs_per_seq,
+    const int32_t* __restrict__ cu_k, const int32_t* __restrict__ blk_off, int batch, int G, int nb_max,
     float* __restrict__ scores) {
   constexpr int DS = DI / 32;  // 32-wide contraction steps of the 16x16 MFMA
-  const int b = blockIdx.x / wgs_per_seq;
-  const int wchunk = (blockIdx.x % wgs_per_seq) * 4 + threadIdx.x / kWave;
   const int lane = lane_id();
-  const int q0 = cu_q[b];
-  if (cu_q[b + 1] - q0 != 1) return;
-  const int k0 = cu_k[b], N = cu_k[b + 1] - k0;
-  if (N <= 0) return;
-  const int local = (N - 1) / kBlock;
-  const int c_lo = wchunk * blocks_per_wave;
-  const int c_hi = min(c_lo + blocks_per_wave, local);
-  if (c_lo >= c_hi) return;
-
-  // B operand: columns are the groups (lane%16 < G), slots 32*ds + 8*(lane/16).
+  const int nwaves = gridDim.x * 4;
+  const int total = blk_off[batch];
   const int gcol = lane & 15;
-  frag8<T> qf[DS];
+  for (int gb = blockIdx.x * 4 + threadIdx.x / kWave; gb < total; gb += nwaves) {
+    const int b = find_seq(blk_off, batch, gb);
+    const int c = gb - blk_off[b];
+    const int q0 = cu_q[b];
+    // B operand: columns are the groups (lane%16 < G), slots 32*ds + 8*(lane/16).
+    frag8<T> qf[DS];
 #pragma unroll
-  for (int ds = 0; ds < DS; ++ds)
-    qf[ds] = gcol < G ? load8(q_idx + ((int64_t)q0 * G + gcol) * DI + 32 * ds + 8 * (lane >> 4))
-                      : zero8<T>();
-
-  const T* kbase = k_idx + ((int64_t)k0 + (lane & 15)) * DI + 8 * (lane >> 4);
-  for (int c = c_lo; c < c_hi; ++c) {
-    const T* kb = kbase + (int64_t)c * kBlock * DI;
+    for (int ds = 0; ds < DS; ++ds)
+      qf[ds] = gcol < G ? load8(q_idx + ((int64_t)q0 * G + gcol) * DI + 32 * ds + 8 * (lane >> 4))
+                        : zero8<T>();
+    const T* kb = k_idx + ((int64_t)cu_k[b] + (int64_t)c * kBlock + (lane & 15)) * DI + 8 * (lane >> 4);
     frag8<T> a[kBlock / 16][DS];
 #pragma unroll
     for (int kt = 0; kt < kBlock / 16; ++kt)
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) a[kt][ds] = load8(kb + (int64_t)kt * 16 * DI + 32 * ds);
+    // keep the whole block's loads in flight together before the MFMAs (the
+    // scheduler would otherwise interleave them and starve the memory system)
+    __builtin_amdgcn_sched_barrier(0);
     float m = -__builtin_inff();
 #pragma unroll
     for (int kt = 0; kt < kBlock / 16; ++kt) {
@@ -325,7 +339,20 @@ __global__ __launch_bounds__(kSelThreads) void idx_decode_select(
   int li[kList];
 #pragma unroll
   for (int j = 0; j < kList; ++j) { ls[j] = -__builtin_inff(); li[j] = -1; }
-  for (int c = threadIdx.x; c < local; c += kSelThreads) list_insert(ls, li, sc[c], c);
+  // ascending ids per thread (strided), fetched 8 at a time so the loads overlap
+  for (int c0 = threadIdx.x; c0 < local; c0 += 8 * kSelThreads) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + u * kSelThreads;
+      v[u] = c < local ? sc[c] : -__builtin_inff();
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + u * kSelThreads;
+      if (c < local) list_insert(ls, li, v[u], c);
+    }
+  }
 
   int mine;
   const int found = wave_merge(ls, li, kList, mine);
@@ -374,13 +401,13 @@ static hipError_t launch_index_decode(const IndexPlan& pl, const void* q_idx, co
                                       const int32_t* cu_q, const int32_t* cu_k, int batch, int G,
                                       int topk, int32_t* block_idx, char* ws, hipStream_t st) {
   float* scores = reinterpret_cast<float*>(ws);
-  if (pl.dec_wgs_per_seq > 0) {
-    hipLaunchKernelGGL((idx_decode_scores<T, DI>), dim3((unsigned)(batch * pl.dec_wgs_per_seq)), dim3(256), 0,
-                       st, static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), cu_q, cu_k, G,
-                       pl.nb_max, pl.dec_blocks_per_wave, pl.dec_wgs_per_seq, scores);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  int32_t* blk_off = reinterpret_cast<int32_t*>(ws + pl.score_bytes);
+  hipLaunchKernelGGL(idx_decode_prefix, dim3(1), dim3(256), 0, st, cu_q, cu_k, batch, blk_off);
+  hipLaunchKernelGGL((idx_decode_scores<T, DI>), dim3((unsigned)pl.dec_wgs), dim3(256), 0, st,
+                     static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), cu_q, cu_k, blk_off, batch, G,
+                     pl.nb_max, scores);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(idx_decode_select, dim3((unsigned)(batch * G)), dim3(kSelThreads), 0, st, cu_q, cu_k, G,
                      topk, pl.nb_max, scores, block_idx);
   return hipGetLastError();

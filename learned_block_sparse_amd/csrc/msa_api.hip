@@ -29,15 +29,14 @@ IndexPlan plan_index(int batch, int max_q_len, int max_kv_len, int G) {
   pl.rows_bound = (int64_t)batch * max_q_len;
   pl.decode = (max_q_len == 1);
   if (pl.decode) {
+    // grid-stride waves over all earlier blocks: enough to fill the GPU, no
+    // more than there are blocks
     const int64_t total_blocks = (int64_t)batch * pl.nb_max;
-    int64_t bpw = ceil_div(total_blocks, kDecodeTargetWaves);
-    if (bpw < 1) bpw = 1;
-    if (bpw > 64) bpw = 64;
-    pl.dec_blocks_per_wave = (int)bpw;
-    const int64_t waves_per_seq = ceil_div(pl.nb_max, bpw);
-    pl.dec_wgs_per_seq = (int)ceil_div(waves_per_seq, 4);
+    int64_t waves = total_blocks < kDecodeTargetWaves ? total_blocks : kDecodeTargetWaves;
+    if (waves < 4) waves = 4;
+    pl.dec_wgs = (int)ceil_div(waves, 4);
     pl.score_bytes = align_up((size_t)batch * G * pl.nb_max * sizeof(float));
-    pl.workspace_bytes = pl.score_bytes;
+    pl.workspace_bytes = pl.score_bytes + align_up((size_t)(batch + 1) * sizeof(int32_t));
     return pl;
   }
   pl.qw = 512 / G < kBlock ? 512 / G : kBlock;

@@ -23,8 +23,7 @@ struct IndexPlan {
   int64_t scan_wgs = 0;
   size_t cand_bytes = 0;     // [chunks][15][rows * G] 64-bit selection keys
   // decode scan
-  int dec_blocks_per_wave = 0;
-  int dec_wgs_per_seq = 0;
+  int dec_wgs = 0;           // workgroups (4 waves) of the grid-stride decode scan
   size_t score_bytes = 0;
   size_t workspace_bytes = 0;
 };

@@ -204,6 +204,121 @@ __global__ __launch_bounds__(1024) void kvo_scan(KvoArgs a, int nbk) {
   }
 }
 
+struct PairQ {
+  bf16x8 q[kHeadDim / 16];  // B operand Q^T: column (jq, h), slots d = 16*ks + 8*a32 .. +7
+  int code;                 // (row in window) << 4 | selection slot
+  bool has;                 // this lane's column holds an edge
+};
+
+__device__ __forceinline__ void kvo_load_pair(const KvoArgs& a, PairQ& P, int e, int e_hi, int jq, int h, int a32,
+                                              int g, int R) {
+  P.has = false;
+  P.code = 0;
+  if (e >= e_hi) return;
+  P.has = e + jq < e_hi;
+  P.code = a.edges[P.has ? e + jq : e];
+  const bool ok = P.has && h < R;
+  const bf16* qp = a.q + ((a.row_lo + (P.code >> 4)) * a.Hq + g * R + (ok ? h : 0)) * kHeadDim + 8 * a32;
+#pragma unroll
+  for (int ks = 0; ks < kHeadDim / 16; ++ks) P.q[ks] = ok ? load8(qp + 16 * ks) : zero8<bf16>();
+}
+
+// One pair of edges (two queries x 16 heads) against the staged block; while
+// the PV MFMAs run, P is refilled with the pair at e_pf.
+__device__ __forceinline__ void kvo_pair(const KvoArgs& a, PairQ& P, int e_pf, int e_hi, const bf16* k_lds,
+                                         const bf16* vt_lds, int c, int g, int R, int N, int M, int64_t q0,
+                                         int col, int a32, int jq, int h) {
+  const int64_t p = (int64_t)N - M + (a.row_lo + (P.code >> 4) - q0);
+    // S^T[key][col] for the 128 keys: 4 tiles of 32 keys
+    f32x16 st[kBlock / 32];
+#pragma unroll
+    for (int kt = 0; kt < kBlock / 32; ++kt) {
+      st[kt] = f32x16{};
+      const bf16* arow = k_lds + (32 * kt + col) * kKStride + 8 * a32;
+#pragma unroll
+      for (int ks = 0; ks < kHeadDim / 16; ++ks)
+        st[kt] = mma32(*reinterpret_cast<const bf16x8*>(arow + 16 * ks), P.q[ks], st[kt]);
+      __builtin_amdgcn_sched_barrier(0);  // keep each tile's LDS reads next to its MFMAs
+    }
+
+    // softmax over the block, per column (the other half of the keys sits in lane ^ 32)
+    // causal limit inside the block: key offsets above `lim` are masked
+    // (lim >= 127 - 4*a32 means nothing in this lane is masked)
+    const int64_t rel = p - (int64_t)c * kBlock - 4 * a32;
+    const int lim = rel > kBlock ? kBlock : (int)rel;
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kt = 0; kt < kBlock / 32; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = st[kt][r] * a.scale_log2;
+        if (32 * kt + 8 * (r >> 2) + (r & 3) > lim) x = -__builtin_inff();
+        st[kt][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    float sum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < kBlock / 32; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float ex = __builtin_amdgcn_exp2f(st[kt][r] - mx);
+        st[kt][r] = ex;
+        sum += ex;
+      }
+    sum += shfl_xor_f(sum, 32);
+
+    // P^T as bf16 B operands: k-step kk covers keys 32*kt + 16*m + 8*(i/4) + 4*a32 + i%4
+    // (kt = kk/2, m = kk%2), which are exactly this lane's S^T registers 8m .. 8m+7.
+    bf16x8 pb[kBlock / 16];
+#pragma unroll
+    for (int kk = 0; kk < kBlock / 16; ++kk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[kk][i] = bf16(st[kk >> 1][8 * (kk & 1) + i]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // qf is free once S^T is done: fetch the pair two steps ahead into it
+    const int64_t trel = P.code >> 4;
+    const int slot_i = P.code & 15;
+    const bool colok = P.has && h < R;
+    kvo_load_pair(a, P, e_pf, e_hi, jq, h, a32, g, R);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const float inv = 1.0f / sum;
+    const int64_t slot = (trel * a.G + g) * a.topk + slot_i;
+    bf16* po = a.part_o + (slot * kRmax + h) * kHeadDim;
+    // O^T[d][col] = V^T[d][key] P^T[key][col], 32 dims at a time
+#pragma unroll
+    for (int dt = 0; dt < kHeadDim / 32; ++dt) {
+      f32x16 o = {};
+#pragma unroll
+      for (int kk = 0; kk < kBlock / 16; ++kk) {
+        const int kb1 = 32 * (kk >> 1) + 16 * (kk & 1) + 4 * a32;
+        // A operand V^T: row d = 32*dt + lane%32, keys kb1 .. kb1+3 and kb1+8 .. kb1+11
+        const bf16* src = vt_lds + (32 * dt + col) * kVtStride + kb1;
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src + 8);
+        bf16x8 va;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          va[i] = lo[i];
+          va[4 + i] = hi[i];
+        }
+        o = mma32(va, pb[kk], o);
+        if (kk & 1) __builtin_amdgcn_sched_barrier(0);
+      }
+      if (colok) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          bf16x4 wv = {bf16(o[4 * qd] * inv), bf16(o[4 * qd + 1] * inv), bf16(o[4 * qd + 2] * inv),
+                       bf16(o[4 * qd + 3] * inv)};
+          *reinterpret_cast<bf16x4*>(po + 32 * dt + 8 * qd + 4 * a32) = wv;
+        }
+      }
+    }
+    if (colok && a32 == 0) a.part_lse[slot * kRmax + h] = mx * 0.69314718055994530942f + logf(sum);
+}
+
 __global__ __launch_bounds__(kKvoThreads, 2) void kvo_attn(KvoArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 k_lds[kBlock * kKStride];
   __shared__ __attribute__((aligned(16))) bf16 vt_lds[kHeadDim * kVtStride];
@@ -272,126 +387,17 @@ __global__ __launch_bounds__(kKvoThreads, 2) void kvo_attn(KvoArgs a) {
   const int jq = col >> 4, h = col & 15;
   const int R = a.Hq / a.G;
 
-  // Pairs of edges per wave; the next pair's edge codes and Q fragments are
-  // fetched while the current pair's PV MFMAs run.
+  // Pairs of edges per wave, software-pipelined two pairs deep: the Q
+  // fragments of pair i+2 load while pair i runs its PV MFMAs.
   constexpr int kPairStride = 2 * (kKvoThreads / kWave);
-  int e = e_lo + 2 * wave;
-  // B operand Q^T: column (jq, h), slots d = 16*ks + 8*a32 .. +7
-  bf16x8 qf[kHeadDim / 16];
-  int code = 0;
-  bool has = false;
-  if (e < e_hi) {
-    has = e + jq < e_hi;
-    code = a.edges[has ? e + jq : e];
-    const bool ok = has && h < R;
-    const bf16* qp = a.q + ((a.row_lo + (code >> 4)) * a.Hq + g * R + (ok ? h : 0)) * kHeadDim + 8 * a32;
-#pragma unroll
-    for (int ks = 0; ks < kHeadDim / 16; ++ks) qf[ks] = ok ? load8(qp + 16 * ks) : zero8<bf16>();
-  }
-  for (; e < e_hi; e += kPairStride) {
-    const int64_t trel = code >> 4;
-    const int slot_i = code & 15;
-    const int64_t t = a.row_lo + trel;
-    const int64_t p = (int64_t)N - M + (t - q0);
-    const bool colok = has && h < R;
-
-    // S^T[key][col] for the 128 keys: 4 tiles of 32 keys
-    f32x16 st[kBlock / 32];
-#pragma unroll
-    for (int kt = 0; kt < kBlock / 32; ++kt) {
-      st[kt] = f32x16{};
-      const bf16* arow = k_lds + (32 * kt + col) * kKStride + 8 * a32;
-#pragma unroll
-      for (int ks = 0; ks < kHeadDim / 16; ++ks)
-        st[kt] = mma32(*reinterpret_cast<const bf16x8*>(arow + 16 * ks), qf[ks], st[kt]);
-      __builtin_amdgcn_sched_barrier(0);  // keep each tile's LDS reads next to its MFMAs
-    }
-
-    // softmax over the block, per column (the other half of the keys sits in lane ^ 32)
-    // causal limit inside the block: key offsets above `lim` are masked
-    // (lim >= 127 - 4*a32 means nothing in this lane is masked)
-    const int64_t rel = p - (int64_t)c * kBlock - 4 * a32;
-    const int lim = rel > kBlock ? kBlock : (int)rel;
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int kt = 0; kt < kBlock / 32; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = st[kt][r] * a.scale_log2;
-        if (32 * kt + 8 * (r >> 2) + (r & 3) > lim) x = -__builtin_inff();
-        st[kt][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    float sum = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < kBlock / 32; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float ex = __builtin_amdgcn_exp2f(st[kt][r] - mx);
-        st[kt][r] = ex;
-        sum += ex;
-      }
-    sum += shfl_xor_f(sum, 32);
-
-    // P^T as bf16 B operands: k-step kk covers keys 32*kt + 16*m + 8*(i/4) + 4*a32 + i%4
-    // (kt = kk/2, m = kk%2), which are exactly this lane's S^T registers 8m .. 8m+7.
-    bf16x8 pb[kBlock / 16];
-#pragma unroll
-    for (int kk = 0; kk < kBlock / 16; ++kk)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pb[kk][i] = bf16(st[kk >> 1][8 * (kk & 1) + i]);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // prefetch the next pair (qf is free once S^T is done)
-    const int en = e + kPairStride;
-    bool has_n = false;
-    int code_n = 0;
-    if (en < e_hi) {
-      has_n = en + jq < e_hi;
-      code_n = a.edges[has_n ? en + jq : en];
-      const bool ok = has_n && h < R;
-      const bf16* qp = a.q + ((a.row_lo + (code_n >> 4)) * a.Hq + g * R + (ok ? h : 0)) * kHeadDim + 8 * a32;
-#pragma unroll
-      for (int ks = 0; ks < kHeadDim / 16; ++ks) qf[ks] = ok ? load8(qp + 16 * ks) : zero8<bf16>();
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    const float inv = 1.0f / sum;
-    const int64_t slot = (trel * a.G + g) * a.topk + slot_i;
-    bf16* po = a.part_o + (slot * kRmax + h) * kHeadDim;
-    // O^T[d][col] = V^T[d][key] P^T[key][col], 32 dims at a time
-#pragma unroll
-    for (int dt = 0; dt < kHeadDim / 32; ++dt) {
-      f32x16 o = {};
-#pragma unroll
-      for (int kk = 0; kk < kBlock / 16; ++kk) {
-        const int kb1 = 32 * (kk >> 1) + 16 * (kk & 1) + 4 * a32;
-        // A operand V^T: row d = 32*dt + lane%32, keys kb1 .. kb1+3 and kb1+8 .. kb1+11
-        const bf16* src = vt_lds + (32 * dt + col) * kVtStride + kb1;
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src + 8);
-        bf16x8 va;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          va[i] = lo[i];
-          va[4 + i] = hi[i];
-        }
-        o = mma32(va, pb[kk], o);
-        if (kk & 1) __builtin_amdgcn_sched_barrier(0);
-      }
-      if (colok) {
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          bf16x4 wv = {bf16(o[4 * qd] * inv), bf16(o[4 * qd + 1] * inv), bf16(o[4 * qd + 2] * inv),
-                       bf16(o[4 * qd + 3] * inv)};
-          *reinterpret_cast<bf16x4*>(po + 32 * dt + 8 * qd + 4 * a32) = wv;
-        }
-      }
-    }
-    if (colok && a32 == 0) a.part_lse[slot * kRmax + h] = mx * 0.69314718055994530942f + logf(sum);
-    code = code_n;
-    has = has_n;
+  const int e0 = e_lo + 2 * wave;
+  PairQ A, B;
+  kvo_load_pair(a, A, e0, e_hi, jq, h, a32, g, R);
+  kvo_load_pair(a, B, e0 + kPairStride, e_hi, jq, h, a32, g, R);
+  for (int e = e0; e < e_hi; e += 2 * kPairStride) {
+    kvo_pair(a, A, e + 2 * kPairStride, e_hi, k_lds, vt_lds, c, g, R, N, M, q0, col, a32, jq, h);
+    if (e + kPairStride >= e_hi) break;
+    kvo_pair(a, B, e + 3 * kPairStride, e_hi, k_lds, vt_lds, c, g, R, N, M, q0, col, a32, jq, h);
   }
 }
 
@@ -433,18 +439,20 @@ __global__ __launch_bounds__(256) void kvo_combine(KvoArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) sum += (mask & (1u << i)) ? expf(ls[i] - mx) : 0.f;
   const float L = mx + logf(sum);
+  // Branch-free over the 16 slots so all partial loads can be in flight at
+  // once: an unused slot reads the first used one with weight 0.
+  const int first = __builtin_ctz(mask);
   float acc[32];
 #pragma unroll
   for (int j = 0; j < 32; ++j) acc[j] = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    if (!(mask & (1u << i))) continue;
-    const float wgt = expf(ls[i] - L);
-    const bf16* src = a.part_o + ((slot0 + i) * kRmax + h) * kHeadDim + d0;
+    const bool use = (mask >> i) & 1u;
+    const float wgt = use ? expf(ls[i] - L) : 0.f;
+    const bf16* src = a.part_o + ((slot0 + (use ? i : first)) * kRmax + h) * kHeadDim + d0;
     bf16x8 v8[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      v8[j] = load8(src + 8 * j);
+    for (int j = 0; j < 4; ++j) v8[j] = load8(src + 8 * j);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll

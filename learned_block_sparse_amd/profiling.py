@@ -1,0 +1,144 @@
+"""Turn rocprofv3 counter passes into per-call HBM traffic for bench.py.
+
+Usage (on the GPU host, from the repository root, after the counter passes):
+
+    python -m learned_block_sparse_amd.profiling \
+        --prefill-fetch DIR --prefill-write DIR --decode-fetch DIR --decode-write DIR \
+        --copy-fetch DIR --copy-write DIR --copy-bytes 1073741824 --out profiles
+
+Each DIR is a ``rocprofv3 --pmc FETCH_SIZE`` (or ``WRITE_SIZE``) output
+directory holding ``*_counter_collection.csv``.  The copy passes calibrate the
+counters: a device-to-device copy of a known size reads and writes exactly
+that many bytes, so the scale factor of each counter is measured value /
+known bytes.  Per-call traffic is the sum over the kernels of one library
+call, averaged over the calls recorded; it is written to
+``profiles/traffic.json`` with the digest of the kernel sources it was taken
+on, and as a text summary.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import json
+import os
+
+# kernels of one library call, by (truncated) kernel-name prefix
+CALLS = {
+    "attention_prefill_128k": ("kvo_zero", "kvo_bucket", "kvo_scan", "kvo_attn", "kvo_combine"),
+    "index_prefill_128k": ("_ZN3msa16idx_scan_prefill", "idx_scan_prefill", "idx_merge_prefill"),
+    "index_decode_1m": ("_ZN3msa17idx_decode_scores", "idx_decode_scores", "idx_decode_select"),
+    "attention_decode_1m": ("_ZN3msa15sparse_attn_fwd", "sparse_attn_fwd", "_ZN3msa12attn_combine",
+                            "attn_combine"),
+}
+# the call's first kernel marks a new call
+CALL_START = {"attention_prefill_128k": "kvo_zero", "index_prefill_128k": "idx_scan_prefill",
+              "index_decode_1m": "idx_decode_scores", "attention_decode_1m": "sparse_attn_fwd"}
+
+
+def _rows(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return rows
+
+
+def _matches(name, prefixes):
+    return any(name.startswith(p) or p in name for p in prefixes)
+
+
+def per_call_kb(rows, call):
+    """Sum of the counter (KB) over each call's kernels, one entry per call."""
+    out, cur = [], None
+    for r in rows:
+        name = r["Kernel_Name"]
+        if not _matches(name, CALLS[call]):
+            continue
+        if CALL_START[call] in name:
+            if cur is not None:
+                out.append(cur)
+            cur = 0.0
+        if cur is not None:
+            cur += float(r["Counter_Value"])
+    if cur is not None:
+        out.append(cur)
+    return out
+
+
+def per_kernel_kb(rows):
+    agg = collections.defaultdict(list)
+    for r in rows:
+        agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def copy_factor(rows, nbytes):
+    vals = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+    big = max(vals)  # the calibration copy is the largest copy dispatch
+    return big * 1024.0 / nbytes
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    for k in ("prefill-fetch", "prefill-write", "decode-fetch", "decode-write", "copy-fetch", "copy-write"):
+        ap.add_argument("--" + k, required=True)
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--out", default="profiles")
+    ap.add_argument("--command", default="", help="the counter commands, recorded in the summary")
+    args = ap.parse_args()
+
+    from learned_block_sparse_amd import build
+    f_fetch = copy_factor(_rows(args.copy_fetch), args.copy_bytes)
+    f_write = copy_factor(_rows(args.copy_write), args.copy_bytes)
+    result, lines = {}, []
+    lines.append("# HBM traffic per library call (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated)")
+    lines.append("")
+    lines.append(f"calibration: a {args.copy_bytes} B device copy reads {f_fetch:.4f} x and writes "
+                 f"{f_write:.4f} x its size in counter units; counters are divided by these factors")
+    if args.command:
+        lines.append("commands:")
+        lines += ["  " + c for c in args.command.split(";")]
+    lines.append("")
+    sources = {"attention_prefill_128k": ("prefill-fetch", "prefill-write"),
+               "index_prefill_128k": ("prefill-fetch", "prefill-write"),
+               "index_decode_1m": ("decode-fetch", "decode-write"),
+               "attention_decode_1m": ("decode-fetch", "decode-write")}
+    digest = build.source_digest()
+    for call, (fd, wd) in sources.items():
+        fr = _rows(getattr(args, fd.replace("-", "_")))
+        wr = _rows(getattr(args, wd.replace("-", "_")))
+        fk, wk = per_call_kb(fr, call), per_call_kb(wr, call)
+        if not fk or not wk:
+            continue
+        fb = sum(fk) / len(fk) * 1024.0 / f_fetch
+        wb = sum(wk) / len(wk) * 1024.0 / f_write
+        result[call] = {"bytes_per_launch": fb + wb, "fetch_bytes": fb, "write_bytes": wb,
+                        "calls": len(fk), "source_sha": digest}
+        lines.append(f"{call:28s} calls={len(fk):3d} fetch={fb / 1e9:8.3f} GB write={wb / 1e9:8.3f} GB "
+                     f"total={(fb + wb) / 1e9:8.3f} GB per call")
+    lines.append("")
+    lines.append("per kernel (mean per dispatch, GB):")
+    for label, fd, wd in (("prefill", args.prefill_fetch, args.prefill_write),
+                          ("decode", args.decode_fetch, args.decode_write)):
+        fk, wk = per_kernel_kb(_rows(fd)), per_kernel_kb(_rows(wd))
+        for name in sorted(fk):
+            if "msa" not in name and not name.startswith(("kvo", "idx", "attn", "sparse")):
+                continue
+            lines.append(f"  {label:8s} {name[:60]:60s} fetch={fk[name] * 1024 / f_fetch / 1e9:8.4f} "
+                         f"write={wk.get(name, 0.0) * 1024 / f_write / 1e9:8.4f}")
+    lines.append(f"\nkernel source digest: {digest}")
+    os.makedirs(args.out, exist_ok=True)
+    with open(os.path.join(args.out, "traffic.json"), "w") as f:
+        json.dump(result, f, indent=1, sort_keys=True)
+    with open(os.path.join(args.out, "hbm_traffic_prefill128k_decode1m.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()
