@@ -128,17 +128,26 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
         stage[u] = *reinterpret_cast<const u32x4*>(kseq + (s + 1) * kBlockBytes + (threadIdx.x + u * kScanThreads) * 16);
     }
     if (active) {
-      const char* kb = lds + buf * L::kBufBytes;
+      const char* kb = lds + buf * L::kBufBytes + (lane & 31) * L::kRowBytes + 8 * (lane >> 5) * (int)sizeof(T);
       float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+      // A operand (K rows) in two register sets: key tile kt+1 is read from
+      // LDS while tile kt's MFMAs run, so LDS latency overlaps the MFMAs.
+      frag8<T> kf[2][KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[0][ks] = *reinterpret_cast<const frag8<T>*>(kb + 16 * ks * (int)sizeof(T));
 #pragma unroll
       for (int kt = 0; kt < kBlock / 32; ++kt) {
+        if (kt + 1 < kBlock / 32) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            kf[(kt + 1) & 1][ks] =
+                *reinterpret_cast<const frag8<T>*>(kb + 32 * (kt + 1) * L::kRowBytes + 16 * ks * (int)sizeof(T));
+        }
         f32x16 acc0 = {}, acc1 = {};
-        const char* arow = kb + (32 * kt + (lane & 31)) * L::kRowBytes + 8 * (lane >> 5) * (int)sizeof(T);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const frag8<T> a = *reinterpret_cast<const frag8<T>*>(arow + 16 * ks * (int)sizeof(T));
-          acc0 = mma32(a, qf[0][ks], acc0);
-          acc1 = mma32(a, qf[1][ks], acc1);
+          acc0 = mma32(kf[kt & 1][ks], qf[0][ks], acc0);
+          acc1 = mma32(kf[kt & 1][ks], qf[1][ks], acc1);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) { m0 = fmaxf(m0, acc0[r]); m1 = fmaxf(m1, acc1[r]); }

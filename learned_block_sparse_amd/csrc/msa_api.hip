@@ -15,7 +15,7 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Scan workgroups aimed at per launch: several per CU on 256 CUs, so the
 // triangular causal work spreads evenly.
-static constexpr int64_t kScanTargetWgs = 2048;
+static constexpr int64_t kScanTargetWgs = 1024;
 // Decode scan: waves aimed at per launch.
 static constexpr int64_t kDecodeTargetWaves = 8192;
 // Attention: work items (waves) aimed at before splitting selections.

@@ -307,12 +307,25 @@ __device__ __forceinline__ void kvo_pair(const KvoArgs& a, PairQ& P, int e_pf, i
         o = mma32(va, pb[kk], o);
         if (kk & 1) __builtin_amdgcn_sched_barrier(0);
       }
-      if (colok) {
+      // Lanes col and col+32 hold alternate 4-dim runs of the same 32 dims;
+      // swap halves so each lane stores two 16-byte runs of 8 dims.
+      u32x2 pk[4];
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          bf16x4 wv = {bf16(o[4 * qd] * inv), bf16(o[4 * qd + 1] * inv), bf16(o[4 * qd + 2] * inv),
-                       bf16(o[4 * qd + 3] * inv)};
-          *reinterpret_cast<bf16x4*>(po + 32 * dt + 8 * qd + 4 * a32) = wv;
+      for (int qd = 0; qd < 4; ++qd) {
+        bf16x4 wv = {bf16(o[4 * qd] * inv), bf16(o[4 * qd + 1] * inv), bf16(o[4 * qd + 2] * inv),
+                     bf16(o[4 * qd + 3] * inv)};
+        pk[qd] = __builtin_bit_cast(u32x2, wv);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const u32x2 mine = a32 ? pk[2 * m + 1] : pk[2 * m];   // run this lane stores
+        const u32x2 give = a32 ? pk[2 * m] : pk[2 * m + 1];   // run the partner stores
+        u32x2 got;
+        got[0] = (uint32_t)__shfl_xor((int)give[0], 32, kWave);
+        got[1] = (uint32_t)__shfl_xor((int)give[1], 32, kWave);
+        if (colok) {
+          const u32x4 run = a32 ? u32x4{got[0], got[1], mine[0], mine[1]} : u32x4{mine[0], mine[1], got[0], got[1]};
+          *reinterpret_cast<u32x4*>(po + 32 * dt + 8 * (2 * m + a32)) = run;
         }
       }
     }
