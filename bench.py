@@ -10,9 +10,12 @@ headline value is prefill tokens/s.  The same JSON line also carries one
 decode step (32 sequences, contexts uniform in [64K, 1M]: msa_index_topk on
 the decode path + msa_sparse_attn_decode) in microseconds per step.
 
-Inputs are resident in HBM before the timed region starts.  Kernel durations
-come from HIP events recorded on the stream the calls are launched on
-(torch's current stream, passed to the library).
+Inputs are resident in HBM before the timed region starts.  The timed steps
+issue nothing but the library calls (prefill: host clock between two device
+synchronisations; decode: two HIP events around the run of steps).  Per-call
+durations come from a second run of the same steps with HIP events recorded
+between the calls, on the stream the calls are launched on (torch's current
+stream, passed to the library).
 
 Roofline: algorithmic FLOPs (index: 2 * d_idx * G * Bk * l(p) per query;
 attention: 4 * D * Hq * |J| per query) per call divided by the call's mean
@@ -139,13 +142,18 @@ def main():
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in calls] for _ in range(args.steps)]
+    # the timed steps: nothing but the library calls between the two synchronisations
     t0 = time.perf_counter()
     for s in range(args.steps):
-        run_step(ev[s])
+        run_step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
+    # the per-call breakdown: the same steps again, with events around every call
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in calls] for _ in range(args.steps)]
+    for s in range(args.steps):
+        run_step(ev[s])
+    torch.cuda.synchronize()
     idx_ms = np.mean([sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for j in range(len(calls)))
                       for s in range(args.steps)])
     att_ms = np.mean([sum(ev[s][j][1].elapsed_time(ev[s][j][2]) for j in range(len(calls)))
@@ -239,15 +247,23 @@ def main():
         for _ in range(5):
             dstep()
         torch.cuda.synchronize()
-        dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.decode_steps)]
+        # steady-state step time: events only around the whole run of steps
+        e_lo, e_hi = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        e_lo.record(stream)
+        for s in range(args.decode_steps):
+            dstep()
+        e_hi.record(stream)
+        torch.cuda.synchronize()
+        dwall = (time.perf_counter() - t0) / args.decode_steps
+        d_step_us = e_lo.elapsed_time(e_hi) * 1e3 / args.decode_steps
+        # per-call breakdown from a second run with events between the calls
+        dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.decode_steps)]
         for s in range(args.decode_steps):
             dstep(dev_ev[s])
         torch.cuda.synchronize()
-        dwall = (time.perf_counter() - t0) / args.decode_steps
         d_idx_us = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_ev])) * 1e3
         d_att_us = float(np.mean([e[1].elapsed_time(e[2]) for e in dev_ev])) * 1e3
-        d_step_us = float(np.mean([e[0].elapsed_time(e[2]) for e in dev_ev])) * 1e3
         idx_b, att_b = workmodel.decode_bytes(ctx, Hq, G, D, DI, wd.block_size, wd.topk)
         gbs = (idx_b + att_b) / (d_step_us * 1e-6) / 1e9
         idx_gbs = idx_b / (d_idx_us * 1e-6) / 1e9

@@ -128,7 +128,9 @@ msa_status_t msa_index_topk(const void* q_idx, const void* k_idx, msa_dtype_t dt
  *
  *   q            [Tq, num_heads, head_dim]
  *   k, v         [Tk, num_kv_heads, head_dim]
- *   block_idx    [Tq, num_kv_heads, topk] int32 (from msa_index_topk)
+ *   block_idx    [Tq, num_kv_heads, topk] int32 (from msa_index_topk); read
+ *                as the set Sel: any order, and -1, ids past the query's
+ *                local block and repeated ids add nothing
  *   cu_seqlens_q, cu_seqlens_k, max_q_len, max_kv_len   as for msa_index_topk
  *   softmax_scale  <= 0 selects 1 / sqrt(head_dim)
  *   num_splits   0 = choose the schedule automatically.  For large prefills
@@ -171,7 +173,8 @@ msa_status_t msa_sparse_attn_prefill(const void* q, const void* k, const void* v
  *   q             [batch, num_heads, head_dim]
  *   k_cache, v_cache  token-major [*, num_kv_heads, head_dim]; sequence b's
  *                 tokens are rows [cache_offsets[b], cache_offsets[b] + ctx_lens[b])
- *   block_idx     [batch, num_kv_heads, topk] int32
+ *   block_idx     [batch, num_kv_heads, topk] int32, read as a set as in the
+ *                 prefill call
  *   cache_offsets [batch] int64, device, in tokens
  *   ctx_lens      [batch] int32, device, >= 1, <= max_ctx
  *   out           [batch, num_heads, head_dim]; lse [batch, num_heads] or NULL

@@ -25,8 +25,9 @@
 //                     all sequences are one flat range scored grid-stride by
 //                     waves (16x16 MFMA, keys x groups), one fp32 per (group,
 //                     block).
-//   idx_decode_select one workgroup per (sequence, group): per-thread register
-//                     lists, then two wave merges.
+//   idx_decode_select one workgroup per (sequence, group): a threshold from
+//                     the per-thread maxima of 64-bit selection keys, then an
+//                     exact rank of the few keys that reach it.
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -262,7 +263,15 @@ __global__ __launch_bounds__(256) void idx_merge_prefill(
 // --------------------------------------------------------------------------
 // Decode: stream the index-key cache once, one fp32 score per (group, block)
 // --------------------------------------------------------------------------
-// Earlier-block counts per sequence, as exclusive prefix sums (one workgroup).
+// Earlier blocks of sequence b that the decode scan scores (0 unless the
+// sequence has exactly one query row and a non-empty context).
+__device__ __forceinline__ int dec_blocks(const int32_t* cu_q, const int32_t* cu_k, int b) {
+  const int N = cu_k[b + 1] - cu_k[b];
+  return (cu_q[b + 1] - cu_q[b] == 1 && N > 0) ? (N - 1) / kBlock : 0;
+}
+
+// Earlier-block counts per sequence as exclusive prefix sums, for batches too
+// large for the scan's LDS copy (one thread).
 __global__ __launch_bounds__(256) void idx_decode_prefix(const int32_t* __restrict__ cu_q,
                                                          const int32_t* __restrict__ cu_k, int batch,
                                                          int32_t* __restrict__ blk_off) {
@@ -270,22 +279,56 @@ __global__ __launch_bounds__(256) void idx_decode_prefix(const int32_t* __restri
   int acc = 0;
   for (int b = 0; b < batch; ++b) {
     blk_off[b] = acc;
-    const int N = cu_k[b + 1] - cu_k[b];
-    if (cu_q[b + 1] - cu_q[b] == 1 && N > 0) acc += (N - 1) / kBlock;
+    acc += dec_blocks(cu_q, cu_k, b);
   }
   blk_off[batch] = acc;
 }
+
+// Batches below this size keep the block offsets in LDS, computed by every
+// scan workgroup itself (no prefix kernel; the per-block sequence search is an
+// LDS binary search).
+constexpr int kDecLdsSeq = 1024;
 
 // The earlier blocks of all sequences form one flat range; wave w scores
 // blocks w, w + W, w + 2W, ... so the waves running at any moment read
 // neighbouring 32 KB runs of the cache (copy-like DRAM locality).  Each block
 // is scored for all groups at once: 16x16 MFMA, keys x groups.
-template <typename T, int DI>
+template <typename T, int DI, bool kLdsOff>
 __global__ __launch_bounds__(256) void idx_decode_scores(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ cu_k, const int32_t* __restrict__ blk_off, int batch, int G, int nb_max,
+    const int32_t* __restrict__ cu_k, const int32_t* __restrict__ blk_off_g, int batch, int G, int nb_max,
     float* __restrict__ scores) {
   constexpr int DS = DI / 32;  // 32-wide contraction steps of the 16x16 MFMA
+  __shared__ int32_t s_off[kLdsOff ? kDecLdsSeq : 1];
+  __shared__ int32_t s_part[kLdsOff ? 256 : 1];
+  const int32_t* blk_off = blk_off_g;
+  if constexpr (kLdsOff) {
+    // thread i counts sequences 4i .. 4i+3; inclusive scan of the 256 sums
+    int cnt[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * (int)threadIdx.x + i;
+      cnt[i] = b < batch ? dec_blocks(cu_q, cu_k, b) : 0;
+      sum += cnt[i];
+    }
+    s_part[threadIdx.x] = sum;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int v = threadIdx.x >= (unsigned)off ? s_part[threadIdx.x - off] : 0;
+      __syncthreads();
+      s_part[threadIdx.x] += v;
+      __syncthreads();
+    }
+    int acc = s_part[threadIdx.x] - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * (int)threadIdx.x + i;
+      if (b <= batch) s_off[b] = acc;  // batch < kDecLdsSeq: the total lands in s_off[batch]
+      acc += cnt[i];
+    }
+    __syncthreads();
+    blk_off = s_off;
+  }
   const int lane = lane_id();
   const int nwaves = gridDim.x * 4;
   const int total = blk_off[batch];
@@ -324,13 +367,49 @@ __global__ __launch_bounds__(256) void idx_decode_scores(
   }
 }
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 1024;                     // 16 waves
+constexpr int kSelPer = 8;                            // keys per thread per round
+constexpr int kSelRound = kSelThreads * kSelPer;      // 8192 blocks per round
+constexpr int kSelCand = 16 * kSelPer + 16;           // candidate bound per round (see below)
 
+// Sort a lane's 16 keys descending (bitonic sorting network).
+__device__ __forceinline__ void key_sort16(uint64_t (&kl)[16]) {
+#pragma unroll
+  for (int k = 2; k <= 16; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint64_t x = kl[i], y = kl[l];
+          const bool sw = ((i & k) == 0) ? (x < y) : (x > y);
+          kl[i] = sw ? y : x;
+          kl[l] = sw ? x : y;
+        }
+      }
+}
+
+// One workgroup per (sequence, group), over rounds of 8192 earlier blocks.
+// A round keeps the 16 best selection keys seen so far (s_best) up to date:
+//   1. each thread forms the keys of its 8 blocks; its largest goes to LDS;
+//   2. wave 0 finds T, the 16th largest of the 1024 thread maxima (a sort of
+//      16 per lane, then butterfly merges), raised to s_best[15] if larger.
+//      At least 16 keys of the round's blocks and the previous best are >= T,
+//      so every member of their top 16 is >= T; and only the 16 threads
+//      whose maximum reaches T hold keys >= T, so there are at most
+//      16 * 8 + 16 candidates;
+//   3. the candidates are gathered in LDS and ranked by wave 0 (keys are
+//      distinct, so ranks are too); ranks 0..15 become the new s_best.
+// The key carries the score bits and the id, so no score is fetched back.
 __global__ __launch_bounds__(kSelThreads) void idx_decode_select(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int G, int topk, int nb_max,
     const float* __restrict__ scores, int32_t* __restrict__ block_idx) {
-  __shared__ float sh_s[kSelThreads / kWave][kList];
-  __shared__ int sh_i[kSelThreads / kWave][kList];
+  __shared__ uint64_t s_max[kSelThreads];
+  __shared__ uint64_t s_cand[kSelCand];
+  __shared__ uint64_t s_best[16];
+  __shared__ uint64_t s_T;
+  __shared__ int s_n;
   const int b = blockIdx.x / G, g = blockIdx.x % G;
   const int q0 = cu_q[b];
   if (cu_q[b + 1] - q0 != 1) return;
@@ -343,45 +422,78 @@ __global__ __launch_bounds__(kSelThreads) void idx_decode_select(
   }
   const int local = (N - 1) / kBlock;
   const float* sc = scores + ((int64_t)b * G + g) * nb_max;
+  if (threadIdx.x < 16) s_best[threadIdx.x] = 0;
 
-  float ls[kList];
-  int li[kList];
+  for (int r0 = 0; r0 < local; r0 += kSelRound) {
+    uint64_t k8[kSelPer];
+    float v[kSelPer];
 #pragma unroll
-  for (int j = 0; j < kList; ++j) { ls[j] = -__builtin_inff(); li[j] = -1; }
-  // ascending ids per thread (strided), fetched 8 at a time so the loads overlap
-  for (int c0 = threadIdx.x; c0 < local; c0 += 8 * kSelThreads) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = c0 + u * kSelThreads;
-      v[u] = c < local ? sc[c] : -__builtin_inff();
+    for (int u = 0; u < kSelPer; ++u) {
+      const int c = r0 + (int)threadIdx.x + u * kSelThreads;
+      v[u] = c < local ? sc[c] : 0.0f;
     }
+    uint64_t mx = 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = c0 + u * kSelThreads;
-      if (c < local) list_insert(ls, li, v[u], c);
+    for (int u = 0; u < kSelPer; ++u) {
+      const int c = r0 + (int)threadIdx.x + u * kSelThreads;
+      k8[u] = c < local ? sel_key(v[u], c) : 0;
+      mx = k8[u] > mx ? k8[u] : mx;
     }
+    s_max[threadIdx.x] = mx;
+    if (threadIdx.x == 0) s_n = 0;
+    __syncthreads();
+    if (wave == 0) {
+      uint64_t kl[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) kl[j] = s_max[j * kWave + lane];
+      key_sort16(kl);
+#pragma unroll
+      for (int m = 1; m < kWave; m <<= 1) key_merge_xor(kl, m);
+      if (lane == 0) s_T = kl[15] > s_best[15] ? kl[15] : s_best[15];
+    }
+    __syncthreads();
+    const uint64_t T = s_T;
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u)
+      if (k8[u] != 0 && k8[u] >= T) {
+        const int slot = atomicAdd(&s_n, 1);
+        if (slot < kSelCand) s_cand[slot] = k8[u];  // always true (bound above)
+      }
+    if (threadIdx.x < 16) {
+      const uint64_t x = s_best[threadIdx.x];
+      if (x != 0 && x >= T) {
+        const int slot = atomicAdd(&s_n, 1);
+        if (slot < kSelCand) s_cand[slot] = x;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int n = min(s_n, kSelCand);
+      uint64_t mine[3];
+      int rank[3];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        mine[i] = lane + kWave * i < n ? s_cand[lane + kWave * i] : 0;
+        rank[i] = 0;
+      }
+      for (int j = 0; j < n; ++j) {
+        const uint64_t x = s_cand[j];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) rank[i] += x > mine[i] ? 1 : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        if (lane + kWave * i < n && rank[i] < 16) s_best[rank[i]] = mine[i];
+      if (lane < 16 && lane >= n) s_best[lane] = 0;
+    }
+    __syncthreads();
   }
-
-  int mine;
-  const int found = wave_merge(ls, li, kList, mine);
-  if (lane < kList) {
-    sh_s[wave][lane] = lane < found ? 0.0f : -__builtin_inff();
-    sh_i[wave][lane] = lane < found ? mine : -1;
-  }
-  // Scores of the winners, fetched back by id (exact copies).
-  if (lane < found) sh_s[wave][lane] = sc[mine];
-  __syncthreads();
   if (wave != 0) return;
-  if (lane < kSelThreads / kWave) {
-#pragma unroll
-    for (int j = 0; j < kList; ++j) { ls[j] = sh_s[lane][j]; li[j] = sh_i[lane][j]; }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kList; ++j) { ls[j] = -__builtin_inff(); li[j] = -1; }
-  }
-  const int found2 = wave_merge(ls, li, topk - 1, mine);
-  write_selection(mine, found2, local, topk, out);
+  // s_best holds the best min(local, 16) earlier blocks, descending
+  const int found = min(local, topk - 1);
+  const uint64_t mk = lane < 16 ? s_best[lane] : 0;
+  const int mine = (lane < found && mk != 0) ? sel_key_id(mk) : -1;
+  write_selection(mine, found, local, topk, out);
 }
 
 // --------------------------------------------------------------------------
@@ -411,10 +523,16 @@ static hipError_t launch_index_decode(const IndexPlan& pl, const void* q_idx, co
                                       int topk, int32_t* block_idx, char* ws, hipStream_t st) {
   float* scores = reinterpret_cast<float*>(ws);
   int32_t* blk_off = reinterpret_cast<int32_t*>(ws + pl.score_bytes);
-  hipLaunchKernelGGL(idx_decode_prefix, dim3(1), dim3(256), 0, st, cu_q, cu_k, batch, blk_off);
-  hipLaunchKernelGGL((idx_decode_scores<T, DI>), dim3((unsigned)pl.dec_wgs), dim3(256), 0, st,
-                     static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), cu_q, cu_k, blk_off, batch, G,
-                     pl.nb_max, scores);
+  if (batch < kDecLdsSeq) {
+    hipLaunchKernelGGL((idx_decode_scores<T, DI, true>), dim3((unsigned)pl.dec_wgs), dim3(256), 0, st,
+                       static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), cu_q, cu_k, nullptr, batch,
+                       G, pl.nb_max, scores);
+  } else {
+    hipLaunchKernelGGL(idx_decode_prefix, dim3(1), dim3(256), 0, st, cu_q, cu_k, batch, blk_off);
+    hipLaunchKernelGGL((idx_decode_scores<T, DI, false>), dim3((unsigned)pl.dec_wgs), dim3(256), 0, st,
+                       static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), cu_q, cu_k, blk_off, batch,
+                       G, pl.nb_max, scores);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(idx_decode_select, dim3((unsigned)(batch * G)), dim3(kSelThreads), 0, st, cu_q, cu_k, G,

@@ -140,7 +140,9 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs a
 
     for (int i = i_lo; i < i_hi; ++i) {
       const int c = sel[i];
-      if (c < 0 || c > local) continue;
+      bool seen = false;  // Sel is a set: a repeated id counts once
+      for (int j = 0; j < i; ++j) seen = seen || sel[j] == c;
+      if (c < 0 || c > local || seen) continue;
       const int64_t key0 = (int64_t)c * kBlock;
       const bool causal = (c == local);
 
@@ -270,31 +272,42 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs a
 }
 
 // Two-phase combine: lse = ln sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s,
-// summed in split order (deterministic, no atomics).  One thread per (row, head, d).
+// summed in split order (deterministic, no atomics); empty chunks (lse_s =
+// -inf) are skipped.  32 threads per (row, head), 4 dims each.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_combine(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_lse,
                                                     const int32_t* __restrict__ cu_q, int batch,
                                                     int64_t rows_bound, int Hq, int nsplit, T* __restrict__ out,
                                                     float* __restrict__ lse) {
-  const int64_t rh = (int64_t)blockIdx.x * 2 + threadIdx.x / kHeadDim;
-  const int d = threadIdx.x % kHeadDim;
+  const int64_t rh = (int64_t)blockIdx.x * 8 + threadIdx.x / 32;
+  const int d0 = (threadIdx.x % 32) * 4;
   if (rh >= rows_bound * Hq) return;
   const int64_t t = rh / Hq;
   const int64_t nrows = cu_q ? cu_q[batch] : batch;
   if (t >= nrows) return;
   const float* pl = part_lse + rh * nsplit;
+  float ls[16];
   float mx = -__builtin_inff();
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, pl[s]);
-  float res = 0.f, L = -__builtin_inff();
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    ls[s] = s < nsplit ? pl[s] : -__builtin_inff();
+    mx = fmaxf(mx, ls[s]);
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float L = -__builtin_inff();
   if (mx != -__builtin_inff()) {
     float sum = 0.f;
-    for (int s = 0; s < nsplit; ++s) sum += expf(pl[s] - mx);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) sum += expf(ls[s] - mx);
     L = mx + logf(sum);
-    for (int s = 0; s < nsplit; ++s) res += expf(pl[s] - L) * part_o[(rh * nsplit + s) * kHeadDim + d];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (ls[s] != -__builtin_inff())
+        acc += expf(ls[s] - L) * *reinterpret_cast<const f32x4*>(part_o + (rh * nsplit + s) * kHeadDim + d0);
   }
-  out[rh * kHeadDim + d] = T(res);
-  if (lse && d == 0) lse[rh] = L;
+  store4<T>(out + rh * kHeadDim + d0, acc[0], acc[1], acc[2], acc[3]);
+  if (lse && d0 == 0) lse[rh] = L;
 }
 
 template <typename T>
@@ -310,12 +323,11 @@ static hipError_t launch_attn_t(const AttnPlan& pl, const AttnArgs& a, void* ws,
   k.part_o = pl.nsplit > 1 ? reinterpret_cast<float*>(w) : nullptr;
   k.part_lse = pl.nsplit > 1 ? reinterpret_cast<float*>(w + pl.part_o_bytes) : nullptr;
   const int64_t items = pl.rows_bound * a.Hkv * pl.nsplit;
-  const int64_t wgs = (items + 3) / 4;
-  hipLaunchKernelGGL(sparse_attn_fwd<T>, dim3((unsigned)wgs), dim3(kAttnThreads), 0, st, k);
+  hipLaunchKernelGGL(sparse_attn_fwd<T>, dim3((unsigned)((items + 3) / 4)), dim3(kAttnThreads), 0, st, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nsplit == 1) return e;
   const int64_t rh = pl.rows_bound * a.Hq;
-  hipLaunchKernelGGL(attn_combine<T>, dim3((unsigned)((rh + 1) / 2)), dim3(256), 0, st, k.part_o, k.part_lse,
+  hipLaunchKernelGGL(attn_combine<T>, dim3((unsigned)((rh + 7) / 8)), dim3(256), 0, st, k.part_o, k.part_lse,
                      a.cu_q, a.batch, pl.rows_bound, a.Hq, pl.nsplit, static_cast<T*>(a.out), a.lse);
   return hipGetLastError();
 }

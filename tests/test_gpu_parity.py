@@ -172,6 +172,61 @@ def test_decode_ragged_small(msa, synth, oracle_lib, splits):
     _decode_check(msa, oracle_lib, synth, wl, ctx, "decode small", num_splits=splits)
 
 
+def _handmade_selection(rng, pos, G, topk, block):
+    """Unsorted selections with a repeated id, -1 holes and ids past the local
+    block: the attention must use exactly the set of valid blocks in each."""
+    sel = np.full((len(pos), G, topk), -1, dtype=np.int32)
+    for r, p in enumerate(pos):
+        local = int(p) // block
+        for g in range(G):
+            ids = rng.integers(0, local + 3, size=topk)
+            ids[rng.random(topk) < 0.2] = -1
+            if topk > 2:
+                ids[1] = ids[0]
+            sel[r, g] = ids
+    return sel
+
+
+@pytest.mark.parametrize("splits", [0, 1, 4])
+def test_decode_attention_handmade_selection(msa, synth, oracle_lib, splits):
+    """Decode attention on hand-made selections, with the selection split into
+    one chunk per block (splits 0 here), one chunk, or four."""
+    wl = synth.WORKLOADS["decode_1m"]
+    ctx = [1, 200, 1000, 4097, 9000]
+    say(f"[parity] decode hand-made selections ctx={ctx} splits={splits}")
+    inp = synth.decode_inputs(wl, device="cuda", seed=11, ctx_lens=ctx)
+    pos = np.asarray(ctx, dtype=np.int64) - 1
+    sel = _handmade_selection(np.random.default_rng(11), pos, wl.num_kv_heads, wl.topk, wl.block_size)
+    sel[0, 0, :] = -1  # a (row, group) with nothing to attend
+    ids = torch.as_tensor(sel, device="cuda")
+    out, lse = msa.msa_sparse_attn_decode(inp["q"], inp["k"], inp["v"], ids, inp["k_offsets"], inp["ctx_lens"],
+                                          max(ctx), wl.block_size, wl.topk, num_splits=splits)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_lib.sparse_attn(host(inp["q"]), host(inp["k"]), host(inp["v"]), sel,
+                                              np.asarray(inp["k_offsets_host"], dtype=np.int64), pos,
+                                              np.arange(len(ctx)), wl.block_size, wl.topk)
+    compare_outputs(out, lse, ref_out, ref_lse, wl.dtype, "decode hand-made")
+
+
+@pytest.mark.parametrize("splits", [0, 1, 16])
+def test_prefill_attention_handmade_selection(msa, synth, oracle_lib, splits):
+    """Prefill attention (KV-outer for splits 0, query-outer otherwise) on
+    hand-made selections."""
+    wl = synth.WORKLOADS["prefill_32k"]
+    L = 1500
+    say(f"[parity] prefill hand-made selections L={L} splits={splits}")
+    inp = synth.prefill_inputs(wl, device="cuda", seed=12, seq_lens=[L])
+    pos = np.arange(L, dtype=np.int64)
+    sel = _handmade_selection(np.random.default_rng(12), pos, wl.num_kv_heads, wl.topk, wl.block_size)
+    ids = torch.as_tensor(sel, device="cuda")
+    out, lse = msa.msa_sparse_attn_prefill(inp["q"], inp["k"], inp["v"], ids, inp["cu_seqlens_q"],
+                                           inp["cu_seqlens_k"], L, L, wl.block_size, wl.topk, num_splits=splits)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_lib.sparse_attn(host(inp["q"]), host(inp["k"]), host(inp["v"]), sel,
+                                              np.zeros(L, dtype=np.int64), pos, pos, wl.block_size, wl.topk)
+    compare_outputs(out, lse, ref_out, ref_lse, wl.dtype, "prefill hand-made")
+
+
 def test_decode_and_prefill_paths_agree(msa, synth):
     """The decode index path (block scores + select) and the prefill path
     (chunked scan + merge) give the same ids for the same newest tokens."""
@@ -232,6 +287,16 @@ def test_fullsize_decode_1m(msa, synth, oracle_lib):
     ctx = synth.decode_ctx_lens(wl, 0)
     seqs = [int(np.argmin(ctx)), int(np.argmax(ctx)), 3, 11, 20, 31]
     _decode_check(msa, oracle_lib, synth, wl, ctx, "decode 1M", seed=0, seqs=sorted(set(seqs)))
+
+
+def test_decode_beyond_one_round_of_blocks(msa, synth, oracle_lib):
+    """Contexts past 8192 earlier blocks (over 1M tokens): the decode selection
+    runs several rounds and carries its best keys across them; with planted
+    blocks so that winners sit in different rounds."""
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS["decode_1m"], planted=64)
+    ctx = [1_300_000, 8193 * 128 + 1, 5000]
+    _decode_check(msa, oracle_lib, synth, wl, ctx, "decode >1M", seed=13)
 
 
 def test_fullsize_prefill_1m_last_tile(msa, synth, oracle_lib):
