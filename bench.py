@@ -197,6 +197,10 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": kernel, "launch_ms": round(dom_ms, 4),
                 "per_launch_flops": dom_flops}
+    if traffic is not None:
+        # the same call seen from the memory side: counted HBM bytes per second
+        roofline["traffic_GBs"] = round(traffic / (dom_ms / 1e3) / 1e9, 1)
+        roofline["traffic_frac_hbm"] = round(traffic / (dom_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)
 
     result = {
         "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
