@@ -53,7 +53,7 @@ template <typename T, int DI>
 __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, int G, int qw, int nsub, int max_qblocks, int chunk,
-    int max_chunks, int64_t cand_stride, uint64_t* __restrict__ cand) {
+    int max_chunks, int nb_stride, float* __restrict__ scores) {
   using L = ScanLds<T, DI>;
   static_assert(L::kChunks % kScanThreads == 0, "key block must split evenly over threads");
   constexpr int KS = DI / 16;  // 16-wide contraction steps
@@ -86,6 +86,16 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
   const int lane = lane_id();
   const int col_base = wave * 64;
   const bool active = col_base < ncols;
+  // This lane's column after the block-max swap, and its row of block scores.
+  // The scores of 16 consecutive blocks are gathered in registers (newest
+  // last) and written as one 64-byte run: chunks start at multiples of 16
+  // blocks and rows are 16-byte aligned, so every full group is aligned.
+  const int col_mine = col_base + lane;
+  const bool col_ok = col_mine < ncols;
+  float* srow = scores + (row0 * G + (col_ok ? col_mine : 0)) * (int64_t)nb_stride;
+  float sbuf[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sbuf[j] = 0.f;
 
   // B operand (Q^T): columns col_base + 32*j + lane%32, contraction slots
   // 16*ks + 8*(lane/32) .. +7.
@@ -98,11 +108,6 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[j][ks] = ok ? load8(qp + 16 * ks) : zero8<T>();
   }
-
-  float ls[kList];
-  int li[kList];
-#pragma unroll
-  for (int j = 0; j < kList; ++j) { ls[j] = -__builtin_inff(); li[j] = -1; }
 
   // Key blocks are staged into LDS in 16-byte pieces (coalesced global reads),
   // double-buffered: block s+1 is fetched into registers while block s is used.
@@ -158,7 +163,14 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
       const float send = lane < 32 ? m1 : m0;
       const float recv = shfl_xor_f(send, 32);
       const float v = fmaxf(lane < 32 ? m0 : m1, recv);
-      list_insert(ls, li, v, s);
+#pragma unroll
+      for (int j = 0; j < 15; ++j) sbuf[j] = sbuf[j + 1];
+      sbuf[15] = v;
+      if ((s & 15) == 15 && col_ok) {
+        f32x4* dst = reinterpret_cast<f32x4*>(srow + (s - 15));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = f32x4{sbuf[4 * q], sbuf[4 * q + 1], sbuf[4 * q + 2], sbuf[4 * q + 3]};
+      }
     }
     if (more) {
       char* dst = lds + (buf ^ 1) * L::kBufBytes;
@@ -171,15 +183,15 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
     }
     __syncthreads();
   }
-
-  // Candidates are stored as selection keys [chunk][list position][row * G +
-  // group]: lanes write consecutive columns, and the merge reads them the same way.
-  const int col = col_base + lane;
-  if (active && col < ncols) {
-    const int64_t rg = row0 * G + col;
+  // a trailing partial group (only at the end of a query block's last chunk)
+  const int n_tail = s_hi & 15;
+  if (active && col_ok && n_tail != 0) {
+    const int g0 = s_hi - n_tail;
 #pragma unroll
-    for (int j = 0; j < kList; ++j)
-      cand[(int64_t)(ch * kList + j) * cand_stride + rg] = li[j] >= 0 ? sel_key(ls[j], li[j]) : 0ull;
+    for (int i = 0; i < 16; ++i) {
+      const int j = i - (16 - n_tail);
+      if (j >= 0) srow[g0 + j] = sbuf[i];
+    }
   }
 }
 
@@ -195,69 +207,125 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int batch, int64_t ro
   return lo;
 }
 
-constexpr int kMergeLanes = 8;  // lanes sharing one (row, group)
+constexpr int kPreRound = 16 * kWave;     // blocks per selection round (16 keys per lane)
+constexpr int kPreCand = 16 * 16 + 16;    // candidate bound per round (see below)
 
-__global__ __launch_bounds__(256) void idx_merge_prefill(
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int64_t rows_bound, int G,
-    int topk, int chunk, const uint64_t* __restrict__ cand, int32_t* __restrict__ block_idx) {
-  // kMergeLanes lanes per (query row, group): lane part keeps the best 16 keys
-  // of chunks part, part + kMergeLanes, ...; three butterfly merges give every
-  // lane of the group the best 16 of all chunks; the best topk-1 plus the local
-  // block are written ascending.
-  const int64_t stride = rows_bound * G;
-  const int part = threadIdx.x % kMergeLanes;
-  const int64_t rg = ((int64_t)blockIdx.x * 256 + threadIdx.x) / kMergeLanes;
-  uint64_t kl[16];
+// Wave-wide bitonic sort of one 64-bit key per lane, descending across lanes.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
+  const int lane = lane_id();
 #pragma unroll
-  for (int j = 0; j < 16; ++j) kl[j] = 0;
-  bool live = rg < stride;
-  const int64_t row = live ? rg / G : 0;
-  live = live && row < cu_q[batch];
-  int64_t p = -1;
-  if (live) {
-    const int b = find_seq(cu_q, batch, row);
-    const int M = cu_q[b + 1] - cu_q[b], N = cu_k[b + 1] - cu_k[b];
-    p = (int64_t)N - M + (row - cu_q[b]);
-  }
-  const int local = p >= 0 ? (int)(p / kBlock) : 0;
-  const int nch = p >= 0 ? (local + chunk - 1) / chunk : 0;
-  for (int ch = part; ch < nch; ch += kMergeLanes) {
-    uint64_t ck[kList];
+  for (int k = 2; k <= kWave; k <<= 1)
 #pragma unroll
-    for (int j = 0; j < kList; ++j) ck[j] = cand[(int64_t)(ch * kList + j) * stride + rg];
-#pragma unroll
-    for (int j = 0; j < kList; ++j) {
-      if (!(ck[j] > kl[15])) break;  // lists are sorted: the rest of this one misses too
-      key_insert(kl, ck[j]);
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t y = shfl_xor_u64(x, j);
+      // the lower lane of a pair keeps the larger key in descending runs
+      const bool desc = (lane & k) == 0;
+      const bool lower = (lane & j) == 0;
+      const bool keep_max = desc == lower;
+      x = keep_max ? (x > y ? x : y) : (x > y ? y : x);
     }
-  }
-  key_merge_xor(kl, 1);
-  key_merge_xor(kl, 2);
-  key_merge_xor(kl, 4);
-  if (!live) return;
+  return x;
+}
+
+// One wave per (query row, group).  The scan left the row's block scores in
+// `scores`; rounds of 1024 earlier blocks (16 per lane) update the 16 best
+// selection keys (per-wave LDS, `best`):
+//   1. lane maxima of the round's keys, sorted across the wave; T = the 16th
+//      largest, raised to best[15] if that is larger.  At least 16 keys of the
+//      round and the previous best are >= T, so every member of their top 16
+//      is; only the 16 lanes whose maximum reaches T hold such keys, so there
+//      are at most 16 * 16 + 16 candidates;
+//   2. candidates are compacted into LDS in lane order (ballots) and ranked
+//      exactly (keys are distinct); ranks 0..15 become the new best.
+// The best topk - 1 plus the local block are written ascending.
+__global__ __launch_bounds__(256) void idx_select_prefill(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int64_t rows_bound, int G,
+    int topk, int nb_stride, const float* __restrict__ scores, int32_t* __restrict__ block_idx) {
+  __shared__ uint64_t s_cand[4][kPreCand];
+  __shared__ uint64_t s_best[4][16];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = lane_id();
+  const int64_t rg = (int64_t)blockIdx.x * 4 + wave;
+  if (rg >= rows_bound * G) return;
+  const int64_t row = rg / G;
+  if (row >= cu_q[batch]) return;
+  const int b = find_seq(cu_q, batch, row);
+  const int M = cu_q[b + 1] - cu_q[b], N = cu_k[b + 1] - cu_k[b];
+  const int64_t p = (int64_t)N - M + (row - cu_q[b]);
   int32_t* out = block_idx + rg * topk;
   if (p < 0) {
-    if (part == 0)
-      for (int i = 0; i < topk; ++i) out[i] = -1;
+    if (lane < topk) out[lane] = -1;
     return;
   }
-  int m = 0;  // earlier blocks kept: the first min(valid, topk - 1) keys
+  const int local = (int)(p / kBlock);
+  const float* sc = scores + rg * (int64_t)nb_stride;
+  uint64_t* cand = s_cand[wave];
+  uint64_t* best = s_best[wave];
+  if (lane < 16) best[lane] = 0;
+  for (int r0 = 0; r0 < local; r0 += kPreRound) {
+    float v[16];
 #pragma unroll
-  for (int j = 0; j < kList; ++j) m += (j < topk - 1 && kl[j] != 0) ? 1 : 0;
-  // lane `part` writes list entries part and part + 8 at their ascending rank
+    for (int u = 0; u < 16; ++u) {
+      const int c = r0 + lane + kWave * u;
+      v[u] = c < local ? sc[c] : 0.0f;
+    }
+    uint64_t k16[16], mx = 0;
 #pragma unroll
-  for (int j = 0; j < kList; ++j) {
-    if (j >= m || (j & (kMergeLanes - 1)) != part) continue;
-    const int id = sel_key_id(kl[j]);
-    int r = 0;
+    for (int u = 0; u < 16; ++u) {
+      const int c = r0 + lane + kWave * u;
+      k16[u] = c < local ? sel_key(v[u], c) : 0;
+      mx = k16[u] > mx ? k16[u] : mx;
+    }
+    const uint64_t sorted = wave_sort_desc(mx);
+    const uint64_t t_round = shfl_u64(sorted, 15);
+    const uint64_t b15 = best[15];
+    const uint64_t T = t_round > b15 ? t_round : b15;
+    // compact the candidates (keys >= T) into LDS, lane order within each u
+    int n = 0;
 #pragma unroll
-    for (int jj = 0; jj < kList; ++jj) r += (jj < m && sel_key_id(kl[jj]) < id) ? 1 : 0;
-    out[r] = id;
+    for (int u = 0; u < 16; ++u) {
+      const bool take = k16[u] != 0 && k16[u] >= T;
+      const uint64_t m = __ballot(take);
+      if (take) {
+        const int slot = n + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (slot < kPreCand) cand[slot] = k16[u];  // always true (bound above)
+      }
+      n += __builtin_popcountll(m);
+    }
+    {
+      const uint64_t x = lane < 16 ? best[lane] : 0;
+      const bool take = x != 0 && x >= T;
+      const uint64_t m = __ballot(take);
+      if (take) {
+        const int slot = n + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (slot < kPreCand) cand[slot] = x;
+      }
+      n += __builtin_popcountll(m);
+    }
+    n = min(n, kPreCand);
+    // exact ranks of the candidates (lane takes candidates lane, lane + 64, ...)
+    constexpr int kPer = (kPreCand + kWave - 1) / kWave;
+    uint64_t mine[kPer];
+    int rank[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      mine[i] = lane + kWave * i < n ? cand[lane + kWave * i] : 0;
+      rank[i] = 0;
+    }
+    for (int j = 0; j < n; ++j) {
+      const uint64_t x = cand[j];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) rank[i] += x > mine[i] ? 1 : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (lane + kWave * i < n && rank[i] < 16) best[rank[i]] = mine[i];
+    if (lane < 16 && lane >= n) best[lane] = 0;
   }
-  if (part == 0) {
-    out[m] = local;  // every earlier id is below the local block
-    for (int i = m + 1; i < topk; ++i) out[i] = -1;
-  }
+  const int found = min(local, topk - 1);
+  const uint64_t mk = lane < 16 ? best[lane] : 0;
+  const int mine = (lane < found && mk != 0) ? sel_key_id(mk) : -1;
+  write_selection(mine, found, local, topk, out);
 }
 
 // --------------------------------------------------------------------------
@@ -503,17 +571,17 @@ template <typename T, int DI>
 static hipError_t launch_index_prefill(const IndexPlan& pl, const void* q_idx, const void* k_idx,
                                        const int32_t* cu_q, const int32_t* cu_k, int batch, int G,
                                        int topk, int32_t* block_idx, char* ws, hipStream_t st) {
-  uint64_t* cand = reinterpret_cast<uint64_t*>(ws);
+  float* scores = reinterpret_cast<float*>(ws);
   if (pl.scan_wgs > 0) {
     hipLaunchKernelGGL((idx_scan_prefill<T, DI>), dim3((unsigned)pl.scan_wgs), dim3(kScanThreads), 0, st,
                        static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), cu_q, cu_k, G,
-                       pl.qw, pl.nsub, pl.max_qblocks, pl.chunk, pl.max_chunks, pl.rows_bound * G, cand);
+                       pl.qw, pl.nsub, pl.max_qblocks, pl.chunk, pl.max_chunks, pl.score_stride, scores);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t items = pl.rows_bound * G * kMergeLanes;
-  hipLaunchKernelGGL(idx_merge_prefill, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, cu_q, cu_k,
-                     batch, pl.rows_bound, G, topk, pl.chunk, cand, block_idx);
+  const int64_t items = pl.rows_bound * G;
+  hipLaunchKernelGGL(idx_select_prefill, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, cu_q, cu_k,
+                     batch, pl.rows_bound, G, topk, pl.score_stride, scores, block_idx);
   return hipGetLastError();
 }
 

@@ -53,17 +53,17 @@ IndexPlan plan_index(int batch, int max_q_len, int max_kv_len, int G) {
     // Work estimate: query blocks c_max-qb+1 .. c_max, each scanning c blocks.
     const int64_t c_first = c_max - qb + 1 > 0 ? c_max - qb + 1 : 0;
     const int64_t work = (int64_t)batch * pl.nsub * (c_first + c_max) * (c_max - c_first + 1) / 2;
-    int64_t chunk = ceil_div(work, kScanTargetWgs);
-    const int64_t min_chunk = ceil_div(c_max, 64);  // merge wave holds <= 64 lists
-    if (chunk < min_chunk) chunk = min_chunk;
-    if (chunk < 1) chunk = 1;
+    // a multiple of 16 blocks: the scan writes its block scores in aligned groups of 16
+    int64_t chunk = ceil_div(ceil_div(work, kScanTargetWgs), 16) * 16;
     pl.chunk = (int)chunk;
     pl.max_chunks = (int)ceil_div(c_max, chunk);
     pl.scan_wgs = (int64_t)batch * pl.max_qblocks * pl.nsub * pl.max_chunks;
   }
-  const size_t nc = (size_t)pl.rows_bound * G * pl.max_chunks * kList;
-  pl.cand_bytes = align_up(nc * sizeof(uint64_t));
-  pl.workspace_bytes = pl.scan_wgs > 0 ? pl.cand_bytes : 0;
+  // block scores [rows, G, score_stride] fp32 (rows padded to 16 bytes),
+  // written by the scan, read by the selection
+  pl.score_stride = (int)ceil_div(pl.nb_max, 4) * 4;
+  pl.score_bytes = pl.scan_wgs > 0 ? align_up((size_t)pl.rows_bound * G * pl.score_stride * sizeof(float)) : 0;
+  pl.workspace_bytes = pl.score_bytes;
   return pl;
 }
 

@@ -31,7 +31,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr int kBlock = 128;    // key block size (tokens)
 constexpr int kHeadDim = 128;  // main-branch head dim
-constexpr int kList = 15;      // per-lane candidate list: topk - 1 for topk <= 16
 
 template <typename T> struct Vec8;
 template <> struct Vec8<bf16> { typedef bf16x8 type; };
@@ -82,59 +81,6 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 __device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, kWave); }
 
-// Selection order: (score, id) precedes (score', id') when the score is higher,
-// or equal with a lower block id.  Invalid entries carry id < 0 and are last.
-__device__ __forceinline__ bool precedes(float s, int i, float s2, int i2) {
-  if (i2 < 0) return i >= 0;
-  if (i < 0) return false;
-  return (s > s2) || (s == s2 && i < i2);
-}
-
-// Wave-wide best (score, id) under `precedes`; every lane gets the result.
-__device__ __forceinline__ void wave_best(float& s, int& i) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) {
-    float so = shfl_xor_f(s, m);
-    int io = shfl_xor_i(i, m);
-    if (precedes(so, io, s, i)) { s = so; i = io; }
-  }
-}
-
-// Insert (v, c) into a descending list of kList entries when it beats the last
-// one.  Blocks arrive in ascending id order, so a strict comparison keeps the
-// earlier (lower) id ahead on equal scores: the lowest-id tie-break.
-__device__ __forceinline__ void list_insert(float (&ls)[kList], int (&li)[kList], float v, int c) {
-  if (!(v > ls[kList - 1])) return;
-  bool gt[kList];
-#pragma unroll
-  for (int j = 0; j < kList; ++j) gt[j] = v > ls[j];
-#pragma unroll
-  for (int j = kList - 1; j > 0; --j) {
-    float ns = gt[j - 1] ? ls[j - 1] : (gt[j] ? v : ls[j]);
-    int ni = gt[j - 1] ? li[j - 1] : (gt[j] ? c : li[j]);
-    ls[j] = ns;
-    li[j] = ni;
-  }
-  if (gt[0]) { ls[0] = v; li[0] = c; }
-}
-
-// Insert (v, c) into a list kept sorted by `precedes` when it precedes the
-// last entry (for candidates arriving in any order).
-__device__ __forceinline__ void list_insert_ordered(float (&ls)[kList], int (&li)[kList], float v, int c) {
-  if (!precedes(v, c, ls[kList - 1], li[kList - 1])) return;
-  bool pr[kList];
-#pragma unroll
-  for (int j = 0; j < kList; ++j) pr[j] = precedes(v, c, ls[j], li[j]);
-#pragma unroll
-  for (int j = kList - 1; j > 0; --j) {
-    float ns = pr[j - 1] ? ls[j - 1] : (pr[j] ? v : ls[j]);
-    int ni = pr[j - 1] ? li[j - 1] : (pr[j] ? c : li[j]);
-    ls[j] = ns;
-    li[j] = ni;
-  }
-  if (pr[0]) { ls[0] = v; li[0] = c; }
-}
-
 // 64-bit selection key: the score's bits mapped to an order-preserving
 // unsigned integer in the high word, the inverted block id in the low word, so
 // a larger key precedes in the selection order (higher score, then lower id).
@@ -146,20 +92,14 @@ __device__ __forceinline__ uint64_t sel_key(float s, int id) {
 }
 __device__ __forceinline__ int sel_key_id(uint64_t k) { return (int)(0xffffffffu - (uint32_t)k); }
 
-// Insert a key into a descending list of 16 keys when it beats the last one.
-__device__ __forceinline__ void key_insert(uint64_t (&kl)[16], uint64_t v) {
-  if (!(v > kl[15])) return;
-  bool gt[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) gt[j] = v > kl[j];
-#pragma unroll
-  for (int j = 15; j > 0; --j) kl[j] = gt[j - 1] ? kl[j - 1] : (gt[j] ? v : kl[j]);
-  if (gt[0]) kl[0] = v;
-}
-
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, kWave);
   const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src, kWave);
+  const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src, kWave);
   return ((uint64_t)hi << 32) | lo;
 }
 
@@ -182,34 +122,6 @@ __device__ __forceinline__ void key_merge_xor(uint64_t (&kl)[16], int m) {
         kl[j] = x > y ? x : y;
         kl[j + d] = x > y ? y : x;
       }
-}
-
-// Remove the head of a list (shift left), padding with an invalid entry.
-__device__ __forceinline__ void list_pop(float (&ls)[kList], int (&li)[kList]) {
-#pragma unroll
-  for (int j = 0; j < kList - 1; ++j) { ls[j] = ls[j + 1]; li[j] = li[j + 1]; }
-  ls[kList - 1] = -__builtin_inff();
-  li[kList - 1] = -1;
-}
-
-// Wave-level merge of per-lane descending lists: the first `take` entries of
-// their union under `precedes` go to lanes 0..take-1 (`mine`), one per lane;
-// returns how many valid entries were found.  Lane ids must be distinct
-// across lanes (they are: lists cover disjoint block ranges).
-__device__ __forceinline__ int wave_merge(float (&ls)[kList], int (&li)[kList], int take, int& mine) {
-  const int lane = lane_id();
-  mine = -1;
-  int found = 0;
-  for (int r = 0; r < take; ++r) {
-    float s = ls[0];
-    int i = li[0];
-    wave_best(s, i);
-    if (i < 0) break;
-    if (li[0] == i) list_pop(ls, li);
-    if (lane == r) mine = i;
-    ++found;
-  }
-  return found;
 }
 
 // Write the final selection: `found` earlier ids held one per lane in lanes

@@ -19,12 +19,12 @@ struct IndexPlan {
   int nsub = 0;              // slices per query block
   int max_qblocks = 0;       // query blocks per sequence (upper bound)
   int chunk = 1;             // key blocks per scan workgroup
-  int max_chunks = 1;        // key chunks per query block (<= 64)
+  int max_chunks = 1;        // key chunks per query block
   int64_t scan_wgs = 0;
-  size_t cand_bytes = 0;     // [chunks][15][rows * G] 64-bit selection keys
+  int score_stride = 0;      // floats per (row, group) of prefill block scores
   // decode scan
   int dec_wgs = 0;           // workgroups (4 waves) of the grid-stride decode scan
-  size_t score_bytes = 0;
+  size_t score_bytes = 0;    // block scores: prefill [rows, G, nb_max], decode [batch, G, nb_max]
   size_t workspace_bytes = 0;
 };
 
