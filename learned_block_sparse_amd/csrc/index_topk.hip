@@ -303,23 +303,14 @@ __global__ __launch_bounds__(256) void idx_select_prefill(
       n += __builtin_popcountll(m);
     }
     n = min(n, kPreCand);
-    // exact ranks of the candidates (lane takes candidates lane, lane + 64, ...)
-    constexpr int kPer = (kPreCand + kWave - 1) / kWave;
-    uint64_t mine[kPer];
-    int rank[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      mine[i] = lane + kWave * i < n ? cand[lane + kWave * i] : 0;
-      rank[i] = 0;
+    // exact ranks of the candidates, 64 at a time (usually one pass)
+    for (int i0 = 0; i0 < n; i0 += kWave) {
+      const bool has = i0 + lane < n;
+      const uint64_t mine = has ? cand[i0 + lane] : 0;
+      int rank = 0;
+      for (int j = 0; j < n; ++j) rank += cand[j] > mine ? 1 : 0;
+      if (has && rank < 16) best[rank] = mine;
     }
-    for (int j = 0; j < n; ++j) {
-      const uint64_t x = cand[j];
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) rank[i] += x > mine[i] ? 1 : 0;
-    }
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      if (lane + kWave * i < n && rank[i] < 16) best[rank[i]] = mine[i];
     if (lane < 16 && lane >= n) best[lane] = 0;
   }
   const int found = min(local, topk - 1);
