@@ -96,15 +96,19 @@ int msa_last_hip_error(void);
  *   num_groups   G (= number of KV heads)
  *   block_idx    [Tq, G, topk] int32 out: ascending ids, -1 padded
  *   workspace    device scratch of at least msa_index_topk_workspace_size()
- *                bytes (may be NULL when that size is 0)
+ *                bytes (may be NULL when that size is 0): the fp32 block
+ *                scores, batch * max_q_len * G * ceil(max_kv_len / 128) floats
+ *                (rounded up to 4 per (row, group)) on the prefill path,
+ *                batch * G * ceil(max_kv_len / 128) on the decode path
  *
  * Scores accumulate in fp32.  With max_q_len == 1 (one new token per
  * sequence) the call takes the decode path: the whole index-key cache is
  * streamed once for all groups, then a per-(sequence, group) selection runs.
  * Otherwise the prefill path scans key blocks per query block with an MFMA
- * GEMM whose epilogue max-pools and keeps a per-lane register top-k, then
- * merges the per-chunk candidates.  Both paths use the same total order and
- * return identical ids on identical inputs.
+ * GEMM whose epilogue max-pools the block scores, then a per-(row, group)
+ * selection runs over them.  Both paths use the same total order (score
+ * descending, then block id ascending) and return identical ids on identical
+ * inputs.
  * ---------------------------------------------------------------------- */
 size_t msa_index_topk_workspace_size(int batch, int max_q_len, int max_kv_len, int num_groups,
                                      int block_size, int topk);
