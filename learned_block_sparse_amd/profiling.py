@@ -27,7 +27,7 @@ import os
 # kernels of one library call, by (truncated) kernel-name prefix
 CALLS = {
     "attention_prefill_128k": ("kvo_zero", "kvo_bucket", "kvo_scan", "kvo_attn", "kvo_combine"),
-    "index_prefill_128k": ("_ZN3msa16idx_scan_prefill", "idx_scan_prefill", "idx_merge_prefill"),
+    "index_prefill_128k": ("_ZN3msa16idx_scan_prefill", "idx_scan_prefill", "idx_select_prefill"),
     "index_decode_1m": ("_ZN3msa17idx_decode_scores", "idx_decode_scores", "idx_decode_select"),
     "attention_decode_1m": ("_ZN3msa15sparse_attn_fwd", "sparse_attn_fwd", "_ZN3msa12attn_combine",
                             "attn_combine"),
