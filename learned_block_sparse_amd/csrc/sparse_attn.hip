@@ -73,6 +73,25 @@ __device__ __forceinline__ void store4<float>(float* p, float a, float b, float 
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
+// V rows key0 + 32ks .. +31 of one block into registers, as the units of the
+// transposed staging: unit u = (key quad u%8, d octet u/8); lane handles
+// u = lane and lane + 64.  Rows past p clamp to p (their P is 0).
+template <typename T>
+__device__ __forceinline__ void load_v_chunk(const T* vseq, int64_t row_stride, int64_t key0, int64_t p, int ks,
+                                             int lane, frag8<T> (&r)[2][4]) {
+#pragma unroll
+  for (int uu = 0; uu < 2; ++uu) {
+    const int u = lane + 64 * uu;
+    const int kq = u & 7, o8 = u >> 3;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      int64_t key = key0 + 32 * ks + 4 * kq + jj;
+      if (key > p) key = p;
+      r[uu][jj] = load8(vseq + key * row_stride + 8 * o8);
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs args) {
   using V = VtTile<T>;
@@ -146,16 +165,27 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs a
       const int64_t key0 = (int64_t)c * kBlock;
       const bool causal = (c == local);
 
-      // ---- S^T[key][head] for the 128 keys of the block (8 tiles of 16 keys)
-      f32x4 st[kBlock / 16];
+      // ---- S^T[key][head] for the 128 keys of the block (8 tiles of 16 keys);
+      // the first V chunk is requested right behind the K rows, and each
+      // later chunk while the previous one is staged and multiplied, so a
+      // block costs about two memory round trips instead of five.
+      frag8<T> kfr[kBlock / 16][kHeadDim / 32];
 #pragma unroll
       for (int kt = 0; kt < kBlock / 16; ++kt) {
         int64_t key = key0 + 16 * kt + h;   // A operand row = lane % 16
         if (key > p) key = p;               // stay inside the sequence; masked below
         const T* kp = kseq + key * row_stride + 8 * a;
+#pragma unroll
+        for (int ds = 0; ds < kHeadDim / 32; ++ds) kfr[kt][ds] = load8(kp + 32 * ds);
+      }
+      frag8<T> vbuf[2][2][4];
+      load_v_chunk<T>(vseq, row_stride, key0, p, 0, lane, vbuf[0]);
+      f32x4 st[kBlock / 16];
+#pragma unroll
+      for (int kt = 0; kt < kBlock / 16; ++kt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ds = 0; ds < kHeadDim / 32; ++ds) acc = mma16(load8(kp + 32 * ds), qf[ds], acc);
+        for (int ds = 0; ds < kHeadDim / 32; ++ds) acc = mma16(kfr[kt][ds], qf[ds], acc);
         st[kt] = acc;
       }
 
@@ -193,19 +223,13 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs a
       // ---- O^T[d][head] += V^T[d][key] P^T[key][head], 32 keys at a time
 #pragma unroll
       for (int ks = 0; ks < kBlock / 32; ++ks) {
+        if (ks + 1 < kBlock / 32) load_v_chunk<T>(vseq, row_stride, key0, p, ks + 1, lane, vbuf[(ks + 1) & 1]);
         // Stage V rows key0+32ks .. +31 transposed: vt[d][key], keys contiguous.
-        // Unit u = (key quad u%8, d octet u/8); lane handles u = lane, lane+64.
 #pragma unroll
         for (int uu = 0; uu < 2; ++uu) {
           const int u = lane + 64 * uu;
           const int kq = u & 7, o8 = u >> 3;
-          frag8<T> r4[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            int64_t key = key0 + 32 * ks + 4 * kq + jj;
-            if (key > p) key = p;
-            r4[jj] = load8(vseq + key * row_stride + 8 * o8);
-          }
+          const frag8<T>(&r4)[4] = vbuf[ks & 1][uu];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             T* dst = vt + (8 * o8 + e) * V::kStride + 4 * kq;
