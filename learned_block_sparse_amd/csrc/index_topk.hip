@@ -392,7 +392,12 @@ __global__ __launch_bounds__(256) void idx_decode_scores(
   const int nwaves = gridDim.x * 4;
   const int total = blk_off[batch];
   const int gcol = lane & 15;
-  for (int gb = blockIdx.x * 4 + threadIdx.x / kWave; gb < total; gb += nwaves) {
+  // Workgroups are dispatched round-robin over the 8 XCDs (grid a multiple of
+  // 8): in every sweep XCD x takes one contiguous range of blocks, so the
+  // 128-byte lines of block scores are written whole from one L2.
+  const int per_xcd = (gridDim.x >> 3) * 4;
+  const int first = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3) * 4 + (int)(threadIdx.x / kWave);
+  for (int gb = first; gb < total; gb += nwaves) {
     const int b = find_seq(blk_off, batch, gb);
     const int c = gb - blk_off[b];
     const int q0 = cu_q[b];

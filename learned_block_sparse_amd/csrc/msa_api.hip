@@ -34,7 +34,7 @@ IndexPlan plan_index(int batch, int max_q_len, int max_kv_len, int G) {
     const int64_t total_blocks = (int64_t)batch * pl.nb_max;
     int64_t waves = total_blocks < kDecodeTargetWaves ? total_blocks : kDecodeTargetWaves;
     if (waves < 4) waves = 4;
-    pl.dec_wgs = (int)ceil_div(waves, 4);
+    pl.dec_wgs = (int)ceil_div(ceil_div(waves, 4), 8) * 8;  // a multiple of the 8 XCDs
     pl.score_bytes = align_up((size_t)batch * G * pl.nb_max * sizeof(float));
     pl.workspace_bytes = pl.score_bytes + align_up((size_t)(batch + 1) * sizeof(int32_t));
     return pl;
