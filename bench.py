@@ -39,6 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MSA prefill tokens/s @128K + decode µs/step @1M ctx, % of roofline (1 GPU)"
 
@@ -219,7 +220,29 @@ def main():
                     "algorithmic_flops": idx_flops + att_flops,
                     "planted_share_last_tile": round(planted_share, 3)},
     }
-    del inp, calls
+    # The same index calls with the index tensors rounded to fp8 E4M3 (an extra
+    # measurement beside the bf16 headline; the block ids are exact for these
+    # inputs on both paths, see the fp8 tests).
+    q8, k8 = inp["q_idx"].to(torch.float8_e4m3fn), inp["k_idx"].to(torch.float8_e4m3fn)
+
+    def index_fp8_step():
+        for c in calls:
+            msa.msa_index_topk(q8[c["lo"]:c["hi"]], k8, c["cu_q"], c["cu_k"], c["m"], c["hi"], wl.block_size,
+                               wl.topk, block_idx=c["ids"], workspace=c["ws_i"], stream=stream)
+
+    index_fp8_step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        index_fp8_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    idx8_ms = e0.elapsed_time(e1) / args.steps
+    result["prefill"]["index_fp8"] = {
+        "ms": round(idx8_ms, 3), "tflops": round(idx_flops / (idx8_ms / 1e3) / 1e12, 1),
+        "frac_fp8_mfma": round(idx_flops / (idx8_ms / 1e3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+    del inp, calls, q8, k8
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ decode
@@ -279,7 +302,30 @@ def main():
             "index_scan_GBs": round(idx_gbs, 1), "index_scan_frac_hbm": round(idx_gbs / PEAK_HBM_GBS, 4),
             "index_scan_traffic": traffic_record("index_decode_1m"),
         }
-        del d
+        # the same decode step with the index tensors in fp8 E4M3 (half the scan bytes)
+        q8, k8 = d["q_idx"].to(torch.float8_e4m3fn), d["k_idx"].to(torch.float8_e4m3fn)
+
+        def dstep8():
+            msa.msa_index_topk(q8, k8, d["cu_seqlens_q"], d["cu_seqlens_k"], 1, max(ctx), wd.block_size,
+                               wd.topk, block_idx=ids, workspace=ws_i, stream=stream)
+            msa.msa_sparse_attn_decode(d["q"], d["k"], d["v"], ids, d["k_offsets"], d["ctx_lens"], max(ctx),
+                                       wd.block_size, wd.topk, out=out, lse=lse, workspace=ws_a, stream=stream)
+
+        for _ in range(5):
+            dstep8()
+        torch.cuda.synchronize()
+        e_lo.record(stream)
+        for s in range(args.decode_steps):
+            dstep8()
+        e_hi.record(stream)
+        torch.cuda.synchronize()
+        d8_us = e_lo.elapsed_time(e_hi) * 1e3 / args.decode_steps
+        idx8_b, _ = workmodel.decode_bytes(ctx, Hq, G, D, DI, wd.block_size, wd.topk, elem_bytes=1)
+        gbs8 = (idx8_b + att_b) / (d8_us * 1e-6) / 1e9
+        result["decode"]["fp8_index"] = {
+            "us_per_step": round(d8_us, 1), "bytes_per_step": idx8_b + att_b, "achieved_GBs": round(gbs8, 1),
+            "frac_hbm": round(gbs8 / PEAK_HBM_GBS, 4)}
+        del d, q8, k8
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU baseline

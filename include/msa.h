@@ -67,7 +67,11 @@ typedef enum {
   MSA_ERR_HIP = 4           /* a HIP launch or runtime call failed */
 } msa_status_t;
 
-typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype_t;
+/* Element types.  MSA_FP8_E4M3 is the OCP 8-bit floating point format E4M3
+ * (sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities; the
+ * pages note the kernels also support fp8): accepted for the index tensors of
+ * msa_index_topk only; the attention calls return MSA_ERR_UNSUPPORTED. */
+typedef enum { MSA_F32 = 0, MSA_BF16 = 1, MSA_FP8_E4M3 = 2 } msa_dtype_t;
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* msa_status_string(msa_status_t status);

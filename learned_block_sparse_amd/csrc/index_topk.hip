@@ -49,14 +49,44 @@ struct ScanLds {
   static constexpr int kChunksPerRow = DI * (int)sizeof(T) / 16;
 };
 
+// Operands of the scan's 32x32 MFMA per element type: a lane feeds kLaneK
+// consecutive contraction elements of its row (one fragment) and one MFMA
+// contracts kStep elements (lanes l and l + 32 cover the two halves).
+template <typename T> struct ScanMma;
+template <> struct ScanMma<bf16> {
+  using frag = bf16x8;
+  static constexpr int kStep = 16, kLaneK = 8;
+  static __device__ __forceinline__ frag load(const bf16* p) { return load8(p); }
+  static __device__ __forceinline__ frag zero() { return zero8<bf16>(); }
+  static __device__ __forceinline__ f32x16 mma(const frag& a, const frag& b, f32x16 c) { return mma32(a, b, c); }
+};
+template <> struct ScanMma<float> {
+  using frag = f32x8;
+  static constexpr int kStep = 16, kLaneK = 8;
+  static __device__ __forceinline__ frag load(const float* p) { return load8(p); }
+  static __device__ __forceinline__ frag zero() { return zero8<float>(); }
+  static __device__ __forceinline__ f32x16 mma(const frag& a, const frag& b, f32x16 c) { return mma32(a, b, c); }
+};
+template <> struct ScanMma<fp8e4m3> {
+  using frag = i32x8;
+  static constexpr int kStep = 64, kLaneK = 32;
+  static __device__ __forceinline__ frag load(const fp8e4m3* p) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(p), hi = *reinterpret_cast<const u32x4*>(p + 16);
+    return frag{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  static __device__ __forceinline__ frag zero() { return frag{0, 0, 0, 0, 0, 0, 0, 0}; }
+  static __device__ __forceinline__ f32x16 mma(const frag& a, const frag& b, f32x16 c) { return mma32_fp8(a, b, c); }
+};
+
 template <typename T, int DI>
 __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, int G, int qw, int nsub, int max_qblocks, int chunk,
     int max_chunks, int nb_stride, float* __restrict__ scores) {
   using L = ScanLds<T, DI>;
+  using Mm = ScanMma<T>;
   static_assert(L::kChunks % kScanThreads == 0, "key block must split evenly over threads");
-  constexpr int KS = DI / 16;  // 16-wide contraction steps
+  constexpr int KS = DI / Mm::kStep;  // MFMA contraction steps
   __shared__ __attribute__((aligned(16))) char lds[2 * L::kBufBytes];
 
   // Decode the workgroup: key chunk fastest, then query slice, then query block
@@ -98,15 +128,15 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
   for (int j = 0; j < 16; ++j) sbuf[j] = 0.f;
 
   // B operand (Q^T): columns col_base + 32*j + lane%32, contraction slots
-  // 16*ks + 8*(lane/32) .. +7.
-  frag8<T> qf[2][KS];
+  // kStep*ks + kLaneK*(lane/32) .. +kLaneK-1.
+  typename Mm::frag qf[2][KS];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int col = col_base + 32 * j + (lane & 31);
     const bool ok = col < ncols;
-    const T* qp = q_idx + (row0 * G + (ok ? col : 0)) * DI + 8 * (lane >> 5);
+    const T* qp = q_idx + (row0 * G + (ok ? col : 0)) * DI + Mm::kLaneK * (lane >> 5);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[j][ks] = ok ? load8(qp + 16 * ks) : zero8<T>();
+    for (int ks = 0; ks < KS; ++ks) qf[j][ks] = ok ? Mm::load(qp + Mm::kStep * ks) : Mm::zero();
   }
 
   // Key blocks are staged into LDS in 16-byte pieces (coalesced global reads),
@@ -134,26 +164,27 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
         stage[u] = *reinterpret_cast<const u32x4*>(kseq + (s + 1) * kBlockBytes + (threadIdx.x + u * kScanThreads) * 16);
     }
     if (active) {
-      const char* kb = lds + buf * L::kBufBytes + (lane & 31) * L::kRowBytes + 8 * (lane >> 5) * (int)sizeof(T);
+      const char* kb = lds + buf * L::kBufBytes + (lane & 31) * L::kRowBytes + Mm::kLaneK * (lane >> 5) * (int)sizeof(T);
+      constexpr int kStepBytes = Mm::kStep * (int)sizeof(T);
       float m0 = -__builtin_inff(), m1 = -__builtin_inff();
       // A operand (K rows) in two register sets: key tile kt+1 is read from
       // LDS while tile kt's MFMAs run, so LDS latency overlaps the MFMAs.
-      frag8<T> kf[2][KS];
+      typename Mm::frag kf[2][KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[0][ks] = *reinterpret_cast<const frag8<T>*>(kb + 16 * ks * (int)sizeof(T));
+      for (int ks = 0; ks < KS; ++ks) kf[0][ks] = *reinterpret_cast<const typename Mm::frag*>(kb + kStepBytes * ks);
 #pragma unroll
       for (int kt = 0; kt < kBlock / 32; ++kt) {
         if (kt + 1 < kBlock / 32) {
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
             kf[(kt + 1) & 1][ks] =
-                *reinterpret_cast<const frag8<T>*>(kb + 32 * (kt + 1) * L::kRowBytes + 16 * ks * (int)sizeof(T));
+                *reinterpret_cast<const typename Mm::frag*>(kb + 32 * (kt + 1) * L::kRowBytes + kStepBytes * ks);
         }
         f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          acc0 = mma32(kf[kt & 1][ks], qf[0][ks], acc0);
-          acc1 = mma32(kf[kt & 1][ks], qf[1][ks], acc1);
+          acc0 = Mm::mma(kf[kt & 1][ks], qf[0][ks], acc0);
+          acc1 = Mm::mma(kf[kt & 1][ks], qf[1][ks], acc1);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) { m0 = fmaxf(m0, acc0[r]); m1 = fmaxf(m1, acc1[r]); }
@@ -401,29 +432,62 @@ __global__ __launch_bounds__(256) void idx_decode_scores(
     const int b = find_seq(blk_off, batch, gb);
     const int c = gb - blk_off[b];
     const int q0 = cu_q[b];
-    // B operand: columns are the groups (lane%16 < G), slots 32*ds + 8*(lane/16).
-    frag8<T> qf[DS];
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds)
-      qf[ds] = gcol < G ? load8(q_idx + ((int64_t)q0 * G + gcol) * DI + 32 * ds + 8 * (lane >> 4))
-                        : zero8<T>();
-    const T* kb = k_idx + ((int64_t)cu_k[b] + (int64_t)c * kBlock + (lane & 15)) * DI + 8 * (lane >> 4);
-    frag8<T> a[kBlock / 16][DS];
-#pragma unroll
-    for (int kt = 0; kt < kBlock / 16; ++kt)
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) a[kt][ds] = load8(kb + (int64_t)kt * 16 * DI + 32 * ds);
-    // keep the whole block's loads in flight together before the MFMAs (the
-    // scheduler would otherwise interleave them and starve the memory system)
-    __builtin_amdgcn_sched_barrier(0);
     float m = -__builtin_inff();
+    if constexpr (sizeof(T) == 1) {
+      // fp8: lane l takes bytes PB*(l/16) .. +PB-1 of its key row (one or two
+      // 16-byte loads); MFMA step j contracts bytes 8j .. 8j+7 of those pieces
+      // across the four lane groups, the index query using the same bytes.
+      constexpr int PB = DI / 4, NL = PB / 16;
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(q_idx) + ((int64_t)q0 * G + gcol) * DI + PB * (lane >> 4);
+      u32x4 qv[NL];
 #pragma unroll
-    for (int kt = 0; kt < kBlock / 16; ++kt) {
-      f32x4 acc = {};
+      for (int u = 0; u < NL; ++u)
+        qv[u] = gcol < G ? *reinterpret_cast<const u32x4*>(qp + 16 * u) : u32x4{0u, 0u, 0u, 0u};
+      const uint8_t* kb = reinterpret_cast<const uint8_t*>(k_idx) +
+                          ((int64_t)cu_k[b] + (int64_t)c * kBlock + (lane & 15)) * DI + PB * (lane >> 4);
+      u32x4 a[kBlock / 16][NL];
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) acc = mma16(a[kt][ds], qf[ds], acc);
+      for (int kt = 0; kt < kBlock / 16; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[r]);
+        for (int u = 0; u < NL; ++u) a[kt][u] = *reinterpret_cast<const u32x4*>(kb + (int64_t)kt * 16 * DI + 16 * u);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kt = 0; kt < kBlock / 16; ++kt) {
+        f32x4 acc = {};
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+          acc = mma16_fp8((long)(((uint64_t)a[kt][u].y << 32) | a[kt][u].x),
+                          (long)(((uint64_t)qv[u].y << 32) | qv[u].x), acc);
+          acc = mma16_fp8((long)(((uint64_t)a[kt][u].w << 32) | a[kt][u].z),
+                          (long)(((uint64_t)qv[u].w << 32) | qv[u].z), acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[r]);
+      }
+    } else {
+      // B operand: columns are the groups (lane%16 < G), slots 32*ds + 8*(lane/16).
+      frag8<T> qf[DS];
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        qf[ds] = gcol < G ? load8(q_idx + ((int64_t)q0 * G + gcol) * DI + 32 * ds + 8 * (lane >> 4))
+                          : zero8<T>();
+      const T* kb = k_idx + ((int64_t)cu_k[b] + (int64_t)c * kBlock + (lane & 15)) * DI + 8 * (lane >> 4);
+      frag8<T> a[kBlock / 16][DS];
+#pragma unroll
+      for (int kt = 0; kt < kBlock / 16; ++kt)
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) a[kt][ds] = load8(kb + (int64_t)kt * 16 * DI + 32 * ds);
+      // keep the whole block's loads in flight together before the MFMAs (the
+      // scheduler would otherwise interleave them and starve the memory system)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kt = 0; kt < kBlock / 16; ++kt) {
+        f32x4 acc = {};
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) acc = mma16(a[kt][ds], qf[ds], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[r]);
+      }
     }
     m = fmaxf(m, shfl_xor_f(m, 16));
     m = fmaxf(m, shfl_xor_f(m, 32));
@@ -604,24 +668,26 @@ static hipError_t launch_index_decode(const IndexPlan& pl, const void* q_idx, co
   return hipGetLastError();
 }
 
+template <typename T>
+static hipError_t launch_index_t(const IndexPlan& pl, int DI, const void* q_idx, const void* k_idx,
+                                 const int32_t* cu_q, const int32_t* cu_k, int batch, int G, int topk,
+                                 int32_t* block_idx, char* w, hipStream_t st) {
+  if (pl.decode)
+    return DI == 64 ? launch_index_decode<T, 64>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st)
+                    : launch_index_decode<T, 128>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st);
+  return DI == 64 ? launch_index_prefill<T, 64>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st)
+                  : launch_index_prefill<T, 128>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st);
+}
+
+// dtype: 0 fp32, 1 bf16, 2 fp8 E4M3
 hipError_t launch_index_topk(const IndexPlan& pl, int dtype, int DI, const void* q_idx, const void* k_idx,
                              const int32_t* cu_q, const int32_t* cu_k, int batch, int G, int topk,
                              int32_t* block_idx, void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
-  if (pl.decode) {
-    if (dtype == 0) {
-      return DI == 64 ? launch_index_decode<float, 64>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st)
-                      : launch_index_decode<float, 128>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st);
-    }
-    return DI == 64 ? launch_index_decode<bf16, 64>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st)
-                    : launch_index_decode<bf16, 128>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st);
-  }
-  if (dtype == 0) {
-    return DI == 64 ? launch_index_prefill<float, 64>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st)
-                    : launch_index_prefill<float, 128>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st);
-  }
-  return DI == 64 ? launch_index_prefill<bf16, 64>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st)
-                  : launch_index_prefill<bf16, 128>(pl, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st);
+  if (dtype == 0) return launch_index_t<float>(pl, DI, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st);
+  if (dtype == 2)
+    return launch_index_t<fp8e4m3>(pl, DI, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st);
+  return launch_index_t<bf16>(pl, DI, q_idx, k_idx, cu_q, cu_k, batch, G, topk, block_idx, w, st);
 }
 
 }  // namespace msa

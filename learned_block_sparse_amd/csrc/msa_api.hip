@@ -120,7 +120,7 @@ static msa_status_t hip_status(hipError_t e) {
   return MSA_ERR_HIP;
 }
 
-static bool dtype_ok(msa_dtype_t d) { return d == MSA_F32 || d == MSA_BF16; }
+static bool dtype_ok(msa_dtype_t d) { return d == MSA_F32 || d == MSA_BF16 || d == MSA_FP8_E4M3; }
 
 extern "C" {
 
@@ -180,7 +180,7 @@ static msa_status_t check_attn(const void* q, const void* k, const void* v, msa_
     return MSA_ERR_INVALID_ARG;
   if (num_heads % num_kv_heads != 0) return MSA_ERR_INVALID_ARG;
   if (block_size != kBlock || head_dim != kHeadDim || topk > 16 || num_heads / num_kv_heads > 16 ||
-      num_kv_heads > 16)
+      num_kv_heads > 16 || dtype == MSA_FP8_E4M3)  // fp8 is implemented for the index tensors only
     return MSA_ERR_UNSUPPORTED;
   return MSA_OK;
 }

@@ -32,6 +32,14 @@ constexpr int kWave = 64;
 constexpr int kBlock = 128;    // key block size (tokens)
 constexpr int kHeadDim = 128;  // main-branch head dim
 
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// 8-bit floating point E4M3 (OCP: bias 7, 3 mantissa bits, no infinities),
+// carried as raw bytes; only the MFMAs interpret them.
+struct fp8e4m3 {
+  uint8_t bits;
+};
+
 template <typename T> struct Vec8;
 template <> struct Vec8<bf16> { typedef bf16x8 type; };
 template <> struct Vec8<float> { typedef f32x8 type; };
@@ -74,6 +82,16 @@ __device__ __forceinline__ f32x16 mma32(const f32x8& a, const f32x8& b, f32x16 c
 #pragma unroll
   for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], c, 0, 0, 0);
   return c;
+}
+
+// fp8: 32x32x64 (lane l: A row l%32, k-slots 32*(l/32) .. +31, i.e. 32 bytes)
+// and 16x16x32 (lane l: A row l%16, k-slots 8*(l/16) .. +7, 8 bytes); both
+// E4M3 operands (format codes 0), fp32 accumulate, C layouts as for bf16.
+__device__ __forceinline__ f32x16 mma32_fp8(const i32x8& a, const i32x8& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16_fp8(long a, long b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

@@ -7,7 +7,7 @@ fallback: if the library is missing or a call fails, an exception is raised.
 
 The functions carry the C names.  Tensor layouts are those of the header:
 
-* ``q_idx [Tq, G, d_idx]``, ``k_idx [Tk, d_idx]``
+* ``q_idx [Tq, G, d_idx]``, ``k_idx [Tk, d_idx]`` (fp32, bf16 or float8_e4m3fn)
 * ``q [Tq, Hq, D]``, ``k, v [Tk, Hkv, D]``
 * ``block_idx [Tq, G, topk]`` int32, ``cu_seqlens_q/k [B + 1]`` int32
 * decode: ``q [B, Hq, D]``, ``cache_offsets [B]`` int64, ``ctx_lens [B]`` int32
@@ -23,7 +23,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = range(5)
-MSA_F32, MSA_BF16 = 0, 1
+MSA_F32, MSA_BF16, MSA_FP8_E4M3 = 0, 1, 2
 
 _lib = None
 
@@ -72,7 +72,9 @@ def _dtype_code(t: torch.Tensor) -> int:
         return MSA_F32
     if t.dtype == torch.bfloat16:
         return MSA_BF16
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    if t.dtype == torch.float8_e4m3fn:
+        return MSA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16, or float8_e4m3fn for index tensors)")
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None) -> int:

@@ -64,6 +64,8 @@ def _load():
         lib.oracle_index_topk.argtypes = [vp, vp, ctypes.c_int, i64p, i64p, ctypes.c_int64,
                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           i32p, vp, ctypes.c_int64]
+        lib.oracle_decode_e4m3.restype = None
+        lib.oracle_decode_e4m3.argtypes = [vp, vp, ctypes.c_int64]
         lib.oracle_sparse_attn.restype = ctypes.c_int
         lib.oracle_sparse_attn.argtypes = [vp, vp, vp, ctypes.c_int, i64p, i64p, i32p,
                                            ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -73,7 +75,8 @@ def _load():
 
 
 def _host_array(x):
-    """Return (contiguous numpy array, dtype code): 0 = fp32, 1 = bf16 bits."""
+    """Return (contiguous numpy array, dtype code): 0 = fp32, 1 = bf16 bits,
+    2 = E4M3 bits."""
     try:
         import torch
         if isinstance(x, torch.Tensor):
@@ -84,6 +87,8 @@ def _host_array(x):
                 return np.ascontiguousarray(x.contiguous().view(torch.int16).numpy().view(np.uint16)), 1
             if x.dtype == torch.float32:
                 return np.ascontiguousarray(x.contiguous().numpy()), 0
+            if x.dtype == torch.float8_e4m3fn:
+                return np.ascontiguousarray(x.contiguous().view(torch.uint8).numpy()), 2
             raise TypeError(f"oracle input dtype {x.dtype} not supported")
     except ImportError:  # pragma: no cover - torch is always present here
         pass
@@ -92,7 +97,18 @@ def _host_array(x):
         return np.ascontiguousarray(x), 0
     if x.dtype == np.uint16:
         return np.ascontiguousarray(x), 1
+    if x.dtype == np.uint8:
+        return np.ascontiguousarray(x), 2
     raise TypeError(f"oracle input dtype {x.dtype} not supported")
+
+
+def decode_e4m3(bits) -> np.ndarray:
+    """fp32 values of E4M3 bit patterns (uint8), as the oracle reads them."""
+    lib = _load()
+    a = np.ascontiguousarray(np.asarray(bits, dtype=np.uint8))
+    out = np.empty(a.shape, dtype=np.float32)
+    lib.oracle_decode_e4m3(_ptr(a), _ptr(out), a.size)
+    return out
 
 
 def _ptr(a: np.ndarray):

@@ -25,8 +25,24 @@
 #include <stdlib.h>
 #include <string.h>
 
+/* E4M3: value = (-1)^s * (1 + m/8) * 2^(e-7) for e > 0, (-1)^s * (m/8) * 2^-6
+ * for e = 0; e = 15 with m = 7 is NaN (there is no infinity). */
+static float e4m3_to_float(uint8_t v) {
+  const int s = v >> 7, e = (v >> 3) & 15, m = v & 7;
+  float x;
+  if (e == 15 && m == 7) x = NAN;
+  else if (e == 0) x = ldexpf((float)m, -9);
+  else x = ldexpf((float)(8 + m), e - 10);
+  return s ? -x : x;
+}
+
+void oracle_decode_e4m3(const uint8_t* in, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_to_float(in[i]);
+}
+
 static float load_elem(const void* base, int dtype, int64_t i) {
   if (dtype == 0) return ((const float*)base)[i];
+  if (dtype == 2) return e4m3_to_float(((const uint8_t*)base)[i]);
   uint32_t bits = ((uint32_t)((const uint16_t*)base)[i]) << 16; /* bf16 -> fp32, exact */
   float f;
   memcpy(&f, &bits, sizeof f);
@@ -70,7 +86,7 @@ int oracle_index_topk(const void* q_idx, const void* k_idx, int dtype,
                       float* scores, int64_t nbmax) {
   if (!q_idx || !k_idx || !kstart || !pos || !sel) return 1;
   if (n < 0 || G <= 0 || DI <= 0 || Bk <= 0 || topk <= 0) return 1;
-  if (dtype != 0 && dtype != 1) return 1;
+  if (dtype != 0 && dtype != 1 && dtype != 2) return 1;
 
   int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
@@ -130,7 +146,7 @@ int oracle_sparse_attn(const void* q, const void* k, const void* v, int dtype,
   if (!q || !k || !v || !kstart || !pos || !sel || !out || !lse) return 1;
   if (n < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Bk <= 0 || topk <= 0) return 1;
   if (Hq % Hkv != 0) return 1;
-  if (dtype != 0 && dtype != 1) return 1;
+  if (dtype != 0 && dtype != 1 && dtype != 2) return 1;
   const int r_heads = Hq / Hkv;
 
   int bad = 0;

@@ -27,7 +27,12 @@
  *   - Attention: fp64 throughout, natural-log LSE, no sink term.
  *
  * Element type codes for inputs: 0 = fp32, 1 = bf16 bit patterns (uint16),
- * widened exactly to fp32 by a 16-bit left shift.
+ * widened exactly to fp32 by a 16-bit left shift, 2 = 8-bit floating point
+ * E4M3 bit patterns (uint8) as the OCP 8-bit floating point specification
+ * defines them (sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * subnormals at exponent 0, no infinities, S.1111.111 is NaN), decoded
+ * exactly.  The pages note that the kernels also support fp8; code 2 is used
+ * for the index tensors.
  */
 #ifndef MSA_ORACLE_H
 #define MSA_ORACLE_H
@@ -61,6 +66,9 @@ int oracle_sparse_attn(const void* q, const void* k, const void* v, int dtype,
                        const int64_t* kstart, const int64_t* pos, const int32_t* sel,
                        int64_t n, int Hq, int Hkv, int D, int Bk, int topk,
                        double scale, double* out, double* lse);
+
+/* Decode n E4M3 bit patterns to fp32 (exact), for checking the decoder. */
+void oracle_decode_e4m3(const uint8_t* in, float* out, int64_t n);
 
 #ifdef __cplusplus
 }

@@ -296,3 +296,41 @@ def test_empty_rows_and_negative_positions(oracle_lib):
     sel, out, lse = oracle_lib.prefill(qi, ki, q, k, v, cu_q, cu_k, 2, 2)
     assert np.all(sel[:2] == -1) and np.all(np.isneginf(lse[:2])) and np.all(out[:2] == 0)
     assert np.all(np.isfinite(lse[2:]))
+
+
+def test_e4m3_decoder(oracle_lib):
+    """The oracle's E4M3 decoder against torch's float8_e4m3fn conversion on
+    all 256 codes, and closed forms of the format (bias 7, 3 mantissa bits,
+    subnormals, no infinity, S.1111.111 = NaN)."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle_lib.decode_e4m3(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(got)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    closed = {0x00: 0.0, 0x38: 1.0, 0xB8: -1.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6,
+              0x3C: 1.5, 0x7E: 448.0, 0x40: 2.0, 0x41: 2.25}
+    for c, v in closed.items():
+        assert got[c] == v, (hex(c), got[c], v)
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+
+
+def test_fp8_grid_is_exact_and_selection_matches_bruteforce(oracle_lib):
+    """Index inputs on the 1/8 grid (with the +1.0 planted bias) rounded to
+    E4M3 stay multiples of 1/8, so fp32 scores remain exact: the oracle's
+    selection on E4M3 inputs equals brute force on the integers 8 x value."""
+    from learned_block_sparse_amd import synth
+    wl = synth.WORKLOADS["prefill_32k"]
+    inp = synth.prefill_inputs(wl, seq_lens=[1500], with_main=False, seed=5)
+    q8 = inp["q_idx"].to(torch.float8_e4m3fn)
+    k8 = inp["k_idx"].float().clone()
+    k8[:256] += 1.0            # a planted pair of blocks, including values like 17/8
+    k8 = k8.to(torch.float8_e4m3fn)
+    uq = (q8.float().double().numpy() * 8.0)
+    uk = (k8.float().double().numpy() * 8.0)
+    assert np.all(uq == np.round(uq)) and np.all(uk == np.round(uk))
+    cu = _cu([1500])
+    want, _ = _brute_selection(uq.astype(np.int64), uk.astype(np.int64), cu, cu, wl.block_size, wl.topk)
+    rows, kstart, pos = oracle_lib.rows_prefill(cu, cu)
+    sel = oracle_lib.index_topk(q8, k8, kstart, pos, rows, wl.block_size, wl.topk)
+    np.testing.assert_array_equal(sel, want)
