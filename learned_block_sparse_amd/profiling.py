@@ -24,17 +24,32 @@ import glob
 import json
 import os
 
-# kernels of one library call, by (truncated) kernel-name prefix
+# kernels of one library call, by kernel-name prefix.  rocprofv3 leaves names
+# it cannot demangle (the bf16 instantiations) mangled, and with -T cuts the
+# others down to the bare function name, so the fp8 index call is told apart
+# by its scan kernel: the fp8e4m3 template argument, or the bare name that
+# only the demangled (non-bf16) instantiation produces.
 CALLS = {
     "attention_prefill_128k": ("kvo_zero", "kvo_bucket", "kvo_scan", "kvo_attn", "kvo_combine"),
     "index_prefill_128k": ("_ZN3msa16idx_scan_prefill", "idx_scan_prefill", "idx_select_prefill"),
+    "index_prefill_128k_fp8": ("_ZN3msa16idx_scan_prefill", "idx_scan_prefill", "idx_select_prefill"),
     "index_decode_1m": ("_ZN3msa17idx_decode_scores", "idx_decode_scores", "idx_decode_select"),
     "attention_decode_1m": ("_ZN3msa15sparse_attn_fwd", "sparse_attn_fwd", "_ZN3msa12attn_combine",
                             "attn_combine"),
 }
 # the call's first kernel marks a new call
 CALL_START = {"attention_prefill_128k": "kvo_zero", "index_prefill_128k": "idx_scan_prefill",
-              "index_decode_1m": "idx_decode_scores", "attention_decode_1m": "sparse_attn_fwd"}
+              "index_prefill_128k_fp8": "idx_scan_prefill", "index_decode_1m": "idx_decode_scores",
+              "attention_decode_1m": "sparse_attn_fwd"}
+
+
+def _is_fp8_scan(name):
+    return "fp8e4m3" in name or name == "idx_scan_prefill"
+
+
+# calls told apart by the element type of their first kernel
+CALL_FILTER = {"index_prefill_128k": lambda n: not _is_fp8_scan(n),
+               "index_prefill_128k_fp8": _is_fp8_scan}
 
 
 def _rows(d):
@@ -55,6 +70,7 @@ def _matches(name, prefixes):
 def per_call_kb(rows, call):
     """Sum of the counter (KB) over each call's kernels, one entry per call."""
     out, cur = [], None
+    keep = CALL_FILTER.get(call, lambda n: True)
     for r in rows:
         name = r["Kernel_Name"]
         if not _matches(name, CALLS[call]):
@@ -62,7 +78,7 @@ def per_call_kb(rows, call):
         if CALL_START[call] in name:
             if cur is not None:
                 out.append(cur)
-            cur = 0.0
+            cur = 0.0 if keep(name) else None
         if cur is not None:
             cur += float(r["Counter_Value"])
     if cur is not None:
@@ -106,6 +122,7 @@ def main():
     lines.append("")
     sources = {"attention_prefill_128k": ("prefill-fetch", "prefill-write"),
                "index_prefill_128k": ("prefill-fetch", "prefill-write"),
+               "index_prefill_128k_fp8": ("prefill-fetch", "prefill-write"),
                "index_decode_1m": ("decode-fetch", "decode-write"),
                "attention_decode_1m": ("decode-fetch", "decode-write")}
     digest = build.source_digest()
