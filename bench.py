@@ -186,7 +186,7 @@ def main():
     if dominant == "index":
         dom_ms = float(np.mean(per_call_idx))
         dom_flops = idx_flops / len(calls)
-        kernel = "idx_scan_prefill<bf16,128> + idx_merge_prefill (one msa_index_topk call)"
+        kernel = "idx_scan_prefill<bf16,128> + idx_select_prefill (one msa_index_topk call)"
         traffic = traffic_record("index_prefill_128k")
     else:
         dom_ms = float(np.mean(per_call_att))
@@ -242,7 +242,28 @@ def main():
     result["prefill"]["index_fp8"] = {
         "ms": round(idx8_ms, 3), "tflops": round(idx_flops / (idx8_ms / 1e3) / 1e12, 1),
         "frac_fp8_mfma": round(idx_flops / (idx8_ms / 1e3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
-    del inp, calls, q8, k8
+    # The attention calls with K and V in fp8 E4M3 (bf16 q and out; the ids of
+    # the calls above, which equal the bf16 ones on these inputs).
+    kv8, vv8 = inp["k"].to(torch.float8_e4m3fn), inp["v"].to(torch.float8_e4m3fn)
+
+    def attn_fp8kv_step():
+        for c in calls:
+            msa.msa_sparse_attn_prefill_ex(c["q"], kv8, vv8, c["ids"], c["cu_q"], c["cu_k"], c["m"], c["hi"],
+                                           wl.block_size, wl.topk, out=c["out"], lse=c["lse"],
+                                           workspace=c["ws_a"], stream=stream)
+
+    attn_fp8kv_step()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        attn_fp8kv_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    att8_ms = e0.elapsed_time(e1) / args.steps
+    result["prefill"]["attention_fp8_kv"] = {
+        "ms": round(att8_ms, 3), "tflops": round(att_flops / (att8_ms / 1e3) / 1e12, 1),
+        "frac_mfma": round(att_flops / (att8_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del inp, calls, q8, k8, kv8, vv8
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ decode
@@ -325,7 +346,31 @@ def main():
         result["decode"]["fp8_index"] = {
             "us_per_step": round(d8_us, 1), "bytes_per_step": idx8_b + att_b, "achieved_GBs": round(gbs8, 1),
             "frac_hbm": round(gbs8 / PEAK_HBM_GBS, 4)}
-        del d, q8, k8
+        # every cache in fp8 E4M3: index keys (and index queries), K and V; bf16 q and out
+        kc8, vc8 = d["k"].to(torch.float8_e4m3fn), d["v"].to(torch.float8_e4m3fn)
+
+        def dstep_all8():
+            msa.msa_index_topk(q8, k8, d["cu_seqlens_q"], d["cu_seqlens_k"], 1, max(ctx), wd.block_size,
+                               wd.topk, block_idx=ids, workspace=ws_i, stream=stream)
+            msa.msa_sparse_attn_decode_ex(d["q"], kc8, vc8, ids, d["k_offsets"], d["ctx_lens"], max(ctx),
+                                          wd.block_size, wd.topk, out=out, lse=lse, workspace=ws_a, stream=stream)
+
+        for _ in range(5):
+            dstep_all8()
+        torch.cuda.synchronize()
+        e_lo.record(stream)
+        for s in range(args.decode_steps):
+            dstep_all8()
+        e_hi.record(stream)
+        torch.cuda.synchronize()
+        da8_us = e_lo.elapsed_time(e_hi) * 1e3 / args.decode_steps
+        ia8_b, aa8_b = workmodel.decode_bytes(ctx, Hq, G, D, DI, wd.block_size, wd.topk, elem_bytes=1,
+                                              kv_elem_bytes=1, qo_elem_bytes=2)
+        gbsa8 = (ia8_b + aa8_b) / (da8_us * 1e-6) / 1e9
+        result["decode"]["fp8_index_and_kv"] = {
+            "us_per_step": round(da8_us, 1), "bytes_per_step": ia8_b + aa8_b, "achieved_GBs": round(gbsa8, 1),
+            "frac_hbm": round(gbsa8 / PEAK_HBM_GBS, 4)}
+        del d, q8, k8, kc8, vc8
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU baseline

@@ -69,8 +69,10 @@ typedef enum {
 
 /* Element types.  MSA_FP8_E4M3 is the OCP 8-bit floating point format E4M3
  * (sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities; the
- * pages note the kernels also support fp8): accepted for the index tensors of
- * msa_index_topk only; the attention calls return MSA_ERR_UNSUPPORTED. */
+ * pages note the kernels also support fp8).  It is accepted for the index
+ * tensors of msa_index_topk and, through the *_ex attention calls, for the
+ * K/V tensors under bf16 q/out; the plain attention calls (one type for q, K,
+ * V and out) return MSA_ERR_UNSUPPORTED for it. */
 typedef enum { MSA_F32 = 0, MSA_BF16 = 1, MSA_FP8_E4M3 = 2 } msa_dtype_t;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -195,6 +197,38 @@ msa_status_t msa_sparse_attn_decode(const void* q, const void* k_cache, const vo
                                     int head_dim, int block_size, int topk, float softmax_scale,
                                     int num_splits, void* out, float* lse, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Main branch with the K/V element type given on its own.
+ *
+ * The same calls as msa_sparse_attn_prefill / msa_sparse_attn_decode, with
+ * `dtype` the element type of q and out and `kv_dtype` that of k and v (the
+ * KV cache on the decode path).  Supported pairs: (F32, F32), (BF16, BF16)
+ * (exactly the plain calls) and (BF16, FP8_E4M3): an 8-bit KV cache, half
+ * the bytes per cached token, for the fp8 support the atlas record of
+ * MiniMax M3 notes.  E4M3 K/V elements are widened exactly to bf16 as they
+ * are loaded; q.k and P.V then run on the same bf16 MFMAs with fp32
+ * accumulation, so an E4M3 K/V tensor gives bit-identical out and lse to
+ * the bf16 call on the same values.  There is no scale operand: a per-tensor
+ * K scale can be folded into softmax_scale, a V scale applied to out.
+ * Other pairs return MSA_ERR_UNSUPPORTED; the workspace size is that of the
+ * plain call.
+ * ---------------------------------------------------------------------- */
+msa_status_t msa_sparse_attn_prefill_ex(const void* q, const void* k, const void* v, msa_dtype_t dtype,
+                                        msa_dtype_t kv_dtype, const int32_t* block_idx,
+                                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                                        int max_q_len, int max_kv_len, int num_heads, int num_kv_heads,
+                                        int head_dim, int block_size, int topk, float softmax_scale,
+                                        int num_splits, void* out, float* lse, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
+
+msa_status_t msa_sparse_attn_decode_ex(const void* q, const void* k_cache, const void* v_cache,
+                                       msa_dtype_t dtype, msa_dtype_t kv_dtype, const int32_t* block_idx,
+                                       const int64_t* cache_offsets, const int32_t* ctx_lens, int batch,
+                                       int max_ctx, int num_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int topk, float softmax_scale, int num_splits,
+                                       void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
 
 #ifdef __cplusplus
 }

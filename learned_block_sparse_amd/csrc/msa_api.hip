@@ -172,21 +172,44 @@ size_t msa_sparse_attn_workspace_size(int batch, int max_q_len, int max_kv_len, 
 }
 
 static msa_status_t check_attn(const void* q, const void* k, const void* v, msa_dtype_t dtype,
-                               const int32_t* block_idx, const void* out, int batch, int num_heads,
-                               int num_kv_heads, int head_dim, int block_size, int topk, int num_splits) {
+                               msa_dtype_t kv_dtype, const int32_t* block_idx, const void* out, int batch,
+                               int num_heads, int num_kv_heads, int head_dim, int block_size, int topk,
+                               int num_splits) {
   if (!q || !k || !v || !block_idx || !out) return MSA_ERR_INVALID_ARG;
   if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || topk <= 0 ||
-      num_splits < 0 || !dtype_ok(dtype))
+      num_splits < 0 || !dtype_ok(dtype) || !dtype_ok(kv_dtype))
     return MSA_ERR_INVALID_ARG;
   if (num_heads % num_kv_heads != 0) return MSA_ERR_INVALID_ARG;
   if (block_size != kBlock || head_dim != kHeadDim || topk > 16 || num_heads / num_kv_heads > 16 ||
-      num_kv_heads > 16 || dtype == MSA_FP8_E4M3)  // fp8 is implemented for the index tensors only
+      num_kv_heads > 16)
     return MSA_ERR_UNSUPPORTED;
+  // element types: q/out fp32 or bf16; K/V of the same type, or E4M3 under bf16 q/out
+  const bool same = (dtype == MSA_F32 || dtype == MSA_BF16) && kv_dtype == dtype;
+  const bool kv8 = dtype == MSA_BF16 && kv_dtype == MSA_FP8_E4M3;
+  if (!same && !kv8) return MSA_ERR_UNSUPPORTED;
   return MSA_OK;
 }
 
 static float resolve_scale(float s, int head_dim) {
   return s > 0.f ? s : 1.0f / sqrtf((float)head_dim);
+}
+
+msa_status_t msa_sparse_attn_prefill_ex(const void* q, const void* k, const void* v, msa_dtype_t dtype,
+                                        msa_dtype_t kv_dtype, const int32_t* block_idx,
+                                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                                        int max_q_len, int max_kv_len, int num_heads, int num_kv_heads,
+                                        int head_dim, int block_size, int topk, float softmax_scale,
+                                        int num_splits, void* out, float* lse, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+  msa_status_t st = check_attn(q, k, v, dtype, kv_dtype, block_idx, out, batch, num_heads, num_kv_heads,
+                               head_dim, block_size, topk, num_splits);
+  if (st != MSA_OK) return st;
+  if (!cu_seqlens_q || !cu_seqlens_k || max_q_len <= 0 || max_kv_len <= 0) return MSA_ERR_INVALID_ARG;
+  const AttnPlan pl = plan_attn(batch, max_q_len, max_kv_len, num_heads, num_kv_heads, head_dim, topk, num_splits);
+  if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes)) return MSA_ERR_WORKSPACE;
+  AttnArgs a{q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, nullptr, nullptr, batch, num_heads, num_kv_heads,
+             topk, resolve_scale(softmax_scale, head_dim), out, lse};
+  return hip_status(launch_sparse_attn(pl, (int)dtype, (int)kv_dtype, a, workspace, stream));
 }
 
 msa_status_t msa_sparse_attn_prefill(const void* q, const void* k, const void* v, msa_dtype_t dtype,
@@ -196,15 +219,27 @@ msa_status_t msa_sparse_attn_prefill(const void* q, const void* k, const void* v
                                      int block_size, int topk, float softmax_scale, int num_splits,
                                      void* out, float* lse, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream) {
-  msa_status_t st = check_attn(q, k, v, dtype, block_idx, out, batch, num_heads, num_kv_heads, head_dim,
-                               block_size, topk, num_splits);
+  return msa_sparse_attn_prefill_ex(q, k, v, dtype, dtype, block_idx, cu_seqlens_q, cu_seqlens_k, batch,
+                                    max_q_len, max_kv_len, num_heads, num_kv_heads, head_dim, block_size, topk,
+                                    softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+}
+
+msa_status_t msa_sparse_attn_decode_ex(const void* q, const void* k_cache, const void* v_cache,
+                                       msa_dtype_t dtype, msa_dtype_t kv_dtype, const int32_t* block_idx,
+                                       const int64_t* cache_offsets, const int32_t* ctx_lens, int batch,
+                                       int max_ctx, int num_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int topk, float softmax_scale, int num_splits,
+                                       void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  msa_status_t st = check_attn(q, k_cache, v_cache, dtype, kv_dtype, block_idx, out, batch, num_heads,
+                               num_kv_heads, head_dim, block_size, topk, num_splits);
   if (st != MSA_OK) return st;
-  if (!cu_seqlens_q || !cu_seqlens_k || max_q_len <= 0 || max_kv_len <= 0) return MSA_ERR_INVALID_ARG;
-  const AttnPlan pl = plan_attn(batch, max_q_len, max_kv_len, num_heads, num_kv_heads, head_dim, topk, num_splits);
+  if (!cache_offsets || !ctx_lens || max_ctx <= 0) return MSA_ERR_INVALID_ARG;
+  const AttnPlan pl = plan_attn(batch, 1, max_ctx, num_heads, num_kv_heads, head_dim, topk, num_splits);
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes)) return MSA_ERR_WORKSPACE;
-  AttnArgs a{q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, nullptr, nullptr, batch, num_heads, num_kv_heads,
-             topk, resolve_scale(softmax_scale, head_dim), out, lse};
-  return hip_status(launch_sparse_attn(pl, (int)dtype, a, workspace, stream));
+  AttnArgs a{q, k_cache, v_cache, block_idx, nullptr, nullptr, cache_offsets, ctx_lens, batch, num_heads,
+             num_kv_heads, topk, resolve_scale(softmax_scale, head_dim), out, lse};
+  return hip_status(launch_sparse_attn(pl, (int)dtype, (int)kv_dtype, a, workspace, stream));
 }
 
 msa_status_t msa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -214,15 +249,9 @@ msa_status_t msa_sparse_attn_decode(const void* q, const void* k_cache, const vo
                                     int head_dim, int block_size, int topk, float softmax_scale,
                                     int num_splits, void* out, float* lse, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream) {
-  msa_status_t st = check_attn(q, k_cache, v_cache, dtype, block_idx, out, batch, num_heads, num_kv_heads,
-                               head_dim, block_size, topk, num_splits);
-  if (st != MSA_OK) return st;
-  if (!cache_offsets || !ctx_lens || max_ctx <= 0) return MSA_ERR_INVALID_ARG;
-  const AttnPlan pl = plan_attn(batch, 1, max_ctx, num_heads, num_kv_heads, head_dim, topk, num_splits);
-  if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes)) return MSA_ERR_WORKSPACE;
-  AttnArgs a{q, k_cache, v_cache, block_idx, nullptr, nullptr, cache_offsets, ctx_lens, batch, num_heads,
-             num_kv_heads, topk, resolve_scale(softmax_scale, head_dim), out, lse};
-  return hip_status(launch_sparse_attn(pl, (int)dtype, a, workspace, stream));
+  return msa_sparse_attn_decode_ex(q, k_cache, v_cache, dtype, dtype, block_idx, cache_offsets, ctx_lens, batch,
+                                   max_ctx, num_heads, num_kv_heads, head_dim, block_size, topk, softmax_scale,
+                                   num_splits, out, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

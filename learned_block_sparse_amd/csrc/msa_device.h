@@ -52,6 +52,30 @@ __device__ __forceinline__ frag8<T> load8(const T* p) {
   return *reinterpret_cast<const frag8<T>*>(p);
 }
 
+// Eight E4M3 values (8 bytes) widened to the bf16 MFMA operand.  Exact: every
+// E4M3 value (subnormals, signed zero and NaN included) is a bf16 value.  The
+// gfx950 conversion takes two bytes of a dword per instruction (scale 1).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8 widen8_e4m3(u32x2 w) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Eight K/V elements of storage type TKV as the compute-type operand T: a
+// plain load when the two agree, E4M3 widened to bf16 otherwise.
+template <typename T, typename TKV>
+__device__ __forceinline__ frag8<T> load8_kv(const TKV* p) {
+  if constexpr (sizeof(TKV) == 1) {
+    static_assert(sizeof(T) == 2, "E4M3 K/V is widened to bf16");
+    return widen8_e4m3(*reinterpret_cast<const u32x2*>(p));
+  } else {
+    return load8(p);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ frag8<T> zero8() {
   frag8<T> z;

@@ -67,8 +67,11 @@ struct AttnArgs {
   float* lse;
 };
 
-hipError_t launch_sparse_attn(const AttnPlan& pl, int dtype, const AttnArgs& a, void* ws, hipStream_t st);
-hipError_t launch_attn_kvouter(const AttnPlan& pl, const AttnArgs& a, void* ws, hipStream_t st);
+// dtype: element type of q and out (0 fp32, 1 bf16); kv_dtype: of K and V
+// (equal to dtype, or 2 = E4M3 with bf16 q/out)
+hipError_t launch_sparse_attn(const AttnPlan& pl, int dtype, int kv_dtype, const AttnArgs& a, void* ws,
+                              hipStream_t st);
+hipError_t launch_attn_kvouter(const AttnPlan& pl, bool kv_e4m3, const AttnArgs& a, void* ws, hipStream_t st);
 size_t kvo_part_slot_bytes();
 int kvo_window_rows();
 

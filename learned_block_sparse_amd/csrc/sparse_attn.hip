@@ -76,8 +76,8 @@ __device__ __forceinline__ void store4<float>(float* p, float a, float b, float 
 // V rows key0 + 32ks .. +31 of one block into registers, as the units of the
 // transposed staging: unit u = (key quad u%8, d octet u/8); lane handles
 // u = lane and lane + 64.  Rows past p clamp to p (their P is 0).
-template <typename T>
-__device__ __forceinline__ void load_v_chunk(const T* vseq, int64_t row_stride, int64_t key0, int64_t p, int ks,
+template <typename T, typename TKV>
+__device__ __forceinline__ void load_v_chunk(const TKV* vseq, int64_t row_stride, int64_t key0, int64_t p, int ks,
                                              int lane, frag8<T> (&r)[2][4]) {
 #pragma unroll
   for (int uu = 0; uu < 2; ++uu) {
@@ -87,12 +87,14 @@ __device__ __forceinline__ void load_v_chunk(const T* vseq, int64_t row_stride, 
     for (int jj = 0; jj < 4; ++jj) {
       int64_t key = key0 + 32 * ks + 4 * kq + jj;
       if (key > p) key = p;
-      r[uu][jj] = load8(vseq + key * row_stride + 8 * o8);
+      r[uu][jj] = load8_kv<T>(vseq + key * row_stride + 8 * o8);
     }
   }
 }
 
-template <typename T>
+// T: element type of q, out and the MFMA operands; TKV: storage type of K
+// and V (T, or E4M3 widened to bf16 as it is loaded).
+template <typename T, typename TKV>
 __global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs args) {
   using V = VtTile<T>;
   __shared__ __attribute__((aligned(16))) T vt_all[kAttnThreads / kWave][V::kElems];
@@ -127,8 +129,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs a
   const int64_t p = (int64_t)N - M + (t - q0);
 
   const T* __restrict__ qg = static_cast<const T*>(args.q);
-  const T* __restrict__ kg = static_cast<const T*>(args.k);
-  const T* __restrict__ vg = static_cast<const T*>(args.v);
+  const TKV* __restrict__ kg = static_cast<const TKV*>(args.k);
+  const TKV* __restrict__ vg = static_cast<const TKV*>(args.v);
   const int R = args.Hq / G;
   const int h = lane & 15;     // head column of the MFMA tile
   const int a = lane >> 4;     // lane group: contraction slots 8a..8a+7
@@ -154,8 +156,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs a
     const int i_lo = s * args.bps;
     const int i_hi = min(i_lo + args.bps, args.topk);
     const int64_t row_stride = (int64_t)G * kHeadDim;   // elements between tokens
-    const T* kseq = kg + kb0 * row_stride + g * kHeadDim;
-    const T* vseq = vg + kb0 * row_stride + g * kHeadDim;
+    const TKV* kseq = kg + kb0 * row_stride + g * kHeadDim;
+    const TKV* vseq = vg + kb0 * row_stride + g * kHeadDim;
 
     for (int i = i_lo; i < i_hi; ++i) {
       const int c = sel[i];
@@ -174,9 +176,9 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs a
       for (int kt = 0; kt < kBlock / 16; ++kt) {
         int64_t key = key0 + 16 * kt + h;   // A operand row = lane % 16
         if (key > p) key = p;               // stay inside the sequence; masked below
-        const T* kp = kseq + key * row_stride + 8 * a;
+        const TKV* kp = kseq + key * row_stride + 8 * a;
 #pragma unroll
-        for (int ds = 0; ds < kHeadDim / 32; ++ds) kfr[kt][ds] = load8(kp + 32 * ds);
+        for (int ds = 0; ds < kHeadDim / 32; ++ds) kfr[kt][ds] = load8_kv<T>(kp + 32 * ds);
       }
       frag8<T> vbuf[2][2][4];
       load_v_chunk<T>(vseq, row_stride, key0, p, 0, lane, vbuf[0]);
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(256) void attn_combine(const float* __restrict__ pa
   if (lse && d0 == 0) lse[rh] = L;
 }
 
-template <typename T>
+template <typename T, typename TKV>
 static hipError_t launch_attn_t(const AttnPlan& pl, const AttnArgs& a, void* ws, hipStream_t st) {
   AttnKernelArgs k;
   k.q = a.q; k.k = a.k; k.v = a.v; k.block_idx = a.block_idx;
@@ -347,7 +349,7 @@ static hipError_t launch_attn_t(const AttnPlan& pl, const AttnArgs& a, void* ws,
   k.part_o = pl.nsplit > 1 ? reinterpret_cast<float*>(w) : nullptr;
   k.part_lse = pl.nsplit > 1 ? reinterpret_cast<float*>(w + pl.part_o_bytes) : nullptr;
   const int64_t items = pl.rows_bound * a.Hkv * pl.nsplit;
-  hipLaunchKernelGGL(sparse_attn_fwd<T>, dim3((unsigned)((items + 3) / 4)), dim3(kAttnThreads), 0, st, k);
+  hipLaunchKernelGGL((sparse_attn_fwd<T, TKV>), dim3((unsigned)((items + 3) / 4)), dim3(kAttnThreads), 0, st, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nsplit == 1) return e;
   const int64_t rh = pl.rows_bound * a.Hq;
@@ -356,17 +358,20 @@ static hipError_t launch_attn_t(const AttnPlan& pl, const AttnArgs& a, void* ws,
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_attn(const AttnPlan& pl, int dtype, const AttnArgs& a, void* ws, hipStream_t st) {
+hipError_t launch_sparse_attn(const AttnPlan& pl, int dtype, int kv_dtype, const AttnArgs& a, void* ws,
+                              hipStream_t st) {
+  const bool kv8 = kv_dtype == 2;  // bf16 q/out with E4M3 K/V
   if (pl.kvouter) {
-    if (dtype != 0) return launch_attn_kvouter(pl, a, ws, st);
+    if (dtype != 0) return launch_attn_kvouter(pl, kv8, a, ws, st);
     // fp32 inputs: the query-outer schedule with one chunk (needs no workspace)
     AttnPlan q1 = pl;
     q1.kvouter = false;
     q1.nsplit = 1;
     q1.bps = a.topk;
-    return launch_attn_t<float>(q1, a, ws, st);
+    return launch_attn_t<float, float>(q1, a, ws, st);
   }
-  return dtype == 0 ? launch_attn_t<float>(pl, a, ws, st) : launch_attn_t<bf16>(pl, a, ws, st);
+  if (dtype == 0) return launch_attn_t<float, float>(pl, a, ws, st);
+  return kv8 ? launch_attn_t<bf16, fp8e4m3>(pl, a, ws, st) : launch_attn_t<bf16, bf16>(pl, a, ws, st);
 }
 
 }  // namespace msa

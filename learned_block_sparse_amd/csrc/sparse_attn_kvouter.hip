@@ -45,8 +45,8 @@ constexpr int kRmax = 16;       // heads per group held by one partial slot
 
 struct KvoArgs {
   const bf16* q;
-  const bf16* k;
-  const bf16* v;
+  const void* k;  // bf16, or E4M3 (widened to bf16 as it is staged)
+  const void* v;
   const int32_t* block_idx;
   const int32_t* cu_q;
   const int32_t* cu_k;
@@ -332,6 +332,7 @@ __device__ __forceinline__ void kvo_pair(const KvoArgs& a, PairQ& P, int e_pf, i
     if (colok && a32 == 0) a.part_lse[slot * kRmax + h] = mx * 0.69314718055994530942f + logf(sum);
 }
 
+template <typename TKV>
 __global__ __launch_bounds__(kKvoThreads, 2) void kvo_attn(KvoArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 k_lds[kBlock * kKStride];
   __shared__ __attribute__((aligned(16))) bf16 vt_lds[kHeadDim * kVtStride];
@@ -350,17 +351,19 @@ __global__ __launch_bounds__(kKvoThreads, 2) void kvo_attn(KvoArgs a) {
   const int64_t q0 = a.cu_q[b];
   const int M = a.cu_q[b + 1] - a.cu_q[b];
   const int64_t rs = (int64_t)a.G * kHeadDim;
+  const TKV* kg = static_cast<const TKV*>(a.k);
+  const TKV* vg = static_cast<const TKV*>(a.v);
 
   // ---- stage K row-major and V transposed (rows past the sequence end clamp
   // to its last row; their scores are masked)
   {
-    u32x4 kr[8];
+    bf16x8 kr[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int piece = threadIdx.x + u * kKvoThreads;
       const int row = piece >> 4, col = (piece & 15) * 8;
       const int64_t key = min(c * kBlock + row, N - 1);
-      kr[u] = *reinterpret_cast<const u32x4*>(a.k + (kb0 + key) * rs + g * kHeadDim + col);
+      kr[u] = load8_kv<bf16>(kg + (kb0 + key) * rs + g * kHeadDim + col);
     }
     // V unit = (key quad kq, dim octet o8): 4 rows x 8 dims, written as 8 runs of 4 keys
     bf16x8 vr[2][4];
@@ -371,14 +374,14 @@ __global__ __launch_bounds__(kKvoThreads, 2) void kvo_attn(KvoArgs a) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int64_t key = min(c * kBlock + 4 * kq + jj, N - 1);
-        vr[uu][jj] = load8(a.v + (kb0 + key) * rs + g * kHeadDim + 8 * o8);
+        vr[uu][jj] = load8_kv<bf16>(vg + (kb0 + key) * rs + g * kHeadDim + 8 * o8);
       }
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int piece = threadIdx.x + u * kKvoThreads;
       const int row = piece >> 4, col = (piece & 15) * 8;
-      *reinterpret_cast<u32x4*>(k_lds + row * kKStride + col) = kr[u];
+      *reinterpret_cast<bf16x8*>(k_lds + row * kKStride + col) = kr[u];
     }
 #pragma unroll
     for (int uu = 0; uu < 2; ++uu) {
@@ -477,12 +480,12 @@ __global__ __launch_bounds__(256) void kvo_combine(KvoArgs a) {
   if (a.lse && (lane & 3) == 0) a.lse[t * a.Hq + g * R + h] = L;
 }
 
-hipError_t launch_attn_kvouter(const AttnPlan& pl, const AttnArgs& x, void* ws, hipStream_t st) {
+hipError_t launch_attn_kvouter(const AttnPlan& pl, bool kv_e4m3, const AttnArgs& x, void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
   KvoArgs a;
   a.q = static_cast<const bf16*>(x.q);
-  a.k = static_cast<const bf16*>(x.k);
-  a.v = static_cast<const bf16*>(x.v);
+  a.k = x.k;
+  a.v = x.v;
   a.block_idx = x.block_idx;
   a.cu_q = x.cu_q;
   a.cu_k = x.cu_k;
@@ -512,7 +515,8 @@ hipError_t launch_attn_kvouter(const AttnPlan& pl, const AttnArgs& x, void* ws, 
     hipLaunchKernelGGL(kvo_scan, dim3(1), dim3(1024), 0, st, a, nbk);
     hipLaunchKernelGGL(kvo_bucket<true>, dim3(eg), dim3(256), 0, st, a, nbk);
     const int64_t ub = entries / kKvoChunk + (entries < nbk ? entries : nbk) + 1;
-    hipLaunchKernelGGL(kvo_attn, dim3((unsigned)ub), dim3(kKvoThreads), 0, st, a);
+    if (kv_e4m3) hipLaunchKernelGGL(kvo_attn<fp8e4m3>, dim3((unsigned)ub), dim3(kKvoThreads), 0, st, a);
+    else hipLaunchKernelGGL(kvo_attn<bf16>, dim3((unsigned)ub), dim3(kKvoThreads), 0, st, a);
     const int64_t items = (a.row_hi - a.row_lo) * a.G;
     hipLaunchKernelGGL(kvo_combine, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();

@@ -63,6 +63,12 @@ def lib():
         L.msa_sparse_attn_decode.restype = i32
         L.msa_sparse_attn_decode.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                              ctypes.c_float, i32, vp, vp, vp, sz, vp]
+        L.msa_sparse_attn_prefill_ex.restype = i32
+        L.msa_sparse_attn_prefill_ex.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                                 i32, i32, ctypes.c_float, i32, vp, vp, vp, sz, vp]
+        L.msa_sparse_attn_decode_ex.restype = i32
+        L.msa_sparse_attn_decode_ex.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                                i32, ctypes.c_float, i32, vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -74,7 +80,7 @@ def _dtype_code(t: torch.Tensor) -> int:
         return MSA_BF16
     if t.dtype == torch.float8_e4m3fn:
         return MSA_FP8_E4M3
-    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16, or float8_e4m3fn for index tensors)")
+    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16, or float8_e4m3fn for index and K/V tensors)")
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
@@ -140,11 +146,8 @@ def msa_index_topk(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, max_q_len: int, max
     return block_idx
 
 
-def msa_sparse_attn_prefill(q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_q_len: int,
-                            max_kv_len: int, block_size: int = 128, topk: int = 16,
-                            softmax_scale: float = 0.0, num_splits: int = 0, out=None, lse=None,
-                            return_lse: bool = True, workspace=None, stream=None):
-    """``(out [Tq, Hq, D], lse [Tq, Hq] fp32 or None)``."""
+def _prefill(ex, q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_q_len, max_kv_len, block_size, topk,
+             softmax_scale, num_splits, out, lse, return_lse, workspace, stream):
     tq, hq, d = q.shape
     hkv = k.shape[1]
     batch = cu_seqlens_q.numel() - 1
@@ -154,22 +157,22 @@ def msa_sparse_attn_prefill(q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_
         lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
     need = msa_sparse_attn_workspace_size(batch, max_q_len, max_kv_len, hq, hkv, d, topk, num_splits)
     ws, ws_bytes = _workspace(need, q.device, workspace)
-    st = lib().msa_sparse_attn_prefill(
-        _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dtype_code(q),
-        _dev(block_idx, "block_idx", torch.int32), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
-        _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32), batch, max_q_len, max_kv_len, hq, hkv, d,
-        block_size, topk, float(softmax_scale), num_splits, _dev(out, "out", q.dtype),
-        _dev(lse, "lse", torch.float32) if lse is not None else None,
-        ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
-    _check(st, "msa_sparse_attn_prefill")
+    kv_dtype = k.dtype if ex else q.dtype
+    ptrs = [_dev(q, "q"), _dev(k, "k", kv_dtype), _dev(v, "v", kv_dtype), _dtype_code(q)]
+    if ex:
+        ptrs.append(_dtype_code(k))
+    fn = lib().msa_sparse_attn_prefill_ex if ex else lib().msa_sparse_attn_prefill
+    st = fn(*ptrs, _dev(block_idx, "block_idx", torch.int32), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+            _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32), batch, max_q_len, max_kv_len, hq, hkv, d,
+            block_size, topk, float(softmax_scale), num_splits, _dev(out, "out", q.dtype),
+            _dev(lse, "lse", torch.float32) if lse is not None else None,
+            ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
+    _check(st, "msa_sparse_attn_prefill_ex" if ex else "msa_sparse_attn_prefill")
     return out, lse
 
 
-def msa_sparse_attn_decode(q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx: int,
-                           block_size: int = 128, topk: int = 16, softmax_scale: float = 0.0,
-                           num_splits: int = 0, out=None, lse=None, return_lse: bool = True,
-                           workspace=None, stream=None):
-    """``(out [B, Hq, D], lse [B, Hq] fp32 or None)`` for one decode step."""
+def _decode(ex, q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx, block_size, topk,
+            softmax_scale, num_splits, out, lse, return_lse, workspace, stream):
     batch, hq, d = q.shape
     hkv = k_cache.shape[1]
     if out is None:
@@ -178,12 +181,52 @@ def msa_sparse_attn_decode(q, k_cache, v_cache, block_idx, cache_offsets, ctx_le
         lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
     need = msa_sparse_attn_workspace_size(batch, 1, max_ctx, hq, hkv, d, topk, num_splits)
     ws, ws_bytes = _workspace(need, q.device, workspace)
-    st = lib().msa_sparse_attn_decode(
-        _dev(q, "q"), _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype), _dtype_code(q),
-        _dev(block_idx, "block_idx", torch.int32), _dev(cache_offsets, "cache_offsets", torch.int64),
-        _dev(ctx_lens, "ctx_lens", torch.int32), batch, max_ctx, hq, hkv, d, block_size, topk,
-        float(softmax_scale), num_splits, _dev(out, "out", q.dtype),
-        _dev(lse, "lse", torch.float32) if lse is not None else None,
-        ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
-    _check(st, "msa_sparse_attn_decode")
+    kv_dtype = k_cache.dtype if ex else q.dtype
+    ptrs = [_dev(q, "q"), _dev(k_cache, "k_cache", kv_dtype), _dev(v_cache, "v_cache", kv_dtype), _dtype_code(q)]
+    if ex:
+        ptrs.append(_dtype_code(k_cache))
+    fn = lib().msa_sparse_attn_decode_ex if ex else lib().msa_sparse_attn_decode
+    st = fn(*ptrs, _dev(block_idx, "block_idx", torch.int32), _dev(cache_offsets, "cache_offsets", torch.int64),
+            _dev(ctx_lens, "ctx_lens", torch.int32), batch, max_ctx, hq, hkv, d, block_size, topk,
+            float(softmax_scale), num_splits, _dev(out, "out", q.dtype),
+            _dev(lse, "lse", torch.float32) if lse is not None else None,
+            ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
+    _check(st, "msa_sparse_attn_decode_ex" if ex else "msa_sparse_attn_decode")
     return out, lse
+
+
+def msa_sparse_attn_prefill(q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_q_len: int,
+                            max_kv_len: int, block_size: int = 128, topk: int = 16,
+                            softmax_scale: float = 0.0, num_splits: int = 0, out=None, lse=None,
+                            return_lse: bool = True, workspace=None, stream=None):
+    """``(out [Tq, Hq, D], lse [Tq, Hq] fp32 or None)``; q, k, v share a dtype."""
+    return _prefill(False, q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_q_len, max_kv_len, block_size,
+                    topk, softmax_scale, num_splits, out, lse, return_lse, workspace, stream)
+
+
+def msa_sparse_attn_prefill_ex(q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_q_len: int,
+                               max_kv_len: int, block_size: int = 128, topk: int = 16,
+                               softmax_scale: float = 0.0, num_splits: int = 0, out=None, lse=None,
+                               return_lse: bool = True, workspace=None, stream=None):
+    """As msa_sparse_attn_prefill with the K/V element type taken from ``k``
+    (e.g. bfloat16 q with float8_e4m3fn k and v)."""
+    return _prefill(True, q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_q_len, max_kv_len, block_size,
+                    topk, softmax_scale, num_splits, out, lse, return_lse, workspace, stream)
+
+
+def msa_sparse_attn_decode(q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx: int,
+                           block_size: int = 128, topk: int = 16, softmax_scale: float = 0.0,
+                           num_splits: int = 0, out=None, lse=None, return_lse: bool = True,
+                           workspace=None, stream=None):
+    """``(out [B, Hq, D], lse [B, Hq] fp32 or None)`` for one decode step."""
+    return _decode(False, q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx, block_size, topk,
+                   softmax_scale, num_splits, out, lse, return_lse, workspace, stream)
+
+
+def msa_sparse_attn_decode_ex(q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx: int,
+                              block_size: int = 128, topk: int = 16, softmax_scale: float = 0.0,
+                              num_splits: int = 0, out=None, lse=None, return_lse: bool = True,
+                              workspace=None, stream=None):
+    """As msa_sparse_attn_decode with the KV-cache element type taken from ``k_cache``."""
+    return _decode(True, q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx, block_size, topk,
+                   softmax_scale, num_splits, out, lse, return_lse, workspace, stream)

@@ -55,15 +55,19 @@ def prefill_flops(q_len, kv_len, num_heads, num_kv_heads, head_dim, index_dim, b
 
 
 def decode_bytes(ctx_lens, num_heads, num_kv_heads, head_dim, index_dim, block_size, topk,
-                 elem_bytes: int = 2):
-    """(index-scan bytes, attention bytes) for one decode step."""
+                 elem_bytes: int = 2, kv_elem_bytes: int | None = None, qo_elem_bytes: int | None = None):
+    """(index-scan bytes, attention bytes) for one decode step.  ``elem_bytes``
+    is the size of an index-tensor element; K/V and q/out elements default to
+    the same size."""
+    kv_eb = elem_bytes if kv_elem_bytes is None else kv_elem_bytes
+    qo_eb = elem_bytes if qo_elem_bytes is None else qo_elem_bytes
     ctx = np.asarray(ctx_lens, dtype=np.int64)
     pos = ctx - 1
     idx_bytes = float((ctx * index_dim * elem_bytes).sum()
                       + len(ctx) * num_kv_heads * index_dim * elem_bytes)
     J = attended_keys(pos, block_size, topk)
-    kv_bytes = float((J * num_kv_heads * head_dim * elem_bytes * 2).sum())
-    qo_bytes = float(len(ctx) * num_heads * head_dim * elem_bytes * 2)
+    kv_bytes = float((J * num_kv_heads * head_dim * kv_eb * 2).sum())
+    qo_bytes = float(len(ctx) * num_heads * head_dim * qo_eb * 2)
     return idx_bytes, kv_bytes + qo_bytes
 
 

@@ -70,6 +70,10 @@ def _load():
         lib.oracle_sparse_attn.argtypes = [vp, vp, vp, ctypes.c_int, i64p, i64p, i32p,
                                            ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_double, vp, vp]
+        lib.oracle_sparse_attn_kv.restype = ctypes.c_int
+        lib.oracle_sparse_attn_kv.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_int, i64p, i64p, i32p,
+                                              ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_double, vp, vp]
         _lib = lib
     return _lib
 
@@ -184,8 +188,8 @@ def sparse_attn(q, k, v, sel, kstart, pos, rows, block_size: int, topk: int, sca
     qa, qt = _gather_rows(q, rows)
     ka, kt = _host_array(k)
     va, vt = _host_array(v)
-    if not (qt == kt == vt):
-        raise TypeError("q, k and v must share a dtype")
+    if kt != vt:
+        raise TypeError("k and v must share a dtype")
     n, Hq, D = qa.shape
     Hkv = ka.shape[1]
     sel = np.ascontiguousarray(np.asarray(sel), dtype=np.int32)
@@ -197,9 +201,9 @@ def sparse_attn(q, k, v, sel, kstart, pos, rows, block_size: int, topk: int, sca
     pos = np.ascontiguousarray(pos, dtype=np.int64)
     out = np.empty((n, Hq, D), dtype=np.float64)
     lse = np.empty((n, Hq), dtype=np.float64)
-    rc = lib.oracle_sparse_attn(_ptr(qa), _ptr(ka), _ptr(va), qt, _ptr(kstart), _ptr(pos),
-                                _ptr(sel), n, Hq, Hkv, D, block_size, topk, float(scale),
-                                _ptr(out), _ptr(lse))
+    rc = lib.oracle_sparse_attn_kv(_ptr(qa), _ptr(ka), _ptr(va), qt, kt, _ptr(kstart), _ptr(pos),
+                                   _ptr(sel), n, Hq, Hkv, D, block_size, topk, float(scale),
+                                   _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError(f"oracle_sparse_attn failed ({rc})")
     return out, lse

@@ -139,14 +139,15 @@ int oracle_index_topk(const void* q_idx, const void* k_idx, int dtype,
  * blocks, for every head of the group, with the causal limit j <= p inside
  * the local block.  z_j = scale * q . k_j; o = sum_j softmax(z)_j v_j;
  * lse = log sum_j exp(z_j).  All in fp64. */
-int oracle_sparse_attn(const void* q, const void* k, const void* v, int dtype,
-                       const int64_t* kstart, const int64_t* pos, const int32_t* sel,
-                       int64_t n, int Hq, int Hkv, int D, int Bk, int topk,
-                       double scale, double* out, double* lse) {
+int oracle_sparse_attn_kv(const void* q, const void* k, const void* v, int dtype, int kv_dtype,
+                          const int64_t* kstart, const int64_t* pos, const int32_t* sel,
+                          int64_t n, int Hq, int Hkv, int D, int Bk, int topk,
+                          double scale, double* out, double* lse) {
   if (!q || !k || !v || !kstart || !pos || !sel || !out || !lse) return 1;
   if (n < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Bk <= 0 || topk <= 0) return 1;
   if (Hq % Hkv != 0) return 1;
   if (dtype != 0 && dtype != 1 && dtype != 2) return 1;
+  if (kv_dtype != 0 && kv_dtype != 1 && kv_dtype != 2) return 1;
   const int r_heads = Hq / Hkv;
 
   int bad = 0;
@@ -184,7 +185,7 @@ int oracle_sparse_attn(const void* q, const void* k, const void* v, int dtype,
         const int64_t koff = ((kstart[r] + keys[a]) * Hkv + g) * (int64_t)D;
         double dot = 0.0;
         for (int d = 0; d < D; ++d)
-          dot += (double)load_elem(q, dtype, qoff + d) * (double)load_elem(k, dtype, koff + d);
+          dot += (double)load_elem(q, dtype, qoff + d) * (double)load_elem(k, kv_dtype, koff + d);
         z[a] = scale * dot;
         if (z[a] > m) m = z[a];
       }
@@ -193,7 +194,7 @@ int oracle_sparse_attn(const void* q, const void* k, const void* v, int dtype,
         const double w = exp(z[a] - m);
         l += w;
         const int64_t voff = ((kstart[r] + keys[a]) * Hkv + g) * (int64_t)D;
-        for (int d = 0; d < D; ++d) o[d] += w * (double)load_elem(v, dtype, voff + d);
+        for (int d = 0; d < D; ++d) o[d] += w * (double)load_elem(v, kv_dtype, voff + d);
       }
       for (int d = 0; d < D; ++d) o[d] /= l;
       lse[r * Hq + h] = m + log(l);
@@ -203,4 +204,12 @@ int oracle_sparse_attn(const void* q, const void* k, const void* v, int dtype,
     free(keys);
   }
   return bad;
+}
+
+int oracle_sparse_attn(const void* q, const void* k, const void* v, int dtype,
+                       const int64_t* kstart, const int64_t* pos, const int32_t* sel,
+                       int64_t n, int Hq, int Hkv, int D, int Bk, int topk,
+                       double scale, double* out, double* lse) {
+  return oracle_sparse_attn_kv(q, k, v, dtype, dtype, kstart, pos, sel, n, Hq, Hkv, D, Bk, topk, scale,
+                               out, lse);
 }

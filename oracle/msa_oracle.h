@@ -31,8 +31,8 @@
  * E4M3 bit patterns (uint8) as the OCP 8-bit floating point specification
  * defines them (sign, 4 exponent bits with bias 7, 3 mantissa bits,
  * subnormals at exponent 0, no infinities, S.1111.111 is NaN), decoded
- * exactly.  The pages note that the kernels also support fp8; code 2 is used
- * for the index tensors.
+ * exactly.  The pages note fp8 support in the kernels; code 2 is used for
+ * the index tensors and for an 8-bit KV cache.
  */
 #ifndef MSA_ORACLE_H
 #define MSA_ORACLE_H
@@ -66,6 +66,13 @@ int oracle_sparse_attn(const void* q, const void* k, const void* v, int dtype,
                        const int64_t* kstart, const int64_t* pos, const int32_t* sel,
                        int64_t n, int Hq, int Hkv, int D, int Bk, int topk,
                        double scale, double* out, double* lse);
+
+/* As oracle_sparse_attn with q read as `dtype` and k, v as `kv_dtype` (an
+ * 8-bit KV cache under bf16 queries: dtype 1, kv_dtype 2). */
+int oracle_sparse_attn_kv(const void* q, const void* k, const void* v, int dtype, int kv_dtype,
+                          const int64_t* kstart, const int64_t* pos, const int32_t* sel,
+                          int64_t n, int Hq, int Hkv, int D, int Bk, int topk,
+                          double scale, double* out, double* lse);
 
 /* Decode n E4M3 bit patterns to fp32 (exact), for checking the decoder. */
 void oracle_decode_e4m3(const uint8_t* in, float* out, int64_t n);

@@ -334,3 +334,22 @@ def test_fp8_grid_is_exact_and_selection_matches_bruteforce(oracle_lib):
     rows, kstart, pos = oracle_lib.rows_prefill(cu, cu)
     sel = oracle_lib.index_topk(q8, k8, kstart, pos, rows, wl.block_size, wl.topk)
     np.testing.assert_array_equal(sel, want)
+
+
+@pytest.mark.parametrize("kv,ql", [([512], [512]), ([300, 41], [100, 41])])
+def test_fp8_kv_attention_equals_dense(oracle_lib, kv, ql):
+    """bf16 queries with an E4M3 KV cache: when every causal block fits the
+    budget, the oracle equals dense causal GQA attention (torch SDPA, fp64) on
+    the values torch's own float8_e4m3fn conversion gives for K and V."""
+    g = torch.Generator().manual_seed(12)
+    Hq, Hkv, D, bk, topk = 8, 2, 32, 128, 4
+    cu_k, cu_q = _cu(kv), _cu(ql)
+    q = torch.randn(cu_q[-1], Hq, D, generator=g).bfloat16()
+    k8 = torch.randn(cu_k[-1], Hkv, D, generator=g).to(torch.float8_e4m3fn)
+    v8 = (3 * torch.randn(cu_k[-1], Hkv, D, generator=g)).to(torch.float8_e4m3fn)
+    qi = torch.randint(-16, 17, (cu_q[-1], Hkv, 8), generator=g).float() / 8
+    ki = torch.randint(-16, 17, (cu_k[-1], 8), generator=g).float() / 8
+    sel, out, lse = oracle_lib.prefill(qi, ki, q, k8, v8, cu_q, cu_k, bk, topk)
+    ref_o, ref_l = _dense_reference(q.float(), k8.float(), v8.float(), cu_q, cu_k, 1.0 / math.sqrt(D))
+    np.testing.assert_allclose(out, ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-12)
