@@ -24,13 +24,10 @@ import glob
 import json
 import os
 
-# kernels of one library call, by kernel-name prefix.  rocprofv3 leaves names
-# it cannot demangle (the bf16 instantiations) mangled, and with -T cuts the
-# others down to the bare function name, so the fp8 index call is told apart
-# by its scan kernel: the fp8e4m3 template argument, or the bare name that
-# only the demangled (non-bf16) instantiation produces.
+# kernels of one library call, by kernel-name prefix
 CALLS = {
     "attention_prefill_128k": ("kvo_zero", "kvo_bucket", "kvo_scan", "kvo_attn", "kvo_combine"),
+    "attention_prefill_128k_fp8kv": ("kvo_zero", "kvo_bucket", "kvo_scan", "kvo_attn", "kvo_combine"),
     "index_prefill_128k": ("_ZN3msa16idx_scan_prefill", "idx_scan_prefill", "idx_select_prefill"),
     "index_prefill_128k_fp8": ("_ZN3msa16idx_scan_prefill", "idx_scan_prefill", "idx_select_prefill"),
     "index_decode_1m": ("_ZN3msa17idx_decode_scores", "idx_decode_scores", "idx_decode_select"),
@@ -38,18 +35,24 @@ CALLS = {
                             "attn_combine"),
 }
 # the call's first kernel marks a new call
-CALL_START = {"attention_prefill_128k": "kvo_zero", "index_prefill_128k": "idx_scan_prefill",
-              "index_prefill_128k_fp8": "idx_scan_prefill", "index_decode_1m": "idx_decode_scores",
-              "attention_decode_1m": "sparse_attn_fwd"}
+CALL_START = {"attention_prefill_128k": "kvo_zero", "attention_prefill_128k_fp8kv": "kvo_zero",
+              "index_prefill_128k": "idx_scan_prefill", "index_prefill_128k_fp8": "idx_scan_prefill",
+              "index_decode_1m": "idx_decode_scores", "attention_decode_1m": "sparse_attn_fwd"}
 
 
-def _is_fp8_scan(name):
-    return "fp8e4m3" in name or name == "idx_scan_prefill"
+def _is_bf16(name):
+    """A bf16 instantiation: rocprofv3 cannot demangle the __bf16 template
+    argument (DF16b) and leaves those names mangled; the others it demangles
+    (and with -T cuts down to the bare function name)."""
+    return "DF16b" in name or "bf16" in name
 
 
-# calls told apart by the element type of their first kernel
-CALL_FILTER = {"index_prefill_128k": lambda n: not _is_fp8_scan(n),
-               "index_prefill_128k_fp8": _is_fp8_scan}
+# calls of the same kernels told apart by the element type of one kernel:
+# (kernel whose type decides, keep the call if that kernel is bf16)
+CALL_TYPE = {"index_prefill_128k": ("idx_scan_prefill", True),
+             "index_prefill_128k_fp8": ("idx_scan_prefill", False),
+             "attention_prefill_128k": ("kvo_attn", True),
+             "attention_prefill_128k_fp8kv": ("kvo_attn", False)}
 
 
 def _rows(d):
@@ -69,21 +72,24 @@ def _matches(name, prefixes):
 
 def per_call_kb(rows, call):
     """Sum of the counter (KB) over each call's kernels, one entry per call."""
-    out, cur = [], None
-    keep = CALL_FILTER.get(call, lambda n: True)
+    calls, cur = [], None
     for r in rows:
         name = r["Kernel_Name"]
         if not _matches(name, CALLS[call]):
             continue
         if CALL_START[call] in name:
             if cur is not None:
-                out.append(cur)
-            cur = 0.0 if keep(name) else None
+                calls.append(cur)
+            cur = []
         if cur is not None:
-            cur += float(r["Counter_Value"])
+            cur.append((name, float(r["Counter_Value"])))
     if cur is not None:
-        out.append(cur)
-    return out
+        calls.append(cur)
+    if call in CALL_TYPE:
+        kernel, want_bf16 = CALL_TYPE[call]
+        calls = [c for c in calls
+                 if any(kernel in n and _is_bf16(n) == want_bf16 for n, _ in c)]
+    return [sum(v for _, v in c) for c in calls]
 
 
 def per_kernel_kb(rows):
@@ -123,6 +129,7 @@ def main():
     sources = {"attention_prefill_128k": ("prefill-fetch", "prefill-write"),
                "index_prefill_128k": ("prefill-fetch", "prefill-write"),
                "index_prefill_128k_fp8": ("prefill-fetch", "prefill-write"),
+               "attention_prefill_128k_fp8kv": ("prefill-fetch", "prefill-write"),
                "index_decode_1m": ("decode-fetch", "decode-write"),
                "attention_decode_1m": ("decode-fetch", "decode-write")}
     digest = build.source_digest()
