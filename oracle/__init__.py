@@ -17,6 +17,8 @@ record of MiniMax M3 (atlas.lewiswon.me), summary paragraph:
   same precision).
 * ``sparse_attn``: exact softmax attention in fp64 over the keys of the
   selected blocks, causal inside the local block, natural-log LSE.
+* ``sparse_attn_bwd``: its gradients with respect to q, k and v (fp64),
+  recomputed from the inputs.
 
 Query row t of a sequence with ``q_len = M`` and ``kv_len = N`` sits at
 absolute position ``p = N - M + t``; blocks are aligned to position 0.
@@ -74,6 +76,10 @@ def _load():
         lib.oracle_sparse_attn_kv.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_int, i64p, i64p, i32p,
                                               ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int, ctypes.c_int, ctypes.c_double, vp, vp]
+        lib.oracle_sparse_attn_bwd.restype = ctypes.c_int
+        lib.oracle_sparse_attn_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64p, i64p, i32p,
+                                               ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_double, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -207,6 +213,37 @@ def sparse_attn(q, k, v, sel, kstart, pos, rows, block_size: int, topk: int, sca
     if rc != 0:
         raise ValueError(f"oracle_sparse_attn failed ({rc})")
     return out, lse
+
+
+def sparse_attn_bwd(q, k, v, dout, sel, kstart, pos, rows, block_size: int, topk: int, scale=None):
+    """Gradients of ``sparse_attn`` for the given query rows:
+    (dq [n, Hq, D], dk [Tk, Hkv, D], dv [Tk, Hkv, D]), all fp64.  dk and dv
+    hold the contributions of these rows only."""
+    lib = _load()
+    qa, qt = _gather_rows(q, rows)
+    da, dt = _gather_rows(dout, rows)
+    ka, kt = _host_array(k)
+    va, vt = _host_array(v)
+    if not (qt == kt == vt == dt) or qt not in (0, 1):
+        raise TypeError("q, k, v and dout must share a dtype (fp32 or bf16)")
+    n, Hq, D = qa.shape
+    Hkv = ka.shape[1]
+    sel = np.ascontiguousarray(np.asarray(sel), dtype=np.int32)
+    if sel.shape != (n, Hkv, topk):
+        raise ValueError(f"sel shape {sel.shape} != {(n, Hkv, topk)}")
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    kstart = np.ascontiguousarray(kstart, dtype=np.int64)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    dq = np.empty((n, Hq, D), dtype=np.float64)
+    dk = np.zeros(ka.shape, dtype=np.float64)
+    dv = np.zeros(va.shape, dtype=np.float64)
+    rc = lib.oracle_sparse_attn_bwd(_ptr(qa), _ptr(ka), _ptr(va), _ptr(da), qt, _ptr(kstart), _ptr(pos),
+                                    _ptr(sel), n, Hq, Hkv, D, block_size, topk, float(scale),
+                                    _ptr(dq), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError(f"oracle_sparse_attn_bwd failed ({rc})")
+    return dq, dk, dv
 
 
 def prefill(q_idx, k_idx, q, k, v, cu_seqlens_q, cu_seqlens_k, block_size: int, topk: int,

@@ -213,3 +213,103 @@ int oracle_sparse_attn(const void* q, const void* k, const void* v, int dtype,
   return oracle_sparse_attn_kv(q, k, v, dtype, dtype, kstart, pos, sel, n, Hq, Hkv, D, Bk, topk, scale,
                                out, lse);
 }
+
+/* Gradients of the main branch ([P4] "The mechanism, precisely": the main
+ * branch is ordinary softmax attention over the selected keys, so its
+ * gradients are those of softmax attention restricted to J).  For one row and
+ * head, with P_j = exp(z_j) / sum_i exp(z_i) over j in J and dO the gradient
+ * of the output:
+ *   dP_j  = dO . v_j
+ *   delta = sum_j P_j dP_j
+ *   dS_j  = P_j (dP_j - delta)          (gradient of the logit z_j)
+ *   dq   += scale * sum_j dS_j k_j
+ *   dk_j += scale * dS_j q               (summed over rows and the group's heads)
+ *   dv_j += P_j dO
+ * All in fp64.  dq is written; dk and dv are accumulated (the caller zeroes
+ * them); rows run in parallel, so the dk/dv updates are atomic. */
+int oracle_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                           const int64_t* kstart, const int64_t* pos, const int32_t* sel,
+                           int64_t n, int Hq, int Hkv, int D, int Bk, int topk, double scale,
+                           double* dq, double* dk, double* dv) {
+  if (!q || !k || !v || !dout || !kstart || !pos || !sel || !dq || !dk || !dv) return 1;
+  if (n < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Bk <= 0 || topk <= 0) return 1;
+  if (Hq % Hkv != 0) return 1;
+  if (dtype != 0 && dtype != 1) return 1;
+  const int r_heads = Hq / Hkv;
+
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t r = 0; r < n; ++r) {
+    int32_t* blocks = (int32_t*)malloc(sizeof(int32_t) * (size_t)topk);
+    double* z = (double*)malloc(sizeof(double) * (size_t)topk * (size_t)Bk);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)topk * (size_t)Bk);
+    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)topk * (size_t)Bk);
+    if (!blocks || !z || !dp || !keys) { bad = 1; free(blocks); free(z); free(dp); free(keys); continue; }
+    const int64_t p = pos[r];
+
+    for (int h = 0; h < Hq; ++h) {
+      const int g = h / r_heads;
+      double* dqh = dq + (r * Hq + h) * (int64_t)D;
+      for (int d = 0; d < D; ++d) dqh[d] = 0.0;
+
+      /* J as in the forward definition: Sel taken as a set, keys j <= p */
+      int nb = 0;
+      for (int i = 0; i < topk; ++i) {
+        int32_t c = sel[(r * Hkv + g) * (int64_t)topk + i];
+        if (c >= 0) blocks[nb++] = c;
+      }
+      qsort(blocks, (size_t)nb, sizeof(int32_t), ascending_int);
+      int64_t nk = 0;
+      for (int i = 0; i < nb; ++i) {
+        if (i > 0 && blocks[i] == blocks[i - 1]) continue;
+        for (int64_t j = (int64_t)blocks[i] * Bk; j < ((int64_t)blocks[i] + 1) * Bk; ++j)
+          if (j <= p) keys[nk++] = j;
+      }
+      if (nk == 0) continue;
+
+      const int64_t qoff = (r * Hq + h) * (int64_t)D;
+      double m = -INFINITY;
+      for (int64_t a = 0; a < nk; ++a) {
+        const int64_t koff = ((kstart[r] + keys[a]) * Hkv + g) * (int64_t)D;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d)
+          dot += (double)load_elem(q, dtype, qoff + d) * (double)load_elem(k, dtype, koff + d);
+        z[a] = scale * dot;
+        if (z[a] > m) m = z[a];
+      }
+      double l = 0.0;
+      for (int64_t a = 0; a < nk; ++a) {
+        z[a] = exp(z[a] - m);
+        l += z[a];
+      }
+      double delta = 0.0;
+      for (int64_t a = 0; a < nk; ++a) {
+        z[a] /= l; /* z now holds P */
+        const int64_t voff = ((kstart[r] + keys[a]) * Hkv + g) * (int64_t)D;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d)
+          dot += (double)load_elem(dout, dtype, qoff + d) * (double)load_elem(v, dtype, voff + d);
+        dp[a] = dot;
+        delta += z[a] * dot;
+      }
+      for (int64_t a = 0; a < nk; ++a) {
+        const double ds = z[a] * (dp[a] - delta);
+        const int64_t koff = ((kstart[r] + keys[a]) * Hkv + g) * (int64_t)D;
+        for (int d = 0; d < D; ++d) {
+          dqh[d] += scale * ds * (double)load_elem(k, dtype, koff + d);
+          const double gk = scale * ds * (double)load_elem(q, dtype, qoff + d);
+          const double gv = z[a] * (double)load_elem(dout, dtype, qoff + d);
+#pragma omp atomic
+          dk[koff + d] += gk;
+#pragma omp atomic
+          dv[koff + d] += gv;
+        }
+      }
+    }
+    free(blocks);
+    free(z);
+    free(dp);
+    free(keys);
+  }
+  return bad;
+}

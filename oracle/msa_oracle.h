@@ -74,6 +74,18 @@ int oracle_sparse_attn_kv(const void* q, const void* k, const void* v, int dtype
                           int64_t n, int Hq, int Hkv, int D, int Bk, int topk,
                           double scale, double* out, double* lse);
 
+/* Gradients of oracle_sparse_attn for n query rows, given dout [n][Hq][D]
+ * (element type `dtype`, 0 or 1 as q, k, v):
+ *   dq     : [n][Hq][D]      fp64 out (written)
+ *   dk, dv : [*][Hkv][D]     fp64, indexed like k and v, ACCUMULATED into (the
+ *                            caller zeroes them)
+ * P, the gradient of the logits and everything else is recomputed from q, k,
+ * v in fp64; no forward result is taken as input. */
+int oracle_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                           const int64_t* kstart, const int64_t* pos, const int32_t* sel,
+                           int64_t n, int Hq, int Hkv, int D, int Bk, int topk, double scale,
+                           double* dq, double* dk, double* dv);
+
 /* Decode n E4M3 bit patterns to fp32 (exact), for checking the decoder. */
 void oracle_decode_e4m3(const uint8_t* in, float* out, int64_t n);
 

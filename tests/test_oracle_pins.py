@@ -353,3 +353,99 @@ def test_fp8_kv_attention_equals_dense(oracle_lib, kv, ql):
     ref_o, ref_l = _dense_reference(q.float(), k8.float(), v8.float(), cu_q, cu_k, 1.0 / math.sqrt(D))
     np.testing.assert_allclose(out, ref_o, rtol=0, atol=1e-12)
     np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-12)
+
+
+def _masked_attention_torch(q, k, v, mask_rows, scale, Hkv):
+    """Dense softmax attention with an explicit boolean mask per (row, group),
+    written with torch ops so autograd gives its gradients."""
+    n, Hq, D = q.shape
+    rep = Hq // Hkv
+    outs = []
+    for r, (kk_idx, mask) in enumerate(mask_rows):
+        heads = []
+        for h in range(Hq):
+            g = h // rep
+            if not mask[g].any():
+                heads.append(torch.zeros(D, dtype=q.dtype) + 0.0 * q[r, h].sum())
+                continue
+            kk = k[kk_idx, g]
+            vv = v[kk_idx, g]
+            z = (kk @ q[r, h]) * scale
+            z = z.masked_fill(~mask[g], float("-inf"))
+            heads.append(torch.softmax(z, dim=0) @ vv)
+        outs.append(torch.stack(heads))
+    return torch.stack(outs)
+
+
+def test_backward_matches_autograd_of_mask_formulation(oracle_lib):
+    """dq, dk, dv of the oracle against torch autograd (fp64) through a dense
+    boolean-mask softmax, for arbitrary selections (duplicates, -1, future
+    blocks, missing local blocks) over two packed sequences."""
+    rng = np.random.default_rng(21)
+    kv, ql, Hq, Hkv, D, bk, topk = [150, 90], [60, 90], 4, 2, 8, 16, 4
+    cu_k, cu_q = _cu(kv), _cu(ql)
+    q = rng.standard_normal((cu_q[-1], Hq, D)).astype(np.float32)
+    k = rng.standard_normal((cu_k[-1], Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((cu_k[-1], Hkv, D)).astype(np.float32)
+    do = rng.standard_normal((cu_q[-1], Hq, D)).astype(np.float32)
+    rows, kstart, pos = oracle_lib.rows_prefill(cu_q, cu_k)
+    sel = rng.integers(-1, 11, size=(len(rows), Hkv, topk)).astype(np.int32)
+    for r in range(len(rows)):
+        if r % 4:
+            sel[r, :, 0] = pos[r] // bk
+    dq, dk, dv = oracle_lib.sparse_attn_bwd(q, k, v, do, sel, kstart, pos, rows, bk, topk)
+
+    qt = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    kt = torch.tensor(k, dtype=torch.float64, requires_grad=True)
+    vt = torch.tensor(v, dtype=torch.float64, requires_grad=True)
+    mask_rows = []
+    for r in range(len(rows)):
+        b = int(np.searchsorted(cu_q, rows[r], side="right") - 1)
+        n = cu_k[b + 1] - cu_k[b]
+        j = np.arange(n)
+        idx = torch.tensor(cu_k[b] + j)
+        mask = torch.tensor(np.stack([np.isin(j // bk, sel[r, g]) & (j <= pos[r]) for g in range(Hkv)]))
+        mask_rows.append((idx, mask))
+    out = _masked_attention_torch(qt, kt, vt, mask_rows, 1.0 / math.sqrt(D), Hkv)
+    (out * torch.tensor(do, dtype=torch.float64)).sum().backward()
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_backward_matches_finite_differences(oracle_lib):
+    """Central differences of L = sum(dO * out) through the oracle's own
+    forward pass (fp64 inside), at a few coordinates of q, k and v, including
+    keys in the causal partial local block."""
+    rng = np.random.default_rng(22)
+    kv, ql, Hq, Hkv, D, bk, topk = [70], [70], 4, 2, 8, 16, 3
+    cu_k, cu_q = _cu(kv), _cu(ql)
+    q = rng.standard_normal((70, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((70, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((70, Hkv, D)).astype(np.float32)
+    do = rng.standard_normal((70, Hq, D)).astype(np.float32)
+    rows, kstart, pos = oracle_lib.rows_prefill(cu_q, cu_k)
+    sel = np.full((70, Hkv, topk), -1, dtype=np.int32)
+    for r in range(70):
+        loc = pos[r] // bk
+        sel[r, 0, :2] = [loc, (loc + 2) // 2 - 1 if loc else -1]
+        sel[r, 1, :3] = [0, loc, max(loc - 1, 0)]
+    dq, dk, dv = oracle_lib.sparse_attn_bwd(q, k, v, do, sel, kstart, pos, rows, bk, topk)
+
+    def loss(qq, kk, vv):
+        out, _ = oracle_lib.sparse_attn(qq, kk, vv, sel, kstart, pos, rows, bk, topk)
+        return float((out * do.astype(np.float64)).sum())
+
+    eps = 2.0 ** -10
+    for name, arr, grad, coords in (("q", q, dq, [(5, 1, 3), (69, 3, 0), (40, 2, 7)]),
+                                    ("k", k, dk, [(0, 1, 2), (33, 0, 5), (66, 1, 1)]),
+                                    ("v", v, dv, [(17, 0, 4), (64, 1, 6), (2, 1, 0)])):
+        for c in coords:
+            plus, minus = arr.copy(), arr.copy()
+            plus[c] += eps
+            minus[c] -= eps
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = plus, minus
+            fd = (loss(args_p["q"], args_p["k"], args_p["v"]) - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * eps)
+            assert abs(fd - grad[c]) <= 1e-5 * max(1.0, abs(grad[c])), (name, c, fd, grad[c])
