@@ -230,6 +230,47 @@ msa_status_t msa_sparse_attn_decode_ex(const void* q, const void* k_cache, const
                                        void* out, float* lse, void* workspace, size_t workspace_bytes,
                                        hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Main branch, backward (prefill layout).
+ *
+ * The main branch of "MiniMax Sparse Attention: let each query pick its own
+ * blocks" ("The mechanism, precisely") is ordinary softmax attention over the
+ * keys J of the selected blocks, so its gradients are those of softmax
+ * attention restricted to J; the atlas record of MiniMax M3 trains the model
+ * through it (the index branch has its own loss and is not differentiated
+ * here: block_idx is an input).  With P_j = exp(z_j - lse), delta = dO . out:
+ *   dq = scale sum_j P_j (dO . v_j - delta) k_j
+ *   dk_j = scale sum over (row, head of the group) of P_j (dO . v_j - delta) q
+ *   dv_j = sum over (row, head of the group) of P_j dO
+ *
+ *   q, k, v, block_idx, cu_seqlens_*, sizes, softmax_scale
+ *                as for msa_sparse_attn_prefill (same values as that call)
+ *   out, lse     that call's outputs (lse is required)
+ *   dout         [Tq, num_heads, head_dim], gradient of out
+ *   dtype        MSA_BF16 (q, k, v, out, dout); other types return
+ *                MSA_ERR_UNSUPPORTED
+ *   dq           [Tq, num_heads, head_dim] fp32 out
+ *   dk, dv       [Tk, num_kv_heads, head_dim] fp32 out, overwritten: key rows
+ *                no query attends get 0
+ *   workspace    at least msa_sparse_attn_backward_workspace_size() bytes:
+ *                the per-block edge lists of one window of at most 8192 query
+ *                rows and one fp32 per (row, head)
+ *
+ * Accumulation is fp32; P and dS enter the dK, dV and dQ products as bf16.
+ * Results are bitwise reproducible (no atomics in any arithmetic: each
+ * block's edges are summed in a fixed order).
+ * ---------------------------------------------------------------------- */
+size_t msa_sparse_attn_backward_workspace_size(int batch, int max_q_len, int max_kv_len, int num_heads,
+                                               int num_kv_heads, int head_dim, int topk);
+
+msa_status_t msa_sparse_attn_backward(const void* q, const void* k, const void* v, const void* out,
+                                      const void* dout, const float* lse, msa_dtype_t dtype,
+                                      const int32_t* block_idx, const int32_t* cu_seqlens_q,
+                                      const int32_t* cu_seqlens_k, int batch, int max_q_len, int max_kv_len,
+                                      int num_heads, int num_kv_heads, int head_dim, int block_size, int topk,
+                                      float softmax_scale, float* dq, float* dk, float* dv, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -254,4 +254,40 @@ msa_status_t msa_sparse_attn_decode(const void* q, const void* k_cache, const vo
                                    num_splits, out, lse, workspace, workspace_bytes, stream);
 }
 
+size_t msa_sparse_attn_backward_workspace_size(int batch, int max_q_len, int max_kv_len, int num_heads,
+                                               int num_kv_heads, int head_dim, int topk) {
+  if (batch <= 0 || max_q_len <= 0 || max_kv_len <= 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || topk <= 0)
+    return 0;
+  return plan_bwd(batch, max_q_len, max_kv_len, num_heads, num_kv_heads, topk).workspace_bytes;
+}
+
+msa_status_t msa_sparse_attn_backward(const void* q, const void* k, const void* v, const void* out,
+                                      const void* dout, const float* lse, msa_dtype_t dtype,
+                                      const int32_t* block_idx, const int32_t* cu_seqlens_q,
+                                      const int32_t* cu_seqlens_k, int batch, int max_q_len, int max_kv_len,
+                                      int num_heads, int num_kv_heads, int head_dim, int block_size, int topk,
+                                      float softmax_scale, float* dq, float* dk, float* dv, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  msa_status_t st = check_attn(q, k, v, dtype, dtype, block_idx, out, batch, num_heads, num_kv_heads, head_dim,
+                               block_size, topk, 0);
+  if (st != MSA_OK) return st;
+  if (!dout || !lse || !dq || !dk || !dv || !cu_seqlens_q || !cu_seqlens_k || max_q_len <= 0 ||
+      max_kv_len <= 0)
+    return MSA_ERR_INVALID_ARG;
+  if (dtype != MSA_BF16) return MSA_ERR_UNSUPPORTED;  // the backward kernels take bf16 inputs
+  const BwdPlan pl = plan_bwd(batch, max_q_len, max_kv_len, num_heads, num_kv_heads, topk);
+  if (!workspace || workspace_bytes < pl.workspace_bytes) return MSA_ERR_WORKSPACE;
+  BwdArgs a;
+  a.fwd = AttnArgs{q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, nullptr, nullptr, batch, num_heads,
+                   num_kv_heads, topk, resolve_scale(softmax_scale, head_dim), nullptr, nullptr};
+  a.o = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  return hip_status(launch_sparse_attn_bwd(pl, a, workspace, stream));
+}
+
 }  // extern "C"

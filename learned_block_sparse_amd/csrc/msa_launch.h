@@ -75,4 +75,34 @@ hipError_t launch_attn_kvouter(const AttnPlan& pl, bool kv_e4m3, const AttnArgs&
 size_t kvo_part_slot_bytes();
 int kvo_window_rows();
 
+// Per-(sequence, group, block) lists of the selection entries of query rows
+// [row_lo, row_hi): each entry is ((row - row_lo) << 4 | selection slot), the
+// entries of bucket i are edges[offsets[i] .. offsets[i + 1]) in no
+// particular order (atomics place them).  counts, chunk_start and cursor are
+// scratch of batch * G * nb_max (+1) ints each.
+hipError_t build_edge_lists(const AttnArgs& x, int nb_max, int64_t row_lo, int64_t row_hi, int32_t* counts,
+                            int32_t* offsets, int32_t* chunk_start, int32_t* cursor, int32_t* edges,
+                            hipStream_t st);
+
+// Backward of the main branch (bf16 inputs, fp32 gradients).
+struct BwdPlan {
+  int nb_max = 0;
+  int nbuckets = 0;
+  int64_t rows_bound = 0;
+  int64_t window = 0;        // query rows per edge-list window
+  size_t counts_off = 0, offsets_off = 0, chunks_off = 0, cursor_off = 0, edges_off = 0, delta_off = 0;
+  size_t workspace_bytes = 0;
+};
+BwdPlan plan_bwd(int batch, int max_q_len, int max_kv_len, int Hq, int G, int topk);
+struct BwdArgs {
+  AttnArgs fwd;               // q, k, v, block_idx, cu_q, cu_k, sizes, scale (out/lse unused)
+  const void* o;              // forward output [Tq, Hq, D]
+  const void* dout;           // gradient of the output [Tq, Hq, D]
+  const float* lse;           // forward LSE [Tq, Hq]
+  float* dq;                  // [Tq, Hq, D]
+  float* dk;                  // [Tk, Hkv, D]
+  float* dv;                  // [Tk, Hkv, D]
+};
+hipError_t launch_sparse_attn_bwd(const BwdPlan& pl, const BwdArgs& a, void* ws, hipStream_t st);
+
 }  // namespace msa

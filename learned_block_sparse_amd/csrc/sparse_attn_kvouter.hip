@@ -480,6 +480,39 @@ __global__ __launch_bounds__(256) void kvo_combine(KvoArgs a) {
   if (a.lse && (lane & 3) == 0) a.lse[t * a.Hq + g * R + h] = L;
 }
 
+// Edge lists of query rows [a.row_lo, a.row_hi): counts, offsets, chunk
+// starts and the edges themselves, per (sequence, group, block) bucket.
+static void launch_edge_lists(const KvoArgs& a, int nbk, hipStream_t st) {
+  const unsigned eg = (unsigned)(((a.row_hi - a.row_lo) * a.G + 255) / 256);
+  hipLaunchKernelGGL(kvo_zero, dim3((unsigned)((nbk + 255) / 256)), dim3(256), 0, st, a.counts, nbk);
+  hipLaunchKernelGGL(kvo_bucket<false>, dim3(eg), dim3(256), 0, st, a, nbk);
+  hipLaunchKernelGGL(kvo_scan, dim3(1), dim3(1024), 0, st, a, nbk);
+  hipLaunchKernelGGL(kvo_bucket<true>, dim3(eg), dim3(256), 0, st, a, nbk);
+}
+
+hipError_t build_edge_lists(const AttnArgs& x, int nb_max, int64_t row_lo, int64_t row_hi, int32_t* counts,
+                            int32_t* offsets, int32_t* chunk_start, int32_t* cursor, int32_t* edges,
+                            hipStream_t st) {
+  KvoArgs a{};
+  a.block_idx = x.block_idx;
+  a.cu_q = x.cu_q;
+  a.cu_k = x.cu_k;
+  a.batch = x.batch;
+  a.G = x.Hkv;
+  a.Hq = x.Hq;
+  a.topk = x.topk;
+  a.nb_max = nb_max;
+  a.row_lo = row_lo;
+  a.row_hi = row_hi;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.chunk_start = chunk_start;
+  a.cursor = cursor;
+  a.edges = edges;
+  launch_edge_lists(a, x.batch * x.Hkv * nb_max, st);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_kvouter(const AttnPlan& pl, bool kv_e4m3, const AttnArgs& x, void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
   KvoArgs a;
@@ -509,11 +542,7 @@ hipError_t launch_attn_kvouter(const AttnPlan& pl, bool kv_e4m3, const AttnArgs&
     a.row_lo = r0;
     a.row_hi = r0 + pl.kvo_window < pl.rows_bound ? r0 + pl.kvo_window : pl.rows_bound;
     const int64_t entries = (a.row_hi - a.row_lo) * a.G * a.topk;
-    const unsigned eg = (unsigned)(((a.row_hi - a.row_lo) * a.G + 255) / 256);
-    hipLaunchKernelGGL(kvo_zero, dim3((unsigned)((nbk + 255) / 256)), dim3(256), 0, st, a.counts, nbk);
-    hipLaunchKernelGGL(kvo_bucket<false>, dim3(eg), dim3(256), 0, st, a, nbk);
-    hipLaunchKernelGGL(kvo_scan, dim3(1), dim3(1024), 0, st, a, nbk);
-    hipLaunchKernelGGL(kvo_bucket<true>, dim3(eg), dim3(256), 0, st, a, nbk);
+    launch_edge_lists(a, nbk, st);
     const int64_t ub = entries / kKvoChunk + (entries < nbk ? entries : nbk) + 1;
     if (kv_e4m3) hipLaunchKernelGGL(kvo_attn<fp8e4m3>, dim3((unsigned)ub), dim3(kKvoThreads), 0, st, a);
     else hipLaunchKernelGGL(kvo_attn<bf16>, dim3((unsigned)ub), dim3(kKvoThreads), 0, st, a);

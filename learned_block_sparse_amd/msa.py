@@ -69,6 +69,11 @@ def lib():
         L.msa_sparse_attn_decode_ex.restype = i32
         L.msa_sparse_attn_decode_ex.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                                 i32, ctypes.c_float, i32, vp, vp, vp, sz, vp]
+        L.msa_sparse_attn_backward_workspace_size.restype = sz
+        L.msa_sparse_attn_backward_workspace_size.argtypes = [i32] * 7
+        L.msa_sparse_attn_backward.restype = i32
+        L.msa_sparse_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
+                                               i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -230,3 +235,37 @@ def msa_sparse_attn_decode_ex(q, k_cache, v_cache, block_idx, cache_offsets, ctx
     """As msa_sparse_attn_decode with the KV-cache element type taken from ``k_cache``."""
     return _decode(True, q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx, block_size, topk,
                    softmax_scale, num_splits, out, lse, return_lse, workspace, stream)
+
+
+def msa_sparse_attn_backward_workspace_size(batch, max_q_len, max_kv_len, num_heads, num_kv_heads, head_dim,
+                                            topk) -> int:
+    return lib().msa_sparse_attn_backward_workspace_size(batch, max_q_len, max_kv_len, num_heads, num_kv_heads,
+                                                         head_dim, topk)
+
+
+def msa_sparse_attn_backward(q, k, v, out, dout, lse, block_idx, cu_seqlens_q, cu_seqlens_k, max_q_len: int,
+                             max_kv_len: int, block_size: int = 128, topk: int = 16, softmax_scale: float = 0.0,
+                             dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """``(dq [Tq, Hq, D], dk [Tk, Hkv, D], dv [Tk, Hkv, D])`` fp32 gradients of
+    msa_sparse_attn_prefill, given its inputs, its ``out`` and ``lse`` and the
+    gradient ``dout`` of out (bf16)."""
+    tq, hq, d = q.shape
+    tk, hkv = k.shape[0], k.shape[1]
+    batch = cu_seqlens_q.numel() - 1
+    if dq is None:
+        dq = torch.empty((tq, hq, d), dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty((tk, hkv, d), dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty((tk, hkv, d), dtype=torch.float32, device=q.device)
+    need = msa_sparse_attn_backward_workspace_size(batch, max_q_len, max_kv_len, hq, hkv, d, topk)
+    ws, ws_bytes = _workspace(need, q.device, workspace)
+    st = lib().msa_sparse_attn_backward(
+        _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(out, "out", q.dtype),
+        _dev(dout, "dout", q.dtype), _dev(lse, "lse", torch.float32), _dtype_code(q),
+        _dev(block_idx, "block_idx", torch.int32), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32), batch, max_q_len, max_kv_len, hq, hkv, d, block_size,
+        topk, float(softmax_scale), _dev(dq, "dq", torch.float32), _dev(dk, "dk", torch.float32),
+        _dev(dv, "dv", torch.float32), ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
+    _check(st, "msa_sparse_attn_backward")
+    return dq, dk, dv

@@ -75,7 +75,7 @@ WORKLOADS = {
         notes="batch 1, L=1048576 in 8192-query tiles, 256 planted blocks"),
 }
 
-_TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "q_idx": 4, "k_idx": 5, "planted": 6, "ctx": 7}
+_TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "q_idx": 4, "k_idx": 5, "planted": 6, "ctx": 7, "dout": 8}
 _CHUNK_ELEMS = 1 << 28  # draw big tensors in pieces to bound fp32 temporaries
 
 

@@ -226,7 +226,8 @@ int oracle_sparse_attn(const void* q, const void* k, const void* v, int dtype,
  *   dk_j += scale * dS_j q               (summed over rows and the group's heads)
  *   dv_j += P_j dO
  * All in fp64.  dq is written; dk and dv are accumulated (the caller zeroes
- * them); rows run in parallel, so the dk/dv updates are atomic. */
+ * them); rows run in parallel, each thread summing its rows' dk / dv
+ * contributions into a private buffer that is added at the end. */
 int oracle_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
                            const int64_t* kstart, const int64_t* pos, const int32_t* sel,
                            int64_t n, int Hq, int Hkv, int D, int Bk, int topk, double scale,
@@ -237,75 +238,95 @@ int oracle_sparse_attn_bwd(const void* q, const void* k, const void* v, const vo
   if (dtype != 0 && dtype != 1) return 1;
   const int r_heads = Hq / Hkv;
 
+  /* dk and dv cover every key row any query row reaches */
+  int64_t nkeys = 0;
+  for (int64_t r = 0; r < n; ++r)
+    if (pos[r] >= 0 && kstart[r] + pos[r] + 1 > nkeys) nkeys = kstart[r] + pos[r] + 1;
+  const size_t kv_elems = (size_t)nkeys * (size_t)Hkv * (size_t)D;
+
   int bad = 0;
-#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
-  for (int64_t r = 0; r < n; ++r) {
+#pragma omp parallel reduction(| : bad)
+  {
+    /* each thread sums its rows' dk / dv contributions privately; the
+     * per-thread sums are added at the end */
+    double* my_dk = (double*)calloc(kv_elems ? kv_elems : 1, sizeof(double));
+    double* my_dv = (double*)calloc(kv_elems ? kv_elems : 1, sizeof(double));
     int32_t* blocks = (int32_t*)malloc(sizeof(int32_t) * (size_t)topk);
     double* z = (double*)malloc(sizeof(double) * (size_t)topk * (size_t)Bk);
     double* dp = (double*)malloc(sizeof(double) * (size_t)topk * (size_t)Bk);
     int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)topk * (size_t)Bk);
-    if (!blocks || !z || !dp || !keys) { bad = 1; free(blocks); free(z); free(dp); free(keys); continue; }
-    const int64_t p = pos[r];
+    const int ok = my_dk && my_dv && blocks && z && dp && keys;
+    if (!ok) bad = 1;
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+      if (!ok) continue;
+      const int64_t p = pos[r];
+      for (int h = 0; h < Hq; ++h) {
+        const int g = h / r_heads;
+        double* dqh = dq + (r * Hq + h) * (int64_t)D;
+        for (int d = 0; d < D; ++d) dqh[d] = 0.0;
 
-    for (int h = 0; h < Hq; ++h) {
-      const int g = h / r_heads;
-      double* dqh = dq + (r * Hq + h) * (int64_t)D;
-      for (int d = 0; d < D; ++d) dqh[d] = 0.0;
+        /* J as in the forward definition: Sel taken as a set, keys j <= p */
+        int nb = 0;
+        for (int i = 0; i < topk; ++i) {
+          int32_t c = sel[(r * Hkv + g) * (int64_t)topk + i];
+          if (c >= 0) blocks[nb++] = c;
+        }
+        qsort(blocks, (size_t)nb, sizeof(int32_t), ascending_int);
+        int64_t nk = 0;
+        for (int i = 0; i < nb; ++i) {
+          if (i > 0 && blocks[i] == blocks[i - 1]) continue;
+          for (int64_t j = (int64_t)blocks[i] * Bk; j < ((int64_t)blocks[i] + 1) * Bk; ++j)
+            if (j <= p) keys[nk++] = j;
+        }
+        if (nk == 0) continue;
 
-      /* J as in the forward definition: Sel taken as a set, keys j <= p */
-      int nb = 0;
-      for (int i = 0; i < topk; ++i) {
-        int32_t c = sel[(r * Hkv + g) * (int64_t)topk + i];
-        if (c >= 0) blocks[nb++] = c;
-      }
-      qsort(blocks, (size_t)nb, sizeof(int32_t), ascending_int);
-      int64_t nk = 0;
-      for (int i = 0; i < nb; ++i) {
-        if (i > 0 && blocks[i] == blocks[i - 1]) continue;
-        for (int64_t j = (int64_t)blocks[i] * Bk; j < ((int64_t)blocks[i] + 1) * Bk; ++j)
-          if (j <= p) keys[nk++] = j;
-      }
-      if (nk == 0) continue;
-
-      const int64_t qoff = (r * Hq + h) * (int64_t)D;
-      double m = -INFINITY;
-      for (int64_t a = 0; a < nk; ++a) {
-        const int64_t koff = ((kstart[r] + keys[a]) * Hkv + g) * (int64_t)D;
-        double dot = 0.0;
-        for (int d = 0; d < D; ++d)
-          dot += (double)load_elem(q, dtype, qoff + d) * (double)load_elem(k, dtype, koff + d);
-        z[a] = scale * dot;
-        if (z[a] > m) m = z[a];
-      }
-      double l = 0.0;
-      for (int64_t a = 0; a < nk; ++a) {
-        z[a] = exp(z[a] - m);
-        l += z[a];
-      }
-      double delta = 0.0;
-      for (int64_t a = 0; a < nk; ++a) {
-        z[a] /= l; /* z now holds P */
-        const int64_t voff = ((kstart[r] + keys[a]) * Hkv + g) * (int64_t)D;
-        double dot = 0.0;
-        for (int d = 0; d < D; ++d)
-          dot += (double)load_elem(dout, dtype, qoff + d) * (double)load_elem(v, dtype, voff + d);
-        dp[a] = dot;
-        delta += z[a] * dot;
-      }
-      for (int64_t a = 0; a < nk; ++a) {
-        const double ds = z[a] * (dp[a] - delta);
-        const int64_t koff = ((kstart[r] + keys[a]) * Hkv + g) * (int64_t)D;
-        for (int d = 0; d < D; ++d) {
-          dqh[d] += scale * ds * (double)load_elem(k, dtype, koff + d);
-          const double gk = scale * ds * (double)load_elem(q, dtype, qoff + d);
-          const double gv = z[a] * (double)load_elem(dout, dtype, qoff + d);
-#pragma omp atomic
-          dk[koff + d] += gk;
-#pragma omp atomic
-          dv[koff + d] += gv;
+        const int64_t qoff = (r * Hq + h) * (int64_t)D;
+        double m = -INFINITY;
+        for (int64_t a = 0; a < nk; ++a) {
+          const int64_t koff = ((kstart[r] + keys[a]) * Hkv + g) * (int64_t)D;
+          double dot = 0.0;
+          for (int d = 0; d < D; ++d)
+            dot += (double)load_elem(q, dtype, qoff + d) * (double)load_elem(k, dtype, koff + d);
+          z[a] = scale * dot;
+          if (z[a] > m) m = z[a];
+        }
+        double l = 0.0;
+        for (int64_t a = 0; a < nk; ++a) {
+          z[a] = exp(z[a] - m);
+          l += z[a];
+        }
+        double delta = 0.0;
+        for (int64_t a = 0; a < nk; ++a) {
+          z[a] /= l; /* z now holds P */
+          const int64_t voff = ((kstart[r] + keys[a]) * Hkv + g) * (int64_t)D;
+          double dot = 0.0;
+          for (int d = 0; d < D; ++d)
+            dot += (double)load_elem(dout, dtype, qoff + d) * (double)load_elem(v, dtype, voff + d);
+          dp[a] = dot;
+          delta += z[a] * dot;
+        }
+        for (int64_t a = 0; a < nk; ++a) {
+          const double ds = z[a] * (dp[a] - delta);
+          const int64_t koff = ((kstart[r] + keys[a]) * Hkv + g) * (int64_t)D;
+          for (int d = 0; d < D; ++d) {
+            dqh[d] += scale * ds * (double)load_elem(k, dtype, koff + d);
+            my_dk[koff + d] += scale * ds * (double)load_elem(q, dtype, qoff + d);
+            my_dv[koff + d] += z[a] * (double)load_elem(dout, dtype, qoff + d);
+          }
         }
       }
     }
+#pragma omp critical
+    {
+      if (ok)
+        for (size_t i = 0; i < kv_elems; ++i) {
+          dk[i] += my_dk[i];
+          dv[i] += my_dv[i];
+        }
+    }
+    free(my_dk);
+    free(my_dv);
     free(blocks);
     free(z);
     free(dp);
