@@ -263,7 +263,37 @@ def main():
     result["prefill"]["attention_fp8_kv"] = {
         "ms": round(att8_ms, 3), "tflops": round(att_flops / (att8_ms / 1e3) / 1e12, 1),
         "frac_mfma": round(att_flops / (att8_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    del inp, calls, q8, k8, kv8, vv8
+    # The backward of the attention calls (an extra measurement): dq, dk, dv
+    # for every tile from its forward out / lse and a seeded dO.
+    dout = synth.normal(inp["q"].shape, torch.bfloat16, dev, 0, "dout")
+    ws_b = torch.empty(max(1, max(msa.msa_sparse_attn_backward_workspace_size(1, c["m"], c["hi"], Hq, G, D, wl.topk)
+                                  for c in calls)), dtype=torch.uint8, device=dev)
+    dq_b = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    dk_b = torch.empty((L, G, D), dtype=torch.float32, device=dev)
+    dv_b = torch.empty_like(dk_b)
+    run_step()  # bf16 K/V forward outputs for the backward
+
+    def bwd_step():
+        for c in calls:
+            msa.msa_sparse_attn_backward(c["q"], inp["k"][:c["hi"]], inp["v"][:c["hi"]], c["out"],
+                                         dout[c["lo"]:c["hi"]], c["lse"], c["ids"], c["cu_q"], c["cu_k"], c["m"],
+                                         c["hi"], wl.block_size, wl.topk, dq=dq_b[:c["m"]], dk=dk_b[:c["hi"]],
+                                         dv=dv_b[:c["hi"]], workspace=ws_b, stream=stream)
+
+    bwd_step()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        bwd_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    bwd_ms = e0.elapsed_time(e1) / args.steps
+    bwd_flops = 2.5 * att_flops  # S recomputed, dP, dV, dK, dQ: five products of the forward's size
+    result["prefill"]["backward"] = {
+        "ms": round(bwd_ms, 3), "tflops": round(bwd_flops / (bwd_ms / 1e3) / 1e12, 1),
+        "frac_mfma": round(bwd_flops / (bwd_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "algorithmic_flops": bwd_flops}
+    del inp, calls, q8, k8, kv8, vv8, dout, dq_b, dk_b, dv_b, ws_b
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ decode

@@ -75,6 +75,10 @@ hipError_t launch_attn_kvouter(const AttnPlan& pl, bool kv_e4m3, const AttnArgs&
 size_t kvo_part_slot_bytes();
 int kvo_window_rows();
 
+// Edges per workgroup chunk of the KV-outer schedules (chunk_start counts
+// chunks of this many edges).
+constexpr int kEdgeChunk = 64;
+
 // Per-(sequence, group, block) lists of the selection entries of query rows
 // [row_lo, row_hi): each entry is ((row - row_lo) << 4 | selection slot), the
 // entries of bucket i are edges[offsets[i] .. offsets[i + 1]) in no
@@ -91,6 +95,7 @@ struct BwdPlan {
   int64_t rows_bound = 0;
   int64_t window = 0;        // query rows per edge-list window
   size_t counts_off = 0, offsets_off = 0, chunks_off = 0, cursor_off = 0, edges_off = 0, delta_off = 0;
+  size_t part_dq_off = 0;    // [window rows, G, topk, 16, 128] fp32
   size_t workspace_bytes = 0;
 };
 BwdPlan plan_bwd(int batch, int max_q_len, int max_kv_len, int Hq, int G, int topk);

@@ -16,24 +16,27 @@
 // Kernels (bf16 inputs, fp32 accumulation and fp32 gradients):
 //   bwd_zero   dk = dv = 0 for the key rows of the call
 //   bwd_delta  delta[row, head] = dO . O
-//   bwd_sort   sorts each bucket's edge list (the lists the KV-outer forward
-//              builds, placed by atomics in no fixed order), so the order in
-//              which bwd_dkdv sums the edges, and so every rounding, is fixed
 //   bwd_dkdv   KV-outer, one workgroup per (sequence, group, block) bucket of
-//              the selection edge lists.  Each of the 4 waves owns 32 keys of
+//              the selection edge lists (the lists the KV-outer forward
+//              builds).  The bucket's list, placed by atomics in no fixed
+//              order, is first sorted in LDS, so the order in which the edges
+//              are summed (and so every rounding) is fixed.  Each of the 4
+//              waves owns 32 keys of
 //              the block and keeps their K and V rows in registers as MFMA
-//              operands; the edges run in pairs (2
-//              queries x 16 heads = 32 MFMA rows), whose Q and dO are staged in
+//              operands; the edges run in quads (4
+//              queries x 16 heads = 64 MFMA rows), whose Q and dO are staged in
 //              LDS twice, row-major for S = Q K^T and dP = dO V^T and
 //              transposed for dV += P^T dO and dK += dS^T Q, so the P and dS
 //              registers of the first two products are directly the A
 //              operands of the last two.  dK and dV accumulate over the
 //              bucket in registers and are added to the output once per
 //              window of query rows.
-//   bwd_dq     query-outer, one wave per (row, group) as in the forward
-//              kernel: S^T = K Q^T and dP^T = V dO^T with the heads as the 16
-//              MFMA columns, then dQ^T += K^T dS^T through a wave-private
-//              transposed K tile.
+//   bwd_dq_kvo KV-outer like the forward, one workgroup per chunk of <= 64
+//              edges of a bucket: S^T = K Q^T and dP^T = V dO^T with two
+//              queries x 16 heads as the 32 MFMA columns, then dQ += dS K
+//              from registers; each edge writes its block's dQ contribution
+//              to the fp32 partial of its selection slot
+//   bwd_dq_combine  dq = sum of a row's slot partials in slot order
 // No atomics touch the arithmetic: every result is bitwise reproducible.
 #include "msa_device.h"
 #include "msa_launch.h"
@@ -42,9 +45,8 @@ namespace msa {
 
 constexpr int kBwdThreads = 256;
 constexpr int kBwdRow = 136;      // LDS row of Q / dO for one MFMA row: 128 bf16 + 8 pad
-constexpr int kBwdT = 36;         // LDS row of Q^T / dO^T for one dim: 32 columns + 4 pad
-constexpr int kSortMax = 8192;    // edges of one bucket in one window (<= rows per window)
-constexpr int kQtStride = 36;     // bwd_dq: wave-private K^T tile row (32 keys + 4 pad)
+constexpr int kBwdWindow = 4096;  // query rows per edge-list window
+constexpr int kSortMax = kBwdWindow;  // edges of one bucket in one window (<= rows per window)
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdKernelArgs {
@@ -61,8 +63,10 @@ struct BwdKernelArgs {
   int64_t rows_bound, row_lo;
   float scale, scale_log2;
   const int32_t* offsets;
+  const int32_t* chunk_start;
   int32_t* edges;
   float* delta;
+  float* part_dq;
   float* dq;
   float* dk;
   float* dv;
@@ -101,118 +105,171 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdKernelArgs a) {
   if ((threadIdx.x & 31) == 0) a.delta[rh] = s;
 }
 
-// One pair of edges, staged by the whole workgroup: each thread holds two
-// 16-byte pieces of Q and two of dO (piece pc = tid + 256 u: MFMA row pc / 16,
-// dims 8 (pc % 16) .. +7).
-struct PairStage {
-  bf16x8 q[2];
-  bf16x8 g[2];
-  float lse, delta;  // threads 0..31: MFMA row tid
-  int pos;           // threads 0..1: position of query tid of the pair
+// One quad of edges (4 queries x 16 heads = 64 MFMA rows), staged by the
+// whole workgroup.  Thread tid owns two units of 4 MFMA rows x 8 dims: unit
+// v = tid + 256 u, tensor v / 256 (Q or dO), row quad (v % 256) / 16, dim
+// octet v % 16 (16 consecutive threads read a row's 256 contiguous bytes).
+constexpr int kQuadRows = 64;
+constexpr int kBwdT = kQuadRows + 4;  // LDS row of Q^T / dO^T for one dim: 64 rows + 4 pad
+
+struct QuadStage {
+  bf16x8 x[2][4];    // unit u: rows 4 rq + j, dims 8 o8 .. +7, as loaded
+  unsigned ok;       // bit 4 u + j: that row exists (else it is stored as 0)
+  float lse, delta;  // threads 0..63: MFMA row tid (lse as loaded, +inf for a missing row)
+  int pos;           // threads 64..67: position of query tid - 64 of the quad
 };
 
-__device__ __forceinline__ void bwd_load_pair(const BwdKernelArgs& a, PairStage& S, int e, int e_hi, int g, int R,
-                                              int N, int M, int64_t q0) {
+// Loads quad `qi` of the bucket (sorted codes in LDS, n edges) into registers.
+// Nothing here consumes the loaded values (the zeroing of missing rows and the
+// lse scaling happen when the quad is stored), so the loads stay in flight
+// while the previous quad is computed.
+__device__ __forceinline__ void bwd_load_quad(const BwdKernelArgs& a, QuadStage& S, const int32_t* codes, int qi,
+                                              int n, int g, int R, int N, int M, int64_t q0) {
   const int tid = threadIdx.x;
+  const int e = 4 * qi;
+  S.ok = 0;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int pc = tid + kBwdThreads * u;
-    const int col = pc >> 4, d8 = (pc & 15) * 8;
-    const int jq = col >> 4, h = col & 15;
-    const bool ok = e + jq < e_hi && h < R;
-    const int64_t t = ok ? a.row_lo + (a.edges[e + jq] >> 4) : 0;
-    const int64_t off = (t * a.Hq + g * R + (ok ? h : 0)) * kHeadDim + d8;
-    S.q[u] = ok ? load8(a.q + off) : zero8<bf16>();
-    S.g[u] = ok ? load8(a.dout + off) : zero8<bf16>();
+    const int v = tid + kBwdThreads * u;
+    const bf16* src = (v >> 8) ? a.dout : a.q;
+    const int rq = (v & 255) >> 4, o8 = v & 15;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // branch-free: a missing row reads the first row of the window
+      const int row = 4 * rq + j;
+      const int jq = row >> 4, h = row & 15;
+      const bool ok = e + jq < n && h < R;
+      const int64_t t = a.row_lo + (ok ? (codes[e + jq] >> 4) : 0);
+      S.x[u][j] = load8(src + (t * a.Hq + g * R + (ok ? h : 0)) * kHeadDim + 8 * o8);
+      S.ok |= ok ? (1u << (4 * u + j)) : 0u;
+    }
   }
-  if (tid < 32) {
+  if (tid < kQuadRows) {
     const int jq = tid >> 4, h = tid & 15;
-    const bool ok = e + jq < e_hi && h < R;
-    const int64_t t = ok ? a.row_lo + (a.edges[e + jq] >> 4) : 0;
-    // an empty MFMA row gets lse = +inf, so its probabilities are exactly 0
-    S.lse = ok ? a.lse[t * a.Hq + g * R + h] * kLog2e : __builtin_inff();
-    S.delta = ok ? a.delta[t * a.Hq + g * R + h] : 0.f;
-  } else if (tid < 34) {
-    const int jq = tid - 32;
-    const bool ok = e + jq < e_hi;
-    const int64_t t = ok ? a.row_lo + (a.edges[e + jq] >> 4) : 0;
+    const bool ok = e + jq < n && h < R;
+    const int64_t t = a.row_lo + (ok ? (codes[e + jq] >> 4) : 0);
+    const int64_t rh = t * a.Hq + g * R + (ok ? h : 0);
+    S.lse = a.lse[rh];
+    S.delta = a.delta[rh];
+    S.ok |= ok ? 256u : 0u;
+  } else if (tid < kQuadRows + 4) {
+    const int jq = tid - kQuadRows;
+    const bool ok = e + jq < n;
+    const int64_t t = a.row_lo + (ok ? (codes[e + jq] >> 4) : 0);
     S.pos = ok ? (int)((int64_t)N - M + (t - q0)) : -1;
   }
 }
 
 struct BwdLds {
-  bf16 q_rm[2][32 * kBwdRow];
-  bf16 g_rm[2][32 * kBwdRow];
+  bf16 q_rm[2][kQuadRows * kBwdRow];
+  bf16 g_rm[2][kQuadRows * kBwdRow];
   bf16 q_t[2][kHeadDim * kBwdT];
   bf16 g_t[2][kHeadDim * kBwdT];
-  float lse[2][32];
-  float delta[2][32];
-  int pos[2][2];
+  float lse[2][kQuadRows];    // per MFMA row, log2 units (read 4 at a time)
+  float delta[2][kQuadRows];
+  int pos[2][4];
 };
 
-__device__ __forceinline__ void bwd_store_pair(BwdLds& L, int buf, const PairStage& S) {
+__device__ __forceinline__ void bwd_store_quad(BwdLds& L, int buf, const QuadStage& S) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int pc = tid + kBwdThreads * u;
-    const int col = pc >> 4, d8 = (pc & 15) * 8;
-    *reinterpret_cast<bf16x8*>(&L.q_rm[buf][col * kBwdRow + d8]) = S.q[u];
-    *reinterpret_cast<bf16x8*>(&L.g_rm[buf][col * kBwdRow + d8]) = S.g[u];
+    const int v = tid + kBwdThreads * u;
+    const int rq = (v & 255) >> 4, o8 = v & 15;
+    bf16* rm = (v >> 8) ? L.g_rm[buf] : L.q_rm[buf];
+    bf16* tr = (v >> 8) ? L.g_t[buf] : L.q_t[buf];
+    bf16x8 x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = ((S.ok >> (4 * u + j)) & 1u) ? S.x[u][j] : zero8<bf16>();
+      *reinterpret_cast<bf16x8*>(rm + (4 * rq + j) * kBwdRow + 8 * o8) = x[j];
+    }
+    // transposed: dim 8 o8 + e, rows 4 rq .. 4 rq + 3 as one 8-byte run
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      L.q_t[buf][(d8 + e) * kBwdT + col] = S.q[u][e];
-      L.g_t[buf][(d8 + e) * kBwdT + col] = S.g[u][e];
+      const bf16x4 w = {x[0][e], x[1][e], x[2][e], x[3][e]};
+      *reinterpret_cast<bf16x4*>(tr + (8 * o8 + e) * kBwdT + 4 * rq) = w;
     }
   }
-  if (tid < 32) {
-    L.lse[buf][tid] = S.lse;
-    L.delta[buf][tid] = S.delta;
-  } else if (tid < 34) {
-    L.pos[buf][tid - 32] = S.pos;
+  if (tid < kQuadRows) {
+    // an empty MFMA row gets lse = +inf, so its probabilities are exactly 0
+    const bool ok = (S.ok >> 8) & 1u;
+    L.lse[buf][tid] = ok ? S.lse * kLog2e : __builtin_inff();
+    L.delta[buf][tid] = ok ? S.delta : 0.f;
+  } else if (tid < kQuadRows + 4) {
+    L.pos[buf][tid - kQuadRows] = S.pos;
   }
 }
 
-// Sort each bucket's edge codes ascending (bitonic, in LDS), in place.  The
-// lists are placed by atomics in no fixed order; sorting them fixes the order
-// in which bwd_dkdv sums the edges, so dK and dV are reproducible bit for bit.
-__global__ __launch_bounds__(kBwdThreads) void bwd_sort(BwdKernelArgs a) {
-  __shared__ int32_t srt[kSortMax];
+// One staged quad against this wave's 32 keys: for each half rh (32 MFMA
+// rows = 2 queries x 16 heads), S = Q K^T and dP = dO V^T (rows x keys), P
+// and dS; then dV += P^T dO and dK += dS^T Q over the 64 rows.
+__device__ __forceinline__ void bwd_quad_compute(const BwdLds& L, int buf, const bf16x8 (&kf)[kHeadDim / 16],
+                                                 const bf16x8 (&vf)[kHeadDim / 16], f32x16 (&dk_acc)[kHeadDim / 32],
+                                                 f32x16 (&dv_acc)[kHeadDim / 32], int key_seq, int col, int a32,
+                                                 float scale_log2) {
+  bf16x8 pa[4], dsa[4];  // k-step 2 rh + s2 of the second products
+#pragma unroll
+  for (int rh = 0; rh < 2; ++rh) {
+    f32x16 s = {}, dp = {};
+    const int arow = (32 * rh + col) * kBwdRow + 8 * a32;
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 16; ++ks) {
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&L.q_rm[buf][arow + 16 * ks]);
+      const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&L.g_rm[buf][arow + 16 * ks]);
+      s = mma32(qa, kf[ks], s);
+      dp = mma32(ga, vf[ks], dp);
+    }
+    // C layout: this lane's key, rows 32 rh + 8 (r / 4) + 4 a32 + r % 4; the
+    // four rows of each r / 4 are consecutive, so their lse and delta are one
+    // 16-byte read each; rows 16 j .. 16 j + 15 belong to query j of the quad
+    const bool live0 = key_seq <= L.pos[buf][2 * rh], live1 = key_seq <= L.pos[buf][2 * rh + 1];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 ls = *reinterpret_cast<const f32x4*>(&L.lse[buf][32 * rh + 8 * q4 + 4 * a32]);
+      const f32x4 dl = *reinterpret_cast<const f32x4*>(&L.delta[buf][32 * rh + 8 * q4 + 4 * a32]);
+      const bool live = q4 < 2 ? live0 : live1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * q4 + i;
+        const float p = live ? __builtin_amdgcn_exp2f(s[r] * scale_log2 - ls[i]) : 0.f;
+        const float ds = p * (dp[r] - dl[i]);
+        pa[2 * rh + (r >> 3)][r & 7] = bf16(p);
+        dsa[2 * rh + (r >> 3)][r & 7] = bf16(ds);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep each half's LDS reads next to its MFMAs
+  }
+  // dV[key][d] += sum_row P[row][key] dO[row][d]; dK likewise with dS and Q.
+  // k-step s4 covers rows 16 s4 .. +15; slot i of lane half a32 is row
+  // 16 s4 + 4 a32 + i (i < 4) or 16 s4 + 8 + 4 a32 + i - 4, matching the
+  // registers of pa / dsa above.
+#pragma unroll
+  for (int dt = 0; dt < kHeadDim / 32; ++dt) {
+    const int d = 32 * dt + col;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int c0 = d * kBwdT + 16 * s4 + 4 * a32;
+      const bf16x4 glo = *reinterpret_cast<const bf16x4*>(&L.g_t[buf][c0]);
+      const bf16x4 ghi = *reinterpret_cast<const bf16x4*>(&L.g_t[buf][c0 + 8]);
+      const bf16x4 qlo = *reinterpret_cast<const bf16x4*>(&L.q_t[buf][c0]);
+      const bf16x4 qhi = *reinterpret_cast<const bf16x4*>(&L.q_t[buf][c0 + 8]);
+      const bf16x8 gb = {glo[0], glo[1], glo[2], glo[3], ghi[0], ghi[1], ghi[2], ghi[3]};
+      const bf16x8 qb = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
+      dv_acc[dt] = mma32(pa[s4], gb, dv_acc[dt]);
+      dk_acc[dt] = mma32(dsa[s4], qb, dk_acc[dt]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
+  __shared__ __attribute__((aligned(16))) BwdLds L;
+  __shared__ int32_t codes[kSortMax];
   const int nbk = a.batch * a.G * a.nb_max;
   const int bucket = blockIdx.x;
   if (bucket >= nbk) return;
   const int e_lo = a.offsets[bucket];
   const int n = a.offsets[bucket + 1] - e_lo;
-  if (n <= 1) return;
-  const int tid = threadIdx.x;
-  int n2 = 1;
-  while (n2 < n) n2 <<= 1;
-  for (int i = tid; i < n2; i += kBwdThreads) srt[i] = i < n ? a.edges[e_lo + i] : 0x7fffffff;
-  __syncthreads();
-  for (int kk = 2; kk <= n2; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < n2; i += kBwdThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const int32_t x = srt[i], y = srt[ixj];
-          if ((x > y) == ((i & kk) == 0)) {
-            srt[i] = y;
-            srt[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int i = tid; i < n; i += kBwdThreads) a.edges[e_lo + i] = srt[i];
-}
-
-__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
-  __shared__ __attribute__((aligned(16))) BwdLds L;
-  const int nbk = a.batch * a.G * a.nb_max;
-  const int bucket = blockIdx.x;
-  if (bucket >= nbk) return;
-  const int e_lo = a.offsets[bucket], e_hi = a.offsets[bucket + 1];
-  const int n = e_hi - e_lo;
   if (n <= 0) return;
   const int c = bucket % a.nb_max;
   const int g = (bucket / a.nb_max) % a.G;
@@ -225,6 +282,31 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
   const int64_t rs = (int64_t)a.G * kHeadDim;
   const int tid = threadIdx.x;
 
+  // ---- the bucket's edge codes, sorted ascending in LDS (bitonic).  The
+  // lists are placed by atomics in no fixed order; sorting fixes the order in
+  // which the edges are summed, so dK and dV are reproducible bit for bit.
+  {
+    int n2 = 1;
+    while (n2 < n) n2 <<= 1;
+    for (int i = tid; i < n2; i += kBwdThreads) codes[i] = i < n ? a.edges[e_lo + i] : 0x7fffffff;
+    __syncthreads();
+    for (int kk = 2; kk <= n2; kk <<= 1) {
+      for (int j = kk >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < n2; i += kBwdThreads) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const int32_t x = codes[i], y = codes[ixj];
+            if ((x > y) == ((i & kk) == 0)) {
+              codes[i] = y;
+              codes[ixj] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+
   const int wave = tid >> 6;
   const int lane = lane_id();
   const int col = lane & 31;  // MFMA row of A / column of B and C
@@ -232,8 +314,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
   // this wave's 32 keys: K and V rows as the B operands of S = Q K^T and
   // dP = dO V^T (column = key, 8 dims per k-step half); rows past the
   // sequence end clamp to its last row and are masked (key > every p)
-  const int key_blk = 32 * wave + col;
-  const int key_seq = c * kBlock + key_blk;
+  const int key_seq = c * kBlock + 32 * wave + col;
   const int64_t krow = kb0 + (key_seq < N ? key_seq : N - 1);
   bf16x8 kf[kHeadDim / 16], vf[kHeadDim / 16];
 #pragma unroll
@@ -248,57 +329,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
     dv_acc[dt] = f32x16{};
   }
 
-  const int npairs = (n + 1) / 2;
-  PairStage S;
-  bwd_load_pair(a, S, e_lo, e_hi, g, R, N, M, q0);
-  bwd_store_pair(L, 0, S);
+  // Quads run through two LDS buffers: quad qi + 1 is loaded into registers
+  // while quad qi is computed, then stored to the other buffer.
+  const int nquads = (n + 3) / 4;
+  QuadStage S;
+  bwd_load_quad(a, S, codes, 0, n, g, R, N, M, q0);
+  bwd_store_quad(L, 0, S);
   __syncthreads();
-  for (int pi = 0; pi < npairs; ++pi) {
-    const int buf = pi & 1;
-    const bool more = pi + 1 < npairs;
-    if (more) bwd_load_pair(a, S, e_lo + 2 * (pi + 1), e_hi, g, R, N, M, q0);
-
-    // S[row][key] and dP[row][key], rows = (query of the pair, head)
-    f32x16 s = {}, dp = {};
-#pragma unroll
-    for (int ks = 0; ks < kHeadDim / 16; ++ks) {
-      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&L.q_rm[buf][col * kBwdRow + 16 * ks + 8 * a32]);
-      const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&L.g_rm[buf][col * kBwdRow + 16 * ks + 8 * a32]);
-      s = mma32(qa, kf[ks], s);
-      dp = mma32(ga, vf[ks], dp);
-    }
-    // C layout: this lane's key, rows 8 (r / 4) + 4 a32 + r % 4
-    bf16x8 pa[2], dsa[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r >> 2) + 4 * a32 + (r & 3);
-      const bool live = key_seq <= L.pos[buf][row >> 4];
-      const float p = live ? __builtin_amdgcn_exp2f(s[r] * a.scale_log2 - L.lse[buf][row]) : 0.f;
-      const float ds = p * (dp[r] - L.delta[buf][row]);
-      pa[r >> 3][r & 7] = bf16(p);
-      dsa[r >> 3][r & 7] = bf16(ds);
-    }
-    // dV[key][d] += sum_row P[row][key] dO[row][d]; dK likewise with dS and Q.
-    // k-step s2 covers rows 16 s2 .. +15; slot i of lane half a32 is row
-    // 16 s2 + 4 a32 + i (i < 4) or 16 s2 + 8 + 4 a32 + i - 4, matching the
-    // registers 8 s2 .. 8 s2 + 7 above.
-#pragma unroll
-    for (int dt = 0; dt < kHeadDim / 32; ++dt) {
-      const int d = 32 * dt + col;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int c0 = 16 * s2 + 4 * a32;
-        const bf16x4 glo = *reinterpret_cast<const bf16x4*>(&L.g_t[buf][d * kBwdT + c0]);
-        const bf16x4 ghi = *reinterpret_cast<const bf16x4*>(&L.g_t[buf][d * kBwdT + c0 + 8]);
-        const bf16x4 qlo = *reinterpret_cast<const bf16x4*>(&L.q_t[buf][d * kBwdT + c0]);
-        const bf16x4 qhi = *reinterpret_cast<const bf16x4*>(&L.q_t[buf][d * kBwdT + c0 + 8]);
-        const bf16x8 gb = {glo[0], glo[1], glo[2], glo[3], ghi[0], ghi[1], ghi[2], ghi[3]};
-        const bf16x8 qb = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
-        dv_acc[dt] = mma32(pa[s2], gb, dv_acc[dt]);
-        dk_acc[dt] = mma32(dsa[s2], qb, dk_acc[dt]);
-      }
-    }
-    if (more) bwd_store_pair(L, buf ^ 1, S);
+  for (int qi = 0; qi < nquads; ++qi) {
+    const int buf = qi & 1;
+    const bool more = qi + 1 < nquads;
+    if (more) bwd_load_quad(a, S, codes, qi + 1, n, g, R, N, M, q0);
+    bwd_quad_compute(L, buf, kf, vf, dk_acc, dv_acc, key_seq, col, a32, a.scale_log2);
+    if (more) bwd_store_quad(L, buf ^ 1, S);
     __syncthreads();
   }
 
@@ -316,149 +359,232 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
     }
 }
 
-// K rows key0 + 32 ks .. +31 as the units of the transposed staging: unit
-// u = (key quad u % 8, dim octet u / 8); lane handles u = lane and lane + 64.
-__device__ __forceinline__ void bwd_load_k_chunk(const bf16* kseq, int64_t rs, int64_t key0, int64_t p, int ks,
-                                                 int lane, bf16x8 (&r)[2][4]) {
+// ---------------------------------------------------------------- dQ
+// KV-outer, one workgroup per chunk of <= kEdgeChunk edges of one bucket (the
+// chunks of the forward's schedule).  K is staged row-major (A operand of
+// S^T = K Q^T) and transposed (B operand of dQ = dS K), V row-major (A operand
+// of dP^T = V dO^T).  Each wave runs pairs of edges (2 queries x 16 heads =
+// 32 MFMA columns) tile by tile over 32 keys: S^T and dP^T, then dS, whose
+// registers (column = the lane's (query, head), 8 keys per k-step) are
+// directly the A operand of dQ += dS K.  Each edge writes its block's dQ
+// contribution (fp32) to the partial slot of its selection entry; a
+// fixed-order sum over the slots follows.
+constexpr int kDqKRow = 136;   // K / V row: 128 bf16 + 8 pad
+constexpr int kDqKtRow = 132;  // K^T row (one dim, 128 keys) + 4 pad
+
+struct DqPair {
+  bf16x8 q[kHeadDim / 16];  // B operand Q^T: column (jq, h), dims 16 ks + 8 a32 .. +7
+  bf16x8 g[kHeadDim / 16];  // B operand dO^T, same layout
+  int code;                 // (row in window) << 4 | selection slot
+  bool has;                 // this lane's column holds an edge
+};
+
+__device__ __forceinline__ void dq_load_pair(const BwdKernelArgs& a, DqPair& P, int e, int e_hi, int jq, int h,
+                                             int a32, int g, int R) {
+  P.has = false;
+  P.code = 0;
+  if (e >= e_hi) return;
+  P.has = e + jq < e_hi;
+  P.code = a.edges[P.has ? e + jq : e];
+  const bool ok = P.has && h < R;
+  const int64_t off = ((a.row_lo + (P.code >> 4)) * a.Hq + g * R + (ok ? h : 0)) * kHeadDim + 8 * a32;
 #pragma unroll
-  for (int uu = 0; uu < 2; ++uu) {
-    const int u = lane + 64 * uu;
-    const int kq = u & 7, o8 = u >> 3;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      int64_t key = key0 + 32 * ks + 4 * kq + jj;
-      if (key > p) key = p;
-      r[uu][jj] = load8(kseq + key * rs + 8 * o8);
-    }
+  for (int ks = 0; ks < kHeadDim / 16; ++ks) {
+    P.q[ks] = ok ? load8(a.q + off + 16 * ks) : zero8<bf16>();
+    P.g[ks] = ok ? load8(a.dout + off + 16 * ks) : zero8<bf16>();
   }
 }
 
-__global__ __launch_bounds__(kBwdThreads) void bwd_dq(BwdKernelArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 kt_all[kBwdThreads / kWave][kHeadDim * kQtStride];
-  const int wave = threadIdx.x / kWave;
-  const int lane = lane_id();
-  bf16* ktile = kt_all[wave];
-  const int G = a.G;
-  const int64_t item = (int64_t)blockIdx.x * (kBwdThreads / kWave) + wave;
-  if (item >= a.rows_bound * G) return;
-  const int64_t t = item % a.rows_bound;
-  const int g = (int)(item / a.rows_bound);
-  if (t >= a.cu_q[a.batch]) return;
-  const int b = bwd_find(a.cu_q, a.batch, t);
-  const int64_t q0 = a.cu_q[b];
-  const int M = a.cu_q[b + 1] - a.cu_q[b];
-  const int64_t kb0 = a.cu_k[b];
-  const int N = a.cu_k[b + 1] - a.cu_k[b];
-  const int64_t p = (int64_t)N - M + (t - q0);
+__device__ __forceinline__ void dq_pair(const BwdKernelArgs& a, DqPair& P, int e_pf, int e_hi, const bf16* k_lds,
+                                        const bf16* v_lds, const bf16* kt_lds, int c, int g, int R, int N, int M,
+                                        int64_t q0, int col, int a32, int jq, int h) {
+  const int64_t trel = P.code >> 4;
+  const int64_t p = (int64_t)N - M + (a.row_lo + trel - q0);
+  const bool colok = P.has && h < R;
+  const int64_t rh = (a.row_lo + trel) * a.Hq + g * R + (colok ? h : 0);
+  // per column: lse in log2 units (+inf for an empty column: P = 0) and delta
+  const float lse2 = colok ? a.lse[rh] * kLog2e : __builtin_inff();
+  const float dlt = colok ? a.delta[rh] : 0.f;
+  // the codes of the pair's two edges, for the partial stores below
+  const int code0 = __shfl(P.code, 0, kWave), code1 = __shfl(P.code, 16, kWave);
+  const bool has1 = __shfl((int)P.has, 16, kWave) != 0;
 
-  const int R = a.Hq / G;
-  const int h = lane & 15;
-  const int a4 = lane >> 4;
-  const int hq = g * R + h;
-  const bool head_ok = h < R;
-  const int64_t qoff = (t * a.Hq + (head_ok ? hq : g * R)) * kHeadDim;
-  // B operands Q^T and dO^T: column h, dims 32 ds + 8 a4 .. +7
-  bf16x8 qf[kHeadDim / 32], gf[kHeadDim / 32];
+  f32x16 acc[kHeadDim / 32];
 #pragma unroll
-  for (int ds = 0; ds < kHeadDim / 32; ++ds) {
-    qf[ds] = head_ok ? load8(a.q + qoff + 32 * ds + 8 * a4) : zero8<bf16>();
-    gf[ds] = head_ok ? load8(a.dout + qoff + 32 * ds + 8 * a4) : zero8<bf16>();
-  }
-  // per column (head): lse in log2 units (+inf for a missing head: P = 0) and delta
-  const float lse2 = head_ok ? a.lse[t * a.Hq + hq] * kLog2e : __builtin_inff();
-  const float dlt = head_ok ? a.delta[t * a.Hq + hq] : 0.f;
-
-  f32x4 acc[kHeadDim / 16];
+  for (int dt = 0; dt < kHeadDim / 32; ++dt) acc[dt] = f32x16{};
+#pragma unroll 1
+  for (int kt = 0; kt < kBlock / 32; ++kt) {
+    f32x16 st = {}, dpt = {};
+    const bf16* krow = k_lds + (32 * kt + col) * kDqKRow + 8 * a32;
+    const bf16* vrow = v_lds + (32 * kt + col) * kDqKRow + 8 * a32;
 #pragma unroll
-  for (int dt = 0; dt < kHeadDim / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (p >= 0) {
-    const int64_t local = p / kBlock;
-    const int32_t* sel = a.block_idx + (t * G + g) * a.topk;
-    const int64_t rs = (int64_t)G * kHeadDim;
-    const bf16* kseq = a.k + kb0 * rs + g * kHeadDim;
-    const bf16* vseq = a.v + kb0 * rs + g * kHeadDim;
-    for (int i = 0; i < a.topk; ++i) {
-      const int c = sel[i];
-      bool seen = false;  // Sel is a set
-      for (int j = 0; j < i; ++j) seen = seen || sel[j] == c;
-      if (c < 0 || c > local || seen) continue;
-      const int64_t key0 = (int64_t)c * kBlock;
-
-      // S^T and dP^T for the block's 8 tiles of 16 keys (A row = lane % 16)
-      f32x4 st[kBlock / 16], dpt[kBlock / 16];
+    for (int ks = 0; ks < kHeadDim / 16; ++ks) {
+      st = mma32(*reinterpret_cast<const bf16x8*>(krow + 16 * ks), P.q[ks], st);
+      dpt = mma32(*reinterpret_cast<const bf16x8*>(vrow + 16 * ks), P.g[ks], dpt);
+    }
+    if (kt == kBlock / 32 - 1) {
+      // Q^T and dO^T are free now: fetch the pair two steps ahead into them
+      // after keeping what the partial stores need
+      dq_load_pair(a, P, e_pf, e_hi, jq, h, a32, g, R);
+    }
+    // C layout: column = this lane's (query, head); rows = keys
+    // 32 kt + 8 (r / 4) + 4 a32 + r % 4
+    const int64_t rel = p - (int64_t)c * kBlock - 32 * kt - 4 * a32;
+    bf16x8 dsa[2];
 #pragma unroll
-      for (int kt = 0; kt < kBlock / 16; ++kt) {
-        int64_t key = key0 + 16 * kt + h;
-        if (key > p) key = p;
-        const bf16* kp = kseq + key * rs + 8 * a4;
-        const bf16* vp = vseq + key * rs + 8 * a4;
-        bf16x8 kfr[kHeadDim / 32], vfr[kHeadDim / 32];
+    for (int r = 0; r < 16; ++r) {
+      const bool live = 8 * (r >> 2) + (r & 3) <= rel;
+      const float pr = live ? __builtin_amdgcn_exp2f(st[r] * a.scale_log2 - lse2) : 0.f;
+      dsa[r >> 3][r & 7] = bf16(pr * (dpt[r] - dlt));
+    }
+    // dQ[(q, h)][d] += dS[(q, h)][key] K[key][d]; k-step s covers keys
+    // 32 kt + 16 s .. +15, slot i of lane half a32 is key 16 s + 4 a32 + i
+    // (i < 4) or 16 s + 8 + 4 a32 + i - 4: the registers 8 s .. 8 s + 7
 #pragma unroll
-        for (int ds = 0; ds < kHeadDim / 32; ++ds) {
-          kfr[ds] = load8(kp + 32 * ds);
-          vfr[ds] = load8(vp + 32 * ds);
-        }
-        f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < kHeadDim / 32; ++dt) {
+      const bf16* src = kt_lds + (32 * dt + col) * kDqKtRow + 32 * kt + 4 * a32;
 #pragma unroll
-        for (int ds = 0; ds < kHeadDim / 32; ++ds) {
-          x = mma16(kfr[ds], qf[ds], x);
-          y = mma16(vfr[ds], gf[ds], y);
-        }
-        st[kt] = x;
-        dpt[kt] = y;
-      }
-      // dS^T = P^T (dP^T - delta); this lane: head h, keys 16 kt + 4 a4 + r
-      const int64_t rel = p - key0 - 4 * a4;
-      const int lim = rel > kBlock ? kBlock : (int)rel;
-#pragma unroll
-      for (int kt = 0; kt < kBlock / 16; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pr = (16 * kt + r > lim) ? 0.f : __builtin_amdgcn_exp2f(st[kt][r] * a.scale_log2 - lse2);
-          st[kt][r] = pr * (dpt[kt][r] - dlt);
-        }
-
-      // dQ^T[d][h] += K^T[d][key] dS^T[key][h], 32 keys at a time
-#pragma unroll
-      for (int ks = 0; ks < kBlock / 32; ++ks) {
-        bf16x8 kr[2][4];
-        bwd_load_k_chunk(kseq, rs, key0, p, ks, lane, kr);
-#pragma unroll
-        for (int uu = 0; uu < 2; ++uu) {
-          const int u = lane + 64 * uu;
-          const int kq = u & 7, o8 = u >> 3;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            bf16x4 w = {kr[uu][0][e], kr[uu][1][e], kr[uu][2][e], kr[uu][3][e]};
-            *reinterpret_cast<bf16x4*>(ktile + (8 * o8 + e) * kQtStride + 4 * kq) = w;
-          }
-        }
-        __builtin_amdgcn_wave_barrier();
-        // B operand dS^T: slots r < 4 -> key 32 ks + 4 a4 + r, r >= 4 -> 32 ks + 16 + 4 a4 + r - 4
-        bf16x8 pb;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pb[r] = bf16(st[2 * ks][r]);
-          pb[4 + r] = bf16(st[2 * ks + 1][r]);
-        }
-#pragma unroll
-        for (int dt = 0; dt < kHeadDim / 16; ++dt) {
-          const bf16* src = ktile + (16 * dt + h) * kQtStride + 4 * a4;
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src + 16);
-          const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[dt] = mma16(va, pb, acc[dt]);
-        }
-        __builtin_amdgcn_wave_barrier();
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src + 16 * s2);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src + 16 * s2 + 8);
+        const bf16x8 kb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[dt] = mma32(dsa[s2], kb, acc[dt]);
       }
     }
   }
-  if (!head_ok) return;
-  float* dq = a.dq + (t * a.Hq + hq) * kHeadDim;
+  // C layout of acc[dt]: column = dim 32 dt + col, rows (query, head)
+  // 8 (r / 4) + 4 a32 + r % 4: rows 0..15 are query 0 of the pair, 16..31 query 1
+  float* part = a.part_dq;
 #pragma unroll
-  for (int dt = 0; dt < kHeadDim / 16; ++dt)
-    *reinterpret_cast<f32x4*>(dq + 16 * dt + 4 * a4) = acc[dt] * a.scale;
+  for (int r = 0; r < 16; ++r) {
+    const int row = 8 * (r >> 2) + 4 * a32 + (r & 3);
+    const int q = row >> 4, hh = row & 15;
+    if (hh >= R || (q == 1 && !has1)) continue;
+    const int cd = q ? code1 : code0;
+    const int64_t slot = ((int64_t)(cd >> 4) * a.G + g) * a.topk + (cd & 15);
+    float* dst = part + (slot * 16 + hh) * kHeadDim + col;
+#pragma unroll
+    for (int dt = 0; dt < kHeadDim / 32; ++dt) dst[32 * dt] = acc[dt][r];
+  }
+}
+
+__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kvo(BwdKernelArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 k_lds[kBlock * kDqKRow];
+  __shared__ __attribute__((aligned(16))) bf16 v_lds[kBlock * kDqKRow];
+  __shared__ __attribute__((aligned(16))) bf16 kt_lds[kHeadDim * kDqKtRow];
+  const int nbk = a.batch * a.G * a.nb_max;
+  const int w = blockIdx.x;
+  if (w >= a.chunk_start[nbk]) return;
+  const int bucket = bwd_find(a.chunk_start, nbk, w);
+  const int chunk = w - a.chunk_start[bucket];
+  const int c = bucket % a.nb_max;
+  const int g = (bucket / a.nb_max) % a.G;
+  const int b = bucket / (a.nb_max * a.G);
+  const int e_lo = a.offsets[bucket] + chunk * kEdgeChunk;
+  const int e_hi = min(e_lo + kEdgeChunk, a.offsets[bucket + 1]);
+  const int64_t kb0 = a.cu_k[b];
+  const int N = a.cu_k[b + 1] - a.cu_k[b];
+  const int64_t q0 = a.cu_q[b];
+  const int M = a.cu_q[b + 1] - a.cu_q[b];
+  const int64_t rs = (int64_t)a.G * kHeadDim;
+
+  // ---- stage K and V row-major, K transposed (rows past the sequence end
+  // clamp to its last row; their scores are masked)
+  {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int piece = threadIdx.x + u * kBwdThreads;
+      const int row = piece >> 4, cc = (piece & 15) * 8;
+      const int64_t key = min(c * kBlock + row, N - 1);
+      const int64_t off = (kb0 + key) * rs + g * kHeadDim + cc;
+      *reinterpret_cast<bf16x8*>(k_lds + row * kDqKRow + cc) = load8(a.k + off);
+      *reinterpret_cast<bf16x8*>(v_lds + row * kDqKRow + cc) = load8(a.v + off);
+    }
+    // K^T unit = (key quad kq, dim octet o8): 4 rows x 8 dims, written as 8 runs of 4 keys
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) {
+      const int u = threadIdx.x + uu * kBwdThreads;
+      const int kq = u & 31, o8 = u >> 5;
+      bf16x8 r4[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int64_t key = min(c * kBlock + 4 * kq + jj, N - 1);
+        r4[jj] = load8(a.k + (kb0 + key) * rs + g * kHeadDim + 8 * o8);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bf16x4 w4 = {r4[0][e], r4[1][e], r4[2][e], r4[3][e]};
+        *reinterpret_cast<bf16x4*>(kt_lds + (8 * o8 + e) * kDqKtRow + 4 * kq) = w4;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int col = lane & 31;
+  const int a32 = lane >> 5;
+  const int jq = col >> 4, h = col & 15;
+  const int R = a.Hq / a.G;
+  constexpr int kPairStride = 2 * (kBwdThreads / kWave);
+  const int e0 = e_lo + 2 * wave;
+  DqPair A, B;
+  dq_load_pair(a, A, e0, e_hi, jq, h, a32, g, R);
+  dq_load_pair(a, B, e0 + kPairStride, e_hi, jq, h, a32, g, R);
+  for (int e = e0; e < e_hi; e += 2 * kPairStride) {
+    dq_pair(a, A, e + 2 * kPairStride, e_hi, k_lds, v_lds, kt_lds, c, g, R, N, M, q0, col, a32, jq, h);
+    if (e + kPairStride >= e_hi) break;
+    dq_pair(a, B, e + 3 * kPairStride, e_hi, k_lds, v_lds, kt_lds, c, g, R, N, M, q0, col, a32, jq, h);
+  }
+}
+
+// Validity of the entries of one selection row: attended when the id names a
+// block at or before the local block and does not repeat an earlier entry.
+__device__ __forceinline__ unsigned bwd_row_mask(const int32_t* sel, int topk, int64_t local, int nb_max) {
+  int cc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) cc[i] = i < topk ? sel[i] : -1;
+  unsigned mask = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    bool ok = cc[i] >= 0 && cc[i] <= local && cc[i] < nb_max;
+#pragma unroll
+    for (int j = 0; j < i; ++j) ok = ok && (cc[j] != cc[i]);
+    mask |= ok ? (1u << i) : 0u;
+  }
+  return mask;
+}
+
+// dq = scale * sum over the row's selection slots (in slot order) of the
+// partials: one wave per (row, group), lane = (head lane / 4, 32 dims).
+__global__ __launch_bounds__(256) void bwd_dq_combine(BwdKernelArgs a, int64_t row_hi) {
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= (row_hi - a.row_lo) * a.G) return;
+  const int64_t trel = item / a.G;
+  const int g = (int)(item % a.G);
+  const int64_t t = a.row_lo + trel;
+  if (t >= a.cu_q[a.batch]) return;
+  const int lane = lane_id();
+  const int h = lane >> 2, d0 = 32 * (lane & 3);
+  const int R = a.Hq / a.G;
+  if (h >= R) return;
+  const int bq = bwd_find(a.cu_q, a.batch, t);
+  const int64_t p = (int64_t)(a.cu_k[bq + 1] - a.cu_k[bq]) - (a.cu_q[bq + 1] - a.cu_q[bq]) + (t - a.cu_q[bq]);
+  const unsigned mask = p >= 0 ? bwd_row_mask(a.block_idx + (t * a.G + g) * a.topk, a.topk, p / kBlock, a.nb_max)
+                               : 0u;
+  const int64_t slot0 = (trel * a.G + g) * a.topk;
+  f32x4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < a.topk; ++i) {
+    if (!((mask >> i) & 1u)) continue;
+    const float* src = a.part_dq + ((slot0 + i) * 16 + h) * kHeadDim + d0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] += *reinterpret_cast<const f32x4*>(src + 4 * j);
+  }
+  float* dst = a.dq + (t * a.Hq + g * R + h) * kHeadDim + d0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4*>(dst + 4 * j) = acc[j] * a.scale;
 }
 
 BwdPlan plan_bwd(int batch, int max_q_len, int max_kv_len, int Hq, int G, int topk) {
@@ -467,7 +593,7 @@ BwdPlan plan_bwd(int batch, int max_q_len, int max_kv_len, int Hq, int G, int to
   pl.nb_max = (max_kv_len + kBlock - 1) / kBlock;
   pl.nbuckets = batch * G * pl.nb_max;
   pl.rows_bound = (int64_t)batch * max_q_len;
-  const int64_t win = kvo_window_rows() < kSortMax ? kvo_window_rows() : kSortMax;
+  const int64_t win = kBwdWindow;
   pl.window = pl.rows_bound < win ? pl.rows_bound : win;
   const size_t nbk = (size_t)pl.nbuckets;
   size_t off = 0;
@@ -477,6 +603,7 @@ BwdPlan plan_bwd(int batch, int max_q_len, int max_kv_len, int Hq, int G, int to
   pl.cursor_off = off;  off += al(nbk * 4);
   pl.edges_off = off;   off += al((size_t)pl.window * G * topk * 4);
   pl.delta_off = off;   off += al((size_t)pl.rows_bound * Hq * 4);
+  pl.part_dq_off = off; off += al((size_t)pl.window * G * topk * 16 * kHeadDim * 4);
   pl.workspace_bytes = off;
   return pl;
 }
@@ -507,8 +634,10 @@ hipError_t launch_sparse_attn_bwd(const BwdPlan& pl, const BwdArgs& x, void* ws,
   int32_t* chunks = reinterpret_cast<int32_t*>(w + pl.chunks_off);
   int32_t* cursor = reinterpret_cast<int32_t*>(w + pl.cursor_off);
   a.offsets = offsets;
+  a.chunk_start = chunks;
   a.edges = reinterpret_cast<int32_t*>(w + pl.edges_off);
   a.delta = reinterpret_cast<float*>(w + pl.delta_off);
+  a.part_dq = reinterpret_cast<float*>(w + pl.part_dq_off);
   a.dq = x.dq;
   a.dk = x.dk;
   a.dv = x.dv;
@@ -520,12 +649,13 @@ hipError_t launch_sparse_attn_bwd(const BwdPlan& pl, const BwdArgs& x, void* ws,
     hipError_t e = build_edge_lists(x.fwd, pl.nb_max, r0, r1, counts, offsets, chunks, cursor, a.edges, st);
     if (e != hipSuccess) return e;
     a.row_lo = r0;
-    hipLaunchKernelGGL(bwd_sort, dim3((unsigned)pl.nbuckets), dim3(kBwdThreads), 0, st, a);
     hipLaunchKernelGGL(bwd_dkdv, dim3((unsigned)pl.nbuckets), dim3(kBwdThreads), 0, st, a);
+    // chunks of kEdgeChunk edges: at most entries / kEdgeChunk + one partial chunk per bucket
+    const int64_t entries = (r1 - r0) * a.G * a.topk;
+    const int64_t ub = entries / kEdgeChunk + (entries < pl.nbuckets ? entries : pl.nbuckets) + 1;
+    hipLaunchKernelGGL(bwd_dq_kvo, dim3((unsigned)ub), dim3(kBwdThreads), 0, st, a);
+    hipLaunchKernelGGL(bwd_dq_combine, dim3((unsigned)(((r1 - r0) * a.G + 3) / 4)), dim3(256), 0, st, a, r1);
   }
-  a.row_lo = 0;
-  const int64_t items = pl.rows_bound * a.G;
-  hipLaunchKernelGGL(bwd_dq, dim3((unsigned)((items + 3) / 4)), dim3(kBwdThreads), 0, st, a);
   return hipGetLastError();
 }
 

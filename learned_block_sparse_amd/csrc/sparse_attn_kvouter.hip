@@ -38,7 +38,7 @@
 namespace msa {
 
 constexpr int kKvoThreads = 256;
-constexpr int kKvoChunk = 64;   // edges per attention workgroup
+constexpr int kKvoChunk = kEdgeChunk;  // edges per attention workgroup
 constexpr int kKStride = 136;   // LDS row of K: 128 bf16 + 8 pad (272 B: 16-byte reads of 16 rows hit distinct banks)
 constexpr int kVtStride = 132;  // LDS row of V^T (one dim, 128 keys): 264 B, so 32 rows read at one key offset hit distinct banks
 constexpr int kRmax = 16;       // heads per group held by one partial slot
