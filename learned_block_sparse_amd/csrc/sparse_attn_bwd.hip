@@ -160,6 +160,11 @@ __device__ __forceinline__ void bwd_load_quad(const BwdKernelArgs& a, QuadStage&
   }
 }
 
+// Row group (4 rows) of dim d in the transposed Q / dO tiles: group grp is
+// stored at grp ^ ((d / 8) % 16).  The staging threads of a wave hold dims
+// 8 apart, whose rows would otherwise fall on the same few LDS banks.
+__device__ __forceinline__ int bwd_tgrp(int grp, int d) { return grp ^ ((d >> 3) & 15); }
+
 struct BwdLds {
   bf16 q_rm[2][kQuadRows * kBwdRow];
   bf16 g_rm[2][kQuadRows * kBwdRow];
@@ -184,11 +189,12 @@ __device__ __forceinline__ void bwd_store_quad(BwdLds& L, int buf, const QuadSta
       x[j] = ((S.ok >> (4 * u + j)) & 1u) ? S.x[u][j] : zero8<bf16>();
       *reinterpret_cast<bf16x8*>(rm + (4 * rq + j) * kBwdRow + 8 * o8) = x[j];
     }
-    // transposed: dim 8 o8 + e, rows 4 rq .. 4 rq + 3 as one 8-byte run
+    // transposed: dim 8 o8 + e, rows 4 rq .. 4 rq + 3 as one 8-byte run, at
+    // row group rq ^ o8 (see bwd_tgrp)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const bf16x4 w = {x[0][e], x[1][e], x[2][e], x[3][e]};
-      *reinterpret_cast<bf16x4*>(tr + (8 * o8 + e) * kBwdT + 4 * rq) = w;
+      *reinterpret_cast<bf16x4*>(tr + (8 * o8 + e) * kBwdT + 4 * bwd_tgrp(rq, 8 * o8 + e)) = w;
     }
   }
   if (tid < kQuadRows) {
@@ -249,11 +255,13 @@ __device__ __forceinline__ void bwd_quad_compute(const BwdLds& L, int buf, const
     const int d = 32 * dt + col;
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      const int c0 = d * kBwdT + 16 * s4 + 4 * a32;
+      // rows 16 s4 + 4 a32 .. +3 and 16 s4 + 8 + 4 a32 .. +3: groups 4 s4 + a32 and 4 s4 + 2 + a32
+      const int c0 = d * kBwdT + 4 * bwd_tgrp(4 * s4 + a32, d);
+      const int c1 = d * kBwdT + 4 * bwd_tgrp(4 * s4 + 2 + a32, d);
       const bf16x4 glo = *reinterpret_cast<const bf16x4*>(&L.g_t[buf][c0]);
-      const bf16x4 ghi = *reinterpret_cast<const bf16x4*>(&L.g_t[buf][c0 + 8]);
+      const bf16x4 ghi = *reinterpret_cast<const bf16x4*>(&L.g_t[buf][c1]);
       const bf16x4 qlo = *reinterpret_cast<const bf16x4*>(&L.q_t[buf][c0]);
-      const bf16x4 qhi = *reinterpret_cast<const bf16x4*>(&L.q_t[buf][c0 + 8]);
+      const bf16x4 qhi = *reinterpret_cast<const bf16x4*>(&L.q_t[buf][c1]);
       const bf16x8 gb = {glo[0], glo[1], glo[2], glo[3], ghi[0], ghi[1], ghi[2], ghi[3]};
       const bf16x8 qb = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
       dv_acc[dt] = mma32(pa[s4], gb, dv_acc[dt]);
