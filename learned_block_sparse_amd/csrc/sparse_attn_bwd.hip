@@ -219,12 +219,21 @@ __device__ __forceinline__ void bwd_quad_compute(const BwdLds& L, int buf, const
   for (int rh = 0; rh < 2; ++rh) {
     f32x16 s = {}, dp = {};
     const int arow = (32 * rh + col) * kBwdRow + 8 * a32;
+    // one wave per SIMD: the next k-step's operands are read from LDS while
+    // the current MFMAs run
+    bf16x8 qa = *reinterpret_cast<const bf16x8*>(&L.q_rm[buf][arow]);
+    bf16x8 ga = *reinterpret_cast<const bf16x8*>(&L.g_rm[buf][arow]);
 #pragma unroll
     for (int ks = 0; ks < kHeadDim / 16; ++ks) {
-      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&L.q_rm[buf][arow + 16 * ks]);
-      const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&L.g_rm[buf][arow + 16 * ks]);
+      bf16x8 qn = qa, gn = ga;
+      if (ks + 1 < kHeadDim / 16) {
+        qn = *reinterpret_cast<const bf16x8*>(&L.q_rm[buf][arow + 16 * (ks + 1)]);
+        gn = *reinterpret_cast<const bf16x8*>(&L.g_rm[buf][arow + 16 * (ks + 1)]);
+      }
       s = mma32(qa, kf[ks], s);
       dp = mma32(ga, vf[ks], dp);
+      qa = qn;
+      ga = gn;
     }
     // C layout: this lane's key, rows 32 rh + 8 (r / 4) + 4 a32 + r % 4; the
     // four rows of each r / 4 are consecutive, so their lse and delta are one
@@ -250,23 +259,27 @@ __device__ __forceinline__ void bwd_quad_compute(const BwdLds& L, int buf, const
   // k-step s4 covers rows 16 s4 .. +15; slot i of lane half a32 is row
   // 16 s4 + 4 a32 + i (i < 4) or 16 s4 + 8 + 4 a32 + i - 4, matching the
   // registers of pa / dsa above.
+  // rows 16 s4 + 4 a32 .. +3 and 16 s4 + 8 + 4 a32 .. +3 of dim d: row groups
+  // 4 s4 + a32 and 4 s4 + 2 + a32; operands of step i + 1 (i = 4 dt + s4) are
+  // read while step i's MFMAs run
+  auto opnd = [&](const bf16* t, int i) {
+    const int d = 32 * (i >> 2) + col, s4 = i & 3;
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(t + d * kBwdT + 4 * bwd_tgrp(4 * s4 + a32, d));
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(t + d * kBwdT + 4 * bwd_tgrp(4 * s4 + 2 + a32, d));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  bf16x8 gb = opnd(L.g_t[buf], 0), qb = opnd(L.q_t[buf], 0);
 #pragma unroll
-  for (int dt = 0; dt < kHeadDim / 32; ++dt) {
-    const int d = 32 * dt + col;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      // rows 16 s4 + 4 a32 .. +3 and 16 s4 + 8 + 4 a32 .. +3: groups 4 s4 + a32 and 4 s4 + 2 + a32
-      const int c0 = d * kBwdT + 4 * bwd_tgrp(4 * s4 + a32, d);
-      const int c1 = d * kBwdT + 4 * bwd_tgrp(4 * s4 + 2 + a32, d);
-      const bf16x4 glo = *reinterpret_cast<const bf16x4*>(&L.g_t[buf][c0]);
-      const bf16x4 ghi = *reinterpret_cast<const bf16x4*>(&L.g_t[buf][c1]);
-      const bf16x4 qlo = *reinterpret_cast<const bf16x4*>(&L.q_t[buf][c0]);
-      const bf16x4 qhi = *reinterpret_cast<const bf16x4*>(&L.q_t[buf][c1]);
-      const bf16x8 gb = {glo[0], glo[1], glo[2], glo[3], ghi[0], ghi[1], ghi[2], ghi[3]};
-      const bf16x8 qb = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
-      dv_acc[dt] = mma32(pa[s4], gb, dv_acc[dt]);
-      dk_acc[dt] = mma32(dsa[s4], qb, dk_acc[dt]);
+  for (int i = 0; i < 4 * (kHeadDim / 32); ++i) {
+    bf16x8 gn = gb, qn = qb;
+    if (i + 1 < 4 * (kHeadDim / 32)) {
+      gn = opnd(L.g_t[buf], i + 1);
+      qn = opnd(L.q_t[buf], i + 1);
     }
+    dv_acc[i >> 2] = mma32(pa[i & 3], gb, dv_acc[i >> 2]);
+    dk_acc[i >> 2] = mma32(dsa[i & 3], qb, dk_acc[i >> 2]);
+    gb = gn;
+    qb = qn;
   }
 }
 
