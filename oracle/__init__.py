@@ -19,6 +19,11 @@ record of MiniMax M3 (atlas.lewiswon.me), summary paragraph:
   selected blocks, causal inside the local block, natural-log LSE.
 * ``sparse_attn_bwd``: its gradients with respect to q, k and v (fp64),
   recomputed from the inputs.
+* ``block_lse``: the main branch's LSE over each selected block's attended
+  keys, per (row, head, selection slot).
+* ``index_kl``: the KL alignment loss of the index branch (the index scores of
+  the selected blocks against the group-averaged share of main attention in
+  each block) and its gradients with respect to q_idx and k_idx.
 
 Query row t of a sequence with ``q_len = M`` and ``kv_len = N`` sits at
 absolute position ``p = N - M + t``; blocks are aligned to position 0.
@@ -80,6 +85,14 @@ def _load():
         lib.oracle_sparse_attn_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64p, i64p, i32p,
                                                ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, ctypes.c_int, ctypes.c_double, vp, vp, vp]
+        lib.oracle_block_lse.restype = ctypes.c_int
+        lib.oracle_block_lse.argtypes = [vp, vp, ctypes.c_int, i64p, i64p, i32p, ctypes.c_int64, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                         vp]
+        lib.oracle_index_kl.restype = ctypes.c_int
+        lib.oracle_index_kl.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, i64p, i64p, i32p,
+                                        ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_double, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -244,6 +257,54 @@ def sparse_attn_bwd(q, k, v, dout, sel, kstart, pos, rows, block_size: int, topk
     if rc != 0:
         raise ValueError(f"oracle_sparse_attn_bwd failed ({rc})")
     return dq, dk, dv
+
+
+def block_lse(q, k, sel, kstart, pos, rows, block_size: int, topk: int, scale=None):
+    """Per-slot block LSEs [n, Hq, topk] (fp64) of the main branch."""
+    lib = _load()
+    qa, qt = _gather_rows(q, rows)
+    ka, kt = _host_array(k)
+    if qt != kt:
+        raise TypeError("q and k must share a dtype")
+    n, Hq, D = qa.shape
+    Hkv = ka.shape[1]
+    sel = np.ascontiguousarray(np.asarray(sel), dtype=np.int32)
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    out = np.empty((n, Hq, topk), dtype=np.float64)
+    rc = lib.oracle_block_lse(_ptr(qa), _ptr(ka), qt, _ptr(np.ascontiguousarray(kstart, dtype=np.int64)),
+                              _ptr(np.ascontiguousarray(pos, dtype=np.int64)), _ptr(sel), n, Hq, Hkv, D,
+                              block_size, topk, float(scale), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_block_lse failed ({rc})")
+    return out
+
+
+def index_kl(q_idx, k_idx, q, k, sel, kstart, pos, rows, block_size: int, topk: int, scale=None):
+    """KL alignment loss of the index branch: (loss [n, G], dq_idx [n, G, d_idx],
+    dk_idx [Tk, d_idx]), fp64; dk_idx holds these rows' contributions."""
+    lib = _load()
+    qia, qit = _gather_rows(q_idx, rows)
+    kia, kit = _host_array(k_idx)
+    qa, qt = _gather_rows(q, rows)
+    ka, kt = _host_array(k)
+    if qit != kit or qt != kt:
+        raise TypeError("q_idx / k_idx and q / k must share a dtype pairwise")
+    n, G, DI = qia.shape
+    Hq, D = qa.shape[1], qa.shape[2]
+    sel = np.ascontiguousarray(np.asarray(sel), dtype=np.int32)
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    loss = np.empty((n, G), dtype=np.float64)
+    dq = np.empty((n, G, DI), dtype=np.float64)
+    dk = np.zeros(kia.shape, dtype=np.float64)
+    rc = lib.oracle_index_kl(_ptr(qia), _ptr(kia), qit, _ptr(qa), _ptr(ka), qt,
+                             _ptr(np.ascontiguousarray(kstart, dtype=np.int64)),
+                             _ptr(np.ascontiguousarray(pos, dtype=np.int64)), _ptr(sel), n, G, DI, Hq, D,
+                             block_size, topk, float(scale), _ptr(loss), _ptr(dq), _ptr(dk))
+    if rc != 0:
+        raise ValueError(f"oracle_index_kl failed ({rc})")
+    return loss, dq, dk
 
 
 def prefill(q_idx, k_idx, q, k, v, cu_seqlens_q, cu_seqlens_k, block_size: int, topk: int,

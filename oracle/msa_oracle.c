@@ -334,3 +334,187 @@ int oracle_sparse_attn_bwd(const void* q, const void* k, const void* v, const vo
   }
   return bad;
 }
+
+/* The distinct attended blocks of one selection row (Sel taken as a set):
+ * slot i is attended when its id is >= 0, at or before the local block and
+ * not a repeat of an earlier slot.  Returns a bit mask of those slots. */
+static unsigned valid_slots(const int32_t* row_sel, int topk, int64_t local) {
+  unsigned mask = 0;
+  for (int i = 0; i < topk; ++i) {
+    const int32_t c = row_sel[i];
+    int ok = c >= 0 && c <= local;
+    for (int j = 0; j < i && ok; ++j) ok = row_sel[j] != c;
+    if (ok) mask |= 1u << i;
+  }
+  return mask;
+}
+
+/* Per-slot block LSE of the main branch: for row r, head h and selection slot
+ * i naming block c, ln sum over the attended keys j of block c (j <= p) of
+ * exp(z_j), z_j = scale * q . k_j in fp64; -inf for a slot that adds no
+ * block.  exp(blse - lse) is the share of the head's attention in the block. */
+int oracle_block_lse(const void* q, const void* k, int dtype, const int64_t* kstart, const int64_t* pos,
+                     const int32_t* sel, int64_t n, int Hq, int Hkv, int D, int Bk, int topk, double scale,
+                     double* blse) {
+  if (!q || !k || !kstart || !pos || !sel || !blse) return 1;
+  if (n < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Bk <= 0 || topk <= 0 || topk > 32) return 1;
+  if (Hq % Hkv != 0) return 1;
+  if (dtype != 0 && dtype != 1 && dtype != 2) return 1;
+  const int r_heads = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n; ++r) {
+    const int64_t p = pos[r];
+    for (int h = 0; h < Hq; ++h) {
+      const int g = h / r_heads;
+      const int32_t* rs = sel + (r * Hkv + g) * (int64_t)topk;
+      const unsigned mask = p >= 0 ? valid_slots(rs, topk, floor_div(p, Bk)) : 0u;
+      const int64_t qoff = (r * Hq + h) * (int64_t)D;
+      for (int i = 0; i < topk; ++i) {
+        double* out = blse + (r * Hq + h) * (int64_t)topk + i;
+        if (!((mask >> i) & 1u)) { *out = -INFINITY; continue; }
+        const int64_t j0 = (int64_t)rs[i] * Bk;
+        const int64_t j1 = j0 + Bk - 1 < p ? j0 + Bk - 1 : p;
+        double m = -INFINITY;
+        for (int64_t j = j0; j <= j1; ++j) {
+          const int64_t koff = ((kstart[r] + j) * Hkv + g) * (int64_t)D;
+          double dot = 0.0;
+          for (int d = 0; d < D; ++d)
+            dot += (double)load_elem(q, dtype, qoff + d) * (double)load_elem(k, dtype, koff + d);
+          if (scale * dot > m) m = scale * dot;
+        }
+        double l = 0.0;
+        for (int64_t j = j0; j <= j1; ++j) {
+          const int64_t koff = ((kstart[r] + j) * Hkv + g) * (int64_t)D;
+          double dot = 0.0;
+          for (int d = 0; d < D; ++d)
+            dot += (double)load_elem(q, dtype, qoff + d) * (double)load_elem(k, dtype, koff + d);
+          l += exp(scale * dot - m);
+        }
+        *out = m + log(l);
+      }
+    }
+  }
+  return 0;
+}
+
+/* KL alignment of the index branch ([P4] "Two design choices": an auxiliary
+ * KL loss aligns the index branch's block scores with the main attention's
+ * distribution over blocks; [P5] summary: against the group-averaged main
+ * distribution, with a stop-gradient so only the index projections learn).
+ * For row r and group g, over the attended slots i of its selection:
+ *   A_i = (1/r_heads) sum_{h in g} exp(blse[h][i] - lse[h])  main branch's
+ *         share of attention in block c_i, averaged over the group's heads
+ *         (blse, lse: oracle_block_lse and the logsumexp over the slots)
+ *   S_i = max over the attended keys j of block c_i of q_idx . k_idx[j]
+ *         (fp32, sequential over d, as the index branch scores; the lowest j
+ *         among equal maxima is the argmax j*_i)
+ *   I   = softmax over the attended slots of S (fp64)
+ *   loss[r][g] = sum_i A_i (ln A_i - ln I_i)   (terms with A_i = 0 are 0)
+ * A is a constant target (no gradient reaches q, k); the gradients of the
+ * sum of loss[r][g] over all rows and groups with respect to S are
+ *   dS_i = I_i (sum_k A_k) - A_i,
+ * and through the max: dq_idx[r][g] = sum_i dS_i k_idx[j*_i] (written),
+ * dk_idx[j*_i] += dS_i q_idx[r][g] (accumulated; the caller zeroes it). */
+int oracle_index_kl(const void* q_idx, const void* k_idx, int idx_dtype, const void* q, const void* k,
+                    int dtype, const int64_t* kstart, const int64_t* pos, const int32_t* sel, int64_t n, int G,
+                    int DI, int Hq, int D, int Bk, int topk, double scale, double* loss, double* dq_idx,
+                    double* dk_idx) {
+  if (!q_idx || !k_idx || !q || !k || !kstart || !pos || !sel || !loss || !dq_idx || !dk_idx) return 1;
+  if (n < 0 || G <= 0 || DI <= 0 || Hq <= 0 || D <= 0 || Bk <= 0 || topk <= 0 || topk > 32) return 1;
+  if (Hq % G != 0) return 1;
+  if (idx_dtype != 0 && idx_dtype != 1 && idx_dtype != 2) return 1;
+  const int r_heads = Hq / G;
+  double* blse = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * (size_t)Hq * (size_t)topk);
+  if (!blse) return 1;
+  if (oracle_block_lse(q, k, dtype, kstart, pos, sel, n, Hq, G, D, Bk, topk, scale, blse) != 0) {
+    free(blse);
+    return 1;
+  }
+  int64_t nkeys = 0;
+  for (int64_t r = 0; r < n; ++r)
+    if (pos[r] >= 0 && kstart[r] + pos[r] + 1 > nkeys) nkeys = kstart[r] + pos[r] + 1;
+  const size_t kv_elems = (size_t)nkeys * (size_t)DI;
+
+  int bad = 0;
+#pragma omp parallel reduction(| : bad)
+  {
+    double* my_dk = (double*)calloc(kv_elems ? kv_elems : 1, sizeof(double));
+    if (!my_dk) bad = 1;
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+      if (!my_dk) continue;
+      const int64_t p = pos[r];
+      for (int g = 0; g < G; ++g) {
+        double* dq = dq_idx + (r * G + g) * (int64_t)DI;
+        for (int d = 0; d < DI; ++d) dq[d] = 0.0;
+        loss[r * G + g] = 0.0;
+        const int32_t* rs = sel + (r * G + g) * (int64_t)topk;
+        const unsigned mask = p >= 0 ? valid_slots(rs, topk, floor_div(p, Bk)) : 0u;
+        if (!mask) continue;
+        double A[32], S[32], I[32];
+        int64_t jstar[32];
+        const int64_t qoff = (r * G + g) * (int64_t)DI;
+        for (int i = 0; i < topk; ++i) {
+          if (!((mask >> i) & 1u)) continue;
+          /* main branch share of block i, averaged over the group's heads */
+          double a = 0.0;
+          for (int hh = 0; hh < r_heads; ++hh) {
+            const int h = g * r_heads + hh;
+            const double* bl = blse + (r * Hq + h) * (int64_t)topk;
+            double m = -INFINITY, l = 0.0;
+            for (int k2 = 0; k2 < topk; ++k2)
+              if (bl[k2] > m) m = bl[k2];
+            for (int k2 = 0; k2 < topk; ++k2)
+              if (bl[k2] > -INFINITY) l += exp(bl[k2] - m);
+            a += exp(bl[i] - (m + log(l)));
+          }
+          A[i] = a / r_heads;
+          /* index score and argmax over the block's attended keys */
+          const int64_t j0 = (int64_t)rs[i] * Bk;
+          const int64_t j1 = j0 + Bk - 1 < p ? j0 + Bk - 1 : p;
+          float best = -INFINITY;
+          int64_t bj = j0;
+          for (int64_t j = j0; j <= j1; ++j) {
+            float s = 0.0f;
+            const int64_t koff = (kstart[r] + j) * (int64_t)DI;
+            for (int d = 0; d < DI; ++d)
+              s += load_elem(q_idx, idx_dtype, qoff + d) * load_elem(k_idx, idx_dtype, koff + d);
+            if (s > best) { best = s; bj = j; }
+          }
+          S[i] = (double)best;
+          jstar[i] = bj;
+        }
+        double m = -INFINITY, z = 0.0, asum = 0.0;
+        for (int i = 0; i < topk; ++i)
+          if ((mask >> i) & 1u && S[i] > m) m = S[i];
+        for (int i = 0; i < topk; ++i)
+          if ((mask >> i) & 1u) z += exp(S[i] - m);
+        double ls = 0.0;
+        for (int i = 0; i < topk; ++i) {
+          if (!((mask >> i) & 1u)) continue;
+          I[i] = exp(S[i] - m) / z;
+          asum += A[i];
+          if (A[i] > 0.0) ls += A[i] * (log(A[i]) - (S[i] - m - log(z)));
+        }
+        loss[r * G + g] = ls;
+        for (int i = 0; i < topk; ++i) {
+          if (!((mask >> i) & 1u)) continue;
+          const double ds = I[i] * asum - A[i];
+          const int64_t koff = (kstart[r] + jstar[i]) * (int64_t)DI;
+          for (int d = 0; d < DI; ++d) {
+            dq[d] += ds * (double)load_elem(k_idx, idx_dtype, koff + d);
+            my_dk[koff + d] += ds * (double)load_elem(q_idx, idx_dtype, qoff + d);
+          }
+        }
+      }
+    }
+#pragma omp critical
+    {
+      if (my_dk)
+        for (size_t i = 0; i < kv_elems; ++i) dk_idx[i] += my_dk[i];
+    }
+    free(my_dk);
+  }
+  free(blse);
+  return bad;
+}

@@ -86,6 +86,26 @@ int oracle_sparse_attn_bwd(const void* q, const void* k, const void* v, const vo
                            int64_t n, int Hq, int Hkv, int D, int Bk, int topk, double scale,
                            double* dq, double* dk, double* dv);
 
+/* Per-slot block LSE of the main branch for n query rows:
+ *   blse : [n][Hq][topk] fp64 out, ln sum over the attended keys of the
+ *          slot's block of exp(scale * q . k); -inf for a slot that adds no
+ *          block (-1, past the local block, a repeat).  topk <= 32. */
+int oracle_block_lse(const void* q, const void* k, int dtype, const int64_t* kstart, const int64_t* pos,
+                     const int32_t* sel, int64_t n, int Hq, int Hkv, int D, int Bk, int topk, double scale,
+                     double* blse);
+
+/* KL alignment loss of the index branch and its gradients for n query rows
+ * (the definition is written out in msa_oracle.c):
+ *   loss   : [n][G] fp64 out, KL(A || softmax(S)) per (row, group)
+ *   dq_idx : [n][G][DI] fp64 out (written)
+ *   dk_idx : [*][DI] fp64, ACCUMULATED into (the caller zeroes it)
+ * q_idx / k_idx are read as idx_dtype, q / k (main branch, which defines the
+ * target A) as dtype.  G = number of KV heads. */
+int oracle_index_kl(const void* q_idx, const void* k_idx, int idx_dtype, const void* q, const void* k,
+                    int dtype, const int64_t* kstart, const int64_t* pos, const int32_t* sel, int64_t n, int G,
+                    int DI, int Hq, int D, int Bk, int topk, double scale, double* loss, double* dq_idx,
+                    double* dk_idx);
+
 /* Decode n E4M3 bit patterns to fp32 (exact), for checking the decoder. */
 void oracle_decode_e4m3(const uint8_t* in, float* out, int64_t n);
 

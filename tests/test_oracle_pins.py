@@ -449,3 +449,113 @@ def test_backward_matches_finite_differences(oracle_lib):
             args_p[name], args_m[name] = plus, minus
             fd = (loss(args_p["q"], args_p["k"], args_p["v"]) - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * eps)
             assert abs(fd - grad[c]) <= 1e-5 * max(1.0, abs(grad[c])), (name, c, fd, grad[c])
+
+
+def _kl_case(rng, kv, ql, Hq, Hkv, D, DI, bk, topk, zero_k=False, zero_qidx=False):
+    cu_k, cu_q = _cu(kv), _cu(ql)
+    q = rng.standard_normal((cu_q[-1], Hq, D)).astype(np.float32)
+    k = np.zeros((cu_k[-1], Hkv, D), np.float32) if zero_k else rng.standard_normal((cu_k[-1], Hkv, D)).astype(np.float32)
+    qi = np.zeros((cu_q[-1], Hkv, DI), np.float32) if zero_qidx else rng.standard_normal((cu_q[-1], Hkv, DI)).astype(np.float32)
+    ki = rng.standard_normal((cu_k[-1], DI)).astype(np.float32)
+    return cu_k, cu_q, q, k, qi, ki
+
+
+def _attended(sel_row, p, bk):
+    """Distinct attended blocks of a selection row, in slot order (Sel as a set)."""
+    seen, out = set(), []
+    for i, c in enumerate(sel_row):
+        if c >= 0 and c <= p // bk and c not in seen:
+            seen.add(c)
+            out.append((i, int(c)))
+    return out
+
+
+def test_block_lse_closed_form_and_consistency(oracle_lib):
+    """K == 0: every logit is 0, so a block's LSE is ln(number of its attended
+    keys) (128 for a full block, p - 128 l + 1 for the local one).  With random
+    K the logsumexp over a row's slots is the attention's own LSE."""
+    rng = np.random.default_rng(31)
+    kv, ql, Hq, Hkv, D, bk, topk = [700, 260], [300, 260], 4, 2, 16, 128, 4
+    cu_k, cu_q, q, k, _, _ = _kl_case(rng, kv, ql, Hq, Hkv, D, 8, bk, topk, zero_k=True)
+    rows, kstart, pos = oracle_lib.rows_prefill(cu_q, cu_k)
+    sel = rng.integers(-1, 6, size=(len(rows), Hkv, topk)).astype(np.int32)
+    sel[:, :, 0] = (pos // bk)[:, None]
+    bl = oracle_lib.block_lse(q, k, sel, kstart, pos, rows, bk, topk)
+    for r in range(len(rows)):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            att = dict(_attended(sel[r, g], pos[r], bk))
+            for i in range(topk):
+                if i in att:
+                    c = att[i]
+                    nk = min(bk, pos[r] - c * bk + 1)
+                    assert bl[r, h, i] == pytest.approx(math.log(nk), abs=1e-12)
+                else:
+                    assert np.isneginf(bl[r, h, i])
+    k = rng.standard_normal(k.shape).astype(np.float32)
+    bl = oracle_lib.block_lse(q, k, sel, kstart, pos, rows, bk, topk)
+    _, lse = oracle_lib.sparse_attn(q, k, k, sel, kstart, pos, rows, bk, topk)
+    m = bl.max(axis=-1, keepdims=True)
+    np.testing.assert_allclose(m[..., 0] + np.log(np.exp(bl - m).sum(-1)), lse, rtol=0, atol=1e-12)
+
+
+def test_index_kl_closed_form(oracle_lib):
+    """K == 0 makes the main attention uniform over the attended keys, so the
+    target share of block c is n_c / |J|; q_idx == 0 makes every index score 0,
+    so the index distribution is uniform over the m attended blocks and every
+    argmax is the block's first key.  Then loss = sum_c (n_c/|J|) ln(m n_c/|J|),
+    dS_c = 1/m - n_c/|J|, dq_idx = sum_c dS_c k_idx[first key of c] and
+    dk_idx[first key of c] = sum over rows of dS_c q_idx = 0."""
+    rng = np.random.default_rng(32)
+    kv, ql, Hq, Hkv, D, DI, bk, topk = [600], [600], 4, 2, 16, 8, 128, 4
+    cu_k, cu_q, q, k, qi, ki = _kl_case(rng, kv, ql, Hq, Hkv, D, DI, bk, topk, zero_k=True, zero_qidx=True)
+    rows, kstart, pos = oracle_lib.rows_prefill(cu_q, cu_k)
+    sel = rng.integers(-1, 5, size=(len(rows), Hkv, topk)).astype(np.int32)
+    sel[:, :, 1] = (pos // bk)[:, None]
+    loss, dq, dk = oracle_lib.index_kl(qi, ki, q, k, sel, kstart, pos, rows, bk, topk)
+    for r in range(len(rows)):
+        for g in range(Hkv):
+            att = _attended(sel[r, g], pos[r], bk)
+            ns = np.array([min(bk, pos[r] - c * bk + 1) for _, c in att], dtype=np.float64)
+            A, m = ns / ns.sum(), len(att)
+            assert loss[r, g] == pytest.approx(float((A * np.log(m * A)).sum()), abs=1e-12)
+            want = sum((1.0 / m - A[j]) * ki[c * bk].astype(np.float64) for j, (_, c) in enumerate(att))
+            np.testing.assert_allclose(dq[r, g], want, rtol=0, atol=1e-12)
+    assert np.all(dk == 0)
+    assert np.all(loss >= -1e-12)
+
+
+def test_index_kl_matches_finite_differences(oracle_lib):
+    """Central differences of the summed loss through the oracle's own loss,
+    at coordinates of q_idx and at the argmax keys of k_idx (random fp32 data:
+    the maxima are unique, so the max is differentiable there)."""
+    rng = np.random.default_rng(33)
+    kv, ql, Hq, Hkv, D, DI, bk, topk = [300], [120], 4, 2, 8, 8, 32, 4
+    cu_k, cu_q, q, k, qi, ki = _kl_case(rng, kv, ql, Hq, Hkv, D, DI, bk, topk)
+    rows, kstart, pos = oracle_lib.rows_prefill(cu_q, cu_k)
+    sel = rng.integers(0, 9, size=(len(rows), Hkv, topk)).astype(np.int32)
+    sel[:, :, 0] = (pos // bk)[:, None]
+    loss, dq, dk = oracle_lib.index_kl(qi, ki, q, k, sel, kstart, pos, rows, bk, topk)
+    assert np.all(loss >= -1e-12)
+
+    def total(qq, kk):
+        return float(oracle_lib.index_kl(qq, kk, q, k, sel, kstart, pos, rows, bk, topk)[0].sum())
+
+    # the index scores are fp32 (as the index branch computes them), so the
+    # differences carry fp32 rounding of S: 1e-3 relative still fails any
+    # wrong sign, factor or term
+    eps = 2.0 ** -10
+    for c in [(0, 0, 3), (57, 1, 0), (119, 0, 7)]:
+        plus, minus = qi.copy(), qi.copy()
+        plus[c] += eps
+        minus[c] -= eps
+        fd = (total(plus, ki) - total(minus, ki)) / (2 * eps)
+        assert abs(fd - dq[c]) <= 1e-3 * max(1.0, abs(dq[c])), (c, fd, dq[c])
+    rows_k = np.argsort(-np.abs(dk).sum(axis=1))[:3]
+    for j in rows_k:
+        for d in (0, DI - 1):
+            plus, minus = ki.copy(), ki.copy()
+            plus[j, d] += eps
+            minus[j, d] -= eps
+            fd = (total(qi, plus) - total(qi, minus)) / (2 * eps)
+            assert abs(fd - dk[j, d]) <= 1e-3 * max(1.0, abs(dk[j, d])), (j, d, fd, dk[j, d])
