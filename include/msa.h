@@ -213,22 +213,30 @@ msa_status_t msa_sparse_attn_decode(const void* q, const void* k_cache, const vo
  * K scale can be folded into softmax_scale, a V scale applied to out.
  * Other pairs return MSA_ERR_UNSUPPORTED; the workspace size is that of the
  * plain call.
+ *
+ * block_lse (nullable), [Tq, num_heads, topk] fp32 out: for each selection
+ * slot, ln sum over the keys of that slot's block that the row attends of
+ * exp(z_j) (z as above), so exp(block_lse - lse) is the share of the head's
+ * attention that falls in the block; -inf for a slot that adds no block (-1,
+ * a repeat, a block past the local one) and for rows with p < 0.  These are
+ * the main branch's block masses the index branch's alignment loss compares
+ * against (msa_index_kl_backward).
  * ---------------------------------------------------------------------- */
 msa_status_t msa_sparse_attn_prefill_ex(const void* q, const void* k, const void* v, msa_dtype_t dtype,
                                         msa_dtype_t kv_dtype, const int32_t* block_idx,
                                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
                                         int max_q_len, int max_kv_len, int num_heads, int num_kv_heads,
                                         int head_dim, int block_size, int topk, float softmax_scale,
-                                        int num_splits, void* out, float* lse, void* workspace,
-                                        size_t workspace_bytes, hipStream_t stream);
+                                        int num_splits, void* out, float* lse, float* block_lse,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 msa_status_t msa_sparse_attn_decode_ex(const void* q, const void* k_cache, const void* v_cache,
                                        msa_dtype_t dtype, msa_dtype_t kv_dtype, const int32_t* block_idx,
                                        const int64_t* cache_offsets, const int32_t* ctx_lens, int batch,
                                        int max_ctx, int num_heads, int num_kv_heads, int head_dim,
                                        int block_size, int topk, float softmax_scale, int num_splits,
-                                       void* out, float* lse, void* workspace, size_t workspace_bytes,
-                                       hipStream_t stream);
+                                       void* out, float* lse, float* block_lse, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Main branch, backward (prefill layout).
@@ -270,6 +278,46 @@ msa_status_t msa_sparse_attn_backward(const void* q, const void* k, const void* 
                                       int num_heads, int num_kv_heads, int head_dim, int block_size, int topk,
                                       float softmax_scale, float* dq, float* dk, float* dv, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Index branch, KL alignment loss and its gradients.
+ *
+ * "MiniMax Sparse Attention: let each query pick its own blocks", section
+ * "Two design choices": an auxiliary KL loss aligns the index branch's block
+ * scores with the main attention's distribution over blocks, behind a
+ * stop-gradient so that only the index projections learn; the atlas record
+ * of MiniMax M3 (summary) takes the group-averaged main-branch distribution
+ * as the target.  For query row t and group g, over the attended slots i of
+ * its selection (Sel read as a set) with c_i the slot's block:
+ *   A_i = mean over the group's heads h of exp(block_lse[t, h, i] - lse[t, h])
+ *   S_i = max over the keys j <= p of block c_i of q_idx[t, g] . k_idx[j]
+ *         (raw dot product in fp32; j*_i = the lowest such key reaching it)
+ *   loss[t, g] = sum_i A_i (ln A_i - ln softmax_i(S))    (0 for rows p < 0)
+ * A is a constant target: no gradient reaches the main branch.  With respect
+ * to the sum of loss over all rows and groups, dS_i = softmax_i(S) sum_k A_k
+ * - A_i, passed through the max to the argmax key:
+ *   dq_idx[t, g] = sum_i dS_i k_idx[j*_i],  dk_idx[j*_i] += dS_i q_idx[t, g].
+ *
+ *   q_idx, k_idx, dtype     as for msa_index_topk (fp32 or bf16)
+ *   block_idx               the selection both calls used
+ *   lse, block_lse          [Tq, num_heads] and [Tq, num_heads, topk] fp32 from
+ *                           msa_sparse_attn_prefill_ex on the same selection
+ *   loss                    [Tq, num_groups] fp32 out
+ *   dq_idx                  [Tq, num_groups, index_dim] fp32 out
+ *   dk_idx                  [Tk, index_dim] fp32 out, overwritten (0 for keys
+ *                           that are no argmax)
+ *   workspace               at least msa_index_kl_workspace_size() bytes
+ * Results are bitwise reproducible (each block's edges are summed in a fixed
+ * order).  Other element types return MSA_ERR_UNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+size_t msa_index_kl_workspace_size(int batch, int max_q_len, int max_kv_len, int num_groups, int topk);
+
+msa_status_t msa_index_kl_backward(const void* q_idx, const void* k_idx, msa_dtype_t dtype,
+                                   const int32_t* block_idx, const float* lse, const float* block_lse,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                                   int max_q_len, int max_kv_len, int num_heads, int num_groups, int index_dim,
+                                   int block_size, int topk, float* loss, float* dq_idx, float* dk_idx,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -199,8 +199,8 @@ msa_status_t msa_sparse_attn_prefill_ex(const void* q, const void* k, const void
                                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
                                         int max_q_len, int max_kv_len, int num_heads, int num_kv_heads,
                                         int head_dim, int block_size, int topk, float softmax_scale,
-                                        int num_splits, void* out, float* lse, void* workspace,
-                                        size_t workspace_bytes, hipStream_t stream) {
+                                        int num_splits, void* out, float* lse, float* block_lse,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   msa_status_t st = check_attn(q, k, v, dtype, kv_dtype, block_idx, out, batch, num_heads, num_kv_heads,
                                head_dim, block_size, topk, num_splits);
   if (st != MSA_OK) return st;
@@ -208,7 +208,7 @@ msa_status_t msa_sparse_attn_prefill_ex(const void* q, const void* k, const void
   const AttnPlan pl = plan_attn(batch, max_q_len, max_kv_len, num_heads, num_kv_heads, head_dim, topk, num_splits);
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes)) return MSA_ERR_WORKSPACE;
   AttnArgs a{q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, nullptr, nullptr, batch, num_heads, num_kv_heads,
-             topk, resolve_scale(softmax_scale, head_dim), out, lse};
+             topk, resolve_scale(softmax_scale, head_dim), out, lse, block_lse};
   return hip_status(launch_sparse_attn(pl, (int)dtype, (int)kv_dtype, a, workspace, stream));
 }
 
@@ -221,7 +221,8 @@ msa_status_t msa_sparse_attn_prefill(const void* q, const void* k, const void* v
                                      size_t workspace_bytes, hipStream_t stream) {
   return msa_sparse_attn_prefill_ex(q, k, v, dtype, dtype, block_idx, cu_seqlens_q, cu_seqlens_k, batch,
                                     max_q_len, max_kv_len, num_heads, num_kv_heads, head_dim, block_size, topk,
-                                    softmax_scale, num_splits, out, lse, workspace, workspace_bytes, stream);
+                                    softmax_scale, num_splits, out, lse, nullptr, workspace, workspace_bytes,
+                                    stream);
 }
 
 msa_status_t msa_sparse_attn_decode_ex(const void* q, const void* k_cache, const void* v_cache,
@@ -229,8 +230,8 @@ msa_status_t msa_sparse_attn_decode_ex(const void* q, const void* k_cache, const
                                        const int64_t* cache_offsets, const int32_t* ctx_lens, int batch,
                                        int max_ctx, int num_heads, int num_kv_heads, int head_dim,
                                        int block_size, int topk, float softmax_scale, int num_splits,
-                                       void* out, float* lse, void* workspace, size_t workspace_bytes,
-                                       hipStream_t stream) {
+                                       void* out, float* lse, float* block_lse, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
   msa_status_t st = check_attn(q, k_cache, v_cache, dtype, kv_dtype, block_idx, out, batch, num_heads,
                                num_kv_heads, head_dim, block_size, topk, num_splits);
   if (st != MSA_OK) return st;
@@ -238,7 +239,7 @@ msa_status_t msa_sparse_attn_decode_ex(const void* q, const void* k_cache, const
   const AttnPlan pl = plan_attn(batch, 1, max_ctx, num_heads, num_kv_heads, head_dim, topk, num_splits);
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes)) return MSA_ERR_WORKSPACE;
   AttnArgs a{q, k_cache, v_cache, block_idx, nullptr, nullptr, cache_offsets, ctx_lens, batch, num_heads,
-             num_kv_heads, topk, resolve_scale(softmax_scale, head_dim), out, lse};
+             num_kv_heads, topk, resolve_scale(softmax_scale, head_dim), out, lse, block_lse};
   return hip_status(launch_sparse_attn(pl, (int)dtype, (int)kv_dtype, a, workspace, stream));
 }
 
@@ -251,7 +252,7 @@ msa_status_t msa_sparse_attn_decode(const void* q, const void* k_cache, const vo
                                     size_t workspace_bytes, hipStream_t stream) {
   return msa_sparse_attn_decode_ex(q, k_cache, v_cache, dtype, dtype, block_idx, cache_offsets, ctx_lens, batch,
                                    max_ctx, num_heads, num_kv_heads, head_dim, block_size, topk, softmax_scale,
-                                   num_splits, out, lse, workspace, workspace_bytes, stream);
+                                   num_splits, out, lse, nullptr, workspace, workspace_bytes, stream);
 }
 
 size_t msa_sparse_attn_backward_workspace_size(int batch, int max_q_len, int max_kv_len, int num_heads,
@@ -288,6 +289,41 @@ msa_status_t msa_sparse_attn_backward(const void* q, const void* k, const void* 
   a.dk = dk;
   a.dv = dv;
   return hip_status(launch_sparse_attn_bwd(pl, a, workspace, stream));
+}
+
+size_t msa_index_kl_workspace_size(int batch, int max_q_len, int max_kv_len, int num_groups, int topk) {
+  if (batch <= 0 || max_q_len <= 0 || max_kv_len <= 0 || num_groups <= 0 || topk <= 0) return 0;
+  return plan_kl(batch, max_q_len, max_kv_len, num_groups, topk).workspace_bytes;
+}
+
+msa_status_t msa_index_kl_backward(const void* q_idx, const void* k_idx, msa_dtype_t dtype,
+                                   const int32_t* block_idx, const float* lse, const float* block_lse,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                                   int max_q_len, int max_kv_len, int num_heads, int num_groups, int index_dim,
+                                   int block_size, int topk, float* loss, float* dq_idx, float* dk_idx,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q_idx || !k_idx || !block_idx || !lse || !block_lse || !cu_seqlens_q || !cu_seqlens_k || !loss ||
+      !dq_idx || !dk_idx)
+    return MSA_ERR_INVALID_ARG;
+  if (batch <= 0 || max_q_len <= 0 || max_kv_len <= 0 || num_heads <= 0 || num_groups <= 0 || index_dim <= 0 ||
+      block_size <= 0 || topk <= 0 || !dtype_ok(dtype) || num_heads % num_groups != 0)
+    return MSA_ERR_INVALID_ARG;
+  if (block_size != kBlock || (index_dim != 64 && index_dim != 128) || topk > 16 || num_groups > 16 ||
+      num_heads / num_groups > 16 || (dtype != MSA_F32 && dtype != MSA_BF16))
+    return MSA_ERR_UNSUPPORTED;
+  const KlPlan pl = plan_kl(batch, max_q_len, max_kv_len, num_groups, topk);
+  if (!workspace || workspace_bytes < pl.workspace_bytes) return MSA_ERR_WORKSPACE;
+  KlLaunch x;
+  x.attn = AttnArgs{nullptr, nullptr, nullptr, block_idx, cu_seqlens_q, cu_seqlens_k, nullptr, nullptr, batch,
+                    num_heads, num_groups, topk, 0.f, nullptr, nullptr};
+  x.q_idx = q_idx;
+  x.k_idx = k_idx;
+  x.lse = lse;
+  x.block_lse = block_lse;
+  x.loss = loss;
+  x.dq_idx = dq_idx;
+  x.dk_idx = dk_idx;
+  return hip_status(launch_index_kl(pl, (int)dtype, index_dim, x, workspace, stream));
 }
 
 }  // extern "C"

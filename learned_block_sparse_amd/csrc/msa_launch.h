@@ -65,6 +65,7 @@ struct AttnArgs {
   float scale;
   void* out;
   float* lse;
+  float* block_lse = nullptr;  // [rows, Hq, topk]: LSE of each selection slot's block, or null
 };
 
 // dtype: element type of q and out (0 fp32, 1 bf16); kv_dtype: of K and V
@@ -109,5 +110,28 @@ struct BwdArgs {
   float* dv;                  // [Tk, Hkv, D]
 };
 hipError_t launch_sparse_attn_bwd(const BwdPlan& pl, const BwdArgs& a, void* ws, hipStream_t st);
+
+// KL alignment loss of the index branch.
+struct KlPlan {
+  int nb_max = 0;
+  int nbuckets = 0;
+  int64_t rows_bound = 0;
+  int64_t window = 0;        // query rows per edge-list window
+  size_t counts_off = 0, offsets_off = 0, chunks_off = 0, cursor_off = 0, edges_off = 0;
+  size_t s_off = 0, j_off = 0, ds_off = 0;  // per selection slot of a window: score, argmax, dS
+  size_t workspace_bytes = 0;
+};
+KlPlan plan_kl(int batch, int max_q_len, int max_kv_len, int G, int topk);
+struct KlLaunch {
+  AttnArgs attn;              // block_idx, cu_q, cu_k, batch, Hq, Hkv (= G), topk
+  const void* q_idx;          // [Tq, G, DI]
+  const void* k_idx;          // [Tk, DI]
+  const float* lse;           // [Tq, Hq] from the attention call
+  const float* block_lse;     // [Tq, Hq, topk] from the attention call
+  float* loss;                // [Tq, G]
+  float* dq_idx;              // [Tq, G, DI]
+  float* dk_idx;              // [Tk, DI]
+};
+hipError_t launch_index_kl(const KlPlan& pl, int dtype, int DI, const KlLaunch& x, void* ws, hipStream_t st);
 
 }  // namespace msa

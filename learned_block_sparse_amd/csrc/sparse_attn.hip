@@ -47,6 +47,7 @@ struct AttnKernelArgs {
   float scale_log2;  // softmax scale * log2(e)
   void* out;
   float* lse;
+  float* block_lse;  // [rows, Hq, topk] or null
   float* part_o;
   float* part_lse;
 };
@@ -150,11 +151,15 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs a
   float m_run = -__builtin_inff();
   float l_run = 0.f;
 
+  const int i_lo = s * args.bps;
+  const int i_hi = min(i_lo + args.bps, args.topk);
+  // per-slot block LSEs: -inf unless the slot's block is attended (set below)
+  float* blse = (args.block_lse && head_ok && a == 0) ? args.block_lse + (t * args.Hq + hq) * args.topk : nullptr;
+  if (blse)
+    for (int i = i_lo; i < i_hi; ++i) blse[i] = -__builtin_inff();
   if (p >= 0) {
     const int64_t local = p / kBlock;
     const int32_t* sel = args.block_idx + (t * G + g) * args.topk;
-    const int i_lo = s * args.bps;
-    const int i_hi = min(i_lo + args.bps, args.topk);
     const int64_t row_stride = (int64_t)G * kHeadDim;   // elements between tokens
     const TKV* kseq = kg + kb0 * row_stride + g * kHeadDim;
     const TKV* vseq = vg + kb0 * row_stride + g * kHeadDim;
@@ -213,14 +218,22 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs a
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < kHeadDim / 16; ++dt) o[dt] *= alpha;
+      float l_blk = 0.f;
 #pragma unroll
       for (int kt = 0; kt < kBlock / 16; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float e = __builtin_amdgcn_exp2f(st[kt][r] - m_new);
           st[kt][r] = e;
-          l_run += e;
+          l_blk += e;
         }
+      l_run += l_blk;
+      if (args.block_lse) {
+        // this block alone: ln sum_j exp(z_j) = m_new ln 2 + ln sum_e, the sum over the 4 lane groups
+        float lb = l_blk + shfl_xor_f(l_blk, 16);
+        lb += shfl_xor_f(lb, 32);
+        if (blse) blse[i] = m_new * 0.69314718055994530942f + logf(lb);
+      }
 
       // ---- O^T[d][head] += V^T[d][key] P^T[key][head], 32 keys at a time
 #pragma unroll
@@ -344,7 +357,7 @@ static hipError_t launch_attn_t(const AttnPlan& pl, const AttnArgs& a, void* ws,
   k.batch = a.batch; k.rows_bound = pl.rows_bound;
   k.Hq = a.Hq; k.Hkv = a.Hkv; k.topk = a.topk; k.nsplit = pl.nsplit; k.bps = pl.bps;
   k.scale_log2 = a.scale * 1.4426950408889634f;
-  k.out = a.out; k.lse = a.lse;
+  k.out = a.out; k.lse = a.lse; k.block_lse = a.block_lse;
   char* w = static_cast<char*>(ws);
   k.part_o = pl.nsplit > 1 ? reinterpret_cast<float*>(w) : nullptr;
   k.part_lse = pl.nsplit > 1 ? reinterpret_cast<float*>(w + pl.part_o_bytes) : nullptr;

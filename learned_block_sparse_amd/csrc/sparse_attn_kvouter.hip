@@ -62,6 +62,7 @@ struct KvoArgs {
   float* part_lse;
   bf16* out;
   float* lse;
+  float* block_lse;
 };
 
 __device__ __forceinline__ int kvo_find(const int32_t* cu, int n, int64_t x) {
@@ -445,6 +446,10 @@ __global__ __launch_bounds__(256) void kvo_combine(KvoArgs a) {
     ls[i] = (mask & (1u << i)) ? a.part_lse[(slot0 + i) * kRmax + h] : -__builtin_inff();
     mx = fmaxf(mx, ls[i]);
   }
+  if (a.block_lse && (lane & 3) == 0) {
+    float* bl = a.block_lse + (t * a.Hq + g * R + h) * a.topk;
+    for (int i = 0; i < a.topk; ++i) bl[i] = ls[i];
+  }
   if (mask == 0u) {
 #pragma unroll
     for (int j = 0; j < 32; j += 4) *reinterpret_cast<bf16x4*>(out + j) = bf16x4{bf16(0.f), bf16(0.f), bf16(0.f), bf16(0.f)};
@@ -537,6 +542,7 @@ hipError_t launch_attn_kvouter(const AttnPlan& pl, bool kv_e4m3, const AttnArgs&
   a.part_lse = reinterpret_cast<float*>(w + pl.kvo_part_lse_off);
   a.out = static_cast<bf16*>(x.out);
   a.lse = x.lse;
+  a.block_lse = x.block_lse;
   const int nbk = pl.kvo_nbuckets;
   for (int64_t r0 = 0; r0 < pl.rows_bound; r0 += pl.kvo_window) {
     a.row_lo = r0;

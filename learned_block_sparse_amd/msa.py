@@ -65,15 +65,20 @@ def lib():
                                              ctypes.c_float, i32, vp, vp, vp, sz, vp]
         L.msa_sparse_attn_prefill_ex.restype = i32
         L.msa_sparse_attn_prefill_ex.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                                 i32, i32, ctypes.c_float, i32, vp, vp, vp, sz, vp]
+                                                 i32, i32, ctypes.c_float, i32, vp, vp, vp, vp, sz, vp]
         L.msa_sparse_attn_decode_ex.restype = i32
         L.msa_sparse_attn_decode_ex.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                                i32, ctypes.c_float, i32, vp, vp, vp, sz, vp]
+                                                i32, ctypes.c_float, i32, vp, vp, vp, vp, sz, vp]
         L.msa_sparse_attn_backward_workspace_size.restype = sz
         L.msa_sparse_attn_backward_workspace_size.argtypes = [i32] * 7
         L.msa_sparse_attn_backward.restype = i32
         L.msa_sparse_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
                                                i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+        L.msa_index_kl_workspace_size.restype = sz
+        L.msa_index_kl_workspace_size.argtypes = [i32] * 5
+        L.msa_index_kl_backward.restype = i32
+        L.msa_index_kl_backward.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                            vp, vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -152,7 +157,7 @@ def msa_index_topk(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, max_q_len: int, max
 
 
 def _prefill(ex, q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_q_len, max_kv_len, block_size, topk,
-             softmax_scale, num_splits, out, lse, return_lse, workspace, stream):
+             softmax_scale, num_splits, out, lse, return_lse, workspace, stream, block_lse=None):
     tq, hq, d = q.shape
     hkv = k.shape[1]
     batch = cu_seqlens_q.numel() - 1
@@ -171,13 +176,14 @@ def _prefill(ex, q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_q_len, max_
             _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32), batch, max_q_len, max_kv_len, hq, hkv, d,
             block_size, topk, float(softmax_scale), num_splits, _dev(out, "out", q.dtype),
             _dev(lse, "lse", torch.float32) if lse is not None else None,
+            *([_dev(block_lse, "block_lse", torch.float32) if block_lse is not None else None] if ex else []),
             ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
     _check(st, "msa_sparse_attn_prefill_ex" if ex else "msa_sparse_attn_prefill")
     return out, lse
 
 
 def _decode(ex, q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx, block_size, topk,
-            softmax_scale, num_splits, out, lse, return_lse, workspace, stream):
+            softmax_scale, num_splits, out, lse, return_lse, workspace, stream, block_lse=None):
     batch, hq, d = q.shape
     hkv = k_cache.shape[1]
     if out is None:
@@ -195,6 +201,7 @@ def _decode(ex, q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx
             _dev(ctx_lens, "ctx_lens", torch.int32), batch, max_ctx, hq, hkv, d, block_size, topk,
             float(softmax_scale), num_splits, _dev(out, "out", q.dtype),
             _dev(lse, "lse", torch.float32) if lse is not None else None,
+            *([_dev(block_lse, "block_lse", torch.float32) if block_lse is not None else None] if ex else []),
             ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
     _check(st, "msa_sparse_attn_decode_ex" if ex else "msa_sparse_attn_decode")
     return out, lse
@@ -212,11 +219,12 @@ def msa_sparse_attn_prefill(q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_
 def msa_sparse_attn_prefill_ex(q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_q_len: int,
                                max_kv_len: int, block_size: int = 128, topk: int = 16,
                                softmax_scale: float = 0.0, num_splits: int = 0, out=None, lse=None,
-                               return_lse: bool = True, workspace=None, stream=None):
+                               return_lse: bool = True, workspace=None, stream=None, block_lse=None):
     """As msa_sparse_attn_prefill with the K/V element type taken from ``k``
-    (e.g. bfloat16 q with float8_e4m3fn k and v)."""
+    (e.g. bfloat16 q with float8_e4m3fn k and v); ``block_lse`` ([Tq, Hq,
+    topk] fp32, optional) receives the per-slot block LSEs."""
     return _prefill(True, q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_q_len, max_kv_len, block_size,
-                    topk, softmax_scale, num_splits, out, lse, return_lse, workspace, stream)
+                    topk, softmax_scale, num_splits, out, lse, return_lse, workspace, stream, block_lse)
 
 
 def msa_sparse_attn_decode(q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx: int,
@@ -231,10 +239,12 @@ def msa_sparse_attn_decode(q, k_cache, v_cache, block_idx, cache_offsets, ctx_le
 def msa_sparse_attn_decode_ex(q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx: int,
                               block_size: int = 128, topk: int = 16, softmax_scale: float = 0.0,
                               num_splits: int = 0, out=None, lse=None, return_lse: bool = True,
-                              workspace=None, stream=None):
-    """As msa_sparse_attn_decode with the KV-cache element type taken from ``k_cache``."""
+                              workspace=None, stream=None, block_lse=None):
+    """As msa_sparse_attn_decode with the KV-cache element type taken from
+    ``k_cache``; ``block_lse`` ([B, Hq, topk] fp32, optional) receives the
+    per-slot block LSEs."""
     return _decode(True, q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx, block_size, topk,
-                   softmax_scale, num_splits, out, lse, return_lse, workspace, stream)
+                   softmax_scale, num_splits, out, lse, return_lse, workspace, stream, block_lse)
 
 
 def msa_sparse_attn_backward_workspace_size(batch, max_q_len, max_kv_len, num_heads, num_kv_heads, head_dim,
@@ -269,3 +279,37 @@ def msa_sparse_attn_backward(q, k, v, out, dout, lse, block_idx, cu_seqlens_q, c
         _dev(dv, "dv", torch.float32), ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
     _check(st, "msa_sparse_attn_backward")
     return dq, dk, dv
+
+
+def msa_index_kl_workspace_size(batch, max_q_len, max_kv_len, num_groups, topk) -> int:
+    return lib().msa_index_kl_workspace_size(batch, max_q_len, max_kv_len, num_groups, topk)
+
+
+def msa_index_kl_backward(q_idx, k_idx, block_idx, lse, block_lse, cu_seqlens_q, cu_seqlens_k, max_q_len: int,
+                          max_kv_len: int, block_size: int = 128, topk: int = 16, loss=None, dq_idx=None,
+                          dk_idx=None, workspace=None, stream=None):
+    """``(loss [Tq, G], dq_idx [Tq, G, d_idx], dk_idx [Tk, d_idx])`` fp32: the
+    index branch's KL alignment loss against the main branch's block shares
+    (``lse`` / ``block_lse`` from msa_sparse_attn_prefill_ex) and its
+    gradients."""
+    tq, G, di = q_idx.shape
+    tk = k_idx.shape[0]
+    hq = lse.shape[1]
+    batch = cu_seqlens_q.numel() - 1
+    if loss is None:
+        loss = torch.empty((tq, G), dtype=torch.float32, device=q_idx.device)
+    if dq_idx is None:
+        dq_idx = torch.empty((tq, G, di), dtype=torch.float32, device=q_idx.device)
+    if dk_idx is None:
+        dk_idx = torch.empty((tk, di), dtype=torch.float32, device=q_idx.device)
+    need = msa_index_kl_workspace_size(batch, max_q_len, max_kv_len, G, topk)
+    ws, ws_bytes = _workspace(need, q_idx.device, workspace)
+    st = lib().msa_index_kl_backward(
+        _dev(q_idx, "q_idx"), _dev(k_idx, "k_idx", q_idx.dtype), _dtype_code(q_idx),
+        _dev(block_idx, "block_idx", torch.int32), _dev(lse, "lse", torch.float32),
+        _dev(block_lse, "block_lse", torch.float32), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32), batch, max_q_len, max_kv_len, hq, G, di, block_size, topk,
+        _dev(loss, "loss", torch.float32), _dev(dq_idx, "dq_idx", torch.float32), _dev(dk_idx, "dk_idx", torch.float32),
+        ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
+    _check(st, "msa_index_kl_backward")
+    return loss, dq_idx, dk_idx

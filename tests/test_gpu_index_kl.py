@@ -1,0 +1,145 @@
+"""GPU parity of the per-slot block LSE output and of the index branch's KL
+alignment loss against the CPU oracle.
+
+Inputs are the seeded workloads: index tensors on the 1/8 grid (scores, and so
+the selection, every argmax and its tie-break, are exact on both sides), main
+branch q, k ~ N(0, 1) in bf16.  The GPU takes the block shares of main
+attention from its own forward call (per-slot block LSEs, fp32 from bf16
+MFMAs); the oracle recomputes them in fp64.  Those shares differ by a few
+fp32 ulps of the logits, so loss differs by ~1e-6 and dS by ~1e-6 absolute:
+the tests require |loss error| <= 1e-4 and, for dq_idx and dk_idx, relative
+RMS <= 1e-3 and max |err| <= 1e-3 * max |ref|.  Block LSEs use the LSE
+tolerances of the attention tests (1e-3 bf16, 1e-4 fp32).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from parity_helpers import host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def msa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from learned_block_sparse_amd import msa as m
+    m.lib()
+    return m
+
+
+@pytest.fixture(scope="module")
+def synth():
+    from learned_block_sparse_amd import synth as s
+    return s
+
+
+def _forward(msa, inp, wl, kv, ql, num_splits=0):
+    mq, mk = max(ql), max(kv)
+    ids = msa.msa_index_topk(inp["q_idx"], inp["k_idx"], inp["cu_seqlens_q"], inp["cu_seqlens_k"], mq, mk,
+                             wl.block_size, wl.topk)
+    tq, hq = inp["q"].shape[0], inp["q"].shape[1]
+    blse = torch.empty((tq, hq, wl.topk), dtype=torch.float32, device="cuda")
+    out, lse = msa.msa_sparse_attn_prefill_ex(inp["q"], inp["k"], inp["v"], ids, inp["cu_seqlens_q"],
+                                              inp["cu_seqlens_k"], mq, mk, wl.block_size, wl.topk,
+                                              num_splits=num_splits, block_lse=blse)
+    return ids, out, lse, blse
+
+
+def _compare_blse(gpu, ref, tol, what):
+    g = gpu.detach().cpu().double().numpy()
+    assert np.array_equal(np.isneginf(g), np.isneginf(ref)), f"{what}: -inf pattern differs"
+    fin = ~np.isneginf(ref)
+    err = float(np.abs(g[fin] - ref[fin]).max()) if fin.any() else 0.0
+    say(f"    {what}: block lse max err {err:.2e}")
+    assert err <= tol, f"{what}: block lse err {err:.3g} > {tol}"
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_block_lse_prefill_vs_oracle(msa, synth, oracle_lib, num_splits):
+    """KV-outer (0: 4,516 (query, group) items) and query-outer (1, 3) schedules."""
+    wl = dataclasses.replace(synth.WORKLOADS["prefill_32k"], planted=8)
+    kv, ql = [1000, 300], [1000, 129]
+    say(f"[kl] block lse kv={kv} q={ql} splits={num_splits}")
+    inp = synth.prefill_inputs(wl, device="cuda", seed=51, seq_lens=kv, q_lens=ql)
+    ids, _, _, blse = _forward(msa, inp, wl, kv, ql, num_splits)
+    torch.cuda.synchronize()
+    rows, kstart, pos = oracle_lib.rows_prefill(inp["cu_q_host"], inp["cu_k_host"])
+    ref = oracle_lib.block_lse(host(inp["q"]), host(inp["k"]), host(ids).numpy(), kstart, pos, rows,
+                               wl.block_size, wl.topk)
+    _compare_blse(blse, ref, 1e-3, f"splits {num_splits}")
+
+
+def test_block_lse_decode_vs_oracle(msa, synth, oracle_lib):
+    wl = synth.WORKLOADS["decode_1m"]
+    ctx = [1, 129, 4000, 20001]
+    say(f"[kl] block lse decode ctx={ctx}")
+    d = synth.decode_inputs(wl, device="cuda", seed=52, ctx_lens=ctx)
+    ids = msa.msa_index_topk(d["q_idx"], d["k_idx"], d["cu_seqlens_q"], d["cu_seqlens_k"], 1, max(ctx),
+                             wl.block_size, wl.topk)
+    blse = torch.empty((len(ctx), wl.num_heads, wl.topk), dtype=torch.float32, device="cuda")
+    msa.msa_sparse_attn_decode_ex(d["q"], d["k"], d["v"], ids, d["k_offsets"], d["ctx_lens"], max(ctx),
+                                  wl.block_size, wl.topk, block_lse=blse)
+    torch.cuda.synchronize()
+    rows, kstart, pos = oracle_lib.rows_decode(d["k_offsets_host"], ctx)
+    ref = oracle_lib.block_lse(host(d["q"]), host(d["k"]), host(ids).numpy(), kstart, pos, rows, wl.block_size,
+                               wl.topk)
+    _compare_blse(blse, ref, 1e-3, "decode")
+
+
+def _kl_check(msa, synth, oracle_lib, wl, kv, ql, seed, what):
+    inp = synth.prefill_inputs(wl, device="cuda", seed=seed, seq_lens=kv, q_lens=ql)
+    ids, _, lse, blse = _forward(msa, inp, wl, kv, ql)
+    loss, dq, dk = msa.msa_index_kl_backward(inp["q_idx"], inp["k_idx"], ids, lse, blse, inp["cu_seqlens_q"],
+                                             inp["cu_seqlens_k"], max(ql), max(kv), wl.block_size, wl.topk)
+    torch.cuda.synchronize()
+    rows, kstart, pos = oracle_lib.rows_prefill(inp["cu_q_host"], inp["cu_k_host"])
+    rl, rdq, rdk = oracle_lib.index_kl(host(inp["q_idx"]), host(inp["k_idx"]), host(inp["q"]), host(inp["k"]),
+                                       host(ids).numpy(), kstart, pos, rows, wl.block_size, wl.topk)
+    lerr = float(np.abs(loss.cpu().double().numpy() - rl).max())
+    say(f"    {what}: loss max err {lerr:.2e} (mean loss {rl.mean():.4f})")
+    assert lerr <= 1e-4, f"{what}: loss err {lerr:.3g}"
+    for name, g, r in (("dq_idx", dq, rdq), ("dk_idx", dk, rdk)):
+        gg = g.cpu().double().numpy()
+        err = np.abs(gg - r)
+        rel = float(np.sqrt((err ** 2).sum() / max((r ** 2).sum(), 1e-300)))
+        mx = float(err.max())
+        say(f"    {what} {name}: rel-RMS {rel:.2e}, max-abs {mx:.2e} (max |ref| {np.abs(r).max():.3g})")
+        assert rel <= 1e-3 and mx <= 1e-3 * float(np.abs(r).max()), f"{what} {name}"
+    return loss, dq, dk
+
+
+def test_index_kl_vs_oracle(msa, synth, oracle_lib):
+    """Measured head configuration, two packed sequences (the second a chunk),
+    planted hot blocks."""
+    wl = dataclasses.replace(synth.WORKLOADS["prefill_32k"], planted=8)
+    kv, ql = [1000, 300], [1000, 129]
+    say(f"[kl] loss kv={kv} q={ql}")
+    _kl_check(msa, synth, oracle_lib, wl, kv, ql, 53, "kl")
+
+
+def test_index_kl_fp32_and_deterministic(msa, synth, oracle_lib):
+    """fp32 inputs, 8 Q / 2 KV heads, d_idx 64, k 4 (the small fp32 workload);
+    a second call gives bit-identical results."""
+    wl = synth.WORKLOADS["tiny_prefill_2k_f32"]
+    kv, ql = [2048, 700], [2048, 300]
+    say(f"[kl] fp32 kv={kv} q={ql}")
+    a = _kl_check(msa, synth, oracle_lib, wl, kv, ql, 54, "kl fp32")
+    inp = synth.prefill_inputs(wl, device="cuda", seed=54, seq_lens=kv, q_lens=ql)
+    ids, _, lse, blse = _forward(msa, inp, wl, kv, ql)
+    b = msa.msa_index_kl_backward(inp["q_idx"], inp["k_idx"], ids, lse, blse, inp["cu_seqlens_q"],
+                                  inp["cu_seqlens_k"], max(ql), max(kv), wl.block_size, wl.topk)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+
+
+def test_index_kl_several_windows(msa, synth, oracle_lib):
+    """9,000 query rows: two edge-list windows, dk_idx accumulated across them."""
+    wl = dataclasses.replace(synth.WORKLOADS["prefill_32k"], num_heads=8, num_kv_heads=2, planted=8)
+    kv = [9000]
+    say(f"[kl] two windows kv={kv}")
+    _kl_check(msa, synth, oracle_lib, wl, kv, kv, 55, "kl 2 windows")
