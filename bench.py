@@ -293,7 +293,40 @@ def main():
         "ms": round(bwd_ms, 3), "tflops": round(bwd_flops / (bwd_ms / 1e3) / 1e12, 1),
         "frac_mfma": round(bwd_flops / (bwd_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "algorithmic_flops": bwd_flops}
-    del inp, calls, q8, k8, kv8, vv8, dout, dq_b, dk_b, dv_b, ws_b
+    del dout, dq_b, dk_b, dv_b, ws_b
+    # The index branch's KL alignment loss (an extra measurement): block LSEs
+    # from the attention calls, then one msa_index_kl_backward call per tile.
+    for c in calls:
+        c["blse"] = torch.empty((c["m"], Hq, wl.topk), dtype=torch.float32, device=dev)
+        msa.msa_sparse_attn_prefill_ex(c["q"], inp["k"], inp["v"], c["ids"], c["cu_q"], c["cu_k"], c["m"], c["hi"],
+                                       wl.block_size, wl.topk, out=c["out"], lse=c["lse"], workspace=c["ws_a"],
+                                       stream=stream, block_lse=c["blse"])
+    ws_kl = torch.empty(max(1, max(msa.msa_index_kl_workspace_size(1, c["m"], c["hi"], G, wl.topk) for c in calls)),
+                        dtype=torch.uint8, device=dev)
+    kl_loss = torch.empty((T, G), dtype=torch.float32, device=dev)
+    kl_dq = torch.empty((T, G, DI), dtype=torch.float32, device=dev)
+    kl_dk = torch.empty((L, DI), dtype=torch.float32, device=dev)
+
+    def kl_step():
+        for c in calls:
+            msa.msa_index_kl_backward(c["q_idx"], inp["k_idx"][:c["hi"]], c["ids"], c["lse"], c["blse"], c["cu_q"],
+                                      c["cu_k"], c["m"], c["hi"], wl.block_size, wl.topk, loss=kl_loss[:c["m"]],
+                                      dq_idx=kl_dq[:c["m"]], dk_idx=kl_dk[:c["hi"]], workspace=ws_kl,
+                                      stream=stream)
+
+    kl_step()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        kl_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kl_ms = e0.elapsed_time(e1) / args.steps
+    # scoring the selected blocks' attended keys: 2 d_idx per key and group
+    kl_flops = att_flops / (4 * D * Hq) * 2 * DI * G
+    result["prefill"]["index_kl"] = {"ms": round(kl_ms, 3), "tflops": round(kl_flops / (kl_ms / 1e3) / 1e12, 1),
+                                     "algorithmic_flops": kl_flops}
+    del inp, calls, q8, k8, kv8, vv8, kl_loss, kl_dq, kl_dk, ws_kl
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ decode

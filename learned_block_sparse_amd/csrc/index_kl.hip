@@ -28,8 +28,9 @@
 //   kl_loss    one wave per (row, group): A, softmax(S), loss, dS per slot and
 //              dq_idx (lanes over the index dims)
 //   kl_dk      one workgroup per (sequence, block): for each group in order,
-//              the bucket's edges sorted in LDS and summed in that order into
-//              a per-key LDS accumulator, added to dk_idx once per window
+//              the bucket's edges sorted in LDS by (argmax key, code), so each
+//              key's contributions are one segment summed in code order by
+//              that key's threads; added to dk_idx once per window
 // No atomics touch the arithmetic: results are bitwise reproducible.
 #include "msa_device.h"
 #include "msa_launch.h"
@@ -233,75 +234,96 @@ __global__ __launch_bounds__(256) void kl_loss(KlArgs a) {
 }
 
 // ------------------------------------------------------------------ kl_dk
-// One workgroup per (sequence, block); thread d < DI owns index dim d.
-template <typename T>
-__global__ __launch_bounds__(128) void kl_dk(KlArgs a) {
-  __shared__ float acc[kBlock * kHeadDim];  // [key][dim], DI <= 128
-  __shared__ int32_t codes[kKlSortMax];
+// One workgroup per (sequence, block), 256 threads: thread (key j = tid / 2,
+// half = tid % 2) owns dims 64 half .. 64 half + 63 of dk_idx[j].  For each
+// group in order, the bucket's edges are keyed (argmax j* << 16 | code) and
+// sorted in LDS, so each key's edges form one segment in code order; the
+// thread sums its key's segment in that order.  Segments come from a count
+// of edges per key and its prefix sum.
+template <typename T, int DI>
+__global__ __launch_bounds__(256) void kl_dk(KlArgs a) {
+  __shared__ int32_t keys[kKlSortMax];
+  __shared__ int32_t seg[kBlock + 1];
+  constexpr int kHalf = DI / 2;
   const int sb = blockIdx.x;  // sequence * nb_max + block
   if (sb >= a.batch * a.nb_max) return;
   const int c = sb % a.nb_max;
   const int b = sb / a.nb_max;
   const int tid = threadIdx.x;
-  const int DI = a.DI;
+  const int j = tid >> 1, half = tid & 1;
   const T* qg = static_cast<const T*>(a.q_idx);
   bool any = false;
-  for (int g = 0; g < a.G; ++g) any = any || a.offsets[(b * a.G + g) * a.nb_max + c + 1] >
-                                                   a.offsets[(b * a.G + g) * a.nb_max + c];
+  for (int g = 0; g < a.G; ++g) {
+    const int bucket = (b * a.G + g) * a.nb_max + c;
+    any = any || a.offsets[bucket + 1] > a.offsets[bucket];
+  }
   if (!any) return;
-  for (int i = tid; i < kBlock * kHeadDim; i += 128) acc[i] = 0.f;
+  float acc[kHalf];
+#pragma unroll
+  for (int d = 0; d < kHalf; ++d) acc[d] = 0.f;
   for (int g = 0; g < a.G; ++g) {
     const int bucket = (b * a.G + g) * a.nb_max + c;
     const int e_lo = a.offsets[bucket];
     const int n = a.offsets[bucket + 1] - e_lo;
     if (n == 0) continue;
-    // sort the bucket's codes (placed by atomics in no fixed order)
     int n2 = 1;
     while (n2 < n) n2 <<= 1;
-    __syncthreads();
-    for (int i = tid; i < n2; i += 128) codes[i] = i < n ? a.edges[e_lo + i] : 0x7fffffff;
+    __syncthreads();  // keys / seg of the previous group are no longer read
+    for (int i = tid; i < n2; i += 256) {
+      int32_t k = 0x7fffffff;
+      if (i < n) {
+        const int code = a.edges[e_lo + i];
+        const int64_t slot = ((int64_t)(code >> 4) * a.G + g) * a.topk + (code & 15);
+        k = (a.j_slot[slot] << 16) | code;  // code < 2^16 (4096 rows x 16 slots)
+      }
+      keys[i] = k;
+    }
+    if (tid <= kBlock) seg[tid] = 0;
     __syncthreads();
     for (int kk = 2; kk <= n2; kk <<= 1) {
-      for (int j = kk >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < n2; i += 128) {
-          const int ixj = i ^ j;
+      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+        for (int i = tid; i < n2; i += 256) {
+          const int ixj = i ^ jj;
           if (ixj > i) {
-            const int32_t x = codes[i], y = codes[ixj];
+            const int32_t x = keys[i], y = keys[ixj];
             if ((x > y) == ((i & kk) == 0)) {
-              codes[i] = y;
-              codes[ixj] = x;
+              keys[i] = y;
+              keys[ixj] = x;
             }
           }
         }
         __syncthreads();
       }
     }
-    // edges in code order: acc[j*][d] += dS q_idx[t, g, d]; the loads of 8
-    // edges are issued together, the sums still run in code order
-    constexpr int kBatch = 8;
-    for (int e0 = 0; e0 < n; e0 += kBatch) {
-      float ds[kBatch], qv[kBatch];
-      int jj[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int code = codes[e0 + u < n ? e0 + u : e0];
+    // segment starts: the first sorted position of each key (keys ascend)
+    for (int i = tid; i < n; i += 256) {
+      const int kj = keys[i] >> 16;
+      if (i == 0 || (keys[i - 1] >> 16) != kj) seg[kj] = i + 1;  // +1: 0 marks "no edge"
+    }
+    __syncthreads();
+    int s0 = seg[j] - 1;
+    if (s0 >= 0) {
+      for (int i = s0; i < n && (keys[i] >> 16) == j; ++i) {
+        const int code = keys[i] & 0xffff;
         const int64_t slot = ((int64_t)(code >> 4) * a.G + g) * a.topk + (code & 15);
-        const int64_t t = a.row_lo + (code >> 4);
-        ds[u] = a.ds_slot[slot];
-        jj[u] = a.j_slot[slot];
-        qv[u] = tid < DI ? (float)qg[(t * a.G + g) * DI + tid] : 0.f;
-      }
+        const float ds = a.ds_slot[slot];
+        const T* qrow = qg + ((a.row_lo + (code >> 4)) * a.G + g) * DI + kHalf * half;
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (e0 + u < n && tid < DI) acc[jj[u] * kHeadDim + tid] += ds[u] * qv[u];
+        for (int d8 = 0; d8 < kHalf; d8 += 8) {
+          const frag8<T> v8 = load8(qrow + d8);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) acc[d8 + u] += ds * (float)v8[u];
+        }
+      }
     }
   }
-  __syncthreads();
   const int64_t kb0 = a.cu_k[b];
   const int N = a.cu_k[b + 1] - a.cu_k[b];
-  if (tid < DI)
-    for (int j = 0; j < kBlock && c * kBlock + j < N; ++j)
-      a.dk_idx[(kb0 + c * kBlock + j) * DI + tid] += acc[j * kHeadDim + tid];
+  if (c * kBlock + j < N) {
+    float* dst = a.dk_idx + (kb0 + c * kBlock + j) * DI + kHalf * half;
+#pragma unroll
+    for (int d = 0; d < kHalf; ++d) dst[d] += acc[d];
+  }
 }
 
 KlPlan plan_kl(int batch, int max_q_len, int max_kv_len, int G, int topk) {
@@ -369,7 +391,7 @@ static hipError_t launch_kl_t(const KlPlan& pl, const KlLaunch& x, void* ws, hip
     const int64_t ub = entries / kEdgeChunk + (entries < pl.nbuckets ? entries : pl.nbuckets) + 1;
     hipLaunchKernelGGL((kl_scores<T, DI>), dim3((unsigned)ub), dim3(128), 0, st, a);
     hipLaunchKernelGGL(kl_loss<T>, dim3((unsigned)(((r1 - r0) * a.G + 3) / 4)), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(kl_dk<T>, dim3((unsigned)(a.batch * pl.nb_max)), dim3(128), 0, st, a);
+    hipLaunchKernelGGL((kl_dk<T, DI>), dim3((unsigned)(a.batch * pl.nb_max)), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
