@@ -264,7 +264,9 @@ msa_status_t msa_sparse_attn_decode_ex(const void* q, const void* k_cache, const
  *                the per-block edge lists of one window of at most 8192 query
  *                rows and one fp32 per (row, head)
  *
- * Accumulation is fp32; P and dS enter the dK, dV and dQ products as bf16.
+ * Accumulation is fp32; P and dS enter the dK, dV and dQ products as bf16,
+ * and each selected block's contribution to dq is kept in bf16 until the
+ * fp32 sum over the row's blocks (measured dq error about 2.5e-3 relative RMS).
  * Results are bitwise reproducible (no atomics in any arithmetic: each
  * block's edges are summed in a fixed order).
  * ---------------------------------------------------------------------- */

@@ -35,7 +35,7 @@
 //              edges of a bucket: S^T = K Q^T and dP^T = V dO^T with two
 //              queries x 16 heads as the 32 MFMA columns, then dQ += dS K
 //              from registers; each edge writes its block's dQ contribution
-//              to the fp32 partial of its selection slot
+//              to the bf16 partial of its selection slot
 //   bwd_dq_combine  dq = sum of a row's slot partials in slot order
 // No atomics touch the arithmetic: every result is bitwise reproducible.
 #include "msa_device.h"
@@ -66,7 +66,7 @@ struct BwdKernelArgs {
   const int32_t* chunk_start;
   int32_t* edges;
   float* delta;
-  float* part_dq;
+  bf16* part_dq;     // [window rows, G, topk, 16, 128]: each edge's block contribution to dq (unscaled)
   float* dq;
   float* dk;
   float* dv;
@@ -388,8 +388,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
 // 32 MFMA columns) tile by tile over 32 keys: S^T and dP^T, then dS, whose
 // registers (column = the lane's (query, head), 8 keys per k-step) are
 // directly the A operand of dQ += dS K.  Each edge writes its block's dQ
-// contribution (fp32) to the partial slot of its selection entry; a
-// fixed-order sum over the slots follows.
+// contribution (bf16) to the partial slot of its selection entry; a
+// fixed-order fp32 sum over the slots follows.
 constexpr int kDqKRow = 136;   // K / V row: 128 bf16 + 8 pad
 constexpr int kDqKtRow = 132;  // K^T row (one dim, 128 keys) + 4 pad
 
@@ -475,7 +475,8 @@ __device__ __forceinline__ void dq_pair(const BwdKernelArgs& a, DqPair& P, int e
   }
   // C layout of acc[dt]: column = dim 32 dt + col, rows (query, head)
   // 8 (r / 4) + 4 a32 + r % 4: rows 0..15 are query 0 of the pair, 16..31 query 1
-  float* part = a.part_dq;
+  // bf16 partials, like the forward's O partials: the combine sums them in fp32
+  bf16* part = a.part_dq;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = 8 * (r >> 2) + 4 * a32 + (r & 3);
@@ -483,9 +484,9 @@ __device__ __forceinline__ void dq_pair(const BwdKernelArgs& a, DqPair& P, int e
     if (hh >= R || (q == 1 && !has1)) continue;
     const int cd = q ? code1 : code0;
     const int64_t slot = ((int64_t)(cd >> 4) * a.G + g) * a.topk + (cd & 15);
-    float* dst = part + (slot * 16 + hh) * kHeadDim + col;
+    bf16* dst = part + (slot * 16 + hh) * kHeadDim + col;
 #pragma unroll
-    for (int dt = 0; dt < kHeadDim / 32; ++dt) dst[32 * dt] = acc[dt][r];
+    for (int dt = 0; dt < kHeadDim / 32; ++dt) dst[32 * dt] = bf16(acc[dt][r]);
   }
 }
 
@@ -599,9 +600,13 @@ __global__ __launch_bounds__(256) void bwd_dq_combine(BwdKernelArgs a, int64_t r
   for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int i = 0; i < a.topk; ++i) {
     if (!((mask >> i) & 1u)) continue;
-    const float* src = a.part_dq + ((slot0 + i) * 16 + h) * kHeadDim + d0;
+    const bf16* src = a.part_dq + ((slot0 + i) * 16 + h) * kHeadDim + d0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] += *reinterpret_cast<const f32x4*>(src + 4 * j);
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 v8 = load8(src + 8 * j);
+      acc[2 * j] += f32x4{(float)v8[0], (float)v8[1], (float)v8[2], (float)v8[3]};
+      acc[2 * j + 1] += f32x4{(float)v8[4], (float)v8[5], (float)v8[6], (float)v8[7]};
+    }
   }
   float* dst = a.dq + (t * a.Hq + g * R + h) * kHeadDim + d0;
 #pragma unroll
@@ -624,7 +629,7 @@ BwdPlan plan_bwd(int batch, int max_q_len, int max_kv_len, int Hq, int G, int to
   pl.cursor_off = off;  off += al(nbk * 4);
   pl.edges_off = off;   off += al((size_t)pl.window * G * topk * 4);
   pl.delta_off = off;   off += al((size_t)pl.rows_bound * Hq * 4);
-  pl.part_dq_off = off; off += al((size_t)pl.window * G * topk * 16 * kHeadDim * 4);
+  pl.part_dq_off = off; off += al((size_t)pl.window * G * topk * 16 * kHeadDim * sizeof(bf16));
   pl.workspace_bytes = off;
   return pl;
 }
@@ -658,7 +663,7 @@ hipError_t launch_sparse_attn_bwd(const BwdPlan& pl, const BwdArgs& x, void* ws,
   a.chunk_start = chunks;
   a.edges = reinterpret_cast<int32_t*>(w + pl.edges_off);
   a.delta = reinterpret_cast<float*>(w + pl.delta_off);
-  a.part_dq = reinterpret_cast<float*>(w + pl.part_dq_off);
+  a.part_dq = reinterpret_cast<bf16*>(w + pl.part_dq_off);
   a.dq = x.dq;
   a.dk = x.dk;
   a.dv = x.dv;

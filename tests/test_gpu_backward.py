@@ -6,7 +6,9 @@ backward call returns fp32 dq, dk, dv; the oracle recomputes everything in
 fp64 from q, k, v, dO and the same ids.
 
 Tolerance.  The GPU rounds P and dS to bf16 before the dV, dK and dQ products
-(relative 2^-9 each) and takes delta = dO . out from the bf16 forward output;
+(relative 2^-9 each), keeps each block's dq contribution in bf16 until the
+fp32 sum over the row's blocks, and takes delta = dO . out from the bf16
+forward output;
 everything else accumulates in fp32 from exact bf16 inputs.  These are
 independent relative perturbations of about 2^-9 per term, so the error of a
 gradient relative to its own scale is a few parts in 10^3: the tests require
