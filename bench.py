@@ -220,6 +220,119 @@ def main():
                     "algorithmic_flops": idx_flops + att_flops,
                     "planted_share_last_tile": round(planted_share, 3)},
     }
+    # ------------------------------------------------------------------ decode
+    # (run right after the headline prefill measurement: the extra prefill
+    # legs below allocate and free several GB, after which the 5 GB decode
+    # caches measured about 3% slower)
+    def decode_leg():
+        if not args.no_decode:
+            wd = synth.WORKLOADS["decode_1m"]
+            ctx = synth.decode_ctx_lens(wd, 0)
+            d = synth.decode_inputs(wd, device=dev, seed=0, ctx_lens=ctx)
+            B = len(ctx)
+            ws_i = torch.empty(max(1, msa.msa_index_topk_workspace_size(B, 1, max(ctx), G, wd.block_size, wd.topk)),
+                               dtype=torch.uint8, device=dev)
+            ws_a = torch.empty(max(1, msa.msa_sparse_attn_workspace_size(B, 1, max(ctx), Hq, G, D, wd.topk, 0)),
+                               dtype=torch.uint8, device=dev)
+            ids = torch.empty((B, G, wd.topk), dtype=torch.int32, device=dev)
+            out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+            lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+
+            def dstep(e=None):
+                if e is not None:
+                    e[0].record(stream)
+                msa.msa_index_topk(d["q_idx"], d["k_idx"], d["cu_seqlens_q"], d["cu_seqlens_k"], 1, max(ctx),
+                                   wd.block_size, wd.topk, block_idx=ids, workspace=ws_i, stream=stream)
+                if e is not None:
+                    e[1].record(stream)
+                msa.msa_sparse_attn_decode(d["q"], d["k"], d["v"], ids, d["k_offsets"], d["ctx_lens"], max(ctx),
+                                           wd.block_size, wd.topk, out=out, lse=lse, workspace=ws_a, stream=stream)
+                if e is not None:
+                    e[2].record(stream)
+
+            for _ in range(5):
+                dstep()
+            torch.cuda.synchronize()
+            # steady-state step time: events only around the whole run of steps
+            e_lo, e_hi = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e_lo.record(stream)
+            for s in range(args.decode_steps):
+                dstep()
+            e_hi.record(stream)
+            torch.cuda.synchronize()
+            dwall = (time.perf_counter() - t0) / args.decode_steps
+            d_step_us = e_lo.elapsed_time(e_hi) * 1e3 / args.decode_steps
+            # per-call breakdown from a second run with events between the calls
+            dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.decode_steps)]
+            for s in range(args.decode_steps):
+                dstep(dev_ev[s])
+            torch.cuda.synchronize()
+            d_idx_us = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_ev])) * 1e3
+            d_att_us = float(np.mean([e[1].elapsed_time(e[2]) for e in dev_ev])) * 1e3
+            idx_b, att_b = workmodel.decode_bytes(ctx, Hq, G, D, DI, wd.block_size, wd.topk)
+            gbs = (idx_b + att_b) / (d_step_us * 1e-6) / 1e9
+            idx_gbs = idx_b / (d_idx_us * 1e-6) / 1e9
+            result["decode"] = {
+                "workload": "decode_1m", "batch": B, "ctx_sum": int(sum(ctx)), "us_per_step": round(d_step_us, 1),
+                "wall_us_per_step": round(dwall * 1e6, 1), "index_us": round(d_idx_us, 1),
+                "attention_us": round(d_att_us, 1), "bytes_per_step": idx_b + att_b,
+                "achieved_GBs": round(gbs, 1), "peak_GBs": PEAK_HBM_GBS, "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                "index_scan_GBs": round(idx_gbs, 1), "index_scan_frac_hbm": round(idx_gbs / PEAK_HBM_GBS, 4),
+                "index_scan_traffic": traffic_record("index_decode_1m"),
+            }
+            # the same decode step with the index tensors in fp8 E4M3 (half the scan bytes)
+            q8, k8 = d["q_idx"].to(torch.float8_e4m3fn), d["k_idx"].to(torch.float8_e4m3fn)
+
+            def dstep8():
+                msa.msa_index_topk(q8, k8, d["cu_seqlens_q"], d["cu_seqlens_k"], 1, max(ctx), wd.block_size,
+                                   wd.topk, block_idx=ids, workspace=ws_i, stream=stream)
+                msa.msa_sparse_attn_decode(d["q"], d["k"], d["v"], ids, d["k_offsets"], d["ctx_lens"], max(ctx),
+                                           wd.block_size, wd.topk, out=out, lse=lse, workspace=ws_a, stream=stream)
+
+            for _ in range(5):
+                dstep8()
+            torch.cuda.synchronize()
+            e_lo.record(stream)
+            for s in range(args.decode_steps):
+                dstep8()
+            e_hi.record(stream)
+            torch.cuda.synchronize()
+            d8_us = e_lo.elapsed_time(e_hi) * 1e3 / args.decode_steps
+            idx8_b, _ = workmodel.decode_bytes(ctx, Hq, G, D, DI, wd.block_size, wd.topk, elem_bytes=1)
+            gbs8 = (idx8_b + att_b) / (d8_us * 1e-6) / 1e9
+            result["decode"]["fp8_index"] = {
+                "us_per_step": round(d8_us, 1), "bytes_per_step": idx8_b + att_b, "achieved_GBs": round(gbs8, 1),
+                "frac_hbm": round(gbs8 / PEAK_HBM_GBS, 4)}
+            # every cache in fp8 E4M3: index keys (and index queries), K and V; bf16 q and out
+            kc8, vc8 = d["k"].to(torch.float8_e4m3fn), d["v"].to(torch.float8_e4m3fn)
+
+            def dstep_all8():
+                msa.msa_index_topk(q8, k8, d["cu_seqlens_q"], d["cu_seqlens_k"], 1, max(ctx), wd.block_size,
+                                   wd.topk, block_idx=ids, workspace=ws_i, stream=stream)
+                msa.msa_sparse_attn_decode_ex(d["q"], kc8, vc8, ids, d["k_offsets"], d["ctx_lens"], max(ctx),
+                                              wd.block_size, wd.topk, out=out, lse=lse, workspace=ws_a, stream=stream)
+
+            for _ in range(5):
+                dstep_all8()
+            torch.cuda.synchronize()
+            e_lo.record(stream)
+            for s in range(args.decode_steps):
+                dstep_all8()
+            e_hi.record(stream)
+            torch.cuda.synchronize()
+            da8_us = e_lo.elapsed_time(e_hi) * 1e3 / args.decode_steps
+            ia8_b, aa8_b = workmodel.decode_bytes(ctx, Hq, G, D, DI, wd.block_size, wd.topk, elem_bytes=1,
+                                                  kv_elem_bytes=1, qo_elem_bytes=2)
+            gbsa8 = (ia8_b + aa8_b) / (da8_us * 1e-6) / 1e9
+            result["decode"]["fp8_index_and_kv"] = {
+                "us_per_step": round(da8_us, 1), "bytes_per_step": ia8_b + aa8_b, "achieved_GBs": round(gbsa8, 1),
+                "frac_hbm": round(gbsa8 / PEAK_HBM_GBS, 4)}
+            del d, q8, k8, kc8, vc8
+            torch.cuda.empty_cache()
+
+    decode_leg()
+
     # The same index calls with the index tensors rounded to fp8 E4M3 (an extra
     # measurement beside the bf16 headline; the block ids are exact for these
     # inputs on both paths, see the fp8 tests).
@@ -328,113 +441,6 @@ def main():
                                      "algorithmic_flops": kl_flops}
     del inp, calls, q8, k8, kv8, vv8, kl_loss, kl_dq, kl_dk, ws_kl
     torch.cuda.empty_cache()
-
-    # ------------------------------------------------------------------ decode
-    if not args.no_decode:
-        wd = synth.WORKLOADS["decode_1m"]
-        ctx = synth.decode_ctx_lens(wd, 0)
-        d = synth.decode_inputs(wd, device=dev, seed=0, ctx_lens=ctx)
-        B = len(ctx)
-        ws_i = torch.empty(max(1, msa.msa_index_topk_workspace_size(B, 1, max(ctx), G, wd.block_size, wd.topk)),
-                           dtype=torch.uint8, device=dev)
-        ws_a = torch.empty(max(1, msa.msa_sparse_attn_workspace_size(B, 1, max(ctx), Hq, G, D, wd.topk, 0)),
-                           dtype=torch.uint8, device=dev)
-        ids = torch.empty((B, G, wd.topk), dtype=torch.int32, device=dev)
-        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-
-        def dstep(e=None):
-            if e is not None:
-                e[0].record(stream)
-            msa.msa_index_topk(d["q_idx"], d["k_idx"], d["cu_seqlens_q"], d["cu_seqlens_k"], 1, max(ctx),
-                               wd.block_size, wd.topk, block_idx=ids, workspace=ws_i, stream=stream)
-            if e is not None:
-                e[1].record(stream)
-            msa.msa_sparse_attn_decode(d["q"], d["k"], d["v"], ids, d["k_offsets"], d["ctx_lens"], max(ctx),
-                                       wd.block_size, wd.topk, out=out, lse=lse, workspace=ws_a, stream=stream)
-            if e is not None:
-                e[2].record(stream)
-
-        for _ in range(5):
-            dstep()
-        torch.cuda.synchronize()
-        # steady-state step time: events only around the whole run of steps
-        e_lo, e_hi = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e_lo.record(stream)
-        for s in range(args.decode_steps):
-            dstep()
-        e_hi.record(stream)
-        torch.cuda.synchronize()
-        dwall = (time.perf_counter() - t0) / args.decode_steps
-        d_step_us = e_lo.elapsed_time(e_hi) * 1e3 / args.decode_steps
-        # per-call breakdown from a second run with events between the calls
-        dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.decode_steps)]
-        for s in range(args.decode_steps):
-            dstep(dev_ev[s])
-        torch.cuda.synchronize()
-        d_idx_us = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_ev])) * 1e3
-        d_att_us = float(np.mean([e[1].elapsed_time(e[2]) for e in dev_ev])) * 1e3
-        idx_b, att_b = workmodel.decode_bytes(ctx, Hq, G, D, DI, wd.block_size, wd.topk)
-        gbs = (idx_b + att_b) / (d_step_us * 1e-6) / 1e9
-        idx_gbs = idx_b / (d_idx_us * 1e-6) / 1e9
-        result["decode"] = {
-            "workload": "decode_1m", "batch": B, "ctx_sum": int(sum(ctx)), "us_per_step": round(d_step_us, 1),
-            "wall_us_per_step": round(dwall * 1e6, 1), "index_us": round(d_idx_us, 1),
-            "attention_us": round(d_att_us, 1), "bytes_per_step": idx_b + att_b,
-            "achieved_GBs": round(gbs, 1), "peak_GBs": PEAK_HBM_GBS, "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
-            "index_scan_GBs": round(idx_gbs, 1), "index_scan_frac_hbm": round(idx_gbs / PEAK_HBM_GBS, 4),
-            "index_scan_traffic": traffic_record("index_decode_1m"),
-        }
-        # the same decode step with the index tensors in fp8 E4M3 (half the scan bytes)
-        q8, k8 = d["q_idx"].to(torch.float8_e4m3fn), d["k_idx"].to(torch.float8_e4m3fn)
-
-        def dstep8():
-            msa.msa_index_topk(q8, k8, d["cu_seqlens_q"], d["cu_seqlens_k"], 1, max(ctx), wd.block_size,
-                               wd.topk, block_idx=ids, workspace=ws_i, stream=stream)
-            msa.msa_sparse_attn_decode(d["q"], d["k"], d["v"], ids, d["k_offsets"], d["ctx_lens"], max(ctx),
-                                       wd.block_size, wd.topk, out=out, lse=lse, workspace=ws_a, stream=stream)
-
-        for _ in range(5):
-            dstep8()
-        torch.cuda.synchronize()
-        e_lo.record(stream)
-        for s in range(args.decode_steps):
-            dstep8()
-        e_hi.record(stream)
-        torch.cuda.synchronize()
-        d8_us = e_lo.elapsed_time(e_hi) * 1e3 / args.decode_steps
-        idx8_b, _ = workmodel.decode_bytes(ctx, Hq, G, D, DI, wd.block_size, wd.topk, elem_bytes=1)
-        gbs8 = (idx8_b + att_b) / (d8_us * 1e-6) / 1e9
-        result["decode"]["fp8_index"] = {
-            "us_per_step": round(d8_us, 1), "bytes_per_step": idx8_b + att_b, "achieved_GBs": round(gbs8, 1),
-            "frac_hbm": round(gbs8 / PEAK_HBM_GBS, 4)}
-        # every cache in fp8 E4M3: index keys (and index queries), K and V; bf16 q and out
-        kc8, vc8 = d["k"].to(torch.float8_e4m3fn), d["v"].to(torch.float8_e4m3fn)
-
-        def dstep_all8():
-            msa.msa_index_topk(q8, k8, d["cu_seqlens_q"], d["cu_seqlens_k"], 1, max(ctx), wd.block_size,
-                               wd.topk, block_idx=ids, workspace=ws_i, stream=stream)
-            msa.msa_sparse_attn_decode_ex(d["q"], kc8, vc8, ids, d["k_offsets"], d["ctx_lens"], max(ctx),
-                                          wd.block_size, wd.topk, out=out, lse=lse, workspace=ws_a, stream=stream)
-
-        for _ in range(5):
-            dstep_all8()
-        torch.cuda.synchronize()
-        e_lo.record(stream)
-        for s in range(args.decode_steps):
-            dstep_all8()
-        e_hi.record(stream)
-        torch.cuda.synchronize()
-        da8_us = e_lo.elapsed_time(e_hi) * 1e3 / args.decode_steps
-        ia8_b, aa8_b = workmodel.decode_bytes(ctx, Hq, G, D, DI, wd.block_size, wd.topk, elem_bytes=1,
-                                              kv_elem_bytes=1, qo_elem_bytes=2)
-        gbsa8 = (ia8_b + aa8_b) / (da8_us * 1e-6) / 1e9
-        result["decode"]["fp8_index_and_kv"] = {
-            "us_per_step": round(da8_us, 1), "bytes_per_step": ia8_b + aa8_b, "achieved_GBs": round(gbsa8, 1),
-            "frac_hbm": round(gbsa8 / PEAK_HBM_GBS, 4)}
-        del d, q8, k8, kc8, vc8
-        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU baseline
     if not args.no_cpu_baseline:

@@ -54,17 +54,27 @@ def build(verbose: bool = False) -> str:
 
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments and blank space removed (string literals in
+    these sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest() -> str:
-    """SHA-256 over the kernel sources and the ABI header (identifies which
-    build a set of hardware-counter measurements belongs to)."""
+    """SHA-256 over the code of the kernel sources and the ABI header, comments
+    and layout excluded (identifies which build a set of hardware-counter
+    measurements belongs to; editing a comment keeps it)."""
     import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".h")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
-    with open(os.path.join(ROOT, "include", "msa.h"), "rb") as f:
-        h.update(f.read())
+            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+                h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
+    with open(os.path.join(ROOT, "include", "msa.h"), encoding="utf-8") as f:
+        h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

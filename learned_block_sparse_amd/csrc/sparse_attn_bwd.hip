@@ -21,11 +21,10 @@
 //              builds).  The bucket's list, placed by atomics in no fixed
 //              order, is first sorted in LDS, so the order in which the edges
 //              are summed (and so every rounding) is fixed.  Each of the 4
-//              waves owns 32 keys of
-//              the block and keeps their K and V rows in registers as MFMA
-//              operands; the edges run in quads (4
-//              queries x 16 heads = 64 MFMA rows), whose Q and dO are staged in
-//              LDS twice, row-major for S = Q K^T and dP = dO V^T and
+//              waves owns 32 keys of the block and keeps their K and V rows
+//              in registers as MFMA operands; the edges run in quads (4
+//              queries x 16 heads = 64 MFMA rows), whose Q and dO are staged
+//              in LDS twice, row-major for S = Q K^T and dP = dO V^T and
 //              transposed for dV += P^T dO and dK += dS^T Q, so the P and dS
 //              registers of the first two products are directly the A
 //              operands of the last two.  dK and dV accumulate over the
