@@ -54,7 +54,7 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--profile", choices=["prefill_tile", "decode", "copy"],
+    ap.add_argument("--profile", choices=["prefill_tile", "train_tile", "decode", "copy"],
                     help="run one workload a few times for hardware-counter collection and exit "
                          "(prefill_tile: the last 8192-query call of the 128K prefill; decode: one "
                          "decode step of the 1M-context batch; copy: a 1 GiB device-to-device copy "
@@ -473,6 +473,28 @@ def profile_run(args, msa, synth, torch):
                                         wl.block_size, wl.topk)
         torch.cuda.synchronize()
         print(f"profile prefill_tile: rows [{lo}, {hi}) x {args.profile_reps}", flush=True)
+        return
+    if args.profile == "train_tile":
+        # the last 8192-row tile of the 128K prefill: forward with block LSEs,
+        # backward of the main branch and the index KL loss
+        wl = synth.WORKLOADS["prefill_128k"]
+        inp = synth.prefill_inputs(wl, device="cuda", seed=0)
+        lo, hi = wl.seq_len - wl.q_tile, wl.seq_len
+        m = hi - lo
+        cu_q = torch.tensor([0, m], dtype=torch.int32, device="cuda")
+        cu_k = torch.tensor([0, hi], dtype=torch.int32, device="cuda")
+        dout = synth.normal((m, wl.num_heads, wl.head_dim), torch.bfloat16, "cuda", 0, "dout")
+        blse = torch.empty((m, wl.num_heads, wl.topk), dtype=torch.float32, device="cuda")
+        for _ in range(args.profile_reps):
+            ids = msa.msa_index_topk(inp["q_idx"][lo:hi], inp["k_idx"], cu_q, cu_k, m, hi, wl.block_size, wl.topk)
+            out, lse = msa.msa_sparse_attn_prefill_ex(inp["q"][lo:hi], inp["k"], inp["v"], ids, cu_q, cu_k, m, hi,
+                                                      wl.block_size, wl.topk, block_lse=blse)
+            msa.msa_sparse_attn_backward(inp["q"][lo:hi], inp["k"], inp["v"], out, dout, lse, ids, cu_q, cu_k, m, hi,
+                                         wl.block_size, wl.topk)
+            msa.msa_index_kl_backward(inp["q_idx"][lo:hi], inp["k_idx"], ids, lse, blse, cu_q, cu_k, m, hi,
+                                      wl.block_size, wl.topk)
+        torch.cuda.synchronize()
+        print(f"profile train_tile: rows [{lo}, {hi}) x {args.profile_reps}", flush=True)
         return
     wd = synth.WORKLOADS["decode_1m"]
     ctx = synth.decode_ctx_lens(wd, 0)
