@@ -533,7 +533,7 @@ def cpu_baseline(target_s: float):
                        inp["cu_k_host"], wl.block_size, wl.topk, rows=rows)
         return time.perf_counter() - t0
 
-    n0 = max(8, threads)
+    n0 = max(64, 8 * threads)  # enough rows that per-call overheads do not skew the calibration
     t_cal = run(n0)
     n = int(max(n0, min(8192, n0 * target_s / max(t_cal, 1e-3))))
     t = run(n)
