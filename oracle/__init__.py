@@ -21,6 +21,10 @@ record of MiniMax M3 (atlas.lewiswon.me), summary paragraph:
   recomputed from the inputs.
 * ``block_lse``: the main branch's LSE over each selected block's attended
   keys, per (row, head, selection slot).
+* ``index_frontend``: the index branch's front end, hidden states through a
+  linear projection, a norm and RoPE to the index-query heads and the shared
+  index-key head (Figure 1 of the first page; the norm's kind and the rotary
+  base are readings, written out in ``msa_oracle.c``).
 * ``index_kl``: the KL alignment loss of the index branch (the index scores of
   the selected blocks against the group-averaged share of main attention in
   each block) and its gradients with respect to q_idx and k_idx.
@@ -93,6 +97,10 @@ def _load():
         lib.oracle_index_kl.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, i64p, i64p, i32p,
                                         ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_double, vp, vp, vp]
+        lib.oracle_index_frontend.restype = ctypes.c_int
+        lib.oracle_index_frontend.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, i64p, ctypes.c_int64, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                              ctypes.c_double, vp, vp]
         _lib = lib
     return _lib
 
@@ -305,6 +313,32 @@ def index_kl(q_idx, k_idx, q, k, sel, kstart, pos, rows, block_size: int, topk: 
     if rc != 0:
         raise ValueError(f"oracle_index_kl failed ({rc})")
     return loss, dq, dk
+
+
+def index_frontend(x, w_q, w_k, gain_q, gain_k, pos, num_groups: int, d_idx: int, rope_dim: int,
+                   theta: float, eps: float):
+    """Index front-end of n tokens at absolute positions ``pos``:
+    (q_idx [n, G, d_idx], k_idx [n, d_idx]), fp64."""
+    lib = _load()
+    xa, xt = _host_array(x)
+    wqa, wqt = _host_array(w_q)
+    wka, wkt = _host_array(w_k)
+    if not (xt == wqt == wkt) or xt == 2:
+        raise TypeError("x, w_q and w_k must share a dtype (fp32 or bf16)")
+    n, d_model = xa.shape
+    G, DI = int(num_groups), int(d_idx)
+    if wqa.shape != (G * DI, d_model) or wka.shape != (DI, d_model):
+        raise ValueError("projection shapes do not match")
+    gq = np.ascontiguousarray(np.asarray(gain_q, dtype=np.float64).reshape(DI))
+    gk = np.ascontiguousarray(np.asarray(gain_k, dtype=np.float64).reshape(DI))
+    pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int64).reshape(n))
+    q = np.empty((n, G, DI), dtype=np.float64)
+    k = np.empty((n, DI), dtype=np.float64)
+    rc = lib.oracle_index_frontend(_ptr(xa), _ptr(wqa), _ptr(wka), xt, _ptr(gq), _ptr(gk), _ptr(pos), n, d_model,
+                                   G, DI, int(rope_dim), float(theta), float(eps), _ptr(q), _ptr(k))
+    if rc != 0:
+        raise ValueError(f"oracle_index_frontend failed ({rc})")
+    return q, k
 
 
 def prefill(q_idx, k_idx, q, k, v, cu_seqlens_q, cu_seqlens_k, block_size: int, topk: int,

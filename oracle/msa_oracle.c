@@ -518,3 +518,78 @@ int oracle_index_kl(const void* q_idx, const void* k_idx, int idx_dtype, const v
   free(blse);
   return bad;
 }
+
+/* Index front-end: [P4] Figure 1 caption (the index branch takes the hidden
+ * states through a linear projection, a norm and RoPE to its index-query
+ * heads, one per GQA group, and its single shared index-key head, [P5]
+ * summary paragraph).  The pages give the order of the three steps, the model
+ * width (3072) and, for the main heads, a rotary width of half the 128-dim
+ * head ([P5] provenance, section 5.1); the norm's kind and the rotary base are
+ * not given.  Readings, for every head vector separately:
+ *   projection : y = W_h x, W_h the DI rows of head h, no bias;
+ *   norm       : y_i <- gain_i * y_i / sqrt(mean_i(y_i^2) + eps) over the DI
+ *                values (one gain vector for the query heads, one for the key
+ *                head);
+ *   RoPE       : for i < rope_dim/2 the pair (y_i, y_{i+rope_dim/2}) is turned
+ *                by the angle p * theta^(-2i/rope_dim), p the token's absolute
+ *                position: (a, b) -> (a cos - b sin, b cos + a sin); values at
+ *                i >= rope_dim pass through.
+ * Everything in fp64 after an exact widening of x and W. */
+int oracle_index_frontend(const void* x, const void* w_q, const void* w_k, int dtype, const double* gain_q,
+                          const double* gain_k, const int64_t* pos, int64_t n, int d_model, int G, int DI,
+                          int rope_dim, double theta, double eps, double* q_idx, double* k_idx) {
+  if (n < 0 || d_model <= 0 || G <= 0 || DI <= 0 || rope_dim < 0 || rope_dim > DI || (rope_dim & 1) ||
+      !(theta > 0.0) || !(eps >= 0.0))
+    return 1;
+  /* widen the G+1 heads' weight rows once: row h*DI + i of wd is row i of head h */
+  const int64_t wrows = (int64_t)(G + 1) * DI;
+  double* wd = malloc((size_t)wrows * d_model * sizeof(double));
+  if (!wd) return 2;
+  for (int64_t rw = 0; rw < wrows; ++rw) {
+    const void* w = rw < (int64_t)G * DI ? w_q : w_k;
+    const int64_t src = rw < (int64_t)G * DI ? rw : rw - (int64_t)G * DI;
+    for (int c = 0; c < d_model; ++c) wd[rw * d_model + c] = (double)load_elem(w, dtype, src * d_model + c);
+  }
+  const int half = rope_dim / 2;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double* xr = malloc((size_t)d_model * sizeof(double));
+    double* y = malloc((size_t)DI * sizeof(double));
+    if (!xr || !y) {
+#pragma omp atomic write
+      bad = 2;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t r = 0; r < n; ++r) {
+      if (!xr || !y) continue;
+      for (int c = 0; c < d_model; ++c) xr[c] = (double)load_elem(x, dtype, r * d_model + c);
+      for (int h = 0; h <= G; ++h) {
+        for (int i = 0; i < DI; ++i) {
+          const double* wrow = wd + ((int64_t)h * DI + i) * d_model;
+          double s = 0.0;
+          for (int c = 0; c < d_model; ++c) s += wrow[c] * xr[c];
+          y[i] = s;
+        }
+        double ms = 0.0;
+        for (int i = 0; i < DI; ++i) ms += y[i] * y[i];
+        const double inv = 1.0 / sqrt(ms / DI + eps);
+        const double* gain = h < G ? gain_q : gain_k;
+        for (int i = 0; i < DI; ++i) y[i] = gain[i] * (y[i] * inv);
+        for (int i = 0; i < half; ++i) {
+          const double ang = (double)pos[r] * pow(theta, -2.0 * i / rope_dim);
+          const double cs = cos(ang), sn = sin(ang);
+          const double a = y[i], b = y[i + half];
+          y[i] = a * cs - b * sn;
+          y[i + half] = b * cs + a * sn;
+        }
+        double* out = h < G ? q_idx + (r * G + h) * DI : k_idx + r * DI;
+        memcpy(out, y, (size_t)DI * sizeof(double));
+      }
+    }
+    free(xr);
+    free(y);
+  }
+  free(wd);
+  return bad;
+}

@@ -106,6 +106,20 @@ int oracle_index_kl(const void* q_idx, const void* k_idx, int idx_dtype, const v
                     int DI, int Hq, int D, int Bk, int topk, double scale, double* loss, double* dq_idx,
                     double* dk_idx);
 
+/* Index front-end for n tokens (the definition and its readings are written
+ * out in msa_oracle.c): hidden states -> projection -> RMS norm -> RoPE.
+ *   x      : [n][d_model]        hidden states (dtype)
+ *   w_q    : [G*DI][d_model]     index-query projection rows, head g = rows g*DI..
+ *   w_k    : [DI][d_model]       index-key projection rows
+ *   gain_q, gain_k : [DI]        norm gains
+ *   pos    : [n]                 absolute position of each token
+ *   q_idx  : [n][G][DI] fp64 out,  k_idx : [n][DI] fp64 out
+ * Returns 0, 1 on a bad argument (rope_dim odd or > DI, theta <= 0, eps < 0),
+ * 2 when out of memory. */
+int oracle_index_frontend(const void* x, const void* w_q, const void* w_k, int dtype, const double* gain_q,
+                          const double* gain_k, const int64_t* pos, int64_t n, int d_model, int G, int DI,
+                          int rope_dim, double theta, double eps, double* q_idx, double* k_idx);
+
 /* Decode n E4M3 bit patterns to fp32 (exact), for checking the decoder. */
 void oracle_decode_e4m3(const uint8_t* in, float* out, int64_t n);
 
