@@ -54,9 +54,11 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--profile", choices=["prefill_tile", "train_tile", "decode", "copy"],
+    ap.add_argument("--profile", choices=["prefill_tile", "train_tile", "frontend", "decode", "copy"],
                     help="run one workload a few times for hardware-counter collection and exit "
-                         "(prefill_tile: the last 8192-query call of the 128K prefill; decode: one "
+                         "(prefill_tile: the last 8192-query call of the 128K prefill; train_tile: that "
+                         "tile's forward, backward and KL loss; frontend: the index front-end over all "
+                         "128K tokens; decode: one "
                          "decode step of the 1M-context batch; copy: a 1 GiB device-to-device copy "
                          "that calibrates the byte counters)")
     ap.add_argument("--profile-reps", type=int, default=3)
@@ -441,6 +443,35 @@ def main():
                                      "algorithmic_flops": kl_flops}
     del inp, calls, q8, k8, kv8, vv8, kl_loss, kl_dq, kl_dk, ws_kl
     torch.cuda.empty_cache()
+    # The index front-end (an extra measurement): the whole 128K sequence's
+    # hidden states through the index projections, RMS norm and RoPE in one
+    # call (q_idx for every token, the index-key rows of every position).
+    fe = synth.frontend_inputs(L, G, DI, synth.D_MODEL, torch.bfloat16, dev, 0)
+    cu_fe = torch.tensor([0, L], dtype=torch.int32, device=dev)
+    fe_q = torch.empty((L, G, DI), dtype=torch.bfloat16, device=dev)
+    fe_k = torch.empty((L, DI), dtype=torch.bfloat16, device=dev)
+
+    def fe_step():
+        msa.msa_index_frontend(fe["x"], fe["w_q"], fe["w_k"], fe["gain_q"], fe["gain_k"], cu_fe, cu_fe, G,
+                               rope_dim=64, q_idx=fe_q, k_idx=fe_k, stream=stream)
+
+    fe_step()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        fe_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fe_ms = e0.elapsed_time(e1) / args.steps
+    fe_flops = 2.0 * L * synth.D_MODEL * (G + 1) * DI
+    fe_bytes = 2.0 * (L * synth.D_MODEL + (G + 1) * DI * synth.D_MODEL + L * (G + 1) * DI)
+    result["prefill"]["index_frontend"] = {
+        "ms": round(fe_ms, 3), "tflops": round(fe_flops / (fe_ms / 1e3) / 1e12, 1),
+        "frac_mfma": round(fe_flops / (fe_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "algorithmic_flops": fe_flops, "bytes": fe_bytes, "GBs": round(fe_bytes / (fe_ms / 1e3) / 1e9, 1),
+        "d_model": synth.D_MODEL, "tokens": L}
+    del fe, fe_q, fe_k
+    torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU baseline
     if not args.no_cpu_baseline:
@@ -495,6 +526,19 @@ def profile_run(args, msa, synth, torch):
                                       wl.block_size, wl.topk)
         torch.cuda.synchronize()
         print(f"profile train_tile: rows [{lo}, {hi}) x {args.profile_reps}", flush=True)
+        return
+    if args.profile == "frontend":
+        wl = synth.WORKLOADS["prefill_128k"]
+        L, G, DI = wl.seq_len, wl.num_kv_heads, wl.index_dim
+        fe = synth.frontend_inputs(L, G, DI, synth.D_MODEL, torch.bfloat16, "cuda", 0)
+        cu = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+        q_idx = torch.empty((L, G, DI), dtype=torch.bfloat16, device="cuda")
+        k_idx = torch.empty((L, DI), dtype=torch.bfloat16, device="cuda")
+        for _ in range(args.profile_reps):
+            msa.msa_index_frontend(fe["x"], fe["w_q"], fe["w_k"], fe["gain_q"], fe["gain_k"], cu, cu, G,
+                                   rope_dim=64, q_idx=q_idx, k_idx=k_idx)
+        torch.cuda.synchronize()
+        print(f"profile frontend: {L} tokens x {args.profile_reps}", flush=True)
         return
     wd = synth.WORKLOADS["decode_1m"]
     ctx = synth.decode_ctx_lens(wd, 0)

@@ -323,6 +323,52 @@ msa_status_t msa_index_kl_backward(const void* q_idx, const void* k_idx, msa_dty
                                    int block_size, int topk, float* loss, float* dq_idx, float* dk_idx,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ----------------------------------------------------------------------
+ * Index front-end: hidden states -> index-query heads and index-key head.
+ *
+ * "MiniMax Sparse Attention: let each query pick its own blocks", Figure 1:
+ * the index branch passes the hidden states through a linear projection, a
+ * norm and RoPE before the score matrix.  The atlas record of MiniMax M3
+ * (provenance notes on section 5.1) gives the model width (3072) and a rotary
+ * width of 64 of the 128 head dims for the main heads; the pages name neither
+ * the norm's kind nor the rotary base.  This call computes, per token and per
+ * head vector (G query heads, then the key head):
+ *   y   = W_h x                               (no bias)
+ *   y_i = gain_i * y_i / sqrt(mean_i y_i^2 + norm_eps)   (RMS norm per head)
+ *   for i < rope_dim/2, the pair (y_i, y_{i + rope_dim/2}) turned by the angle
+ *   p * rope_theta^(-2i/rope_dim): (a, b) -> (a cos - b sin, b cos + a sin);
+ *   dims >= rope_dim are left as they are.
+ * p is the token's absolute position, p = N - M + t for token t of a sequence
+ * with q_len M and kv_len N (the convention of the other calls).
+ *
+ *   x                     [total_q, d_model] hidden states of the new tokens,
+ *                         packed by cu_seqlens_q (dtype fp32 or bf16)
+ *   w_q                   [num_groups * index_dim, d_model]: rows g*index_dim ..
+ *                         (g+1)*index_dim-1 project to the query head of group g
+ *   w_k                   [index_dim, d_model]: the shared key head
+ *   q_norm_weight         [index_dim] fp32 gain of the query heads' norm
+ *   k_norm_weight         [index_dim] fp32 gain of the key head's norm
+ *   cu_seqlens_q/_k       device [batch+1] int32; cu_seqlens_q[batch] must equal
+ *                         total_q
+ *   q_idx                 out [total_q, num_groups, index_dim] (out_dtype)
+ *   k_idx                 out: the index-key rows of the new tokens, written at
+ *                         row cu_seqlens_k[b] + p (the caller's index-key cache
+ *                         laid out as msa_index_topk reads it: in a decode step
+ *                         with M = 1 this appends the new token's key at
+ *                         position N - 1; rows of other positions are not
+ *                         touched; a token with p < 0 writes no key row)
+ *   out_dtype             fp32 or bf16 (the type msa_index_topk then reads)
+ * Sizes: index_dim 64 or 128, d_model a multiple of 64, rope_dim 0, 64 or (for
+ * index_dim 128) 128; others return MSA_ERR_UNSUPPORTED.  fp32 accumulation;
+ * the angle is reduced in fp64.  No workspace; deterministic.
+ * ---------------------------------------------------------------------- */
+msa_status_t msa_index_frontend(const void* x, const void* w_q, const void* w_k, msa_dtype_t dtype,
+                                const float* q_norm_weight, const float* k_norm_weight,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                                int64_t total_q, int d_model, int num_groups, int index_dim, int rope_dim,
+                                float rope_theta, float norm_eps, void* q_idx, void* k_idx,
+                                msa_dtype_t out_dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

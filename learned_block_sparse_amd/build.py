@@ -12,7 +12,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["msa_api.hip", "index_topk.hip", "sparse_attn.hip", "sparse_attn_kvouter.hip", "sparse_attn_bwd.hip", "index_kl.hip"]
+SOURCES = ["msa_api.hip", "index_topk.hip", "sparse_attn.hip", "sparse_attn_kvouter.hip", "sparse_attn_bwd.hip", "index_kl.hip",
+           "index_frontend.hip"]
 LIB = os.path.join(PKG, "libmsa.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 

@@ -326,4 +326,43 @@ msa_status_t msa_index_kl_backward(const void* q_idx, const void* k_idx, msa_dty
   return hip_status(launch_index_kl(pl, (int)dtype, index_dim, x, workspace, stream));
 }
 
+msa_status_t msa_index_frontend(const void* x, const void* w_q, const void* w_k, msa_dtype_t dtype,
+                                const float* q_norm_weight, const float* k_norm_weight,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                                int64_t total_q, int d_model, int num_groups, int index_dim, int rope_dim,
+                                float rope_theta, float norm_eps, void* q_idx, void* k_idx,
+                                msa_dtype_t out_dtype, hipStream_t stream) {
+  if (!x || !w_q || !w_k || !q_norm_weight || !k_norm_weight || !cu_seqlens_q || !cu_seqlens_k || !q_idx ||
+      !k_idx)
+    return MSA_ERR_INVALID_ARG;
+  if (batch <= 0 || total_q < 0 || d_model <= 0 || num_groups <= 0 || index_dim <= 0 || rope_dim < 0 ||
+      rope_dim > index_dim || !(rope_theta > 0.f) || !(norm_eps >= 0.f) || !dtype_ok(dtype) ||
+      !dtype_ok(out_dtype))
+    return MSA_ERR_INVALID_ARG;
+  if ((dtype != MSA_F32 && dtype != MSA_BF16) || (out_dtype != MSA_F32 && out_dtype != MSA_BF16) ||
+      (index_dim != 64 && index_dim != 128) || d_model % 64 != 0 || rope_dim % 64 != 0 || num_groups > 65535)
+    return MSA_ERR_UNSUPPORTED;
+  FrontendLaunch f;
+  f.x = x;
+  f.w_q = w_q;
+  f.w_k = w_k;
+  f.gain_q = q_norm_weight;
+  f.gain_k = k_norm_weight;
+  f.cu_q = cu_seqlens_q;
+  f.cu_k = cu_seqlens_k;
+  f.batch = batch;
+  f.G = num_groups;
+  f.DI = index_dim;
+  f.d_model = d_model;
+  f.rope_dim = rope_dim;
+  f.total = total_q;
+  f.theta = rope_theta;
+  f.eps = norm_eps;
+  f.in_f32 = dtype == MSA_F32;
+  f.out_f32 = out_dtype == MSA_F32;
+  f.q_out = q_idx;
+  f.k_out = k_idx;
+  return hip_status(launch_index_frontend(f, stream));
+}
+
 }  // extern "C"

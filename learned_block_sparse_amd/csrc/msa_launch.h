@@ -134,4 +134,22 @@ struct KlLaunch {
 };
 hipError_t launch_index_kl(const KlPlan& pl, int dtype, int DI, const KlLaunch& x, void* ws, hipStream_t st);
 
+// Index front-end: projection + RMS norm + RoPE (no workspace).
+struct FrontendLaunch {
+  const void* x;              // [T, d_model]
+  const void* w_q;            // [G*DI, d_model]
+  const void* w_k;            // [DI, d_model]
+  const float* gain_q;        // [DI]
+  const float* gain_k;        // [DI]
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int batch, G, DI, d_model, rope_dim;
+  int64_t total;              // T
+  float theta, eps;
+  bool in_f32, out_f32;
+  void* q_out;                // [T, G, DI]
+  void* k_out;                // key rows at cu_k[b] + p
+};
+hipError_t launch_index_frontend(const FrontendLaunch& f, hipStream_t st);
+
 }  // namespace msa

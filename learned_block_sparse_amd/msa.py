@@ -79,6 +79,9 @@ def lib():
         L.msa_index_kl_backward.restype = i32
         L.msa_index_kl_backward.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                             vp, vp, vp, vp, sz, vp]
+        L.msa_index_frontend.restype = i32
+        L.msa_index_frontend.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, ctypes.c_int64, i32, i32, i32, i32,
+                                         ctypes.c_float, ctypes.c_float, vp, vp, i32, vp]
         _lib = L
     return _lib
 
@@ -313,3 +316,35 @@ def msa_index_kl_backward(q_idx, k_idx, block_idx, lse, block_lse, cu_seqlens_q,
         ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
     _check(st, "msa_index_kl_backward")
     return loss, dq_idx, dk_idx
+
+
+def msa_index_frontend(x, w_q, w_k, q_norm_weight, k_norm_weight, cu_seqlens_q, cu_seqlens_k, num_groups: int,
+                       rope_dim: int = 64, rope_theta: float = 10000.0, norm_eps: float = 1e-6, out_dtype=None,
+                       q_idx=None, k_idx=None, num_keys=None, stream=None):
+    """Index front-end: ``x [T, d_model]`` through the projections ``w_q
+    [G*d_idx, d_model]`` / ``w_k [d_idx, d_model]``, the RMS norm (fp32 gains
+    ``[d_idx]``) and RoPE on the first ``rope_dim`` dims.  Returns ``(q_idx
+    [T, G, d_idx], k_idx)``; the new tokens' key rows are written into
+    ``k_idx`` at ``cu_seqlens_k[b] + position`` (pass the index-key cache to
+    append to it; otherwise a zero tensor of ``num_keys`` rows is made, by
+    default ``cu_seqlens_k[-1]``, read from the device)."""
+    t, d_model = x.shape
+    di = w_k.shape[0]
+    G = int(num_groups)
+    batch = cu_seqlens_q.numel() - 1
+    odt = x.dtype if out_dtype is None else out_dtype
+    if q_idx is None:
+        q_idx = torch.empty((t, G, di), dtype=odt, device=x.device)
+    if k_idx is None:
+        rows = int(cu_seqlens_k[-1].item()) if num_keys is None else int(num_keys)
+        k_idx = torch.zeros((rows, di), dtype=odt, device=x.device)
+    if q_idx.dtype != k_idx.dtype:
+        raise TypeError("q_idx and k_idx must share a dtype")
+    st = lib().msa_index_frontend(
+        _dev(x, "x"), _dev(w_q, "w_q", x.dtype), _dev(w_k, "w_k", x.dtype), _dtype_code(x),
+        _dev(q_norm_weight, "q_norm_weight", torch.float32), _dev(k_norm_weight, "k_norm_weight", torch.float32),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32), batch, t,
+        d_model, G, di, int(rope_dim), float(rope_theta), float(norm_eps), _dev(q_idx, "q_idx"), _dev(k_idx, "k_idx"),
+        _dtype_code(q_idx), _stream(stream))
+    _check(st, "msa_index_frontend")
+    return q_idx, k_idx

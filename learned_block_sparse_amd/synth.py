@@ -18,6 +18,11 @@ query / 4 KV heads, head dim 128, block 128, k = 16, contexts from 32K to 1M):
   every index-key element of each of their tokens; values stay multiples of
   1/8, so exactness is kept.  This makes a few blocks "hot", as the pages note
   real selections have (a first-token sink emerges).
+* Index front-end (hidden states -> index heads): d_model = 3072 (the
+  testbed's stated width, atlas record of MiniMax M3); hidden states
+  ~ N(0, 1); projection weights ~ N(0, 1/d_model) (so projected values are
+  about N(0, 1)); norm gains uniform on [0.5, 1.5] in fp32.  Synthetic
+  weights: the pages publish none.
 * Decode: one new token per sequence, context lengths uniform on
   [65536, 1048576]; the caches are packed one sequence after another.
 
@@ -75,7 +80,8 @@ WORKLOADS = {
         notes="batch 1, L=1048576 in 8192-query tiles, 256 planted blocks"),
 }
 
-_TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "q_idx": 4, "k_idx": 5, "planted": 6, "ctx": 7, "dout": 8}
+_TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "q_idx": 4, "k_idx": 5, "planted": 6, "ctx": 7, "dout": 8,
+               "hidden": 9, "w_q_idx": 10, "w_k_idx": 11, "gain_q_idx": 12, "gain_k_idx": 13}
 _CHUNK_ELEMS = 1 << 28  # draw big tensors in pieces to bound fp32 temporaries
 
 
@@ -206,3 +212,22 @@ def decode_inputs(wl: Workload, device="cpu", seed: int = 0, ctx_lens=None):
     out["planted"] = plant_blocks(out["k_idx"], offs[:-1], ctx_lens, wl.planted, seed,
                                   wl.block_size) if wl.planted else []
     return out
+
+
+D_MODEL = 3072
+
+
+def frontend_inputs(num_tokens: int, num_groups: int = 4, index_dim: int = 128, d_model: int = D_MODEL,
+                    dtype=torch.bfloat16, device="cpu", seed: int = 0):
+    """Hidden states and synthetic index front-end weights: ``x [T, d_model]``,
+    ``w_q [G*d_idx, d_model]``, ``w_k [d_idx, d_model]``, fp32 gains
+    ``[d_idx]`` each."""
+    x = normal((num_tokens, d_model), dtype, device, seed, "hidden")
+    sc = d_model ** -0.5
+    w_q = (normal((num_groups * index_dim, d_model), torch.float32, device, seed, "w_q_idx") * sc).to(dtype)
+    w_k = (normal((index_dim, d_model), torch.float32, device, seed, "w_k_idx") * sc).to(dtype)
+    gains = []
+    for name in ("gain_q_idx", "gain_k_idx"):
+        g = _gen(device, seed, name)
+        gains.append(torch.rand((index_dim,), generator=g, device=device, dtype=torch.float32) + 0.5)
+    return {"x": x, "w_q": w_q, "w_k": w_k, "gain_q": gains[0], "gain_k": gains[1]}

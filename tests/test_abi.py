@@ -126,3 +126,30 @@ def test_decode_argument_errors(L):
     bad = list(args)
     bad[11] = 96                                     # head_dim
     assert L.msa_sparse_attn_decode(*bad) == 2
+
+
+def _frontend(L, **kw):
+    a = dict(x=FAKE, wq=FAKE, wk=FAKE, dtype=1, gq=FAKE, gk=FAKE, cuq=FAKE, cuk=FAKE, batch=1, total=256,
+             dm=3072, G=4, DI=128, rope=64, theta=10000.0, eps=1e-6, q=FAKE, k=FAKE, odt=1, stream=None)
+    a.update(kw)
+    return L.msa_index_frontend(a["x"], a["wq"], a["wk"], a["dtype"], a["gq"], a["gk"], a["cuq"], a["cuk"],
+                                a["batch"], a["total"], a["dm"], a["G"], a["DI"], a["rope"], a["theta"], a["eps"],
+                                a["q"], a["k"], a["odt"], a["stream"])
+
+
+def test_frontend_argument_errors(L):
+    assert _frontend(L, x=None) == 1
+    assert _frontend(L, gk=None) == 1
+    assert _frontend(L, total=-1) == 1
+    assert _frontend(L, rope=130) == 1       # wider than the head
+    assert _frontend(L, theta=0.0) == 1
+    assert _frontend(L, eps=-1.0) == 1
+    assert _frontend(L, dtype=7) == 1
+    assert _frontend(L, dtype=2) == 2        # fp8 hidden states
+    assert _frontend(L, odt=2) == 2
+    assert _frontend(L, DI=96) == 2
+    assert _frontend(L, dm=3000) == 2        # not a multiple of 64
+    assert _frontend(L, rope=32) == 2
+    assert _frontend(L, DI=64, rope=128) == 1
+    # no tokens: nothing to launch
+    assert _frontend(L, total=0) == 0
