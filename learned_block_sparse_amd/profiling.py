@@ -33,11 +33,13 @@ CALLS = {
     "index_decode_1m": ("_ZN3msa17idx_decode_scores", "idx_decode_scores", "idx_decode_select"),
     "attention_decode_1m": ("_ZN3msa15sparse_attn_fwd", "sparse_attn_fwd", "_ZN3msa12attn_combine",
                             "attn_combine"),
+    "index_frontend_128k": ("_ZN3msa14index_frontend", "index_frontend"),
 }
 # the call's first kernel marks a new call
 CALL_START = {"attention_prefill_128k": "kvo_zero", "attention_prefill_128k_fp8kv": "kvo_zero",
               "index_prefill_128k": "idx_scan_prefill", "index_prefill_128k_fp8": "idx_scan_prefill",
-              "index_decode_1m": "idx_decode_scores", "attention_decode_1m": "sparse_attn_fwd"}
+              "index_decode_1m": "idx_decode_scores", "attention_decode_1m": "sparse_attn_fwd",
+              "index_frontend_128k": "index_frontend"}
 
 
 def _is_bf16(name):
@@ -131,7 +133,8 @@ def main():
                "index_prefill_128k_fp8": ("prefill-fetch", "prefill-write"),
                "attention_prefill_128k_fp8kv": ("prefill-fetch", "prefill-write"),
                "index_decode_1m": ("decode-fetch", "decode-write"),
-               "attention_decode_1m": ("decode-fetch", "decode-write")}
+               "attention_decode_1m": ("decode-fetch", "decode-write"),
+               "index_frontend_128k": ("prefill-fetch", "prefill-write")}
     digest = build.source_digest()
     for call, (fd, wd) in sources.items():
         fr = _rows(getattr(args, fd.replace("-", "_")))
