@@ -24,7 +24,8 @@ record of MiniMax M3 (atlas.lewiswon.me), summary paragraph:
 * ``index_frontend``: the index branch's front end, hidden states through a
   linear projection, a norm and RoPE to the index-query heads and the shared
   index-key head (Figure 1 of the first page; the norm's kind and the rotary
-  base are readings, written out in ``msa_oracle.c``).
+  base are readings, written out in ``msa_oracle.c``); ``index_frontend_bwd``:
+  its gradients with respect to the projections and the norm gains.
 * ``index_kl``: the KL alignment loss of the index branch (the index scores of
   the selected blocks against the group-averaged share of main attention in
   each block) and its gradients with respect to q_idx and k_idx.
@@ -101,6 +102,10 @@ def _load():
         lib.oracle_index_frontend.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, i64p, ctypes.c_int64, ctypes.c_int,
                                               ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                               ctypes.c_double, vp, vp]
+        lib.oracle_index_frontend_bwd.restype = ctypes.c_int
+        lib.oracle_index_frontend_bwd.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, i64p, ctypes.c_int64,
+                                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.c_double, ctypes.c_double, vp, vp, vp, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -339,6 +344,38 @@ def index_frontend(x, w_q, w_k, gain_q, gain_k, pos, num_groups: int, d_idx: int
     if rc != 0:
         raise ValueError(f"oracle_index_frontend failed ({rc})")
     return q, k
+
+
+def index_frontend_bwd(x, w_q, w_k, gain_q, gain_k, pos, num_groups: int, d_idx: int, rope_dim: int,
+                       theta: float, eps: float, dq, dk):
+    """Parameter gradients of the index front-end for upstream gradients
+    ``dq [n, G, d_idx]`` and ``dk [n, d_idx]`` (one key row per token): (dw_q,
+    dw_k, dgain_q, dgain_k), fp64; x is held constant."""
+    lib = _load()
+    xa, xt = _host_array(x)
+    wqa, wqt = _host_array(w_q)
+    wka, wkt = _host_array(w_k)
+    if not (xt == wqt == wkt) or xt == 2:
+        raise TypeError("x, w_q and w_k must share a dtype (fp32 or bf16)")
+    n, d_model = xa.shape
+    G, DI = int(num_groups), int(d_idx)
+    if wqa.shape != (G * DI, d_model) or wka.shape != (DI, d_model):
+        raise ValueError("projection shapes do not match")
+    gq = np.ascontiguousarray(np.asarray(gain_q, dtype=np.float64).reshape(DI))
+    gk = np.ascontiguousarray(np.asarray(gain_k, dtype=np.float64).reshape(DI))
+    pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int64).reshape(n))
+    dqa = np.ascontiguousarray(np.asarray(dq, dtype=np.float64).reshape(n, G, DI))
+    dka = np.ascontiguousarray(np.asarray(dk, dtype=np.float64).reshape(n, DI))
+    dwq = np.empty((G * DI, d_model), dtype=np.float64)
+    dwk = np.empty((DI, d_model), dtype=np.float64)
+    dgq = np.empty(DI, dtype=np.float64)
+    dgk = np.empty(DI, dtype=np.float64)
+    rc = lib.oracle_index_frontend_bwd(_ptr(xa), _ptr(wqa), _ptr(wka), xt, _ptr(gq), _ptr(gk), _ptr(pos), n,
+                                       d_model, G, DI, int(rope_dim), float(theta), float(eps), _ptr(dqa), _ptr(dka),
+                                       _ptr(dwq), _ptr(dwk), _ptr(dgq), _ptr(dgk))
+    if rc != 0:
+        raise ValueError(f"oracle_index_frontend_bwd failed ({rc})")
+    return dwq, dwk, dgq, dgk
 
 
 def prefill(q_idx, k_idx, q, k, v, cu_seqlens_q, cu_seqlens_k, block_size: int, topk: int,

@@ -593,3 +593,110 @@ int oracle_index_frontend(const void* x, const void* w_q, const void* w_k, int d
   free(wd);
   return bad;
 }
+
+/* Gradients of the index front-end with respect to its parameters, for
+ * upstream gradients dq (of q_idx) and dk (of k_idx).  The indexer's input x
+ * is held constant ([P5] summary: the alignment loss reaches only the index
+ * projections, through a stop-gradient on the indexer's input), so there is
+ * no dx.  Per head vector, with n = y / r, r = sqrt(mean(y^2) + eps),
+ * z = gain * n and out = R z (R the rotation written out above):
+ *   dz      = R^T dout                       (each pair turned back by -angle)
+ *   dgain  += dz * n
+ *   dn      = dz * gain
+ *   dy      = (dn - n * (dn . n) / DI) / r
+ *   dW_h   += dy x^T
+ * All in fp64.  dw_q [G*DI][d_model], dw_k [DI][d_model], dgain_q [DI],
+ * dgain_k [DI] are overwritten. */
+int oracle_index_frontend_bwd(const void* x, const void* w_q, const void* w_k, int dtype, const double* gain_q,
+                              const double* gain_k, const int64_t* pos, int64_t n, int d_model, int G, int DI,
+                              int rope_dim, double theta, double eps, const double* dq, const double* dk,
+                              double* dw_q, double* dw_k, double* dgain_q, double* dgain_k) {
+  if (n < 0 || d_model <= 0 || G <= 0 || DI <= 0 || rope_dim < 0 || rope_dim > DI || (rope_dim & 1) ||
+      !(theta > 0.0) || !(eps >= 0.0))
+    return 1;
+  const int64_t wrows = (int64_t)(G + 1) * DI;
+  const size_t wsize = (size_t)wrows * d_model;
+  double* wd = malloc(wsize * sizeof(double));
+  if (!wd) return 2;
+  for (int64_t rw = 0; rw < wrows; ++rw) {
+    const void* w = rw < (int64_t)G * DI ? w_q : w_k;
+    const int64_t src = rw < (int64_t)G * DI ? rw : rw - (int64_t)G * DI;
+    for (int c = 0; c < d_model; ++c) wd[rw * d_model + c] = (double)load_elem(w, dtype, src * d_model + c);
+  }
+  memset(dw_q, 0, (size_t)G * DI * d_model * sizeof(double));
+  memset(dw_k, 0, (size_t)DI * d_model * sizeof(double));
+  memset(dgain_q, 0, (size_t)DI * sizeof(double));
+  memset(dgain_k, 0, (size_t)DI * sizeof(double));
+  const int half = rope_dim / 2;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double* xr = malloc((size_t)d_model * sizeof(double));
+    double* y = malloc((size_t)DI * sizeof(double));
+    double* dz = malloc((size_t)DI * sizeof(double));
+    double* my_dw = calloc(wsize, sizeof(double));
+    double* my_dg = calloc(2 * (size_t)DI, sizeof(double));
+    if (!xr || !y || !dz || !my_dw || !my_dg) {
+#pragma omp atomic write
+      bad = 2;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t r = 0; r < n; ++r) {
+      if (!xr || !y || !dz || !my_dw || !my_dg) continue;
+      for (int c = 0; c < d_model; ++c) xr[c] = (double)load_elem(x, dtype, r * d_model + c);
+      for (int h = 0; h <= G; ++h) {
+        for (int i = 0; i < DI; ++i) {
+          const double* wrow = wd + ((int64_t)h * DI + i) * d_model;
+          double s = 0.0;
+          for (int c = 0; c < d_model; ++c) s += wrow[c] * xr[c];
+          y[i] = s;
+        }
+        double ms = 0.0;
+        for (int i = 0; i < DI; ++i) ms += y[i] * y[i];
+        const double rr = sqrt(ms / DI + eps);
+        const double* dout = h < G ? dq + (r * G + h) * DI : dk + r * DI;
+        for (int i = 0; i < DI; ++i) dz[i] = dout[i];
+        for (int i = 0; i < half; ++i) {
+          const double ang = (double)pos[r] * pow(theta, -2.0 * i / rope_dim);
+          const double cs = cos(ang), sn = sin(ang);
+          const double a = dz[i], b = dz[i + half];
+          dz[i] = a * cs + b * sn;
+          dz[i + half] = b * cs - a * sn;
+        }
+        const double* gain = h < G ? gain_q : gain_k;
+        double* dg = my_dg + (h < G ? 0 : DI);
+        double dot = 0.0;
+        for (int i = 0; i < DI; ++i) {
+          const double nv = y[i] / rr;
+          dg[i] += dz[i] * nv;
+          dot += dz[i] * gain[i] * nv;
+        }
+        double* dwh = my_dw + (int64_t)h * DI * d_model;
+        for (int i = 0; i < DI; ++i) {
+          const double nv = y[i] / rr;
+          const double dy = (dz[i] * gain[i] - nv * dot / DI) / rr;
+          double* row = dwh + (int64_t)i * d_model;
+          for (int c = 0; c < d_model; ++c) row[c] += dy * xr[c];
+        }
+      }
+    }
+#pragma omp critical
+    {
+      if (my_dw && my_dg) {
+        for (size_t i = 0; i < (size_t)G * DI * d_model; ++i) dw_q[i] += my_dw[i];
+        for (size_t i = 0; i < (size_t)DI * d_model; ++i) dw_k[i] += my_dw[(size_t)G * DI * d_model + i];
+        for (int i = 0; i < DI; ++i) {
+          dgain_q[i] += my_dg[i];
+          dgain_k[i] += my_dg[DI + i];
+        }
+      }
+    }
+    free(xr);
+    free(y);
+    free(dz);
+    free(my_dw);
+    free(my_dg);
+  }
+  free(wd);
+  return bad;
+}

@@ -120,6 +120,15 @@ int oracle_index_frontend(const void* x, const void* w_q, const void* w_k, int d
                           const double* gain_k, const int64_t* pos, int64_t n, int d_model, int G, int DI,
                           int rope_dim, double theta, double eps, double* q_idx, double* k_idx);
 
+/* Parameter gradients of the index front-end for upstream gradients dq
+ * [n][G][DI] (of q_idx) and dk [n][DI] (of each token's k_idx row), fp64; x is
+ * held constant (no dx).  dw_q [G*DI][d_model], dw_k [DI][d_model],
+ * dgain_q [DI], dgain_k [DI] are overwritten.  Same return codes. */
+int oracle_index_frontend_bwd(const void* x, const void* w_q, const void* w_k, int dtype, const double* gain_q,
+                              const double* gain_k, const int64_t* pos, int64_t n, int d_model, int G, int DI,
+                              int rope_dim, double theta, double eps, const double* dq, const double* dk,
+                              double* dw_q, double* dw_k, double* dgain_q, double* dgain_k);
+
 /* Decode n E4M3 bit patterns to fp32 (exact), for checking the decoder. */
 void oracle_decode_e4m3(const uint8_t* in, float* out, int64_t n);
 

@@ -17,7 +17,10 @@ readings.  Each test below fails for a plausible slip in the oracle:
   rotation sense, a wrong frequency exponent, dims past the rotary width
   rotated, positions relative to the chunk instead of absolute (unit vectors
   with textbook angles, a frequency of exactly one half, pass-through dims,
-  and the front-end of a chunk against the rows of the whole sequence).
+  and the front-end of a chunk against the rows of the whole sequence);
+* backward (gradients of the projections and gains, x held constant): torch
+  autograd through a front-end written independently in torch ops, and
+  central differences of the oracle's own forward.
 """
 import math
 
@@ -178,3 +181,92 @@ def test_bad_arguments_are_rejected(oracle_lib):
     for rope_dim, theta, eps in ((3, 1e4, 0.0), (10, 1e4, 0.0), (8, 0.0, 0.0), (8, 1e4, -1.0)):
         with pytest.raises(ValueError):
             oracle_lib.index_frontend(x, wq, wk, np.ones(DI), np.ones(DI), [0], G, DI, rope_dim, theta, eps)
+
+
+def _torch_frontend(x, wq, wk, gq, gk, pos, G, DI, rope_dim, theta, eps):
+    """The front-end written independently in torch ops (fp64), for autograd."""
+    import torch
+    y = torch.cat([(x @ wq.T).reshape(x.shape[0], G, DI), (x @ wk.T)[:, None, :]], dim=1)  # [n, G+1, DI]
+    n = y / torch.sqrt((y * y).mean(dim=-1, keepdim=True) + eps)
+    gain = torch.cat([gq.expand(G, DI), gk[None, :]], dim=0)
+    z = n * gain
+    if rope_dim:
+        half = rope_dim // 2
+        i = torch.arange(half, dtype=torch.float64)
+        ang = pos[:, None].double() * theta ** (-2.0 * i / rope_dim)  # [n, half]
+        c, s = torch.cos(ang)[:, None, :], torch.sin(ang)[:, None, :]
+        a, b = z[..., :half], z[..., half:rope_dim]
+        z = torch.cat([a * c - b * s, b * c + a * s, z[..., rope_dim:]], dim=-1)
+    return z[:, :G], z[:, G]
+
+
+@pytest.mark.parametrize("rope_dim", [0, 8, 16])
+def test_frontend_backward_matches_autograd(oracle_lib, rope_dim):
+    import torch
+    rng = np.random.default_rng(6)
+    n, d_model, G, DI, theta, eps = 7, 24, 3, 16, 50.0, 1e-3
+    x = rng.standard_normal((n, d_model)).astype(np.float32)
+    wq = rng.standard_normal((G * DI, d_model)).astype(np.float32)
+    wk = rng.standard_normal((DI, d_model)).astype(np.float32)
+    gq = rng.uniform(0.5, 1.5, DI)
+    gk = rng.uniform(0.5, 1.5, DI)
+    pos = np.array([0, 3, 17, 100, 5, 2, 999])
+    dq = rng.standard_normal((n, G, DI))
+    dk = rng.standard_normal((n, DI))
+    tw = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (wq, wk, gq, gk)]
+    q, k = _torch_frontend(torch.tensor(x, dtype=torch.float64), *tw, torch.tensor(pos), G, DI, rope_dim, theta, eps)
+    ((q * torch.tensor(dq)).sum() + (k * torch.tensor(dk)).sum()).backward()
+    got = oracle_lib.index_frontend_bwd(x, wq, wk, gq, gk, pos, G, DI, rope_dim, theta, eps, dq, dk)
+    for name, g, t in zip(("dw_q", "dw_k", "dgain_q", "dgain_k"), got, tw):
+        assert np.allclose(g, t.grad.numpy(), rtol=1e-10, atol=1e-10), name
+    # the forward of the torch formulation agrees with the oracle's forward too
+    rq, rk = oracle_lib.index_frontend(x, wq, wk, gq, gk, pos, G, DI, rope_dim, theta, eps)
+    assert np.allclose(q.detach().numpy(), rq, atol=1e-12) and np.allclose(k.detach().numpy(), rk, atol=1e-12)
+
+
+def test_frontend_backward_matches_finite_differences(oracle_lib):
+    """Central differences of L = sum(dq * q_idx) + sum(dk * k_idx), with the
+    oracle's own forward, at coordinates of every parameter."""
+    rng = np.random.default_rng(7)
+    n, d_model, G, DI, rope, theta, eps = 5, 16, 2, 8, 8, 30.0, 1e-2
+    x = rng.standard_normal((n, d_model))
+    wq = rng.standard_normal((G * DI, d_model))
+    wk = rng.standard_normal((DI, d_model))
+    gq = rng.uniform(0.5, 1.5, DI)
+    gk = rng.uniform(0.5, 1.5, DI)
+    pos = np.array([1, 4, 9, 33, 70])
+    dq = rng.standard_normal((n, G, DI))
+    dk = rng.standard_normal((n, DI))
+    # fp32 inputs for the oracle's loader; the perturbed copies stay fp64 until here
+    f32 = lambda a: np.asarray(a, dtype=np.float32)
+    x, wq, wk = f32(x), f32(wq), f32(wk)
+    dwq, dwk, dgq, dgk = oracle_lib.index_frontend_bwd(x, wq, wk, gq, gk, pos, G, DI, rope, theta, eps, dq, dk)
+
+    def loss(wq_, wk_, gq_, gk_):
+        q, k = oracle_lib.index_frontend(x, wq_, wk_, gq_, gk_, pos, G, DI, rope, theta, eps)
+        return float((q * dq).sum() + (k * dk).sum())
+
+    # weights: steps that are exact in fp32 (the loader reads fp32), gains: fp64
+    h = 2.0 ** -8
+    for (r, c) in ((0, 0), (5, 7), (G * DI - 1, d_model - 1)):
+        a, b = wq.copy(), wq.copy()
+        a[r, c] += h
+        b[r, c] -= h
+        fd = (loss(a, wk, gq, gk) - loss(b, wk, gq, gk)) / (2 * h)
+        assert fd == pytest.approx(dwq[r, c], rel=1e-3, abs=1e-4)
+    for (r, c) in ((0, 3), (DI - 1, 11)):
+        a, b = wk.copy(), wk.copy()
+        a[r, c] += h
+        b[r, c] -= h
+        fd = (loss(wq, a, gq, gk) - loss(wq, b, gq, gk)) / (2 * h)
+        assert fd == pytest.approx(dwk[r, c], rel=1e-3, abs=1e-4)
+    e = 1e-6
+    for i in (0, 3, DI - 1):
+        a, b = gq.copy(), gq.copy()
+        a[i] += e
+        b[i] -= e
+        assert (loss(wq, wk, a, gk) - loss(wq, wk, b, gk)) / (2 * e) == pytest.approx(dgq[i], rel=1e-6, abs=1e-8)
+        a, b = gk.copy(), gk.copy()
+        a[i] += e
+        b[i] -= e
+        assert (loss(wq, wk, gq, a) - loss(wq, wk, gq, b)) / (2 * e) == pytest.approx(dgk[i], rel=1e-6, abs=1e-8)
