@@ -470,7 +470,33 @@ def main():
         "frac_mfma": round(fe_flops / (fe_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "algorithmic_flops": fe_flops, "bytes": fe_bytes, "GBs": round(fe_bytes / (fe_ms / 1e3) / 1e9, 1),
         "d_model": synth.D_MODEL, "tokens": L}
-    del fe, fe_q, fe_k
+    # Its backward (an extra measurement): the projections' and gains'
+    # gradients for seeded upstream gradients of q_idx / k_idx, x held constant.
+    g_up = torch.Generator(device=dev)
+    g_up.manual_seed(17)
+    fe_dq = torch.randn((L, G, DI), generator=g_up, device=dev, dtype=torch.float32)
+    fe_dk = torch.randn((L, DI), generator=g_up, device=dev, dtype=torch.float32)
+    ws_feb = torch.empty(max(1, msa.msa_index_frontend_backward_workspace_size(L, synth.D_MODEL, G, DI)),
+                         dtype=torch.uint8, device=dev)
+
+    def feb_step():
+        msa.msa_index_frontend_backward(fe["x"], fe["w_q"], fe["w_k"], fe["gain_q"], fe["gain_k"], cu_fe, cu_fe, G,
+                                        fe_dq, fe_dk, rope_dim=64, workspace=ws_feb, stream=stream)
+
+    feb_step()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        feb_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    feb_ms = e0.elapsed_time(e1) / args.steps
+    # the weight-gradient contraction dW = dy^T x; y is recomputed (another fe_flops) rather than stored
+    result["prefill"]["index_frontend_backward"] = {
+        "ms": round(feb_ms, 3), "tflops": round(fe_flops / (feb_ms / 1e3) / 1e12, 1),
+        "tflops_with_recompute": round(2 * fe_flops / (feb_ms / 1e3) / 1e12, 1),
+        "algorithmic_flops": fe_flops}
+    del fe, fe_q, fe_k, fe_dq, fe_dk, ws_feb
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU baseline

@@ -360,7 +360,8 @@ msa_status_t msa_index_kl_backward(const void* q_idx, const void* k_idx, msa_dty
  *   out_dtype             fp32 or bf16 (the type msa_index_topk then reads)
  * Sizes: index_dim 64 or 128, d_model a multiple of 64, rope_dim 0, 64 or (for
  * index_dim 128) 128; others return MSA_ERR_UNSUPPORTED.  fp32 accumulation;
- * the angle is reduced in fp64.  No workspace; deterministic.
+ * the angle is reduced in fp64.  No workspace; deterministic.  With total_q 0,
+ * x, q_idx and k_idx may be null and nothing is launched.
  * ---------------------------------------------------------------------- */
 msa_status_t msa_index_frontend(const void* x, const void* w_q, const void* w_k, msa_dtype_t dtype,
                                 const float* q_norm_weight, const float* k_norm_weight,
@@ -368,6 +369,51 @@ msa_status_t msa_index_frontend(const void* x, const void* w_q, const void* w_k,
                                 int64_t total_q, int d_model, int num_groups, int index_dim, int rope_dim,
                                 float rope_theta, float norm_eps, void* q_idx, void* k_idx,
                                 msa_dtype_t out_dtype, hipStream_t stream);
+
+/* ----------------------------------------------------------------------
+ * Index front-end backward: gradients of the front-end's parameters.
+ *
+ * The alignment loss trains only the index branch: the atlas record of
+ * MiniMax M3 (summary paragraph) confines it to the index projections by a
+ * stop-gradient on the indexer's input, so x is held constant and no dx is
+ * produced.  For upstream gradients dq_idx (of q_idx) and dk_idx (of the
+ * index-key rows, e.g. those of msa_index_kl_backward), per token and head
+ * vector, with n = y / r, r = sqrt(mean y^2 + norm_eps), z = gain * n and
+ * out = R z (R the rotation of msa_index_frontend):
+ *   dz = R^T dout,  dgain += dz * n,  dn = dz * gain,
+ *   dy = (dn - n (dn . n) / index_dim) / r,  dW_h += dy x^T.
+ *
+ *   x, w_q, w_k, norm weights, cu_seqlens, sizes, rope_dim, rope_theta,
+ *   norm_eps               as for msa_index_frontend (bf16 x and weights only)
+ *   dq_idx                 [total_q, num_groups, index_dim] fp32
+ *   dk_idx                 fp32 index-key gradient rows; the row of token t of
+ *                          sequence b is cu_seqlens_k[b] + p (rows of other
+ *                          positions are not read; tokens with p < 0 or
+ *                          p >= kv_len have no key row and contribute nothing
+ *                          through the key head)
+ *   dw_q, dw_k             out [num_groups * index_dim, d_model] and
+ *                          [index_dim, d_model] fp32, overwritten
+ *   dq_norm_weight,
+ *   dk_norm_weight         out [index_dim] fp32, overwritten
+ *   workspace              at least msa_index_frontend_backward_workspace_size()
+ *                          bytes: dy in bf16 per (token, projection row), fp32
+ *                          weight-gradient slices of the token ranges, and
+ *                          per-workgroup gain partials (about 240 MB for
+ *                          128K tokens at d_model 3072)
+ * The weight gradient is accumulated in fp32 from bf16 dy and x on MFMAs;
+ * slices and partials are summed in a fixed order, so results are bitwise
+ * reproducible.  fp32 inputs return MSA_ERR_UNSUPPORTED.  With total_q 0, x,
+ * dq_idx and dk_idx may be null and the outputs are set to zero.
+ * ---------------------------------------------------------------------- */
+size_t msa_index_frontend_backward_workspace_size(int64_t total_q, int d_model, int num_groups, int index_dim);
+
+msa_status_t msa_index_frontend_backward(const void* x, const void* w_q, const void* w_k, msa_dtype_t dtype,
+                                         const float* q_norm_weight, const float* k_norm_weight,
+                                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                                         int64_t total_q, int d_model, int num_groups, int index_dim, int rope_dim,
+                                         float rope_theta, float norm_eps, const float* dq_idx, const float* dk_idx,
+                                         float* dw_q, float* dw_k, float* dq_norm_weight, float* dk_norm_weight,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

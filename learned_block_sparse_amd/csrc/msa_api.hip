@@ -332,8 +332,9 @@ msa_status_t msa_index_frontend(const void* x, const void* w_q, const void* w_k,
                                 int64_t total_q, int d_model, int num_groups, int index_dim, int rope_dim,
                                 float rope_theta, float norm_eps, void* q_idx, void* k_idx,
                                 msa_dtype_t out_dtype, hipStream_t stream) {
-  if (!x || !w_q || !w_k || !q_norm_weight || !k_norm_weight || !cu_seqlens_q || !cu_seqlens_k || !q_idx ||
-      !k_idx)
+  // token-indexed buffers may be null when there are no tokens
+  if (!w_q || !w_k || !q_norm_weight || !k_norm_weight || !cu_seqlens_q || !cu_seqlens_k ||
+      (total_q > 0 && (!x || !q_idx || !k_idx)))
     return MSA_ERR_INVALID_ARG;
   if (batch <= 0 || total_q < 0 || d_model <= 0 || num_groups <= 0 || index_dim <= 0 || rope_dim < 0 ||
       rope_dim > index_dim || !(rope_theta > 0.f) || !(norm_eps >= 0.f) || !dtype_ok(dtype) ||
@@ -363,6 +364,55 @@ msa_status_t msa_index_frontend(const void* x, const void* w_q, const void* w_k,
   f.q_out = q_idx;
   f.k_out = k_idx;
   return hip_status(launch_index_frontend(f, stream));
+}
+
+size_t msa_index_frontend_backward_workspace_size(int64_t total_q, int d_model, int num_groups, int index_dim) {
+  if (total_q < 0 || d_model <= 0 || num_groups <= 0 || (index_dim != 64 && index_dim != 128) || d_model % 64 != 0)
+    return 0;
+  return plan_index_frontend_bwd(total_q, d_model, num_groups, index_dim).workspace_bytes;
+}
+
+msa_status_t msa_index_frontend_backward(const void* x, const void* w_q, const void* w_k, msa_dtype_t dtype,
+                                         const float* q_norm_weight, const float* k_norm_weight,
+                                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                                         int64_t total_q, int d_model, int num_groups, int index_dim, int rope_dim,
+                                         float rope_theta, float norm_eps, const float* dq_idx, const float* dk_idx,
+                                         float* dw_q, float* dw_k, float* dq_norm_weight, float* dk_norm_weight,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  // token-indexed buffers may be null when there are no tokens
+  if (!w_q || !w_k || !q_norm_weight || !k_norm_weight || !cu_seqlens_q || !cu_seqlens_k || !dw_q || !dw_k ||
+      !dq_norm_weight || !dk_norm_weight || (total_q > 0 && (!x || !dq_idx || !dk_idx)))
+    return MSA_ERR_INVALID_ARG;
+  if (batch <= 0 || total_q < 0 || d_model <= 0 || num_groups <= 0 || index_dim <= 0 || rope_dim < 0 ||
+      rope_dim > index_dim || !(rope_theta > 0.f) || !(norm_eps >= 0.f) || !dtype_ok(dtype))
+    return MSA_ERR_INVALID_ARG;
+  if (dtype != MSA_BF16 || (index_dim != 64 && index_dim != 128) || d_model % 64 != 0 || rope_dim % 64 != 0 ||
+      num_groups > 65535)
+    return MSA_ERR_UNSUPPORTED;
+  const FrontendBwdPlan pl = plan_index_frontend_bwd(total_q, d_model, num_groups, index_dim);
+  if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes)) return MSA_ERR_WORKSPACE;
+  FrontendLaunch f;
+  f.x = x;
+  f.w_q = w_q;
+  f.w_k = w_k;
+  f.gain_q = q_norm_weight;
+  f.gain_k = k_norm_weight;
+  f.cu_q = cu_seqlens_q;
+  f.cu_k = cu_seqlens_k;
+  f.batch = batch;
+  f.G = num_groups;
+  f.DI = index_dim;
+  f.d_model = d_model;
+  f.rope_dim = rope_dim;
+  f.total = total_q;
+  f.theta = rope_theta;
+  f.eps = norm_eps;
+  f.in_f32 = false;
+  f.out_f32 = true;
+  f.q_out = nullptr;
+  f.k_out = nullptr;
+  return hip_status(launch_index_frontend_bwd(pl, f, dq_idx, dk_idx, dw_q, dw_k, dq_norm_weight, dk_norm_weight,
+                                              workspace, stream));
 }
 
 }  // extern "C"

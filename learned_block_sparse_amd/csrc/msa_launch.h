@@ -151,5 +151,18 @@ struct FrontendLaunch {
   void* k_out;                // key rows at cu_k[b] + p
 };
 hipError_t launch_index_frontend(const FrontendLaunch& f, hipStream_t st);
+struct FrontendBwdPlan {
+  int64_t tiles = 0;         // 128-token tiles of the recompute kernel
+  int64_t tp = 0;            // tiles * 128
+  int mrows = 0;             // (G+1) * DI
+  int splits = 1;            // token ranges of the weight-gradient GEMM
+  int chunks_per_split = 1;  // 64-token chunks per range
+  size_t dy_off = 0, gain_off = 0, dw_off = 0;
+  size_t workspace_bytes = 0;
+};
+FrontendBwdPlan plan_index_frontend_bwd(int64_t total, int d_model, int G, int DI);
+hipError_t launch_index_frontend_bwd(const FrontendBwdPlan& pl, const FrontendLaunch& f, const float* dq,
+                                     const float* dk, float* dw_q, float* dw_k, float* dgain_q, float* dgain_k,
+                                     void* ws, hipStream_t st);
 
 }  // namespace msa

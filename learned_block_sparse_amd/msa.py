@@ -82,6 +82,12 @@ def lib():
         L.msa_index_frontend.restype = i32
         L.msa_index_frontend.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, ctypes.c_int64, i32, i32, i32, i32,
                                          ctypes.c_float, ctypes.c_float, vp, vp, i32, vp]
+        L.msa_index_frontend_backward_workspace_size.restype = sz
+        L.msa_index_frontend_backward_workspace_size.argtypes = [ctypes.c_int64, i32, i32, i32]
+        L.msa_index_frontend_backward.restype = i32
+        L.msa_index_frontend_backward.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, ctypes.c_int64, i32, i32, i32,
+                                                  i32, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
+                                                  sz, vp]
         _lib = L
     return _lib
 
@@ -348,3 +354,43 @@ def msa_index_frontend(x, w_q, w_k, q_norm_weight, k_norm_weight, cu_seqlens_q, 
         _dtype_code(q_idx), _stream(stream))
     _check(st, "msa_index_frontend")
     return q_idx, k_idx
+
+
+def msa_index_frontend_backward_workspace_size(total_q, d_model, num_groups, index_dim) -> int:
+    return int(lib().msa_index_frontend_backward_workspace_size(int(total_q), d_model, num_groups, index_dim))
+
+
+def msa_index_frontend_backward(x, w_q, w_k, q_norm_weight, k_norm_weight, cu_seqlens_q, cu_seqlens_k,
+                                num_groups: int, dq_idx, dk_idx, rope_dim: int = 64, rope_theta: float = 10000.0,
+                                norm_eps: float = 1e-6, dw_q=None, dw_k=None, dq_norm_weight=None,
+                                dk_norm_weight=None, workspace=None, stream=None):
+    """Gradients of the index front-end's parameters for upstream gradients
+    ``dq_idx [T, G, d_idx]`` and ``dk_idx`` (index-key rows, read at
+    ``cu_seqlens_k[b] + position``), x held constant: ``(dw_q, dw_k,
+    dq_norm_weight, dk_norm_weight)``, fp32."""
+    t, d_model = x.shape
+    di = w_k.shape[0]
+    G = int(num_groups)
+    batch = cu_seqlens_q.numel() - 1
+    dev = x.device
+    if dw_q is None:
+        dw_q = torch.empty((G * di, d_model), dtype=torch.float32, device=dev)
+    if dw_k is None:
+        dw_k = torch.empty((di, d_model), dtype=torch.float32, device=dev)
+    if dq_norm_weight is None:
+        dq_norm_weight = torch.empty((di,), dtype=torch.float32, device=dev)
+    if dk_norm_weight is None:
+        dk_norm_weight = torch.empty((di,), dtype=torch.float32, device=dev)
+    need = msa_index_frontend_backward_workspace_size(t, d_model, G, di)
+    ws, ws_bytes = _workspace(need, dev, workspace)
+    st = lib().msa_index_frontend_backward(
+        _dev(x, "x"), _dev(w_q, "w_q", x.dtype), _dev(w_k, "w_k", x.dtype), _dtype_code(x),
+        _dev(q_norm_weight, "q_norm_weight", torch.float32), _dev(k_norm_weight, "k_norm_weight", torch.float32),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32), batch, t,
+        d_model, G, di, int(rope_dim), float(rope_theta), float(norm_eps),
+        _dev(dq_idx, "dq_idx", torch.float32), _dev(dk_idx, "dk_idx", torch.float32),
+        _dev(dw_q, "dw_q", torch.float32), _dev(dw_k, "dw_k", torch.float32),
+        _dev(dq_norm_weight, "dq_norm_weight", torch.float32), _dev(dk_norm_weight, "dk_norm_weight", torch.float32),
+        ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
+    _check(st, "msa_index_frontend_backward")
+    return dw_q, dw_k, dq_norm_weight, dk_norm_weight

@@ -139,6 +139,7 @@ def _frontend(L, **kw):
 
 def test_frontend_argument_errors(L):
     assert _frontend(L, x=None) == 1
+    assert _frontend(L, wq=None, total=0) == 1
     assert _frontend(L, gk=None) == 1
     assert _frontend(L, total=-1) == 1
     assert _frontend(L, rope=130) == 1       # wider than the head
@@ -151,5 +152,27 @@ def test_frontend_argument_errors(L):
     assert _frontend(L, dm=3000) == 2        # not a multiple of 64
     assert _frontend(L, rope=32) == 2
     assert _frontend(L, DI=64, rope=128) == 1
-    # no tokens: nothing to launch
+    # no tokens: nothing to launch, and the token-indexed buffers may be null
     assert _frontend(L, total=0) == 0
+    assert _frontend(L, total=0, x=None, q=None, k=None) == 0
+
+
+def test_frontend_backward_argument_errors_and_workspace(L):
+    def call(**kw):
+        a = dict(x=FAKE, wq=FAKE, wk=FAKE, dtype=1, gq=FAKE, gk=FAKE, cuq=FAKE, cuk=FAKE, batch=1, total=256,
+                 dm=3072, G=4, DI=128, rope=64, theta=10000.0, eps=1e-6, dq=FAKE, dk=FAKE, dwq=FAKE, dwk=FAKE,
+                 dgq=FAKE, dgk=FAKE, ws=None, wsb=0, stream=None)
+        a.update(kw)
+        return L.msa_index_frontend_backward(*a.values())
+    assert call(dq=None) == 1
+    assert call(dgk=None) == 1
+    assert call(theta=-1.0) == 1
+    assert call(dtype=0) == 2                # fp32 hidden states
+    assert call(DI=96) == 2
+    assert call(rope=32) == 2
+    assert call() == 3                       # needs a workspace
+    ws = L.msa_index_frontend_backward_workspace_size(131072, 3072, 4, 128)
+    # dy (bf16) + at least one fp32 slice of the weight gradient
+    assert ws >= 131072 * 640 * 2 + 640 * 3072 * 4
+    assert L.msa_index_frontend_backward_workspace_size(0, 3072, 4, 128) == 0
+    assert L.msa_index_frontend_backward_workspace_size(10, 3000, 4, 128) == 0

@@ -149,3 +149,85 @@ def test_frontend_feeds_index_topk(msa, synth):
         valid = sel >= 0
         assert bool(((sel <= local[:, None]) | ~valid).all())
         assert valid.sum(dim=1).equal(torch.clamp(local + 1, max=16))
+
+
+# ---------------------------------------------------------------- backward
+# The GPU recomputes y in fp32 from bf16 x and W, forms dy in fp32, rounds it
+# to bf16 (relative 2^-9) and accumulates dW = dy^T x in fp32 on MFMAs; the
+# gain gradients stay fp32 throughout.  dW: relative RMS <= 1e-2 and max |err|
+# <= 2e-2 * max |ref| (the bf16 bounds of the other backward); gains: relative
+# RMS <= 1e-3.
+
+def _bwd_run(msa, synth, oracle_lib, q_lens, kv_lens, *, G=4, DI=128, d_model=3072, rope=64, seed=0, what=""):
+    T = int(sum(q_lens))
+    cu_q, cu_k = _cu(q_lens), _cu(kv_lens)
+    inp = synth.frontend_inputs(T, G, DI, d_model, torch.bfloat16, "cuda", seed)
+    cuq_d = torch.tensor(cu_q, dtype=torch.int32, device="cuda")
+    cuk_d = torch.tensor(cu_k, dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1000 + seed)
+    dq = torch.randn((T, G, DI), generator=g, device="cuda", dtype=torch.float32)
+    dk = torch.randn((int(cu_k[-1]), DI), generator=g, device="cuda", dtype=torch.float32)
+    got = msa.msa_index_frontend_backward(inp["x"], inp["w_q"], inp["w_k"], inp["gain_q"], inp["gain_k"], cuq_d,
+                                          cuk_d, G, dq, dk, rope_dim=rope, rope_theta=THETA, norm_eps=EPS)
+    torch.cuda.synchronize()
+    rows, kstart, pos = oracle_lib.rows_prefill(cu_q, cu_k)
+    n_k = (cu_k[1:] - cu_k[:-1])[np.searchsorted(cu_q, rows, side="right") - 1]
+    has_key = (pos >= 0) & (pos < n_k)
+    dk_tok = np.zeros((T, DI))
+    dk_host = dk.cpu().double().numpy()
+    dk_tok[has_key] = dk_host[(kstart + pos)[has_key]]
+    ref = oracle_lib.index_frontend_bwd(host(inp["x"]), host(inp["w_q"]), host(inp["w_k"]),
+                                        inp["gain_q"].cpu().numpy(), inp["gain_k"].cpu().numpy(), pos, G, DI, rope,
+                                        THETA, EPS, dq.cpu().double().numpy(), dk_tok)
+    for name, gg, r in zip(("dw_q", "dw_k", "dgain_q", "dgain_k"), got, ref):
+        gv = gg.cpu().double().numpy()
+        err = np.abs(gv - r)
+        rel = float(np.sqrt((err ** 2).sum() / max((r ** 2).sum(), 1e-300)))
+        mx = float(err.max())
+        say(f"    {what} {name}: rel-RMS {rel:.2e}, max-abs {mx:.2e} (max |ref| {np.abs(r).max():.3g})")
+        if name.startswith("dw"):
+            assert rel <= 1e-2 and mx <= 2e-2 * float(np.abs(r).max()), f"{what} {name}"
+        else:
+            assert rel <= 1e-3, f"{what} {name}"
+    return got
+
+
+def test_frontend_backward_measured_config(msa, synth, oracle_lib):
+    """d_model 3072, 4 + 1 heads of 128 dims, rotary width 64; two packed
+    sequences (the second a chunk), a ragged tail."""
+    say("[frontend bwd] measured config")
+    _bwd_run(msa, synth, oracle_lib, [1000, 300], [1000, 2500], seed=11, what="bwd")
+
+
+def test_frontend_backward_rope128_and_missing_keys(msa, synth, oracle_lib):
+    """Rotary width 128; tokens at p < 0 (no key row) and an empty sequence."""
+    say("[frontend bwd] rope 128, p < 0")
+    _bwd_run(msa, synth, oracle_lib, [40, 0, 300], [30, 50, 300], rope=128, seed=12, what="bwd rope128")
+
+
+def test_frontend_backward_small_index_dim(msa, synth, oracle_lib):
+    """d_idx 64 with 2 groups: 192 projection rows (a partial 128-row tile of
+    the weight-gradient GEMM), d_model 256."""
+    say("[frontend bwd] d_idx 64")
+    _bwd_run(msa, synth, oracle_lib, [700], [700], G=2, DI=64, d_model=256, seed=13, what="bwd di64")
+
+
+def test_frontend_backward_deterministic_and_empty(msa, synth):
+    inp = synth.frontend_inputs(900, device="cuda", seed=14)
+    cu = torch.tensor([0, 900], dtype=torch.int32, device="cuda")
+    dq = torch.randn((900, 4, 128), device="cuda")
+    dk = torch.randn((900, 128), device="cuda")
+    a = msa.msa_index_frontend_backward(inp["x"], inp["w_q"], inp["w_k"], inp["gain_q"], inp["gain_k"], cu, cu, 4,
+                                        dq, dk)
+    b = msa.msa_index_frontend_backward(inp["x"], inp["w_q"], inp["w_k"], inp["gain_q"], inp["gain_k"], cu, cu, 4,
+                                        dq, dk)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+    # no tokens: every gradient is exactly zero
+    cu0 = torch.tensor([0, 0], dtype=torch.int32, device="cuda")
+    z = msa.msa_index_frontend_backward(inp["x"][:0], inp["w_q"], inp["w_k"], inp["gain_q"], inp["gain_k"], cu0, cu0,
+                                        4, dq[:0], dk)
+    torch.cuda.synchronize()
+    assert all(bool((t == 0).all()) for t in z)
