@@ -286,14 +286,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
   __shared__ __attribute__((aligned(16))) BwdLds L;
   __shared__ int32_t codes[kSortMax];
   const int nbk = a.batch * a.G * a.nb_max;
-  const int bucket = blockIdx.x;
-  if (bucket >= nbk) return;
+  if ((int)blockIdx.x >= nbk) return;
+  // Dispatch order: key blocks from the last to the first, the (sequence,
+  // group) pairs interleaved.  A window's largest buckets are the local
+  // blocks of its own query rows, the highest block ids; started first, they
+  // no longer stretch the end of the grid.
+  const int nbg = a.batch * a.G;
+  const int c = a.nb_max - 1 - (int)blockIdx.x / nbg;
+  const int g = (int)blockIdx.x % nbg % a.G;
+  const int b = (int)blockIdx.x % nbg / a.G;
+  const int bucket = (b * a.G + g) * a.nb_max + c;
   const int e_lo = a.offsets[bucket];
   const int n = a.offsets[bucket + 1] - e_lo;
   if (n <= 0) return;
-  const int c = bucket % a.nb_max;
-  const int g = (bucket / a.nb_max) % a.G;
-  const int b = bucket / (a.nb_max * a.G);
   const int64_t kb0 = a.cu_k[b];
   const int N = a.cu_k[b + 1] - a.cu_k[b];
   const int64_t q0 = a.cu_q[b];
