@@ -62,7 +62,7 @@ extern "C" {
 typedef enum {
   MSA_OK = 0,
   MSA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad combination */
-  MSA_ERR_UNSUPPORTED = 2,  /* a shape or type this build does not implement */
+  MSA_ERR_UNSUPPORTED = 2,  /* a shape or type the library does not implement */
   MSA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
   MSA_ERR_HIP = 4           /* a HIP launch or runtime call failed */
 } msa_status_t;
