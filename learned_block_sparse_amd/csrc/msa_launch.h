@@ -96,6 +96,7 @@ struct BwdPlan {
   int64_t rows_bound = 0;
   int64_t window = 0;        // query rows per edge-list window
   size_t counts_off = 0, offsets_off = 0, chunks_off = 0, cursor_off = 0, edges_off = 0, delta_off = 0;
+  size_t order_off = 0;      // [nbuckets] int32: bwd_dkdv's dispatch order
   size_t part_dq_off = 0;    // [window rows, G, topk, 16, 128] bf16
   size_t workspace_bytes = 0;
 };

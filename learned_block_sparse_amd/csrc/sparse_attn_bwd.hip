@@ -16,6 +16,8 @@
 // Kernels (bf16 inputs, fp32 accumulation and fp32 gradients):
 //   bwd_zero   dk = dv = 0 for the key rows of the call
 //   bwd_delta  delta[row, head] = dO . O
+//   bwd_order  the buckets by edge count, largest first (bwd_dkdv's dispatch
+//              order)
 //   bwd_dkdv   KV-outer, one workgroup per (sequence, group, block) bucket of
 //              the selection edge lists (the lists the KV-outer forward
 //              builds).  The bucket's list, placed by atomics in no fixed
@@ -65,6 +67,7 @@ struct BwdKernelArgs {
   const int32_t* chunk_start;
   int32_t* edges;
   float* delta;
+  int32_t* order;    // bwd_dkdv's bucket for each workgroup, largest buckets first
   bf16* part_dq;     // [window rows, G, topk, 16, 128]: each edge's block contribution to dq (unscaled)
   float* dq;
   float* dk;
@@ -102,6 +105,58 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdKernelArgs a) {
 #pragma unroll
   for (int m = 16; m >= 1; m >>= 1) s += __shfl_xor(s, m, 32);
   if ((threadIdx.x & 31) == 0) a.delta[rh] = s;
+}
+
+// Dispatch order of bwd_dkdv: one workgroup per bucket runs the bucket's
+// quads one after another, and a bucket can hold several times the average
+// (planted blocks, the window's own local blocks), so the buckets go longest
+// first.  Keys (edge count << 15 | 32767 - bucket) are sorted descending by a
+// bitonic network in LDS: largest count first, ties by lower bucket id, the
+// same order on every run.  More than kOrderMax buckets (not met by the
+// single-sequence workloads up to 1M tokens with 4 groups): key blocks from
+// the last to the first instead, groups interleaved.
+constexpr int kOrderMax = 32768;
+
+__global__ __launch_bounds__(1024) void bwd_order(BwdKernelArgs a) {
+  __shared__ uint32_t keys[kOrderMax];
+  const int nbk = a.batch * a.G * a.nb_max;
+  const int tid = threadIdx.x;
+  if (nbk > kOrderMax) {
+    const int nbg = a.batch * a.G;
+    for (int i = tid; i < nbk; i += 1024) {
+      const int c = a.nb_max - 1 - i / nbg;
+      a.order[i] = (i % nbg) * a.nb_max + c;
+    }
+    return;
+  }
+  int n2 = 1;
+  while (n2 < nbk) n2 <<= 1;
+  for (int i = tid; i < n2; i += 1024) {
+    if (i < nbk) {
+      const int cnt = a.offsets[i + 1] - a.offsets[i];  // <= rows per window < 2^17
+      keys[i] = ((uint32_t)cnt << 15) | (uint32_t)(32767 - i);
+    } else {
+      keys[i] = 0u;  // padding sorts last
+    }
+  }
+  __syncthreads();
+  for (int kk = 2; kk <= n2; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < n2; i += 1024) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint32_t x = keys[i], y = keys[ixj];
+          // descending within blocks of kk whose bit kk is clear
+          if ((x < y) == ((i & kk) == 0)) {
+            keys[i] = y;
+            keys[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < nbk; i += 1024) a.order[i] = 32767 - (int)(keys[i] & 32767u);
 }
 
 // One quad of edges (4 queries x 16 heads = 64 MFMA rows), staged by the
@@ -287,15 +342,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
   __shared__ int32_t codes[kSortMax];
   const int nbk = a.batch * a.G * a.nb_max;
   if ((int)blockIdx.x >= nbk) return;
-  // Dispatch order: key blocks from the last to the first, the (sequence,
-  // group) pairs interleaved.  A window's largest buckets are the local
-  // blocks of its own query rows, the highest block ids; started first, they
-  // no longer stretch the end of the grid.
-  const int nbg = a.batch * a.G;
-  const int c = a.nb_max - 1 - (int)blockIdx.x / nbg;
-  const int g = (int)blockIdx.x % nbg % a.G;
-  const int b = (int)blockIdx.x % nbg / a.G;
-  const int bucket = (b * a.G + g) * a.nb_max + c;
+  // largest buckets first (bwd_order), so no long bucket starts at the end
+  const int bucket = a.order[blockIdx.x];
+  const int c = bucket % a.nb_max;
+  const int g = (bucket / a.nb_max) % a.G;
+  const int b = bucket / (a.nb_max * a.G);
   const int e_lo = a.offsets[bucket];
   const int n = a.offsets[bucket + 1] - e_lo;
   if (n <= 0) return;
@@ -633,6 +684,7 @@ BwdPlan plan_bwd(int batch, int max_q_len, int max_kv_len, int Hq, int G, int to
   pl.cursor_off = off;  off += al(nbk * 4);
   pl.edges_off = off;   off += al((size_t)pl.window * G * topk * 4);
   pl.delta_off = off;   off += al((size_t)pl.rows_bound * Hq * 4);
+  pl.order_off = off;   off += al(nbk * 4);
   pl.part_dq_off = off; off += al((size_t)pl.window * G * topk * 16 * kHeadDim * sizeof(bf16));
   pl.workspace_bytes = off;
   return pl;
@@ -667,6 +719,7 @@ hipError_t launch_sparse_attn_bwd(const BwdPlan& pl, const BwdArgs& x, void* ws,
   a.chunk_start = chunks;
   a.edges = reinterpret_cast<int32_t*>(w + pl.edges_off);
   a.delta = reinterpret_cast<float*>(w + pl.delta_off);
+  a.order = reinterpret_cast<int32_t*>(w + pl.order_off);
   a.part_dq = reinterpret_cast<bf16*>(w + pl.part_dq_off);
   a.dq = x.dq;
   a.dk = x.dk;
@@ -679,6 +732,7 @@ hipError_t launch_sparse_attn_bwd(const BwdPlan& pl, const BwdArgs& x, void* ws,
     hipError_t e = build_edge_lists(x.fwd, pl.nb_max, r0, r1, counts, offsets, chunks, cursor, a.edges, st);
     if (e != hipSuccess) return e;
     a.row_lo = r0;
+    hipLaunchKernelGGL(bwd_order, dim3(1), dim3(1024), 0, st, a);
     hipLaunchKernelGGL(bwd_dkdv, dim3((unsigned)pl.nbuckets), dim3(kBwdThreads), 0, st, a);
     // chunks of kEdgeChunk edges: at most entries / kEdgeChunk + one partial chunk per bucket
     const int64_t entries = (r1 - r0) * a.G * a.topk;
