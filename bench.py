@@ -57,7 +57,8 @@ def parse():
     ap.add_argument("--profile", choices=["prefill_tile", "train_tile", "frontend", "decode", "copy"],
                     help="run one workload a few times for hardware-counter collection and exit "
                          "(prefill_tile: the last 8192-query call of the 128K prefill; train_tile: that "
-                         "tile's forward, backward and KL loss; frontend: the index front-end over all "
+                         "tile's index front-end (forward and backward), index call, forward, backward and KL loss; frontend: "
+                         "the index front-end over all "
                          "128K tokens; decode: one "
                          "decode step of the 1M-context batch; copy: a 1 GiB device-to-device copy "
                          "that calibrates the byte counters)")
@@ -542,7 +543,16 @@ def profile_run(args, msa, synth, torch):
         cu_k = torch.tensor([0, hi], dtype=torch.int32, device="cuda")
         dout = synth.normal((m, wl.num_heads, wl.head_dim), torch.bfloat16, "cuda", 0, "dout")
         blse = torch.empty((m, wl.num_heads, wl.topk), dtype=torch.float32, device="cuda")
+        # the tile's index front-end (its 8192 tokens at positions lo..hi-1) and its backward
+        fe = synth.frontend_inputs(m, wl.num_kv_heads, wl.index_dim, synth.D_MODEL, torch.bfloat16, "cuda", 0)
+        fe_k = torch.empty((hi, wl.index_dim), dtype=torch.bfloat16, device="cuda")
+        fe_dq = torch.randn((m, wl.num_kv_heads, wl.index_dim), device="cuda")
+        fe_dk = torch.randn((hi, wl.index_dim), device="cuda")
         for _ in range(args.profile_reps):
+            msa.msa_index_frontend(fe["x"], fe["w_q"], fe["w_k"], fe["gain_q"], fe["gain_k"], cu_q, cu_k,
+                                   wl.num_kv_heads, k_idx=fe_k)
+            msa.msa_index_frontend_backward(fe["x"], fe["w_q"], fe["w_k"], fe["gain_q"], fe["gain_k"], cu_q, cu_k,
+                                            wl.num_kv_heads, fe_dq, fe_dk)
             ids = msa.msa_index_topk(inp["q_idx"][lo:hi], inp["k_idx"], cu_q, cu_k, m, hi, wl.block_size, wl.topk)
             out, lse = msa.msa_sparse_attn_prefill_ex(inp["q"][lo:hi], inp["k"], inp["v"], ids, cu_q, cu_k, m, hi,
                                                       wl.block_size, wl.topk, block_lse=blse)
