@@ -55,9 +55,21 @@ struct FeArgs {
   void* k_out;
 };
 
+// LDS layout of a staged weight chunk (rows = the head's dims, kFeKc values
+// each), as the element offset of 16-byte piece c16 of a row.  bf16: 64-byte
+// rows, unpadded, with the piece index XOR-ed by (row / 4) % 4, so both the
+// staging writes (4 rows x 4 pieces per 16 lanes) and the MFMA fragment reads
+// (16 rows at one piece) cover all 16 bank groups.  fp32: 144-byte padded
+// rows.
 template <typename T> struct FeLds;
-template <> struct FeLds<bf16> { static constexpr int stride = kFeKc + 8; };   // 80-byte rows
-template <> struct FeLds<float> { static constexpr int stride = kFeKc + 4; };  // 144-byte rows
+template <> struct FeLds<bf16> {
+  static constexpr int stride = kFeKc;
+  static __device__ __forceinline__ int off(int row, int c16) { return row * kFeKc + ((c16 ^ ((row >> 2) & 3)) << 3); }
+};
+template <> struct FeLds<float> {
+  static constexpr int stride = kFeKc + 4;
+  static __device__ __forceinline__ int off(int row, int c16) { return row * (kFeKc + 4) + (c16 << 2); }
+};
 
 __device__ __forceinline__ int fe_find(const int32_t* cu, int n, int64_t x) {
   int lo = 0, hi = n;  // cu[lo] <= x < cu[hi]
@@ -186,7 +198,6 @@ template <typename T, int DI, int CTW>
 __device__ __forceinline__ void fe_gemm(const FeArgs& a, const T* w, int64_t t0, f32x16 (&acc)[DI / 32][CTW],
                                         T (&w_lds)[2][DI * FeLds<T>::stride]) {
   constexpr int RT = DI / 32;             // row tiles (32 dims each)
-  constexpr int LS = FeLds<T>::stride;
   constexpr int V16 = 16 / sizeof(T);     // elements per 16-byte piece
   constexpr int PIECES = DI * kFeKc / V16 / kFeThreads;  // 16-byte pieces per thread per chunk
   const T* x = static_cast<const T*>(a.x);
@@ -215,7 +226,7 @@ __device__ __forceinline__ void fe_gemm(const FeArgs& a, const T* w, int64_t t0,
     for (int u = 0; u < PIECES; ++u) {
       const int piece = threadIdx.x + u * kFeThreads;
       const int row = piece / (kFeKc / V16), c16 = piece % (kFeKc / V16);
-      *reinterpret_cast<u32x4*>(&w_lds[buf][row * LS + c16 * V16]) = wr[u];
+      *reinterpret_cast<u32x4*>(&w_lds[buf][FeLds<T>::off(row, c16)]) = wr[u];
     }
   };
   auto load_x = [&](frag8<T> (&dst)[CTW][kFeS], int kc) {
@@ -246,7 +257,8 @@ __device__ __forceinline__ void fe_gemm(const FeArgs& a, const T* w, int64_t t0,
     for (int s = 0; s < kFeS; ++s)
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const frag8<T> av = load8(wl + (32 * rt + col) * LS + (kFeKc / 2) * h + 8 * s);
+        // 8 elements = 16 bytes (bf16: one piece) or 32 bytes (fp32: two pieces)
+        const frag8<T> av = load8(wl + FeLds<T>::off(32 * rt + col, ((kFeKc / 2) * h + 8 * s) / V16));
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) acc[rt][ct] = mma32(av, xr[ct][s], acc[rt][ct]);
       }
