@@ -143,3 +143,15 @@ def test_backward_unsupported_type(msa, synth):
         msa.msa_sparse_attn_backward(inp["q"], inp["k"], inp["v"], out, out, lse, ids, inp["cu_seqlens_q"],
                                      inp["cu_seqlens_k"], 300, 300, wl.block_size, wl.topk)
     assert e.value.status == msa.MSA_ERR_UNSUPPORTED
+
+
+def test_backward_beyond_sort_capacity(msa, synth, oracle_lib):
+    """65 packed sequences, one of 16,384 tokens and 64 of 3: 65 x 4 groups x 128
+    blocks = 33,280 buckets, more than the dK/dV dispatch sort holds, so the
+    fixed last-block-first order is used instead; results as for any order."""
+    wl = dataclasses.replace(synth.WORKLOADS["prefill_32k"], planted=8)
+    kv = [16384] + [3] * 64
+    ql = [256] + [3] * 64
+    say(f"[bwd] 65 sequences, {65 * 4 * 128} buckets")
+    inp, ids, dout, grads = _forward_backward(msa, synth, wl, kv, ql, 47)
+    _check_vs_oracle(oracle_lib, inp, ids, dout, grads, wl, "bwd many buckets")
