@@ -231,3 +231,59 @@ def test_frontend_backward_deterministic_and_empty(msa, synth):
                                         4, dq[:0], dk)
     torch.cuda.synchronize()
     assert all(bool((t == 0).all()) for t in z)
+
+
+# ------------------------------------------------------- full size (128K)
+def test_frontend_full_128k_sampled(msa, synth, oracle_lib):
+    """The bench's call: 131,072 tokens, d_model 3072, bf16 out.  Sampled rows
+    (the first and last 256-token tiles and 512 random tokens) against the
+    oracle on exactly those rows and positions."""
+    L = 131072
+    say("[frontend] 128K tokens, sampled rows")
+    inp = synth.frontend_inputs(L, device="cuda", seed=21)
+    cu = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+    q_idx, k_idx = msa.msa_index_frontend(inp["x"], inp["w_q"], inp["w_k"], inp["gain_q"], inp["gain_k"], cu, cu, 4,
+                                          rope_theta=THETA, norm_eps=EPS)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(21)
+    rows = np.unique(np.concatenate([np.arange(256), np.arange(L - 256, L), rng.integers(0, L, 512)]))
+    ridx = torch.as_tensor(rows, device="cuda")
+    rq, rk = oracle_lib.index_frontend(host(inp["x"][ridx]), host(inp["w_q"]), host(inp["w_k"]),
+                                       inp["gain_q"].cpu().numpy(), inp["gain_k"].cpu().numpy(), rows, 4, 128, 64,
+                                       THETA, EPS)
+    _check(q_idx[ridx], rq, torch.bfloat16, "128K q_idx")
+    _check(k_idx[ridx], rk, torch.bfloat16, "128K k_idx")
+
+
+def test_frontend_backward_full_128k_sampled(msa, synth, oracle_lib):
+    """The bench's backward call over 131,072 tokens with the upstream
+    gradients zero except on 384 sampled tokens: the parameter gradients are
+    then exactly those of the sampled tokens, which the oracle computes."""
+    L = 131072
+    say("[frontend bwd] 128K tokens, sampled upstream gradients")
+    inp = synth.frontend_inputs(L, device="cuda", seed=22)
+    cu = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(22)
+    rows = np.unique(np.concatenate([np.arange(128), np.arange(L - 128, L), rng.integers(0, L, 128)]))
+    ridx = torch.as_tensor(rows, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(22)
+    dq = torch.zeros((L, 4, 128), device="cuda")
+    dk = torch.zeros((L, 128), device="cuda")
+    dq[ridx] = torch.randn((len(rows), 4, 128), generator=g, device="cuda")
+    dk[ridx] = torch.randn((len(rows), 128), generator=g, device="cuda")
+    got = msa.msa_index_frontend_backward(inp["x"], inp["w_q"], inp["w_k"], inp["gain_q"], inp["gain_k"], cu, cu, 4,
+                                          dq, dk, rope_theta=THETA, norm_eps=EPS)
+    torch.cuda.synchronize()
+    ref = oracle_lib.index_frontend_bwd(host(inp["x"][ridx]), host(inp["w_q"]), host(inp["w_k"]),
+                                        inp["gain_q"].cpu().numpy(), inp["gain_k"].cpu().numpy(), rows, 4, 128, 64,
+                                        THETA, EPS, dq[ridx].cpu().double().numpy(), dk[ridx].cpu().double().numpy())
+    for name, gg, r in zip(("dw_q", "dw_k", "dgain_q", "dgain_k"), got, ref):
+        gv = gg.cpu().double().numpy()
+        err = np.abs(gv - r)
+        rel = float(np.sqrt((err ** 2).sum() / max((r ** 2).sum(), 1e-300)))
+        say(f"    128K {name}: rel-RMS {rel:.2e}, max-abs {float(err.max()):.2e} (max |ref| {np.abs(r).max():.3g})")
+        if name.startswith("dw"):
+            assert rel <= 1e-2 and float(err.max()) <= 2e-2 * float(np.abs(r).max()), name
+        else:
+            assert rel <= 1e-3, name
