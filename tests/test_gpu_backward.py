@@ -155,3 +155,37 @@ def test_backward_beyond_sort_capacity(msa, synth, oracle_lib):
     say(f"[bwd] 65 sequences, {65 * 4 * 128} buckets")
     inp, ids, dout, grads = _forward_backward(msa, synth, wl, kv, ql, 47)
     _check_vs_oracle(oracle_lib, inp, ids, dout, grads, wl, "bwd many buckets")
+
+
+def test_backward_128k_tile_sampled(msa, synth, oracle_lib):
+    """The bench's launch: the last 8192 query rows against the 128K prefix.
+    dO is zero except on 48 sampled rows, so dk / dv are exactly those rows'
+    contributions (which the oracle computes row by row) and dq is exactly 0
+    on every other row."""
+    wl = synth.WORKLOADS["prefill_128k"]
+    lo, hi = wl.seq_len - wl.q_tile, wl.seq_len
+    m = hi - lo
+    say(f"[bwd] 128K tile rows [{lo}, {hi}), sampled dO")
+    inp = synth.prefill_inputs(wl, device="cuda", seed=0)
+    cu_q = torch.tensor([0, m], dtype=torch.int32, device="cuda")
+    cu_k = torch.tensor([0, hi], dtype=torch.int32, device="cuda")
+    q = inp["q"][lo:hi]
+    ids = msa.msa_index_topk(inp["q_idx"][lo:hi], inp["k_idx"], cu_q, cu_k, m, hi, wl.block_size, wl.topk)
+    out, lse = msa.msa_sparse_attn_prefill(q, inp["k"], inp["v"], ids, cu_q, cu_k, m, hi, wl.block_size, wl.topk)
+    rng = np.random.default_rng(48)
+    sample = np.unique(np.concatenate([[0, m - 1], rng.integers(0, m, 46)]))
+    sidx = torch.as_tensor(sample, device="cuda")
+    dout = torch.zeros_like(q)
+    dout[sidx] = synth.normal((len(sample), wl.num_heads, wl.head_dim), torch.bfloat16, "cuda", 48, "dout")
+    dq, dk, dv = msa.msa_sparse_attn_backward(q, inp["k"], inp["v"], out, dout, lse, ids, cu_q, cu_k, m, hi,
+                                              wl.block_size, wl.topk)
+    torch.cuda.synchronize()
+    others = torch.ones(m, dtype=torch.bool, device="cuda")
+    others[sidx] = False
+    assert bool((dq[others] == 0).all()), "dq must be exactly 0 where dO is 0"
+    rows, kstart, pos = oracle_lib.rows_prefill([0, m], [0, hi], sample)
+    rdq, rdk, rdv = oracle_lib.sparse_attn_bwd(host(q), host(inp["k"]), host(inp["v"]), host(dout),
+                                               host(ids).numpy()[sample], kstart, pos, rows, wl.block_size, wl.topk)
+    _compare("dq", dq[sidx], rdq, "128K tile")
+    _compare("dk", dk, rdk, "128K tile")
+    _compare("dv", dv, rdv, "128K tile")
