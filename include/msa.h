@@ -261,9 +261,9 @@ msa_status_t msa_sparse_attn_decode_ex(const void* q, const void* k_cache, const
  *   dk, dv       [Tk, num_kv_heads, head_dim] fp32 out, overwritten: key rows
  *                no query attends get 0
  *   workspace    at least msa_sparse_attn_backward_workspace_size() bytes:
- *                the per-block edge lists of one window of at most 4096 query
+ *                the per-block edge lists of one window of at most 8192 query
  *                rows, one fp32 per (row, head) and the window's bf16 per-slot
- *                dq contributions (4 KB per (row, group, slot): about 1 GB for
+ *                dq contributions (4 KB per (row, group, slot): about 2 GB for
  *                64 query heads, 4 groups and k = 16)
  *
  * Accumulation is fp32; P and dS enter the dK, dV and dQ products as bf16,

@@ -46,8 +46,9 @@ namespace msa {
 
 constexpr int kBwdThreads = 256;
 constexpr int kBwdRow = 136;      // LDS row of Q / dO for one MFMA row: 128 bf16 + 8 pad
-constexpr int kBwdWindow = 4096;  // query rows per edge-list window
+constexpr int kBwdWindow = 8192;  // query rows per edge-list window
 constexpr int kSortMax = kBwdWindow;  // edges of one bucket in one window (<= rows per window)
+static_assert(kBwdWindow <= 65536, "bwd_dkdv sorts rows of the window as 16-bit numbers");
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdKernelArgs {
@@ -173,11 +174,12 @@ struct QuadStage {
   int pos;           // threads 64..67: position of query tid - 64 of the quad
 };
 
-// Loads quad `qi` of the bucket (sorted codes in LDS, n edges) into registers.
+// Loads quad `qi` of the bucket (its edges' rows in the window, sorted, in LDS;
+// n edges) into registers.
 // Nothing here consumes the loaded values (the zeroing of missing rows and the
 // lse scaling happen when the quad is stored), so the loads stay in flight
 // while the previous quad is computed.
-__device__ __forceinline__ void bwd_load_quad(const BwdKernelArgs& a, QuadStage& S, const int32_t* codes, int qi,
+__device__ __forceinline__ void bwd_load_quad(const BwdKernelArgs& a, QuadStage& S, const uint16_t* rows, int qi,
                                               int n, int g, int R, int N, int M, int64_t q0) {
   const int tid = threadIdx.x;
   const int e = 4 * qi;
@@ -193,7 +195,7 @@ __device__ __forceinline__ void bwd_load_quad(const BwdKernelArgs& a, QuadStage&
       const int row = 4 * rq + j;
       const int jq = row >> 4, h = row & 15;
       const bool ok = e + jq < n && h < R;
-      const int64_t t = a.row_lo + (ok ? (codes[e + jq] >> 4) : 0);
+      const int64_t t = a.row_lo + (ok ? rows[e + jq] : 0);
       S.x[u][j] = load8(src + (t * a.Hq + g * R + (ok ? h : 0)) * kHeadDim + 8 * o8);
       S.ok |= ok ? (1u << (4 * u + j)) : 0u;
     }
@@ -201,7 +203,7 @@ __device__ __forceinline__ void bwd_load_quad(const BwdKernelArgs& a, QuadStage&
   if (tid < kQuadRows) {
     const int jq = tid >> 4, h = tid & 15;
     const bool ok = e + jq < n && h < R;
-    const int64_t t = a.row_lo + (ok ? (codes[e + jq] >> 4) : 0);
+    const int64_t t = a.row_lo + (ok ? rows[e + jq] : 0);
     const int64_t rh = t * a.Hq + g * R + (ok ? h : 0);
     S.lse = a.lse[rh];
     S.delta = a.delta[rh];
@@ -209,7 +211,7 @@ __device__ __forceinline__ void bwd_load_quad(const BwdKernelArgs& a, QuadStage&
   } else if (tid < kQuadRows + 4) {
     const int jq = tid - kQuadRows;
     const bool ok = e + jq < n;
-    const int64_t t = a.row_lo + (ok ? (codes[e + jq] >> 4) : 0);
+    const int64_t t = a.row_lo + (ok ? rows[e + jq] : 0);
     S.pos = ok ? (int)((int64_t)N - M + (t - q0)) : -1;
   }
 }
@@ -339,7 +341,7 @@ __device__ __forceinline__ void bwd_quad_compute(const BwdLds& L, int buf, const
 
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
   __shared__ __attribute__((aligned(16))) BwdLds L;
-  __shared__ int32_t codes[kSortMax];
+  __shared__ uint16_t rows[kSortMax];
   const int nbk = a.batch * a.G * a.nb_max;
   if ((int)blockIdx.x >= nbk) return;
   // largest buckets first (bwd_order), so no long bucket starts at the end
@@ -358,23 +360,24 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
   const int64_t rs = (int64_t)a.G * kHeadDim;
   const int tid = threadIdx.x;
 
-  // ---- the bucket's edge codes, sorted ascending in LDS (bitonic).  The
-  // lists are placed by atomics in no fixed order; sorting fixes the order in
-  // which the edges are summed, so dK and dV are reproducible bit for bit.
+  // ---- the rows of the bucket's edges, sorted ascending in LDS (bitonic).
+  // A row selects a block at most once, so the rows are distinct.  The lists
+  // are placed by atomics in no fixed order; sorting fixes the order in which
+  // the edges are summed, so dK and dV are reproducible bit for bit.
   {
     int n2 = 1;
     while (n2 < n) n2 <<= 1;
-    for (int i = tid; i < n2; i += kBwdThreads) codes[i] = i < n ? a.edges[e_lo + i] : 0x7fffffff;
+    for (int i = tid; i < n2; i += kBwdThreads) rows[i] = i < n ? (uint16_t)(a.edges[e_lo + i] >> 4) : (uint16_t)0xffff;
     __syncthreads();
     for (int kk = 2; kk <= n2; kk <<= 1) {
       for (int j = kk >> 1; j > 0; j >>= 1) {
         for (int i = tid; i < n2; i += kBwdThreads) {
           const int ixj = i ^ j;
           if (ixj > i) {
-            const int32_t x = codes[i], y = codes[ixj];
+            const uint16_t x = rows[i], y = rows[ixj];
             if ((x > y) == ((i & kk) == 0)) {
-              codes[i] = y;
-              codes[ixj] = x;
+              rows[i] = y;
+              rows[ixj] = x;
             }
           }
         }
@@ -409,13 +412,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
   // while quad qi is computed, then stored to the other buffer.
   const int nquads = (n + 3) / 4;
   QuadStage S;
-  bwd_load_quad(a, S, codes, 0, n, g, R, N, M, q0);
+  bwd_load_quad(a, S, rows, 0, n, g, R, N, M, q0);
   bwd_store_quad(L, 0, S);
   __syncthreads();
   for (int qi = 0; qi < nquads; ++qi) {
     const int buf = qi & 1;
     const bool more = qi + 1 < nquads;
-    if (more) bwd_load_quad(a, S, codes, qi + 1, n, g, R, N, M, q0);
+    if (more) bwd_load_quad(a, S, rows, qi + 1, n, g, R, N, M, q0);
     bwd_quad_compute(L, buf, kf, vf, dk_acc, dv_acc, key_seq, col, a32, a.scale_log2);
     if (more) bwd_store_quad(L, buf ^ 1, S);
     __syncthreads();
