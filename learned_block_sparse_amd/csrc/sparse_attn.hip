@@ -96,7 +96,7 @@ __device__ __forceinline__ void load_v_chunk(const TKV* vseq, int64_t row_stride
 // T: element type of q, out and the MFMA operands; TKV: storage type of K
 // and V (T, or E4M3 widened to bf16 as it is loaded).
 template <typename T, typename TKV>
-__global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs args) {
+__global__ __launch_bounds__(kAttnThreads, sizeof(T) == 2 ? 2 : 1) void sparse_attn_fwd(AttnKernelArgs args) {
   using V = VtTile<T>;
   __shared__ __attribute__((aligned(16))) T vt_all[kAttnThreads / kWave][V::kElems];
   const int wave = threadIdx.x / kWave;
@@ -185,8 +185,16 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs a
 #pragma unroll
         for (int ds = 0; ds < kHeadDim / 32; ++ds) kfr[kt][ds] = load8_kv<T>(kp + 32 * ds);
       }
-      frag8<T> vbuf[2][2][4];
-      load_v_chunk<T>(vseq, row_stride, key0, p, 0, lane, vbuf[0]);
+      // E4M3 K/V: the four V chunks (128 keys) are all requested right after
+      // the score MFMAs, into the registers the K rows free, so a block costs
+      // two memory round trips (K, then V) and the kernel still fits two
+      // waves per SIMD (30.7 against 42.5 us for the 1M-context decode
+      // batch).  Otherwise two chunk buffers: the first chunk is requested
+      // with K and each later one a chunk ahead (for bf16 K/V the four-chunk
+      // form measured no faster and spills).
+      constexpr int kVBufs = sizeof(TKV) == 1 ? kBlock / 32 : 2;
+      frag8<T> vbuf[kVBufs][2][4];
+      if constexpr (kVBufs == 2) load_v_chunk<T>(vseq, row_stride, key0, p, 0, lane, vbuf[0]);
       f32x4 st[kBlock / 16];
 #pragma unroll
       for (int kt = 0; kt < kBlock / 16; ++kt) {
@@ -194,6 +202,12 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs a
 #pragma unroll
         for (int ds = 0; ds < kHeadDim / 32; ++ds) acc = mma16(kfr[kt][ds], qf[ds], acc);
         st[kt] = acc;
+      }
+      if constexpr (kVBufs == kBlock / 32) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < kBlock / 32; ++ks) load_v_chunk<T>(vseq, row_stride, key0, p, ks, lane, vbuf[ks]);
+        __builtin_amdgcn_sched_barrier(0);
       }
 
       // ---- online softmax (log2 units)
@@ -238,13 +252,14 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_fwd(AttnKernelArgs a
       // ---- O^T[d][head] += V^T[d][key] P^T[key][head], 32 keys at a time
 #pragma unroll
       for (int ks = 0; ks < kBlock / 32; ++ks) {
-        if (ks + 1 < kBlock / 32) load_v_chunk<T>(vseq, row_stride, key0, p, ks + 1, lane, vbuf[(ks + 1) & 1]);
+        if (kVBufs == 2 && ks + 1 < kBlock / 32)
+          load_v_chunk<T>(vseq, row_stride, key0, p, ks + 1, lane, vbuf[(ks + 1) % kVBufs]);
         // Stage V rows key0+32ks .. +31 transposed: vt[d][key], keys contiguous.
 #pragma unroll
         for (int uu = 0; uu < 2; ++uu) {
           const int u = lane + 64 * uu;
           const int kq = u & 7, o8 = u >> 3;
-          const frag8<T>(&r4)[4] = vbuf[ks & 1][uu];
+          const frag8<T>(&r4)[4] = vbuf[ks % kVBufs][uu];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             T* dst = vt + (8 * o8 + e) * V::kStride + 4 * kq;
