@@ -18,7 +18,7 @@
 // and the gradients of sum_{t, g} loss[t, g]: dS_i = softmax(S)_i sum_k A_k - A_i,
 // dq_idx[t, g] = sum_i dS_i k_idx[j*_i], dk_idx[j*_i] += dS_i q_idx[t, g].
 //
-// Kernels, per window of at most 4096 query rows (the selection edge lists of
+// Kernels, per window of at most 8192 query rows (the selection edge lists of
 // the KV-outer schedule, built by the same kernels):
 //   kl_scores  one workgroup per chunk of <= 64 edges of a (sequence, group,
 //              block) bucket: the block's 128 index keys staged in LDS once,
@@ -37,8 +37,12 @@
 
 namespace msa {
 
-constexpr int kKlWindow = 4096;  // query rows per edge-list window
+constexpr int kKlWindow = 8192;  // query rows per edge-list window
 constexpr int kKlSortMax = kKlWindow;
+// kl_dk's sort keys: argmax key (7 bits) above the edge code (row in the window << 4 | slot)
+constexpr int kKlCodeBits = 17;
+static_assert((kKlWindow << 4) <= (1 << kKlCodeBits) && kBlock <= (1 << (31 - kKlCodeBits)),
+              "kl_dk sort key fields");
 constexpr float kKlNegInf = -__builtin_inff();
 
 struct KlArgs {
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(256) void kl_loss(KlArgs a) {
 // ------------------------------------------------------------------ kl_dk
 // One workgroup per (sequence, block), 256 threads: thread (key j = tid / 2,
 // half = tid % 2) owns dims 64 half .. 64 half + 63 of dk_idx[j].  For each
-// group in order, the bucket's edges are keyed (argmax j* << 16 | code) and
+// group in order, the bucket's edges are keyed (argmax j* << 17 | code) and
 // sorted in LDS, so each key's edges form one segment in code order; the
 // thread sums its key's segment in that order.  Segments come from a count
 // of edges per key and its prefix sum.
@@ -274,7 +278,7 @@ __global__ __launch_bounds__(256) void kl_dk(KlArgs a) {
       if (i < n) {
         const int code = a.edges[e_lo + i];
         const int64_t slot = ((int64_t)(code >> 4) * a.G + g) * a.topk + (code & 15);
-        k = (a.j_slot[slot] << 16) | code;  // code < 2^16 (4096 rows x 16 slots)
+        k = (a.j_slot[slot] << kKlCodeBits) | code;
       }
       keys[i] = k;
     }
@@ -297,14 +301,14 @@ __global__ __launch_bounds__(256) void kl_dk(KlArgs a) {
     }
     // segment starts: the first sorted position of each key (keys ascend)
     for (int i = tid; i < n; i += 256) {
-      const int kj = keys[i] >> 16;
-      if (i == 0 || (keys[i - 1] >> 16) != kj) seg[kj] = i + 1;  // +1: 0 marks "no edge"
+      const int kj = keys[i] >> kKlCodeBits;
+      if (i == 0 || (keys[i - 1] >> kKlCodeBits) != kj) seg[kj] = i + 1;  // +1: 0 marks "no edge"
     }
     __syncthreads();
     int s0 = seg[j] - 1;
     if (s0 >= 0) {
-      for (int i = s0; i < n && (keys[i] >> 16) == j; ++i) {
-        const int code = keys[i] & 0xffff;
+      for (int i = s0; i < n && (keys[i] >> kKlCodeBits) == j; ++i) {
+        const int code = keys[i] & ((1 << kKlCodeBits) - 1);
         const int64_t slot = ((int64_t)(code >> 4) * a.G + g) * a.topk + (code & 15);
         const float ds = a.ds_slot[slot];
         const T* qrow = qg + ((a.row_lo + (code >> 4)) * a.G + g) * DI + kHalf * half;
