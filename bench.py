@@ -44,6 +44,11 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MSA prefill tokens/s @128K + decode µs/step @1M ctx, % of roofline (1 GPU)"
 
 
+def note(msg: str) -> None:
+    """A progress line on stderr after each measured leg (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +228,7 @@ def main():
                     "algorithmic_flops": idx_flops + att_flops,
                     "planted_share_last_tile": round(planted_share, 3)},
     }
+    note(f"prefill: {ms_step:.3f} ms/step")
     # ------------------------------------------------------------------ decode
     # (run right after the headline prefill measurement: the extra prefill
     # legs below allocate and free several GB, after which the 5 GB decode
@@ -335,6 +341,7 @@ def main():
             torch.cuda.empty_cache()
 
     decode_leg()
+    note("decode leg done")
 
     # The same index calls with the index tensors rounded to fp8 E4M3 (an extra
     # measurement beside the bf16 headline; the block ids are exact for these
@@ -355,6 +362,7 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     idx8_ms = e0.elapsed_time(e1) / args.steps
+    note("fp8 index leg done")
     result["prefill"]["index_fp8"] = {
         "ms": round(idx8_ms, 3), "tflops": round(idx_flops / (idx8_ms / 1e3) / 1e12, 1),
         "frac_fp8_mfma": round(idx_flops / (idx8_ms / 1e3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
@@ -376,6 +384,7 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     att8_ms = e0.elapsed_time(e1) / args.steps
+    note("fp8 K/V leg done")
     result["prefill"]["attention_fp8_kv"] = {
         "ms": round(att8_ms, 3), "tflops": round(att_flops / (att8_ms / 1e3) / 1e12, 1),
         "frac_mfma": round(att_flops / (att8_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
@@ -405,6 +414,7 @@ def main():
     torch.cuda.synchronize()
     bwd_ms = e0.elapsed_time(e1) / args.steps
     bwd_flops = 2.5 * att_flops  # S recomputed, dP, dV, dK, dQ: five products of the forward's size
+    note("backward leg done")
     result["prefill"]["backward"] = {
         "ms": round(bwd_ms, 3), "tflops": round(bwd_flops / (bwd_ms / 1e3) / 1e12, 1),
         "frac_mfma": round(bwd_flops / (bwd_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -440,6 +450,7 @@ def main():
     kl_ms = e0.elapsed_time(e1) / args.steps
     # scoring the selected blocks' attended keys: 2 d_idx per key and group
     kl_flops = att_flops / (4 * D * Hq) * 2 * DI * G
+    note("KL leg done")
     result["prefill"]["index_kl"] = {"ms": round(kl_ms, 3), "tflops": round(kl_flops / (kl_ms / 1e3) / 1e12, 1),
                                      "algorithmic_flops": kl_flops}
     del inp, calls, q8, k8, kv8, vv8, kl_loss, kl_dq, kl_dk, ws_kl
@@ -466,6 +477,7 @@ def main():
     fe_ms = e0.elapsed_time(e1) / args.steps
     fe_flops = 2.0 * L * synth.D_MODEL * (G + 1) * DI
     fe_bytes = 2.0 * (L * synth.D_MODEL + (G + 1) * DI * synth.D_MODEL + L * (G + 1) * DI)
+    note("front-end leg done")
     result["prefill"]["index_frontend"] = {
         "ms": round(fe_ms, 3), "tflops": round(fe_flops / (fe_ms / 1e3) / 1e12, 1),
         "frac_mfma": round(fe_flops / (fe_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -493,6 +505,7 @@ def main():
     torch.cuda.synchronize()
     feb_ms = e0.elapsed_time(e1) / args.steps
     # the weight-gradient contraction dW = dy^T x; y is recomputed (another fe_flops) rather than stored
+    note("front-end backward leg done")
     result["prefill"]["index_frontend_backward"] = {
         "ms": round(feb_ms, 3), "tflops": round(fe_flops / (feb_ms / 1e3) / 1e12, 1),
         "tflops_with_recompute": round(2 * fe_flops / (feb_ms / 1e3) / 1e12, 1),
@@ -503,6 +516,7 @@ def main():
     # ------------------------------------------------------------ CPU baseline
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        note("CPU baseline done")
 
     print(json.dumps(result), flush=True)
 
