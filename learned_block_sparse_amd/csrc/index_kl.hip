@@ -44,6 +44,7 @@ constexpr int kKlCodeBits = 17;
 static_assert((kKlWindow << 4) <= (1 << kKlCodeBits) && kBlock <= (1 << (31 - kKlCodeBits)),
               "kl_dk sort key fields");
 constexpr float kKlNegInf = -__builtin_inff();
+constexpr int kRmaxKl = 16;  // query heads per group at most
 
 struct KlArgs {
   const void* q_idx;
@@ -196,10 +197,16 @@ __global__ __launch_bounds__(256) void kl_loss(KlArgs a) {
   float Ai = 0.f, Si = kKlNegInf;
   const bool mine = lane < a.topk && ((mask >> lane) & 1u);
   if (mine) {
-    for (int hh = 0; hh < R; ++hh) {
-      const int64_t rh = t * a.Hq + g * R + hh;
-      Ai += __expf(a.block_lse[rh * a.topk + lane] - a.lse[rh]);
+    // all heads' loads in flight together, then summed in head order (R <= 16)
+    float e[kRmaxKl];
+#pragma unroll
+    for (int hh = 0; hh < kRmaxKl; ++hh) {
+      const int64_t rh = t * a.Hq + g * R + (hh < R ? hh : 0);
+      e[hh] = __expf(a.block_lse[rh * a.topk + lane] - a.lse[rh]);
     }
+#pragma unroll
+    for (int hh = 0; hh < kRmaxKl; ++hh)
+      if (hh < R) Ai += e[hh];
     Ai /= (float)R;
     Si = a.s_slot[slot0 + lane];
   }
@@ -222,15 +229,29 @@ __global__ __launch_bounds__(256) void kl_loss(KlArgs a) {
   if (mine) a.ds_slot[slot0 + lane] = dsi;
   if (lane == 0) a.loss[t * a.G + g] = mask ? li : 0.f;
 
-  // dq_idx = sum_i dS_i k_idx[j*_i], slots in order
+  // dq_idx = sum_i dS_i k_idx[j*_i], slots in order.  The key rows of all
+  // slots are loaded first (an unattended slot reads the first attended
+  // slot's row and is not summed), so their loads are in flight together.
   const T* kg = static_cast<const T*>(a.k_idx);
   float acc0 = 0.f, acc1 = 0.f;
-  for (int i = 0; i < a.topk; ++i) {
-    if (!((mask >> i) & 1u)) continue;
-    const float ds = __shfl(dsi, i, kWave);
-    const int64_t key = kb0 + (int64_t)sel[i] * kBlock + a.j_slot[slot0 + i];
-    acc0 += ds * (float)kg[key * a.DI + lane];
-    if (lane + 64 < a.DI) acc1 += ds * (float)kg[key * a.DI + lane + 64];
+  if (mask != 0u) {
+    const int first = __builtin_ctz(mask);
+    float kv0[16], kv1[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int ii = (i < a.topk && ((mask >> i) & 1u)) ? i : first;
+      const int64_t key = kb0 + (int64_t)sel[ii] * kBlock + a.j_slot[slot0 + ii];
+      kv0[i] = (float)kg[key * a.DI + lane];
+      kv1[i] = lane + 64 < a.DI ? (float)kg[key * a.DI + lane + 64] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < a.topk && ((mask >> i) & 1u)) {
+        const float ds = __shfl(dsi, i, kWave);
+        acc0 += ds * kv0[i];
+        if (lane + 64 < a.DI) acc1 += ds * kv1[i];
+      }
+    }
   }
   float* dq = a.dq_idx + (t * a.G + g) * a.DI;
   dq[lane] = acc0;
