@@ -253,6 +253,12 @@ def main():
                    "num_kv_heads": G, "head_dim": D, "index_dim": DI, "block_size": wl.block_size,
                    "topk": wl.topk, "planted_blocks": wl.planted},
         "roofline": roofline,
+        # the pages' own figures (H800, 1M context, against dense GQA with the same heads): context only,
+        # not a target; the FLOP ratio is also recomputed from the work model used for the roofline
+        "context": {"pages_prefill_speedup_vs_gqa_1m_h800": 14.2, "pages_decode_speedup_vs_gqa_1m_h800": 7.6,
+                    "pages_attention_flop_cut_1m": 28.4,
+                    "work_model_attention_flop_cut_1m": round(workmodel.per_token_flop_ratio(
+                        1 << 20, Hq, G, D, DI, wl.block_size, wl.topk), 2)},
         "prefill": {"index_ms": round(float(idx_ms), 3), "attention_ms": round(float(att_ms), 3),
                     "index_tflops": round(idx_tflops, 1), "attention_tflops": round(att_tflops, 1),
                     "total_tflops": round(tot_tflops, 1),
