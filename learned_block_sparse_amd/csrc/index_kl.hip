@@ -326,18 +326,34 @@ __global__ __launch_bounds__(256) void kl_dk(KlArgs a) {
       if (i == 0 || (keys[i - 1] >> kKlCodeBits) != kj) seg[kj] = i + 1;  // +1: 0 marks "no edge"
     }
     __syncthreads();
-    int s0 = seg[j] - 1;
+    const int s0 = seg[j] - 1;
     if (s0 >= 0) {
-      for (int i = s0; i < n && (keys[i] >> kKlCodeBits) == j; ++i) {
-        const int code = keys[i] & ((1 << kKlCodeBits) - 1);
-        const int64_t slot = ((int64_t)(code >> 4) * a.G + g) * a.topk + (code & 15);
-        const float ds = a.ds_slot[slot];
-        const T* qrow = qg + ((a.row_lo + (code >> 4)) * a.G + g) * DI + kHalf * half;
+      int s1 = s0 + 1;  // end of this key's segment
+      while (s1 < n && (keys[s1] >> kKlCodeBits) == j) ++s1;
+      // kBatch edges' rows are loaded together, then summed in segment order
+      // (a batch past the end re-reads the segment's last edge, not summed;
+      // 2 measured faster than 4, which costs the kernel a wave per SIMD)
+      constexpr int kBatch = 2;
+      for (int i0 = s0; i0 < s1; i0 += kBatch) {
+        float ds[kBatch];
+        frag8<T> v[kBatch][kHalf / 8];
 #pragma unroll
-        for (int d8 = 0; d8 < kHalf; d8 += 8) {
-          const frag8<T> v8 = load8(qrow + d8);
+        for (int u = 0; u < kBatch; ++u) {
+          const int code = keys[min(i0 + u, s1 - 1)] & ((1 << kKlCodeBits) - 1);
+          const int64_t slot = ((int64_t)(code >> 4) * a.G + g) * a.topk + (code & 15);
+          ds[u] = a.ds_slot[slot];
+          const T* qrow = qg + ((a.row_lo + (code >> 4)) * a.G + g) * DI + kHalf * half;
 #pragma unroll
-          for (int u = 0; u < 8; ++u) acc[d8 + u] += ds * (float)v8[u];
+          for (int d8 = 0; d8 < kHalf; d8 += 8) v[u][d8 / 8] = load8(qrow + d8);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (i0 + u < s1) {
+#pragma unroll
+            for (int d8 = 0; d8 < kHalf; d8 += 8)
+#pragma unroll
+              for (int w = 0; w < 8; ++w) acc[d8 + w] += ds[u] * (float)v[u][d8 / 8][w];
+          }
         }
       }
     }
