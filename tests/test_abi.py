@@ -176,3 +176,70 @@ def test_frontend_backward_argument_errors_and_workspace(L):
     assert ws >= 131072 * 640 * 2 + 640 * 3072 * 4
     assert L.msa_index_frontend_backward_workspace_size(0, 3072, 4, 128) == 0
     assert L.msa_index_frontend_backward_workspace_size(10, 3000, 4, 128) == 0
+
+
+def _backward(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, dtype=1, bi=FAKE, cuq=FAKE, cuk=FAKE, batch=1,
+             mq=256, mk=256, Hq=64, Hkv=4, D=128, bk=128, topk=16, scale=0.0, dq=FAKE, dk=FAKE, dv=FAKE, ws=None,
+             wsb=0, stream=None)
+    a.update(kw)
+    return L.msa_sparse_attn_backward(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dtype"], a["bi"],
+                                      a["cuq"], a["cuk"], a["batch"], a["mq"], a["mk"], a["Hq"], a["Hkv"], a["D"],
+                                      a["bk"], a["topk"], a["scale"], a["dq"], a["dk"], a["dv"], a["ws"], a["wsb"],
+                                      a["stream"])
+
+
+def test_backward_argument_errors_and_workspace(L):
+    assert _backward(L, dout=None) == 1
+    assert _backward(L, lse=None) == 1
+    assert _backward(L, dk=None) == 1
+    assert _backward(L, Hq=63) == 1          # not a multiple of Hkv
+    assert _backward(L, dtype=0) == 2        # the backward takes bf16 inputs only
+    assert _backward(L, D=64) == 2
+    assert _backward(L, topk=17) == 2
+    assert _backward(L) == 3                 # edge lists and dq partials need a workspace
+    # one window of at most 8192 rows: edge lists, delta per (row, head) and bf16 dq partials per slot
+    ws = L.msa_sparse_attn_backward_workspace_size(1, 8192, 131072, 64, 4, 128, 16)
+    assert ws >= 8192 * 4 * 16 * 16 * 128 * 2 + 8192 * 64 * 4
+    # the window is capped: a longer call needs no more partial space than 8192 rows
+    ws2 = L.msa_sparse_attn_backward_workspace_size(1, 65536, 131072, 64, 4, 128, 16)
+    assert ws2 - ws < 65536 * 64 * 4 + (1 << 20)
+    assert L.msa_sparse_attn_backward_workspace_size(0, 8192, 131072, 64, 4, 128, 16) == 0
+
+
+def _kl(L, **kw):
+    a = dict(qi=FAKE, ki=FAKE, dtype=1, bi=FAKE, lse=FAKE, blse=FAKE, cuq=FAKE, cuk=FAKE, batch=1, mq=256, mk=256,
+             Hq=64, G=4, DI=128, bk=128, topk=16, loss=FAKE, dq=FAKE, dk=FAKE, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return L.msa_index_kl_backward(a["qi"], a["ki"], a["dtype"], a["bi"], a["lse"], a["blse"], a["cuq"], a["cuk"],
+                                   a["batch"], a["mq"], a["mk"], a["Hq"], a["G"], a["DI"], a["bk"], a["topk"],
+                                   a["loss"], a["dq"], a["dk"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_index_kl_argument_errors_and_workspace(L):
+    assert _kl(L, blse=None) == 1            # the forward's per-slot block LSEs are required
+    assert _kl(L, loss=None) == 1
+    assert _kl(L, Hq=62) == 1                # not a multiple of the groups
+    assert _kl(L, DI=96) == 2
+    assert _kl(L, Hq=68, G=4) == 2           # 17 heads per group
+    assert _kl(L, dtype=2) == 2              # E4M3 index tensors are not taken here
+    assert _kl(L) == 3
+    ws = L.msa_index_kl_workspace_size(1, 8192, 131072, 4, 16)
+    assert ws >= 8192 * 4 * 16 * 4 * 3       # score, argmax and dS per attended slot of one window
+    assert L.msa_index_kl_workspace_size(1, 8192, 131072, 0, 16) == 0
+
+
+def test_attention_ex_element_types(L):
+    # bf16 q/out with E4M3 K/V is the one mixed pair; E4M3 q, or E4M3 K/V under fp32 q, is unsupported
+    # (the accepted pair itself is not called here: it would launch)
+    args = [FAKE, FAKE, FAKE, 1, 2, FAKE, FAKE, FAKE, 1, 256, 256, 64, 4, 128, 128, 16, 0.0, 1, FAKE, None, None,
+            None, 0, None]
+    bad = list(args)
+    bad[3], bad[4] = 0, 2
+    assert L.msa_sparse_attn_prefill_ex(*bad) == 2
+    bad = list(args)
+    bad[3], bad[4] = 2, 2
+    assert L.msa_sparse_attn_prefill_ex(*bad) == 2
+    dec = [FAKE, FAKE, FAKE, 0, 2, FAKE, FAKE, FAKE, 4, 4096, 64, 4, 128, 128, 16, 0.0, 1, FAKE, None, None, None,
+           0, None]
+    assert L.msa_sparse_attn_decode_ex(*dec) == 2
