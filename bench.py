@@ -554,6 +554,21 @@ def main():
     del fe, fe_q, fe_k, fe_dq, fe_dk, ws_feb
     torch.cuda.empty_cache()
 
+    # what this GPU reaches on a plain 1 GiB device-to-device copy (bytes read + written per second), for
+    # comparison with the attention call's counted traffic rate (measured last: its 2 GiB of buffers
+    # would otherwise precede the decode leg)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    result["roofline"]["copy_GBs"] = round(2 * (1 << 30) * 10 / (c0.elapsed_time(c1) / 1e3) / 1e9, 1)
+    del src, dst
+
     # ------------------------------------------------------------ CPU baseline
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
