@@ -62,6 +62,9 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--workload", default="prefill_128k", choices=["prefill_128k", "prefill_32k", "prefill_1m"],
+                    help="prefill workload of the headline measurement; other than the default, only the "
+                         "prefill leg runs (32K: one call for the whole sequence; 1M: 128 calls of 8192 queries)")
     ap.add_argument("--two-stream", action="store_true",
                     help="also time the prefill step with its index calls on a second stream ahead of the "
                          "attention calls (reported as prefill.two_stream_ms_per_step)")
@@ -118,8 +121,9 @@ def main():
         return
 
     # ------------------------------------------------------------------ prefill
-    wl = synth.WORKLOADS["prefill_128k"]
-    L, T = wl.seq_len, wl.q_tile
+    wl = synth.WORKLOADS[args.workload]
+    L = wl.seq_len
+    T = wl.q_tile or L  # one call for the whole sequence when the workload has no tile size
     inp = synth.prefill_inputs(wl, device=dev, seed=0)
     G, DI, Hq, D = wl.num_kv_heads, wl.index_dim, wl.num_heads, wl.head_dim
     tiles = [(lo, min(lo + T, L)) for lo in range(0, L, T)]
@@ -228,12 +232,12 @@ def main():
         dom_ms = float(np.mean(per_call_idx))
         dom_flops = idx_flops / len(calls)
         kernel = "idx_scan_prefill<bf16,128> + idx_select_prefill (one msa_index_topk call)"
-        traffic = traffic_record("index_prefill_128k")
+        traffic = traffic_record(f"index_{args.workload}")
     else:
         dom_ms = float(np.mean(per_call_att))
         dom_flops = att_flops / len(calls)
         kernel = "kvo_attn + kvo_combine + edge-list kernels (one msa_sparse_attn_prefill call)"
-        traffic = traffic_record("attention_prefill_128k")
+        traffic = traffic_record(f"attention_{args.workload}")
     achieved = dom_flops / (dom_ms / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
@@ -249,7 +253,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "prefill_128k", "batch": 1, "seq_len": L, "q_tile": T, "num_heads": Hq,
+        "config": {"workload": args.workload, "batch": 1, "seq_len": L, "q_tile": T, "num_heads": Hq,
                    "num_kv_heads": G, "head_dim": D, "index_dim": DI, "block_size": wl.block_size,
                    "topk": wl.topk, "planted_blocks": wl.planted},
         "roofline": roofline,
@@ -270,6 +274,11 @@ def main():
     if ms_step_two_stream is not None:
         result["prefill"]["two_stream_ms_per_step"] = round(ms_step_two_stream, 3)
     note(f"prefill: {ms_step:.3f} ms/step")
+    if args.workload != "prefill_128k":
+        # the other prefill lengths: the prefill measurement alone (the decode and extra legs are sized for
+        # the 128K workload)
+        print(json.dumps(result), flush=True)
+        return
     # ------------------------------------------------------------------ decode
     # (run right after the headline prefill measurement: the extra prefill
     # legs below allocate and free several GB, after which the 5 GB decode
