@@ -696,11 +696,30 @@ def cpu_baseline(target_s: float):
     t_cal = run(n0)
     n = int(max(n0, min(8192, n0 * target_s / max(t_cal, 1e-3))))
     t = run(n)
+    # one core: the oracle's OpenMP regions limited to one thread, on a smaller sample (about half the time)
+    single = None
+    try:
+        import ctypes
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(1)
+        n1 = max(8, n // (2 * threads))
+        t1 = run(n1)
+        gomp.omp_set_num_threads(threads)
+        single = {"value": round(n1 / t1, 2), "rows": n1, "seconds": round(t1, 1)}
+    except OSError:
+        pass
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     del inp
     torch.set_num_threads(torch.get_num_threads())
     return {"value": round(n / t, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} query rows evenly spaced over positions 0..131071 of the 128K prefill "
-                      f"(index scan + top-k + attention per row), {t:.1f} s"}
+                      f"(index scan + top-k + attention per row), {t:.1f} s",
+            "cpu_model": model, "single_core": single}
 
 
 if __name__ == "__main__":
