@@ -38,8 +38,12 @@
  *    buffers; the kernels never read outside [row 0, last row of the
  *    sequence], ignore block ids < 0 or > l, and never write outside the rows
  *    the lengths describe.
- *  - Results are deterministic: the same inputs give bit-identical outputs,
- *    independent of how the work is split.
+ *  - Results are deterministic: repeated calls with the same inputs, sizes
+ *    and num_splits give bit-identical outputs.  Block ids never depend on
+ *    the schedule.  Attention outputs of calls that take different schedules
+ *    (another num_splits, or a batch whose size switches between the
+ *    KV-outer and the query-outer schedule) agree within bf16 rounding of the
+ *    partial results, not bitwise.
  *
  * Supported shapes: block_size 128; head_dim 128; index_dim 64 or 128;
  * 1 <= topk <= 16; num_heads % num_kv_heads == 0 with at most 16 heads per

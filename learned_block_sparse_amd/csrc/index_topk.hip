@@ -15,11 +15,21 @@
 //                     by 8 waves; scores come from 32x32 MFMA tiles oriented
 //                     keys x columns, so a column's 128 scores sit in two lanes
 //                     (16 registers x 4 tiles each) and the block max is a
-//                     register max plus one lane swap.  Each lane then owns
-//                     one column and keeps a sorted top-15 list in registers.
-//   idx_merge_prefill 8 lanes per (query, group): merge the per-chunk lists
-//                     under the same total order, adds the local block, writes
-//                     ids ascending.
+//                     register max plus one lane swap.  The pooled score of
+//                     every (row, group, earlier block) is written to the
+//                     workspace as fp32, [rows, G, score_stride], in aligned
+//                     64-byte runs of 16 consecutive blocks.  The top-k is not
+//                     kept inside the GEMM: a per-lane sorted list there costs
+//                     the whole wave an insertion whenever any of its 64 lanes
+//                     takes a block, which is nearly every block.
+//   idx_select_prefill one wave per (row, group): 64-bit selection keys
+//                     (order-preserving score bits, inverted block id, so the
+//                     lower id wins ties) are read back in rounds of 1024; the
+//                     lane maxima, sorted across the wave, give a threshold
+//                     (their 16th largest, or the 16th best kept from earlier
+//                     rounds if larger), the few keys at or above it are
+//                     compacted by ballots and ranked exactly; the best k-1
+//                     and the local block are written ascending, -1 padded.
 // Decode path (two kernels):
 //   idx_decode_scores streams the index-key cache once: the earlier blocks of
 //                     all sequences are one flat range scored grid-stride by

@@ -15,7 +15,7 @@
 //
 // Steps for one window of query rows (the host loops over windows so the
 // partial buffer stays bounded):
-//   kvo_zero / kvo_count / kvo_scan / kvo_scatter
+//   kvo_zero / kvo_bucket<false> (count) / kvo_scan / kvo_bucket<true> (place)
 //       invert the selection into per-(sequence, group, block) edge lists and
 //       cut each list into chunks of kKvoChunk edges (the pre-scheduled
 //       chunking: hot blocks get several workgroups).  Atomics only count and

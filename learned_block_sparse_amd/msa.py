@@ -15,6 +15,7 @@ The functions carry the C names.  Tensor layouts are those of the header:
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -118,6 +119,24 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _on_launch_stream(fn):
+    """Run ``fn`` with its launch stream as torch's current stream.
+
+    Outputs and workspaces the binding allocates are then owned by the stream
+    the library's kernels run on: the caching allocator hands their memory to
+    a later allocation only on that same stream, ordered after the kernels,
+    even when the caller launches on a side stream and drops the workspace.
+    A raw ``hipStream_t`` handle is wrapped as an external stream."""
+    @functools.wraps(fn)
+    def wrapped(*args, stream=None, **kwargs):
+        if stream is None:
+            return fn(*args, stream=None, **kwargs)
+        s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+        with torch.cuda.stream(s):
+            return fn(*args, stream=s, **kwargs)
+    return wrapped
+
+
 def _check(status: int, where: str):
     if status != MSA_OK:
         raise MSAError(status, where)
@@ -143,6 +162,7 @@ def msa_sparse_attn_workspace_size(batch, max_q_len, max_kv_len, num_heads, num_
                                                 head_dim, topk, num_splits)
 
 
+@_on_launch_stream
 def msa_index_topk(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, max_q_len: int, max_kv_len: int,
                    block_size: int = 128, topk: int = 16, block_idx=None, workspace=None, stream=None):
     """Selected block ids ``[Tq, G, topk]`` (int32, ascending, -1 padded)."""
@@ -216,6 +236,7 @@ def _decode(ex, q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx
     return out, lse
 
 
+@_on_launch_stream
 def msa_sparse_attn_prefill(q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_q_len: int,
                             max_kv_len: int, block_size: int = 128, topk: int = 16,
                             softmax_scale: float = 0.0, num_splits: int = 0, out=None, lse=None,
@@ -225,6 +246,7 @@ def msa_sparse_attn_prefill(q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_
                     topk, softmax_scale, num_splits, out, lse, return_lse, workspace, stream)
 
 
+@_on_launch_stream
 def msa_sparse_attn_prefill_ex(q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, max_q_len: int,
                                max_kv_len: int, block_size: int = 128, topk: int = 16,
                                softmax_scale: float = 0.0, num_splits: int = 0, out=None, lse=None,
@@ -236,6 +258,7 @@ def msa_sparse_attn_prefill_ex(q, k, v, block_idx, cu_seqlens_q, cu_seqlens_k, m
                     topk, softmax_scale, num_splits, out, lse, return_lse, workspace, stream, block_lse)
 
 
+@_on_launch_stream
 def msa_sparse_attn_decode(q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx: int,
                            block_size: int = 128, topk: int = 16, softmax_scale: float = 0.0,
                            num_splits: int = 0, out=None, lse=None, return_lse: bool = True,
@@ -245,6 +268,7 @@ def msa_sparse_attn_decode(q, k_cache, v_cache, block_idx, cache_offsets, ctx_le
                    softmax_scale, num_splits, out, lse, return_lse, workspace, stream)
 
 
+@_on_launch_stream
 def msa_sparse_attn_decode_ex(q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx: int,
                               block_size: int = 128, topk: int = 16, softmax_scale: float = 0.0,
                               num_splits: int = 0, out=None, lse=None, return_lse: bool = True,
@@ -262,6 +286,7 @@ def msa_sparse_attn_backward_workspace_size(batch, max_q_len, max_kv_len, num_he
                                                          head_dim, topk)
 
 
+@_on_launch_stream
 def msa_sparse_attn_backward(q, k, v, out, dout, lse, block_idx, cu_seqlens_q, cu_seqlens_k, max_q_len: int,
                              max_kv_len: int, block_size: int = 128, topk: int = 16, softmax_scale: float = 0.0,
                              dq=None, dk=None, dv=None, workspace=None, stream=None):
@@ -294,6 +319,7 @@ def msa_index_kl_workspace_size(batch, max_q_len, max_kv_len, num_groups, topk) 
     return lib().msa_index_kl_workspace_size(batch, max_q_len, max_kv_len, num_groups, topk)
 
 
+@_on_launch_stream
 def msa_index_kl_backward(q_idx, k_idx, block_idx, lse, block_lse, cu_seqlens_q, cu_seqlens_k, max_q_len: int,
                           max_kv_len: int, block_size: int = 128, topk: int = 16, loss=None, dq_idx=None,
                           dk_idx=None, workspace=None, stream=None):
@@ -324,6 +350,7 @@ def msa_index_kl_backward(q_idx, k_idx, block_idx, lse, block_lse, cu_seqlens_q,
     return loss, dq_idx, dk_idx
 
 
+@_on_launch_stream
 def msa_index_frontend(x, w_q, w_k, q_norm_weight, k_norm_weight, cu_seqlens_q, cu_seqlens_k, num_groups: int,
                        rope_dim: int = 64, rope_theta: float = 10000.0, norm_eps: float = 1e-6, out_dtype=None,
                        q_idx=None, k_idx=None, num_keys=None, stream=None):
@@ -360,6 +387,7 @@ def msa_index_frontend_backward_workspace_size(total_q, d_model, num_groups, ind
     return int(lib().msa_index_frontend_backward_workspace_size(int(total_q), d_model, num_groups, index_dim))
 
 
+@_on_launch_stream
 def msa_index_frontend_backward(x, w_q, w_k, q_norm_weight, k_norm_weight, cu_seqlens_q, cu_seqlens_k,
                                 num_groups: int, dq_idx, dk_idx, rope_dim: int = 64, rope_theta: float = 10000.0,
                                 norm_eps: float = 1e-6, dw_q=None, dw_k=None, dq_norm_weight=None,
