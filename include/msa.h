@@ -419,6 +419,30 @@ msa_status_t msa_index_frontend_backward(const void* x, const void* w_q, const v
                                          float* dw_q, float* dw_k, float* dq_norm_weight, float* dk_norm_weight,
                                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * msa_index_topk without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation.  Same arguments, checks, kernels and results as
+ * msa_index_topk (bit-identical block ids), minus the workspace: the scratch
+ * is a static device array of MSA_NOALLOC_SCRATCH_BYTES inside the library,
+ * one per GPU, held until the process ends.  Calls whose
+ * msa_index_topk_workspace_size() exceeds it return MSA_ERR_WORKSPACE before
+ * any launch (for example decode of 32 sequences at 1M context needs 4 MiB;
+ * prefill needs rows * G * ceil(max_kv_len / 128) * 4 bytes).  `stream` must
+ * belong to the current device (MSA_ERR_INVALID_ARG otherwise).  The call
+ * allocates nothing (no hipMalloc, no memset) and keeps no result in the
+ * scratch that a later call relies on.  All calls on one GPU share its
+ * scratch: calls that may overlap in time on one GPU (different streams
+ * without ordering, several host threads) race and give undefined ids;
+ * serialize them on one stream.
+ * ---------------------------------------------------------------------- */
+#define MSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+msa_status_t msa_index_topk_noalloc(const void* q_idx, const void* k_idx, msa_dtype_t dtype,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                                    int max_q_len, int max_kv_len, int num_groups, int index_dim,
+                                    int block_size, int topk, int32_t* block_idx, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,6 +7,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace msa {
 
 static constexpr size_t kAlign = 256;
@@ -117,6 +119,17 @@ using namespace msa;
 
 static thread_local int g_last_hip_error = 0;
 
+// Scratch of msa_index_topk_noalloc: a file-scope device array, so that call
+// needs no allocation.  Every GPU the library runs on holds its own copy, at
+// its own address, until the process ends.  In host code the array's name is
+// not a device address: the per-device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MSA_NOALLOC_SCRATCH_BYTES];
+static constexpr int kMaxDevices = 64;
+static void* g_scratch_addr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
 static msa_status_t hip_status(hipError_t e) {
   if (e == hipSuccess) return MSA_OK;
   g_last_hip_error = (int)e;
@@ -163,6 +176,47 @@ msa_status_t msa_index_topk(const void* q_idx, const void* k_idx, msa_dtype_t dt
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes)) return MSA_ERR_WORKSPACE;
   return hip_status(launch_index_topk(pl, (int)dtype, index_dim, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k,
                                       batch, num_groups, topk, block_idx, workspace, stream));
+}
+
+msa_status_t msa_index_topk_noalloc(const void* q_idx, const void* k_idx, msa_dtype_t dtype,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                                    int max_q_len, int max_kv_len, int num_groups, int index_dim,
+                                    int block_size, int topk, int32_t* block_idx, hipStream_t stream) {
+  if (!q_idx || !k_idx || !cu_seqlens_q || !cu_seqlens_k || !block_idx) return MSA_ERR_INVALID_ARG;
+  if (batch <= 0 || max_q_len <= 0 || max_kv_len <= 0 || num_groups <= 0 || index_dim <= 0 ||
+      block_size <= 0 || topk <= 0 || !dtype_ok(dtype))
+    return MSA_ERR_INVALID_ARG;
+  if (block_size != kBlock || (index_dim != 64 && index_dim != 128) || topk > 16 || num_groups > 16)
+    return MSA_ERR_UNSUPPORTED;
+  const IndexPlan pl = plan_index(batch, max_q_len, max_kv_len, num_groups);
+  if (pl.workspace_bytes > (size_t)MSA_NOALLOC_SCRATCH_BYTES) return MSA_ERR_WORKSPACE;
+  // the scratch of the device the stream runs on, which must be the current one
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (stream != nullptr) {
+    int sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return hip_status(e);
+    if (sdev != dev) return MSA_ERR_INVALID_ARG;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return MSA_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_addr[dev] == nullptr) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e);
+      if (addr == nullptr) return hip_status(hipErrorInvalidSymbol);
+      g_scratch_addr[dev] = addr;
+    }
+    ws = g_scratch_addr[dev];
+  }
+  // Nothing in the scratch has to start at zero: the scans write every block
+  // score (and the decode block offsets) before the selection reads it.
+  return hip_status(launch_index_topk(pl, (int)dtype, index_dim, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k,
+                                      batch, num_groups, topk, block_idx, ws, stream));
 }
 
 size_t msa_sparse_attn_workspace_size(int batch, int max_q_len, int max_kv_len, int num_heads,

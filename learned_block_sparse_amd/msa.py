@@ -56,6 +56,8 @@ def lib():
         L.msa_index_topk_workspace_size.argtypes = [i32] * 6
         L.msa_index_topk.restype = i32
         L.msa_index_topk.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, sz, vp]
+        L.msa_index_topk_noalloc.restype = i32
+        L.msa_index_topk_noalloc.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
         L.msa_sparse_attn_workspace_size.restype = sz
         L.msa_sparse_attn_workspace_size.argtypes = [i32] * 8
         L.msa_sparse_attn_prefill.restype = i32
@@ -234,6 +236,34 @@ def _decode(ex, q, k_cache, v_cache, block_idx, cache_offsets, ctx_lens, max_ctx
             ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
     _check(st, "msa_sparse_attn_decode_ex" if ex else "msa_sparse_attn_decode")
     return out, lse
+
+
+# Size of the static scratch msa_index_topk_noalloc uses (MSA_NOALLOC_SCRATCH_BYTES in include/msa.h).
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+@_on_launch_stream
+def msa_index_topk_noalloc(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, max_q_len: int, max_kv_len: int,
+                           block_size: int = 128, topk: int = 16, block_idx=None, stream=None):
+    """msa_index_topk with the library's static scratch instead of a workspace.
+
+    Pass ``block_idx`` (``[Tq, G, topk]`` int32) to make the call allocate
+    nothing at all; calls on one GPU must not overlap in time."""
+    if q_idx.dim() != 3 or k_idx.dim() != 2 or q_idx.shape[2] != k_idx.shape[1]:
+        raise ValueError("q_idx must be [Tq, G, d_idx] and k_idx [Tk, d_idx]")
+    if q_idx.dtype != k_idx.dtype:
+        raise TypeError("q_idx and k_idx must share a dtype")
+    tq, G, di = q_idx.shape
+    batch = cu_seqlens_q.numel() - 1
+    if block_idx is None:
+        block_idx = torch.empty((tq, G, topk), dtype=torch.int32, device=q_idx.device)
+    st = lib().msa_index_topk_noalloc(_dev(q_idx, "q_idx"), _dev(k_idx, "k_idx"), _dtype_code(q_idx),
+                                      _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+                                      _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32), batch, max_q_len,
+                                      max_kv_len, G, di, block_size, topk,
+                                      _dev(block_idx, "block_idx", torch.int32), _stream(stream))
+    _check(st, "msa_index_topk_noalloc")
+    return block_idx
 
 
 @_on_launch_stream

@@ -79,6 +79,26 @@ def test_index_topk_argument_errors(L):
     assert _index(L, ws=FAKE, wsb=16) == 3
 
 
+def test_index_topk_noalloc_argument_errors(L):
+    """The allocation-free variant checks like msa_index_topk and refuses calls
+    whose scratch would exceed its static array, all before any HIP call."""
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, dtype=1, cuq=FAKE, cuk=FAKE, batch=1, mq=256, mk=256, G=4, DI=128,
+                 bk=128, topk=16, out=FAKE, stream=None)
+        a.update(kw)
+        return L.msa_index_topk_noalloc(a["q"], a["k"], a["dtype"], a["cuq"], a["cuk"], a["batch"], a["mq"],
+                                        a["mk"], a["G"], a["DI"], a["bk"], a["topk"], a["out"], a["stream"])
+    assert call(out=None) == 1
+    assert call(batch=0) == 1
+    assert call(dtype=7) == 1
+    assert call(bk=64) == 2
+    assert call(topk=17) == 2
+    limit = 32 << 20
+    assert L.msa_index_topk_workspace_size(1, 32768, 32768, 4, 128, 16) > limit
+    assert call(mq=32768, mk=32768) == 3
+    assert L.msa_index_topk_workspace_size(32, 1, 1 << 20, 4, 128, 16) <= limit
+
+
 def test_workspace_sizes(L):
     # a single block per sequence needs no candidate buffer
     assert L.msa_index_topk_workspace_size(1, 100, 100, 4, 128, 16) == 0
