@@ -25,8 +25,14 @@ attention: 4 * D * Hq * |J| per query) per call divided by the call's mean
 duration, against MI355X's dense bf16 MFMA peak (2.5 PFLOP/s); decode against
 HBM (8 TB/s) with the index-key scan plus selected K/V bytes.
 
-cpu_baseline: the CPU oracle (unchanged, as the tests use it) on a stratified
-sample of query rows of the same 128K workload, on this host's cores.
+The default run also times the other prefill lengths of the sweep the pages
+measure (32K in one call; 1M in 128 calls of 8192 queries, 256 planted
+blocks) and reports them under "prefill_32k" / "prefill_1m".
+
+cpu_baseline: the CPU oracle (unchanged, as the tests use it) on this host's
+cores: a stratified sample of query rows of the same 128K workload, and
+(under "decode") every fourth sequence of the decode step, scaled to the
+whole step by context tokens.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -62,6 +68,8 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extra-prefill", action="store_true",
+                    help="skip the 32K and 1M prefill legs of the default 128K run")
     ap.add_argument("--workload", default="prefill_128k", choices=["prefill_128k", "prefill_32k", "prefill_1m"],
                     help="prefill workload of the headline measurement; other than the default, only the "
                          "prefill leg runs (32K: one call for the whole sequence; 1M: 128 calls of 8192 queries)")
@@ -80,50 +88,17 @@ def parse():
     return ap.parse_args()
 
 
-def traffic_record(kernel_key):
-    """HBM bytes per launch measured with rocprofv3 counters, if the kernel
-    source is unchanged since they were taken (else None)."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
-        return None
-    try:
-        rec = json.load(open(path)).get(kernel_key)
-    except (OSError, ValueError):
-        return None
-    if not rec:
-        return None
-    from learned_block_sparse_amd import build
-    if rec.get("source_sha") != build.source_digest():
-        return None
-    return rec.get("bytes_per_launch")
+def prefill_workload(args, msa, synth, workmodel, torch, np, wl, stream, steps, warmup, two_stream=False):
+    """Set up one prefill workload on the GPU and time its step.
 
-
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the MSA path here is a "
-              "single-GPU library and no multi-GPU figure is produced", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-
-    from learned_block_sparse_amd import msa, synth, workmodel
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    msa.lib()
+    A step runs the workload's query tiles in order (one call for the whole
+    sequence when the workload has no tile size), each tile an index call
+    (msa_index_topk) then an attention call (msa_sparse_attn_prefill) against
+    the causal prefix ending at the tile.  Returns the inputs, the calls, the
+    step function and the measurements."""
     dev = "cuda"
-    stream = torch.cuda.current_stream()
-    if args.profile:
-        profile_run(args, msa, synth, torch)
-        return
-
-    # ------------------------------------------------------------------ prefill
-    wl = synth.WORKLOADS[args.workload]
     L = wl.seq_len
-    T = wl.q_tile or L  # one call for the whole sequence when the workload has no tile size
+    T = wl.q_tile or L
     inp = synth.prefill_inputs(wl, device=dev, seed=0)
     G, DI, Hq, D = wl.num_kv_heads, wl.index_dim, wl.num_heads, wl.head_dim
     tiles = [(lo, min(lo + T, L)) for lo in range(0, L, T)]
@@ -180,44 +155,36 @@ def main():
         stream.wait_stream(side)
 
     def timed(step):
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             step()
         torch.cuda.synchronize()
         # the timed steps: nothing but the library calls between the two synchronisations
         t0 = time.perf_counter()
-        for s in range(args.steps):
+        for s in range(steps):
             step()
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / args.steps
+        return (time.perf_counter() - t0) * 1e3 / steps
 
     ms_step = timed(run_step)
     # opt-in: the same step with the index calls running ahead on the second
     # stream (its kernels overlap, so it is kept out of default runs, whose
     # per-kernel profiles must match the one-stream per-call timings)
-    ms_step_two_stream = timed(run_step_pipelined) if args.two_stream else None
+    ms_step_two_stream = timed(run_step_pipelined) if two_stream else None
     # the per-call breakdown: the same steps again, with events around every call
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in calls] for _ in range(args.steps)]
-    for s in range(args.steps):
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in calls] for _ in range(steps)]
+    for s in range(steps):
         run_step(ev[s])
     torch.cuda.synchronize()
-    idx_ms = np.mean([sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for j in range(len(calls)))
-                      for s in range(args.steps)])
-    att_ms = np.mean([sum(ev[s][j][1].elapsed_time(ev[s][j][2]) for j in range(len(calls)))
-                      for s in range(args.steps)])
-    per_call_idx = [np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)])
-                    for j in range(len(calls))]
-    per_call_att = [np.mean([ev[s][j][1].elapsed_time(ev[s][j][2]) for s in range(args.steps)])
-                    for j in range(len(calls))]
+    idx_ms = np.mean([sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for j in range(len(calls))) for s in range(steps)])
+    att_ms = np.mean([sum(ev[s][j][1].elapsed_time(ev[s][j][2]) for j in range(len(calls))) for s in range(steps)])
+    per_call_idx = [np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(steps)]) for j in range(len(calls))]
+    per_call_att = [np.mean([ev[s][j][1].elapsed_time(ev[s][j][2]) for s in range(steps)]) for j in range(len(calls))]
 
     idx_flops = att_flops = 0.0
     for c in calls:
         pos = np.arange(c["lo"], c["hi"])
         idx_flops += workmodel.index_flops(pos, G, DI, wl.block_size)
         att_flops += workmodel.attn_flops(pos, Hq, D, wl.block_size, wl.topk)
-    tokens_s = L / (ms_step / 1e3)
-    idx_tflops = idx_flops / (idx_ms / 1e3) / 1e12
-    att_tflops = att_flops / (att_ms / 1e3) / 1e12
-    tot_tflops = (idx_flops + att_flops) / (ms_step / 1e3) / 1e12
 
     # planted-block share of the selections (workload skew), last tile
     last = calls[-1]
@@ -226,6 +193,82 @@ def main():
     local = (np.arange(last["lo"], last["hi"]) // wl.block_size)[:, None, None]
     nonlocal_sel = sel[(sel >= 0) & (sel != local)]
     planted_share = float(np.isin(nonlocal_sel, list(planted)).mean()) if planted else 0.0
+    return dict(inp=inp, calls=calls, run_step=run_step, T=T, ms_step=ms_step, ms_step_two_stream=ms_step_two_stream,
+                idx_ms=float(idx_ms), att_ms=float(att_ms), per_call_idx=per_call_idx, per_call_att=per_call_att,
+                idx_flops=idx_flops, att_flops=att_flops, planted_share=planted_share)
+
+
+def prefill_summary(wl, P):
+    """The JSON record of a prefill workload measured by prefill_workload."""
+    ms = P["ms_step"]
+    flops = P["idx_flops"] + P["att_flops"]
+    idx_t = P["idx_flops"] / (P["idx_ms"] / 1e3) / 1e12
+    att_t = P["att_flops"] / (P["att_ms"] / 1e3) / 1e12
+    return {"seq_len": wl.seq_len, "q_tile": P["T"], "calls": len(P["calls"]), "planted_blocks": wl.planted,
+            "ms_per_step": round(ms, 3), "tokens_s": round(wl.seq_len / (ms / 1e3), 1),
+            "total_tflops": round(flops / (ms / 1e3) / 1e12, 1),
+            "frac_mfma": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "index_ms": round(P["idx_ms"], 3), "attention_ms": round(P["att_ms"], 3),
+            "index_frac_mfma": round(idx_t / PEAK_BF16_TFLOPS, 4),
+            "attention_frac_mfma": round(att_t / PEAK_BF16_TFLOPS, 4), "algorithmic_flops": flops,
+            "planted_share_last_tile": round(P["planted_share"], 3)}
+
+
+def traffic_record(kernel_key):
+    """HBM bytes per launch measured with rocprofv3 counters, if the kernel
+    source is unchanged since they were taken (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    from learned_block_sparse_amd import build
+    if rec.get("source_sha") != build.source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the MSA path here is a "
+              "single-GPU library and no multi-GPU figure is produced", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from learned_block_sparse_amd import msa, synth, workmodel
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    msa.lib()
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    if args.profile:
+        profile_run(args, msa, synth, torch)
+        return
+
+    # ------------------------------------------------------------------ prefill
+    wl = synth.WORKLOADS[args.workload]
+    L = wl.seq_len
+    G, DI, Hq, D = wl.num_kv_heads, wl.index_dim, wl.num_heads, wl.head_dim
+    P = prefill_workload(args, msa, synth, workmodel, torch, np, wl, stream, args.steps, args.warmup,
+                         two_stream=args.two_stream)
+    inp, calls, run_step, T = P["inp"], P["calls"], P["run_step"], P["T"]
+    ms_step, ms_step_two_stream = P["ms_step"], P["ms_step_two_stream"]
+    idx_ms, att_ms, per_call_idx, per_call_att = P["idx_ms"], P["att_ms"], P["per_call_idx"], P["per_call_att"]
+    idx_flops, att_flops = P["idx_flops"], P["att_flops"]
+    tokens_s = L / (ms_step / 1e3)
+    idx_tflops = idx_flops / (idx_ms / 1e3) / 1e12
+    att_tflops = att_flops / (att_ms / 1e3) / 1e12
+    tot_tflops = (idx_flops + att_flops) / (ms_step / 1e3) / 1e12
+    planted_share = P["planted_share"]
 
     dominant = "index" if idx_ms >= att_ms else "attention"
     if dominant == "index":
@@ -387,9 +430,13 @@ def main():
             result["decode"]["fp8_index_and_kv"] = {
                 "us_per_step": round(da8_us, 1), "bytes_per_step": ia8_b + aa8_b, "achieved_GBs": round(gbsa8, 1),
                 "frac_hbm": round(gbsa8 / PEAK_HBM_GBS, 4)}
+            if not args.no_cpu_baseline:
+                cpu_decode.update(cpu_baseline_decode(d, ctx, wd, args.cpu_seconds / 2))
+                note("CPU decode baseline done")
             del d, q8, k8, kc8, vc8
             torch.cuda.empty_cache()
 
+    cpu_decode = {}
     decode_leg()
     note("decode leg done")
 
@@ -504,7 +551,19 @@ def main():
     result["prefill"]["index_kl"] = {"ms": round(kl_ms, 3), "tflops": round(kl_flops / (kl_ms / 1e3) / 1e12, 1),
                                      "algorithmic_flops": kl_flops}
     del inp, calls, q8, k8, kv8, vv8, kl_loss, kl_dq, kl_dk, ws_kl
+    P = run_step = None
     torch.cuda.empty_cache()
+    # The other prefill lengths of the pages' 32K -> 1M sweep, timed like the
+    # headline: 32K in one call for the whole sequence, 1M in 128 calls of 8192
+    # queries against the causal prefix (two timed steps of about 0.6 s).
+    if not args.no_extra_prefill:
+        for name, st, wu in (("prefill_32k", args.steps, args.warmup), ("prefill_1m", 2, 1)):
+            wx = synth.WORKLOADS[name]
+            Px = prefill_workload(args, msa, synth, workmodel, torch, np, wx, stream, st, wu)
+            result[name] = dict(prefill_summary(wx, Px), steps=st, warmup=wu)
+            del Px
+            torch.cuda.empty_cache()
+            note(f"{name} leg done")
     # The index front-end (an extra measurement): the whole 128K sequence's
     # hidden states through the index projections, RMS norm and RoPE in one
     # call (q_idx for every token, the index-key rows of every position).
@@ -581,6 +640,8 @@ def main():
     # ------------------------------------------------------------ CPU baseline
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        if cpu_decode:
+            result["cpu_baseline"]["decode"] = cpu_decode
         note("CPU baseline done")
 
     print(json.dumps(result), flush=True)
@@ -720,6 +781,47 @@ def cpu_baseline(target_s: float):
             "sample": f"{n} query rows evenly spaced over positions 0..131071 of the 128K prefill "
                       f"(index scan + top-k + attention per row), {t:.1f} s",
             "cpu_model": model, "single_core": single}
+
+
+def cpu_baseline_decode(d, ctx, wd, target_s: float):
+    """The oracle's decode step on a sample of the decode workload's sequences:
+    every fourth of the 32 (their index-key, K and V caches copied from the
+    GPU inputs, so the values are those the GPU step reads), repeated for
+    about ``target_s`` seconds; scaled to the 32-sequence step by context
+    tokens (the index-key scan, linear in the context, is nearly all the
+    work)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    B = len(ctx)
+    sample = list(range(0, B, 4))
+    offs, lens = d["k_offsets_host"], d["ctx_lens_host"]
+    sl = [slice(offs[b], offs[b] + lens[b]) for b in sample]
+    kc = torch.cat([d["k"][s] for s in sl]).cpu()
+    vc = torch.cat([d["v"][s] for s in sl]).cpu()
+    kic = torch.cat([d["k_idx"][s] for s in sl]).cpu()
+    r = torch.as_tensor(sample, device=d["q"].device)
+    qi, q = d["q_idx"][r].cpu(), d["q"][r].cpu()
+    slens = [lens[b] for b in sample]
+    soffs = np.concatenate([[0], np.cumsum(slens)[:-1]]).astype(np.int64)
+
+    def run():
+        t0 = time.perf_counter()
+        oracle.decode(qi, kic, q, kc, vc, soffs, slens, wd.block_size, wd.topk)
+        return time.perf_counter() - t0
+
+    t_cal = run()
+    reps = int(max(1, min(50, target_s / max(t_cal, 1e-3))))
+    t = sum(run() for _ in range(reps)) / reps
+    scale = float(sum(ctx)) / float(sum(slens))
+    del kc, vc, kic
+    return {"value": round(t * scale * 1e6, 1), "unit": "us/step", "higher_is_better": False,
+            "sample": f"sequences {sample} of the 32 (contexts {slens}, {sum(slens)} tokens of {sum(ctx)}): "
+                      f"oracle decode step (index scan + top-k + attention) {t:.3f} s, mean of {reps} runs; "
+                      f"value = that time x {scale:.3f} (all contexts / sampled contexts)",
+            "sample_seconds": round(t, 4)}
 
 
 if __name__ == "__main__":

@@ -264,6 +264,46 @@ def test_fullsize_prefill_32k_sampled(msa, synth, oracle_lib):
     assert bool((valid.sum(-1) == torch.clamp(local + 1, max=wl.topk)).all())
 
 
+def test_fullsize_ids_32k_every_row(msa, synth, oracle_lib):
+    """L=32768, 64/4, k=16, 32 planted blocks, the bench's one-call launch:
+    block ids of every one of the 32,768 rows x 4 groups against the oracle
+    (index branch only; the oracle scores every row on the host cores)."""
+    wl = synth.WORKLOADS["prefill_32k"]
+    inp = synth.prefill_inputs(wl, device="cuda", seed=0, with_main=False)
+    L = wl.seq_len
+    say("[parity] 32K ids, every row")
+    cu = inp["cu_seqlens_q"]
+    ids = msa.msa_index_topk(inp["q_idx"], inp["k_idx"], cu, cu, L, L, wl.block_size, wl.topk)
+    torch.cuda.synchronize()
+    rows = np.arange(L, dtype=np.int64)
+    ref = oracle_lib.index_topk(host(inp["q_idx"]), host(inp["k_idx"]), np.zeros(L, dtype=np.int64), rows.copy(),
+                                rows, wl.block_size, wl.topk)
+    compare_ids(ids, ref, "32K every row")
+
+
+def test_fullsize_ids_128k_every_tile_edge(msa, synth, oracle_lib):
+    """L=131072 in 8192-query calls against the causal prefix (the bench's
+    launches): ids of the first and last query block (128 rows each) of every
+    one of the 16 calls, all 4 groups, against the oracle."""
+    wl = synth.WORKLOADS["prefill_128k"]
+    inp = synth.prefill_inputs(wl, device="cuda", seed=0, with_main=False)
+    T, B = wl.q_tile, wl.block_size
+    got, rows = [], []
+    for lo in range(0, wl.seq_len, T):
+        hi = lo + T
+        say(f"[parity] 128K ids, call [{lo}, {hi})")
+        cu_q = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+        cu_k = torch.tensor([0, hi], dtype=torch.int32, device="cuda")
+        ids = msa.msa_index_topk(inp["q_idx"][lo:hi], inp["k_idx"], cu_q, cu_k, T, hi, wl.block_size, wl.topk)
+        edge = torch.cat([ids[:B], ids[T - B:]])
+        got.append(edge.cpu())
+        rows.append(np.r_[lo:lo + B, hi - B:hi])
+    rows = np.concatenate(rows).astype(np.int64)
+    ref = oracle_lib.index_topk(host(inp["q_idx"]), host(inp["k_idx"]), np.zeros(len(rows), dtype=np.int64),
+                                rows.copy(), rows, wl.block_size, wl.topk)
+    compare_ids(torch.cat(got), ref, "128K tile edges")
+
+
 @pytest.mark.parametrize("tile", [0, 7, 15])
 def test_fullsize_prefill_128k_tiles(msa, synth, oracle_lib, tile):
     """L=131072 in 8192-query tiles against the full causal prefix: the first,
