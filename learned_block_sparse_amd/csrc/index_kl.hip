@@ -25,24 +25,28 @@
 //              S^T = K q_idx^T on 32x32 MFMAs (32 edges per wave as the
 //              columns), then each column's causal max and argmax, written to
 //              the edge's selection slot
-//   kl_loss    one wave per (row, group): A, softmax(S), loss, dS per slot and
-//              dq_idx (lanes over the index dims)
-//   kl_dk      one workgroup per (sequence, block): for each group in order,
-//              the bucket's edges sorted in LDS by (argmax key, code), so each
-//              key's contributions are one segment summed in code order by
-//              that key's threads; added to dk_idx once per window
+//   kl_loss    16 lanes per (row, group), four per wave: A, softmax(S),
+//              loss, dS per slot and dq_idx (lanes over the index dims)
+//   kl_dk      workgroups per (sequence, block) and range of its keys, each
+//              wave owning a few keys: it reads the block's edges (group by
+//              group, each bucket sorted) 64 at a time, picks those whose
+//              argmax is one of its keys by a ballot, and adds dS q_idx to its
+//              LDS accumulator rows in edge order; added to dk_idx once per
+//              window
 // No atomics touch the arithmetic: results are bitwise reproducible.
+#include <type_traits>
+
 #include "msa_device.h"
 #include "msa_launch.h"
 
 namespace msa {
 
 constexpr int kKlWindow = 8192;  // query rows per edge-list window
-constexpr int kKlSortMax = kKlWindow;
 // kl_dk's sort keys: argmax key (7 bits) above the edge code (row in the window << 4 | slot)
 constexpr int kKlCodeBits = 17;
 static_assert((kKlWindow << 4) <= (1 << kKlCodeBits) && kBlock <= (1 << (31 - kKlCodeBits)),
               "kl_dk sort key fields");
+constexpr int kKlGShift = kKlCodeBits + 7;  // edge keys: group above the argmax key (7 bits) and the code
 constexpr float kKlNegInf = -__builtin_inff();
 constexpr int kRmaxKl = 16;  // query heads per group at most
 
@@ -59,9 +63,11 @@ struct KlArgs {
   const int32_t* offsets;
   const int32_t* chunk_start;
   const int32_t* edges;
-  float* s_slot;    // [window rows, G, topk] index score of each attended slot
-  int32_t* j_slot;  // [window rows, G, topk] argmax key within the block (0..127)
-  float* ds_slot;   // [window rows, G, topk] dS of each attended slot
+  float* s_slot;      // [window rows, G, topk] index score of each attended slot
+  int32_t* j_slot;    // [window rows, G, topk] argmax key within the block (0..127)
+  int32_t* pos_slot;  // [window rows, G, topk] position of the slot's edge in the edge lists
+  int32_t* key_edge;  // [edges] per edge-list position: group << 24 | argmax << 17 | code
+  float* ds_edge;     // [edges] per edge-list position: dS of the edge's slot
   float* loss;
   float* dq_idx;
   float* dk_idx;
@@ -171,199 +177,245 @@ __global__ __launch_bounds__(128) void kl_scores(KlArgs a) {
     const int64_t slot = ((int64_t)(code >> 4) * a.G + g) * a.topk + (code & 15);
     a.s_slot[slot] = best;
     a.j_slot[slot] = bj;
+    a.pos_slot[slot] = e;
+    a.key_edge[e] = (g << kKlGShift) | (bj << kKlCodeBits) | code;
   }
 }
 
 // ---------------------------------------------------------------- kl_loss
-// One wave per (row, group); lane l holds index dims l and l + 64.
+// Four (row, group) items per wave, 16 lanes each: lane l of an item owns
+// selection slot l (its attended flag, A, S, dS) and index dims
+// DI / 16 * l .. + DI / 16 - 1 of dq_idx, so each slot's argmax key row is
+// read as one 16-byte (bf16, DI 128) piece per lane, all 16 slots' pieces in
+// flight together, then summed in slot order.
 template <typename T>
 __global__ __launch_bounds__(256) void kl_loss(KlArgs a) {
-  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= (a.row_hi - a.row_lo) * a.G) return;
-  const int64_t trel = item / a.G;
-  const int g = (int)(item % a.G);
-  const int64_t t = a.row_lo + trel;
-  if (t >= a.cu_q[a.batch]) return;
+  constexpr int kItemLanes = 16;
   const int lane = lane_id();
-  const int bq = kl_find(a.cu_q, a.batch, t);
+  const int l = lane & (kItemLanes - 1);
+  const int base = lane & ~(kItemLanes - 1);
+  const int64_t item = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+  const int64_t nitems = (a.row_hi - a.row_lo) * a.G;
+  const int64_t trel = item < nitems ? item / a.G : 0;
+  const int g = item < nitems ? (int)(item % a.G) : 0;
+  const int64_t t = a.row_lo + trel;
+  const bool live = item < nitems && t < a.cu_q[a.batch];
+  const int bq = kl_find(a.cu_q, a.batch, live ? t : 0);
   const int64_t kb0 = a.cu_k[bq];
   const int64_t p = (int64_t)(a.cu_k[bq + 1] - a.cu_k[bq]) - (a.cu_q[bq + 1] - a.cu_q[bq]) + (t - a.cu_q[bq]);
-  const int32_t* sel = a.block_idx + (t * a.G + g) * a.topk;
-  const unsigned mask = p >= 0 ? kl_row_mask(sel, a.topk, p / kBlock) : 0u;
   const int R = a.Hq / a.G;
   const int64_t slot0 = (trel * a.G + g) * a.topk;
-
-  // A_i: lane i (< topk) owns slot i; the r heads' shares are averaged
+  // slot l attended: an id at or before the local block, not repeating an
+  // earlier slot of the row (Sel is a set)
+  const int cid = (live && l < a.topk) ? a.block_idx[(t * a.G + g) * a.topk + l] : -1;
+  bool mine = live && p >= 0 && cid >= 0 && cid <= p / kBlock;
+#pragma unroll
+  for (int k = 0; k < kItemLanes; ++k) {
+    const int other = __shfl(cid, base + k, kWave);
+    mine = mine && !(k < l && other == cid);
+  }
+  // A_l: the heads' shares of block c_l, averaged; all heads' loads in flight
+  // together, summed in head order (R <= 16)
   float Ai = 0.f, Si = kKlNegInf;
-  const bool mine = lane < a.topk && ((mask >> lane) & 1u);
+  int jl = 0, pos = 0;
   if (mine) {
-    // all heads' loads in flight together, then summed in head order (R <= 16)
     float e[kRmaxKl];
 #pragma unroll
     for (int hh = 0; hh < kRmaxKl; ++hh) {
       const int64_t rh = t * a.Hq + g * R + (hh < R ? hh : 0);
-      e[hh] = __expf(a.block_lse[rh * a.topk + lane] - a.lse[rh]);
+      e[hh] = a.block_lse[rh * a.topk + l] - a.lse[rh];
     }
 #pragma unroll
     for (int hh = 0; hh < kRmaxKl; ++hh)
-      if (hh < R) Ai += e[hh];
+      if (hh < R) Ai += __expf(e[hh]);
     Ai /= (float)R;
-    Si = a.s_slot[slot0 + lane];
+    Si = a.s_slot[slot0 + l];
+    jl = a.j_slot[slot0 + l];
+    pos = a.pos_slot[slot0 + l];
   }
-  // softmax of S over the attended slots, sum of A, loss (wave reductions)
+  // softmax of S over the attended slots, sum of A, loss (16-lane reductions)
   float m = Si;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-  float ez = mine ? __expf(Si - m) : 0.f;
+  for (int o = kItemLanes / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  const float ez = mine ? __expf(Si - m) : 0.f;
   float z = ez, asum = Ai;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
+  for (int o = kItemLanes / 2; o >= 1; o >>= 1) {
     z += __shfl_xor(z, o, kWave);
     asum += __shfl_xor(asum, o, kWave);
   }
   const float logI = mine ? Si - m - __logf(z) : 0.f;
   float li = (mine && Ai > 0.f) ? Ai * (__logf(Ai) - logI) : 0.f;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) li += __shfl_xor(li, o, kWave);
+  for (int o = kItemLanes / 2; o >= 1; o >>= 1) li += __shfl_xor(li, o, kWave);
   const float dsi = mine ? (ez / z) * asum - Ai : 0.f;
-  if (mine) a.ds_slot[slot0 + lane] = dsi;
-  if (lane == 0) a.loss[t * a.G + g] = mask ? li : 0.f;
+  if (mine) a.ds_edge[pos] = dsi;
+  const unsigned any = __ballot(mine) >> base & 0xffffu;
+  if (live && l == 0) a.loss[t * a.G + g] = any ? li : 0.f;
 
-  // dq_idx = sum_i dS_i k_idx[j*_i], slots in order.  The key rows of all
-  // slots are loaded first (an unattended slot reads the first attended
-  // slot's row and is not summed), so their loads are in flight together.
+  // dq_idx = sum_i dS_i k_idx[j*_i]: this lane's dims of every slot's key row
+  // (an unattended slot reads this item's first attended row, not summed)
+  constexpr int kDims = 8;  // elements per lane and load (DI 128; DI 64 uses the first half of the lanes)
   const T* kg = static_cast<const T*>(a.k_idx);
-  float acc0 = 0.f, acc1 = 0.f;
-  if (mask != 0u) {
-    const int first = __builtin_ctz(mask);
-    float kv0[16], kv1[16];
+  const bool dim_ok = kDims * l < a.DI;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  if (any) {
+    const int first = __builtin_ctz(any);
+    frag8<T> kv[kItemLanes];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int ii = (i < a.topk && ((mask >> i) & 1u)) ? i : first;
-      const int64_t key = kb0 + (int64_t)sel[ii] * kBlock + a.j_slot[slot0 + ii];
-      kv0[i] = (float)kg[key * a.DI + lane];
-      kv1[i] = lane + 64 < a.DI ? (float)kg[key * a.DI + lane + 64] : 0.f;
+    for (int i = 0; i < kItemLanes; ++i) {
+      const int src = ((any >> i) & 1u) ? i : first;
+      const int ci = __shfl(cid, base + src, kWave);
+      const int ji = __shfl(jl, base + src, kWave);
+      const int64_t key = kb0 + (int64_t)ci * kBlock + ji;
+      kv[i] = dim_ok ? load8(kg + key * a.DI + kDims * l) : zero8<T>();
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < a.topk && ((mask >> i) & 1u)) {
-        const float ds = __shfl(dsi, i, kWave);
-        acc0 += ds * kv0[i];
-        if (lane + 64 < a.DI) acc1 += ds * kv1[i];
+    for (int i = 0; i < kItemLanes; ++i) {
+      const float ds = __shfl(dsi, base + i, kWave);
+      if ((any >> i) & 1u) {
+        acc0 += ds * f32x4{(float)kv[i][0], (float)kv[i][1], (float)kv[i][2], (float)kv[i][3]};
+        acc1 += ds * f32x4{(float)kv[i][4], (float)kv[i][5], (float)kv[i][6], (float)kv[i][7]};
       }
     }
   }
-  float* dq = a.dq_idx + (t * a.G + g) * a.DI;
-  dq[lane] = acc0;
-  if (lane + 64 < a.DI) dq[lane + 64] = acc1;
+  if (live && dim_ok) {
+    float* dq = a.dq_idx + (t * a.G + g) * a.DI + kDims * l;
+    *reinterpret_cast<f32x4*>(dq) = acc0;
+    *reinterpret_cast<f32x4*>(dq + 4) = acc1;
+  }
 }
 
 // ------------------------------------------------------------------ kl_dk
-// One workgroup per (sequence, block), 256 threads: thread (key j = tid / 2,
-// half = tid % 2) owns dims 64 half .. 64 half + 63 of dk_idx[j].  For each
-// group in order, the bucket's edges are keyed (argmax j* << 17 | code) and
-// sorted in LDS, so each key's edges form one segment in code order; the
-// thread sums its key's segment in that order.  Segments come from a count
-// of edges per key and its prefix sum.
+// `split` workgroups per (sequence, block), each 128 / split of the block's
+// keys; each of the 4 waves owns a quarter of those keys and works alone (no
+// barriers).  The edges of the block's buckets, group by group and each
+// bucket in its sorted (row, slot) order, form one sequence.  A wave
+//   1. reads it 4 x 64 positions at a time (lane i: a position's key and dS,
+//      all loads in flight together) and lists, in position order, the edges
+//      whose argmax is one of its keys (ballot + compaction into LDS), until
+//      its list could overflow;
+//   2. applies the listed edges in order, kKlApply at a time: their q_idx
+//      rows are loaded together (lane l: dims DI / 64 * l ..), then
+//      dk[j*] += dS * q_idx[row, g] is added to the wave's accumulator rows in
+//      LDS.
+// Each key is summed by one wave over its edges in (group, row, slot) order.
+constexpr int kKlKeysWave = 16;  // most keys per wave (split >= 2)
+constexpr int kKlList = 256;     // listed edges per wave before they are applied
+constexpr int kKlApply = 32;     // q_idx rows in flight per wave
+
 template <typename T, int DI>
-__global__ __launch_bounds__(256) void kl_dk(KlArgs a) {
-  __shared__ int32_t keys[kKlSortMax];
-  __shared__ int32_t seg[kBlock + 1];
-  constexpr int kHalf = DI / 2;
-  const int sb = blockIdx.x;  // sequence * nb_max + block
+struct KlLane {  // this lane's DI / 64 dims of an index row, as loaded
+  static constexpr int kN = DI / 64;
+  using Raw = typename std::conditional<sizeof(T) * kN == 4, uint32_t,
+                                        typename std::conditional<sizeof(T) * kN == 8, u32x2, T>::type>::type;
+  Raw raw;
+  __device__ __forceinline__ void load(const T* row, int lane) {
+    raw = *reinterpret_cast<const Raw*>(row + kN * lane);
+  }
+  __device__ __forceinline__ float get(int i) const {
+    const T* p = reinterpret_cast<const T*>(&raw);
+    return (float)p[i];
+  }
+};
+
+template <typename T, int DI>
+__global__ __launch_bounds__(256) void kl_dk(KlArgs a, int split) {
+  constexpr int kN = DI / 64;
+  __shared__ float s_acc[4][kKlKeysWave * DI];
+  __shared__ int32_t s_lk[4][kKlList];
+  __shared__ float s_ld[4][kKlList];
+  const int r = blockIdx.x % split;
+  const int sb = blockIdx.x / split;  // sequence * nb_max + block
   if (sb >= a.batch * a.nb_max) return;
   const int c = sb % a.nb_max;
   const int b = sb / a.nb_max;
-  const int tid = threadIdx.x;
-  const int j = tid >> 1, half = tid & 1;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int keys_wave = kBlock / split / 4;
+  const int k0 = r * (kBlock / split) + wave * keys_wave;  // this wave's first key
+  float* acc = s_acc[wave];
+  int32_t* lk = s_lk[wave];
+  float* ld = s_ld[wave];
   const T* qg = static_cast<const T*>(a.q_idx);
-  bool any = false;
-  for (int g = 0; g < a.G; ++g) {
-    const int bucket = (b * a.G + g) * a.nb_max + c;
-    any = any || a.offsets[bucket + 1] > a.offsets[bucket];
+  // the block's edge sequence: group g's bucket holds positions [pre[g], pre[g + 1]),
+  // which are edge-list positions ebase[g] .. (uniform values)
+  int pre[kRmaxKl + 1], ebase[kRmaxKl];
+  pre[0] = 0;
+#pragma unroll
+  for (int g = 0; g < kRmaxKl; ++g) {
+    const int bucket = (b * a.G + (g < a.G ? g : 0)) * a.nb_max + c;
+    ebase[g] = a.offsets[bucket];
+    pre[g + 1] = pre[g] + (g < a.G ? a.offsets[bucket + 1] - ebase[g] : 0);
   }
-  if (!any) return;
-  float acc[kHalf];
+  const int total = pre[kRmaxKl];
+  if (total == 0) return;
+  for (int i = lane; i < keys_wave * DI; i += kWave) acc[i] = 0.f;
+
+  // key and dS of sequence position f
+  auto load_meta = [&](int f, int32_t& key, float& ds) {
+    key = -1;
+    ds = 0.f;
+    if (f >= total) return;
+    int e = f;
 #pragma unroll
-  for (int d = 0; d < kHalf; ++d) acc[d] = 0.f;
-  for (int g = 0; g < a.G; ++g) {
-    const int bucket = (b * a.G + g) * a.nb_max + c;
-    const int e_lo = a.offsets[bucket];
-    const int n = a.offsets[bucket + 1] - e_lo;
-    if (n == 0) continue;
-    int n2 = 1;
-    while (n2 < n) n2 <<= 1;
-    __syncthreads();  // keys / seg of the previous group are no longer read
-    for (int i = tid; i < n2; i += 256) {
-      int32_t k = 0x7fffffff;
-      if (i < n) {
-        const int code = a.edges[e_lo + i];
-        const int64_t slot = ((int64_t)(code >> 4) * a.G + g) * a.topk + (code & 15);
-        k = (a.j_slot[slot] << kKlCodeBits) | code;
+    for (int g = 0; g < kRmaxKl; ++g)
+      if (f >= pre[g] && f < pre[g + 1]) e = ebase[g] + f - pre[g];
+    key = a.key_edge[e];
+    ds = a.ds_edge[e];
+  };
+  int f0 = 0;
+  while (f0 < total) {
+    // 1. list this wave's edges in position order
+    int cnt = 0;
+    while (f0 < total && cnt + 4 * kWave <= kKlList) {
+      int32_t k4[4];
+      float d4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load_meta(f0 + u * kWave + lane, k4[u], d4[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kj = (k4[u] >> kKlCodeBits) & 127;
+        const bool hit = k4[u] >= 0 && kj >= k0 && kj < k0 + keys_wave;
+        const uint64_t m = __ballot(hit);
+        if (hit) {
+          const int slot =
+              cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+          lk[slot] = k4[u];
+          ld[slot] = d4[u];
+        }
+        cnt += __builtin_popcountll(m);
       }
-      keys[i] = k;
+      f0 += 4 * kWave;
     }
-    if (tid <= kBlock) seg[tid] = 0;
-    __syncthreads();
-    for (int kk = 2; kk <= n2; kk <<= 1) {
-      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-        for (int i = tid; i < n2; i += 256) {
-          const int ixj = i ^ jj;
-          if (ixj > i) {
-            const int32_t x = keys[i], y = keys[ixj];
-            if ((x > y) == ((i & kk) == 0)) {
-              keys[i] = y;
-              keys[ixj] = x;
-            }
-          }
-        }
-        __syncthreads();
+    // 2. apply them in order
+    for (int i0 = 0; i0 < cnt; i0 += kKlApply) {
+      KlLane<T, DI> q[kKlApply];
+#pragma unroll
+      for (int u = 0; u < kKlApply; ++u) {
+        const int32_t ku = lk[min(i0 + u, cnt - 1)];
+        const int g = ku >> kKlGShift;
+        const int row = (ku & ((1 << kKlCodeBits) - 1)) >> 4;
+        q[u].load(qg + ((a.row_lo + row) * a.G + g) * DI, lane);
       }
-    }
-    // segment starts: the first sorted position of each key (keys ascend)
-    for (int i = tid; i < n; i += 256) {
-      const int kj = keys[i] >> kKlCodeBits;
-      if (i == 0 || (keys[i - 1] >> kKlCodeBits) != kj) seg[kj] = i + 1;  // +1: 0 marks "no edge"
-    }
-    __syncthreads();
-    const int s0 = seg[j] - 1;
-    if (s0 >= 0) {
-      int s1 = s0 + 1;  // end of this key's segment
-      while (s1 < n && (keys[s1] >> kKlCodeBits) == j) ++s1;
-      // kBatch edges' rows are loaded together, then summed in segment order
-      // (a batch past the end re-reads the segment's last edge, not summed;
-      // 2 measured faster than 4, which costs the kernel a wave per SIMD)
-      constexpr int kBatch = 2;
-      for (int i0 = s0; i0 < s1; i0 += kBatch) {
-        float ds[kBatch];
-        frag8<T> v[kBatch][kHalf / 8];
+      __builtin_amdgcn_sched_barrier(0);  // the loads stay in flight together
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int code = keys[min(i0 + u, s1 - 1)] & ((1 << kKlCodeBits) - 1);
-          const int64_t slot = ((int64_t)(code >> 4) * a.G + g) * a.topk + (code & 15);
-          ds[u] = a.ds_slot[slot];
-          const T* qrow = qg + ((a.row_lo + (code >> 4)) * a.G + g) * DI + kHalf * half;
+      for (int u = 0; u < kKlApply; ++u) {
+        if (i0 + u >= cnt) break;
+        const int32_t ku = lk[i0 + u];
+        const float du = ld[i0 + u];
+        float* arow = acc + (((ku >> kKlCodeBits) & 127) - k0) * DI + kN * lane;
 #pragma unroll
-          for (int d8 = 0; d8 < kHalf; d8 += 8) v[u][d8 / 8] = load8(qrow + d8);
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          if (i0 + u < s1) {
-#pragma unroll
-            for (int d8 = 0; d8 < kHalf; d8 += 8)
-#pragma unroll
-              for (int w = 0; w < 8; ++w) acc[d8 + w] += ds[u] * (float)v[u][d8 / 8][w];
-          }
-        }
+        for (int i = 0; i < kN; ++i) arow[i] += du * q[u].get(i);
       }
     }
   }
   const int64_t kb0 = a.cu_k[b];
   const int N = a.cu_k[b + 1] - a.cu_k[b];
-  if (c * kBlock + j < N) {
-    float* dst = a.dk_idx + (kb0 + c * kBlock + j) * DI + kHalf * half;
+  for (int kk = 0; kk < keys_wave; ++kk) {
+    if (c * kBlock + k0 + kk >= N) break;
+    float* dst = a.dk_idx + (kb0 + c * kBlock + k0 + kk) * DI + kN * lane;
 #pragma unroll
-    for (int d = 0; d < kHalf; ++d) dst[d] += acc[d];
+    for (int i = 0; i < kN; ++i) dst[i] += acc[kk * DI + kN * lane + i];
   }
 }
 
@@ -384,6 +436,8 @@ KlPlan plan_kl(int batch, int max_q_len, int max_kv_len, int G, int topk) {
   pl.edges_off = off;   off += al(slots * 4);
   pl.s_off = off;       off += al(slots * 4);
   pl.j_off = off;       off += al(slots * 4);
+  pl.pos_off = off;     off += al(slots * 4);
+  pl.key_off = off;     off += al(slots * 4);
   pl.ds_off = off;      off += al(slots * 4);
   pl.workspace_bytes = off;
   return pl;
@@ -417,22 +471,29 @@ static hipError_t launch_kl_t(const KlPlan& pl, const KlLaunch& x, void* ws, hip
   a.edges = edges;
   a.s_slot = reinterpret_cast<float*>(w + pl.s_off);
   a.j_slot = reinterpret_cast<int32_t*>(w + pl.j_off);
-  a.ds_slot = reinterpret_cast<float*>(w + pl.ds_off);
+  a.pos_slot = reinterpret_cast<int32_t*>(w + pl.pos_off);
+  a.key_edge = reinterpret_cast<int32_t*>(w + pl.key_off);
+  a.ds_edge = reinterpret_cast<float*>(w + pl.ds_off);
   a.loss = x.loss;
   a.dq_idx = x.dq_idx;
   a.dk_idx = x.dk_idx;
   hipLaunchKernelGGL(kl_zero, dim3(1024), dim3(256), 0, st, a);
   for (int64_t r0 = 0; r0 < pl.rows_bound; r0 += pl.window) {
     const int64_t r1 = r0 + pl.window < pl.rows_bound ? r0 + pl.window : pl.rows_bound;
-    hipError_t e = build_edge_lists(x.attn, pl.nb_max, r0, r1, counts, offsets, chunks, cursor, edges, st);
+    hipError_t e = build_edge_lists(x.attn, pl.nb_max, r0, r1, counts, offsets, chunks, cursor, edges, true, st);
     if (e != hipSuccess) return e;
     a.row_lo = r0;
     a.row_hi = r1;
     const int64_t entries = (r1 - r0) * a.G * a.topk;
     const int64_t ub = entries / kEdgeChunk + (entries < pl.nbuckets ? entries : pl.nbuckets) + 1;
     hipLaunchKernelGGL((kl_scores<T, DI>), dim3((unsigned)ub), dim3(128), 0, st, a);
-    hipLaunchKernelGGL(kl_loss<T>, dim3((unsigned)(((r1 - r0) * a.G + 3) / 4)), dim3(256), 0, st, a);
-    hipLaunchKernelGGL((kl_dk<T, DI>), dim3((unsigned)(a.batch * pl.nb_max)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(kl_loss<T>, dim3((unsigned)(((r1 - r0) * a.G + 15) / 16)), dim3(256), 0, st, a);
+    // keys per workgroup: 64, or fewer when there are few blocks (the first
+    // window of a long prefill), so that the blocks' long edge sequences are
+    // spread over more workgroups
+    const int64_t nblk = (int64_t)a.batch * pl.nb_max;
+    const int split = nblk >= 256 ? 2 : nblk >= 128 ? 4 : 8;
+    hipLaunchKernelGGL((kl_dk<T, DI>), dim3((unsigned)(nblk * split)), dim3(256), 0, st, a, split);
   }
   return hipGetLastError();
 }

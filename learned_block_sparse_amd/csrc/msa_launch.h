@@ -81,12 +81,13 @@ int kvo_window_rows();
 constexpr int kEdgeChunk = 64;
 
 // Per-(sequence, group, block) lists of the selection entries of query rows
-// [row_lo, row_hi): each entry is ((row - row_lo) << 4 | selection slot), the
-// entries of bucket i are edges[offsets[i] .. offsets[i + 1]) in no
-// particular order (atomics place them).  counts, chunk_start and cursor are
-// scratch of batch * G * nb_max (+1) ints each.
+// [row_lo, row_hi) (at most 8192 rows): each entry is ((row - row_lo) << 4 |
+// selection slot), the entries of bucket i are edges[offsets[i] ..
+// offsets[i + 1]), ascending when `sorted`, else in the order the placing
+// atomics handed out.  counts, chunk_start and cursor are scratch of
+// batch * G * nb_max (+1) ints each.
 hipError_t build_edge_lists(const AttnArgs& x, int nb_max, int64_t row_lo, int64_t row_hi, int32_t* counts,
-                            int32_t* offsets, int32_t* chunk_start, int32_t* cursor, int32_t* edges,
+                            int32_t* offsets, int32_t* chunk_start, int32_t* cursor, int32_t* edges, bool sorted,
                             hipStream_t st);
 
 // Backward of the main branch (bf16 inputs, fp32 gradients).
@@ -96,7 +97,9 @@ struct BwdPlan {
   int64_t rows_bound = 0;
   int64_t window = 0;        // query rows per edge-list window
   size_t counts_off = 0, offsets_off = 0, chunks_off = 0, cursor_off = 0, edges_off = 0, delta_off = 0;
-  size_t order_off = 0;      // [nbuckets] int32: bwd_dkdv's dispatch order
+  size_t dkv_chunk_off = 0;  // [nbuckets + 1] int32: bwd_dkdv chunk starts
+  size_t dkv_part_off = 0;   // [nbuckets + 1] int32: partial-slot starts of multi-chunk buckets
+  size_t part_dkv_off = 0;   // [slots][2][128][128] fp32 chunk partials of dK, dV
   size_t part_dq_off = 0;    // [window rows, G, topk, 16, 128] bf16
   size_t workspace_bytes = 0;
 };
@@ -119,7 +122,8 @@ struct KlPlan {
   int64_t rows_bound = 0;
   int64_t window = 0;        // query rows per edge-list window
   size_t counts_off = 0, offsets_off = 0, chunks_off = 0, cursor_off = 0, edges_off = 0;
-  size_t s_off = 0, j_off = 0, ds_off = 0;  // per selection slot of a window: score, argmax, dS
+  size_t s_off = 0, j_off = 0, pos_off = 0;  // per selection slot of a window: score, argmax, edge position
+  size_t key_off = 0, ds_off = 0;            // per edge-list position: edge key, dS
   size_t workspace_bytes = 0;
 };
 KlPlan plan_kl(int batch, int max_q_len, int max_kv_len, int G, int topk);

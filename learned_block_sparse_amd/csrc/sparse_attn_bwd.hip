@@ -16,22 +16,25 @@
 // Kernels (bf16 inputs, fp32 accumulation and fp32 gradients):
 //   bwd_zero   dk = dv = 0 for the key rows of the call
 //   bwd_delta  delta[row, head] = dO . O
-//   bwd_order  the buckets by edge count, largest first (bwd_dkdv's dispatch
-//              order)
-//   bwd_dkdv   KV-outer, one workgroup per (sequence, group, block) bucket of
-//              the selection edge lists (the lists the KV-outer forward
-//              builds).  The bucket's list, placed by atomics in no fixed
-//              order, is first sorted in LDS, so the order in which the edges
-//              are summed (and so every rounding) is fixed.  Each of the 4
-//              waves owns 32 keys of the block and keeps their K and V rows
-//              in registers as MFMA operands; the edges run in quads (4
-//              queries x 16 heads = 64 MFMA rows), whose Q and dO are staged
-//              in LDS twice, row-major for S = Q K^T and dP = dO V^T and
-//              transposed for dV += P^T dO and dK += dS^T Q, so the P and dS
-//              registers of the first two products are directly the A
-//              operands of the last two.  dK and dV accumulate over the
-//              bucket in registers and are added to the output once per
-//              window of query rows.
+//   bwd_dkv_scan  chunk starts of bwd_dkdv: each bucket of the selection
+//              edge lists (the lists the KV-outer forward builds, here sorted
+//              per bucket, so the order in which edges are summed is fixed) is
+//              cut into chunks of at most kDkvChunk edges; buckets of more
+//              than one chunk (planted blocks, the early blocks of the first
+//              query window, which nearly every row picks) also get one
+//              partial slot per chunk
+//   bwd_dkdv   KV-outer, one workgroup per chunk.  Each of the 4 waves owns
+//              32 keys of the block and keeps their K and V rows in registers
+//              as MFMA operands; the edges run in quads (4 queries x 16 heads
+//              = 64 MFMA rows), whose Q and dO are staged in LDS twice,
+//              row-major for S = Q K^T and dP = dO V^T and transposed for
+//              dV += P^T dO and dK += dS^T Q, so the P and dS registers of the
+//              first two products are directly the A operands of the last
+//              two.  dK and dV accumulate over the chunk in registers; a
+//              bucket's only chunk adds them to the output, the chunks of a
+//              longer bucket write fp32 partials
+//   bwd_dkdv_reduce  adds each long bucket's partials to dK / dV in chunk
+//              order
 //   bwd_dq_kvo KV-outer like the forward, one workgroup per chunk of <= 64
 //              edges of a bucket: S^T = K Q^T and dP^T = V dO^T with two
 //              queries x 16 heads as the 32 MFMA columns, then dQ += dS K
@@ -47,8 +50,8 @@ namespace msa {
 constexpr int kBwdThreads = 256;
 constexpr int kBwdRow = 136;      // LDS row of Q / dO for one MFMA row: 128 bf16 + 8 pad
 constexpr int kBwdWindow = 8192;  // query rows per edge-list window
-constexpr int kSortMax = kBwdWindow;  // edges of one bucket in one window (<= rows per window)
-static_assert(kBwdWindow <= 65536, "bwd_dkdv sorts rows of the window as 16-bit numbers");
+constexpr int kDkvChunk = 256;    // edges per bwd_dkdv workgroup (64 quads)
+static_assert(kBwdWindow <= 65536, "bwd_dkdv keeps rows of the window as 16-bit numbers");
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdKernelArgs {
@@ -68,7 +71,9 @@ struct BwdKernelArgs {
   const int32_t* chunk_start;
   int32_t* edges;
   float* delta;
-  int32_t* order;    // bwd_dkdv's bucket for each workgroup, largest buckets first
+  int32_t* dkv_chunk;  // [nbuckets + 1] exclusive prefix of the buckets' bwd_dkdv chunks
+  int32_t* dkv_part;   // [nbuckets + 1] exclusive prefix of the partial slots (buckets of > 1 chunk)
+  float* part_dkv;     // [slots][2][128 keys][128 dims]: a chunk's dK (unscaled) and dV
   bf16* part_dq;     // [window rows, G, topk, 16, 128]: each edge's block contribution to dq (unscaled)
   float* dq;
   float* dk;
@@ -108,56 +113,43 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdKernelArgs a) {
   if ((threadIdx.x & 31) == 0) a.delta[rh] = s;
 }
 
-// Dispatch order of bwd_dkdv: one workgroup per bucket runs the bucket's
-// quads one after another, and a bucket can hold several times the average
-// (planted blocks, the window's own local blocks), so the buckets go longest
-// first.  Keys (edge count << 15 | 32767 - bucket) are sorted descending by a
-// bitonic network in LDS: largest count first, ties by lower bucket id, the
-// same order on every run.  More than kOrderMax buckets (not met by the
-// single-sequence workloads up to 1M tokens with 4 groups): key blocks from
-// the last to the first instead, groups interleaved.
-constexpr int kOrderMax = 32768;
-
-__global__ __launch_bounds__(1024) void bwd_order(BwdKernelArgs a) {
-  __shared__ uint32_t keys[kOrderMax];
-  const int nbk = a.batch * a.G * a.nb_max;
+// Chunk starts and partial slots of bwd_dkdv, one workgroup: thread i scans
+// a contiguous range of buckets, then the 1024 range sums are scanned in LDS.
+__global__ __launch_bounds__(1024) void bwd_dkv_scan(BwdKernelArgs a, int nbk) {
+  __shared__ int s_c[1024];
+  __shared__ int s_p[1024];
   const int tid = threadIdx.x;
-  if (nbk > kOrderMax) {
-    const int nbg = a.batch * a.G;
-    for (int i = tid; i < nbk; i += 1024) {
-      const int c = a.nb_max - 1 - i / nbg;
-      a.order[i] = (i % nbg) * a.nb_max + c;
-    }
-    return;
+  const int seg = (nbk + 1023) / 1024;
+  const int lo = min(tid * seg, nbk), hi = min(lo + seg, nbk);
+  int sc = 0, sp = 0;
+  for (int j = lo; j < hi; ++j) {
+    const int ch = (a.offsets[j + 1] - a.offsets[j] + kDkvChunk - 1) / kDkvChunk;
+    sc += ch;
+    sp += ch > 1 ? ch : 0;
   }
-  int n2 = 1;
-  while (n2 < nbk) n2 <<= 1;
-  for (int i = tid; i < n2; i += 1024) {
-    if (i < nbk) {
-      const int cnt = a.offsets[i + 1] - a.offsets[i];  // <= rows per window < 2^17
-      keys[i] = ((uint32_t)cnt << 15) | (uint32_t)(32767 - i);
-    } else {
-      keys[i] = 0u;  // padding sorts last
-    }
-  }
+  s_c[tid] = sc;
+  s_p[tid] = sp;
   __syncthreads();
-  for (int kk = 2; kk <= n2; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < n2; i += 1024) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint32_t x = keys[i], y = keys[ixj];
-          // descending within blocks of kk whose bit kk is clear
-          if ((x < y) == ((i & kk) == 0)) {
-            keys[i] = y;
-            keys[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int vc = tid >= off ? s_c[tid - off] : 0;
+    const int vp = tid >= off ? s_p[tid - off] : 0;
+    __syncthreads();
+    s_c[tid] += vc;
+    s_p[tid] += vp;
+    __syncthreads();
   }
-  for (int i = tid; i < nbk; i += 1024) a.order[i] = 32767 - (int)(keys[i] & 32767u);
+  int oc = s_c[tid] - sc, op = s_p[tid] - sp;
+  for (int j = lo; j < hi; ++j) {
+    const int ch = (a.offsets[j + 1] - a.offsets[j] + kDkvChunk - 1) / kDkvChunk;
+    a.dkv_chunk[j] = oc;
+    a.dkv_part[j] = op;
+    oc += ch;
+    op += ch > 1 ? ch : 0;
+  }
+  if (tid == 1023) {
+    a.dkv_chunk[nbk] = s_c[1023];
+    a.dkv_part[nbk] = s_p[1023];
+  }
 }
 
 // One quad of edges (4 queries x 16 heads = 64 MFMA rows), staged by the
@@ -341,16 +333,18 @@ __device__ __forceinline__ void bwd_quad_compute(const BwdLds& L, int buf, const
 
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
   __shared__ __attribute__((aligned(16))) BwdLds L;
-  __shared__ uint16_t rows[kSortMax];
+  __shared__ uint16_t rows[kDkvChunk];
   const int nbk = a.batch * a.G * a.nb_max;
-  if ((int)blockIdx.x >= nbk) return;
-  // largest buckets first (bwd_order), so no long bucket starts at the end
-  const int bucket = a.order[blockIdx.x];
+  const int w = blockIdx.x;
+  if (w >= a.dkv_chunk[nbk]) return;
+  const int bucket = bwd_find(a.dkv_chunk, nbk, w);
+  const int chunk = w - a.dkv_chunk[bucket];
+  const int nchunks = a.dkv_chunk[bucket + 1] - a.dkv_chunk[bucket];
   const int c = bucket % a.nb_max;
   const int g = (bucket / a.nb_max) % a.G;
   const int b = bucket / (a.nb_max * a.G);
-  const int e_lo = a.offsets[bucket];
-  const int n = a.offsets[bucket + 1] - e_lo;
+  const int e_lo = a.offsets[bucket] + chunk * kDkvChunk;
+  const int n = min(kDkvChunk, a.offsets[bucket + 1] - e_lo);
   if (n <= 0) return;
   const int64_t kb0 = a.cu_k[b];
   const int N = a.cu_k[b + 1] - a.cu_k[b];
@@ -360,31 +354,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
   const int64_t rs = (int64_t)a.G * kHeadDim;
   const int tid = threadIdx.x;
 
-  // ---- the rows of the bucket's edges, sorted ascending in LDS (bitonic).
-  // A row selects a block at most once, so the rows are distinct.  The lists
-  // are placed by atomics in no fixed order; sorting fixes the order in which
-  // the edges are summed, so dK and dV are reproducible bit for bit.
-  {
-    int n2 = 1;
-    while (n2 < n) n2 <<= 1;
-    for (int i = tid; i < n2; i += kBwdThreads) rows[i] = i < n ? (uint16_t)(a.edges[e_lo + i] >> 4) : (uint16_t)0xffff;
-    __syncthreads();
-    for (int kk = 2; kk <= n2; kk <<= 1) {
-      for (int j = kk >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < n2; i += kBwdThreads) {
-          const int ixj = i ^ j;
-          if (ixj > i) {
-            const uint16_t x = rows[i], y = rows[ixj];
-            if ((x > y) == ((i & kk) == 0)) {
-              rows[i] = y;
-              rows[ixj] = x;
-            }
-          }
-        }
-        __syncthreads();
-      }
-    }
-  }
+  // ---- the rows of the chunk's edges (the bucket's list is sorted, so the
+  // order in which edges are summed is fixed)
+  for (int i = tid; i < n; i += kBwdThreads) rows[i] = (uint16_t)(a.edges[e_lo + i] >> 4);
+  __syncthreads();
 
   const int wave = tid >> 6;
   const int lane = lane_id();
@@ -424,18 +397,77 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
     __syncthreads();
   }
 
-  // ---- add this window's contribution: lane column d = 32 dt + col, rows =
-  // keys 8 (r / 4) + 4 a32 + r % 4 of the wave's 32
+  // ---- lane column d = 32 dt + col, rows = keys 8 (r / 4) + 4 a32 + r % 4 of
+  // the wave's 32.  A bucket's only chunk adds this window's contribution to
+  // dK / dV; the chunks of a longer bucket write partials for bwd_dkdv_reduce.
+  if (nchunks == 1) {
 #pragma unroll
-  for (int dt = 0; dt < kHeadDim / 32; ++dt)
+    for (int dt = 0; dt < kHeadDim / 32; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kk = c * kBlock + 32 * wave + 8 * (r >> 2) + 4 * a32 + (r & 3);
-      if (kk >= N) continue;
-      const int64_t off = (kb0 + kk) * rs + g * kHeadDim + 32 * dt + col;
-      a.dk[off] += dk_acc[dt][r] * a.scale;
-      a.dv[off] += dv_acc[dt][r];
+      for (int r = 0; r < 16; ++r) {
+        const int kk = c * kBlock + 32 * wave + 8 * (r >> 2) + 4 * a32 + (r & 3);
+        if (kk >= N) continue;
+        const int64_t off = (kb0 + kk) * rs + g * kHeadDim + 32 * dt + col;
+        a.dk[off] += dk_acc[dt][r] * a.scale;
+        a.dv[off] += dv_acc[dt][r];
+      }
+  } else {
+    float* pk = a.part_dkv + (int64_t)(a.dkv_part[bucket] + chunk) * (2 * kBlock * kHeadDim);
+    float* pv = pk + kBlock * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < kHeadDim / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * wave + 8 * (r >> 2) + 4 * a32 + (r & 3);
+        pk[key * kHeadDim + 32 * dt + col] = dk_acc[dt][r];
+        pv[key * kHeadDim + 32 * dt + col] = dv_acc[dt][r];
+      }
+  }
+}
+
+// dK += scale * (sum of the chunk partials), dV += sum of the partials, for
+// each bucket of more than one chunk, the chunks summed in order: four
+// workgroups per bucket, each a quarter of the partial; a thread's four
+// chunk loads are issued together before their in-order sum.
+constexpr int kReduceSplit = 4;
+
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce(BwdKernelArgs a) {
+  const int nbk = a.batch * a.G * a.nb_max;
+  const int bucket = blockIdx.x / kReduceSplit;
+  const int quarter = blockIdx.x % kReduceSplit;
+  if (bucket >= nbk) return;
+  const int nchunks = a.dkv_chunk[bucket + 1] - a.dkv_chunk[bucket];
+  if (nchunks <= 1) return;
+  const int c = bucket % a.nb_max;
+  const int g = (bucket / a.nb_max) % a.G;
+  const int b = bucket / (a.nb_max * a.G);
+  const int64_t kb0 = a.cu_k[b];
+  const int N = a.cu_k[b + 1] - a.cu_k[b];
+  const int64_t rs = (int64_t)a.G * kHeadDim;
+  constexpr int64_t kSlot = 2 * kBlock * kHeadDim;  // floats of one partial
+  const f32x4* p0 = reinterpret_cast<const f32x4*>(a.part_dkv + (int64_t)a.dkv_part[bucket] * kSlot);
+  constexpr int kPer = (int)(kSlot / 4) / kReduceSplit;  // float4 units of this workgroup
+  for (int u = quarter * kPer + threadIdx.x; u < (quarter + 1) * kPer; u += 256) {
+    f32x4 acc = p0[u];
+    int k = 1;
+    for (; k + 4 <= nchunks; k += 4) {
+      const f32x4 x0 = p0[(int64_t)k * (kSlot / 4) + u], x1 = p0[(int64_t)(k + 1) * (kSlot / 4) + u];
+      const f32x4 x2 = p0[(int64_t)(k + 2) * (kSlot / 4) + u], x3 = p0[(int64_t)(k + 3) * (kSlot / 4) + u];
+      acc += x0;
+      acc += x1;
+      acc += x2;
+      acc += x3;
     }
+    for (; k < nchunks; ++k) acc += p0[(int64_t)k * (kSlot / 4) + u];
+    const int e = 4 * u;
+    const bool is_v = e >= kBlock * kHeadDim;
+    const int key = (e % (kBlock * kHeadDim)) / kHeadDim, d = e % kHeadDim;
+    const int kk = c * kBlock + key;
+    if (kk >= N) continue;
+    float* dst = (is_v ? a.dv : a.dk) + (kb0 + kk) * rs + g * kHeadDim + d;
+    const f32x4 cur = *reinterpret_cast<f32x4*>(dst);
+    *reinterpret_cast<f32x4*>(dst) = cur + (is_v ? acc : acc * a.scale);
+  }
 }
 
 // ---------------------------------------------------------------- dQ
@@ -687,7 +719,11 @@ BwdPlan plan_bwd(int batch, int max_q_len, int max_kv_len, int Hq, int G, int to
   pl.cursor_off = off;  off += al(nbk * 4);
   pl.edges_off = off;   off += al((size_t)pl.window * G * topk * 4);
   pl.delta_off = off;   off += al((size_t)pl.rows_bound * Hq * 4);
-  pl.order_off = off;   off += al(nbk * 4);
+  pl.dkv_chunk_off = off; off += al((nbk + 1) * 4);
+  pl.dkv_part_off = off;  off += al((nbk + 1) * 4);
+  // a bucket of n > kDkvChunk edges takes ceil(n / kDkvChunk) < 2 n / kDkvChunk slots
+  const size_t slots = 2 * (size_t)pl.window * G * topk / kDkvChunk + 1;
+  pl.part_dkv_off = off;  off += al(slots * 2 * kBlock * kHeadDim * sizeof(float));
   pl.part_dq_off = off; off += al((size_t)pl.window * G * topk * 16 * kHeadDim * sizeof(bf16));
   pl.workspace_bytes = off;
   return pl;
@@ -722,7 +758,9 @@ hipError_t launch_sparse_attn_bwd(const BwdPlan& pl, const BwdArgs& x, void* ws,
   a.chunk_start = chunks;
   a.edges = reinterpret_cast<int32_t*>(w + pl.edges_off);
   a.delta = reinterpret_cast<float*>(w + pl.delta_off);
-  a.order = reinterpret_cast<int32_t*>(w + pl.order_off);
+  a.dkv_chunk = reinterpret_cast<int32_t*>(w + pl.dkv_chunk_off);
+  a.dkv_part = reinterpret_cast<int32_t*>(w + pl.dkv_part_off);
+  a.part_dkv = reinterpret_cast<float*>(w + pl.part_dkv_off);
   a.part_dq = reinterpret_cast<bf16*>(w + pl.part_dq_off);
   a.dq = x.dq;
   a.dk = x.dk;
@@ -732,13 +770,16 @@ hipError_t launch_sparse_attn_bwd(const BwdPlan& pl, const BwdArgs& x, void* ws,
   hipLaunchKernelGGL(bwd_delta, dim3((unsigned)((pl.rows_bound * a.Hq + 7) / 8)), dim3(256), 0, st, a);
   for (int64_t r0 = 0; r0 < pl.rows_bound; r0 += pl.window) {
     const int64_t r1 = r0 + pl.window < pl.rows_bound ? r0 + pl.window : pl.rows_bound;
-    hipError_t e = build_edge_lists(x.fwd, pl.nb_max, r0, r1, counts, offsets, chunks, cursor, a.edges, st);
+    hipError_t e = build_edge_lists(x.fwd, pl.nb_max, r0, r1, counts, offsets, chunks, cursor, a.edges, true, st);
     if (e != hipSuccess) return e;
     a.row_lo = r0;
-    hipLaunchKernelGGL(bwd_order, dim3(1), dim3(1024), 0, st, a);
-    hipLaunchKernelGGL(bwd_dkdv, dim3((unsigned)pl.nbuckets), dim3(kBwdThreads), 0, st, a);
-    // chunks of kEdgeChunk edges: at most entries / kEdgeChunk + one partial chunk per bucket
     const int64_t entries = (r1 - r0) * a.G * a.topk;
+    hipLaunchKernelGGL(bwd_dkv_scan, dim3(1), dim3(1024), 0, st, a, pl.nbuckets);
+    // chunks of kDkvChunk edges: at most entries / kDkvChunk + one partial chunk per bucket
+    const int64_t ub_kv = entries / kDkvChunk + (entries < pl.nbuckets ? entries : pl.nbuckets) + 1;
+    hipLaunchKernelGGL(bwd_dkdv, dim3((unsigned)ub_kv), dim3(kBwdThreads), 0, st, a);
+    hipLaunchKernelGGL(bwd_dkdv_reduce, dim3((unsigned)pl.nbuckets * kReduceSplit), dim3(256), 0, st, a);
+    // chunks of kEdgeChunk edges: at most entries / kEdgeChunk + one partial chunk per bucket
     const int64_t ub = entries / kEdgeChunk + (entries < pl.nbuckets ? entries : pl.nbuckets) + 1;
     hipLaunchKernelGGL(bwd_dq_kvo, dim3((unsigned)ub), dim3(kBwdThreads), 0, st, a);
     hipLaunchKernelGGL(bwd_dq_combine, dim3((unsigned)(((r1 - r0) * a.G + 3) / 4)), dim3(256), 0, st, a, r1);

@@ -485,6 +485,60 @@ __global__ __launch_bounds__(256) void kvo_combine(KvoArgs a) {
   if (a.lse && (lane & 3) == 0) a.lse[t * a.Hq + g * R + h] = L;
 }
 
+// Each bucket's edge codes sorted ascending (row in the window, then slot):
+// the placing pass above leaves them in the order the atomics handed out, and
+// a consumer that sums over a bucket's edges (the backward's dK / dV, the KL
+// loss's index-key gradient) needs one fixed order to be bitwise
+// reproducible.  A row selects a block at most once, so a bucket's rows are
+// distinct: each edge sets its row's bit in an LDS bitmap of the window's
+// rows (and records its slot by row), and a prefix count of the bitmap gives
+// every row its rank.  One workgroup per bucket.
+constexpr int kSortCap = 8192;  // rows of a window
+
+__global__ __launch_bounds__(256) void kvo_sort(const int32_t* __restrict__ offsets, int32_t* __restrict__ edges,
+                                                int nbk) {
+  __shared__ uint32_t bits[kSortCap / 32];
+  __shared__ uint8_t slot_of[kSortCap];
+  __shared__ int wsum[4];
+  const int bucket = blockIdx.x;
+  if (bucket >= nbk) return;
+  const int lo = offsets[bucket];
+  const int n = offsets[bucket + 1] - lo;
+  if (n <= 1) return;
+  const int tid = threadIdx.x;
+  bits[tid] = 0u;  // kSortCap / 32 == 256 words, one per thread
+  __syncthreads();
+  for (int i = tid; i < n; i += 256) {
+    const int code = edges[lo + i];
+    const int row = code >> 4;
+    slot_of[row] = (uint8_t)(code & 15);
+    atomicOr(&bits[row >> 5], 1u << (row & 31));
+  }
+  __syncthreads();
+  // exclusive prefix of the words' popcounts: within the wave, then across
+  const uint32_t w = bits[tid];
+  const int cnt = __builtin_popcount(w);
+  const int lane = tid & 63;
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[tid >> 6] = incl;
+  __syncthreads();
+  int base = incl - cnt;
+  for (int k = 0; k < (tid >> 6); ++k) base += wsum[k];
+  uint32_t m = w;
+  while (m != 0u) {
+    const int bit = __builtin_ctz(m);
+    m &= m - 1u;
+    const int row = 32 * tid + bit;
+    edges[lo + base] = (row << 4) | slot_of[row];
+    ++base;
+  }
+}
+
 // Edge lists of query rows [a.row_lo, a.row_hi): counts, offsets, chunk
 // starts and the edges themselves, per (sequence, group, block) bucket.
 static void launch_edge_lists(const KvoArgs& a, int nbk, hipStream_t st) {
@@ -496,8 +550,9 @@ static void launch_edge_lists(const KvoArgs& a, int nbk, hipStream_t st) {
 }
 
 hipError_t build_edge_lists(const AttnArgs& x, int nb_max, int64_t row_lo, int64_t row_hi, int32_t* counts,
-                            int32_t* offsets, int32_t* chunk_start, int32_t* cursor, int32_t* edges,
+                            int32_t* offsets, int32_t* chunk_start, int32_t* cursor, int32_t* edges, bool sorted,
                             hipStream_t st) {
+  if (row_hi - row_lo > kSortCap) return hipErrorInvalidValue;
   KvoArgs a{};
   a.block_idx = x.block_idx;
   a.cu_q = x.cu_q;
@@ -514,7 +569,9 @@ hipError_t build_edge_lists(const AttnArgs& x, int nb_max, int64_t row_lo, int64
   a.chunk_start = chunk_start;
   a.cursor = cursor;
   a.edges = edges;
-  launch_edge_lists(a, x.batch * x.Hkv * nb_max, st);
+  const int nbk = x.batch * x.Hkv * nb_max;
+  launch_edge_lists(a, nbk, st);
+  if (sorted) hipLaunchKernelGGL(kvo_sort, dim3((unsigned)nbk), dim3(256), 0, st, offsets, edges, nbk);
   return hipGetLastError();
 }
 

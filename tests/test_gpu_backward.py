@@ -157,13 +157,33 @@ def test_backward_beyond_sort_capacity(msa, synth, oracle_lib):
     _check_vs_oracle(oracle_lib, inp, ids, dout, grads, wl, "bwd many buckets")
 
 
-def test_backward_128k_tile_sampled(msa, synth, oracle_lib):
-    """The bench's launch: the last 8192 query rows against the 128K prefix.
-    dO is zero except on 48 sampled rows, so dk / dv are exactly those rows'
-    contributions (which the oracle computes row by row) and dq is exactly 0
-    on every other row."""
+def test_backward_hot_buckets(msa, synth, oracle_lib):
+    """8,192 rows against 8,192 keys: the early blocks are picked by nearly
+    every row (every block of rows below 2,048, a growing share after), so
+    buckets hold up to several thousand edges and dK / dV are summed from
+    many 256-edge chunks; checked against the oracle and for bitwise
+    reproducibility.  8 Q / 2 KV heads keep the oracle fast."""
+    wl = dataclasses.replace(synth.WORKLOADS["prefill_32k"], num_heads=8, num_kv_heads=2, planted=8)
+    kv = [8192]
+    say(f"[bwd] hot buckets kv={kv} heads 8/2")
+    inp, ids, dout, grads = _forward_backward(msa, synth, wl, kv, kv, 49)
+    largest = max(int(torch.bincount(ids[:, g][ids[:, g] >= 0]).max()) for g in range(ids.shape[1]))
+    say(f"    largest bucket {largest} edges")
+    assert largest > 4 * 256
+    _check_vs_oracle(oracle_lib, inp, ids, dout, grads, wl, "bwd hot buckets")
+    _, _, _, again = _forward_backward(msa, synth, wl, kv, kv, 49)
+    for a, b in zip(grads, again):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("tile", [0, 15])
+def test_backward_128k_tile_sampled(msa, synth, oracle_lib, tile):
+    """The bench's launches: 8192 query rows against the 128K causal prefix,
+    the first call (hot early blocks) and the last.  dO is zero except on 48
+    sampled rows, so dk / dv are exactly those rows' contributions (which the
+    oracle computes row by row) and dq is exactly 0 on every other row."""
     wl = synth.WORKLOADS["prefill_128k"]
-    lo, hi = wl.seq_len - wl.q_tile, wl.seq_len
+    lo, hi = tile * wl.q_tile, (tile + 1) * wl.q_tile
     m = hi - lo
     say(f"[bwd] 128K tile rows [{lo}, {hi}), sampled dO")
     inp = synth.prefill_inputs(wl, device="cuda", seed=0)
@@ -177,14 +197,16 @@ def test_backward_128k_tile_sampled(msa, synth, oracle_lib):
     sidx = torch.as_tensor(sample, device="cuda")
     dout = torch.zeros_like(q)
     dout[sidx] = synth.normal((len(sample), wl.num_heads, wl.head_dim), torch.bfloat16, "cuda", 48, "dout")
-    dq, dk, dv = msa.msa_sparse_attn_backward(q, inp["k"], inp["v"], out, dout, lse, ids, cu_q, cu_k, m, hi,
+    # K / V of the call's causal prefix: dk / dv have one row per key of the call
+    kp, vp = inp["k"][:hi], inp["v"][:hi]
+    dq, dk, dv = msa.msa_sparse_attn_backward(q, kp, vp, out, dout, lse, ids, cu_q, cu_k, m, hi,
                                               wl.block_size, wl.topk)
     torch.cuda.synchronize()
     others = torch.ones(m, dtype=torch.bool, device="cuda")
     others[sidx] = False
     assert bool((dq[others] == 0).all()), "dq must be exactly 0 where dO is 0"
     rows, kstart, pos = oracle_lib.rows_prefill([0, m], [0, hi], sample)
-    rdq, rdk, rdv = oracle_lib.sparse_attn_bwd(host(q), host(inp["k"]), host(inp["v"]), host(dout),
+    rdq, rdk, rdv = oracle_lib.sparse_attn_bwd(host(q), host(kp), host(vp), host(dout),
                                                host(ids).numpy()[sample], kstart, pos, rows, wl.block_size, wl.topk)
     _compare("dq", dq[sidx], rdq, "128K tile")
     _compare("dk", dk, rdk, "128K tile")

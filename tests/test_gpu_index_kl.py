@@ -143,3 +143,22 @@ def test_index_kl_several_windows(msa, synth, oracle_lib):
     kv = [9000]
     say(f"[kl] two windows kv={kv}")
     _kl_check(msa, synth, oracle_lib, wl, kv, kv, 55, "kl 2 windows")
+
+
+def test_index_kl_hot_buckets(msa, synth, oracle_lib):
+    """8,192 rows against 8,192 keys: early blocks are picked by nearly every
+    row, so a block's bucket holds thousands of edges (more than one LDS run
+    of the index-key gradient kernel); against the oracle, and bit-identical
+    on a second call.  8 Q / 2 KV heads keep the oracle fast."""
+    wl = dataclasses.replace(synth.WORKLOADS["prefill_32k"], num_heads=8, num_kv_heads=2, planted=8)
+    kv = [8192]
+    say(f"[kl] hot buckets kv={kv}")
+    a = _kl_check(msa, synth, oracle_lib, wl, kv, kv, 56, "kl hot buckets")
+    inp = synth.prefill_inputs(wl, device="cuda", seed=56, seq_lens=kv, q_lens=kv)
+    ids, _, lse, blse = _forward(msa, inp, wl, kv, kv)
+    assert int(torch.bincount(ids[:, 0][ids[:, 0] >= 0]).max()) > 4096
+    b = msa.msa_index_kl_backward(inp["q_idx"], inp["k_idx"], ids, lse, blse, inp["cu_seqlens_q"],
+                                  inp["cu_seqlens_k"], kv[0], kv[0], wl.block_size, wl.topk)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
