@@ -50,13 +50,17 @@ constexpr int kScanThreads = 512;  // 8 waves; each owns 64 columns (two 32-wide
 
 template <typename T, int DI>
 struct ScanLds {
-  // One key block, rows padded by 16 bytes so 16-byte reads of 32 rows at the
-  // same column spread over the banks.
-  static constexpr int kRowBytes = DI * (int)sizeof(T) + 16;
-  static constexpr int kBufBytes = kBlock * kRowBytes;
-  static constexpr int kChunks = kBlock * DI * (int)sizeof(T) / 16;   // 16-byte pieces
-  static constexpr int kPerThread = kChunks / kScanThreads;
+  // One key block in LDS: rows of kChunksPerRow 16-byte chunks plus one chunk
+  // of padding, so 16-byte reads of 32 rows at the same column spread over
+  // the banks.  It is written by direct global-to-LDS loads, each filling 64
+  // consecutive 16-byte slots (lane i slot i), so the padding slots are
+  // written too (with a copy of the row's first chunk) and the buffer is a
+  // whole number of such runs.
   static constexpr int kChunksPerRow = DI * (int)sizeof(T) / 16;
+  static constexpr int kRowSlots = kChunksPerRow + 1;
+  static constexpr int kRowBytes = kRowSlots * 16;
+  static constexpr int kRuns = (kBlock * kRowSlots + kWave - 1) / kWave;  // 64-slot loads per block
+  static constexpr int kBufBytes = kRuns * kWave * 16;
 };
 
 // Operands of the scan's 32x32 MFMA per element type: a lane feeds kLaneK
@@ -95,9 +99,17 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
     int max_chunks, int nb_stride, float* __restrict__ scores) {
   using L = ScanLds<T, DI>;
   using Mm = ScanMma<T>;
-  static_assert(L::kChunks % kScanThreads == 0, "key block must split evenly over threads");
   constexpr int KS = DI / Mm::kStep;  // MFMA contraction steps
-  __shared__ __attribute__((aligned(16))) char lds[2 * L::kBufBytes];
+  // three LDS buffers where they fit beside nothing else (all but fp32 with
+  // d_idx 128); the next key tile's fragments are read ahead, except for fp32,
+  // whose fragments would not fit beside the query fragments in registers
+  constexpr int kRing = 3 * L::kBufBytes <= 112 * 1024 ? 3 : 2;
+  constexpr bool kPrefetch = sizeof(T) < 4;
+  // block scores of the current group of 16 blocks, per wave [block % 16][lane]
+  // (in LDS where it fits, else in registers)
+  constexpr bool kSbLds = kRing * L::kBufBytes + 16 * kScanThreads * 4 <= 128 * 1024;
+  __shared__ __attribute__((aligned(16))) char lds[kRing * L::kBufBytes];
+  __shared__ float s_sb[kSbLds ? kScanThreads / kWave : 1][16][kWave];
 
   // Decode the workgroup: key chunk fastest, then query slice, then query block
   // (heaviest query blocks first), then sequence.
@@ -122,7 +134,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
 
   const int ncols = (phi - plo) * G;
   const int64_t row0 = (int64_t)(plo - (N - M)) + q0;  // first query row
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = lane_id();
   const int col_base = wave * 64;
   const bool active = col_base < ncols;
@@ -133,9 +145,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
   const int col_mine = col_base + lane;
   const bool col_ok = col_mine < ncols;
   float* srow = scores + (row0 * G + (col_ok ? col_mine : 0)) * (int64_t)nb_stride;
-  float sbuf[16];
+  float sbuf[kSbLds ? 1 : 16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) sbuf[j] = 0.f;
+  for (int j = 0; j < (kSbLds ? 1 : 16); ++j) sbuf[j] = 0.f;
 
   // B operand (Q^T): columns col_base + 32*j + lane%32, contraction slots
   // kStep*ks + kLaneK*(lane/32) .. +kLaneK-1.
@@ -149,52 +161,95 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
     for (int ks = 0; ks < KS; ++ks) qf[j][ks] = ok ? Mm::load(qp + Mm::kStep * ks) : Mm::zero();
   }
 
-  // Key blocks are staged into LDS in 16-byte pieces (coalesced global reads),
-  // double-buffered: block s+1 is fetched into registers while block s is used.
+  // Key blocks are staged into LDS in 16-byte pieces (coalesced global reads)
+  // through a ring of kRing buffers: block s + kRing - 1 is fetched into
+  // registers while block s is used, and stored at the end of the step.  With
+  // three buffers, block s + 1 is already in LDS while block s is scored, so
+  // the key fragments of its first tile are read before the step's barrier
+  // and the MFMAs of one block follow those of the previous without a gap.
   const char* kseq = reinterpret_cast<const char*>(k_idx + (int64_t)k0 * DI);
   constexpr int64_t kBlockBytes = (int64_t)kBlock * DI * sizeof(T);
-  u32x4 stage[L::kPerThread];
+  // Block `blk` into ring buffer `ring`: run u (of kRuns) fills slots
+  // 64 u .. 64 u + 63, lane i slot 64 u + i; wave w does runs w, w + 8, ...
+  // A slot's byte offset in the block (its row's chunk, or the row's first
+  // chunk for a padding slot) does not depend on the block.
+  constexpr int kRunsPerWave = (L::kRuns + kScanThreads / kWave - 1) / (kScanThreads / kWave);
+  int src_off[kRunsPerWave];
 #pragma unroll
-  for (int u = 0; u < L::kPerThread; ++u)
-    stage[u] = *reinterpret_cast<const u32x4*>(kseq + s_lo * kBlockBytes + (threadIdx.x + u * kScanThreads) * 16);
-#pragma unroll
-  for (int u = 0; u < L::kPerThread; ++u) {
-    const int piece = threadIdx.x + u * kScanThreads;
-    *reinterpret_cast<u32x4*>(lds + (piece / L::kChunksPerRow) * L::kRowBytes + (piece % L::kChunksPerRow) * 16) =
-        stage[u];
+  for (int u = 0; u < kRunsPerWave; ++u) {
+    const int sl = (u * (kScanThreads / kWave) + wave) * kWave + lane;
+    const int row = min(sl / L::kRowSlots, kBlock - 1);
+    const int chunk = sl % L::kRowSlots;
+    src_off[u] = row * (L::kChunksPerRow * 16) + (chunk < L::kChunksPerRow ? chunk : 0) * 16;
   }
+  auto fetch = [&](int blk, int ring) {
+    const char* src = kseq + blk * kBlockBytes;
+#pragma unroll
+    for (int u = 0; u < kRunsPerWave; ++u) {
+      const int run = u * (kScanThreads / kWave) + wave;
+      if (run < L::kRuns)
+        lds_load16(src + src_off[u], lds + ring * L::kBufBytes + run * kWave * 16);
+    }
+  };
+#pragma unroll
+  for (int pre = 0; pre < kRing - 1; ++pre)
+    if (s_lo + pre < s_hi) fetch(s_lo + pre, pre);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
+  // A operand (K rows): this lane's fragment of key tile kt, step ks, of ring
+  // buffer r: row 32 kt + lane % 32, elements kStep ks + kLaneK (lane / 32) ..
+  constexpr int kStepBytes = Mm::kStep * (int)sizeof(T);
+  const int frag_off = (lane & 31) * L::kRowBytes + Mm::kLaneK * (lane >> 5) * (int)sizeof(T);
+  auto kfrag = [&](int ring, int kt, int ks) {
+    return *reinterpret_cast<const typename Mm::frag*>(lds + ring * L::kBufBytes + 32 * kt * L::kRowBytes + frag_off +
+                                                       kStepBytes * ks);
+  };
+  typename Mm::frag kf[kPrefetch ? 2 : 1][KS];
+  // kf[0]: tile 0 of the first block (later blocks' first tiles are read
+  // during the tile before, with three buffers)
+  if (kPrefetch && active) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[0][ks] = kfrag(0, 0, ks);
+  }
+  int ring = 0;  // ring buffer of block s
   for (int s = s_lo; s < s_hi; ++s) {
-    const int buf = (s - s_lo) & 1;
-    const bool more = s + 1 < s_hi;
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < L::kPerThread; ++u)
-        stage[u] = *reinterpret_cast<const u32x4*>(kseq + (s + 1) * kBlockBytes + (threadIdx.x + u * kScanThreads) * 16);
-    }
+    const int ring_next = ring + 1 == kRing ? 0 : ring + 1;
+    // the buffer of block s - 1, which nothing reads any more
+    if (s + kRing - 1 < s_hi) fetch(s + kRing - 1, ring == 0 ? kRing - 1 : ring - 1);
     if (active) {
-      const char* kb = lds + buf * L::kBufBytes + (lane & 31) * L::kRowBytes + Mm::kLaneK * (lane >> 5) * (int)sizeof(T);
-      constexpr int kStepBytes = Mm::kStep * (int)sizeof(T);
-      float m0 = -__builtin_inff(), m1 = -__builtin_inff();
-      // A operand (K rows) in two register sets: key tile kt+1 is read from
-      // LDS while tile kt's MFMAs run, so LDS latency overlaps the MFMAs.
-      typename Mm::frag kf[2][KS];
+      if (kPrefetch && kRing == 2 && s > s_lo) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[0][ks] = *reinterpret_cast<const typename Mm::frag*>(kb + kStepBytes * ks);
+        for (int ks = 0; ks < KS; ++ks) kf[0][ks] = kfrag(ring, 0, ks);
+      }
+      float m0 = -__builtin_inff(), m1 = -__builtin_inff();
 #pragma unroll
       for (int kt = 0; kt < kBlock / 32; ++kt) {
-        if (kt + 1 < kBlock / 32) {
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            kf[(kt + 1) & 1][ks] =
-                *reinterpret_cast<const typename Mm::frag*>(kb + 32 * (kt + 1) * L::kRowBytes + kStepBytes * ks);
-        }
+        const int cur = kPrefetch ? (kt & 1) : 0;
         f32x16 acc0 = {}, acc1 = {};
+        if constexpr (kPrefetch) {
+          // the next tile's fragments are read between this tile's MFMAs
+          // (the next ring buffer's first tile is read even after the last
+          // block: in bounds, and then unused)
+          const bool pf = kt + 1 < kBlock / 32 || kRing == 3;
+          const int pr = kt + 1 < kBlock / 32 ? ring : ring_next;
+          const int pk = kt + 1 < kBlock / 32 ? kt + 1 : 0;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          acc0 = Mm::mma(kf[kt & 1][ks], qf[0][ks], acc0);
-          acc1 = Mm::mma(kf[kt & 1][ks], qf[1][ks], acc1);
+          for (int ks = 0; ks < KS; ++ks) {
+            acc0 = Mm::mma(kf[cur][ks], qf[0][ks], acc0);
+            acc1 = Mm::mma(kf[cur][ks], qf[1][ks], acc1);
+            if (pf) kf[cur ^ 1][ks] = kfrag(pr, pk, ks);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // then one LDS read
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) kf[0][ks] = kfrag(ring, kt, ks);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            acc0 = Mm::mma(kf[0][ks], qf[0][ks], acc0);
+            acc1 = Mm::mma(kf[0][ks], qf[1][ks], acc1);
+          }
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) { m0 = fmaxf(m0, acc0[r]); m1 = fmaxf(m1, acc1[r]); }
@@ -204,34 +259,42 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
       const float send = lane < 32 ? m1 : m0;
       const float recv = shfl_xor_f(send, 32);
       const float v = fmaxf(lane < 32 ? m0 : m1, recv);
+      if constexpr (kSbLds) {
+        s_sb[wave][s & 15][lane] = v;
+        if ((s & 15) == 15 && col_ok) {
+          f32x4* dst = reinterpret_cast<f32x4*>(srow + (s - 15));
 #pragma unroll
-      for (int j = 0; j < 15; ++j) sbuf[j] = sbuf[j + 1];
-      sbuf[15] = v;
-      if ((s & 15) == 15 && col_ok) {
-        f32x4* dst = reinterpret_cast<f32x4*>(srow + (s - 15));
+          for (int q = 0; q < 4; ++q)
+            dst[q] = f32x4{s_sb[wave][4 * q][lane], s_sb[wave][4 * q + 1][lane], s_sb[wave][4 * q + 2][lane],
+                           s_sb[wave][4 * q + 3][lane]};
+        }
+      } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dst[q] = f32x4{sbuf[4 * q], sbuf[4 * q + 1], sbuf[4 * q + 2], sbuf[4 * q + 3]};
+        for (int j = 0; j < 15; ++j) sbuf[j] = sbuf[j + 1];
+        sbuf[15] = v;
+        if ((s & 15) == 15 && col_ok) {
+          f32x4* dst = reinterpret_cast<f32x4*>(srow + (s - 15));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dst[q] = f32x4{sbuf[4 * q], sbuf[4 * q + 1], sbuf[4 * q + 2], sbuf[4 * q + 3]};
+        }
       }
     }
-    if (more) {
-      char* dst = lds + (buf ^ 1) * L::kBufBytes;
-#pragma unroll
-      for (int u = 0; u < L::kPerThread; ++u) {
-        const int piece = threadIdx.x + u * kScanThreads;
-        *reinterpret_cast<u32x4*>(dst + (piece / L::kChunksPerRow) * L::kRowBytes + (piece % L::kChunksPerRow) * 16) =
-            stage[u];
-      }
-    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // block s + kRing - 1 is in LDS
     __syncthreads();
+    ring = ring_next;
   }
   // a trailing partial group (only at the end of a query block's last chunk)
   const int n_tail = s_hi & 15;
   if (active && col_ok && n_tail != 0) {
     const int g0 = s_hi - n_tail;
+    if constexpr (kSbLds) {
+      for (int j = 0; j < n_tail; ++j) srow[g0 + j] = s_sb[wave][j][lane];
+    } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = i - (16 - n_tail);
-      if (j >= 0) srow[g0 + j] = sbuf[i];
+      for (int i = 0; i < 16; ++i) {
+        const int j = i - (16 - n_tail);
+        if (j >= 0) srow[g0 + j] = sbuf[i];
+      }
     }
   }
 }

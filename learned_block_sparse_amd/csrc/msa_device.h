@@ -118,6 +118,17 @@ __device__ __forceinline__ f32x4 mma16_fp8(long a, long b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
 }
 
+// Direct global-to-LDS load of 16 bytes per lane (gfx950): lane i's 16 bytes
+// from `src` land at lds_base + 16 i; lds_base must be the same for the whole
+// wave.  The load counts in vmcnt: wait for it (s_waitcnt vmcnt) before a
+// barrier that makes the data visible to other waves.  The builtin exists
+// only in the device pass; the host pass of a kernel body never runs it.
+__device__ __forceinline__ void lds_load16(const void* src, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+#endif
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
