@@ -95,10 +95,6 @@ __device__ __forceinline__ unsigned kl_row_mask(const int32_t* sel, int topk, in
   return mask;
 }
 
-__global__ __launch_bounds__(256) void kl_zero(KlArgs a) {
-  const int64_t n = (int64_t)a.cu_k[a.batch] * a.DI;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) a.dk_idx[i] = 0.f;
-}
 
 // ------------------------------------------------------------- kl_scores
 template <typename T, int DI>
@@ -348,7 +344,15 @@ __global__ __launch_bounds__(256) void kl_dk(KlArgs a, int split) {
     pre[g + 1] = pre[g] + (g < a.G ? a.offsets[bucket + 1] - ebase[g] : 0);
   }
   const int total = pre[kRmaxKl];
-  if (total == 0) return;
+  const int64_t kb0 = a.cu_k[b];
+  const int N = a.cu_k[b + 1] - a.cu_k[b];
+  if (total == 0) {
+    // no edge in this window: the first window writes the keys' rows as zero
+    if (a.row_lo == 0)
+      for (int kk = 0; kk < keys_wave && c * kBlock + k0 + kk < N; ++kk)
+        for (int d = lane; d < DI; d += kWave) a.dk_idx[(kb0 + c * kBlock + k0 + kk) * DI + d] = 0.f;
+    return;
+  }
   for (int i = lane; i < keys_wave * DI; i += kWave) acc[i] = 0.f;
 
   // key and dS of sequence position f
@@ -409,13 +413,14 @@ __global__ __launch_bounds__(256) void kl_dk(KlArgs a, int split) {
       }
     }
   }
-  const int64_t kb0 = a.cu_k[b];
-  const int N = a.cu_k[b + 1] - a.cu_k[b];
   for (int kk = 0; kk < keys_wave; ++kk) {
     if (c * kBlock + k0 + kk >= N) break;
     float* dst = a.dk_idx + (kb0 + c * kBlock + k0 + kk) * DI + kN * lane;
 #pragma unroll
-    for (int i = 0; i < kN; ++i) dst[i] += acc[kk * DI + kN * lane + i];
+    for (int i = 0; i < kN; ++i) {
+      const float v = acc[kk * DI + kN * lane + i];
+      dst[i] = a.row_lo == 0 ? v : dst[i] + v;  // the first window writes outright
+    }
   }
 }
 
@@ -477,7 +482,6 @@ static hipError_t launch_kl_t(const KlPlan& pl, const KlLaunch& x, void* ws, hip
   a.loss = x.loss;
   a.dq_idx = x.dq_idx;
   a.dk_idx = x.dk_idx;
-  hipLaunchKernelGGL(kl_zero, dim3(1024), dim3(256), 0, st, a);
   for (int64_t r0 = 0; r0 < pl.rows_bound; r0 += pl.window) {
     const int64_t r1 = r0 + pl.window < pl.rows_bound ? r0 + pl.window : pl.rows_bound;
     hipError_t e = build_edge_lists(x.attn, pl.nb_max, r0, r1, counts, offsets, chunks, cursor, edges, true, st);

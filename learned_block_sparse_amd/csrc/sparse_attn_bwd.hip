@@ -14,7 +14,10 @@
 // (dk, dv summed over every row and head of the group that attends j).
 //
 // Kernels (bf16 inputs, fp32 accumulation and fp32 gradients):
-//   bwd_zero   dk = dv = 0 for the key rows of the call
+//   bwd_zero   dk = dv = 0 for the key rows no selection of the first query
+//              window reaches (the rows of every other block are written
+//              outright by that window's bwd_dkdv / bwd_dkdv_reduce, and later
+//              windows add to them)
 //   bwd_delta  delta[row, head] = dO . O
 //   bwd_dkv_scan  chunk starts of bwd_dkdv: each bucket of the selection
 //              edge lists (the lists the KV-outer forward builds, here sorted
@@ -89,12 +92,25 @@ __device__ __forceinline__ int bwd_find(const int32_t* cu, int n, int64_t x) {
   return lo;
 }
 
-// dk = dv = 0 over the call's key rows (cu_k[batch] of them), grid-stride.
+// dk = dv = 0 over the key rows of the buckets without an edge in the first
+// window: one workgroup per bucket (sequence, group, block), 128 rows of the
+// group's 128 dims.
 __global__ __launch_bounds__(256) void bwd_zero(BwdKernelArgs a) {
-  const int64_t n = (int64_t)a.cu_k[a.batch] * a.G * kHeadDim / 4;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    reinterpret_cast<f32x4*>(a.dk)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    reinterpret_cast<f32x4*>(a.dv)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nbk = a.batch * a.G * a.nb_max;
+  const int bucket = blockIdx.x;
+  if (bucket >= nbk || a.offsets[bucket + 1] > a.offsets[bucket]) return;
+  const int c = bucket % a.nb_max;
+  const int g = (bucket / a.nb_max) % a.G;
+  const int b = bucket / (a.nb_max * a.G);
+  const int64_t kb0 = a.cu_k[b];
+  const int N = a.cu_k[b + 1] - a.cu_k[b];
+  const int64_t rs = (int64_t)a.G * kHeadDim;
+  for (int u = threadIdx.x; u < kBlock * kHeadDim / 4; u += 256) {
+    const int kk = c * kBlock + u / (kHeadDim / 4), d = 4 * (u % (kHeadDim / 4));
+    if (kk >= N) continue;
+    const int64_t off = (kb0 + kk) * rs + g * kHeadDim + d;
+    *reinterpret_cast<f32x4*>(a.dk + off) = f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4*>(a.dv + off) = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -408,8 +424,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
         const int kk = c * kBlock + 32 * wave + 8 * (r >> 2) + 4 * a32 + (r & 3);
         if (kk >= N) continue;
         const int64_t off = (kb0 + kk) * rs + g * kHeadDim + 32 * dt + col;
-        a.dk[off] += dk_acc[dt][r] * a.scale;
-        a.dv[off] += dv_acc[dt][r];
+        if (a.row_lo == 0) {  // the first window writes its blocks' rows outright
+          a.dk[off] = dk_acc[dt][r] * a.scale;
+          a.dv[off] = dv_acc[dt][r];
+        } else {
+          a.dk[off] += dk_acc[dt][r] * a.scale;
+          a.dv[off] += dv_acc[dt][r];
+        }
       }
   } else {
     float* pk = a.part_dkv + (int64_t)(a.dkv_part[bucket] + chunk) * (2 * kBlock * kHeadDim);
@@ -465,8 +486,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce(BwdKernelArgs a) {
     const int kk = c * kBlock + key;
     if (kk >= N) continue;
     float* dst = (is_v ? a.dv : a.dk) + (kb0 + kk) * rs + g * kHeadDim + d;
-    const f32x4 cur = *reinterpret_cast<f32x4*>(dst);
-    *reinterpret_cast<f32x4*>(dst) = cur + (is_v ? acc : acc * a.scale);
+    const f32x4 add = is_v ? acc : acc * a.scale;
+    if (a.row_lo == 0) *reinterpret_cast<f32x4*>(dst) = add;  // the first window writes outright
+    else *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<f32x4*>(dst) + add;
   }
 }
 
@@ -766,13 +788,13 @@ hipError_t launch_sparse_attn_bwd(const BwdPlan& pl, const BwdArgs& x, void* ws,
   a.dk = x.dk;
   a.dv = x.dv;
 
-  hipLaunchKernelGGL(bwd_zero, dim3(2048), dim3(256), 0, st, a);
   hipLaunchKernelGGL(bwd_delta, dim3((unsigned)((pl.rows_bound * a.Hq + 7) / 8)), dim3(256), 0, st, a);
   for (int64_t r0 = 0; r0 < pl.rows_bound; r0 += pl.window) {
     const int64_t r1 = r0 + pl.window < pl.rows_bound ? r0 + pl.window : pl.rows_bound;
     hipError_t e = build_edge_lists(x.fwd, pl.nb_max, r0, r1, counts, offsets, chunks, cursor, a.edges, true, st);
     if (e != hipSuccess) return e;
     a.row_lo = r0;
+    if (r0 == 0) hipLaunchKernelGGL(bwd_zero, dim3((unsigned)pl.nbuckets), dim3(256), 0, st, a);
     const int64_t entries = (r1 - r0) * a.G * a.topk;
     hipLaunchKernelGGL(bwd_dkv_scan, dim3(1), dim3(1024), 0, st, a, pl.nbuckets);
     // chunks of kDkvChunk edges: at most entries / kDkvChunk + one partial chunk per bucket
