@@ -38,11 +38,13 @@
 //              longer bucket write fp32 partials
 //   bwd_dkdv_reduce  adds each long bucket's partials to dK / dV in chunk
 //              order
-//   bwd_dq_kvo KV-outer like the forward, one workgroup per chunk of <= 64
-//              edges of a bucket: S^T = K Q^T and dP^T = V dO^T with two
-//              queries x 16 heads as the 32 MFMA columns, then dQ += dS K
-//              from registers; each edge writes its block's dQ contribution
-//              to the bf16 partial of its selection slot
+//   bwd_dq_kvo KV-outer like the forward, one workgroup of 8 waves (two per
+//              SIMD) per chunk of bwd_dkdv (<= 256 edges of a bucket, so the
+//              staging of K, V and K^T is paid once per 256 edges): S^T = K Q^T and
+//              dP^T = V dO^T with two queries x 16 heads as the 32 MFMA
+//              columns, then dQ += dS K from registers; each edge writes its
+//              block's dQ contribution to the bf16 partial of its selection
+//              slot
 //   bwd_dq_combine  dq = sum of a row's slot partials in slot order
 // No atomics touch the arithmetic: every result is bitwise reproducible.
 #include "msa_device.h"
@@ -602,20 +604,22 @@ __device__ __forceinline__ void dq_pair(const BwdKernelArgs& a, DqPair& P, int e
   }
 }
 
-__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kvo(BwdKernelArgs a) {
+constexpr int kDqThreads = 512;  // 8 waves: two per SIMD, one pair of edges in flight each
+
+__global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kvo(BwdKernelArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 k_lds[kBlock * kDqKRow];
   __shared__ __attribute__((aligned(16))) bf16 v_lds[kBlock * kDqKRow];
   __shared__ __attribute__((aligned(16))) bf16 kt_lds[kHeadDim * kDqKtRow];
   const int nbk = a.batch * a.G * a.nb_max;
   const int w = blockIdx.x;
-  if (w >= a.chunk_start[nbk]) return;
-  const int bucket = bwd_find(a.chunk_start, nbk, w);
-  const int chunk = w - a.chunk_start[bucket];
+  if (w >= a.dkv_chunk[nbk]) return;
+  const int bucket = bwd_find(a.dkv_chunk, nbk, w);
+  const int chunk = w - a.dkv_chunk[bucket];
   const int c = bucket % a.nb_max;
   const int g = (bucket / a.nb_max) % a.G;
   const int b = bucket / (a.nb_max * a.G);
-  const int e_lo = a.offsets[bucket] + chunk * kEdgeChunk;
-  const int e_hi = min(e_lo + kEdgeChunk, a.offsets[bucket + 1]);
+  const int e_lo = a.offsets[bucket] + chunk * kDkvChunk;
+  const int e_hi = min(e_lo + kDkvChunk, a.offsets[bucket + 1]);
   const int64_t kb0 = a.cu_k[b];
   const int N = a.cu_k[b + 1] - a.cu_k[b];
   const int64_t q0 = a.cu_q[b];
@@ -626,8 +630,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kvo(BwdKernelArgs a) {
   // clamp to its last row; their scores are masked)
   {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int piece = threadIdx.x + u * kBwdThreads;
+    for (int u = 0; u < kBlock * kHeadDim / 8 / kDqThreads; ++u) {
+      const int piece = threadIdx.x + u * kDqThreads;
       const int row = piece >> 4, cc = (piece & 15) * 8;
       const int64_t key = min(c * kBlock + row, N - 1);
       const int64_t off = (kb0 + key) * rs + g * kHeadDim + cc;
@@ -636,8 +640,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kvo(BwdKernelArgs a) {
     }
     // K^T unit = (key quad kq, dim octet o8): 4 rows x 8 dims, written as 8 runs of 4 keys
 #pragma unroll
-    for (int uu = 0; uu < 2; ++uu) {
-      const int u = threadIdx.x + uu * kBwdThreads;
+    for (int uu = 0; uu < kBlock * kHeadDim / 32 / kDqThreads; ++uu) {
+      const int u = threadIdx.x + uu * kDqThreads;
       const int kq = u & 31, o8 = u >> 5;
       bf16x8 r4[4];
 #pragma unroll
@@ -660,16 +664,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kvo(BwdKernelArgs a) {
   const int a32 = lane >> 5;
   const int jq = col >> 4, h = col & 15;
   const int R = a.Hq / a.G;
-  constexpr int kPairStride = 2 * (kBwdThreads / kWave);
+  constexpr int kPairStride = 2 * (kDqThreads / kWave);
   const int e0 = e_lo + 2 * wave;
-  DqPair A, B;
+  DqPair A;
   dq_load_pair(a, A, e0, e_hi, jq, h, a32, g, R);
-  dq_load_pair(a, B, e0 + kPairStride, e_hi, jq, h, a32, g, R);
-  for (int e = e0; e < e_hi; e += 2 * kPairStride) {
-    dq_pair(a, A, e + 2 * kPairStride, e_hi, k_lds, v_lds, kt_lds, c, g, R, N, M, q0, col, a32, jq, h);
-    if (e + kPairStride >= e_hi) break;
-    dq_pair(a, B, e + 3 * kPairStride, e_hi, k_lds, v_lds, kt_lds, c, g, R, N, M, q0, col, a32, jq, h);
-  }
+  for (int e = e0; e < e_hi; e += kPairStride)
+    dq_pair(a, A, e + kPairStride, e_hi, k_lds, v_lds, kt_lds, c, g, R, N, M, q0, col, a32, jq, h);
 }
 
 // Validity of the entries of one selection row: attended when the id names a
@@ -801,9 +801,7 @@ hipError_t launch_sparse_attn_bwd(const BwdPlan& pl, const BwdArgs& x, void* ws,
     const int64_t ub_kv = entries / kDkvChunk + (entries < pl.nbuckets ? entries : pl.nbuckets) + 1;
     hipLaunchKernelGGL(bwd_dkdv, dim3((unsigned)ub_kv), dim3(kBwdThreads), 0, st, a);
     hipLaunchKernelGGL(bwd_dkdv_reduce, dim3((unsigned)pl.nbuckets * kReduceSplit), dim3(256), 0, st, a);
-    // chunks of kEdgeChunk edges: at most entries / kEdgeChunk + one partial chunk per bucket
-    const int64_t ub = entries / kEdgeChunk + (entries < pl.nbuckets ? entries : pl.nbuckets) + 1;
-    hipLaunchKernelGGL(bwd_dq_kvo, dim3((unsigned)ub), dim3(kBwdThreads), 0, st, a);
+    hipLaunchKernelGGL(bwd_dq_kvo, dim3((unsigned)ub_kv), dim3(kDqThreads), 0, st, a);
     hipLaunchKernelGGL(bwd_dq_combine, dim3((unsigned)(((r1 - r0) * a.G + 3) / 4)), dim3(256), 0, st, a, r1);
   }
   return hipGetLastError();
