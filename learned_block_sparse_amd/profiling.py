@@ -107,7 +107,123 @@ def copy_factor(rows, nbytes):
     return big * 1024.0 / nbytes
 
 
+# readable names for the kernels rocprofv3 leaves mangled (the bf16
+# instantiations: it cannot demangle the __bf16 template argument)
+KERNEL_NAMES = {
+    "_ZN3msa8kvo_attnIDF16bEEvNS_7KvoArgsE": "kvo_attn<bf16>", "kvo_attn": "kvo_attn<fp8e4m3>",
+    "_ZN3msa16idx_scan_prefillIDF16bLi128EEEvPKT_S3_PKiS5_iiiiiiiPf": "idx_scan_prefill<bf16,128>",
+    "idx_scan_prefill": "idx_scan_prefill<fp8e4m3,128>",
+    "_ZN3msa17idx_decode_scoresIDF16bLi128ELb1EEEvPKT_S3_PKiS5_S5_iiiPf": "idx_decode_scores<bf16,128,lds>",
+    "idx_decode_scores": "idx_decode_scores<fp8e4m3,128,lds>",
+    "_ZN3msa5kl_dkIDF16bLi128EEEvNS_6KlArgsEi": "kl_dk<bf16,128>",
+    "_ZN3msa7kl_lossIDF16bEEvNS_6KlArgsE": "kl_loss<bf16>",
+    "_ZN3msa9kl_scoresIDF16bLi128EEEvNS_6KlArgsE": "kl_scores<bf16,128>",
+    "_ZN3msa14index_frontendIDF16bDF16bLi128EEEvNS_6FeArgsE": "index_frontend<bf16,bf16,128>",
+    "_ZN3msa15sparse_attn_fwdIDF16bDF16bEEvNS_14AttnKernelArgsE": "sparse_attn_fwd<bf16,bf16>",
+    "_ZN3msa15sparse_attn_fwdIDF16bNS_7fp8e4m3EEEvNS_14AttnKernelArgsE": "sparse_attn_fwd<bf16,fp8e4m3>",
+    "_ZN3msa12attn_combineIDF16bEEvPKfS2_PKiiliiPT_Pf": "attn_combine<bf16>",
+}
+OURS = ("kvo_", "idx_", "bwd_", "kl_", "fe_bwd", "index_frontend", "sparse_attn", "attn_combine")
+
+
+def kernel_table(stats_csv):
+    """Rows (name, calls, avg_us, min_us, max_us, total_ms, pct of all kernel
+    time) of a rocprofv3 --stats kernel csv, the library's kernels only,
+    largest total first."""
+    rows = list(csv.DictReader(open(stats_csv)))
+    total_all = sum(float(r["TotalDurationNs"]) for r in rows)
+    tab = []
+    for r in rows:
+        n = KERNEL_NAMES.get(r["Name"], r["Name"])
+        if not n.startswith(OURS):
+            continue
+        tab.append((n, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                    float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6,
+                    100 * float(r["TotalDurationNs"]) / total_all))
+    tab.sort(key=lambda x: -x[5])
+    return tab
+
+
+def kernels_main(argv):
+    """``kernels --stats CSV --title T --command C --out FILE``: the kernel
+    table of one rocprofv3 --kernel-trace --stats run as a text summary."""
+    ap = argparse.ArgumentParser(prog="profiling kernels")
+    ap.add_argument("--stats", required=True)
+    ap.add_argument("--title", required=True)
+    ap.add_argument("--command", required=True)
+    ap.add_argument("--note", action="append", default=[])
+    ap.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    from learned_block_sparse_amd import build
+    lines = [f"# {a.title}", "", "Command (repository root, GPU host):", "  " + a.command, ""]
+    lines += a.note + ([""] if a.note else [])
+    lines.append(f"{'kernel':44s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_ms':>9s} {'pct':>6s}")
+    for n, c, av, mn, mx, t, pc in kernel_table(a.stats):
+        lines.append(f"{n[:44]:44s} {c:6d} {av:9.1f} {mn:9.1f} {mx:9.1f} {t:9.2f} {pc:6.1f}")
+    lines.append("")
+    lines.append("pct is of all GPU kernel time in the run, input generation included.")
+    lines.append(f"kernel source digest: {build.source_digest()}")
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def counters_main(argv):
+    """``counters --dir DIR --title T --command C --out FILE``: MFMA busy,
+    wait and LDS bank conflicts per kernel from one rocprofv3 --pmc pass with
+    SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_ANY
+    SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE (kernel cycles = SQ_BUSY_CYCLES /
+    32: the counter sums over the 32 shader engines; mfma_busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / (kernel cycles x 1024 SIMDs))."""
+    ap = argparse.ArgumentParser(prog="profiling counters")
+    ap.add_argument("--dir", required=True)
+    ap.add_argument("--title", required=True)
+    ap.add_argument("--command", required=True)
+    ap.add_argument("--note", action="append", default=[])
+    ap.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    from learned_block_sparse_amd import build
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    for r in _rows(a.dir):
+        n = KERNEL_NAMES.get(r["Kernel_Name"], r["Kernel_Name"])
+        if not n.startswith(OURS):
+            continue
+        per[n][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[n].add(r["Dispatch_Id"])
+    tab = []
+    for n, c in per.items():
+        nd = len(disp[n])
+        kc = c["SQ_BUSY_CYCLES"] / 32 / nd
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / nd / (kc * 1024) if kc else 0.0
+        wait = c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"] if c["SQ_WAVE_CYCLES"] else 0.0
+        conf = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"] if c["SQ_LDS_IDX_ACTIVE"] else 0.0
+        tab.append((n, nd, kc, busy, wait, conf))
+    tab.sort(key=lambda x: -x[2])
+    lines = [f"# {a.title}", "", "Command (repository root, GPU host):", "  " + a.command, ""]
+    lines += a.note + ([""] if a.note else [])
+    lines.append("Columns: kernel cycles = SQ_BUSY_CYCLES / 32 (the counter sums over the 32 shader engines);")
+    lines.append("mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (kernel cycles x 1024 SIMDs); wait = SQ_WAIT_ANY /")
+    lines.append("SQ_WAVE_CYCLES (share of wave time spent waiting); lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.")
+    lines.append("")
+    lines.append(f"{'kernel':32s} {'disp':>5s} {'kcycles':>10s} {'mfma_busy':>10s} {'wait':>7s} {'lds_conflict':>13s}")
+    for n, nd, kc, b, w, cf in tab:
+        lines.append(f"{n[:32]:32s} {nd:5d} {kc:10.3g} {100 * b:9.1f}% {100 * w:6.1f}% {100 * cf:12.1f}%")
+    lines.append("")
+    lines.append(f"kernel source digest: {build.source_digest()}")
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
+    import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "kernels":
+        kernels_main(sys.argv[2:])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "counters":
+        counters_main(sys.argv[2:])
+        return
     ap = argparse.ArgumentParser()
     for k in ("prefill-fetch", "prefill-write", "decode-fetch", "decode-write", "copy-fetch", "copy-write"):
         ap.add_argument("--" + k, required=True)
