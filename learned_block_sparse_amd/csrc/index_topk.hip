@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
     for (int u = 0; u < kRunsPerWave; ++u) {
       const int run = u * (kScanThreads / kWave) + wave;
       if (run < L::kRuns)
-        lds_load16(src + src_off[u], lds + ring * L::kBufBytes + run * kWave * 16);
+        lds_load16(src, (int)kBlockBytes, src_off[u], lds + ring * L::kBufBytes + run * kWave * 16);
     }
   };
 #pragma unroll
@@ -223,11 +223,18 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
         for (int ks = 0; ks < KS; ++ks) kf[0][ks] = kfrag(ring, 0, ks);
       }
       float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+      if constexpr (kPrefetch) {
+        // Two accumulator sets: tile kt's scores are max-pooled during the
+        // second half of tile kt + 1's MFMAs (its results are complete by
+        // then), so the MFMA pipe does not wait for the pooling; the last
+        // tile's are pooled after the loop.
+        f32x16 acc[2][2];
+        // the pooling runs in the last kPool steps of a tile (at least one)
+        constexpr int kPool = KS / 2 > 0 ? KS / 2 : 1;
+        constexpr int kRowsPerStep = (16 + kPool - 1) / kPool;
 #pragma unroll
-      for (int kt = 0; kt < kBlock / 32; ++kt) {
-        const int cur = kPrefetch ? (kt & 1) : 0;
-        f32x16 acc0 = {}, acc1 = {};
-        if constexpr (kPrefetch) {
+        for (int kt = 0; kt < kBlock / 32; ++kt) {
+          const int cur = kt & 1;
           // the next tile's fragments are read between this tile's MFMAs
           // (the next ring buffer's first tile is read even after the last
           // block: in bounds, and then unused)
@@ -236,13 +243,32 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
           const int pk = kt + 1 < kBlock / 32 ? kt + 1 : 0;
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            acc0 = Mm::mma(kf[cur][ks], qf[0][ks], acc0);
-            acc1 = Mm::mma(kf[cur][ks], qf[1][ks], acc1);
+            acc[cur][0] = Mm::mma(kf[cur][ks], qf[0][ks], ks == 0 ? f32x16{} : acc[cur][0]);
+            acc[cur][1] = Mm::mma(kf[cur][ks], qf[1][ks], ks == 0 ? f32x16{} : acc[cur][1]);
             if (pf) kf[cur ^ 1][ks] = kfrag(pr, pk, ks);
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // then one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            const int h = ks - (KS - kPool);
+            if (kt > 0 && h >= 0) {
+#pragma unroll
+              for (int r = h * kRowsPerStep; r < (h + 1) * kRowsPerStep && r < 16; ++r) {
+                m0 = fmaxf(m0, acc[cur ^ 1][0][r]);
+                m1 = fmaxf(m1, acc[cur ^ 1][1][r]);
+              }
+              __builtin_amdgcn_sched_group_barrier(0x002, kRowsPerStep, 0);  // the pooling
+            }
           }
-        } else {
+          // keep each tile's MFMAs within its own step: the next tile's
+          // MFMAs would otherwise be pulled up behind their fragment reads
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        constexpr int last = (kBlock / 32 - 1) & 1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { m0 = fmaxf(m0, acc[last][0][r]); m1 = fmaxf(m1, acc[last][1][r]); }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < kBlock / 32; ++kt) {
+          f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) kf[0][ks] = kfrag(ring, kt, ks);
 #pragma unroll
@@ -250,9 +276,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
             acc0 = Mm::mma(kf[0][ks], qf[0][ks], acc0);
             acc1 = Mm::mma(kf[0][ks], qf[1][ks], acc1);
           }
-        }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { m0 = fmaxf(m0, acc0[r]); m1 = fmaxf(m1, acc1[r]); }
+          for (int r = 0; r < 16; ++r) { m0 = fmaxf(m0, acc0[r]); m1 = fmaxf(m1, acc1[r]); }
+        }
       }
       // Lane l < 32 owns column l of tile 0, lane l >= 32 column l-32 of tile 1;
       // each needs the other half-wave's partial max of its own column.
@@ -314,28 +340,33 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int batch, int64_t ro
 constexpr int kPreRound = 16 * kWave;     // blocks per selection round (16 keys per lane)
 constexpr int kPreCand = 16 * 16 + 16;    // candidate bound per round (see below)
 
-// Wave-wide bitonic sort of one 64-bit key per lane, descending across lanes.
-__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
-  const int lane = lane_id();
+// The kth largest of the wave's 64-bit keys (one per lane), or a value no
+// larger than any nonzero key when fewer than kth are nonzero: a bitwise
+// binary search for the largest t with at least kth keys >= t, counted by
+// ballots.  The high words are searched first; among keys whose high word
+// equals the result, only the low `lo_bits` bits vary (selection keys hold
+// 0xffffffff - id with id < 2^lo_bits), so the bits above are set at once.
+__device__ __forceinline__ uint64_t wave_kth_largest(uint64_t x, int kth, int lo_bits) {
+  const uint32_t xh = (uint32_t)(x >> 32);
+  uint32_t th = 0;
 #pragma unroll
-  for (int k = 2; k <= kWave; k <<= 1)
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t y = shfl_xor_u64(x, j);
-      // the lower lane of a pair keeps the larger key in descending runs
-      const bool desc = (lane & k) == 0;
-      const bool lower = (lane & j) == 0;
-      const bool keep_max = desc == lower;
-      x = keep_max ? (x > y ? x : y) : (x > y ? y : x);
-    }
-  return x;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t t = th | (1u << b);
+    if (__popcll(__ballot(xh >= t)) >= kth) th = t;
+  }
+  uint32_t tl = lo_bits >= 32 ? 0u : (0xffffffffu << lo_bits);
+  for (int b = lo_bits - 1; b >= 0; --b) {
+    const uint64_t t = ((uint64_t)th << 32) | (tl | (1u << b));
+    if (__popcll(__ballot(x >= t)) >= kth) tl |= 1u << b;
+  }
+  return ((uint64_t)th << 32) | tl;
 }
 
 // One wave per (query row, group).  The scan left the row's block scores in
 // `scores`; rounds of 1024 earlier blocks (16 per lane) update the 16 best
 // selection keys (per-wave LDS, `best`):
-//   1. lane maxima of the round's keys, sorted across the wave; T = the 16th
-//      largest, raised to best[15] if that is larger.  At least 16 keys of the
+//   1. lane maxima of the round's keys; T = their 16th largest (a ballot
+//      search), raised to best[15] if that is larger.  At least 16 keys of the
 //      round and the previous best are >= T, so every member of their top 16
 //      is; only the 16 lanes whose maximum reaches T hold such keys, so there
 //      are at most 16 * 16 + 16 candidates;
@@ -366,6 +397,7 @@ __global__ __launch_bounds__(256) void idx_select_prefill(
   uint64_t* cand = s_cand[wave];
   uint64_t* best = s_best[wave];
   if (lane < 16) best[lane] = 0;
+  const int lo_bits = local > 1 ? 32 - __clz(local - 1) : 0;  // bits of the largest earlier id
   for (int r0 = 0; r0 < local; r0 += kPreRound) {
     float v[16];
 #pragma unroll
@@ -380,8 +412,7 @@ __global__ __launch_bounds__(256) void idx_select_prefill(
       k16[u] = c < local ? sel_key(v[u], c) : 0;
       mx = k16[u] > mx ? k16[u] : mx;
     }
-    const uint64_t sorted = wave_sort_desc(mx);
-    const uint64_t t_round = shfl_u64(sorted, 15);
+    const uint64_t t_round = wave_kth_largest(mx, 16, lo_bits);
     const uint64_t b15 = best[15];
     const uint64_t T = t_round > b15 ? t_round : b15;
     // compact the candidates (keys >= T) into LDS, lane order within each u

@@ -118,14 +118,22 @@ __device__ __forceinline__ f32x4 mma16_fp8(long a, long b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
 }
 
-// Direct global-to-LDS load of 16 bytes per lane (gfx950): lane i's 16 bytes
-// from `src` land at lds_base + 16 i; lds_base must be the same for the whole
-// wave.  The load counts in vmcnt: wait for it (s_waitcnt vmcnt) before a
-// barrier that makes the data visible to other waves.  The builtin exists
-// only in the device pass; the host pass of a kernel body never runs it.
-__device__ __forceinline__ void lds_load16(const void* src, void* lds_base) {
+// Direct memory-to-LDS load of 16 bytes per lane (gfx950), through a buffer
+// resource over [base, base + bytes): lane i reads the 16 bytes at byte offset
+// voff and they land at lds_base + 16 i; lds_base must be the same for the
+// whole wave.  A lane whose 16 bytes are not inside the range reads zeros (the
+// buffer unit's range check), so a wrong offset cannot reach other memory.  The
+// load counts in vmcnt only: wait for it (s_waitcnt vmcnt) before a barrier
+// that makes the data visible to other waves.  The global-address form of this
+// load is taken by the compiler as an event of the LDS counter too, after which
+// every wait for an LDS read becomes a wait for all of them; the buffer form is
+// not.  The builtins exist only in the device pass; the host pass of a kernel
+// body never runs this.
+__device__ __forceinline__ void lds_load16(const void* base, int bytes, int voff, void* lds_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+  // word 3: 32-bit data format (required for untyped loads on this family)
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, 0, 0, 0);
 #endif
 }
 
