@@ -137,6 +137,20 @@ __device__ __forceinline__ void lds_load16(const void* base, int bytes, int voff
 #endif
 }
 
+// Transposed LDS read of 16-bit data (gfx950): every lane gives the address
+// of four consecutive 16-bit values (8-byte aligned); lane 16 g + i receives,
+// as element e, value i % 4 of the four at the address of lane 16 g + 4 e +
+// i / 4.  With lane 16 g + 4 e + q pointing at row r0 + e, columns c0 + 4 q
+// .. + 3 of a row-major tile, lane 16 g + i gets column c0 + i of rows r0 ..
+// r0 + 3: a column fragment of an MFMA operand read from a row-major tile.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)p);
+#else
+  return bf16x4{};
+#endif
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }

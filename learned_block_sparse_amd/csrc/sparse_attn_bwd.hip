@@ -170,188 +170,220 @@ __global__ __launch_bounds__(1024) void bwd_dkv_scan(BwdKernelArgs a, int nbk) {
   }
 }
 
-// One quad of edges (4 queries x 16 heads = 64 MFMA rows), staged by the
-// whole workgroup.  Thread tid owns two units of 4 MFMA rows x 8 dims: unit
-// v = tid + 256 u, tensor v / 256 (Q or dO), row quad (v % 256) / 16, dim
-// octet v % 16 (16 consecutive threads read a row's 256 contiguous bytes).
+// One quad of edges (4 queries x 16 heads = 64 MFMA rows).  Its Q and dO are
+// staged in LDS row-major, one tile each, rows of kBwdRow bf16 (256 bytes of
+// data and a 16-byte pad slot, so 16-byte reads of 32 rows at one column
+// spread over the banks), by direct buffer-to-LDS loads: a tile is 64 x 17
+// slots of 16 bytes, filled by 17 loads of 64 consecutive slots (lane i slot
+// i); a pad slot receives a copy of its row's first slot.  S = Q K^T and
+// dP = dO V^T read the tiles row-major; dV += P^T dO and dK += dS^T Q read
+// them transposed (lds_read_tr4), so no second copy is staged.
 constexpr int kQuadRows = 64;
-constexpr int kBwdT = kQuadRows + 4;  // LDS row of Q^T / dO^T for one dim: 64 rows + 4 pad
+constexpr int kRowSlots = kBwdRow * 2 / 16;               // 17 slots of 16 bytes per row
+constexpr int kTileRuns = kQuadRows * kRowSlots / kWave;  // 17 loads of 64 slots per tile
+constexpr int kQuadRuns = 2 * kTileRuns;                  // Q and dO
+constexpr int kDkvWaves = kBwdThreads / kWave;
+constexpr int kRunsPerWave = (kQuadRuns + kDkvWaves - 1) / kDkvWaves;
+static_assert(kQuadRows * kRowSlots % kWave == 0, "a tile is a whole number of 64-slot loads");
 
-struct QuadStage {
-  bf16x8 x[2][4];    // unit u: rows 4 rq + j, dims 8 o8 .. +7, as loaded
-  unsigned ok;       // bit 4 u + j: that row exists (else it is stored as 0)
-  float lse, delta;  // threads 0..63: MFMA row tid (lse as loaded, +inf for a missing row)
-  int pos;           // threads 64..67: position of query tid - 64 of the quad
+// One staging buffer.  The kernel keeps two as separate LDS objects and
+// alternates them in an unrolled loop, so the compiler can see that the
+// tile being read is never the one the staging loads are filling (with one
+// array indexed by the buffer number it waits for those loads first).
+struct BwdTile {
+  bf16 rm[2][kQuadRows * kBwdRow];  // [Q, dO]
+  float lse[kQuadRows];             // per MFMA row, log2 units (read 4 at a time)
+  float delta[kQuadRows];
+  int pos[4];
 };
 
-// Loads quad `qi` of the bucket (its edges' rows in the window, sorted, in LDS;
-// n edges) into registers.
-// Nothing here consumes the loaded values (the zeroing of missing rows and the
-// lse scaling happen when the quad is stored), so the loads stay in flight
-// while the previous quad is computed.
-__device__ __forceinline__ void bwd_load_quad(const BwdKernelArgs& a, QuadStage& S, const uint16_t* rows, int qi,
-                                              int n, int g, int R, int N, int M, int64_t q0) {
-  const int tid = threadIdx.x;
-  const int e = 4 * qi;
-  S.ok = 0;
+// A lane's part of a quad's staging loads (the same for every quad of the
+// chunk but for the quad's query rows): for its run u, the query of the quad
+// (0..3) whose row the lane's slot belongs to, and the byte offset of the
+// slot inside that query's row of heads.  Slots of heads past R read the
+// group's first head (finite values; those MFMA rows get probability 0).
+struct QuadDma {
+  uint32_t cst[kRunsPerWave];
+  int jq[kRunsPerWave];
+};
+
+__device__ __forceinline__ QuadDma bwd_dma_plan(int wave, int lane, int g, int R) {
+  QuadDma d;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int v = tid + kBwdThreads * u;
-    const bf16* src = (v >> 8) ? a.dout : a.q;
-    const int rq = (v & 255) >> 4, o8 = v & 15;
+  for (int u = 0; u < kRunsPerWave; ++u) {
+    const int run = wave + kDkvWaves * u;
+    const int slot = (run % kTileRuns) * kWave + lane;
+    const int row = slot / kRowSlots, c = slot % kRowSlots;
+    const int h = row & 15;
+    d.jq[u] = row >> 4;
+    d.cst[u] = (uint32_t)(((g * R + (h < R ? h : 0)) * kHeadDim + 8 * (c < 16 ? c : 0)) * 2);
+  }
+  return d;
+}
+
+// Issue the staging loads of quad qi into tile T (nothing waits for them
+// here).  The quad's four query rows are read from LDS at once, before any
+// load (a staging load writes LDS, so a row read after it would wait for
+// it).  A missing query (past the chunk's n edges) reads the first row of
+// the window: finite values whose MFMA rows get probability 0.
+__device__ __forceinline__ void bwd_issue_quad(BwdTile& T, const QuadDma& d, const uint16_t* rows, int qi, int n,
+                                               int wave, const bf16* win_q, const bf16* win_g, int win_bytes,
+                                               uint32_t row_bytes) {
+  const u32x2 rr = *reinterpret_cast<const u32x2*>(rows + 4 * qi);  // rows 4 qi .. 4 qi + 3 (16 bits each)
+  uint32_t rq[4] = {rr.x & 0xffffu, rr.x >> 16, rr.y & 0xffffu, rr.y >> 16};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // branch-free: a missing row reads the first row of the window
-      const int row = 4 * rq + j;
-      const int jq = row >> 4, h = row & 15;
-      const bool ok = e + jq < n && h < R;
-      const int64_t t = a.row_lo + (ok ? rows[e + jq] : 0);
-      S.x[u][j] = load8(src + (t * a.Hq + g * R + (ok ? h : 0)) * kHeadDim + 8 * o8);
-      S.ok |= ok ? (1u << (4 * u + j)) : 0u;
+  for (int j = 0; j < 4; ++j)
+    if (4 * qi + j >= n) rq[j] = 0;
+#pragma unroll
+  for (int u = 0; u < kRunsPerWave; ++u) {
+    const int run = wave + kDkvWaves * u;
+    if (run < kQuadRuns) {
+      const int jq = d.jq[u];
+      const uint32_t t = jq == 0 ? rq[0] : jq == 1 ? rq[1] : jq == 2 ? rq[2] : rq[3];
+      const int tsr = run / kTileRuns;
+      lds_load16(tsr ? win_g : win_q, win_bytes, (int)(t * row_bytes + d.cst[u]),
+                 &T.rm[tsr][(run % kTileRuns) * kWave * 8]);
     }
   }
+}
+
+// lse, delta of the quad's 64 MFMA rows (threads 0..63) and the positions of
+// its 4 queries (threads 64..67), loaded into registers while the previous
+// quad is computed and stored after it.
+struct QuadAux {
+  float lse, delta;
+  int pos;
+  bool ok;
+};
+
+__device__ __forceinline__ void bwd_load_aux(const BwdKernelArgs& a, QuadAux& x, const uint16_t* rows, int qi,
+                                             int n, int g, int R, int N, int M, int64_t q0) {
+  const int tid = threadIdx.x;
+  const int e = 4 * qi;
   if (tid < kQuadRows) {
     const int jq = tid >> 4, h = tid & 15;
-    const bool ok = e + jq < n && h < R;
-    const int64_t t = a.row_lo + (ok ? rows[e + jq] : 0);
-    const int64_t rh = t * a.Hq + g * R + (ok ? h : 0);
-    S.lse = a.lse[rh];
-    S.delta = a.delta[rh];
-    S.ok |= ok ? 256u : 0u;
+    x.ok = e + jq < n && h < R;
+    const int64_t t = a.row_lo + (x.ok ? rows[e + jq] : 0);
+    const int64_t rh = t * a.Hq + g * R + (x.ok ? h : 0);
+    x.lse = a.lse[rh];
+    x.delta = a.delta[rh];
   } else if (tid < kQuadRows + 4) {
     const int jq = tid - kQuadRows;
     const bool ok = e + jq < n;
     const int64_t t = a.row_lo + (ok ? rows[e + jq] : 0);
-    S.pos = ok ? (int)((int64_t)N - M + (t - q0)) : -1;
+    x.pos = ok ? (int)((int64_t)N - M + (t - q0)) : -1;
   }
 }
 
-// Row group (4 rows) of dim d in the transposed Q / dO tiles: group grp is
-// stored at grp ^ ((d / 8) % 16).  The staging threads of a wave hold dims
-// 8 apart, whose rows would otherwise fall on the same few LDS banks.
-__device__ __forceinline__ int bwd_tgrp(int grp, int d) { return grp ^ ((d >> 3) & 15); }
-
-struct BwdLds {
-  bf16 q_rm[2][kQuadRows * kBwdRow];
-  bf16 g_rm[2][kQuadRows * kBwdRow];
-  bf16 q_t[2][kHeadDim * kBwdT];
-  bf16 g_t[2][kHeadDim * kBwdT];
-  float lse[2][kQuadRows];    // per MFMA row, log2 units (read 4 at a time)
-  float delta[2][kQuadRows];
-  int pos[2][4];
-};
-
-__device__ __forceinline__ void bwd_store_quad(BwdLds& L, int buf, const QuadStage& S) {
+__device__ __forceinline__ void bwd_store_aux(BwdTile& T, const QuadAux& x) {
   const int tid = threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int v = tid + kBwdThreads * u;
-    const int rq = (v & 255) >> 4, o8 = v & 15;
-    bf16* rm = (v >> 8) ? L.g_rm[buf] : L.q_rm[buf];
-    bf16* tr = (v >> 8) ? L.g_t[buf] : L.q_t[buf];
-    bf16x8 x[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[j] = ((S.ok >> (4 * u + j)) & 1u) ? S.x[u][j] : zero8<bf16>();
-      *reinterpret_cast<bf16x8*>(rm + (4 * rq + j) * kBwdRow + 8 * o8) = x[j];
-    }
-    // transposed: dim 8 o8 + e, rows 4 rq .. 4 rq + 3 as one 8-byte run, at
-    // row group rq ^ o8 (see bwd_tgrp)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bf16x4 w = {x[0][e], x[1][e], x[2][e], x[3][e]};
-      *reinterpret_cast<bf16x4*>(tr + (8 * o8 + e) * kBwdT + 4 * bwd_tgrp(rq, 8 * o8 + e)) = w;
-    }
-  }
   if (tid < kQuadRows) {
-    // an empty MFMA row gets lse = +inf, so its probabilities are exactly 0
-    const bool ok = (S.ok >> 8) & 1u;
-    L.lse[buf][tid] = ok ? S.lse * kLog2e : __builtin_inff();
-    L.delta[buf][tid] = ok ? S.delta : 0.f;
+    // a missing MFMA row gets lse = +inf, so its probabilities are exactly 0
+    T.lse[tid] = x.ok ? x.lse * kLog2e : __builtin_inff();
+    T.delta[tid] = x.ok ? x.delta : 0.f;
   } else if (tid < kQuadRows + 4) {
-    L.pos[buf][tid - kQuadRows] = S.pos;
+    T.pos[tid - kQuadRows] = x.pos;
   }
 }
 
 // One staged quad against this wave's 32 keys: for each half rh (32 MFMA
 // rows = 2 queries x 16 heads), S = Q K^T and dP = dO V^T (rows x keys), P
-// and dS; then dV += P^T dO and dK += dS^T Q over the 64 rows.
-__device__ __forceinline__ void bwd_quad_compute(const BwdLds& L, int buf, const bf16x8 (&kf)[kHeadDim / 16],
+// and dS; then dV += P^T dO and dK += dS^T Q over the 64 rows.  One wave per
+// SIMD, so the order hides the softmax arithmetic under independent MFMAs:
+// half 0's P / dS are computed while half 1's S / dP MFMAs run, and half 1's
+// while the dV / dK steps over half 0's rows run.  Each dV / dK accumulator
+// still sums its k-steps in order 0..3.
+__device__ __forceinline__ void bwd_softmax_half(const BwdTile& T, int rh, const f32x16& s, const f32x16& dp,
+                                                 int key_seq, int a32, float scale_log2, bf16x8 (&pa)[4],
+                                                 bf16x8 (&dsa)[4]) {
+  // C layout: this lane's key, rows 32 rh + 8 (r / 4) + 4 a32 + r % 4; the
+  // four rows of each r / 4 are consecutive, so their lse and delta are one
+  // 16-byte read each; rows 16 j .. 16 j + 15 belong to query j of the quad
+  const bool live0 = key_seq <= T.pos[2 * rh], live1 = key_seq <= T.pos[2 * rh + 1];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const f32x4 ls = *reinterpret_cast<const f32x4*>(&T.lse[32 * rh + 8 * q4 + 4 * a32]);
+    const f32x4 dl = *reinterpret_cast<const f32x4*>(&T.delta[32 * rh + 8 * q4 + 4 * a32]);
+    const bool live = q4 < 2 ? live0 : live1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * q4 + i;
+      const float p = live ? __builtin_amdgcn_exp2f(s[r] * scale_log2 - ls[i]) : 0.f;
+      const float ds = p * (dp[r] - dl[i]);
+      pa[2 * rh + (r >> 3)][r & 7] = bf16(p);
+      dsa[2 * rh + (r >> 3)][r & 7] = bf16(ds);
+    }
+  }
+}
+
+__device__ __forceinline__ void bwd_quad_compute(const BwdTile& T, const bf16x8 (&kf)[kHeadDim / 16],
                                                  const bf16x8 (&vf)[kHeadDim / 16], f32x16 (&dk_acc)[kHeadDim / 32],
                                                  f32x16 (&dv_acc)[kHeadDim / 32], int key_seq, int col, int a32,
-                                                 float scale_log2) {
+                                                 int tr_off, float scale_log2) {
+  const bf16* qt = T.rm[0];
+  const bf16* gt = T.rm[1];
   bf16x8 pa[4], dsa[4];  // k-step 2 rh + s2 of the second products
+  f32x16 s[2], dp[2];
+  // S and dP of both halves; the next k-step's operands are read from LDS
+  // while the current MFMAs run
 #pragma unroll
   for (int rh = 0; rh < 2; ++rh) {
-    f32x16 s = {}, dp = {};
+    s[rh] = f32x16{};
+    dp[rh] = f32x16{};
     const int arow = (32 * rh + col) * kBwdRow + 8 * a32;
-    // one wave per SIMD: the next k-step's operands are read from LDS while
-    // the current MFMAs run
-    bf16x8 qa = *reinterpret_cast<const bf16x8*>(&L.q_rm[buf][arow]);
-    bf16x8 ga = *reinterpret_cast<const bf16x8*>(&L.g_rm[buf][arow]);
+    bf16x8 qa = *reinterpret_cast<const bf16x8*>(&qt[arow]);
+    bf16x8 ga = *reinterpret_cast<const bf16x8*>(&gt[arow]);
 #pragma unroll
     for (int ks = 0; ks < kHeadDim / 16; ++ks) {
       bf16x8 qn = qa, gn = ga;
       if (ks + 1 < kHeadDim / 16) {
-        qn = *reinterpret_cast<const bf16x8*>(&L.q_rm[buf][arow + 16 * (ks + 1)]);
-        gn = *reinterpret_cast<const bf16x8*>(&L.g_rm[buf][arow + 16 * (ks + 1)]);
+        qn = *reinterpret_cast<const bf16x8*>(&qt[arow + 16 * (ks + 1)]);
+        gn = *reinterpret_cast<const bf16x8*>(&gt[arow + 16 * (ks + 1)]);
       }
-      s = mma32(qa, kf[ks], s);
-      dp = mma32(ga, vf[ks], dp);
+      s[rh] = mma32(qa, kf[ks], s[rh]);
+      dp[rh] = mma32(ga, vf[ks], dp[rh]);
       qa = qn;
       ga = gn;
     }
-    // C layout: this lane's key, rows 32 rh + 8 (r / 4) + 4 a32 + r % 4; the
-    // four rows of each r / 4 are consecutive, so their lse and delta are one
-    // 16-byte read each; rows 16 j .. 16 j + 15 belong to query j of the quad
-    const bool live0 = key_seq <= L.pos[buf][2 * rh], live1 = key_seq <= L.pos[buf][2 * rh + 1];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 ls = *reinterpret_cast<const f32x4*>(&L.lse[buf][32 * rh + 8 * q4 + 4 * a32]);
-      const f32x4 dl = *reinterpret_cast<const f32x4*>(&L.delta[buf][32 * rh + 8 * q4 + 4 * a32]);
-      const bool live = q4 < 2 ? live0 : live1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * q4 + i;
-        const float p = live ? __builtin_amdgcn_exp2f(s[r] * scale_log2 - ls[i]) : 0.f;
-        const float ds = p * (dp[r] - dl[i]);
-        pa[2 * rh + (r >> 3)][r & 7] = bf16(p);
-        dsa[2 * rh + (r >> 3)][r & 7] = bf16(ds);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep each half's LDS reads next to its MFMAs
+    if (rh == 1) bwd_softmax_half(T, 0, s[0], dp[0], key_seq, a32, scale_log2, pa, dsa);
   }
   // dV[key][d] += sum_row P[row][key] dO[row][d]; dK likewise with dS and Q.
   // k-step s4 covers rows 16 s4 .. +15; slot i of lane half a32 is row
   // 16 s4 + 4 a32 + i (i < 4) or 16 s4 + 8 + 4 a32 + i - 4, matching the
-  // registers of pa / dsa above.
-  // rows 16 s4 + 4 a32 .. +3 and 16 s4 + 8 + 4 a32 .. +3 of dim d: row groups
-  // 4 s4 + a32 and 4 s4 + 2 + a32; operands of step i + 1 (i = 4 dt + s4) are
-  // read while step i's MFMAs run
-  auto opnd = [&](const bf16* t, int i) {
-    const int d = 32 * (i >> 2) + col, s4 = i & 3;
-    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(t + d * kBwdT + 4 * bwd_tgrp(4 * s4 + a32, d));
-    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(t + d * kBwdT + 4 * bwd_tgrp(4 * s4 + 2 + a32, d));
+  // registers of pa / dsa above: two transposed reads per operand, rows
+  // 16 s4 + 4 a32 .. +3 and 8 rows further, of dims 32 dt + col (tr_off holds
+  // the lane's row 4 a32 + e and column 16 (lane / 16 % 2) + 4 q of a step).
+  // Steps run half 0's rows (s4 = 0, 1) for every dt, then half 1's; the
+  // operands of the next step are read while the current step's MFMAs run.
+  auto opnd = [&](const bf16* t, int s4, int dt) {
+    const bf16* p = t + tr_off + 16 * s4 * kBwdRow + 32 * dt;
+    const bf16x4 lo = lds_read_tr4(p), hi = lds_read_tr4(p + 8 * kBwdRow);
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
-  bf16x8 gb = opnd(L.g_t[buf], 0), qb = opnd(L.q_t[buf], 0);
+  constexpr int kSteps = 4 * (kHeadDim / 32);
+  auto step_s4 = [](int i) { return 2 * (i / (2 * (kHeadDim / 32))) + (i & 1); };
+  auto step_dt = [](int i) { return (i >> 1) % (kHeadDim / 32); };
+  bf16x8 gb = opnd(gt, step_s4(0), step_dt(0)), qb = opnd(qt, step_s4(0), step_dt(0));
 #pragma unroll
-  for (int i = 0; i < 4 * (kHeadDim / 32); ++i) {
+  for (int i = 0; i < kSteps; ++i) {
+    const int s4 = step_s4(i), dt = step_dt(i);
     bf16x8 gn = gb, qn = qb;
-    if (i + 1 < 4 * (kHeadDim / 32)) {
-      gn = opnd(L.g_t[buf], i + 1);
-      qn = opnd(L.q_t[buf], i + 1);
+    if (i + 1 < kSteps) {
+      gn = opnd(gt, step_s4(i + 1), step_dt(i + 1));
+      qn = opnd(qt, step_s4(i + 1), step_dt(i + 1));
     }
-    dv_acc[i >> 2] = mma32(pa[i & 3], gb, dv_acc[i >> 2]);
-    dk_acc[i >> 2] = mma32(dsa[i & 3], qb, dk_acc[i >> 2]);
+    dv_acc[dt] = mma32(pa[s4], gb, dv_acc[dt]);
+    dk_acc[dt] = mma32(dsa[s4], qb, dk_acc[dt]);
     gb = gn;
     qb = qn;
+    if (i == 0) bwd_softmax_half(T, 1, s[1], dp[1], key_seq, a32, scale_log2, pa, dsa);
   }
 }
 
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
-  __shared__ __attribute__((aligned(16))) BwdLds L;
-  __shared__ uint16_t rows[kDkvChunk];
+  __shared__ __attribute__((aligned(16))) BwdTile T0;
+  __shared__ __attribute__((aligned(16))) BwdTile T1;
+  __shared__ __attribute__((aligned(16))) uint16_t rows[kDkvChunk];
   const int nbk = a.batch * a.G * a.nb_max;
   const int w = blockIdx.x;
   if (w >= a.dkv_chunk[nbk]) return;
@@ -377,10 +409,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
   for (int i = tid; i < n; i += kBwdThreads) rows[i] = (uint16_t)(a.edges[e_lo + i] >> 4);
   __syncthreads();
 
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = lane_id();
   const int col = lane & 31;  // MFMA row of A / column of B and C
   const int a32 = lane >> 5;
+  // staging: buffer resources over the window's rows of Q and dO (a window
+  // holds at most kBwdWindow rows of at most 256 heads: offsets fit 32 bits)
+  const int64_t win_rows = min((int64_t)kBwdWindow, (int64_t)a.cu_q[a.batch] - a.row_lo);
+  const uint32_t row_bytes = (uint32_t)a.Hq * kHeadDim * 2;
+  const int win_bytes = (int)(win_rows * row_bytes);
+  const bf16* win_q = a.q + a.row_lo * a.Hq * kHeadDim;
+  const bf16* win_g = a.dout + a.row_lo * a.Hq * kHeadDim;
+  const QuadDma dma = bwd_dma_plan(wave, lane, g, R);
+  // transposed reads: this lane's row 4 a32 + e and column 16 (lane / 16 % 2)
+  // + 4 q inside a 16-row k-step (lane = 16 (2 a32 + lane / 16 % 2) + 4 e + q)
+  const int tr_off = (4 * a32 + ((lane & 15) >> 2)) * kBwdRow + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   // this wave's 32 keys: K and V rows as the B operands of S = Q K^T and
   // dP = dO V^T (column = key, 8 dims per k-step half); rows past the
   // sequence end clamp to its last row and are masked (key > every p)
@@ -399,26 +442,51 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
     dv_acc[dt] = f32x16{};
   }
 
-  // Quads run through two LDS buffers: quad qi + 1 is loaded into registers
-  // while quad qi is computed, then stored to the other buffer.
+  // Quads alternate between the two tiles: the staging loads of quad qi + 1
+  // are issued before quad qi is computed and waited for after it.
   const int nquads = (n + 3) / 4;
-  QuadStage S;
-  bwd_load_quad(a, S, rows, 0, n, g, R, N, M, q0);
-  bwd_store_quad(L, 0, S);
+  QuadAux x;
+  bwd_issue_quad(T0, dma, rows, 0, n, wave, win_q, win_g, win_bytes, row_bytes);
+  bwd_load_aux(a, x, rows, 0, n, g, R, N, M, q0);
+  bwd_store_aux(T0, x);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int qi = 0; qi < nquads; ++qi) {
-    const int buf = qi & 1;
+  auto step = [&](BwdTile& cur, BwdTile& nxt, int qi) {
     const bool more = qi + 1 < nquads;
-    if (more) bwd_load_quad(a, S, rows, qi + 1, n, g, R, N, M, q0);
-    bwd_quad_compute(L, buf, kf, vf, dk_acc, dv_acc, key_seq, col, a32, a.scale_log2);
-    if (more) bwd_store_quad(L, buf ^ 1, S);
+    if (more) {
+      bwd_issue_quad(nxt, dma, rows, qi + 1, n, wave, win_q, win_g, win_bytes, row_bytes);
+      bwd_load_aux(a, x, rows, qi + 1, n, g, R, N, M, q0);
+    }
+    bwd_quad_compute(cur, kf, vf, dk_acc, dv_acc, key_seq, col, a32, tr_off, a.scale_log2);
+    if (more) bwd_store_aux(nxt, x);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // quad qi + 1 is in LDS
     __syncthreads();
+  };
+  for (int qi = 0; qi < nquads; qi += 2) {
+    step(T0, T1, qi);
+    if (qi + 1 < nquads) step(T1, T0, qi + 1);
   }
 
   // ---- lane column d = 32 dt + col, rows = keys 8 (r / 4) + 4 a32 + r % 4 of
   // the wave's 32.  A bucket's only chunk adds this window's contribution to
   // dK / dV; the chunks of a longer bucket write partials for bwd_dkdv_reduce.
   if (nchunks == 1) {
+    // the first window writes its blocks' rows outright; later ones add, all
+    // loads issued (branch-free: rows past the sequence end read its last
+    // row) before the first store
+    const bool add = a.row_lo != 0;
+    float vk[kHeadDim / 32][16], vv[kHeadDim / 32][16];
+    if (add) {
+#pragma unroll
+      for (int dt = 0; dt < kHeadDim / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = c * kBlock + 32 * wave + 8 * (r >> 2) + 4 * a32 + (r & 3);
+          const int64_t off = (kb0 + (kk < N ? kk : N - 1)) * rs + g * kHeadDim + 32 * dt + col;
+          vk[dt][r] = a.dk[off];
+          vv[dt][r] = a.dv[off];
+        }
+    }
 #pragma unroll
     for (int dt = 0; dt < kHeadDim / 32; ++dt)
 #pragma unroll
@@ -426,13 +494,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
         const int kk = c * kBlock + 32 * wave + 8 * (r >> 2) + 4 * a32 + (r & 3);
         if (kk >= N) continue;
         const int64_t off = (kb0 + kk) * rs + g * kHeadDim + 32 * dt + col;
-        if (a.row_lo == 0) {  // the first window writes its blocks' rows outright
-          a.dk[off] = dk_acc[dt][r] * a.scale;
-          a.dv[off] = dv_acc[dt][r];
-        } else {
-          a.dk[off] += dk_acc[dt][r] * a.scale;
-          a.dv[off] += dv_acc[dt][r];
-        }
+        const float xk = dk_acc[dt][r] * a.scale, xv = dv_acc[dt][r];
+        a.dk[off] = add ? vk[dt][r] + xk : xk;
+        a.dv[off] = add ? vv[dt][r] + xv : xv;
       }
   } else {
     float* pk = a.part_dkv + (int64_t)(a.dkv_part[bucket] + chunk) * (2 * kBlock * kHeadDim);
