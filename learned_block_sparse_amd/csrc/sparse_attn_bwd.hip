@@ -198,27 +198,21 @@ struct BwdTile {
 };
 
 // A lane's part of a quad's staging loads (the same for every quad of the
-// chunk but for the quad's query rows): for its run u, the query of the quad
-// (0..3) whose row the lane's slot belongs to, and the byte offset of the
-// slot inside that query's row of heads.  Slots of heads past R read the
-// group's first head (finite values; those MFMA rows get probability 0).
-struct QuadDma {
-  uint32_t cst[kRunsPerWave];
-  int jq[kRunsPerWave];
-};
-
-__device__ __forceinline__ QuadDma bwd_dma_plan(int wave, int lane, int g, int R) {
-  QuadDma d;
+// chunk but for the quad's query rows), kept in LDS rather than registers:
+// for its run u, the query of the quad (0..3, bits 30..31) whose row the
+// lane's slot belongs to, and the byte offset of the slot inside that
+// query's row of heads (bits 0..29).  Slots of heads past R read the group's
+// first head (finite values; those MFMA rows get probability 0).
+__device__ __forceinline__ void bwd_dma_plan(uint32_t* plan, int wave, int lane, int g, int R) {
 #pragma unroll
   for (int u = 0; u < kRunsPerWave; ++u) {
     const int run = wave + kDkvWaves * u;
     const int slot = (run % kTileRuns) * kWave + lane;
     const int row = slot / kRowSlots, c = slot % kRowSlots;
     const int h = row & 15;
-    d.jq[u] = row >> 4;
-    d.cst[u] = (uint32_t)(((g * R + (h < R ? h : 0)) * kHeadDim + 8 * (c < 16 ? c : 0)) * 2);
+    const uint32_t cst = (uint32_t)(((g * R + (h < R ? h : 0)) * kHeadDim + 8 * (c < 16 ? c : 0)) * 2);
+    plan[u * kWave + lane] = cst | ((uint32_t)(row >> 4) << 30);
   }
-  return d;
 }
 
 // Issue the staging loads of quad qi into tile T (nothing waits for them
@@ -226,10 +220,13 @@ __device__ __forceinline__ QuadDma bwd_dma_plan(int wave, int lane, int g, int R
 // load (a staging load writes LDS, so a row read after it would wait for
 // it).  A missing query (past the chunk's n edges) reads the first row of
 // the window: finite values whose MFMA rows get probability 0.
-__device__ __forceinline__ void bwd_issue_quad(BwdTile& T, const QuadDma& d, const uint16_t* rows, int qi, int n,
-                                               int wave, const bf16* win_q, const bf16* win_g, int win_bytes,
-                                               uint32_t row_bytes) {
+__device__ __forceinline__ void bwd_issue_quad(BwdTile& T, const uint32_t* plan, const uint16_t* rows, int qi, int n,
+                                               int wave, int lane, const bf16* win_q, const bf16* win_g,
+                                               int win_bytes, uint32_t row_bytes) {
   const u32x2 rr = *reinterpret_cast<const u32x2*>(rows + 4 * qi);  // rows 4 qi .. 4 qi + 3 (16 bits each)
+  uint32_t pk[kRunsPerWave];
+#pragma unroll
+  for (int u = 0; u < kRunsPerWave; ++u) pk[u] = plan[u * kWave + lane];
   uint32_t rq[4] = {rr.x & 0xffffu, rr.x >> 16, rr.y & 0xffffu, rr.y >> 16};
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -238,10 +235,10 @@ __device__ __forceinline__ void bwd_issue_quad(BwdTile& T, const QuadDma& d, con
   for (int u = 0; u < kRunsPerWave; ++u) {
     const int run = wave + kDkvWaves * u;
     if (run < kQuadRuns) {
-      const int jq = d.jq[u];
+      const uint32_t jq = pk[u] >> 30;
       const uint32_t t = jq == 0 ? rq[0] : jq == 1 ? rq[1] : jq == 2 ? rq[2] : rq[3];
       const int tsr = run / kTileRuns;
-      lds_load16(tsr ? win_g : win_q, win_bytes, (int)(t * row_bytes + d.cst[u]),
+      lds_load16(tsr ? win_g : win_q, win_bytes, (int)(t * row_bytes + (pk[u] & 0x3fffffffu)),
                  &T.rm[tsr][(run % kTileRuns) * kWave * 8]);
     }
   }
@@ -324,28 +321,27 @@ __device__ __forceinline__ void bwd_quad_compute(const BwdTile& T, const bf16x8 
   const bf16* gt = T.rm[1];
   bf16x8 pa[4], dsa[4];  // k-step 2 rh + s2 of the second products
   f32x16 s[2], dp[2];
-  // S and dP of both halves; the next k-step's operands are read from LDS
-  // while the current MFMAs run
+  // S and dP of both halves as one run of 16 k-steps, operands read from LDS
+  // two steps ahead of their MFMAs
+  constexpr int kKs = kHeadDim / 16;
+  const int arow0 = col * kBwdRow + 8 * a32;
+  auto aofs = [&](int st) { return arow0 + (st / kKs) * 32 * kBwdRow + 16 * (st % kKs); };
+  bf16x8 qa[3], ga[3];
+  qa[0] = *reinterpret_cast<const bf16x8*>(&qt[aofs(0)]);
+  ga[0] = *reinterpret_cast<const bf16x8*>(&gt[aofs(0)]);
+  qa[1] = *reinterpret_cast<const bf16x8*>(&qt[aofs(1)]);
+  ga[1] = *reinterpret_cast<const bf16x8*>(&gt[aofs(1)]);
+  s[0] = s[1] = dp[0] = dp[1] = f32x16{};
 #pragma unroll
-  for (int rh = 0; rh < 2; ++rh) {
-    s[rh] = f32x16{};
-    dp[rh] = f32x16{};
-    const int arow = (32 * rh + col) * kBwdRow + 8 * a32;
-    bf16x8 qa = *reinterpret_cast<const bf16x8*>(&qt[arow]);
-    bf16x8 ga = *reinterpret_cast<const bf16x8*>(&gt[arow]);
-#pragma unroll
-    for (int ks = 0; ks < kHeadDim / 16; ++ks) {
-      bf16x8 qn = qa, gn = ga;
-      if (ks + 1 < kHeadDim / 16) {
-        qn = *reinterpret_cast<const bf16x8*>(&qt[arow + 16 * (ks + 1)]);
-        gn = *reinterpret_cast<const bf16x8*>(&gt[arow + 16 * (ks + 1)]);
-      }
-      s[rh] = mma32(qa, kf[ks], s[rh]);
-      dp[rh] = mma32(ga, vf[ks], dp[rh]);
-      qa = qn;
-      ga = gn;
+  for (int st = 0; st < 2 * kKs; ++st) {
+    const int rh = st / kKs, ks = st % kKs;
+    if (st + 2 < 2 * kKs) {
+      qa[(st + 2) % 3] = *reinterpret_cast<const bf16x8*>(&qt[aofs(st + 2)]);
+      ga[(st + 2) % 3] = *reinterpret_cast<const bf16x8*>(&gt[aofs(st + 2)]);
     }
-    if (rh == 1) bwd_softmax_half(T, 0, s[0], dp[0], key_seq, a32, scale_log2, pa, dsa);
+    s[rh] = mma32(qa[st % 3], kf[ks], s[rh]);
+    dp[rh] = mma32(ga[st % 3], vf[ks], dp[rh]);
+    if (st == kKs) bwd_softmax_half(T, 0, s[0], dp[0], key_seq, a32, scale_log2, pa, dsa);
   }
   // dV[key][d] += sum_row P[row][key] dO[row][d]; dK likewise with dS and Q.
   // k-step s4 covers rows 16 s4 .. +15; slot i of lane half a32 is row
@@ -384,6 +380,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
   __shared__ __attribute__((aligned(16))) BwdTile T0;
   __shared__ __attribute__((aligned(16))) BwdTile T1;
   __shared__ __attribute__((aligned(16))) uint16_t rows[kDkvChunk];
+  __shared__ uint32_t plan[kDkvWaves][kRunsPerWave * kWave];
   const int nbk = a.batch * a.G * a.nb_max;
   const int w = blockIdx.x;
   if (w >= a.dkv_chunk[nbk]) return;
@@ -420,7 +417,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
   const int win_bytes = (int)(win_rows * row_bytes);
   const bf16* win_q = a.q + a.row_lo * a.Hq * kHeadDim;
   const bf16* win_g = a.dout + a.row_lo * a.Hq * kHeadDim;
-  const QuadDma dma = bwd_dma_plan(wave, lane, g, R);
+  bwd_dma_plan(plan[wave], wave, lane, g, R);
   // transposed reads: this lane's row 4 a32 + e and column 16 (lane / 16 % 2)
   // + 4 q inside a 16-row k-step (lane = 16 (2 a32 + lane / 16 % 2) + 4 e + q)
   const int tr_off = (4 * a32 + ((lane & 15) >> 2)) * kBwdRow + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -446,7 +443,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
   // are issued before quad qi is computed and waited for after it.
   const int nquads = (n + 3) / 4;
   QuadAux x;
-  bwd_issue_quad(T0, dma, rows, 0, n, wave, win_q, win_g, win_bytes, row_bytes);
+  __syncthreads();  // the plan is written
+  bwd_issue_quad(T0, plan[wave], rows, 0, n, wave, lane, win_q, win_g, win_bytes, row_bytes);
   bwd_load_aux(a, x, rows, 0, n, g, R, N, M, q0);
   bwd_store_aux(T0, x);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -454,7 +452,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
   auto step = [&](BwdTile& cur, BwdTile& nxt, int qi) {
     const bool more = qi + 1 < nquads;
     if (more) {
-      bwd_issue_quad(nxt, dma, rows, qi + 1, n, wave, win_q, win_g, win_bytes, row_bytes);
+      bwd_issue_quad(nxt, plan[wave], rows, qi + 1, n, wave, lane, win_q, win_g, win_bytes, row_bytes);
       bwd_load_aux(a, x, rows, qi + 1, n, g, R, N, M, q0);
     }
     bwd_quad_compute(cur, kf, vf, dk_acc, dv_acc, key_seq, col, a32, tr_off, a.scale_log2);
