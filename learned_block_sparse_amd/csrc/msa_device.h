@@ -151,6 +151,18 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
 #endif
 }
 
+// Workgroup barrier that orders LDS accesses only: the wave's own LDS
+// writes are complete before it (lgkmcnt) and later LDS reads see the other
+// waves' writes, while global loads and direct-to-LDS loads stay in flight
+// across it.  A compiler fence would also wait for those: __syncthreads
+// waits for every outstanding global access, and even a fence restricted to
+// LDS waits for direct-to-LDS loads, which write LDS.  Data staged by such
+// loads needs its own s_waitcnt vmcnt before the barrier that publishes it.
+// The memory clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }

@@ -182,9 +182,23 @@ constexpr int kQuadRows = 64;
 constexpr int kRowSlots = kBwdRow * 2 / 16;               // 17 slots of 16 bytes per row
 constexpr int kTileRuns = kQuadRows * kRowSlots / kWave;  // 17 loads of 64 slots per tile
 constexpr int kQuadRuns = 2 * kTileRuns;                  // Q and dO
-constexpr int kDkvWaves = kBwdThreads / kWave;
+constexpr int kDkvThreads = 512;  // bwd_dkdv: two waves per key tile of 32 keys, two per SIMD
+constexpr int kDkvWaves = kDkvThreads / kWave;
 constexpr int kRunsPerWave = (kQuadRuns + kDkvWaves - 1) / kDkvWaves;
 static_assert(kQuadRows * kRowSlots % kWave == 0, "a tile is a whole number of 64-slot loads");
+
+// Tile row of MFMA row m = 4 k + j: 8 (k / 2) + 2 j + k % 2.  The four MFMA
+// rows a transposed read gathers (4 k .. 4 k + 3) then lie two tile rows
+// apart, 8 banks, so its 16 lanes' 8-byte pieces fall on distinct banks;
+// any 8 consecutive MFMA rows still fall on distinct banks for the 16-byte
+// row-major reads (a 272-byte row shifts the banks by 4).  Without the
+// permutation the transposed reads conflicted two-way (44% of LDS cycles).
+__device__ __forceinline__ int bwd_tile_row(int m) {
+  return (m & ~7) | ((m & 3) << 1) | ((m >> 2) & 1);
+}
+__device__ __forceinline__ int bwd_mfma_row(int p) {  // inverse of bwd_tile_row
+  return (p & ~7) | ((p & 1) << 2) | ((p >> 1) & 3);
+}
 
 // One staging buffer.  The kernel keeps two as separate LDS objects and
 // alternates them in an unrolled loop, so the compiler can see that the
@@ -208,7 +222,7 @@ __device__ __forceinline__ void bwd_dma_plan(uint32_t* plan, int wave, int lane,
   for (int u = 0; u < kRunsPerWave; ++u) {
     const int run = wave + kDkvWaves * u;
     const int slot = (run % kTileRuns) * kWave + lane;
-    const int row = slot / kRowSlots, c = slot % kRowSlots;
+    const int row = bwd_mfma_row(slot / kRowSlots), c = slot % kRowSlots;
     const int h = row & 15;
     const uint32_t cst = (uint32_t)(((g * R + (h < R ? h : 0)) * kHeadDim + 8 * (c < 16 ? c : 0)) * 2);
     plan[u * kWave + lane] = cst | ((uint32_t)(row >> 4) << 30);
@@ -283,102 +297,68 @@ __device__ __forceinline__ void bwd_store_aux(BwdTile& T, const QuadAux& x) {
   }
 }
 
-// One staged quad against this wave's 32 keys: for each half rh (32 MFMA
-// rows = 2 queries x 16 heads), S = Q K^T and dP = dO V^T (rows x keys), P
-// and dS; then dV += P^T dO and dK += dS^T Q over the 64 rows.  One wave per
-// SIMD, so the order hides the softmax arithmetic under independent MFMAs:
-// half 0's P / dS are computed while half 1's S / dP MFMAs run, and half 1's
-// while the dV / dK steps over half 0's rows run.  Each dV / dK accumulator
-// still sums its k-steps in order 0..3.
-__device__ __forceinline__ void bwd_softmax_half(const BwdTile& T, int rh, const f32x16& s, const f32x16& dp,
-                                                 int key_seq, int a32, float scale_log2, bf16x8 (&pa)[4],
-                                                 bf16x8 (&dsa)[4]) {
-  // C layout: this lane's key, rows 32 rh + 8 (r / 4) + 4 a32 + r % 4; the
-  // four rows of each r / 4 are consecutive, so their lse and delta are one
-  // 16-byte read each; rows 16 j .. 16 j + 15 belong to query j of the quad
-  const bool live0 = key_seq <= T.pos[2 * rh], live1 = key_seq <= T.pos[2 * rh + 1];
+// One staged quad against a key tile of 32 keys, by the tile's two waves.
+// Wave A (keeps the keys' K rows as MFMA operands) computes S = Q K^T over
+// the quad's 64 rows, P = exp(S - lse) (0 where the key is past the query),
+// hands P to wave B through LDS (fp32, each lane its own 16 values per half)
+// and accumulates dV += P^T dO; wave B (keeps the V rows) computes
+// dP = dO V^T, dS = P (dP - delta) and accumulates dK += dS^T Q.  The two
+// share a SIMD, so one's arithmetic runs while the other waits.  S, dP, P
+// and dS are the same numbers in the same order as a single wave computing
+// all four products.
+struct BwdXch {
+  float p[kBlock / 32][2 * 16][kWave];  // [key tile][half * 16 + C register][lane]
+};
+
+// S (A) or dP (B) of the quad's 64 rows: two halves of 32 MFMA rows, 8 k-steps
+// each, as one run of 16 steps with operands read from LDS two steps ahead.
+__device__ __forceinline__ void bwd_first_product(const bf16* tile, const bf16x8 (&kv)[kHeadDim / 16], int col,
+                                                  int a32, f32x16 (&acc)[2]) {
+  constexpr int kKs = kHeadDim / 16;
+  const int arow0 = bwd_tile_row(col) * kBwdRow + 8 * a32;  // MFMA row col (+ 32 for the second half)
+  auto aofs = [&](int st) { return arow0 + (st / kKs) * 32 * kBwdRow + 16 * (st % kKs); };
+  bf16x8 op[3];
+  op[0] = *reinterpret_cast<const bf16x8*>(&tile[aofs(0)]);
+  op[1] = *reinterpret_cast<const bf16x8*>(&tile[aofs(1)]);
+  acc[0] = acc[1] = f32x16{};
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    const f32x4 ls = *reinterpret_cast<const f32x4*>(&T.lse[32 * rh + 8 * q4 + 4 * a32]);
-    const f32x4 dl = *reinterpret_cast<const f32x4*>(&T.delta[32 * rh + 8 * q4 + 4 * a32]);
-    const bool live = q4 < 2 ? live0 : live1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * q4 + i;
-      const float p = live ? __builtin_amdgcn_exp2f(s[r] * scale_log2 - ls[i]) : 0.f;
-      const float ds = p * (dp[r] - dl[i]);
-      pa[2 * rh + (r >> 3)][r & 7] = bf16(p);
-      dsa[2 * rh + (r >> 3)][r & 7] = bf16(ds);
-    }
+  for (int st = 0; st < 2 * kKs; ++st) {
+    if (st + 2 < 2 * kKs) op[(st + 2) % 3] = *reinterpret_cast<const bf16x8*>(&tile[aofs(st + 2)]);
+    acc[st / kKs] = mma32(op[st % 3], kv[st % kKs], acc[st / kKs]);
   }
 }
 
-__device__ __forceinline__ void bwd_quad_compute(const BwdTile& T, const bf16x8 (&kf)[kHeadDim / 16],
-                                                 const bf16x8 (&vf)[kHeadDim / 16], f32x16 (&dk_acc)[kHeadDim / 32],
-                                                 f32x16 (&dv_acc)[kHeadDim / 32], int key_seq, int col, int a32,
-                                                 int tr_off, float scale_log2) {
-  const bf16* qt = T.rm[0];
-  const bf16* gt = T.rm[1];
-  bf16x8 pa[4], dsa[4];  // k-step 2 rh + s2 of the second products
-  f32x16 s[2], dp[2];
-  // S and dP of both halves as one run of 16 k-steps, operands read from LDS
-  // two steps ahead of their MFMAs
-  constexpr int kKs = kHeadDim / 16;
-  const int arow0 = col * kBwdRow + 8 * a32;
-  auto aofs = [&](int st) { return arow0 + (st / kKs) * 32 * kBwdRow + 16 * (st % kKs); };
-  bf16x8 qa[3], ga[3];
-  qa[0] = *reinterpret_cast<const bf16x8*>(&qt[aofs(0)]);
-  ga[0] = *reinterpret_cast<const bf16x8*>(&gt[aofs(0)]);
-  qa[1] = *reinterpret_cast<const bf16x8*>(&qt[aofs(1)]);
-  ga[1] = *reinterpret_cast<const bf16x8*>(&gt[aofs(1)]);
-  s[0] = s[1] = dp[0] = dp[1] = f32x16{};
-#pragma unroll
-  for (int st = 0; st < 2 * kKs; ++st) {
-    const int rh = st / kKs, ks = st % kKs;
-    if (st + 2 < 2 * kKs) {
-      qa[(st + 2) % 3] = *reinterpret_cast<const bf16x8*>(&qt[aofs(st + 2)]);
-      ga[(st + 2) % 3] = *reinterpret_cast<const bf16x8*>(&gt[aofs(st + 2)]);
-    }
-    s[rh] = mma32(qa[st % 3], kf[ks], s[rh]);
-    dp[rh] = mma32(ga[st % 3], vf[ks], dp[rh]);
-    if (st == kKs) bwd_softmax_half(T, 0, s[0], dp[0], key_seq, a32, scale_log2, pa, dsa);
-  }
-  // dV[key][d] += sum_row P[row][key] dO[row][d]; dK likewise with dS and Q.
-  // k-step s4 covers rows 16 s4 .. +15; slot i of lane half a32 is row
-  // 16 s4 + 4 a32 + i (i < 4) or 16 s4 + 8 + 4 a32 + i - 4, matching the
-  // registers of pa / dsa above: two transposed reads per operand, rows
-  // 16 s4 + 4 a32 .. +3 and 8 rows further, of dims 32 dt + col (tr_off holds
-  // the lane's row 4 a32 + e and column 16 (lane / 16 % 2) + 4 q of a step).
-  // Steps run half 0's rows (s4 = 0, 1) for every dt, then half 1's; the
-  // operands of the next step are read while the current step's MFMAs run.
-  auto opnd = [&](const bf16* t, int s4, int dt) {
-    const bf16* p = t + tr_off + 16 * s4 * kBwdRow + 32 * dt;
+// acc[dt] += X^T Y over the quad's 64 rows: A operands x (P or dS, k-step s4
+// = rows 16 s4 .. +15 in the slots of the C layout: slot i of lane half a32
+// is row 16 s4 + 4 a32 + i (i < 4) or 16 s4 + 8 + 4 a32 + i - 4), B operands
+// read transposed from the row-major tile (dO or Q): two reads per step,
+// MFMA rows 16 s4 + 4 a32 .. +3 and 8 rows further, dims 32 dt + col; in
+// tile rows that is 16 s4 (+ 8) + 2 e + a32 for the lane's e (tr_off holds
+// the lane's tile row 2 e + a32 and column 16 (lane / 16 % 2) + 4 q).
+// Each accumulator sums its k-steps in order 0..3; the next step's operands
+// are read while the current MFMA runs.
+__device__ __forceinline__ void bwd_second_product(const bf16* tile, const bf16x8 (&x)[4], int tr_off,
+                                                   f32x16 (&acc)[kHeadDim / 32]) {
+  auto opnd = [&](int st) {
+    const bf16* p = tile + tr_off + 16 * (st & 3) * kBwdRow + 32 * (st >> 2);
     const bf16x4 lo = lds_read_tr4(p), hi = lds_read_tr4(p + 8 * kBwdRow);
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
   constexpr int kSteps = 4 * (kHeadDim / 32);
-  auto step_s4 = [](int i) { return 2 * (i / (2 * (kHeadDim / 32))) + (i & 1); };
-  auto step_dt = [](int i) { return (i >> 1) % (kHeadDim / 32); };
-  bf16x8 gb = opnd(gt, step_s4(0), step_dt(0)), qb = opnd(qt, step_s4(0), step_dt(0));
+  bf16x8 b[2];
+  b[0] = opnd(0);
 #pragma unroll
-  for (int i = 0; i < kSteps; ++i) {
-    const int s4 = step_s4(i), dt = step_dt(i);
-    bf16x8 gn = gb, qn = qb;
-    if (i + 1 < kSteps) {
-      gn = opnd(gt, step_s4(i + 1), step_dt(i + 1));
-      qn = opnd(qt, step_s4(i + 1), step_dt(i + 1));
-    }
-    dv_acc[dt] = mma32(pa[s4], gb, dv_acc[dt]);
-    dk_acc[dt] = mma32(dsa[s4], qb, dk_acc[dt]);
-    gb = gn;
-    qb = qn;
-    if (i == 0) bwd_softmax_half(T, 1, s[1], dp[1], key_seq, a32, scale_log2, pa, dsa);
+  for (int st = 0; st < kSteps; ++st) {
+    if (st + 1 < kSteps) b[(st + 1) & 1] = opnd(st + 1);
+    acc[st >> 2] = mma32(x[st & 3], b[st & 1], acc[st >> 2]);
   }
 }
 
-__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
+__global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
   __shared__ __attribute__((aligned(16))) BwdTile T0;
   __shared__ __attribute__((aligned(16))) BwdTile T1;
+  __shared__ __attribute__((aligned(16))) BwdTile T2;
+  __shared__ __attribute__((aligned(16))) BwdXch X;
   __shared__ __attribute__((aligned(16))) uint16_t rows[kDkvChunk];
   __shared__ uint32_t plan[kDkvWaves][kRunsPerWave * kWave];
   const int nbk = a.batch * a.G * a.nb_max;
@@ -403,10 +383,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
 
   // ---- the rows of the chunk's edges (the bucket's list is sorted, so the
   // order in which edges are summed is fixed)
-  for (int i = tid; i < n; i += kBwdThreads) rows[i] = (uint16_t)(a.edges[e_lo + i] >> 4);
-  __syncthreads();
+  for (int i = tid; i < n; i += kDkvThreads) rows[i] = (uint16_t)(a.edges[e_lo + i] >> 4);
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kt = wave & 3;          // key tile: keys 32 kt .. 32 kt + 31 of the block
+  const bool role_b = wave >= 4;    // A: S, P, dV (K rows); B: dP, dS, dK (V rows)
   const int lane = lane_id();
   const int col = lane & 31;  // MFMA row of A / column of B and C
   const int a32 = lane >> 5;
@@ -418,94 +399,143 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv(BwdKernelArgs a) {
   const bf16* win_q = a.q + a.row_lo * a.Hq * kHeadDim;
   const bf16* win_g = a.dout + a.row_lo * a.Hq * kHeadDim;
   bwd_dma_plan(plan[wave], wave, lane, g, R);
-  // transposed reads: this lane's row 4 a32 + e and column 16 (lane / 16 % 2)
-  // + 4 q inside a 16-row k-step (lane = 16 (2 a32 + lane / 16 % 2) + 4 e + q)
-  const int tr_off = (4 * a32 + ((lane & 15) >> 2)) * kBwdRow + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  // this wave's 32 keys: K and V rows as the B operands of S = Q K^T and
-  // dP = dO V^T (column = key, 8 dims per k-step half); rows past the
+  // transposed reads: this lane's MFMA row 4 a32 + e (tile row 2 e + a32) and
+  // column 16 (lane / 16 % 2) + 4 q inside a 16-row k-step (lane = 16 (2 a32
+  // + lane / 16 % 2) + 4 e + q)
+  const int tr_off = (2 * ((lane & 15) >> 2) + a32) * kBwdRow + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // this tile's 32 keys: K (wave A) or V (wave B) rows as the B operands of
+  // the first product (column = key, 8 dims per k-step half); rows past the
   // sequence end clamp to its last row and are masked (key > every p)
-  const int key_seq = c * kBlock + 32 * wave + col;
+  const int key_seq = c * kBlock + 32 * kt + col;
   const int64_t krow = kb0 + (key_seq < N ? key_seq : N - 1);
-  bf16x8 kf[kHeadDim / 16], vf[kHeadDim / 16];
+  const bf16* kvsrc = role_b ? a.v : a.k;
+  bf16x8 kvf[kHeadDim / 16];
 #pragma unroll
-  for (int ks = 0; ks < kHeadDim / 16; ++ks) {
-    kf[ks] = load8(a.k + krow * rs + g * kHeadDim + 16 * ks + 8 * a32);
-    vf[ks] = load8(a.v + krow * rs + g * kHeadDim + 16 * ks + 8 * a32);
-  }
-  f32x16 dk_acc[kHeadDim / 32], dv_acc[kHeadDim / 32];
+  for (int ks = 0; ks < kHeadDim / 16; ++ks) kvf[ks] = load8(kvsrc + krow * rs + g * kHeadDim + 16 * ks + 8 * a32);
+  f32x16 acc[kHeadDim / 32];  // dV (A) or dK (B, unscaled)
 #pragma unroll
-  for (int dt = 0; dt < kHeadDim / 32; ++dt) {
-    dk_acc[dt] = f32x16{};
-    dv_acc[dt] = f32x16{};
-  }
+  for (int dt = 0; dt < kHeadDim / 32; ++dt) acc[dt] = f32x16{};
 
-  // Quads alternate between the two tiles: the staging loads of quad qi + 1
-  // are issued before quad qi is computed and waited for after it.
+  // Quads rotate through three tiles: the staging loads of quad qi + 2 are
+  // issued before quad qi is computed, and the loads of quad qi + 1 (issued
+  // one quad earlier) are waited for after it.
   const int nquads = (n + 3) / 4;
   QuadAux x;
-  __syncthreads();  // the plan is written
+  lds_barrier();  // rows and the plan are written
   bwd_issue_quad(T0, plan[wave], rows, 0, n, wave, lane, win_q, win_g, win_bytes, row_bytes);
+  if (nquads > 1) bwd_issue_quad(T1, plan[wave], rows, 1, n, wave, lane, win_q, win_g, win_bytes, row_bytes);
   bwd_load_aux(a, x, rows, 0, n, g, R, N, M, q0);
   bwd_store_aux(T0, x);
+  if (nquads > 1) {
+    bwd_load_aux(a, x, rows, 1, n, g, R, N, M, q0);
+    bwd_store_aux(T1, x);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  auto step = [&](BwdTile& cur, BwdTile& nxt, int qi) {
-    const bool more = qi + 1 < nquads;
+  lds_barrier();
+  const float sl2 = a.scale_log2;
+  // staging loads this wave issues per quad (runs wave, wave + 8, ... < kQuadRuns)
+  const bool five = wave < kQuadRuns - kDkvWaves * (kRunsPerWave - 1);
+  auto step = [&](BwdTile& cur, BwdTile& nxt2, int qi) {
+    const bool more = qi + 2 < nquads;
     if (more) {
-      bwd_issue_quad(nxt, plan[wave], rows, qi + 1, n, wave, lane, win_q, win_g, win_bytes, row_bytes);
-      bwd_load_aux(a, x, rows, qi + 1, n, g, R, N, M, q0);
+      // the lse / delta loads first: waiting for them later then does not
+      // wait for the staging loads issued after them
+      bwd_load_aux(a, x, rows, qi + 2, n, g, R, N, M, q0);
+      bwd_issue_quad(nxt2, plan[wave], rows, qi + 2, n, wave, lane, win_q, win_g, win_bytes, row_bytes);
     }
-    bwd_quad_compute(cur, kf, vf, dk_acc, dv_acc, key_seq, col, a32, tr_off, a.scale_log2);
-    if (more) bwd_store_aux(nxt, x);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // quad qi + 1 is in LDS
-    __syncthreads();
+    f32x16 f[2];  // S (A) or dP (B), halves of 32 rows
+    bwd_first_product(cur.rm[role_b ? 1 : 0], kvf, col, a32, f);
+    bf16x8 xa[4];  // P (A) or dS (B) as the A operands of the second product
+    if (!role_b) {
+      // C layout: this lane's key, rows 32 rh + 8 (r / 4) + 4 a32 + r % 4;
+      // rows 16 j .. 16 j + 15 belong to query j of the quad
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh) {
+        const bool live0 = key_seq <= cur.pos[2 * rh], live1 = key_seq <= cur.pos[2 * rh + 1];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 ls = *reinterpret_cast<const f32x4*>(&cur.lse[32 * rh + 8 * q4 + 4 * a32]);
+          const bool live = q4 < 2 ? live0 : live1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * q4 + i;
+            const float pv = live ? __builtin_amdgcn_exp2f(f[rh][r] * sl2 - ls[i]) : 0.f;
+            X.p[kt][16 * rh + r][lane] = pv;
+            xa[2 * rh + (r >> 3)][r & 7] = bf16(pv);
+          }
+        }
+      }
+    }
+    lds_barrier();  // P is in LDS
+    if (role_b) {
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 dl = *reinterpret_cast<const f32x4*>(&cur.delta[32 * rh + 8 * q4 + 4 * a32]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * q4 + i;
+            const float ds = X.p[kt][16 * rh + r][lane] * (f[rh][r] - dl[i]);
+            xa[2 * rh + (r >> 3)][r & 7] = bf16(ds);
+          }
+        }
+    }
+    bwd_second_product(cur.rm[role_b ? 0 : 1], xa, tr_off, acc);
+    if (more) bwd_store_aux(nxt2, x);
+    // quad qi + 1 is in LDS (its loads were issued a quad ago): everything
+    // but this wave's staging loads of quad qi + 2, the newest, is complete
+    if (!more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (five) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kRunsPerWave) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kRunsPerWave - 1) : "memory");
+    lds_barrier();
   };
-  for (int qi = 0; qi < nquads; qi += 2) {
-    step(T0, T1, qi);
+  for (int qi = 0; qi < nquads; qi += 3) {
+    step(T0, T2, qi);
     if (qi + 1 < nquads) step(T1, T0, qi + 1);
+    if (qi + 2 < nquads) step(T2, T1, qi + 2);
   }
 
   // ---- lane column d = 32 dt + col, rows = keys 8 (r / 4) + 4 a32 + r % 4 of
-  // the wave's 32.  A bucket's only chunk adds this window's contribution to
-  // dK / dV; the chunks of a longer bucket write partials for bwd_dkdv_reduce.
+  // the tile's 32.  A bucket's only chunk adds this window's contribution to
+  // dV (wave A) / dK (wave B); the chunks of a longer bucket write partials
+  // for bwd_dkdv_reduce.
+  const float osc = role_b ? a.scale : 1.f;
   if (nchunks == 1) {
     // the first window writes its blocks' rows outright; later ones add, all
     // loads issued (branch-free: rows past the sequence end read its last
     // row) before the first store
+    float* dst = role_b ? a.dk : a.dv;
     const bool add = a.row_lo != 0;
-    float vk[kHeadDim / 32][16], vv[kHeadDim / 32][16];
+    float old[kHeadDim / 32][16];
     if (add) {
 #pragma unroll
       for (int dt = 0; dt < kHeadDim / 32; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kk = c * kBlock + 32 * wave + 8 * (r >> 2) + 4 * a32 + (r & 3);
-          const int64_t off = (kb0 + (kk < N ? kk : N - 1)) * rs + g * kHeadDim + 32 * dt + col;
-          vk[dt][r] = a.dk[off];
-          vv[dt][r] = a.dv[off];
+          const int kk = c * kBlock + 32 * kt + 8 * (r >> 2) + 4 * a32 + (r & 3);
+          old[dt][r] = dst[(kb0 + (kk < N ? kk : N - 1)) * rs + g * kHeadDim + 32 * dt + col];
         }
     }
 #pragma unroll
     for (int dt = 0; dt < kHeadDim / 32; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kk = c * kBlock + 32 * wave + 8 * (r >> 2) + 4 * a32 + (r & 3);
+        const int kk = c * kBlock + 32 * kt + 8 * (r >> 2) + 4 * a32 + (r & 3);
         if (kk >= N) continue;
-        const int64_t off = (kb0 + kk) * rs + g * kHeadDim + 32 * dt + col;
-        const float xk = dk_acc[dt][r] * a.scale, xv = dv_acc[dt][r];
-        a.dk[off] = add ? vk[dt][r] + xk : xk;
-        a.dv[off] = add ? vv[dt][r] + xv : xv;
+        const float xv = acc[dt][r] * osc;
+        dst[(kb0 + kk) * rs + g * kHeadDim + 32 * dt + col] = add ? old[dt][r] + xv : xv;
       }
   } else {
-    float* pk = a.part_dkv + (int64_t)(a.dkv_part[bucket] + chunk) * (2 * kBlock * kHeadDim);
-    float* pv = pk + kBlock * kHeadDim;
+    // partial: [dK (unscaled) | dV] of the chunk
+    float* part = a.part_dkv + (int64_t)(a.dkv_part[bucket] + chunk) * (2 * kBlock * kHeadDim) +
+                  (role_b ? 0 : kBlock * kHeadDim);
 #pragma unroll
     for (int dt = 0; dt < kHeadDim / 32; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = 32 * wave + 8 * (r >> 2) + 4 * a32 + (r & 3);
-        pk[key * kHeadDim + 32 * dt + col] = dk_acc[dt][r];
-        pv[key * kHeadDim + 32 * dt + col] = dv_acc[dt][r];
+        const int key = 32 * kt + 8 * (r >> 2) + 4 * a32 + (r & 3);
+        part[key * kHeadDim + 32 * dt + col] = acc[dt][r];
       }
   }
 }
@@ -861,7 +891,7 @@ hipError_t launch_sparse_attn_bwd(const BwdPlan& pl, const BwdArgs& x, void* ws,
     hipLaunchKernelGGL(bwd_dkv_scan, dim3(1), dim3(1024), 0, st, a, pl.nbuckets);
     // chunks of kDkvChunk edges: at most entries / kDkvChunk + one partial chunk per bucket
     const int64_t ub_kv = entries / kDkvChunk + (entries < pl.nbuckets ? entries : pl.nbuckets) + 1;
-    hipLaunchKernelGGL(bwd_dkdv, dim3((unsigned)ub_kv), dim3(kBwdThreads), 0, st, a);
+    hipLaunchKernelGGL(bwd_dkdv, dim3((unsigned)ub_kv), dim3(kDkvThreads), 0, st, a);
     hipLaunchKernelGGL(bwd_dkdv_reduce, dim3((unsigned)pl.nbuckets * kReduceSplit), dim3(256), 0, st, a);
     hipLaunchKernelGGL(bwd_dq_kvo, dim3((unsigned)ub_kv), dim3(kDqThreads), 0, st, a);
     hipLaunchKernelGGL(bwd_dq_combine, dim3((unsigned)(((r1 - r0) * a.G + 3) / 4)), dim3(256), 0, st, a, r1);
