@@ -187,18 +187,19 @@ constexpr int kDkvWaves = kDkvThreads / kWave;
 constexpr int kRunsPerWave = (kQuadRuns + kDkvWaves - 1) / kDkvWaves;
 static_assert(kQuadRows * kRowSlots % kWave == 0, "a tile is a whole number of 64-slot loads");
 
-// Tile row of MFMA row m = 4 k + j: 8 (k / 2) + 2 j + k % 2.  The four MFMA
-// rows a transposed read gathers (4 k .. 4 k + 3) then lie two tile rows
-// apart, 8 banks, so its 16 lanes' 8-byte pieces fall on distinct banks;
-// any 8 consecutive MFMA rows still fall on distinct banks for the 16-byte
-// row-major reads (a 272-byte row shifts the banks by 4).  Without the
-// permutation the transposed reads conflicted two-way (44% of LDS cycles).
+// Tile row of MFMA row m = 16 s + 4 k + e: 16 s + 4 e + k (a 4 x 4 transpose
+// inside each block of 16 rows; its own inverse).  A 272-byte row shifts the
+// LDS banks by 4 (of 64), so the four MFMA rows 4 k .. 4 k + 3 that a
+// transposed read gathers, four tile rows apart, start 16 banks apart and,
+// with the second 16-dim half of the 32 lanes read together 8 banks further
+// on, the 32 lanes' 8-byte pieces fill distinct banks; 16 consecutive MFMA
+// rows of a 16-byte row-major read are still 16 distinct tile rows of the
+// block.  Consecutive rows made the transposed reads conflict (44% of LDS
+// cycles; 21% with the rows only two apart).
 __device__ __forceinline__ int bwd_tile_row(int m) {
-  return (m & ~7) | ((m & 3) << 1) | ((m >> 2) & 1);
+  return (m & ~15) | ((m & 3) << 2) | ((m >> 2) & 3);
 }
-__device__ __forceinline__ int bwd_mfma_row(int p) {  // inverse of bwd_tile_row
-  return (p & ~7) | ((p & 1) << 2) | ((p >> 1) & 3);
-}
+__device__ __forceinline__ int bwd_mfma_row(int p) { return bwd_tile_row(p); }
 
 // One staging buffer.  The kernel keeps two as separate LDS objects and
 // alternates them in an unrolled loop, so the compiler can see that the
@@ -333,15 +334,15 @@ __device__ __forceinline__ void bwd_first_product(const bf16* tile, const bf16x8
 // is row 16 s4 + 4 a32 + i (i < 4) or 16 s4 + 8 + 4 a32 + i - 4), B operands
 // read transposed from the row-major tile (dO or Q): two reads per step,
 // MFMA rows 16 s4 + 4 a32 .. +3 and 8 rows further, dims 32 dt + col; in
-// tile rows that is 16 s4 (+ 8) + 2 e + a32 for the lane's e (tr_off holds
-// the lane's tile row 2 e + a32 and column 16 (lane / 16 % 2) + 4 q).
+// tile rows that is 16 s4 + 4 e + a32 (+ 2) for the lane's e (tr_off holds
+// the lane's tile row 4 e + a32 and column 16 (lane / 16 % 2) + 4 q).
 // Each accumulator sums its k-steps in order 0..3; the next step's operands
 // are read while the current MFMA runs.
 __device__ __forceinline__ void bwd_second_product(const bf16* tile, const bf16x8 (&x)[4], int tr_off,
                                                    f32x16 (&acc)[kHeadDim / 32]) {
   auto opnd = [&](int st) {
     const bf16* p = tile + tr_off + 16 * (st & 3) * kBwdRow + 32 * (st >> 2);
-    const bf16x4 lo = lds_read_tr4(p), hi = lds_read_tr4(p + 8 * kBwdRow);
+    const bf16x4 lo = lds_read_tr4(p), hi = lds_read_tr4(p + 2 * kBwdRow);
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
   constexpr int kSteps = 4 * (kHeadDim / 32);
@@ -399,10 +400,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
   const bf16* win_q = a.q + a.row_lo * a.Hq * kHeadDim;
   const bf16* win_g = a.dout + a.row_lo * a.Hq * kHeadDim;
   bwd_dma_plan(plan[wave], wave, lane, g, R);
-  // transposed reads: this lane's MFMA row 4 a32 + e (tile row 2 e + a32) and
+  // transposed reads: this lane's MFMA row 4 a32 + e (tile row 4 e + a32) and
   // column 16 (lane / 16 % 2) + 4 q inside a 16-row k-step (lane = 16 (2 a32
   // + lane / 16 % 2) + 4 e + q)
-  const int tr_off = (2 * ((lane & 15) >> 2) + a32) * kBwdRow + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int tr_off = (4 * ((lane & 15) >> 2) + a32) * kBwdRow + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   // this tile's 32 keys: K (wave A) or V (wave B) rows as the B operands of
   // the first product (column = key, 8 dims per k-step half); rows past the
   // sequence end clamp to its last row and are masked (key > every p)

@@ -7,7 +7,7 @@ lane 16 g + i receives, as element e, value i % 4 of the four named by lane
 addresses and inside MFMA chains before the kernel used the instruction.)
 
 bwd_dkdv reads the row-major Q / dO tile (the quad's 64 MFMA rows, pitch
-136 bf16, MFMA row 4 k + j stored at tile row 8 (k / 2) + 2 j + k % 2 so
+136 bf16, MFMA row 16 s + 4 k + e stored at tile row 16 s + 4 e + k so
 that both read kinds avoid LDS bank conflicts) this way for the B operand of
 dV += P^T dO and dK += dS^T Q: lane L needs dim 32 dt + L % 32 and, for
 k-step s4, the MFMA rows that the P / dS registers hold in the same slots --
@@ -35,17 +35,18 @@ def tr_read(tile_flat, addr):
 
 
 def tile_row(m):
-    """Tile row of MFMA row m = 4 k + j."""
-    k, j = divmod(m, 4)
-    return 8 * (k // 2) + 2 * j + (k & 1)
+    """Tile row of MFMA row m = 16 s + 4 k + e."""
+    s, r = divmod(m, 16)
+    k, e = divmod(r, 4)
+    return 16 * s + 4 * e + k
 
 
 def kernel_addresses(s4, dt, pitch=PITCH):
-    """Lane addresses of the low read (the high read is 8 tile rows further)."""
+    """Lane addresses of the low read (the high read is 2 tile rows further)."""
     addr = np.empty(64, dtype=np.int64)
     for lam in range(64):
         a32 = lam >> 5
-        tr_off = (2 * ((lam & 15) >> 2) + a32) * pitch + 16 * ((lam >> 4) & 1) + 4 * (lam & 3)
+        tr_off = (4 * ((lam & 15) >> 2) + a32) * pitch + 16 * ((lam >> 4) & 1) + 4 * (lam & 3)
         addr[lam] = tr_off + 16 * s4 * pitch + 32 * dt
     return addr
 
@@ -63,7 +64,7 @@ def expected_fragment(tile2d, s4, dt):
 def fragments(tile_flat, s4, dt, pitch=PITCH):
     lo_addr = kernel_addresses(s4, dt, pitch)
     lo = tr_read(tile_flat, lo_addr)
-    hi = tr_read(tile_flat, lo_addr + 8 * pitch)
+    hi = tr_read(tile_flat, lo_addr + 2 * pitch)
     return np.concatenate([lo, hi], axis=1)
 
 
@@ -105,7 +106,7 @@ def test_planted_mistakes_fail():
     # lane halves swapped
     bad = kernel_addresses(1, 2)
     bad = np.concatenate([bad[32:], bad[:32]])
-    got = np.concatenate([tr_read(flat, bad), tr_read(flat, bad + 8 * PITCH)], axis=1)
+    got = np.concatenate([tr_read(flat, bad), tr_read(flat, bad + 2 * PITCH)], axis=1)
     assert not np.array_equal(got, want)
     # rows and columns exchanged (a transposed tile)
     tt = np.full((ROWS, PITCH), -1, dtype=np.int64)
