@@ -26,25 +26,21 @@
 //              than one chunk (planted blocks, the early blocks of the first
 //              query window, which nearly every row picks) also get one
 //              partial slot per chunk
-//   bwd_dkdv   KV-outer, one workgroup per chunk.  Each of the 4 waves owns
-//              32 keys of the block and keeps their K and V rows in registers
-//              as MFMA operands; the edges run in quads (4 queries x 16 heads
-//              = 64 MFMA rows), whose Q and dO are staged in LDS twice,
-//              row-major for S = Q K^T and dP = dO V^T and transposed for
-//              dV += P^T dO and dK += dS^T Q, so the P and dS registers of the
-//              first two products are directly the A operands of the last
-//              two.  dK and dV accumulate over the chunk in registers; a
-//              bucket's only chunk adds them to the output, the chunks of a
-//              longer bucket write fp32 partials
+//   bwd_dkdv   KV-outer, one workgroup per chunk, 8 waves: two per key tile
+//              of 32 keys sharing a SIMD, one keeping the tile's K rows as MFMA
+//              operands (S = Q K^T, P, dV += P^T dO), the other its V rows
+//              (dP = dO V^T, dS = P (dP - delta) with P passed through LDS,
+//              dK += dS^T Q).  The edges run in quads (4 queries x 16 heads =
+//              64 MFMA rows) whose Q and dO rows are staged once in LDS by
+//              direct-to-LDS loads, a quad ahead; the second products read
+//              them transposed.  dS also goes to LDS key-major, and every wave
+//              computes a 32 x 32 tile of the quad's dQ^T = K^T dS^T over the
+//              block's 128 keys, written to the bf16 partial of each edge's
+//              selection slot.  dK and dV accumulate over the chunk in
+//              registers; a bucket's only chunk adds them to the output, the
+//              chunks of a longer bucket write fp32 partials
 //   bwd_dkdv_reduce  adds each long bucket's partials to dK / dV in chunk
 //              order
-//   bwd_dq_kvo KV-outer like the forward, one workgroup of 8 waves (two per
-//              SIMD) per chunk of bwd_dkdv (<= 256 edges of a bucket, so the
-//              staging of K, V and K^T is paid once per 256 edges): S^T = K Q^T and
-//              dP^T = V dO^T with two queries x 16 heads as the 32 MFMA
-//              columns, then dQ += dS K from registers; each edge writes its
-//              block's dQ contribution to the bf16 partial of its selection
-//              slot
 //   bwd_dq_combine  dq = sum of a row's slot partials in slot order
 // No atomics touch the arithmetic: every result is bitwise reproducible.
 #include "msa_device.h"
@@ -235,14 +231,14 @@ __device__ __forceinline__ void bwd_dma_plan(uint32_t* plan, int wave, int lane,
 // load (a staging load writes LDS, so a row read after it would wait for
 // it).  A missing query (past the chunk's n edges) reads the first row of
 // the window: finite values whose MFMA rows get probability 0.
-__device__ __forceinline__ void bwd_issue_quad(BwdTile& T, const uint32_t* plan, const uint16_t* rows, int qi, int n,
+__device__ __forceinline__ void bwd_issue_quad(BwdTile& T, const uint32_t* plan, const uint32_t* codes, int qi, int n,
                                                int wave, int lane, const bf16* win_q, const bf16* win_g,
                                                int win_bytes, uint32_t row_bytes) {
-  const u32x2 rr = *reinterpret_cast<const u32x2*>(rows + 4 * qi);  // rows 4 qi .. 4 qi + 3 (16 bits each)
+  const u32x4 cc = *reinterpret_cast<const u32x4*>(codes + 4 * qi);  // edges 4 qi .. 4 qi + 3
   uint32_t pk[kRunsPerWave];
 #pragma unroll
   for (int u = 0; u < kRunsPerWave; ++u) pk[u] = plan[u * kWave + lane];
-  uint32_t rq[4] = {rr.x & 0xffffu, rr.x >> 16, rr.y & 0xffffu, rr.y >> 16};
+  uint32_t rq[4] = {cc.x >> 4, cc.y >> 4, cc.z >> 4, cc.w >> 4};
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     if (4 * qi + j >= n) rq[j] = 0;
@@ -268,21 +264,21 @@ struct QuadAux {
   bool ok;
 };
 
-__device__ __forceinline__ void bwd_load_aux(const BwdKernelArgs& a, QuadAux& x, const uint16_t* rows, int qi,
+__device__ __forceinline__ void bwd_load_aux(const BwdKernelArgs& a, QuadAux& x, const uint32_t* codes, int qi,
                                              int n, int g, int R, int N, int M, int64_t q0) {
   const int tid = threadIdx.x;
   const int e = 4 * qi;
   if (tid < kQuadRows) {
     const int jq = tid >> 4, h = tid & 15;
     x.ok = e + jq < n && h < R;
-    const int64_t t = a.row_lo + (x.ok ? rows[e + jq] : 0);
+    const int64_t t = a.row_lo + (x.ok ? (codes[e + jq] >> 4) : 0);
     const int64_t rh = t * a.Hq + g * R + (x.ok ? h : 0);
     x.lse = a.lse[rh];
     x.delta = a.delta[rh];
   } else if (tid < kQuadRows + 4) {
     const int jq = tid - kQuadRows;
     const bool ok = e + jq < n;
-    const int64_t t = a.row_lo + (ok ? rows[e + jq] : 0);
+    const int64_t t = a.row_lo + (ok ? (codes[e + jq] >> 4) : 0);
     x.pos = ok ? (int)((int64_t)N - M + (t - q0)) : -1;
   }
 }
@@ -355,13 +351,65 @@ __device__ __forceinline__ void bwd_second_product(const bf16* tile, const bf16x
   }
 }
 
+// dS of a quad, key-major for the dQ product: [key][MFMA row], rows of kDsRow
+// bf16.  160 elements (80 dwords, 16 banks of 64 modulo the bank count) put
+// the four keys a transposed read gathers 16 banks apart, so its 32 lanes
+// fill distinct banks.
+constexpr int kDsRow = 160;
+struct BwdDsT {
+  bf16 ds[kBlock * kDsRow];
+};
+
+// dQ^T of quad qi over the block's 128 keys, one 32 x 32 tile per wave: dims
+// 32 (wave % 4) .., MFMA rows 32 (wave / 4) ..; A operands K^T (registers,
+// k-step ks = keys 16 ks .. +15, lane half a32 holding keys 16 ks + 8 a32
+// .. +7), B operands dS^T read transposed from the key-major tile.  Each
+// edge's rows go to the bf16 partial of its selection slot (unscaled, like
+// the forward's partial outputs; bwd_dq_combine sums a row's slots in order).
+__device__ __forceinline__ void bwd_dq_quad(const BwdKernelArgs& a, const BwdDsT& D, const bf16x8 (&kt)[kHeadDim / 16],
+                                            const uint32_t* codes, int qi, int n, int wave, int lane, int g, int R) {
+  const int a32 = lane >> 5;
+  const int rb = 32 * (wave >> 2);  // MFMA rows of this wave's tile
+  // lane 16 g + 4 e + q of a transposed read: key row 8 (g / 2) + e, column
+  // rb + 16 (g % 2) + 4 q
+  const int gq = lane >> 4;
+  const bf16* src = D.ds + (8 * (gq >> 1) + ((lane & 15) >> 2)) * kDsRow + rb + 16 * (gq & 1) + 4 * (lane & 3);
+  f32x16 acc = {};
+  auto opnd = [&](int ks) {
+    const bf16* p = src + 16 * ks * kDsRow;
+    const bf16x4 lo = lds_read_tr4(p), hi = lds_read_tr4(p + 4 * kDsRow);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  bf16x8 bq[2];
+  bq[0] = opnd(0);
+#pragma unroll
+  for (int ks = 0; ks < kHeadDim / 16; ++ks) {
+    if (ks + 1 < kHeadDim / 16) bq[(ks + 1) & 1] = opnd(ks + 1);
+    acc = mma32(kt[ks], bq[ks & 1], acc);
+  }
+  // C layout: column = MFMA row rb + lane % 32 of the quad (query jq, head h),
+  // rows = dims 32 (wave % 4) + 8 j + 4 a32 + i
+  const int row = rb + (lane & 31);
+  const int jq = row >> 4, h = row & 15;
+  if (h >= R || 4 * qi + jq >= n) return;
+  const uint32_t cd = codes[4 * qi + jq];
+  const int64_t slot = ((int64_t)(cd >> 4) * a.G + g) * a.topk + (cd & 15);
+  bf16* dst = a.part_dq + (slot * 16 + h) * kHeadDim + 32 * (wave & 3) + 4 * a32;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bf16x4 v = {bf16(acc[4 * j]), bf16(acc[4 * j + 1]), bf16(acc[4 * j + 2]), bf16(acc[4 * j + 3])};
+    *reinterpret_cast<bf16x4*>(dst + 8 * j) = v;
+  }
+}
+
 __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
   __shared__ __attribute__((aligned(16))) BwdTile T0;
   __shared__ __attribute__((aligned(16))) BwdTile T1;
-  __shared__ __attribute__((aligned(16))) BwdTile T2;
   __shared__ __attribute__((aligned(16))) BwdXch X;
-  __shared__ __attribute__((aligned(16))) uint16_t rows[kDkvChunk];
+  __shared__ __attribute__((aligned(16))) BwdDsT D;
+  __shared__ __attribute__((aligned(16))) uint32_t codes[kDkvChunk];
   __shared__ uint32_t plan[kDkvWaves][kRunsPerWave * kWave];
+  static_assert(sizeof(T0.rm) >= (size_t)kBlock * kBwdRow * sizeof(bf16), "the K tile of the set-up fits a staging tile");
   const int nbk = a.batch * a.G * a.nb_max;
   const int w = blockIdx.x;
   if (w >= a.dkv_chunk[nbk]) return;
@@ -382,9 +430,9 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
   const int64_t rs = (int64_t)a.G * kHeadDim;
   const int tid = threadIdx.x;
 
-  // ---- the rows of the chunk's edges (the bucket's list is sorted, so the
-  // order in which edges are summed is fixed)
-  for (int i = tid; i < n; i += kDkvThreads) rows[i] = (uint16_t)(a.edges[e_lo + i] >> 4);
+  // ---- the chunk's edge codes, (row in window) << 4 | selection slot (the
+  // bucket's list is sorted, so the order in which edges are summed is fixed)
+  for (int i = tid; i < n; i += kDkvThreads) codes[i] = (uint32_t)a.edges[e_lo + i];
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kt = wave & 3;          // key tile: keys 32 kt .. 32 kt + 31 of the block
@@ -417,33 +465,52 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
 #pragma unroll
   for (int dt = 0; dt < kHeadDim / 32; ++dt) acc[dt] = f32x16{};
 
-  // Quads rotate through three tiles: the staging loads of quad qi + 2 are
-  // issued before quad qi is computed, and the loads of quad qi + 1 (issued
-  // one quad earlier) are waited for after it.
+  // ---- K^T fragments of the dQ product: the block's K rows staged row-major
+  // in T0 for the set-up, then read transposed: wave w holds dims 32 (w % 4)
+  // + lane % 32, keys 16 ks + 8 (lane / 32) .. +7 (rows past the sequence end
+  // clamp to its last row; their dS are 0)
+  bf16x8 ktf[kHeadDim / 16];
+  {
+    bf16* kt_lds = &T0.rm[0][0];
+#pragma unroll
+    for (int u = 0; u < kBlock * kHeadDim / 8 / kDkvThreads; ++u) {
+      const int piece = tid + u * kDkvThreads;
+      const int row = piece >> 4, cc = (piece & 15) * 8;
+      const int64_t key = min(c * kBlock + row, N - 1);
+      *reinterpret_cast<bf16x8*>(kt_lds + row * kBwdRow + cc) = load8(a.k + (kb0 + key) * rs + g * kHeadDim + cc);
+    }
+    lds_barrier();
+    const int gq = lane >> 4;
+    const bf16* src = kt_lds + (8 * (gq >> 1) + ((lane & 15) >> 2)) * kBwdRow + 32 * (wave & 3) + 16 * (gq & 1) +
+                      4 * (lane & 3);
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 16; ++ks) {
+      const bf16x4 lo = lds_read_tr4(src + 16 * ks * kBwdRow), hi = lds_read_tr4(src + (16 * ks + 4) * kBwdRow);
+      ktf[ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  }
+
+  // Quads alternate between the two tiles: the staging loads of quad qi + 1
+  // are issued before quad qi is computed and waited for after it; quad
+  // qi - 1's dQ is computed at the start of quad qi (its dS tile is complete).
   const int nquads = (n + 3) / 4;
   QuadAux x;
-  lds_barrier();  // rows and the plan are written
-  bwd_issue_quad(T0, plan[wave], rows, 0, n, wave, lane, win_q, win_g, win_bytes, row_bytes);
-  if (nquads > 1) bwd_issue_quad(T1, plan[wave], rows, 1, n, wave, lane, win_q, win_g, win_bytes, row_bytes);
-  bwd_load_aux(a, x, rows, 0, n, g, R, N, M, q0);
+  lds_barrier();  // the codes and the plan are written; the K tile is read
+  bwd_issue_quad(T0, plan[wave], codes, 0, n, wave, lane, win_q, win_g, win_bytes, row_bytes);
+  bwd_load_aux(a, x, codes, 0, n, g, R, N, M, q0);
   bwd_store_aux(T0, x);
-  if (nquads > 1) {
-    bwd_load_aux(a, x, rows, 1, n, g, R, N, M, q0);
-    bwd_store_aux(T1, x);
-  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
   const float sl2 = a.scale_log2;
-  // staging loads this wave issues per quad (runs wave, wave + 8, ... < kQuadRuns)
-  const bool five = wave < kQuadRuns - kDkvWaves * (kRunsPerWave - 1);
-  auto step = [&](BwdTile& cur, BwdTile& nxt2, int qi) {
-    const bool more = qi + 2 < nquads;
+  auto step = [&](BwdTile& cur, BwdTile& nxt, int qi) {
+    const bool more = qi + 1 < nquads;
     if (more) {
       // the lse / delta loads first: waiting for them later then does not
       // wait for the staging loads issued after them
-      bwd_load_aux(a, x, rows, qi + 2, n, g, R, N, M, q0);
-      bwd_issue_quad(nxt2, plan[wave], rows, qi + 2, n, wave, lane, win_q, win_g, win_bytes, row_bytes);
+      bwd_load_aux(a, x, codes, qi + 1, n, g, R, N, M, q0);
+      bwd_issue_quad(nxt, plan[wave], codes, qi + 1, n, wave, lane, win_q, win_g, win_bytes, row_bytes);
     }
+    if (qi > 0) bwd_dq_quad(a, D, ktf, codes, qi - 1, n, wave, lane, g, R);
     f32x16 f[2];  // S (A) or dP (B), halves of 32 rows
     bwd_first_product(cur.rm[role_b ? 1 : 0], kvf, col, a32, f);
     bf16x8 xa[4];  // P (A) or dS (B) as the A operands of the second product
@@ -467,7 +534,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
         }
       }
     }
-    lds_barrier();  // P is in LDS
+    lds_barrier();  // P is in LDS; every wave is done with quad qi - 1's dS tile
     if (role_b) {
 #pragma unroll
       for (int rh = 0; rh < 2; ++rh)
@@ -480,22 +547,23 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
             const float ds = X.p[kt][16 * rh + r][lane] * (f[rh][r] - dl[i]);
             xa[2 * rh + (r >> 3)][r & 7] = bf16(ds);
           }
+          // dS^T for the dQ product: this lane's key, rows 32 rh + 8 q4 + 4 a32 .. +3
+          const bf16x8& v = xa[2 * rh + (q4 >> 1)];
+          const int o = 4 * (q4 & 1);
+          *reinterpret_cast<bf16x4*>(&D.ds[(32 * kt + col) * kDsRow + 32 * rh + 8 * q4 + 4 * a32]) =
+              bf16x4{v[o], v[o + 1], v[o + 2], v[o + 3]};
         }
     }
     bwd_second_product(cur.rm[role_b ? 0 : 1], xa, tr_off, acc);
-    if (more) bwd_store_aux(nxt2, x);
-    // quad qi + 1 is in LDS (its loads were issued a quad ago): everything
-    // but this wave's staging loads of quad qi + 2, the newest, is complete
-    if (!more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (five) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kRunsPerWave) : "memory");
-    else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kRunsPerWave - 1) : "memory");
-    lds_barrier();
+    if (more) bwd_store_aux(nxt, x);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // quad qi + 1 is in LDS
+    lds_barrier();  // and quad qi's dS tile is complete
   };
-  for (int qi = 0; qi < nquads; qi += 3) {
-    step(T0, T2, qi);
+  for (int qi = 0; qi < nquads; qi += 2) {
+    step(T0, T1, qi);
     if (qi + 1 < nquads) step(T1, T0, qi + 1);
-    if (qi + 2 < nquads) step(T2, T1, qi + 2);
   }
+  bwd_dq_quad(a, D, ktf, codes, nquads - 1, n, wave, lane, g, R);
 
   // ---- lane column d = 32 dt + col, rows = keys 8 (r / 4) + 4 a32 + r % 4 of
   // the tile's 32.  A bucket's only chunk adds this window's contribution to
@@ -597,174 +665,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce(BwdKernelArgs a) {
 // directly the A operand of dQ += dS K.  Each edge writes its block's dQ
 // contribution (bf16) to the partial slot of its selection entry; a
 // fixed-order fp32 sum over the slots follows.
-constexpr int kDqKRow = 136;   // K / V row: 128 bf16 + 8 pad
-constexpr int kDqKtRow = 132;  // K^T row (one dim, 128 keys) + 4 pad
-
-struct DqPair {
-  bf16x8 q[kHeadDim / 16];  // B operand Q^T: column (jq, h), dims 16 ks + 8 a32 .. +7
-  bf16x8 g[kHeadDim / 16];  // B operand dO^T, same layout
-  int code;                 // (row in window) << 4 | selection slot
-  bool has;                 // this lane's column holds an edge
-};
-
-__device__ __forceinline__ void dq_load_pair(const BwdKernelArgs& a, DqPair& P, int e, int e_hi, int jq, int h,
-                                             int a32, int g, int R) {
-  P.has = false;
-  P.code = 0;
-  if (e >= e_hi) return;
-  P.has = e + jq < e_hi;
-  P.code = a.edges[P.has ? e + jq : e];
-  const bool ok = P.has && h < R;
-  const int64_t off = ((a.row_lo + (P.code >> 4)) * a.Hq + g * R + (ok ? h : 0)) * kHeadDim + 8 * a32;
-#pragma unroll
-  for (int ks = 0; ks < kHeadDim / 16; ++ks) {
-    P.q[ks] = ok ? load8(a.q + off + 16 * ks) : zero8<bf16>();
-    P.g[ks] = ok ? load8(a.dout + off + 16 * ks) : zero8<bf16>();
-  }
-}
-
-__device__ __forceinline__ void dq_pair(const BwdKernelArgs& a, DqPair& P, int e_pf, int e_hi, const bf16* k_lds,
-                                        const bf16* v_lds, const bf16* kt_lds, int c, int g, int R, int N, int M,
-                                        int64_t q0, int col, int a32, int jq, int h) {
-  const int64_t trel = P.code >> 4;
-  const int64_t p = (int64_t)N - M + (a.row_lo + trel - q0);
-  const bool colok = P.has && h < R;
-  const int64_t rh = (a.row_lo + trel) * a.Hq + g * R + (colok ? h : 0);
-  // per column: lse in log2 units (+inf for an empty column: P = 0) and delta
-  const float lse2 = colok ? a.lse[rh] * kLog2e : __builtin_inff();
-  const float dlt = colok ? a.delta[rh] : 0.f;
-  // the codes of the pair's two edges, for the partial stores below
-  const int code0 = __shfl(P.code, 0, kWave), code1 = __shfl(P.code, 16, kWave);
-  const bool has1 = __shfl((int)P.has, 16, kWave) != 0;
-
-  f32x16 acc[kHeadDim / 32];
-#pragma unroll
-  for (int dt = 0; dt < kHeadDim / 32; ++dt) acc[dt] = f32x16{};
-#pragma unroll 1
-  for (int kt = 0; kt < kBlock / 32; ++kt) {
-    f32x16 st = {}, dpt = {};
-    const bf16* krow = k_lds + (32 * kt + col) * kDqKRow + 8 * a32;
-    const bf16* vrow = v_lds + (32 * kt + col) * kDqKRow + 8 * a32;
-#pragma unroll
-    for (int ks = 0; ks < kHeadDim / 16; ++ks) {
-      st = mma32(*reinterpret_cast<const bf16x8*>(krow + 16 * ks), P.q[ks], st);
-      dpt = mma32(*reinterpret_cast<const bf16x8*>(vrow + 16 * ks), P.g[ks], dpt);
-    }
-    if (kt == kBlock / 32 - 1) {
-      // Q^T and dO^T are free now: fetch the pair two steps ahead into them
-      // after keeping what the partial stores need
-      dq_load_pair(a, P, e_pf, e_hi, jq, h, a32, g, R);
-    }
-    // C layout: column = this lane's (query, head); rows = keys
-    // 32 kt + 8 (r / 4) + 4 a32 + r % 4
-    const int64_t rel = p - (int64_t)c * kBlock - 32 * kt - 4 * a32;
-    bf16x8 dsa[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool live = 8 * (r >> 2) + (r & 3) <= rel;
-      const float pr = live ? __builtin_amdgcn_exp2f(st[r] * a.scale_log2 - lse2) : 0.f;
-      dsa[r >> 3][r & 7] = bf16(pr * (dpt[r] - dlt));
-    }
-    // dQ[(q, h)][d] += dS[(q, h)][key] K[key][d]; k-step s covers keys
-    // 32 kt + 16 s .. +15, slot i of lane half a32 is key 16 s + 4 a32 + i
-    // (i < 4) or 16 s + 8 + 4 a32 + i - 4: the registers 8 s .. 8 s + 7
-#pragma unroll
-    for (int dt = 0; dt < kHeadDim / 32; ++dt) {
-      const bf16* src = kt_lds + (32 * dt + col) * kDqKtRow + 32 * kt + 4 * a32;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src + 16 * s2);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src + 16 * s2 + 8);
-        const bf16x8 kb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[dt] = mma32(dsa[s2], kb, acc[dt]);
-      }
-    }
-  }
-  // C layout of acc[dt]: column = dim 32 dt + col, rows (query, head)
-  // 8 (r / 4) + 4 a32 + r % 4: rows 0..15 are query 0 of the pair, 16..31 query 1
-  // bf16 partials, like the forward's O partials: the combine sums them in fp32
-  bf16* part = a.part_dq;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = 8 * (r >> 2) + 4 * a32 + (r & 3);
-    const int q = row >> 4, hh = row & 15;
-    if (hh >= R || (q == 1 && !has1)) continue;
-    const int cd = q ? code1 : code0;
-    const int64_t slot = ((int64_t)(cd >> 4) * a.G + g) * a.topk + (cd & 15);
-    bf16* dst = part + (slot * 16 + hh) * kHeadDim + col;
-#pragma unroll
-    for (int dt = 0; dt < kHeadDim / 32; ++dt) dst[32 * dt] = bf16(acc[dt][r]);
-  }
-}
-
-constexpr int kDqThreads = 512;  // 8 waves: two per SIMD, one pair of edges in flight each
-
-__global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kvo(BwdKernelArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 k_lds[kBlock * kDqKRow];
-  __shared__ __attribute__((aligned(16))) bf16 v_lds[kBlock * kDqKRow];
-  __shared__ __attribute__((aligned(16))) bf16 kt_lds[kHeadDim * kDqKtRow];
-  const int nbk = a.batch * a.G * a.nb_max;
-  const int w = blockIdx.x;
-  if (w >= a.dkv_chunk[nbk]) return;
-  const int bucket = bwd_find(a.dkv_chunk, nbk, w);
-  const int chunk = w - a.dkv_chunk[bucket];
-  const int c = bucket % a.nb_max;
-  const int g = (bucket / a.nb_max) % a.G;
-  const int b = bucket / (a.nb_max * a.G);
-  const int e_lo = a.offsets[bucket] + chunk * kDkvChunk;
-  const int e_hi = min(e_lo + kDkvChunk, a.offsets[bucket + 1]);
-  const int64_t kb0 = a.cu_k[b];
-  const int N = a.cu_k[b + 1] - a.cu_k[b];
-  const int64_t q0 = a.cu_q[b];
-  const int M = a.cu_q[b + 1] - a.cu_q[b];
-  const int64_t rs = (int64_t)a.G * kHeadDim;
-
-  // ---- stage K and V row-major, K transposed (rows past the sequence end
-  // clamp to its last row; their scores are masked)
-  {
-#pragma unroll
-    for (int u = 0; u < kBlock * kHeadDim / 8 / kDqThreads; ++u) {
-      const int piece = threadIdx.x + u * kDqThreads;
-      const int row = piece >> 4, cc = (piece & 15) * 8;
-      const int64_t key = min(c * kBlock + row, N - 1);
-      const int64_t off = (kb0 + key) * rs + g * kHeadDim + cc;
-      *reinterpret_cast<bf16x8*>(k_lds + row * kDqKRow + cc) = load8(a.k + off);
-      *reinterpret_cast<bf16x8*>(v_lds + row * kDqKRow + cc) = load8(a.v + off);
-    }
-    // K^T unit = (key quad kq, dim octet o8): 4 rows x 8 dims, written as 8 runs of 4 keys
-#pragma unroll
-    for (int uu = 0; uu < kBlock * kHeadDim / 32 / kDqThreads; ++uu) {
-      const int u = threadIdx.x + uu * kDqThreads;
-      const int kq = u & 31, o8 = u >> 5;
-      bf16x8 r4[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int64_t key = min(c * kBlock + 4 * kq + jj, N - 1);
-        r4[jj] = load8(a.k + (kb0 + key) * rs + g * kHeadDim + 8 * o8);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bf16x4 w4 = {r4[0][e], r4[1][e], r4[2][e], r4[3][e]};
-        *reinterpret_cast<bf16x4*>(kt_lds + (8 * o8 + e) * kDqKtRow + 4 * kq) = w4;
-      }
-    }
-  }
-  __syncthreads();
-
-  const int wave = threadIdx.x >> 6;
-  const int lane = lane_id();
-  const int col = lane & 31;
-  const int a32 = lane >> 5;
-  const int jq = col >> 4, h = col & 15;
-  const int R = a.Hq / a.G;
-  constexpr int kPairStride = 2 * (kDqThreads / kWave);
-  const int e0 = e_lo + 2 * wave;
-  DqPair A;
-  dq_load_pair(a, A, e0, e_hi, jq, h, a32, g, R);
-  for (int e = e0; e < e_hi; e += kPairStride)
-    dq_pair(a, A, e + kPairStride, e_hi, k_lds, v_lds, kt_lds, c, g, R, N, M, q0, col, a32, jq, h);
-}
-
 // Validity of the entries of one selection row: attended when the id names a
 // block at or before the local block and does not repeat an earlier entry.
 __device__ __forceinline__ unsigned bwd_row_mask(const int32_t* sel, int topk, int64_t local, int nb_max) {
@@ -894,7 +794,6 @@ hipError_t launch_sparse_attn_bwd(const BwdPlan& pl, const BwdArgs& x, void* ws,
     const int64_t ub_kv = entries / kDkvChunk + (entries < pl.nbuckets ? entries : pl.nbuckets) + 1;
     hipLaunchKernelGGL(bwd_dkdv, dim3((unsigned)ub_kv), dim3(kDkvThreads), 0, st, a);
     hipLaunchKernelGGL(bwd_dkdv_reduce, dim3((unsigned)pl.nbuckets * kReduceSplit), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(bwd_dq_kvo, dim3((unsigned)ub_kv), dim3(kDqThreads), 0, st, a);
     hipLaunchKernelGGL(bwd_dq_combine, dim3((unsigned)(((r1 - r0) * a.G + 3) / 4)), dim3(256), 0, st, a, r1);
   }
   return hipGetLastError();
