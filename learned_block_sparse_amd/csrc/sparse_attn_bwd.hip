@@ -352,13 +352,18 @@ __device__ __forceinline__ void bwd_second_product(const bf16* tile, const bf16x
 }
 
 // dS of a quad, key-major for the dQ product: [key][MFMA row], rows of kDsRow
-// bf16.  160 elements (80 dwords, 16 banks of 64 modulo the bank count) put
-// the four keys a transposed read gathers 16 banks apart, so its 32 lanes
-// fill distinct banks.
+// bf16.  160 elements (80 dwords: 16 of the 64 banks apart) put the four keys
+// a transposed read gathers on distinct banks; within a key row, the 8-byte
+// unit of MFMA rows 4 u .. 4 u + 3 is stored at unit u ^ ((key / 4) % 8), so
+// the writes of 32 keys at one unit also spread over all banks (without it
+// they fell on 4 bank groups, 8-way).  The four keys of a read share the XOR.
 constexpr int kDsRow = 160;
 struct BwdDsT {
   bf16 ds[kBlock * kDsRow];
 };
+__device__ __forceinline__ int bwd_ds_off(int key, int row4) {  // row4: first of 4 MFMA rows, a multiple of 4
+  return key * kDsRow + 4 * ((row4 >> 2) ^ ((key >> 2) & 7));
+}
 
 // dQ^T of quad qi over the block's 128 keys, one 32 x 32 tile per wave: dims
 // 32 (wave % 4) .., MFMA rows 32 (wave / 4) ..; A operands K^T (registers,
@@ -370,14 +375,14 @@ __device__ __forceinline__ void bwd_dq_quad(const BwdKernelArgs& a, const BwdDsT
                                             const uint32_t* codes, int qi, int n, int wave, int lane, int g, int R) {
   const int a32 = lane >> 5;
   const int rb = 32 * (wave >> 2);  // MFMA rows of this wave's tile
-  // lane 16 g + 4 e + q of a transposed read: key row 8 (g / 2) + e, column
-  // rb + 16 (g % 2) + 4 q
+  // lane 16 g + 4 e + q of a transposed read: key 16 ks + 8 (g / 2) + e (+ 4),
+  // MFMA rows rb + 16 (g % 2) + 4 q .. +3
   const int gq = lane >> 4;
-  const bf16* src = D.ds + (8 * (gq >> 1) + ((lane & 15) >> 2)) * kDsRow + rb + 16 * (gq & 1) + 4 * (lane & 3);
+  const int key0 = 8 * (gq >> 1) + ((lane & 15) >> 2), row4 = rb + 16 * (gq & 1) + 4 * (lane & 3);
   f32x16 acc = {};
   auto opnd = [&](int ks) {
-    const bf16* p = src + 16 * ks * kDsRow;
-    const bf16x4 lo = lds_read_tr4(p), hi = lds_read_tr4(p + 4 * kDsRow);
+    const bf16x4 lo = lds_read_tr4(D.ds + bwd_ds_off(16 * ks + key0, row4));
+    const bf16x4 hi = lds_read_tr4(D.ds + bwd_ds_off(16 * ks + key0 + 4, row4));
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
   bf16x8 bq[2];
@@ -550,7 +555,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
           // dS^T for the dQ product: this lane's key, rows 32 rh + 8 q4 + 4 a32 .. +3
           const bf16x8& v = xa[2 * rh + (q4 >> 1)];
           const int o = 4 * (q4 & 1);
-          *reinterpret_cast<bf16x4*>(&D.ds[(32 * kt + col) * kDsRow + 32 * rh + 8 * q4 + 4 * a32]) =
+          *reinterpret_cast<bf16x4*>(&D.ds[bwd_ds_off(32 * kt + col, 32 * rh + 8 * q4 + 4 * a32)]) =
               bf16x4{v[o], v[o + 1], v[o + 2], v[o + 3]};
         }
     }
