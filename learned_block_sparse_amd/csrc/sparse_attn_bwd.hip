@@ -365,16 +365,16 @@ __device__ __forceinline__ int bwd_ds_off(int key, int row4) {  // row4: first o
   return key * kDsRow + 4 * ((row4 >> 2) ^ ((key >> 2) & 7));
 }
 
-// dQ^T of quad qi over the block's 128 keys, one 32 x 32 tile per wave: dims
-// 32 (wave % 4) .., MFMA rows 32 (wave / 4) ..; A operands K^T (registers,
-// k-step ks = keys 16 ks .. +15, lane half a32 holding keys 16 ks + 8 a32
-// .. +7), B operands dS^T read transposed from the key-major tile.  Each
-// edge's rows go to the bf16 partial of its selection slot (unscaled, like
-// the forward's partial outputs; bwd_dq_combine sums a row's slots in order).
-__device__ __forceinline__ void bwd_dq_quad(const BwdKernelArgs& a, const BwdDsT& D, const bf16x8 (&kt)[kHeadDim / 16],
-                                            const uint32_t* codes, int qi, int n, int wave, int lane, int g, int R) {
+// One 32 x 32 tile of quad qi's dQ^T over the block's 128 keys: dims 32 dt
+// .., MFMA rows rb ..; A operands K^T of those dims (registers, k-step ks =
+// keys 16 ks .. +15, lane half a32 holding keys 16 ks + 8 a32 .. +7), B
+// operands dS^T read transposed from the key-major tile.  Each edge's rows go
+// to the bf16 partial of its selection slot (unscaled, like the forward's
+// partial outputs; bwd_dq_combine sums a row's slots in order).
+__device__ __forceinline__ void bwd_dq_tile(const BwdKernelArgs& a, const BwdDsT& D, const bf16x8 (&kt)[kHeadDim / 16],
+                                            const uint32_t* codes, int qi, int n, int dt, int rb, int lane, int g,
+                                            int R) {
   const int a32 = lane >> 5;
-  const int rb = 32 * (wave >> 2);  // MFMA rows of this wave's tile
   // lane 16 g + 4 e + q of a transposed read: key 16 ks + 8 (g / 2) + e (+ 4),
   // MFMA rows rb + 16 (g % 2) + 4 q .. +3
   const int gq = lane >> 4;
@@ -393,13 +393,13 @@ __device__ __forceinline__ void bwd_dq_quad(const BwdKernelArgs& a, const BwdDsT
     acc = mma32(kt[ks], bq[ks & 1], acc);
   }
   // C layout: column = MFMA row rb + lane % 32 of the quad (query jq, head h),
-  // rows = dims 32 (wave % 4) + 8 j + 4 a32 + i
+  // rows = dims 32 dt + 8 j + 4 a32 + i
   const int row = rb + (lane & 31);
   const int jq = row >> 4, h = row & 15;
   if (h >= R || 4 * qi + jq >= n) return;
   const uint32_t cd = codes[4 * qi + jq];
   const int64_t slot = ((int64_t)(cd >> 4) * a.G + g) * a.topk + (cd & 15);
-  bf16* dst = a.part_dq + (slot * 16 + h) * kHeadDim + 32 * (wave & 3) + 4 * a32;
+  bf16* dst = a.part_dq + (slot * 16 + h) * kHeadDim + 32 * dt + 4 * a32;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const bf16x4 v = {bf16(acc[4 * j]), bf16(acc[4 * j + 1]), bf16(acc[4 * j + 2]), bf16(acc[4 * j + 3])};
@@ -470,10 +470,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
 #pragma unroll
   for (int dt = 0; dt < kHeadDim / 32; ++dt) acc[dt] = f32x16{};
 
-  // ---- K^T fragments of the dQ product: the block's K rows staged row-major
-  // in T0 for the set-up, then read transposed: wave w holds dims 32 (w % 4)
-  // + lane % 32, keys 16 ks + 8 (lane / 32) .. +7 (rows past the sequence end
-  // clamp to its last row; their dS are 0)
+  // ---- K^T fragments of the dQ product (wave B: the dQ^T tiles of dims 32 kt,
+  // both row halves): the block's K rows staged row-major in T0 for the
+  // set-up, then read transposed: dims 32 kt + lane % 32, keys 16 ks + 8
+  // (lane / 32) .. +7 (rows past the sequence end clamp to its last row;
+  // their dS are 0)
   bf16x8 ktf[kHeadDim / 16];
   {
     bf16* kt_lds = &T0.rm[0][0];
@@ -486,18 +487,21 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
     }
     lds_barrier();
     const int gq = lane >> 4;
-    const bf16* src = kt_lds + (8 * (gq >> 1) + ((lane & 15) >> 2)) * kBwdRow + 32 * (wave & 3) + 16 * (gq & 1) +
+    const bf16* src = kt_lds + (8 * (gq >> 1) + ((lane & 15) >> 2)) * kBwdRow + 32 * kt + 16 * (gq & 1) +
                       4 * (lane & 3);
+    if (role_b) {
 #pragma unroll
-    for (int ks = 0; ks < kHeadDim / 16; ++ks) {
-      const bf16x4 lo = lds_read_tr4(src + 16 * ks * kBwdRow), hi = lds_read_tr4(src + (16 * ks + 4) * kBwdRow);
-      ktf[ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      for (int ks = 0; ks < kHeadDim / 16; ++ks) {
+        const bf16x4 lo = lds_read_tr4(src + 16 * ks * kBwdRow), hi = lds_read_tr4(src + (16 * ks + 4) * kBwdRow);
+        ktf[ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
     }
   }
 
   // Quads alternate between the two tiles: the staging loads of quad qi + 1
-  // are issued before quad qi is computed and waited for after it; quad
-  // qi - 1's dQ is computed at the start of quad qi (its dS tile is complete).
+  // are issued before quad qi is computed and waited for after it.  Quad
+  // qi - 1's dQ (its dS tile is complete) is computed by the B waves between
+  // their dP and the exchange of P, i.e. while the A waves compute P.
   const int nquads = (n + 3) / 4;
   QuadAux x;
   lds_barrier();  // the codes and the plan are written; the K tile is read
@@ -515,9 +519,12 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
       bwd_load_aux(a, x, codes, qi + 1, n, g, R, N, M, q0);
       bwd_issue_quad(nxt, plan[wave], codes, qi + 1, n, wave, lane, win_q, win_g, win_bytes, row_bytes);
     }
-    if (qi > 0) bwd_dq_quad(a, D, ktf, codes, qi - 1, n, wave, lane, g, R);
     f32x16 f[2];  // S (A) or dP (B), halves of 32 rows
     bwd_first_product(cur.rm[role_b ? 1 : 0], kvf, col, a32, f);
+    if (role_b && qi > 0) {
+      bwd_dq_tile(a, D, ktf, codes, qi - 1, n, kt, 0, lane, g, R);
+      bwd_dq_tile(a, D, ktf, codes, qi - 1, n, kt, 32, lane, g, R);
+    }
     bf16x8 xa[4];  // P (A) or dS (B) as the A operands of the second product
     if (!role_b) {
       // C layout: this lane's key, rows 32 rh + 8 (r / 4) + 4 a32 + r % 4;
@@ -539,7 +546,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
         }
       }
     }
-    lds_barrier();  // P is in LDS; every wave is done with quad qi - 1's dS tile
+    lds_barrier();  // P is in LDS; the B waves are done with quad qi - 1's dS tile
     if (role_b) {
 #pragma unroll
       for (int rh = 0; rh < 2; ++rh)
@@ -568,7 +575,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
     step(T0, T1, qi);
     if (qi + 1 < nquads) step(T1, T0, qi + 1);
   }
-  bwd_dq_quad(a, D, ktf, codes, nquads - 1, n, wave, lane, g, R);
+  if (role_b) {
+    bwd_dq_tile(a, D, ktf, codes, nquads - 1, n, kt, 0, lane, g, R);
+    bwd_dq_tile(a, D, ktf, codes, nquads - 1, n, kt, 32, lane, g, R);
+  }
 
   // ---- lane column d = 32 dt + col, rows = keys 8 (r / 4) + 4 a32 + r % 4 of
   // the tile's 32.  A bucket's only chunk adds this window's contribution to
