@@ -25,11 +25,12 @@
 //   idx_select_prefill one wave per (row, group): 64-bit selection keys
 //                     (order-preserving score bits, inverted block id, so the
 //                     lower id wins ties) are read back in rounds of 1024; the
-//                     lane maxima, sorted across the wave, give a threshold
-//                     (their 16th largest, or the 16th best kept from earlier
-//                     rounds if larger), the few keys at or above it are
-//                     compacted by ballots and ranked exactly; the best k-1
-//                     and the local block are written ascending, -1 padded.
+//                     16th largest of the lane maxima (a bitwise search
+//                     counted by ballots), or the 16th best kept from earlier
+//                     rounds if larger, is a threshold; the few keys at or
+//                     above it are compacted by ballots and ranked exactly;
+//                     the best k-1 and the local block are written ascending,
+//                     -1 padded.
 // Decode path (two kernels):
 //   idx_decode_scores streams the index-key cache once: the earlier blocks of
 //                     all sequences are one flat range scored grid-stride by
@@ -161,12 +162,13 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
     for (int ks = 0; ks < KS; ++ks) qf[j][ks] = ok ? Mm::load(qp + Mm::kStep * ks) : Mm::zero();
   }
 
-  // Key blocks are staged into LDS in 16-byte pieces (coalesced global reads)
-  // through a ring of kRing buffers: block s + kRing - 1 is fetched into
-  // registers while block s is used, and stored at the end of the step.  With
-  // three buffers, block s + 1 is already in LDS while block s is scored, so
-  // the key fragments of its first tile are read before the step's barrier
-  // and the MFMAs of one block follow those of the previous without a gap.
+  // Key blocks are staged into LDS in 16-byte pieces (coalesced global reads
+  // that write LDS directly, no register round trip) through a ring of kRing
+  // buffers: block s + kRing - 1 is requested while block s is scored, and
+  // the wait and barrier at the end of the step make it visible.  With three
+  // buffers, block s + 1 is already in LDS while block s is scored, so the
+  // key fragments of its first tile are read before the step's barrier and
+  // the MFMAs of one block follow those of the previous without a gap.
   const char* kseq = reinterpret_cast<const char*>(k_idx + (int64_t)k0 * DI);
   constexpr int64_t kBlockBytes = (int64_t)kBlock * DI * sizeof(T);
   // Block `blk` into ring buffer `ring`: run u (of kRuns) fills slots
