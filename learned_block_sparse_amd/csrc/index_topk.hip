@@ -112,13 +112,17 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
   __shared__ __attribute__((aligned(16))) char lds[kRing * L::kBufBytes];
   __shared__ float s_sb[kSbLds ? kScanThreads / kWave : 1][16][kWave];
 
-  // Decode the workgroup: key chunk fastest, then query slice, then query block
-  // (heaviest query blocks first), then sequence.
+  // Decode the workgroup: query block fastest (latest, i.e. heaviest, first),
+  // then query slice, then key chunk, then sequence.  Workgroups are handed
+  // to the 8 XCDs in turn by id, and each XCD runs its own share on its own
+  // CUs, so neighbouring ids must carry similar work: with the key chunk
+  // fastest and 2 or 4 chunks, an XCD received one chunk index only (all
+  // full chunks on some XCDs, all short last chunks on others).
   int bid = blockIdx.x;
-  const int ch = bid % max_chunks;  bid /= max_chunks;
+  const int slot = max_qblocks - 1 - (bid % max_qblocks);  bid /= max_qblocks;
   const int sub = bid % nsub;       bid /= nsub;
-  const int slot = max_qblocks - 1 - (bid % max_qblocks);
-  const int b = bid / max_qblocks;
+  const int ch = bid % max_chunks;
+  const int b = bid / max_chunks;
 
   const int q0 = cu_q[b], M = cu_q[b + 1] - q0;
   const int k0 = cu_k[b], N = cu_k[b + 1] - k0;
@@ -342,43 +346,61 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int batch, int64_t ro
 constexpr int kPreRound = 16 * kWave;     // blocks per selection round (16 keys per lane)
 constexpr int kPreCand = 16 * 16 + 16;    // candidate bound per round (see below)
 
-// The kth largest of the wave's 64-bit keys (one per lane), or a value no
-// larger than any nonzero key when fewer than kth are nonzero: a bitwise
-// binary search for the largest t with at least kth keys >= t, counted by
-// ballots.  The high words are searched first; among keys whose high word
-// equals the result, only the low `lo_bits` bits vary (selection keys hold
-// 0xffffffff - id with id < 2^lo_bits), so the bits above are set at once.
+// Number of keys >= t among the wave's lanes, as a 32-bit scalar (a 64-bit
+// population count compared as such would go to the vector unit).
+__device__ __forceinline__ int wave_count(bool pred) {
+  const uint64_t m = __ballot(pred);
+  return __builtin_popcount((uint32_t)m) + __builtin_popcount((uint32_t)(m >> 32));
+}
+
+// A threshold for the kth largest of the wave's 64-bit keys (one per lane):
+// at least kth keys are >= the result, and when at least kth keys are
+// nonzero, at most kth lanes hold a key >= it unless their high words tie.
+// A bitwise binary search, counted by ballots: the high words first (the
+// largest th with kth high words >= th); only if more than kth lanes reach th
+// are the low bits searched, and among keys whose high word equals th only
+// the low `lo_bits` bits vary (selection keys hold 0xffffffff - id with
+// id < 2^lo_bits), so the bits above are set at once.  With fewer than kth
+// nonzero keys the result is no larger than any nonzero key.
 __device__ __forceinline__ uint64_t wave_kth_largest(uint64_t x, int kth, int lo_bits) {
   const uint32_t xh = (uint32_t)(x >> 32);
   uint32_t th = 0;
 #pragma unroll
   for (int b = 31; b >= 0; --b) {
     const uint32_t t = th | (1u << b);
-    if (__popcll(__ballot(xh >= t)) >= kth) th = t;
+    if (wave_count(xh >= t) >= kth) th = t;
   }
+  if (wave_count(xh >= th) <= kth) return (uint64_t)th << 32;
   uint32_t tl = lo_bits >= 32 ? 0u : (0xffffffffu << lo_bits);
   for (int b = lo_bits - 1; b >= 0; --b) {
     const uint64_t t = ((uint64_t)th << 32) | (tl | (1u << b));
-    if (__popcll(__ballot(x >= t)) >= kth) tl |= 1u << b;
+    if (wave_count(x >= t) >= kth) tl |= 1u << b;
   }
   return ((uint64_t)th << 32) | tl;
 }
 
 // One wave per (query row, group).  The scan left the row's block scores in
-// `scores`; rounds of 1024 earlier blocks (16 per lane) update the 16 best
-// selection keys (per-wave LDS, `best`):
-//   1. lane maxima of the round's keys; T = their 16th largest (a ballot
-//      search), raised to best[15] if that is larger.  At least 16 keys of the
-//      round and the previous best are >= T, so every member of their top 16
-//      is; only the 16 lanes whose maximum reaches T hold such keys, so there
-//      are at most 16 * 16 + 16 candidates;
-//   2. candidates are compacted into LDS in lane order (ballots) and ranked
-//      exactly (keys are distinct); ranks 0..15 become the new best.
+// `scores`; rounds of 1024 earlier blocks (16 per lane, of which only the
+// first `nu` slices of 64 hold blocks) update the 16 best selection keys
+// (per-wave LDS, `best`):
+//   1. lane maxima of the round's keys; T = the threshold of their 16th
+//      largest (wave_kth_largest), raised to best[15] if that is larger, and
+//      to 1 (keys of real blocks are nonzero).  At least 16 keys of the round
+//      and the previous best are >= T, so every member of their top 16 is.
+//      Only lanes whose maximum reaches T hold such keys, and there are at
+//      most 16 of them: either exactly 16 lanes reach the high word of T, or
+//      T is the exact 16th largest maximum (keys are distinct), or fewer than
+//      16 lanes hold any key.  So there are at most 16 * 16 + 16 candidates;
+//   2. candidates are compacted into LDS in lane order (ballots; lanes that
+//      take nothing write to a slot of their own past the candidates) and
+//      ranked exactly (keys are distinct); ranks 0..15 become the new best.
 // The best topk - 1 plus the local block are written ascending.
 __global__ __launch_bounds__(256) void idx_select_prefill(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int64_t rows_bound, int G,
     int topk, int nb_stride, const float* __restrict__ scores, int32_t* __restrict__ block_idx) {
-  __shared__ uint64_t s_cand[4][kPreCand];
+  // candidates, 4 zero keys that pad the rank loop, and one discard slot per lane
+  constexpr int kCandSlots = kPreCand + 4 + kWave;
+  __shared__ __attribute__((aligned(16))) uint64_t s_cand[4][kCandSlots];
   __shared__ uint64_t s_best[4][16];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = lane_id();
@@ -401,51 +423,61 @@ __global__ __launch_bounds__(256) void idx_select_prefill(
   if (lane < 16) best[lane] = 0;
   const int lo_bits = local > 1 ? 32 - __clz(local - 1) : 0;  // bits of the largest earlier id
   for (int r0 = 0; r0 < local; r0 += kPreRound) {
+    const int nu = min(16, (local - r0 + kWave - 1) / kWave);  // slices holding blocks (wave-uniform)
     float v[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int c = r0 + lane + kWave * u;
-      v[u] = c < local ? sc[c] : 0.0f;
+      if (u < nu) v[u] = sc[min(c, local - 1)];
     }
     uint64_t k16[16], mx = 0;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int c = r0 + lane + kWave * u;
-      k16[u] = c < local ? sel_key(v[u], c) : 0;
-      mx = k16[u] > mx ? k16[u] : mx;
+      k16[u] = 0;
+      if (u < nu) {
+        const uint64_t key = sel_key(v[u], c);
+        k16[u] = c < local ? key : 0;
+        mx = k16[u] > mx ? k16[u] : mx;
+      }
     }
     const uint64_t t_round = wave_kth_largest(mx, 16, lo_bits);
     const uint64_t b15 = best[15];
-    const uint64_t T = t_round > b15 ? t_round : b15;
+    uint64_t T = t_round > b15 ? t_round : b15;
+    T = T > 1 ? T : 1;
     // compact the candidates (keys >= T) into LDS, lane order within each u
     int n = 0;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      const bool take = k16[u] != 0 && k16[u] >= T;
-      const uint64_t m = __ballot(take);
-      if (take) {
+      if (u < nu) {
+        const bool take = k16[u] >= T;
+        const uint64_t m = __ballot(take);
         const int slot = n + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        if (slot < kPreCand) cand[slot] = k16[u];  // always true (bound above)
+        cand[take ? min(slot, kPreCand - 1) : kPreCand + 4 + lane] = k16[u];  // slot < kPreCand (bound above)
+        n += __builtin_popcount((uint32_t)m) + __builtin_popcount((uint32_t)(m >> 32));
       }
-      n += __builtin_popcountll(m);
     }
     {
       const uint64_t x = lane < 16 ? best[lane] : 0;
-      const bool take = x != 0 && x >= T;
+      const bool take = x >= T;
       const uint64_t m = __ballot(take);
-      if (take) {
-        const int slot = n + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        if (slot < kPreCand) cand[slot] = x;
-      }
-      n += __builtin_popcountll(m);
+      const int slot = n + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      cand[take ? min(slot, kPreCand - 1) : kPreCand + 4 + lane] = x;
+      n += __builtin_popcount((uint32_t)m) + __builtin_popcount((uint32_t)(m >> 32));
     }
     n = min(n, kPreCand);
-    // exact ranks of the candidates, 64 at a time (usually one pass)
+    if (lane < 4) cand[n + lane] = 0;  // pads the rank loop to a multiple of 4
+    // exact ranks of the candidates, 64 at a time (usually one pass), 4
+    // candidates per LDS read pair
     for (int i0 = 0; i0 < n; i0 += kWave) {
       const bool has = i0 + lane < n;
       const uint64_t mine = has ? cand[i0 + lane] : 0;
       int rank = 0;
-      for (int j = 0; j < n; ++j) rank += cand[j] > mine ? 1 : 0;
+      for (int j = 0; j < n; j += 4) {
+        const u64x2 c01 = *reinterpret_cast<const u64x2*>(cand + j);
+        const u64x2 c23 = *reinterpret_cast<const u64x2*>(cand + j + 2);
+        rank += (c01.x > mine ? 1 : 0) + (c01.y > mine ? 1 : 0) + (c23.x > mine ? 1 : 0) + (c23.y > mine ? 1 : 0);
+      }
       if (has && rank < 16) best[rank] = mine;
     }
     if (lane < 16 && lane >= n) best[lane] = 0;
