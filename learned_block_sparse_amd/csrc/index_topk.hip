@@ -218,6 +218,46 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[0][ks] = kfrag(0, 0, ks);
   }
+  // A block's score: lane l < 32 owns column l of tile 0, lane l >= 32 column
+  // l - 32 of tile 1; each needs the other half-wave's partial max of its own
+  // column.  The scores of 16 consecutive blocks are stored together.
+  auto finish = [&](int sb, float a0, float a1) {
+    const float send = lane < 32 ? a1 : a0;
+    const float recv = shfl_xor_f(send, 32);
+    const float v = fmaxf(lane < 32 ? a0 : a1, recv);
+    if constexpr (kSbLds) {
+      s_sb[wave][sb & 15][lane] = v;
+      if ((sb & 15) == 15 && col_ok) {
+        f32x4* dst = reinterpret_cast<f32x4*>(srow + (sb - 15));
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          dst[q] = f32x4{s_sb[wave][4 * q][lane], s_sb[wave][4 * q + 1][lane], s_sb[wave][4 * q + 2][lane],
+                         s_sb[wave][4 * q + 3][lane]};
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 15; ++j) sbuf[j] = sbuf[j + 1];
+      sbuf[15] = v;
+      if ((sb & 15) == 15 && col_ok) {
+        f32x4* dst = reinterpret_cast<f32x4*>(srow + (sb - 15));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = f32x4{sbuf[4 * q], sbuf[4 * q + 1], sbuf[4 * q + 2], sbuf[4 * q + 3]};
+      }
+    }
+  };
+  // With the fragments read ahead (kPrefetch), two accumulator sets persist
+  // across blocks: tile kt's scores are max-pooled during the second half of
+  // tile kt + 1's MFMAs (its results are complete by then), the last tile of
+  // block s - 1 during tile 0 of block s, and block s - 1's score is finished
+  // after that tile.  So the MFMA pipe never waits for the pooling, and the
+  // score stores have a whole block to complete before the wait at its end.
+  static_assert((kBlock / 32) % 2 == 0, "the last tile of a block must land in acc[1]");
+  f32x16 acc[2][2];
+  float pm0 = -__builtin_inff(), pm1 = -__builtin_inff();  // block s - 1 over tiles 0 .. 2
+  if constexpr (kPrefetch) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { acc[1][0][r] = -__builtin_inff(); acc[1][1][r] = -__builtin_inff(); }
+  }
   int ring = 0;  // ring buffer of block s
   for (int s = s_lo; s < s_hi; ++s) {
     const int ring_next = ring + 1 == kRing ? 0 : ring + 1;
@@ -230,11 +270,6 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
       }
       float m0 = -__builtin_inff(), m1 = -__builtin_inff();
       if constexpr (kPrefetch) {
-        // Two accumulator sets: tile kt's scores are max-pooled during the
-        // second half of tile kt + 1's MFMAs (its results are complete by
-        // then), so the MFMA pipe does not wait for the pooling; the last
-        // tile's are pooled after the loop.
-        f32x16 acc[2][2];
         // the pooling runs in the last kPool steps of a tile (at least one)
         constexpr int kPool = KS / 2 > 0 ? KS / 2 : 1;
         constexpr int kRowsPerStep = (16 + kPool - 1) / kPool;
@@ -255,22 +290,25 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
             const int h = ks - (KS - kPool);
-            if (kt > 0 && h >= 0) {
+            if (h >= 0) {
+              // tile kt - 1 of this block, or the last tile of the previous one
+              float& a0 = kt > 0 ? m0 : pm0;
+              float& a1 = kt > 0 ? m1 : pm1;
 #pragma unroll
               for (int r = h * kRowsPerStep; r < (h + 1) * kRowsPerStep && r < 16; ++r) {
-                m0 = fmaxf(m0, acc[cur ^ 1][0][r]);
-                m1 = fmaxf(m1, acc[cur ^ 1][1][r]);
+                a0 = fmaxf(a0, acc[cur ^ 1][0][r]);
+                a1 = fmaxf(a1, acc[cur ^ 1][1][r]);
               }
               __builtin_amdgcn_sched_group_barrier(0x002, kRowsPerStep, 0);  // the pooling
             }
           }
+          if (kt == 0 && s > s_lo) finish(s - 1, pm0, pm1);
           // keep each tile's MFMAs within its own step: the next tile's
           // MFMAs would otherwise be pulled up behind their fragment reads
           __builtin_amdgcn_sched_barrier(0);
         }
-        constexpr int last = (kBlock / 32 - 1) & 1;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { m0 = fmaxf(m0, acc[last][0][r]); m1 = fmaxf(m1, acc[last][1][r]); }
+        pm0 = m0;
+        pm1 = m1;
       } else {
 #pragma unroll
         for (int kt = 0; kt < kBlock / 32; ++kt) {
@@ -285,35 +323,20 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
 #pragma unroll
           for (int r = 0; r < 16; ++r) { m0 = fmaxf(m0, acc0[r]); m1 = fmaxf(m1, acc1[r]); }
         }
-      }
-      // Lane l < 32 owns column l of tile 0, lane l >= 32 column l-32 of tile 1;
-      // each needs the other half-wave's partial max of its own column.
-      const float send = lane < 32 ? m1 : m0;
-      const float recv = shfl_xor_f(send, 32);
-      const float v = fmaxf(lane < 32 ? m0 : m1, recv);
-      if constexpr (kSbLds) {
-        s_sb[wave][s & 15][lane] = v;
-        if ((s & 15) == 15 && col_ok) {
-          f32x4* dst = reinterpret_cast<f32x4*>(srow + (s - 15));
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            dst[q] = f32x4{s_sb[wave][4 * q][lane], s_sb[wave][4 * q + 1][lane], s_sb[wave][4 * q + 2][lane],
-                           s_sb[wave][4 * q + 3][lane]};
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 15; ++j) sbuf[j] = sbuf[j + 1];
-        sbuf[15] = v;
-        if ((s & 15) == 15 && col_ok) {
-          f32x4* dst = reinterpret_cast<f32x4*>(srow + (s - 15));
-#pragma unroll
-          for (int q = 0; q < 4; ++q) dst[q] = f32x4{sbuf[4 * q], sbuf[4 * q + 1], sbuf[4 * q + 2], sbuf[4 * q + 3]};
-        }
+        finish(s, m0, m1);
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // block s + kRing - 1 is in LDS
     __syncthreads();
     ring = ring_next;
+  }
+  if constexpr (kPrefetch) {
+    // the last block's last tile
+    if (active) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { pm0 = fmaxf(pm0, acc[1][0][r]); pm1 = fmaxf(pm1, acc[1][1][r]); }
+      finish(s_hi - 1, pm0, pm1);
+    }
   }
   // a trailing partial group (only at the end of a query block's last chunk)
   const int n_tail = s_hi & 15;
