@@ -152,6 +152,44 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
 #endif
 }
 
+// An 8-byte LDS store issued from an asm statement.  The compiler's
+// wait-count pass orders its own LDS stores after any direct-to-LDS load
+// still in flight that it cannot tell apart from the stored buffer, with a
+// full vector-memory wait; this store never waits.  The caller must order it
+// against other accesses of the same buffer by barriers (the LDS-counter wait
+// of lds_barrier completes it; LDS operations complete in order, so the
+// compiler's own LDS-counter waits are never made too short by it).
+__device__ __forceinline__ void lds_store8(bf16* p, bf16x4 v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)p;
+  asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(v));
+#endif
+}
+
+// Wait until every vector memory operation of this wave has completed
+// (loads, stores, direct-to-LDS loads): s_waitcnt vmcnt(0), with the gfx9
+// immediate (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 left at
+// their maxima).  Unlike the same instruction in an asm statement, the
+// builtin is seen by the compiler's wait-count pass, which then knows that
+// registers loaded earlier are complete and adds no waits of its own for
+// them later (an asm wait left it waiting again, for everything in flight,
+// inside loops).  It does not order memory accesses: follow it with a
+// barrier or fence where the staged data is read.
+__device__ __forceinline__ void vmem_wait_all() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+#endif
+}
+// The same, but leaving the N most recently issued operations in flight
+// (s_waitcnt vmcnt(N), N < 16).
+template <int N>
+__device__ __forceinline__ void vmem_wait_all_but() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate of 4 bits");
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+#endif
+}
+
 // Workgroup barrier that orders LDS accesses only: the wave's own LDS
 // writes are complete before it (lgkmcnt) and later LDS reads see the other
 // waves' writes, while global loads and direct-to-LDS loads stay in flight

@@ -33,12 +33,13 @@
 //              dK += dS^T Q).  The edges run in quads (4 queries x 16 heads =
 //              64 MFMA rows) whose Q and dO rows are staged once in LDS by
 //              direct-to-LDS loads, a quad ahead; the second products read
-//              them transposed.  dS also goes to LDS key-major, and every wave
-//              computes a 32 x 32 tile of the quad's dQ^T = K^T dS^T over the
-//              block's 128 keys, written to the bf16 partial of each edge's
-//              selection slot.  dK and dV accumulate over the chunk in
-//              registers; a bucket's only chunk adds them to the output, the
-//              chunks of a longer bucket write fp32 partials
+//              them transposed.  dS also goes to LDS key-major; during the
+//              next quad each B wave computes 32 dims of dQ^T = K^T dS^T over
+//              the block's 128 keys into an LDS stage, from which each A wave
+//              writes one edge's rows (4 KB, whole cache lines) to the bf16
+//              partial of its selection slot.  dK and dV accumulate over the
+//              chunk in registers; a bucket's only chunk adds them to the
+//              output, the chunks of a longer bucket write fp32 partials
 //   bwd_dkdv_reduce  adds each long bucket's partials to dK / dV in chunk
 //              order
 //   bwd_dq_combine  dq = sum of a row's slot partials in slot order
@@ -227,9 +228,9 @@ __device__ __forceinline__ void bwd_dma_plan(uint32_t* plan, int wave, int lane,
 }
 
 // Issue the staging loads of quad qi into tile T (nothing waits for them
-// here).  The quad's four query rows are read from LDS at once, before any
-// load (a staging load writes LDS, so a row read after it would wait for
-// it).  A missing query (past the chunk's n edges) reads the first row of
+// here).  The quad's four query rows and the lane's plan are read from LDS
+// at once, before any load (a staging load writes LDS, so a read after it
+// could wait for it).  A missing query (past the chunk's n edges) reads the first row of
 // the window: finite values whose MFMA rows get probability 0.
 __device__ __forceinline__ void bwd_issue_quad(BwdTile& T, const uint32_t* plan, const uint32_t* codes, int qi, int n,
                                                int wave, int lane, const bf16* win_q, const bf16* win_g,
@@ -308,12 +309,15 @@ struct BwdXch {
 };
 
 // S (A) or dP (B) of the quad's 64 rows: two halves of 32 MFMA rows, 8 k-steps
-// each, as one run of 16 steps with operands read from LDS two steps ahead.
+// each, the halves' MFMAs alternating (each accumulator sums its k-steps in
+// order, and consecutive MFMAs do not depend on each other) with operands
+// read from LDS two steps ahead.
 __device__ __forceinline__ void bwd_first_product(const bf16* tile, const bf16x8 (&kv)[kHeadDim / 16], int col,
                                                   int a32, f32x16 (&acc)[2]) {
   constexpr int kKs = kHeadDim / 16;
   const int arow0 = bwd_tile_row(col) * kBwdRow + 8 * a32;  // MFMA row col (+ 32 for the second half)
-  auto aofs = [&](int st) { return arow0 + (st / kKs) * 32 * kBwdRow + 16 * (st % kKs); };
+  // step st: half st % 2, k-step st / 2
+  auto aofs = [&](int st) { return arow0 + (st & 1) * 32 * kBwdRow + 16 * (st >> 1); };
   bf16x8 op[3];
   op[0] = *reinterpret_cast<const bf16x8*>(&tile[aofs(0)]);
   op[1] = *reinterpret_cast<const bf16x8*>(&tile[aofs(1)]);
@@ -321,7 +325,7 @@ __device__ __forceinline__ void bwd_first_product(const bf16* tile, const bf16x8
 #pragma unroll
   for (int st = 0; st < 2 * kKs; ++st) {
     if (st + 2 < 2 * kKs) op[(st + 2) % 3] = *reinterpret_cast<const bf16x8*>(&tile[aofs(st + 2)]);
-    acc[st / kKs] = mma32(op[st % 3], kv[st % kKs], acc[st / kKs]);
+    acc[st & 1] = mma32(op[st % 3], kv[st >> 1], acc[st & 1]);
   }
 }
 
@@ -332,32 +336,37 @@ __device__ __forceinline__ void bwd_first_product(const bf16* tile, const bf16x8
 // MFMA rows 16 s4 + 4 a32 .. +3 and 8 rows further, dims 32 dt + col; in
 // tile rows that is 16 s4 + 4 e + a32 (+ 2) for the lane's e (tr_off holds
 // the lane's tile row 4 e + a32 and column 16 (lane / 16 % 2) + 4 q).
-// Each accumulator sums its k-steps in order 0..3; the next step's operands
-// are read while the current MFMA runs.
+// The four dim tiles' MFMAs alternate (each accumulator still sums its
+// k-steps in order 0..3); operands are read two steps ahead.
 __device__ __forceinline__ void bwd_second_product(const bf16* tile, const bf16x8 (&x)[4], int tr_off,
                                                    f32x16 (&acc)[kHeadDim / 32]) {
+  constexpr int kDt = kHeadDim / 32;
+  // step st: dim tile st % kDt, k-step st / kDt
   auto opnd = [&](int st) {
-    const bf16* p = tile + tr_off + 16 * (st & 3) * kBwdRow + 32 * (st >> 2);
+    const bf16* p = tile + tr_off + 16 * (st / kDt) * kBwdRow + 32 * (st % kDt);
     const bf16x4 lo = lds_read_tr4(p), hi = lds_read_tr4(p + 2 * kBwdRow);
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
-  constexpr int kSteps = 4 * (kHeadDim / 32);
-  bf16x8 b[2];
+  constexpr int kSteps = 4 * kDt;
+  bf16x8 b[3];
   b[0] = opnd(0);
+  b[1] = opnd(1);
 #pragma unroll
   for (int st = 0; st < kSteps; ++st) {
-    if (st + 1 < kSteps) b[(st + 1) & 1] = opnd(st + 1);
-    acc[st >> 2] = mma32(x[st & 3], b[st & 1], acc[st >> 2]);
+    if (st + 2 < kSteps) b[(st + 2) % 3] = opnd(st + 2);
+    acc[st % kDt] = mma32(x[st / kDt], b[st % 3], acc[st % kDt]);
   }
 }
 
 // dS of a quad, key-major for the dQ product: [key][MFMA row], rows of kDsRow
-// bf16.  160 elements (80 dwords: 16 of the 64 banks apart) put the four keys
-// a transposed read gathers on distinct banks; within a key row, the 8-byte
+// bf16.  96 elements (48 dwords, 16 of the 64 banks back) put the four keys a
+// transposed read gathers on distinct banks; within a key row, the 8-byte
 // unit of MFMA rows 4 u .. 4 u + 3 is stored at unit u ^ ((key / 4) % 8), so
 // the writes of 32 keys at one unit also spread over all banks (without it
 // they fell on 4 bank groups, 8-way).  The four keys of a read share the XOR.
-constexpr int kDsRow = 160;
+// Both the writes and the transposed reads take the minimum two cycles per
+// 512 bytes (a model of the 64 banks; 64 or 80 elements would take four).
+constexpr int kDsRow = 96;
 struct BwdDsT {
   bf16 ds[kBlock * kDsRow];
 };
@@ -365,45 +374,76 @@ __device__ __forceinline__ int bwd_ds_off(int key, int row4) {  // row4: first o
   return key * kDsRow + 4 * ((row4 >> 2) ^ ((key >> 2) & 7));
 }
 
-// One 32 x 32 tile of quad qi's dQ^T over the block's 128 keys: dims 32 dt
-// .., MFMA rows rb ..; A operands K^T of those dims (registers, k-step ks =
-// keys 16 ks .. +15, lane half a32 holding keys 16 ks + 8 a32 .. +7), B
-// operands dS^T read transposed from the key-major tile.  Each edge's rows go
-// to the bf16 partial of its selection slot (unscaled, like the forward's
-// partial outputs; bwd_dq_combine sums a row's slots in order).
-__device__ __forceinline__ void bwd_dq_tile(const BwdKernelArgs& a, const BwdDsT& D, const bf16x8 (&kt)[kHeadDim / 16],
-                                            const uint32_t* codes, int qi, int n, int dt, int rb, int lane, int g,
-                                            int R) {
+// A quad's dQ, staged in LDS by the B waves (each 32 of the 128 dims of all
+// 64 MFMA rows) and stored to the partials by the A waves, one edge (16 heads
+// x 128 dims, 4 KB contiguous in the partials) each: whole rows, so every
+// store writes 1 KB of whole cache lines (the C layout would scatter 16-byte
+// pieces of 32 rows per store).  Rows of 136 bf16 (272 bytes) keep both the
+// 8-byte writes of 32 rows and the 16-byte reads of 4 rows free of bank
+// conflicts.
+struct BwdDqStage {
+  bf16 q[kQuadRows * kBwdRow];
+};
+
+// Quad qi's dQ^T over the block's 128 keys for dims 32 dt .. +31: two 32 x 32
+// tiles, MFMA rows 0..31 and 32..63, their MFMAs alternating; A operands K^T
+// of those dims (registers, k-step ks = keys 16 ks .. +15, lane half a32
+// holding keys 16 ks + 8 a32 .. +7), B operands dS^T read transposed from the
+// key-major tile two steps ahead.  The result goes to the staging tile.
+__device__ __forceinline__ void bwd_dq_tiles(const BwdDsT& D, BwdDqStage& Q, const bf16x8 (&kt)[kHeadDim / 16], int dt,
+                                             int lane) {
   const int a32 = lane >> 5;
   // lane 16 g + 4 e + q of a transposed read: key 16 ks + 8 (g / 2) + e (+ 4),
   // MFMA rows rb + 16 (g % 2) + 4 q .. +3
   const int gq = lane >> 4;
-  const int key0 = 8 * (gq >> 1) + ((lane & 15) >> 2), row4 = rb + 16 * (gq & 1) + 4 * (lane & 3);
-  f32x16 acc = {};
-  auto opnd = [&](int ks) {
-    const bf16x4 lo = lds_read_tr4(D.ds + bwd_ds_off(16 * ks + key0, row4));
-    const bf16x4 hi = lds_read_tr4(D.ds + bwd_ds_off(16 * ks + key0 + 4, row4));
+  const int key0 = 8 * (gq >> 1) + ((lane & 15) >> 2), row4 = 16 * (gq & 1) + 4 * (lane & 3);
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  constexpr int kKs = kHeadDim / 16;
+  // step st: row tile st % 2 (rb = 32 (st % 2)), k-step st / 2
+  auto opnd = [&](int st) {
+    const int ks = st >> 1, rb = 32 * (st & 1);
+    const bf16x4 lo = lds_read_tr4(D.ds + bwd_ds_off(16 * ks + key0, rb + row4));
+    const bf16x4 hi = lds_read_tr4(D.ds + bwd_ds_off(16 * ks + key0 + 4, rb + row4));
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
-  bf16x8 bq[2];
+  bf16x8 bq[3];
   bq[0] = opnd(0);
+  bq[1] = opnd(1);
 #pragma unroll
-  for (int ks = 0; ks < kHeadDim / 16; ++ks) {
-    if (ks + 1 < kHeadDim / 16) bq[(ks + 1) & 1] = opnd(ks + 1);
-    acc = mma32(kt[ks], bq[ks & 1], acc);
+  for (int st = 0; st < 2 * kKs; ++st) {
+    if (st + 2 < 2 * kKs) bq[(st + 2) % 3] = opnd(st + 2);
+    acc[st & 1] = mma32(kt[st >> 1], bq[st % 3], acc[st & 1]);
   }
-  // C layout: column = MFMA row rb + lane % 32 of the quad (query jq, head h),
-  // rows = dims 32 dt + 8 j + 4 a32 + i
-  const int row = rb + (lane & 31);
-  const int jq = row >> 4, h = row & 15;
-  if (h >= R || 4 * qi + jq >= n) return;
-  const uint32_t cd = codes[4 * qi + jq];
-  const int64_t slot = ((int64_t)(cd >> 4) * a.G + g) * a.topk + (cd & 15);
-  bf16* dst = a.part_dq + (slot * 16 + h) * kHeadDim + 32 * dt + 4 * a32;
+  // C layout: column = MFMA row 32 t + lane % 32, rows = dims 32 dt + 8 j + 4 a32 + i
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const bf16x4 v = {bf16(acc[4 * j]), bf16(acc[4 * j + 1]), bf16(acc[4 * j + 2]), bf16(acc[4 * j + 3])};
-    *reinterpret_cast<bf16x4*>(dst + 8 * j) = v;
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      lds_store8(&Q.q[(32 * t + (lane & 31)) * kBwdRow + 32 * dt + 8 * j + 4 * a32],
+                 bf16x4{bf16(acc[t][4 * j]), bf16(acc[t][4 * j + 1]), bf16(acc[t][4 * j + 2]), bf16(acc[t][4 * j + 3])});
+}
+
+// Edge e's rows of the staged dQ (MFMA rows 16 jq .. 16 jq + 15, jq = e % 4)
+// to the bf16 partial of its selection slot (unscaled, like the forward's
+// partial outputs; bwd_dq_combine sums a row's slots in order): four stores
+// of 64 lanes x 16 bytes, heads 4 i .. 4 i + 3.  The stores go through a
+// buffer that spans the edge's R heads only, so the hardware drops those of
+// heads past R, and all of them for a missing edge (e >= n): the wave always
+// issues exactly four stores, which lets the end of a step wait for its
+// earlier loads without waiting for these.
+constexpr int kDqStores = 4;
+__device__ __forceinline__ void bwd_dq_store(const BwdKernelArgs& a, const BwdDqStage& Q, const uint32_t* codes, int e,
+                                             int n, int lane, int g, int R) {
+  const bool ok = e < n;
+  const uint32_t cd = __builtin_amdgcn_readfirstlane(ok ? codes[e] : 0u);
+  const int64_t slot = ((int64_t)(cd >> 4) * a.G + g) * a.topk + (cd & 15);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(a.part_dq + slot * 16 * kHeadDim, 0,
+                                                                     ok ? R * kHeadDim * 2 : 0, 0x00020000);
+  const bf16* src = Q.q + (16 * (e & 3) + (lane >> 4)) * kBwdRow + 8 * (lane & 15);
+#pragma unroll
+  for (int i = 0; i < kDqStores; ++i) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + 4 * i * kBwdRow);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (4 * i + (lane >> 4)) * kHeadDim * 2 + 16 * (lane & 15), 0, 0);
   }
 }
 
@@ -413,6 +453,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
   __shared__ __attribute__((aligned(16))) BwdXch X;
   __shared__ __attribute__((aligned(16))) BwdDsT D;
   __shared__ __attribute__((aligned(16))) uint32_t codes[kDkvChunk];
+  __shared__ __attribute__((aligned(16))) BwdDqStage Q;
   __shared__ uint32_t plan[kDkvWaves][kRunsPerWave * kWave];
   static_assert(sizeof(T0.rm) >= (size_t)kBlock * kBwdRow * sizeof(bf16), "the K tile of the set-up fits a staging tile");
   const int nbk = a.batch * a.G * a.nb_max;
@@ -500,15 +541,16 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
 
   // Quads alternate between the two tiles: the staging loads of quad qi + 1
   // are issued before quad qi is computed and waited for after it.  Quad
-  // qi - 1's dQ (its dS tile is complete) is computed by the B waves between
-  // their dP and the exchange of P, i.e. while the A waves compute P.
+  // qi - 1's dQ (its dS tile is complete) is computed by the B waves before
+  // their dP, while the A waves compute S, so the two waves' MFMAs share the
+  // SIMD's pipe, and the A waves' P runs beside the B waves' dP.
   const int nquads = (n + 3) / 4;
   QuadAux x;
   lds_barrier();  // the codes and the plan are written; the K tile is read
   bwd_issue_quad(T0, plan[wave], codes, 0, n, wave, lane, win_q, win_g, win_bytes, row_bytes);
   bwd_load_aux(a, x, codes, 0, n, g, R, N, M, q0);
   bwd_store_aux(T0, x);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  vmem_wait_all();
   lds_barrier();
   const float sl2 = a.scale_log2;
   auto step = [&](BwdTile& cur, BwdTile& nxt, int qi) {
@@ -519,12 +561,9 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
       bwd_load_aux(a, x, codes, qi + 1, n, g, R, N, M, q0);
       bwd_issue_quad(nxt, plan[wave], codes, qi + 1, n, wave, lane, win_q, win_g, win_bytes, row_bytes);
     }
+    if (role_b && qi > 0) bwd_dq_tiles(D, Q, ktf, kt, lane);
     f32x16 f[2];  // S (A) or dP (B), halves of 32 rows
     bwd_first_product(cur.rm[role_b ? 1 : 0], kvf, col, a32, f);
-    if (role_b && qi > 0) {
-      bwd_dq_tile(a, D, ktf, codes, qi - 1, n, kt, 0, lane, g, R);
-      bwd_dq_tile(a, D, ktf, codes, qi - 1, n, kt, 32, lane, g, R);
-    }
     bf16x8 xa[4];  // P (A) or dS (B) as the A operands of the second product
     if (!role_b) {
       // C layout: this lane's key, rows 32 rh + 8 (r / 4) + 4 a32 + r % 4;
@@ -546,7 +585,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
         }
       }
     }
-    lds_barrier();  // P is in LDS; the B waves are done with quad qi - 1's dS tile
+    lds_barrier();  // P and quad qi - 1's dQ are in LDS; the B waves are done with its dS tile
     if (role_b) {
 #pragma unroll
       for (int rh = 0; rh < 2; ++rh)
@@ -562,23 +601,24 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv(BwdKernelArgs a) {
           // dS^T for the dQ product: this lane's key, rows 32 rh + 8 q4 + 4 a32 .. +3
           const bf16x8& v = xa[2 * rh + (q4 >> 1)];
           const int o = 4 * (q4 & 1);
-          *reinterpret_cast<bf16x4*>(&D.ds[bwd_ds_off(32 * kt + col, 32 * rh + 8 * q4 + 4 * a32)]) =
-              bf16x4{v[o], v[o + 1], v[o + 2], v[o + 3]};
+          lds_store8(&D.ds[bwd_ds_off(32 * kt + col, 32 * rh + 8 * q4 + 4 * a32)], bf16x4{v[o], v[o + 1], v[o + 2], v[o + 3]});
         }
     }
     bwd_second_product(cur.rm[role_b ? 0 : 1], xa, tr_off, acc);
-    if (more) bwd_store_aux(nxt, x);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // quad qi + 1 is in LDS
-    lds_barrier();  // and quad qi's dS tile is complete
+    if (more) bwd_store_aux(nxt, x);  // before the dQ stores: its wait for the lse / delta loads then excludes them
+    if (!role_b && qi > 0) bwd_dq_store(a, Q, codes, 4 * (qi - 1) + kt, n, lane, g, R);
+    // quad qi + 1 is in LDS (an A wave's four dQ stores, issued last, may
+    // still be in flight)
+    if (!role_b && qi > 0) vmem_wait_all_but<kDqStores>(); else vmem_wait_all();
+    lds_barrier();  // and quad qi's dS tile is complete; the dQ stage is read
   };
   for (int qi = 0; qi < nquads; qi += 2) {
     step(T0, T1, qi);
     if (qi + 1 < nquads) step(T1, T0, qi + 1);
   }
-  if (role_b) {
-    bwd_dq_tile(a, D, ktf, codes, nquads - 1, n, kt, 0, lane, g, R);
-    bwd_dq_tile(a, D, ktf, codes, nquads - 1, n, kt, 32, lane, g, R);
-  }
+  if (role_b) bwd_dq_tiles(D, Q, ktf, kt, lane);
+  lds_barrier();
+  if (!role_b) bwd_dq_store(a, Q, codes, 4 * (nquads - 1) + kt, n, lane, g, R);
 
   // ---- lane column d = 32 dt + col, rows = keys 8 (r / 4) + 4 a32 + r % 4 of
   // the tile's 32.  A bucket's only chunk adds this window's contribution to
