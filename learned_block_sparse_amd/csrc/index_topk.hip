@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
   // column.  The scores of 16 consecutive blocks are stored together.
   auto finish = [&](int sb, float a0, float a1) {
     const float send = lane < 32 ? a1 : a0;
-    const float recv = shfl_xor_f(send, 32);
+    const float recv = xchg_halves_f(send);
     const float v = fmaxf(lane < 32 ? a0 : a1, recv);
     if constexpr (kSbLds) {
       s_sb[wave][sb & 15][lane] = v;
@@ -301,6 +301,10 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
               }
               __builtin_amdgcn_sched_group_barrier(0x002, kRowsPerStep, 0);  // the pooling
             }
+            // keep the next tile's fragment reads in k-step order: left free,
+            // the compiler issued k-step 0's last, so the next tile's first
+            // MFMA waited for the most recent read
+            __builtin_amdgcn_sched_barrier(0);
           }
           if (kt == 0 && s > s_lo) finish(s - 1, pm0, pm1);
           // keep each tile's MFMAs within its own step: the next tile's
@@ -327,7 +331,14 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // block s + kRing - 1 is in LDS
-    __syncthreads();
+    if constexpr (kPrefetch && kRing == 3) {
+      // every wave has read block s (its buffer is refilled next); the KS
+      // reads of block s + 1's first tile, the last LDS operations issued,
+      // may stay in flight (LDS operations complete in order)
+      asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(KS) : "memory");
+    } else {
+      __syncthreads();
+    }
     ring = ring_next;
   }
   if constexpr (kPrefetch) {

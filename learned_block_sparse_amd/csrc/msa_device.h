@@ -205,6 +205,18 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+// The value of lane l ^ 32 (the other half of the wave), by gfx950's
+// permlane32 swap: a vector-ALU exchange, so unlike a shuffle through LDS it
+// adds nothing to the LDS counter that later LDS waits would also drain
+// (probed against the LDS shuffle on all 64 lanes).
+__device__ __forceinline__ float xchg_halves_f(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(lane_id() < 32 ? r[1] : r[0]);
+#else
+  return x;
+#endif
+}
 __device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, kWave); }
 
 // 64-bit selection key: the score's bits mapped to an order-preserving
