@@ -209,14 +209,15 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_x
 // permlane32 swap: a vector-ALU exchange, so unlike a shuffle through LDS it
 // adds nothing to the LDS counter that later LDS waits would also drain
 // (probed against the LDS shuffle on all 64 lanes).
-__device__ __forceinline__ float xchg_halves_f(float x) {
+__device__ __forceinline__ uint32_t xchg_halves_u32(uint32_t x) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(lane_id() < 32 ? r[1] : r[0]);
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return lane_id() < 32 ? r[1] : r[0];
 #else
   return x;
 #endif
 }
+__device__ __forceinline__ float xchg_halves_f(float x) { return __uint_as_float(xchg_halves_u32(__float_as_uint(x))); }
 __device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, kWave); }
 
 // 64-bit selection key: the score's bits mapped to an order-preserving

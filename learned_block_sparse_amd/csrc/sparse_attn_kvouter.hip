@@ -205,6 +205,14 @@ __global__ __launch_bounds__(1024) void kvo_scan(KvoArgs a, int nbk) {
   }
 }
 
+// A selection slot's partial output: 16 heads x 128 dims in bf16, stored
+// run-major: the 16-byte run of dims 8 r .. 8 r + 7 of head h at element
+// kvo_run_off(r, h).  A run's 16 heads are adjacent (256 bytes), so the
+// attention kernel's stores (16 heads of one run per half-wave) and the
+// combine's loads (16 heads of one run per quarter-wave) each cover whole
+// cache lines; head-major rows made every access touch all 32 lines of a slot.
+__device__ __forceinline__ int kvo_run_off(int r, int h) { return (r * kRmax + h) * 8; }
+
 struct PairQ {
   bf16x8 q[kHeadDim / 16];  // B operand Q^T: column (jq, h), slots d = 16*ks + 8*a32 .. +7
   int code;                 // (row in window) << 4 | selection slot
@@ -257,7 +265,7 @@ __device__ __forceinline__ void kvo_pair(const KvoArgs& a, PairQ& P, int e_pf, i
         st[kt][r] = x;
         mx = fmaxf(mx, x);
       }
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    mx = fmaxf(mx, xchg_halves_f(mx));
     float sum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < kBlock / 32; ++kt)
@@ -267,7 +275,7 @@ __device__ __forceinline__ void kvo_pair(const KvoArgs& a, PairQ& P, int e_pf, i
         st[kt][r] = ex;
         sum += ex;
       }
-    sum += shfl_xor_f(sum, 32);
+    sum += xchg_halves_f(sum);
 
     // P^T as bf16 B operands: k-step kk covers keys 32*kt + 16*m + 8*(i/4) + 4*a32 + i%4
     // (kt = kk/2, m = kk%2), which are exactly this lane's S^T registers 8m .. 8m+7.
@@ -287,7 +295,7 @@ __device__ __forceinline__ void kvo_pair(const KvoArgs& a, PairQ& P, int e_pf, i
 
     const float inv = 1.0f / sum;
     const int64_t slot = (trel * a.G + g) * a.topk + slot_i;
-    bf16* po = a.part_o + (slot * kRmax + h) * kHeadDim;
+    bf16* po = a.part_o + slot * kRmax * kHeadDim;  // the slot's partial, run-major (kvo_run_off)
     // O^T[d][col] = V^T[d][key] P^T[key][col], 32 dims at a time
 #pragma unroll
     for (int dt = 0; dt < kHeadDim / 32; ++dt) {
@@ -309,7 +317,9 @@ __device__ __forceinline__ void kvo_pair(const KvoArgs& a, PairQ& P, int e_pf, i
         if (kk & 1) __builtin_amdgcn_sched_barrier(0);
       }
       // Lanes col and col+32 hold alternate 4-dim runs of the same 32 dims;
-      // swap halves so each lane stores two 16-byte runs of 8 dims.
+      // swap halves so each lane stores two 16-byte runs of 8 dims.  The 16
+      // heads of one run are adjacent in the partial, so each store writes
+      // whole 256-byte pieces.
       u32x2 pk[4];
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
@@ -322,11 +332,11 @@ __device__ __forceinline__ void kvo_pair(const KvoArgs& a, PairQ& P, int e_pf, i
         const u32x2 mine = a32 ? pk[2 * m + 1] : pk[2 * m];   // run this lane stores
         const u32x2 give = a32 ? pk[2 * m] : pk[2 * m + 1];   // run the partner stores
         u32x2 got;
-        got[0] = (uint32_t)__shfl_xor((int)give[0], 32, kWave);
-        got[1] = (uint32_t)__shfl_xor((int)give[1], 32, kWave);
+        got[0] = xchg_halves_u32(give[0]);
+        got[1] = xchg_halves_u32(give[1]);
         if (colok) {
           const u32x4 run = a32 ? u32x4{got[0], got[1], mine[0], mine[1]} : u32x4{mine[0], mine[1], got[0], got[1]};
-          *reinterpret_cast<u32x4*>(po + 32 * dt + 8 * (2 * m + a32)) = run;
+          *reinterpret_cast<u32x4*>(po + kvo_run_off(4 * dt + 2 * m + a32, h)) = run;
         }
       }
     }
@@ -419,7 +429,7 @@ __global__ __launch_bounds__(kKvoThreads, 2) void kvo_attn(KvoArgs a) {
 }
 
 // Fixed-order LSE combine of the selection slots: one wave per (row, group);
-// lane = (head lane/4, 32 dims at 32*(lane%4)).  The row's selection and slot
+// lane = (head lane % 16, 32 dims at 32 * (lane / 16)).  The row's selection and slot
 // LSEs are read once; the partial loads of all slots are independent.
 __global__ __launch_bounds__(256) void kvo_combine(KvoArgs a) {
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -429,7 +439,7 @@ __global__ __launch_bounds__(256) void kvo_combine(KvoArgs a) {
   const int64_t t = a.row_lo + trel;
   if (t >= a.cu_q[a.batch]) return;
   const int lane = lane_id();
-  const int h = lane >> 2, d0 = 32 * (lane & 3);
+  const int h = lane & 15, q = lane >> 4, d0 = 32 * q;
   const int R = a.Hq / a.G;
   if (h >= R) return;
   const RowInfo ri = kvo_row(a, t);
@@ -446,14 +456,14 @@ __global__ __launch_bounds__(256) void kvo_combine(KvoArgs a) {
     ls[i] = (mask & (1u << i)) ? a.part_lse[(slot0 + i) * kRmax + h] : -__builtin_inff();
     mx = fmaxf(mx, ls[i]);
   }
-  if (a.block_lse && (lane & 3) == 0) {
+  if (a.block_lse && q == 0) {
     float* bl = a.block_lse + (t * a.Hq + g * R + h) * a.topk;
     for (int i = 0; i < a.topk; ++i) bl[i] = ls[i];
   }
   if (mask == 0u) {
 #pragma unroll
     for (int j = 0; j < 32; j += 4) *reinterpret_cast<bf16x4*>(out + j) = bf16x4{bf16(0.f), bf16(0.f), bf16(0.f), bf16(0.f)};
-    if (a.lse && (lane & 3) == 0) a.lse[t * a.Hq + g * R + h] = -__builtin_inff();
+    if (a.lse && q == 0) a.lse[t * a.Hq + g * R + h] = -__builtin_inff();
     return;
   }
   float sum = 0.f;
@@ -470,10 +480,10 @@ __global__ __launch_bounds__(256) void kvo_combine(KvoArgs a) {
   for (int i = 0; i < 16; ++i) {
     const bool use = (mask >> i) & 1u;
     const float wgt = use ? expf(ls[i] - L) : 0.f;
-    const bf16* src = a.part_o + ((slot0 + (use ? i : first)) * kRmax + h) * kHeadDim + d0;
+    const bf16* src = a.part_o + (slot0 + (use ? i : first)) * kRmax * kHeadDim;
     bf16x8 v8[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v8[j] = load8(src + 8 * j);
+    for (int j = 0; j < 4; ++j) v8[j] = load8(src + kvo_run_off(4 * q + j, h));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -482,7 +492,7 @@ __global__ __launch_bounds__(256) void kvo_combine(KvoArgs a) {
 #pragma unroll
   for (int j = 0; j < 32; j += 4)
     *reinterpret_cast<bf16x4*>(out + j) = bf16x4{bf16(acc[j]), bf16(acc[j + 1]), bf16(acc[j + 2]), bf16(acc[j + 3])};
-  if (a.lse && (lane & 3) == 0) a.lse[t * a.Hq + g * R + h] = L;
+  if (a.lse && q == 0) a.lse[t * a.Hq + g * R + h] = L;
 }
 
 // Each bucket's edge codes sorted ascending (row in the window, then slot):
