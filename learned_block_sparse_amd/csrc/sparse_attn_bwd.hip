@@ -747,30 +747,42 @@ __global__ __launch_bounds__(256) void bwd_dq_combine(BwdKernelArgs a, int64_t r
   const int64_t t = a.row_lo + trel;
   if (t >= a.cu_q[a.batch]) return;
   const int lane = lane_id();
-  const int h = lane >> 2, d0 = 32 * (lane & 3);
   const int R = a.Hq / a.G;
-  if (h >= R) return;
+  // lane: dims 8 (lane % 16) .. +7 of heads lane / 16 + 4 j, j < nj, so each
+  // load (fixed j) reads 1 KB of a slot's partial and each store writes 512
+  // contiguous bytes of dq per head
+  const int hl = lane >> 4, d0 = 8 * (lane & 15);
+  const int nj = (R + 3) / 4;  // quads of heads that hold heads < R
   const int bq = bwd_find(a.cu_q, a.batch, t);
   const int64_t p = (int64_t)(a.cu_k[bq + 1] - a.cu_k[bq]) - (a.cu_q[bq + 1] - a.cu_q[bq]) + (t - a.cu_q[bq]);
   const unsigned mask = p >= 0 ? bwd_row_mask(a.block_idx + (t * a.G + g) * a.topk, a.topk, p / kBlock, a.nb_max)
                                : 0u;
   const int64_t slot0 = (trel * a.G + g) * a.topk;
-  f32x4 acc[8];
+  f32x4 acc[4][2];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 4; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int i = 0; i < a.topk; ++i) {
     if (!((mask >> i) & 1u)) continue;
-    const bf16* src = a.part_dq + ((slot0 + i) * 16 + h) * kHeadDim + d0;
+    const bf16* src = a.part_dq + ((slot0 + i) * 16 + hl) * kHeadDim + d0;
+    bf16x8 v8[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8 v8 = load8(src + 8 * j);
-      acc[2 * j] += f32x4{(float)v8[0], (float)v8[1], (float)v8[2], (float)v8[3]};
-      acc[2 * j + 1] += f32x4{(float)v8[4], (float)v8[5], (float)v8[6], (float)v8[7]};
-    }
+    for (int j = 0; j < 4; ++j)
+      if (j < nj) v8[j] = load8(src + 4 * j * kHeadDim);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < nj) {
+        acc[j][0] += f32x4{(float)v8[j][0], (float)v8[j][1], (float)v8[j][2], (float)v8[j][3]};
+        acc[j][1] += f32x4{(float)v8[j][4], (float)v8[j][5], (float)v8[j][6], (float)v8[j][7]};
+      }
   }
-  float* dst = a.dq + (t * a.Hq + g * R + h) * kHeadDim + d0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4*>(dst + 4 * j) = acc[j] * a.scale;
+  for (int j = 0; j < 4; ++j) {
+    const int h = 4 * j + hl;
+    if (h >= R) continue;
+    float* dst = a.dq + (t * a.Hq + g * R + h) * kHeadDim + d0;
+    *reinterpret_cast<f32x4*>(dst) = acc[j][0] * a.scale;
+    *reinterpret_cast<f32x4*>(dst + 4) = acc[j][1] * a.scale;
+  }
 }
 
 BwdPlan plan_bwd(int batch, int max_q_len, int max_kv_len, int Hq, int G, int topk) {
