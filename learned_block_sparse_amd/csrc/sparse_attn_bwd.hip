@@ -738,7 +738,7 @@ __device__ __forceinline__ unsigned bwd_row_mask(const int32_t* sel, int topk, i
 }
 
 // dq = scale * sum over the row's selection slots (in slot order) of the
-// partials: one wave per (row, group), lane = (head lane / 4, 32 dims).
+// partials: one wave per (row, group).
 __global__ __launch_bounds__(256) void bwd_dq_combine(BwdKernelArgs a, int64_t row_hi) {
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= (row_hi - a.row_lo) * a.G) return;
