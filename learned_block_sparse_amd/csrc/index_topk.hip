@@ -28,7 +28,8 @@
 //                     16th largest of the lane maxima (a bitwise search
 //                     counted by ballots), or the 16th best kept from earlier
 //                     rounds if larger, is a threshold; the few keys at or
-//                     above it are compacted by ballots and ranked exactly;
+//                     above it are compacted (lane offsets from one ballot
+//                     per bit of the lanes' counts) and ranked exactly;
 //                     the best k-1 and the local block are written ascending,
 //                     -1 padded.
 // Decode path (two kernels):
@@ -380,31 +381,36 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int batch, int64_t ro
 constexpr int kPreRound = 16 * kWave;     // blocks per selection round (16 keys per lane)
 constexpr int kPreCand = 16 * 16 + 16;    // candidate bound per round (see below)
 
-// Number of keys >= t among the wave's lanes, as a 32-bit scalar (a 64-bit
-// population count compared as such would go to the vector unit).
+// Number of lanes whose predicate holds: one 64-bit population count of the
+// ballot.  The empty asm hands the count on as an opaque 32-bit scalar, so
+// the comparison that follows stays a scalar 32-bit one (seen as a 64-bit
+// value it is compared on the vector unit).
 __device__ __forceinline__ int wave_count(bool pred) {
-  const uint64_t m = __ballot(pred);
-  return __builtin_popcount((uint32_t)m) + __builtin_popcount((uint32_t)(m >> 32));
+  int c = (int)__builtin_popcountll(__ballot(pred));
+  asm volatile("" : "+s"(c));
+  return c;
 }
 
-// A threshold for the kth largest of the wave's 64-bit keys (one per lane):
-// at least kth keys are >= the result, and when at least kth keys are
-// nonzero, at most kth lanes hold a key >= it unless their high words tie.
-// A bitwise binary search, counted by ballots: the high words first (the
-// largest th with kth high words >= th); only if more than kth lanes reach th
-// are the low bits searched, and among keys whose high word equals th only
-// the low `lo_bits` bits vary (selection keys hold 0xffffffff - id with
-// id < 2^lo_bits), so the bits above are set at once.  With fewer than kth
-// nonzero keys the result is no larger than any nonzero key.
-__device__ __forceinline__ uint64_t wave_kth_largest(uint64_t x, int kth, int lo_bits) {
-  const uint32_t xh = (uint32_t)(x >> 32);
+// The largest th such that at least kth of the lanes' xh are >= th (0 when
+// fewer than kth lanes hold a nonzero xh): a bitwise binary search from the
+// top bit, counted by ballots.
+__device__ __forceinline__ uint32_t wave_kth_hi(uint32_t xh, int kth) {
   uint32_t th = 0;
 #pragma unroll
   for (int b = 31; b >= 0; --b) {
     const uint32_t t = th | (1u << b);
     if (wave_count(xh >= t) >= kth) th = t;
   }
-  if (wave_count(xh >= th) <= kth) return (uint64_t)th << 32;
+  return th;
+}
+
+// Continues wave_kth_hi on the full 64-bit keys x (one per lane, high words
+// xh) when more than kth lanes reach its th: among keys whose high word
+// equals th only the low `lo_bits` bits vary (selection keys hold
+// 0xffffffff - id with id < 2^lo_bits), so the bits above are set at once
+// and the rest are searched.  The result r has at least kth keys >= r and,
+// keys being distinct, at most kth.
+__device__ __forceinline__ uint64_t wave_kth_lo(uint64_t x, uint32_t th, int kth, int lo_bits) {
   uint32_t tl = lo_bits >= 32 ? 0u : (0xffffffffu << lo_bits);
   for (int b = lo_bits - 1; b >= 0; --b) {
     const uint64_t t = ((uint64_t)th << 32) | (tl | (1u << b));
@@ -413,22 +419,94 @@ __device__ __forceinline__ uint64_t wave_kth_largest(uint64_t x, int kth, int lo
   return ((uint64_t)th << 32) | tl;
 }
 
-// One wave per (query row, group).  The scan left the row's block scores in
-// `scores`; rounds of 1024 earlier blocks (16 per lane, of which only the
-// first `nu` slices of 64 hold blocks) update the 16 best selection keys
-// (per-wave LDS, `best`):
+// One selection round over the blocks r0 .. r0 + 64 NU - 1 of a row (block
+// r0 + lane + 64 u in key u of a lane; ids >= local give the empty key 0):
 //   1. lane maxima of the round's keys; T = the threshold of their 16th
-//      largest (wave_kth_largest), raised to best[15] if that is larger, and
+//      largest (wave_kth_hi on the high words, wave_kth_lo on ties), raised to best[15] if that is larger, and
 //      to 1 (keys of real blocks are nonzero).  At least 16 keys of the round
 //      and the previous best are >= T, so every member of their top 16 is.
 //      Only lanes whose maximum reaches T hold such keys, and there are at
 //      most 16 of them: either exactly 16 lanes reach the high word of T, or
 //      T is the exact 16th largest maximum (keys are distinct), or fewer than
 //      16 lanes hold any key.  So there are at most 16 * 16 + 16 candidates;
-//   2. candidates are compacted into LDS in lane order (ballots; lanes that
-//      take nothing write to a slot of their own past the candidates) and
-//      ranked exactly (keys are distinct); ranks 0..15 become the new best.
-// The best topk - 1 plus the local block are written ascending.
+//   2. candidates are compacted into LDS lane by lane: each lane counts its
+//      keys >= T (and lanes < 16 the previous best[lane]), the lane offsets
+//      are an exclusive prefix sum of those counts built from one ballot per
+//      count bit, and every key is stored unconditionally (keys below T to a
+//      discard slot of the lane's own), so no scalar instruction is spent per
+//      key; the candidates are ranked exactly (keys are distinct); ranks
+//      0..15 become the new best.
+// NU is the round's number of 64-block slices rounded up to a power of two,
+// so the loops have no per-slice branches.
+template <int NU>
+__device__ __forceinline__ void sel_round(const float* __restrict__ sc, int r0, int local, int lo_bits, int lane,
+                                          uint64_t* cand, uint64_t* best) {
+  float v[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) v[u] = sc[min(r0 + lane + kWave * u, local - 1)];
+  uint64_t k[NU];
+  uint32_t mxh = 0;  // high word of the lane's largest key
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int c = r0 + lane + kWave * u;
+    k[u] = c < local ? sel_key(v[u], c) : 0;
+    mxh = max(mxh, (uint32_t)(k[u] >> 32));
+  }
+  const uint32_t th = wave_kth_hi(mxh, 16);
+  uint64_t t_round = (uint64_t)th << 32;
+  if (wave_count(mxh >= th) > 16) {
+    // high words tie at th: search the low bits of the exact lane maxima
+    uint64_t mx = 0;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) mx = k[u] > mx ? k[u] : mx;
+    t_round = wave_kth_lo(mx, th, 16, lo_bits);
+  }
+  const uint64_t b15 = best[15];
+  uint64_t T = t_round > b15 ? t_round : b15;
+  T = T > 1 ? T : 1;
+  const uint64_t x = lane < 16 ? best[lane] : 0;
+  int cnt = x >= T ? 1 : 0;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) cnt += k[u] >= T ? 1 : 0;
+  // exclusive prefix of cnt (<= NU + 1) over the lanes, one ballot per bit
+  constexpr int kBits = NU >= 16 ? 5 : NU >= 8 ? 4 : NU >= 4 ? 3 : 2;
+  int off = 0;
+#pragma unroll
+  for (int j = 0; j < kBits; ++j) {
+    const uint64_t m = __ballot((cnt >> j) & 1);
+    off += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0)) << j;
+  }
+  int n = __builtin_amdgcn_readlane(off + cnt, kWave - 1);
+  uint64_t* discard = cand + kPreCand + 4 + lane;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const bool take = k[u] >= T;
+    *(take ? cand + min(off, kPreCand - 1) : discard) = k[u];  // off < kPreCand (bound above)
+    off += take ? 1 : 0;
+  }
+  *(x >= T ? cand + min(off, kPreCand - 1) : discard) = x;
+  n = min(n, kPreCand);
+  if (lane < 4) cand[n + lane] = 0;  // pads the rank loop to a multiple of 4
+  // exact ranks of the candidates, 64 at a time (usually one pass), 4
+  // candidates per LDS read pair
+  for (int i0 = 0; i0 < n; i0 += kWave) {
+    const bool has = i0 + lane < n;
+    const uint64_t mine = has ? cand[i0 + lane] : 0;
+    int rank = 0;
+    for (int j = 0; j < n; j += 4) {
+      const u64x2 c01 = *reinterpret_cast<const u64x2*>(cand + j);
+      const u64x2 c23 = *reinterpret_cast<const u64x2*>(cand + j + 2);
+      rank += (c01.x > mine ? 1 : 0) + (c01.y > mine ? 1 : 0) + (c23.x > mine ? 1 : 0) + (c23.y > mine ? 1 : 0);
+    }
+    if (has && rank < 16) best[rank] = mine;
+  }
+  if (lane < 16 && lane >= n) best[lane] = 0;
+}
+
+// One wave per (query row, group).  The scan left the row's block scores in
+// `scores`; rounds of 1024 earlier blocks (16 per lane) update the 16 best
+// selection keys (per-wave LDS, `best`, see sel_round).  The best topk - 1
+// plus the local block are written ascending.
 __global__ __launch_bounds__(256) void idx_select_prefill(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int64_t rows_bound, int G,
     int topk, int nb_stride, const float* __restrict__ scores, int32_t* __restrict__ block_idx) {
@@ -457,64 +535,12 @@ __global__ __launch_bounds__(256) void idx_select_prefill(
   if (lane < 16) best[lane] = 0;
   const int lo_bits = local > 1 ? 32 - __clz(local - 1) : 0;  // bits of the largest earlier id
   for (int r0 = 0; r0 < local; r0 += kPreRound) {
-    const int nu = min(16, (local - r0 + kWave - 1) / kWave);  // slices holding blocks (wave-uniform)
-    float v[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int c = r0 + lane + kWave * u;
-      if (u < nu) v[u] = sc[min(c, local - 1)];
-    }
-    uint64_t k16[16], mx = 0;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int c = r0 + lane + kWave * u;
-      k16[u] = 0;
-      if (u < nu) {
-        const uint64_t key = sel_key(v[u], c);
-        k16[u] = c < local ? key : 0;
-        mx = k16[u] > mx ? k16[u] : mx;
-      }
-    }
-    const uint64_t t_round = wave_kth_largest(mx, 16, lo_bits);
-    const uint64_t b15 = best[15];
-    uint64_t T = t_round > b15 ? t_round : b15;
-    T = T > 1 ? T : 1;
-    // compact the candidates (keys >= T) into LDS, lane order within each u
-    int n = 0;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      if (u < nu) {
-        const bool take = k16[u] >= T;
-        const uint64_t m = __ballot(take);
-        const int slot = n + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        cand[take ? min(slot, kPreCand - 1) : kPreCand + 4 + lane] = k16[u];  // slot < kPreCand (bound above)
-        n += __builtin_popcount((uint32_t)m) + __builtin_popcount((uint32_t)(m >> 32));
-      }
-    }
-    {
-      const uint64_t x = lane < 16 ? best[lane] : 0;
-      const bool take = x >= T;
-      const uint64_t m = __ballot(take);
-      const int slot = n + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-      cand[take ? min(slot, kPreCand - 1) : kPreCand + 4 + lane] = x;
-      n += __builtin_popcount((uint32_t)m) + __builtin_popcount((uint32_t)(m >> 32));
-    }
-    n = min(n, kPreCand);
-    if (lane < 4) cand[n + lane] = 0;  // pads the rank loop to a multiple of 4
-    // exact ranks of the candidates, 64 at a time (usually one pass), 4
-    // candidates per LDS read pair
-    for (int i0 = 0; i0 < n; i0 += kWave) {
-      const bool has = i0 + lane < n;
-      const uint64_t mine = has ? cand[i0 + lane] : 0;
-      int rank = 0;
-      for (int j = 0; j < n; j += 4) {
-        const u64x2 c01 = *reinterpret_cast<const u64x2*>(cand + j);
-        const u64x2 c23 = *reinterpret_cast<const u64x2*>(cand + j + 2);
-        rank += (c01.x > mine ? 1 : 0) + (c01.y > mine ? 1 : 0) + (c23.x > mine ? 1 : 0) + (c23.y > mine ? 1 : 0);
-      }
-      if (has && rank < 16) best[rank] = mine;
-    }
-    if (lane < 16 && lane >= n) best[lane] = 0;
+    const int nu = (local - r0 + kWave - 1) / kWave;  // slices holding blocks (wave-uniform)
+    if (nu > 8) sel_round<16>(sc, r0, local, lo_bits, lane, cand, best);
+    else if (nu > 4) sel_round<8>(sc, r0, local, lo_bits, lane, cand, best);
+    else if (nu > 2) sel_round<4>(sc, r0, local, lo_bits, lane, cand, best);
+    else if (nu > 1) sel_round<2>(sc, r0, local, lo_bits, lane, cand, best);
+    else sel_round<1>(sc, r0, local, lo_bits, lane, cand, best);
   }
   const int found = min(local, topk - 1);
   const uint64_t mk = lane < 16 ? best[lane] : 0;

@@ -226,7 +226,7 @@ __device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v
 // Every finite score maps to a non-zero high word; 0 is "no entry".
 __device__ __forceinline__ uint64_t sel_key(float s, int id) {
   const uint32_t b = __float_as_uint(s);
-  const uint32_t hi = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  const uint32_t hi = b ^ (uint32_t)(((int32_t)b >> 31) | INT32_MIN);  // ~b if negative, else b | 2^31
   return ((uint64_t)hi << 32) | (uint32_t)(0xffffffffu - (uint32_t)id);
 }
 __device__ __forceinline__ int sel_key_id(uint64_t k) { return (int)(0xffffffffu - (uint32_t)k); }
