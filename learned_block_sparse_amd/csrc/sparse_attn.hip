@@ -327,7 +327,10 @@ __global__ __launch_bounds__(kAttnThreads, sizeof(T) == 2 ? 2 : 1) void sparse_a
 
 // Two-phase combine: lse = ln sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s,
 // summed in split order (deterministic, no atomics); empty chunks (lse_s =
-// -inf) are skipped.  32 threads per (row, head), 4 dims each.
+// -inf) are skipped.  32 threads per (row, head), 4 dims each.  Every
+// chunk's LSE and partial output are requested at once, before the row
+// count is known (rows past it are in the workspace but never stored), so
+// the kernel waits for one memory round trip.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_combine(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_lse,
@@ -337,15 +340,22 @@ __global__ __launch_bounds__(256) void attn_combine(const float* __restrict__ pa
   const int64_t rh = (int64_t)blockIdx.x * 8 + threadIdx.x / 32;
   const int d0 = (threadIdx.x % 32) * 4;
   if (rh >= rows_bound * Hq) return;
-  const int64_t t = rh / Hq;
-  const int64_t nrows = cu_q ? cu_q[batch] : batch;
-  if (t >= nrows) return;
   const float* pl = part_lse + rh * nsplit;
+  const float* po = part_o + rh * nsplit * kHeadDim + d0;
   float ls[16];
+  f32x4 ov[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int sc = min(s, nsplit - 1);  // in bounds; chunks past nsplit are masked below
+    ls[s] = pl[sc];
+    ov[s] = *reinterpret_cast<const f32x4*>(po + sc * kHeadDim);
+  }
+  const int64_t nrows = cu_q ? cu_q[batch] : batch;
+  if (rh / Hq >= nrows) return;
   float mx = -__builtin_inff();
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
-    ls[s] = s < nsplit ? pl[s] : -__builtin_inff();
+    if (s >= nsplit) ls[s] = -__builtin_inff();
     mx = fmaxf(mx, ls[s]);
   }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -357,8 +367,7 @@ __global__ __launch_bounds__(256) void attn_combine(const float* __restrict__ pa
     L = mx + logf(sum);
 #pragma unroll
     for (int s = 0; s < 16; ++s)
-      if (ls[s] != -__builtin_inff())
-        acc += expf(ls[s] - L) * *reinterpret_cast<const f32x4*>(part_o + (rh * nsplit + s) * kHeadDim + d0);
+      if (ls[s] != -__builtin_inff()) acc += expf(ls[s] - L) * ov[s];
   }
   store4<T>(out + rh * kHeadDim + d0, acc[0], acc[1], acc[2], acc[3]);
   if (lse && d0 == 0) lse[rh] = L;
