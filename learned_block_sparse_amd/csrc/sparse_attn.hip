@@ -74,12 +74,31 @@ __device__ __forceinline__ void store4<float>(float* p, float a, float b, float 
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
+// Eight K/V elements in registers as loaded: the compute-type fragment, or
+// for E4M3 storage the 8 raw bytes, widened to bf16 where they are used (so a
+// block's K and V fit in registers together).
+template <typename T, typename TKV> struct KvReg { using type = frag8<T>; };
+template <> struct KvReg<bf16, fp8e4m3> { using type = u32x2; };
+template <typename T, typename TKV>
+using kvreg = typename KvReg<T, TKV>::type;
+
+template <typename T, typename TKV>
+__device__ __forceinline__ kvreg<T, TKV> load_kvreg(const TKV* p) {
+  if constexpr (sizeof(TKV) == 1) return *reinterpret_cast<const u32x2*>(p);
+  else return load8(p);
+}
+template <typename T, typename R>
+__device__ __forceinline__ frag8<T> kv_op(const R& r) {
+  if constexpr (sizeof(R) == 8) return widen8_e4m3(r);
+  else return r;
+}
+
 // V rows key0 + 32ks .. +31 of one block into registers, as the units of the
 // transposed staging: unit u = (key quad u%8, d octet u/8); lane handles
 // u = lane and lane + 64.  Rows past p clamp to p (their P is 0).
 template <typename T, typename TKV>
 __device__ __forceinline__ void load_v_chunk(const TKV* vseq, int64_t row_stride, int64_t key0, int64_t p, int ks,
-                                             int lane, frag8<T> (&r)[2][4]) {
+                                             int lane, kvreg<T, TKV> (&r)[2][4]) {
 #pragma unroll
   for (int uu = 0; uu < 2; ++uu) {
     const int u = lane + 64 * uu;
@@ -88,7 +107,7 @@ __device__ __forceinline__ void load_v_chunk(const TKV* vseq, int64_t row_stride
     for (int jj = 0; jj < 4; ++jj) {
       int64_t key = key0 + 32 * ks + 4 * kq + jj;
       if (key > p) key = p;
-      r[uu][jj] = load8_kv<T>(vseq + key * row_stride + 8 * o8);
+      r[uu][jj] = load_kvreg<T>(vseq + key * row_stride + 8 * o8);
     }
   }
 }
@@ -176,38 +195,36 @@ __global__ __launch_bounds__(kAttnThreads, sizeof(T) == 2 ? 2 : 1) void sparse_a
       // the first V chunk is requested right behind the K rows, and each
       // later chunk while the previous one is staged and multiplied, so a
       // block costs about two memory round trips instead of five.
-      frag8<T> kfr[kBlock / 16][kHeadDim / 32];
+      kvreg<T, TKV> kfr[kBlock / 16][kHeadDim / 32];
 #pragma unroll
       for (int kt = 0; kt < kBlock / 16; ++kt) {
         int64_t key = key0 + 16 * kt + h;   // A operand row = lane % 16
         if (key > p) key = p;               // stay inside the sequence; masked below
         const TKV* kp = kseq + key * row_stride + 8 * a;
 #pragma unroll
-        for (int ds = 0; ds < kHeadDim / 32; ++ds) kfr[kt][ds] = load8_kv<T>(kp + 32 * ds);
+        for (int ds = 0; ds < kHeadDim / 32; ++ds) kfr[kt][ds] = load_kvreg<T>(kp + 32 * ds);
       }
-      // E4M3 K/V: the four V chunks (128 keys) are all requested right after
-      // the score MFMAs, into the registers the K rows free, so a block costs
-      // two memory round trips (K, then V) and the kernel still fits two
-      // waves per SIMD (30.7 against 42.5 us for the 1M-context decode
-      // batch).  Otherwise two chunk buffers: the first chunk is requested
-      // with K and each later one a chunk ahead (for bf16 K/V the four-chunk
-      // form measured no faster and spills).
+      // E4M3 K/V: the raw bytes of the block's K rows and of all four V
+      // chunks (128 keys) are requested together, one memory round trip per
+      // block, and still fit two waves per SIMD (widened to bf16 only as
+      // they are used).  Otherwise two chunk buffers: the first chunk is
+      // requested with K and each later one a chunk ahead (for bf16 K/V the
+      // four-chunk form measured no faster and spills).
       constexpr int kVBufs = sizeof(TKV) == 1 ? kBlock / 32 : 2;
-      frag8<T> vbuf[kVBufs][2][4];
-      if constexpr (kVBufs == 2) load_v_chunk<T>(vseq, row_stride, key0, p, 0, lane, vbuf[0]);
+      kvreg<T, TKV> vbuf[kVBufs][2][4];
+      if constexpr (kVBufs == 2) {
+        load_v_chunk<T>(vseq, row_stride, key0, p, 0, lane, vbuf[0]);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < kBlock / 32; ++ks) load_v_chunk<T>(vseq, row_stride, key0, p, ks, lane, vbuf[ks]);
+      }
       f32x4 st[kBlock / 16];
 #pragma unroll
       for (int kt = 0; kt < kBlock / 16; ++kt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ds = 0; ds < kHeadDim / 32; ++ds) acc = mma16(kfr[kt][ds], qf[ds], acc);
+        for (int ds = 0; ds < kHeadDim / 32; ++ds) acc = mma16(kv_op<T>(kfr[kt][ds]), qf[ds], acc);
         st[kt] = acc;
-      }
-      if constexpr (kVBufs == kBlock / 32) {
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks < kBlock / 32; ++ks) load_v_chunk<T>(vseq, row_stride, key0, p, ks, lane, vbuf[ks]);
-        __builtin_amdgcn_sched_barrier(0);
       }
 
       // ---- online softmax (log2 units)
@@ -259,7 +276,9 @@ __global__ __launch_bounds__(kAttnThreads, sizeof(T) == 2 ? 2 : 1) void sparse_a
         for (int uu = 0; uu < 2; ++uu) {
           const int u = lane + 64 * uu;
           const int kq = u & 7, o8 = u >> 3;
-          const frag8<T>(&r4)[4] = vbuf[ks % kVBufs][uu];
+          frag8<T> r4[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) r4[jj] = kv_op<T>(vbuf[ks % kVBufs][uu][jj]);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             T* dst = vt + (8 * o8 + e) * V::kStride + 4 * kq;
