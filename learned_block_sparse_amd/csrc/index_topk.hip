@@ -422,7 +422,9 @@ __device__ __forceinline__ uint64_t wave_kth_lo(uint64_t x, uint32_t th, int kth
 // One selection round over the blocks r0 .. r0 + 64 NU - 1 of a row (block
 // r0 + lane + 64 u in key u of a lane; ids >= local give the empty key 0):
 //   1. lane maxima of the round's keys; T = the threshold of their 16th
-//      largest (wave_kth_hi on the high words, wave_kth_lo on ties), raised to best[15] if that is larger, and
+//      largest (wave_kth_hi on the high words, wave_kth_lo on ties), raised
+//      to best[15] if that is larger (taken at once when fewer than 16 lanes
+//      reach best[15], as the 16th largest maximum is then below it), and
 //      to 1 (keys of real blocks are nonzero).  At least 16 keys of the round
 //      and the previous best are >= T, so every member of their top 16 is.
 //      Only lanes whose maximum reaches T hold such keys, and there are at
@@ -452,17 +454,33 @@ __device__ __forceinline__ void sel_round(const float* __restrict__ sc, int r0, 
     k[u] = c < local ? sel_key(v[u], c) : 0;
     mxh = max(mxh, (uint32_t)(k[u] >> 32));
   }
-  const uint32_t th = wave_kth_hi(mxh, 16);
-  uint64_t t_round = (uint64_t)th << 32;
-  if (wave_count(mxh >= th) > 16) {
-    // high words tie at th: search the low bits of the exact lane maxima
-    uint64_t mx = 0;
+  // best[15] is the same for every lane: read it as a scalar
+  const uint64_t b15l = best[15];
+  const uint64_t b15 = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b15l >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b15l);
+  uint64_t T = b15;
+  // Later rounds: when fewer than 16 lanes hold a key >= best[15], the 16th
+  // largest lane maximum is below it, so T = best[15] without the search
+  // (usually so once a full round has been seen).
+  bool search = true;
+  if (b15 != 0) {
+    bool reach = false;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) mx = k[u] > mx ? k[u] : mx;
-    t_round = wave_kth_lo(mx, th, 16, lo_bits);
+    for (int u = 0; u < NU; ++u) reach = reach || k[u] >= b15;
+    search = wave_count(reach) >= 16;
   }
-  const uint64_t b15 = best[15];
-  uint64_t T = t_round > b15 ? t_round : b15;
+  if (search) {
+    const uint32_t th = wave_kth_hi(mxh, 16);
+    uint64_t t_round = (uint64_t)th << 32;
+    if (wave_count(mxh >= th) > 16) {
+      // high words tie at th: search the low bits of the exact lane maxima
+      uint64_t mx = 0;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) mx = k[u] > mx ? k[u] : mx;
+      t_round = wave_kth_lo(mx, th, 16, lo_bits);
+    }
+    T = t_round > b15 ? t_round : b15;
+  }
   T = T > 1 ? T : 1;
   const uint64_t x = lane < 16 ? best[lane] : 0;
   int cnt = x >= T ? 1 : 0;
