@@ -391,15 +391,20 @@ __device__ __forceinline__ int wave_count(bool pred) {
   return c;
 }
 
-// The largest th such that at least kth of the lanes' xh are >= th (0 when
-// fewer than kth lanes hold a nonzero xh): a bitwise binary search from the
-// top bit, counted by ballots.
+// A th such that at least kth of the lanes' xh are >= th: a bitwise binary
+// search from the top bit, counted by ballots, for the largest such th (0 when
+// fewer than kth lanes hold a nonzero xh).  It stops early once exactly kth
+// lanes reach th: those are then the kth largest, and th is below every one
+// of them, which is all a threshold needs (it happens as soon as th passes
+// the (kth+1)-th largest, typically half-way down the bits).
 __device__ __forceinline__ uint32_t wave_kth_hi(uint32_t xh, int kth) {
   uint32_t th = 0;
 #pragma unroll
   for (int b = 31; b >= 0; --b) {
     const uint32_t t = th | (1u << b);
-    if (wave_count(xh >= t) >= kth) th = t;
+    const int c = wave_count(xh >= t);
+    if (c >= kth) th = t;
+    if (c == kth) break;
   }
   return th;
 }

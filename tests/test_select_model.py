@@ -5,8 +5,8 @@ What is restated: 64-bit selection keys (order-preserving score bits above the
 inverted block id, 0 = no block); rounds of 1024 earlier blocks, block
 r0 + lane + 64 u in key u of a lane, with the round's slice count rounded up
 to a power of two; the threshold T = the 16th largest lane maximum (a
-bitwise search on the high words, the low bits an id can have only when high
-words tie), raised to best[15], or best[15] at once when fewer than 16 lanes
+bitwise search on the high words that stops once exactly 16 lanes reach it,
+the low bits an id can have only when high words tie), raised to best[15], or best[15] at once when fewer than 16 lanes
 reach it; candidates compacted lane by lane at offsets from a prefix sum built
 from one ballot per bit of the lanes' counts; exact ranks.  The checks: the
 best 16 after every row equal the brute-force best 16 (score descending, id
@@ -35,11 +35,16 @@ def key_id(k):
 
 
 def kth_hi(xh, kth):
+    """A th with at least kth of xh >= th; the search stops once exactly kth
+    reach it (those are the kth largest and th is below all of them)."""
     th = 0
     for b in range(31, -1, -1):
         t = th | (1 << b)
-        if sum(1 for x in xh if x >= t) >= kth:
+        c = sum(1 for x in xh if x >= t)
+        if c >= kth:
             th = t
+        if c == kth:
+            break
     return th
 
 
