@@ -227,6 +227,25 @@ def test_prefill_attention_handmade_selection(msa, synth, oracle_lib, splits):
     compare_outputs(out, lse, ref_out, ref_lse, wl.dtype, "prefill hand-made")
 
 
+def test_decode_tie_dense_index_inputs(msa, synth, oracle_lib):
+    """Decode rows whose index values lie in {-1/8, 0, 1/8}: block scores tie
+    often, so the decode selection's search over the high words of the thread
+    maxima ends on ties, its exact fallback runs, and the lowest-id tie-break
+    decides most selections."""
+    wl = synth.WORKLOADS["decode_1m"]
+    ctx = [129, 2049, 20000, 70001]
+    say(f"[parity] tie-dense decode ctx={ctx}")
+    d = synth.decode_inputs(wl, device="cuda", seed=46, ctx_lens=ctx)
+    g = torch.Generator(device="cuda").manual_seed(47)
+    q = (torch.randint(-1, 2, d["q_idx"].shape, generator=g, device="cuda").float() / 8).bfloat16()
+    k = (torch.randint(-1, 2, d["k_idx"].shape, generator=g, device="cuda").float() / 8).bfloat16()
+    ids = msa.msa_index_topk(q, k, d["cu_seqlens_q"], d["cu_seqlens_k"], 1, max(ctx), wl.block_size, wl.topk)
+    torch.cuda.synchronize()
+    _, kstart, pos = oracle_lib.rows_decode(d["k_offsets_host"], ctx)
+    ref = oracle_lib.index_topk(host(q), host(k), kstart, pos, np.arange(len(ctx)), wl.block_size, wl.topk)
+    compare_ids(ids, ref, "tie-dense decode")
+
+
 def test_decode_and_prefill_paths_agree(msa, synth):
     """The decode index path (block scores + select) and the prefill path
     (chunked scan + merge) give the same ids for the same newest tokens."""
