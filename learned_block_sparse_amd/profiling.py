@@ -185,12 +185,15 @@ def counters_main(argv):
     from learned_block_sparse_amd import build
     per = collections.defaultdict(lambda: collections.defaultdict(float))
     disp = collections.defaultdict(set)
+    dur = collections.defaultdict(dict)  # kernel -> dispatch -> ns
     for r in _rows(a.dir):
         n = KERNEL_NAMES.get(r["Kernel_Name"], r["Kernel_Name"])
         if not n.startswith(OURS):
             continue
         per[n][r["Counter_Name"]] += float(r["Counter_Value"])
         disp[n].add(r["Dispatch_Id"])
+        if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+            dur[n][r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     tab = []
     for n, c in per.items():
         nd = len(disp[n])
@@ -198,17 +201,22 @@ def counters_main(argv):
         busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / nd / (kc * 1024) if kc else 0.0
         wait = c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"] if c["SQ_WAVE_CYCLES"] else 0.0
         conf = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"] if c["SQ_LDS_IDX_ACTIVE"] else 0.0
-        tab.append((n, nd, kc, busy, wait, conf))
+        ns = sum(dur[n].values()) / len(dur[n]) if dur[n] else 0.0
+        ghz = kc / ns if ns > 0 else 0.0
+        tab.append((n, nd, kc, busy, wait, conf, ghz))
     tab.sort(key=lambda x: -x[2])
     lines = [f"# {a.title}", "", "Command (repository root, GPU host):", "  " + a.command, ""]
     lines += a.note + ([""] if a.note else [])
     lines.append("Columns: kernel cycles = SQ_BUSY_CYCLES / 32 (the counter sums over the 32 shader engines);")
     lines.append("mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (kernel cycles x 1024 SIMDs); wait = SQ_WAIT_ANY /")
-    lines.append("SQ_WAVE_CYCLES (share of wave time spent waiting); lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.")
+    lines.append("SQ_WAVE_CYCLES (share of wave time spent waiting); lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE;")
+    lines.append("GHz = kernel cycles / the dispatch's duration (its timestamps): the shader clock while the kernel ran, less any")
+    lines.append("time whole shader engines sat idle (MFMA busy x kernel cycles x 1024 SIMDs x 1024 FLOP accounts for a bf16 MFMA")
+    lines.append("kernel's FLOPs, so these are shader clock cycles).")
     lines.append("")
-    lines.append(f"{'kernel':32s} {'disp':>5s} {'kcycles':>10s} {'mfma_busy':>10s} {'wait':>7s} {'lds_conflict':>13s}")
-    for n, nd, kc, b, w, cf in tab:
-        lines.append(f"{n[:32]:32s} {nd:5d} {kc:10.3g} {100 * b:9.1f}% {100 * w:6.1f}% {100 * cf:12.1f}%")
+    lines.append(f"{'kernel':32s} {'disp':>5s} {'kcycles':>10s} {'mfma_busy':>10s} {'wait':>7s} {'lds_conflict':>13s} {'GHz':>6s}")
+    for n, nd, kc, b, w, cf, ghz in tab:
+        lines.append(f"{n[:32]:32s} {nd:5d} {kc:10.3g} {100 * b:9.1f}% {100 * w:6.1f}% {100 * cf:12.1f}% {ghz:6.2f}")
     lines.append("")
     lines.append(f"kernel source digest: {build.source_digest()}")
     with open(a.out, "w") as f:
