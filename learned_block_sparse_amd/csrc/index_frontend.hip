@@ -194,7 +194,8 @@ __device__ __forceinline__ FeTile fe_tile(int G) {  // tile size: the kernel's o
 
 // acc[rt][ct] = C^T tile: rows = the head's dims 32*rt + .., columns = the
 // wave's tokens t0 + 32*ct + ...  (see the schedule at the top of the file).
-template <typename T, int DI, int CTW>
+// PD: chunks of x requested ahead of the one being multiplied.
+template <typename T, int DI, int CTW, int PD = 1>
 __device__ __forceinline__ void fe_gemm(const FeArgs& a, const T* w, int64_t t0, f32x16 (&acc)[DI / 32][CTW],
                                         T (&w_lds)[2][DI * FeLds<T>::stride]) {
   constexpr int RT = DI / 32;             // row tiles (32 dims each)
@@ -211,7 +212,7 @@ __device__ __forceinline__ void fe_gemm(const FeArgs& a, const T* w, int64_t t0,
     xp[ct] = x + (t < a.total ? t : a.total - 1) * a.d_model + (kFeKc / 2) * h;
   }
 
-  frag8<T> xr[CTW][kFeS], xn[CTW][kFeS];
+  frag8<T> xr[CTW][kFeS], xn[PD][CTW][kFeS];
   u32x4 wr[PIECES];
   auto load_w = [&](int kc) {
 #pragma unroll
@@ -244,14 +245,15 @@ __device__ __forceinline__ void fe_gemm(const FeArgs& a, const T* w, int64_t t0,
   const int nc = a.d_model / kFeKc;
   load_w(0);
   load_x(xr, 0);
+#pragma unroll
+  for (int p = 0; p + 1 < PD; ++p)
+    if (p + 1 < nc) load_x(xn[p], (p + 1) * kFeKc);
   store_w(0);
   __syncthreads();
   for (int c = 0; c < nc; ++c) {
     const bool more = c + 1 < nc;
-    if (more) {
-      load_w((c + 1) * kFeKc);
-      load_x(xn, (c + 1) * kFeKc);
-    }
+    if (more) load_w((c + 1) * kFeKc);
+    if (c + PD < nc) load_x(xn[PD - 1], (c + PD) * kFeKc);
     const T* wl = w_lds[c & 1];
 #pragma unroll
     for (int s = 0; s < kFeS; ++s)
@@ -267,7 +269,11 @@ __device__ __forceinline__ void fe_gemm(const FeArgs& a, const T* w, int64_t t0,
 #pragma unroll
       for (int ct = 0; ct < CTW; ++ct)
 #pragma unroll
-        for (int s = 0; s < kFeS; ++s) xr[ct][s] = xn[ct][s];
+        for (int s = 0; s < kFeS; ++s) {
+          xr[ct][s] = xn[0][ct][s];
+#pragma unroll
+          for (int p = 0; p + 1 < PD; ++p) xn[p][ct][s] = xn[p + 1][ct][s];
+        }
     }
     __syncthreads();
   }
@@ -291,7 +297,7 @@ __global__ __launch_bounds__(kFeThreads, sizeof(T) == 2 ? 2 : 1) void index_fron
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int64_t t0 = ft.tile * kFeTok + wave * kFeTokWave;
   f32x16 acc[DI / 32][kFeCt];
-  fe_gemm<T, DI, kFeCt>(a, w, t0, acc, w_lds);
+  fe_gemm<T, DI, kFeCt, 2>(a, w, t0, acc, w_lds);  // x two chunks ahead (three: no faster, four: spills)
   fe_inv_freq(inv_freq, a.rope_dim, a.log2_theta);
   const int64_t tw = t0 + (lane & 31);
   fe_finish<TO, DI, 0, kFeCt>(acc, a, ft.head, tw, lane >> 5, inv_freq);
