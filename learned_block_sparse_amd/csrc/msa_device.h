@@ -269,11 +269,14 @@ __device__ __forceinline__ void write_selection(int mine, int found, int local, 
                                                 int32_t* out) {
   const int lane = lane_id();
   int v = lane < found ? mine : (lane == found ? local : 0x7fffffff);
-  const int cnt = found + 1;
+  const int cnt = found + 1;  // <= 16
+  // rank among the first cnt lanes, each value read as a scalar (no LDS
+  // round trip per lane, unlike a shuffle)
   int rank = 0;
-  for (int j = 0; j < cnt; ++j) {
-    int o = __shfl(v, j, kWave);
-    rank += (o < v) ? 1 : 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int o = __builtin_amdgcn_readlane(v, j);
+    rank += (j < cnt && o < v) ? 1 : 0;
   }
   if (lane < cnt) out[rank] = v;
   if (lane >= cnt && lane < topk) out[lane] = -1;
