@@ -98,7 +98,7 @@ template <typename T, int DI>
 __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, int G, int qw, int nsub, int max_qblocks, int chunk,
-    int max_chunks, int nb_stride, float* __restrict__ scores) {
+    int max_chunks, int nb_stride, int n_items, float* __restrict__ scores) {
   using L = ScanLds<T, DI>;
   using Mm = ScanMma<T>;
   constexpr int KS = DI / Mm::kStep;  // MFMA contraction steps
@@ -113,254 +113,267 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
   __shared__ __attribute__((aligned(16))) char lds[kRing * L::kBufBytes];
   __shared__ float s_sb[kSbLds ? kScanThreads / kWave : 1][16][kWave];
 
-  // Decode the workgroup: query block fastest (latest, i.e. heaviest, first),
-  // then query slice, then key chunk, then sequence.  Workgroups are handed
-  // to the 8 XCDs in turn by id, and each XCD runs its own share on its own
-  // CUs, so neighbouring ids must carry similar work: with the key chunk
-  // fastest and 2 or 4 chunks, an XCD received one chunk index only (all
-  // full chunks on some XCDs, all short last chunks on others).
-  int bid = blockIdx.x;
-  const int slot = max_qblocks - 1 - (bid % max_qblocks);  bid /= max_qblocks;
-  const int sub = bid % nsub;       bid /= nsub;
-  const int ch = bid % max_chunks;
-  const int b = bid / max_chunks;
+  // The plan may pair items: item k and its mirror n_items - 1 - k on one
+  // workgroup, one after the other.  With the heaviest query blocks first
+  // in each key chunk, a mirror pair sums to about the same work everywhere
+  // (for one causal sequence cut into two chunks, a full first chunk plus an
+  // empty last one, or a short first chunk plus a long last one), so one
+  // round of workgroups does a call that would otherwise take one and a half.
+  const int n_pass = n_items > (int)gridDim.x ? 2 : 1;
+  for (int pass = 0; pass < n_pass; ++pass) {
+    if (pass == 1) {
+      if (n_items - 1 - (int)blockIdx.x == (int)blockIdx.x) break;  // the middle item of an odd count
+      __syncthreads();  // every wave is done with the ring buffers and the score stage
+    }
+    // Decode the workgroup: query block fastest (latest, i.e. heaviest, first),
+    // then query slice, then key chunk, then sequence.  Workgroups are handed
+    // to the 8 XCDs in turn by id, and each XCD runs its own share on its own
+    // CUs, so neighbouring ids must carry similar work: with the key chunk
+    // fastest and 2 or 4 chunks, an XCD received one chunk index only (all
+    // full chunks on some XCDs, all short last chunks on others).
+    int bid = pass == 0 ? (int)blockIdx.x : n_items - 1 - (int)blockIdx.x;
+    const int slot = max_qblocks - 1 - (bid % max_qblocks);  bid /= max_qblocks;
+    const int sub = bid % nsub;       bid /= nsub;
+    const int ch = bid % max_chunks;
+    const int b = bid / max_chunks;
 
-  const int q0 = cu_q[b], M = cu_q[b + 1] - q0;
-  const int k0 = cu_k[b], N = cu_k[b + 1] - k0;
-  if (M <= 0 || N <= 0) return;
-  const int pfirst = N - M > 0 ? N - M : 0;  // first position that has keys
-  const int c = pfirst / kBlock + slot;      // this workgroup's query block
-  if (c * kBlock >= N) return;
-  const int plo = max(c * kBlock, pfirst) + sub * qw;
-  const int phi = min(min((c + 1) * kBlock, N), plo + qw);
-  if (plo >= phi) return;
-  const int s_lo = ch * chunk;
-  const int s_hi = min(s_lo + chunk, c);  // scan earlier blocks only
-  if (s_lo >= s_hi) return;
+    const int q0 = cu_q[b], M = cu_q[b + 1] - q0;
+    const int k0 = cu_k[b], N = cu_k[b + 1] - k0;
+    if (M <= 0 || N <= 0) continue;
+    const int pfirst = N - M > 0 ? N - M : 0;  // first position that has keys
+    const int c = pfirst / kBlock + slot;      // this workgroup's query block
+    if (c * kBlock >= N) continue;
+    const int plo = max(c * kBlock, pfirst) + sub * qw;
+    const int phi = min(min((c + 1) * kBlock, N), plo + qw);
+    if (plo >= phi) continue;
+    const int s_lo = ch * chunk;
+    const int s_hi = min(s_lo + chunk, c);  // scan earlier blocks only
+    if (s_lo >= s_hi) continue;
 
-  const int ncols = (phi - plo) * G;
-  const int64_t row0 = (int64_t)(plo - (N - M)) + q0;  // first query row
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = lane_id();
-  const int col_base = wave * 64;
-  const bool active = col_base < ncols;
-  // This lane's column after the block-max swap, and its row of block scores.
-  // The scores of 16 consecutive blocks are gathered in registers (newest
-  // last) and written as one 64-byte run: chunks start at multiples of 16
-  // blocks and rows are 16-byte aligned, so every full group is aligned.
-  const int col_mine = col_base + lane;
-  const bool col_ok = col_mine < ncols;
-  float* srow = scores + (row0 * G + (col_ok ? col_mine : 0)) * (int64_t)nb_stride;
-  float sbuf[kSbLds ? 1 : 16];
-#pragma unroll
-  for (int j = 0; j < (kSbLds ? 1 : 16); ++j) sbuf[j] = 0.f;
+    const int ncols = (phi - plo) * G;
+    const int64_t row0 = (int64_t)(plo - (N - M)) + q0;  // first query row
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = lane_id();
+    const int col_base = wave * 64;
+    const bool active = col_base < ncols;
+    // This lane's column after the block-max swap, and its row of block scores.
+    // The scores of 16 consecutive blocks are gathered in registers (newest
+    // last) and written as one 64-byte run: chunks start at multiples of 16
+    // blocks and rows are 16-byte aligned, so every full group is aligned.
+    const int col_mine = col_base + lane;
+    const bool col_ok = col_mine < ncols;
+    float* srow = scores + (row0 * G + (col_ok ? col_mine : 0)) * (int64_t)nb_stride;
+    float sbuf[kSbLds ? 1 : 16];
+  #pragma unroll
+    for (int j = 0; j < (kSbLds ? 1 : 16); ++j) sbuf[j] = 0.f;
 
-  // B operand (Q^T): columns col_base + 32*j + lane%32, contraction slots
-  // kStep*ks + kLaneK*(lane/32) .. +kLaneK-1.
-  typename Mm::frag qf[2][KS];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = col_base + 32 * j + (lane & 31);
-    const bool ok = col < ncols;
-    const T* qp = q_idx + (row0 * G + (ok ? col : 0)) * DI + Mm::kLaneK * (lane >> 5);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[j][ks] = ok ? Mm::load(qp + Mm::kStep * ks) : Mm::zero();
-  }
+    // B operand (Q^T): columns col_base + 32*j + lane%32, contraction slots
+    // kStep*ks + kLaneK*(lane/32) .. +kLaneK-1.
+    typename Mm::frag qf[2][KS];
+  #pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = col_base + 32 * j + (lane & 31);
+      const bool ok = col < ncols;
+      const T* qp = q_idx + (row0 * G + (ok ? col : 0)) * DI + Mm::kLaneK * (lane >> 5);
+  #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[j][ks] = ok ? Mm::load(qp + Mm::kStep * ks) : Mm::zero();
+    }
 
-  // Key blocks are staged into LDS in 16-byte pieces (coalesced global reads
-  // that write LDS directly, no register round trip) through a ring of kRing
-  // buffers: block s + kRing - 1 is requested while block s is scored, and
-  // the wait and barrier at the end of the step make it visible.  With three
-  // buffers, block s + 1 is already in LDS while block s is scored, so the
-  // key fragments of its first tile are read before the step's barrier and
-  // the MFMAs of one block follow those of the previous without a gap.
-  const char* kseq = reinterpret_cast<const char*>(k_idx + (int64_t)k0 * DI);
-  constexpr int64_t kBlockBytes = (int64_t)kBlock * DI * sizeof(T);
-  // Block `blk` into ring buffer `ring`: run u (of kRuns) fills slots
-  // 64 u .. 64 u + 63, lane i slot 64 u + i; wave w does runs w, w + 8, ...
-  // A slot's byte offset in the block (its row's chunk, or the row's first
-  // chunk for a padding slot) does not depend on the block.
-  constexpr int kRunsPerWave = (L::kRuns + kScanThreads / kWave - 1) / (kScanThreads / kWave);
-  int src_off[kRunsPerWave];
-#pragma unroll
-  for (int u = 0; u < kRunsPerWave; ++u) {
-    const int sl = (u * (kScanThreads / kWave) + wave) * kWave + lane;
-    const int row = min(sl / L::kRowSlots, kBlock - 1);
-    const int chunk = sl % L::kRowSlots;
-    src_off[u] = row * (L::kChunksPerRow * 16) + (chunk < L::kChunksPerRow ? chunk : 0) * 16;
-  }
-  auto fetch = [&](int blk, int ring) {
-    const char* src = kseq + blk * kBlockBytes;
-#pragma unroll
+    // Key blocks are staged into LDS in 16-byte pieces (coalesced global reads
+    // that write LDS directly, no register round trip) through a ring of kRing
+    // buffers: block s + kRing - 1 is requested while block s is scored, and
+    // the wait and barrier at the end of the step make it visible.  With three
+    // buffers, block s + 1 is already in LDS while block s is scored, so the
+    // key fragments of its first tile are read before the step's barrier and
+    // the MFMAs of one block follow those of the previous without a gap.
+    const char* kseq = reinterpret_cast<const char*>(k_idx + (int64_t)k0 * DI);
+    constexpr int64_t kBlockBytes = (int64_t)kBlock * DI * sizeof(T);
+    // Block `blk` into ring buffer `ring`: run u (of kRuns) fills slots
+    // 64 u .. 64 u + 63, lane i slot 64 u + i; wave w does runs w, w + 8, ...
+    // A slot's byte offset in the block (its row's chunk, or the row's first
+    // chunk for a padding slot) does not depend on the block.
+    constexpr int kRunsPerWave = (L::kRuns + kScanThreads / kWave - 1) / (kScanThreads / kWave);
+    int src_off[kRunsPerWave];
+  #pragma unroll
     for (int u = 0; u < kRunsPerWave; ++u) {
-      const int run = u * (kScanThreads / kWave) + wave;
-      if (run < L::kRuns)
-        lds_load16(src, (int)kBlockBytes, src_off[u], lds + ring * L::kBufBytes + run * kWave * 16);
+      const int sl = (u * (kScanThreads / kWave) + wave) * kWave + lane;
+      const int row = min(sl / L::kRowSlots, kBlock - 1);
+      const int chunk = sl % L::kRowSlots;
+      src_off[u] = row * (L::kChunksPerRow * 16) + (chunk < L::kChunksPerRow ? chunk : 0) * 16;
     }
-  };
-#pragma unroll
-  for (int pre = 0; pre < kRing - 1; ++pre)
-    if (s_lo + pre < s_hi) fetch(s_lo + pre, pre);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+    auto fetch = [&](int blk, int ring) {
+      const char* src = kseq + blk * kBlockBytes;
+  #pragma unroll
+      for (int u = 0; u < kRunsPerWave; ++u) {
+        const int run = u * (kScanThreads / kWave) + wave;
+        if (run < L::kRuns)
+          lds_load16(src, (int)kBlockBytes, src_off[u], lds + ring * L::kBufBytes + run * kWave * 16);
+      }
+    };
+  #pragma unroll
+    for (int pre = 0; pre < kRing - 1; ++pre)
+      if (s_lo + pre < s_hi) fetch(s_lo + pre, pre);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
 
-  // A operand (K rows): this lane's fragment of key tile kt, step ks, of ring
-  // buffer r: row 32 kt + lane % 32, elements kStep ks + kLaneK (lane / 32) ..
-  constexpr int kStepBytes = Mm::kStep * (int)sizeof(T);
-  const int frag_off = (lane & 31) * L::kRowBytes + Mm::kLaneK * (lane >> 5) * (int)sizeof(T);
-  auto kfrag = [&](int ring, int kt, int ks) {
-    return *reinterpret_cast<const typename Mm::frag*>(lds + ring * L::kBufBytes + 32 * kt * L::kRowBytes + frag_off +
-                                                       kStepBytes * ks);
-  };
-  typename Mm::frag kf[kPrefetch ? 2 : 1][KS];
-  // kf[0]: tile 0 of the first block (later blocks' first tiles are read
-  // during the tile before, with three buffers)
-  if (kPrefetch && active) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[0][ks] = kfrag(0, 0, ks);
-  }
-  // A block's score: lane l < 32 owns column l of tile 0, lane l >= 32 column
-  // l - 32 of tile 1; each needs the other half-wave's partial max of its own
-  // column.  The scores of 16 consecutive blocks are stored together.
-  auto finish = [&](int sb, float a0, float a1) {
-    const float send = lane < 32 ? a1 : a0;
-    const float recv = xchg_halves_f(send);
-    const float v = fmaxf(lane < 32 ? a0 : a1, recv);
-    if constexpr (kSbLds) {
-      s_sb[wave][sb & 15][lane] = v;
-      if ((sb & 15) == 15 && col_ok) {
-        f32x4* dst = reinterpret_cast<f32x4*>(srow + (sb - 15));
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          dst[q] = f32x4{s_sb[wave][4 * q][lane], s_sb[wave][4 * q + 1][lane], s_sb[wave][4 * q + 2][lane],
-                         s_sb[wave][4 * q + 3][lane]};
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 15; ++j) sbuf[j] = sbuf[j + 1];
-      sbuf[15] = v;
-      if ((sb & 15) == 15 && col_ok) {
-        f32x4* dst = reinterpret_cast<f32x4*>(srow + (sb - 15));
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dst[q] = f32x4{sbuf[4 * q], sbuf[4 * q + 1], sbuf[4 * q + 2], sbuf[4 * q + 3]};
-      }
+    // A operand (K rows): this lane's fragment of key tile kt, step ks, of ring
+    // buffer r: row 32 kt + lane % 32, elements kStep ks + kLaneK (lane / 32) ..
+    constexpr int kStepBytes = Mm::kStep * (int)sizeof(T);
+    const int frag_off = (lane & 31) * L::kRowBytes + Mm::kLaneK * (lane >> 5) * (int)sizeof(T);
+    auto kfrag = [&](int ring, int kt, int ks) {
+      return *reinterpret_cast<const typename Mm::frag*>(lds + ring * L::kBufBytes + 32 * kt * L::kRowBytes + frag_off +
+                                                         kStepBytes * ks);
+    };
+    typename Mm::frag kf[kPrefetch ? 2 : 1][KS];
+    // kf[0]: tile 0 of the first block (later blocks' first tiles are read
+    // during the tile before, with three buffers)
+    if (kPrefetch && active) {
+  #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[0][ks] = kfrag(0, 0, ks);
     }
-  };
-  // With the fragments read ahead (kPrefetch), two accumulator sets persist
-  // across blocks: tile kt's scores are max-pooled during the second half of
-  // tile kt + 1's MFMAs (its results are complete by then), the last tile of
-  // block s - 1 during tile 0 of block s, and block s - 1's score is finished
-  // after that tile.  So the MFMA pipe never waits for the pooling, and the
-  // score stores have a whole block to complete before the wait at its end.
-  static_assert((kBlock / 32) % 2 == 0, "the last tile of a block must land in acc[1]");
-  f32x16 acc[2][2];
-  float pm0 = -__builtin_inff(), pm1 = -__builtin_inff();  // block s - 1 over tiles 0 .. 2
-  if constexpr (kPrefetch) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { acc[1][0][r] = -__builtin_inff(); acc[1][1][r] = -__builtin_inff(); }
-  }
-  int ring = 0;  // ring buffer of block s
-  for (int s = s_lo; s < s_hi; ++s) {
-    const int ring_next = ring + 1 == kRing ? 0 : ring + 1;
-    // the buffer of block s - 1, which nothing reads any more
-    if (s + kRing - 1 < s_hi) fetch(s + kRing - 1, ring == 0 ? kRing - 1 : ring - 1);
-    if (active) {
-      if (kPrefetch && kRing == 2 && s > s_lo) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[0][ks] = kfrag(ring, 0, ks);
+    // A block's score: lane l < 32 owns column l of tile 0, lane l >= 32 column
+    // l - 32 of tile 1; each needs the other half-wave's partial max of its own
+    // column.  The scores of 16 consecutive blocks are stored together.
+    auto finish = [&](int sb, float a0, float a1) {
+      const float send = lane < 32 ? a1 : a0;
+      const float recv = xchg_halves_f(send);
+      const float v = fmaxf(lane < 32 ? a0 : a1, recv);
+      if constexpr (kSbLds) {
+        s_sb[wave][sb & 15][lane] = v;
+        if ((sb & 15) == 15 && col_ok) {
+          f32x4* dst = reinterpret_cast<f32x4*>(srow + (sb - 15));
+  #pragma unroll
+          for (int q = 0; q < 4; ++q)
+            dst[q] = f32x4{s_sb[wave][4 * q][lane], s_sb[wave][4 * q + 1][lane], s_sb[wave][4 * q + 2][lane],
+                           s_sb[wave][4 * q + 3][lane]};
+        }
+      } else {
+  #pragma unroll
+        for (int j = 0; j < 15; ++j) sbuf[j] = sbuf[j + 1];
+        sbuf[15] = v;
+        if ((sb & 15) == 15 && col_ok) {
+          f32x4* dst = reinterpret_cast<f32x4*>(srow + (sb - 15));
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) dst[q] = f32x4{sbuf[4 * q], sbuf[4 * q + 1], sbuf[4 * q + 2], sbuf[4 * q + 3]};
+        }
       }
-      float m0 = -__builtin_inff(), m1 = -__builtin_inff();
-      if constexpr (kPrefetch) {
-        // the pooling runs in the last kPool steps of a tile (at least one)
-        constexpr int kPool = KS / 2 > 0 ? KS / 2 : 1;
-        constexpr int kRowsPerStep = (16 + kPool - 1) / kPool;
-#pragma unroll
-        for (int kt = 0; kt < kBlock / 32; ++kt) {
-          const int cur = kt & 1;
-          // the next tile's fragments are read between this tile's MFMAs
-          // (the next ring buffer's first tile is read even after the last
-          // block: in bounds, and then unused)
-          const bool pf = kt + 1 < kBlock / 32 || kRing == 3;
-          const int pr = kt + 1 < kBlock / 32 ? ring : ring_next;
-          const int pk = kt + 1 < kBlock / 32 ? kt + 1 : 0;
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            acc[cur][0] = Mm::mma(kf[cur][ks], qf[0][ks], ks == 0 ? f32x16{} : acc[cur][0]);
-            acc[cur][1] = Mm::mma(kf[cur][ks], qf[1][ks], ks == 0 ? f32x16{} : acc[cur][1]);
-            if (pf) kf[cur ^ 1][ks] = kfrag(pr, pk, ks);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-            const int h = ks - (KS - kPool);
-            if (h >= 0) {
-              // tile kt - 1 of this block, or the last tile of the previous one
-              float& a0 = kt > 0 ? m0 : pm0;
-              float& a1 = kt > 0 ? m1 : pm1;
-#pragma unroll
-              for (int r = h * kRowsPerStep; r < (h + 1) * kRowsPerStep && r < 16; ++r) {
-                a0 = fmaxf(a0, acc[cur ^ 1][0][r]);
-                a1 = fmaxf(a1, acc[cur ^ 1][1][r]);
+    };
+    // With the fragments read ahead (kPrefetch), two accumulator sets persist
+    // across blocks: tile kt's scores are max-pooled during the second half of
+    // tile kt + 1's MFMAs (its results are complete by then), the last tile of
+    // block s - 1 during tile 0 of block s, and block s - 1's score is finished
+    // after that tile.  So the MFMA pipe never waits for the pooling, and the
+    // score stores have a whole block to complete before the wait at its end.
+    static_assert((kBlock / 32) % 2 == 0, "the last tile of a block must land in acc[1]");
+    f32x16 acc[2][2];
+    float pm0 = -__builtin_inff(), pm1 = -__builtin_inff();  // block s - 1 over tiles 0 .. 2
+    if constexpr (kPrefetch) {
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) { acc[1][0][r] = -__builtin_inff(); acc[1][1][r] = -__builtin_inff(); }
+    }
+    int ring = 0;  // ring buffer of block s
+    for (int s = s_lo; s < s_hi; ++s) {
+      const int ring_next = ring + 1 == kRing ? 0 : ring + 1;
+      // the buffer of block s - 1, which nothing reads any more
+      if (s + kRing - 1 < s_hi) fetch(s + kRing - 1, ring == 0 ? kRing - 1 : ring - 1);
+      if (active) {
+        if (kPrefetch && kRing == 2 && s > s_lo) {
+  #pragma unroll
+          for (int ks = 0; ks < KS; ++ks) kf[0][ks] = kfrag(ring, 0, ks);
+        }
+        float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+        if constexpr (kPrefetch) {
+          // the pooling runs in the last kPool steps of a tile (at least one)
+          constexpr int kPool = KS / 2 > 0 ? KS / 2 : 1;
+          constexpr int kRowsPerStep = (16 + kPool - 1) / kPool;
+  #pragma unroll
+          for (int kt = 0; kt < kBlock / 32; ++kt) {
+            const int cur = kt & 1;
+            // the next tile's fragments are read between this tile's MFMAs
+            // (the next ring buffer's first tile is read even after the last
+            // block: in bounds, and then unused)
+            const bool pf = kt + 1 < kBlock / 32 || kRing == 3;
+            const int pr = kt + 1 < kBlock / 32 ? ring : ring_next;
+            const int pk = kt + 1 < kBlock / 32 ? kt + 1 : 0;
+  #pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              acc[cur][0] = Mm::mma(kf[cur][ks], qf[0][ks], ks == 0 ? f32x16{} : acc[cur][0]);
+              acc[cur][1] = Mm::mma(kf[cur][ks], qf[1][ks], ks == 0 ? f32x16{} : acc[cur][1]);
+              if (pf) kf[cur ^ 1][ks] = kfrag(pr, pk, ks);
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+              const int h = ks - (KS - kPool);
+              if (h >= 0) {
+                // tile kt - 1 of this block, or the last tile of the previous one
+                float& a0 = kt > 0 ? m0 : pm0;
+                float& a1 = kt > 0 ? m1 : pm1;
+  #pragma unroll
+                for (int r = h * kRowsPerStep; r < (h + 1) * kRowsPerStep && r < 16; ++r) {
+                  a0 = fmaxf(a0, acc[cur ^ 1][0][r]);
+                  a1 = fmaxf(a1, acc[cur ^ 1][1][r]);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x002, kRowsPerStep, 0);  // the pooling
               }
-              __builtin_amdgcn_sched_group_barrier(0x002, kRowsPerStep, 0);  // the pooling
+              // keep the next tile's fragment reads in k-step order: left free,
+              // the compiler issued k-step 0's last, so the next tile's first
+              // MFMA waited for the most recent read
+              __builtin_amdgcn_sched_barrier(0);
             }
-            // keep the next tile's fragment reads in k-step order: left free,
-            // the compiler issued k-step 0's last, so the next tile's first
-            // MFMA waited for the most recent read
+            if (kt == 0 && s > s_lo) finish(s - 1, pm0, pm1);
+            // keep each tile's MFMAs within its own step: the next tile's
+            // MFMAs would otherwise be pulled up behind their fragment reads
             __builtin_amdgcn_sched_barrier(0);
           }
-          if (kt == 0 && s > s_lo) finish(s - 1, pm0, pm1);
-          // keep each tile's MFMAs within its own step: the next tile's
-          // MFMAs would otherwise be pulled up behind their fragment reads
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        pm0 = m0;
-        pm1 = m1;
-      } else {
-#pragma unroll
-        for (int kt = 0; kt < kBlock / 32; ++kt) {
-          f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) kf[0][ks] = kfrag(ring, kt, ks);
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            acc0 = Mm::mma(kf[0][ks], qf[0][ks], acc0);
-            acc1 = Mm::mma(kf[0][ks], qf[1][ks], acc1);
+          pm0 = m0;
+          pm1 = m1;
+        } else {
+  #pragma unroll
+          for (int kt = 0; kt < kBlock / 32; ++kt) {
+            f32x16 acc0 = {}, acc1 = {};
+  #pragma unroll
+            for (int ks = 0; ks < KS; ++ks) kf[0][ks] = kfrag(ring, kt, ks);
+  #pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              acc0 = Mm::mma(kf[0][ks], qf[0][ks], acc0);
+              acc1 = Mm::mma(kf[0][ks], qf[1][ks], acc1);
+            }
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) { m0 = fmaxf(m0, acc0[r]); m1 = fmaxf(m1, acc1[r]); }
           }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) { m0 = fmaxf(m0, acc0[r]); m1 = fmaxf(m1, acc1[r]); }
+          finish(s, m0, m1);
         }
-        finish(s, m0, m1);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // block s + kRing - 1 is in LDS
+      if constexpr (kPrefetch && kRing == 3) {
+        // every wave has read block s (its buffer is refilled next); the KS
+        // reads of block s + 1's first tile, the last LDS operations issued,
+        // may stay in flight (LDS operations complete in order)
+        asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(KS) : "memory");
+      } else {
+        __syncthreads();
+      }
+      ring = ring_next;
+    }
+    if constexpr (kPrefetch) {
+      // the last block's last tile
+      if (active) {
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) { pm0 = fmaxf(pm0, acc[1][0][r]); pm1 = fmaxf(pm1, acc[1][1][r]); }
+        finish(s_hi - 1, pm0, pm1);
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // block s + kRing - 1 is in LDS
-    if constexpr (kPrefetch && kRing == 3) {
-      // every wave has read block s (its buffer is refilled next); the KS
-      // reads of block s + 1's first tile, the last LDS operations issued,
-      // may stay in flight (LDS operations complete in order)
-      asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(KS) : "memory");
-    } else {
-      __syncthreads();
-    }
-    ring = ring_next;
-  }
-  if constexpr (kPrefetch) {
-    // the last block's last tile
-    if (active) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { pm0 = fmaxf(pm0, acc[1][0][r]); pm1 = fmaxf(pm1, acc[1][1][r]); }
-      finish(s_hi - 1, pm0, pm1);
-    }
-  }
-  // a trailing partial group (only at the end of a query block's last chunk)
-  const int n_tail = s_hi & 15;
-  if (active && col_ok && n_tail != 0) {
-    const int g0 = s_hi - n_tail;
-    if constexpr (kSbLds) {
-      for (int j = 0; j < n_tail; ++j) srow[g0 + j] = s_sb[wave][j][lane];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = i - (16 - n_tail);
-        if (j >= 0) srow[g0 + j] = sbuf[i];
+    // a trailing partial group (only at the end of a query block's last chunk)
+    const int n_tail = s_hi & 15;
+    if (active && col_ok && n_tail != 0) {
+      const int g0 = s_hi - n_tail;
+      if constexpr (kSbLds) {
+        for (int j = 0; j < n_tail; ++j) srow[g0 + j] = s_sb[wave][j][lane];
+      } else {
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = i - (16 - n_tail);
+          if (j >= 0) srow[g0 + j] = sbuf[i];
+        }
       }
     }
   }
@@ -891,9 +904,11 @@ static hipError_t launch_index_prefill(const IndexPlan& pl, const void* q_idx, c
                                        int topk, int32_t* block_idx, char* ws, hipStream_t st) {
   float* scores = reinterpret_cast<float*>(ws);
   if (pl.scan_wgs > 0) {
-    hipLaunchKernelGGL((idx_scan_prefill<T, DI>), dim3((unsigned)pl.scan_wgs), dim3(kScanThreads), 0, st,
+    const int64_t grid = pl.scan_pair ? (pl.scan_wgs + 1) / 2 : pl.scan_wgs;
+    hipLaunchKernelGGL((idx_scan_prefill<T, DI>), dim3((unsigned)grid), dim3(kScanThreads), 0, st,
                        static_cast<const T*>(q_idx), static_cast<const T*>(k_idx), cu_q, cu_k, G,
-                       pl.qw, pl.nsub, pl.max_qblocks, pl.chunk, pl.max_chunks, pl.score_stride, scores);
+                       pl.qw, pl.nsub, pl.max_qblocks, pl.chunk, pl.max_chunks, pl.score_stride, (int)pl.scan_wgs,
+                       scores);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

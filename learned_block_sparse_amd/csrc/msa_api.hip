@@ -63,6 +63,8 @@ IndexPlan plan_index(int batch, int max_q_len, int max_kv_len, int G) {
     pl.chunk = (int)chunk;
     pl.max_chunks = (int)ceil_div(c_max, chunk);
     pl.scan_wgs = (int64_t)batch * pl.max_qblocks * pl.nsub * pl.max_chunks;
+    // at least two rounds of workgroups: pair mirror items, one round of equal work
+    pl.scan_pair = pl.scan_wgs >= 2 * kScanTargetWgs;
   }
   // block scores [rows, G, score_stride] fp32 (rows padded to 16 bytes),
   // written by the scan, read by the selection

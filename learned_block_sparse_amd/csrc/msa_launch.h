@@ -20,7 +20,8 @@ struct IndexPlan {
   int max_qblocks = 0;       // query blocks per sequence (upper bound)
   int chunk = 1;             // key blocks per scan workgroup
   int max_chunks = 1;        // key chunks per query block
-  int64_t scan_wgs = 0;
+  int64_t scan_wgs = 0;      // scan items (query block, slice, key chunk, sequence)
+  bool scan_pair = false;    // two mirror items per workgroup (when there are enough of them)
   int score_stride = 0;      // floats per (row, group) of prefill block scores
   // decode scan
   int dec_wgs = 0;           // workgroups (4 waves) of the grid-stride decode scan
