@@ -8,7 +8,8 @@
 //
 // Prefill path (two kernels):
 //   idx_scan_prefill  one workgroup per (sequence, query block, query slice,
-//                     key chunk).  Its columns are the (query, group) pairs of
+//                     key chunk), or per mirror pair of them when a call has
+//                     two rounds of those.  Its columns are the (query, group) pairs of
 //                     one query block -- all queries of a block scan the same
 //                     earlier blocks, so no causal mask is ever needed.  Each
 //                     key block (128 x d_idx) is staged in LDS once and shared
