@@ -300,6 +300,23 @@ def test_fullsize_ids_32k_every_row(msa, synth, oracle_lib):
     compare_ids(ids, ref, "32K every row")
 
 
+def test_mirror_paired_scan_ragged_batch(msa, synth, oracle_lib):
+    """A ragged causal batch whose index scan has two rounds of items (4
+    sequences x 157 query blocks x 1 key chunk = 628), so each workgroup
+    scores an item and its mirror, here from another sequence: ids of every
+    row against the oracle."""
+    wl = synth.WORKLOADS["prefill_32k"]
+    lens = [9000, 3000, 20000, 12000]
+    say(f"[parity] mirror-paired scan, ragged batch {lens}")
+    inp = synth.prefill_inputs(wl, device="cuda", seed=51, seq_lens=lens, with_main=False)
+    ids = msa.msa_index_topk(inp["q_idx"], inp["k_idx"], inp["cu_seqlens_q"], inp["cu_seqlens_k"], max(lens),
+                             max(lens), wl.block_size, wl.topk)
+    torch.cuda.synchronize()
+    rows, kstart, pos = oracle_lib.rows_prefill(inp["cu_q_host"], inp["cu_k_host"])
+    ref = oracle_lib.index_topk(host(inp["q_idx"]), host(inp["k_idx"]), kstart, pos, rows, wl.block_size, wl.topk)
+    compare_ids(ids, ref, "mirror-paired ragged batch")
+
+
 def test_fullsize_ids_128k_every_tile_edge(msa, synth, oracle_lib):
     """L=131072 in 8192-query calls against the causal prefix (the bench's
     launches): ids of the first and last query block (128 rows each) of every
