@@ -271,13 +271,11 @@ __device__ __forceinline__ void write_selection(int mine, int found, int local, 
   int v = lane < found ? mine : (lane == found ? local : 0x7fffffff);
   const int cnt = found + 1;  // <= 16
   // rank among the first cnt lanes, each value read as a scalar (no LDS
-  // round trip per lane, unlike a shuffle)
+  // round trip per lane, unlike a shuffle); lanes from cnt on hold INT_MAX,
+  // which is below no value
   int rank = 0;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int o = __builtin_amdgcn_readlane(v, j);
-    rank += (j < cnt && o < v) ? 1 : 0;
-  }
+  for (int j = 0; j < 16; ++j) rank += __builtin_amdgcn_readlane(v, j) < v ? 1 : 0;
   if (lane < cnt) out[rank] = v;
   if (lane >= cnt && lane < topk) out[lane] = -1;
 }
