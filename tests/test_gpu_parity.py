@@ -300,13 +300,14 @@ def test_fullsize_ids_32k_every_row(msa, synth, oracle_lib):
     compare_ids(ids, ref, "32K every row")
 
 
-def test_mirror_paired_scan_ragged_batch(msa, synth, oracle_lib):
-    """A ragged causal batch whose index scan has two rounds of items (4
-    sequences x 157 query blocks x 1 key chunk = 628), so each workgroup
-    scores an item and its mirror, here from another sequence: ids of every
-    row against the oracle."""
+@pytest.mark.parametrize("lens", [[9000, 3000, 20000, 12000], [21888, 5000, 15000]])
+def test_mirror_paired_scan_ragged_batch(msa, synth, oracle_lib, lens):
+    """Ragged causal batches whose index scan has two rounds of items (4
+    sequences x 157 query blocks x 1 key chunk = 628; 3 x 171 = 513, an odd
+    count whose middle item has no partner), so each workgroup scores an item
+    and its mirror, here from another sequence: ids of every row against the
+    oracle."""
     wl = synth.WORKLOADS["prefill_32k"]
-    lens = [9000, 3000, 20000, 12000]
     say(f"[parity] mirror-paired scan, ragged batch {lens}")
     inp = synth.prefill_inputs(wl, device="cuda", seed=51, seq_lens=lens, with_main=False)
     ids = msa.msa_index_topk(inp["q_idx"], inp["k_idx"], inp["cu_seqlens_q"], inp["cu_seqlens_k"], max(lens),
