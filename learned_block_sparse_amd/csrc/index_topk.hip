@@ -165,18 +165,18 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
     const bool col_ok = col_mine < ncols;
     float* srow = scores + (row0 * G + (col_ok ? col_mine : 0)) * (int64_t)nb_stride;
     float sbuf[kSbLds ? 1 : 16];
-  #pragma unroll
+#pragma unroll
     for (int j = 0; j < (kSbLds ? 1 : 16); ++j) sbuf[j] = 0.f;
 
     // B operand (Q^T): columns col_base + 32*j + lane%32, contraction slots
     // kStep*ks + kLaneK*(lane/32) .. +kLaneK-1.
     typename Mm::frag qf[2][KS];
-  #pragma unroll
+#pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = col_base + 32 * j + (lane & 31);
       const bool ok = col < ncols;
       const T* qp = q_idx + (row0 * G + (ok ? col : 0)) * DI + Mm::kLaneK * (lane >> 5);
-  #pragma unroll
+#pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[j][ks] = ok ? Mm::load(qp + Mm::kStep * ks) : Mm::zero();
     }
 
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
     // chunk for a padding slot) does not depend on the block.
     constexpr int kRunsPerWave = (L::kRuns + kScanThreads / kWave - 1) / (kScanThreads / kWave);
     int src_off[kRunsPerWave];
-  #pragma unroll
+#pragma unroll
     for (int u = 0; u < kRunsPerWave; ++u) {
       const int sl = (u * (kScanThreads / kWave) + wave) * kWave + lane;
       const int row = min(sl / L::kRowSlots, kBlock - 1);
@@ -204,14 +204,14 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
     }
     auto fetch = [&](int blk, int ring) {
       const char* src = kseq + blk * kBlockBytes;
-  #pragma unroll
+#pragma unroll
       for (int u = 0; u < kRunsPerWave; ++u) {
         const int run = u * (kScanThreads / kWave) + wave;
         if (run < L::kRuns)
           lds_load16(src, (int)kBlockBytes, src_off[u], lds + ring * L::kBufBytes + run * kWave * 16);
       }
     };
-  #pragma unroll
+#pragma unroll
     for (int pre = 0; pre < kRing - 1; ++pre)
       if (s_lo + pre < s_hi) fetch(s_lo + pre, pre);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
     // kf[0]: tile 0 of the first block (later blocks' first tiles are read
     // during the tile before, with three buffers)
     if (kPrefetch && active) {
-  #pragma unroll
+#pragma unroll
       for (int ks = 0; ks < KS; ++ks) kf[0][ks] = kfrag(0, 0, ks);
     }
     // A block's score: lane l < 32 owns column l of tile 0, lane l >= 32 column
@@ -243,18 +243,18 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
         s_sb[wave][sb & 15][lane] = v;
         if ((sb & 15) == 15 && col_ok) {
           f32x4* dst = reinterpret_cast<f32x4*>(srow + (sb - 15));
-  #pragma unroll
+#pragma unroll
           for (int q = 0; q < 4; ++q)
             dst[q] = f32x4{s_sb[wave][4 * q][lane], s_sb[wave][4 * q + 1][lane], s_sb[wave][4 * q + 2][lane],
                            s_sb[wave][4 * q + 3][lane]};
         }
       } else {
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < 15; ++j) sbuf[j] = sbuf[j + 1];
         sbuf[15] = v;
         if ((sb & 15) == 15 && col_ok) {
           f32x4* dst = reinterpret_cast<f32x4*>(srow + (sb - 15));
-  #pragma unroll
+#pragma unroll
           for (int q = 0; q < 4; ++q) dst[q] = f32x4{sbuf[4 * q], sbuf[4 * q + 1], sbuf[4 * q + 2], sbuf[4 * q + 3]};
         }
       }
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
     f32x16 acc[2][2];
     float pm0 = -__builtin_inff(), pm1 = -__builtin_inff();  // block s - 1 over tiles 0 .. 2
     if constexpr (kPrefetch) {
-  #pragma unroll
+#pragma unroll
       for (int r = 0; r < 16; ++r) { acc[1][0][r] = -__builtin_inff(); acc[1][1][r] = -__builtin_inff(); }
     }
     int ring = 0;  // ring buffer of block s
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
       if (s + kRing - 1 < s_hi) fetch(s + kRing - 1, ring == 0 ? kRing - 1 : ring - 1);
       if (active) {
         if (kPrefetch && kRing == 2 && s > s_lo) {
-  #pragma unroll
+#pragma unroll
           for (int ks = 0; ks < KS; ++ks) kf[0][ks] = kfrag(ring, 0, ks);
         }
         float m0 = -__builtin_inff(), m1 = -__builtin_inff();
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
           // the pooling runs in the last kPool steps of a tile (at least one)
           constexpr int kPool = KS / 2 > 0 ? KS / 2 : 1;
           constexpr int kRowsPerStep = (16 + kPool - 1) / kPool;
-  #pragma unroll
+#pragma unroll
           for (int kt = 0; kt < kBlock / 32; ++kt) {
             const int cur = kt & 1;
             // the next tile's fragments are read between this tile's MFMAs
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
             const bool pf = kt + 1 < kBlock / 32 || kRing == 3;
             const int pr = kt + 1 < kBlock / 32 ? ring : ring_next;
             const int pk = kt + 1 < kBlock / 32 ? kt + 1 : 0;
-  #pragma unroll
+#pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
               acc[cur][0] = Mm::mma(kf[cur][ks], qf[0][ks], ks == 0 ? f32x16{} : acc[cur][0]);
               acc[cur][1] = Mm::mma(kf[cur][ks], qf[1][ks], ks == 0 ? f32x16{} : acc[cur][1]);
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
                 // tile kt - 1 of this block, or the last tile of the previous one
                 float& a0 = kt > 0 ? m0 : pm0;
                 float& a1 = kt > 0 ? m1 : pm1;
-  #pragma unroll
+#pragma unroll
                 for (int r = h * kRowsPerStep; r < (h + 1) * kRowsPerStep && r < 16; ++r) {
                   a0 = fmaxf(a0, acc[cur ^ 1][0][r]);
                   a1 = fmaxf(a1, acc[cur ^ 1][1][r]);
@@ -328,17 +328,18 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
           pm0 = m0;
           pm1 = m1;
         } else {
-  #pragma unroll
+#pragma unroll
           for (int kt = 0; kt < kBlock / 32; ++kt) {
             f32x16 acc0 = {}, acc1 = {};
-  #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) kf[0][ks] = kfrag(ring, kt, ks);
-  #pragma unroll
+            // one fragment at a time: with all of a tile's fp32 fragments
+            // held at once beside the query fragments, registers spilled
+#pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-              acc0 = Mm::mma(kf[0][ks], qf[0][ks], acc0);
-              acc1 = Mm::mma(kf[0][ks], qf[1][ks], acc1);
+              const typename Mm::frag kv = kfrag(ring, kt, ks);
+              acc0 = Mm::mma(kv, qf[0][ks], acc0);
+              acc1 = Mm::mma(kv, qf[1][ks], acc1);
             }
-  #pragma unroll
+#pragma unroll
             for (int r = 0; r < 16; ++r) { m0 = fmaxf(m0, acc0[r]); m1 = fmaxf(m1, acc1[r]); }
           }
           finish(s, m0, m1);
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
     if constexpr (kPrefetch) {
       // the last block's last tile
       if (active) {
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 16; ++r) { pm0 = fmaxf(pm0, acc[1][0][r]); pm1 = fmaxf(pm1, acc[1][1][r]); }
         finish(s_hi - 1, pm0, pm1);
       }
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void idx_scan_prefill(
       if constexpr (kSbLds) {
         for (int j = 0; j < n_tail; ++j) srow[g0 + j] = s_sb[wave][j][lane];
       } else {
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int j = i - (16 - n_tail);
           if (j >= 0) srow[g0 + j] = sbuf[i];
@@ -553,14 +554,16 @@ __global__ __launch_bounds__(256) void idx_select_prefill(
   __shared__ uint64_t s_best[4][16];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = lane_id();
-  const int64_t rg = (int64_t)blockIdx.x * 4 + wave;
-  if (rg >= rows_bound * G) return;
-  const int64_t row = rg / G;
+  // (row, group) items fit 31 bits (the launcher refuses more), so the item
+  // arithmetic is 32-bit; a power-of-two group count divides by a shift
+  const int rg = (int)blockIdx.x * 4 + wave;
+  if (rg >= (int)(rows_bound * G)) return;
+  const int row = (G & (G - 1)) == 0 ? rg >> __builtin_ctz((unsigned)G) : rg / G;
   if (row >= cu_q[batch]) return;
   const int b = find_seq(cu_q, batch, row);
   const int M = cu_q[b + 1] - cu_q[b], N = cu_k[b + 1] - cu_k[b];
-  const int64_t p = (int64_t)N - M + (row - cu_q[b]);
-  int32_t* out = block_idx + rg * topk;
+  const int p = N - M + (row - cu_q[b]);
+  int32_t* out = block_idx + (int64_t)rg * topk;
   if (p < 0) {
     if (lane < topk) out[lane] = -1;
     return;
@@ -914,6 +917,7 @@ static hipError_t launch_index_prefill(const IndexPlan& pl, const void* q_idx, c
     if (e != hipSuccess) return e;
   }
   const int64_t items = pl.rows_bound * G;
+  if (items >= INT32_MAX) return hipErrorInvalidValue;  // the selection's item indices are 32-bit
   hipLaunchKernelGGL(idx_select_prefill, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, cu_q, cu_k,
                      batch, pl.rows_bound, G, topk, pl.score_stride, scores, block_idx);
   return hipGetLastError();
