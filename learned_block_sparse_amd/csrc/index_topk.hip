@@ -666,6 +666,14 @@ __global__ __launch_bounds__(256) void idx_decode_scores(
   // 128-byte lines of block scores are written whole from one L2.
   const int per_xcd = (gridDim.x >> 3) * 4;
   const int first = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3) * 4 + (int)(threadIdx.x / kWave);
+  // A wave visits its blocks in increasing order, so each block's sequence
+  // is found by stepping forward from the previous one (one or two offsets
+  // read per block instead of a binary search's chain of dependent reads).
+  int bseq = 0;
+  auto locate = [&](int gb) {
+    while (blk_off[bseq + 1] <= gb) ++bseq;  // blk_off[batch] = total > gb ends it
+    return bseq;
+  };
   if constexpr (sizeof(T) == 1) {
     // fp8: lane l takes the 16-byte pieces 16 (l/16) + 64 u (u < NL) of its
     // key row, so the four lane groups of a row read 64 contiguous bytes per
@@ -684,7 +692,7 @@ __global__ __launch_bounds__(256) void idx_decode_scores(
       int b, c;
     };
     auto issue = [&](int gb, Blk& B) {
-      B.b = find_seq(blk_off, batch, gb);
+      B.b = locate(gb);
       B.c = gb - blk_off[B.b];
       const uint8_t* qp =
           reinterpret_cast<const uint8_t*>(q_idx) + ((int64_t)cu_q[B.b] * G + gcol) * DI + 16 * (lane >> 4);
@@ -734,7 +742,7 @@ __global__ __launch_bounds__(256) void idx_decode_scores(
     }
   } else {
   for (int gb = first; gb < total; gb += nwaves) {
-    const int b = find_seq(blk_off, batch, gb);
+    const int b = locate(gb);
     const int c = gb - blk_off[b];
     const int q0 = cu_q[b];
     float m = -__builtin_inff();
