@@ -93,6 +93,8 @@ AttnPlan plan_attn(int batch, int max_q_len, int max_kv_len, int Hq, int G, int 
     pl.kvo_chunks_off = off;  off += align_up((nbk + 1) * 4);
     pl.kvo_cursor_off = off;  off += align_up(nbk * 4);
     pl.kvo_edges_off = off;   off += align_up(slots * 4);
+    // chunks of <= kEdgeChunk edges: at most slots / kEdgeChunk full ones plus one partial per bucket
+    pl.kvo_cbucket_off = off; off += align_up((slots / kEdgeChunk + (slots < nbk ? slots : nbk) + 1) * 4);
     pl.kvo_part_o_off = off;  off += align_up(slots * kvo_part_slot_bytes());
     pl.kvo_part_lse_off = off; off += align_up(slots * 16 * sizeof(float));
     pl.workspace_bytes = off;

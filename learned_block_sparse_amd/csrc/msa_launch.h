@@ -42,6 +42,7 @@ struct AttnPlan {
   int kvo_nbuckets = 0;      // batch * G * nb_max
   size_t kvo_counts_off = 0, kvo_offsets_off = 0, kvo_chunks_off = 0, kvo_cursor_off = 0;
   size_t kvo_edges_off = 0, kvo_part_o_off = 0, kvo_part_lse_off = 0;
+  size_t kvo_cbucket_off = 0;  // bucket of each edge chunk
   size_t workspace_bytes = 0;
 };
 

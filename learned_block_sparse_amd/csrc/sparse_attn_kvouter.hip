@@ -56,6 +56,7 @@ struct KvoArgs {
   int32_t* counts;
   int32_t* offsets;
   int32_t* chunk_start;
+  int32_t* chunk_bucket;  // bucket of each chunk (filled by kvo_scan when set)
   int32_t* cursor;
   int32_t* edges;
   bf16* part_o;
@@ -196,8 +197,11 @@ __global__ __launch_bounds__(1024) void kvo_scan(KvoArgs a, int nbk) {
     a.offsets[j] = oe;
     a.cursor[j] = oe;
     a.chunk_start[j] = oc;
+    const int nc = (n + kKvoChunk - 1) / kKvoChunk;
+    if (a.chunk_bucket)
+      for (int q = 0; q < nc; ++q) a.chunk_bucket[oc + q] = j;
     oe += n;
-    oc += (n + kKvoChunk - 1) / kKvoChunk;
+    oc += nc;
   }
   if (tid == 1023) {
     a.offsets[nbk] = s_e[1023];
@@ -350,7 +354,7 @@ __global__ __launch_bounds__(kKvoThreads, 2) void kvo_attn(KvoArgs a) {
   const int nbk = a.batch * a.G * a.nb_max;
   const int w = blockIdx.x;
   if (w >= a.chunk_start[nbk]) return;
-  const int bucket = kvo_find(a.chunk_start, nbk, w);
+  const int bucket = a.chunk_bucket[w];  // one read (a search of chunk_start was a chain of ~log2(nbk) reads)
   const int chunk = w - a.chunk_start[bucket];
   const int c = bucket % a.nb_max;
   const int g = (bucket / a.nb_max) % a.G;
@@ -603,6 +607,7 @@ hipError_t launch_attn_kvouter(const AttnPlan& pl, bool kv_e4m3, const AttnArgs&
   a.counts = reinterpret_cast<int32_t*>(w + pl.kvo_counts_off);
   a.offsets = reinterpret_cast<int32_t*>(w + pl.kvo_offsets_off);
   a.chunk_start = reinterpret_cast<int32_t*>(w + pl.kvo_chunks_off);
+  a.chunk_bucket = reinterpret_cast<int32_t*>(w + pl.kvo_cbucket_off);
   a.cursor = reinterpret_cast<int32_t*>(w + pl.kvo_cursor_off);
   a.edges = reinterpret_cast<int32_t*>(w + pl.kvo_edges_off);
   a.part_o = reinterpret_cast<bf16*>(w + pl.kvo_part_o_off);
