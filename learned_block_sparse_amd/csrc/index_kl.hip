@@ -62,6 +62,7 @@ struct KlArgs {
   int64_t rows_bound, row_lo, row_hi;
   const int32_t* offsets;
   const int32_t* chunk_start;
+  const int32_t* chunk_bucket;  // bucket of each edge chunk
   const int32_t* edges;
   float* s_slot;      // [window rows, G, topk] index score of each attended slot
   int32_t* j_slot;    // [window rows, G, topk] argmax key within the block (0..127)
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(128) void kl_scores(KlArgs a) {
   const int nbk = a.batch * a.G * a.nb_max;
   const int w = blockIdx.x;
   if (w >= a.chunk_start[nbk]) return;
-  const int bucket = kl_find(a.chunk_start, nbk, w);
+  const int bucket = a.chunk_bucket[w];
   const int chunk = w - a.chunk_start[bucket];
   const int c = bucket % a.nb_max;
   const int g = (bucket / a.nb_max) % a.G;
@@ -439,6 +440,7 @@ KlPlan plan_kl(int batch, int max_q_len, int max_kv_len, int G, int topk) {
   pl.chunks_off = off;  off += al((nbk + 1) * 4);
   pl.cursor_off = off;  off += al(nbk * 4);
   pl.edges_off = off;   off += al(slots * 4);
+  pl.cbucket_off = off; off += al((slots / kEdgeChunk + (slots < nbk ? slots : nbk) + 1) * 4);
   pl.s_off = off;       off += al(slots * 4);
   pl.j_off = off;       off += al(slots * 4);
   pl.pos_off = off;     off += al(slots * 4);
@@ -471,8 +473,10 @@ static hipError_t launch_kl_t(const KlPlan& pl, const KlLaunch& x, void* ws, hip
   int32_t* chunks = reinterpret_cast<int32_t*>(w + pl.chunks_off);
   int32_t* cursor = reinterpret_cast<int32_t*>(w + pl.cursor_off);
   int32_t* edges = reinterpret_cast<int32_t*>(w + pl.edges_off);
+  int32_t* cbucket = reinterpret_cast<int32_t*>(w + pl.cbucket_off);
   a.offsets = offsets;
   a.chunk_start = chunks;
+  a.chunk_bucket = cbucket;
   a.edges = edges;
   a.s_slot = reinterpret_cast<float*>(w + pl.s_off);
   a.j_slot = reinterpret_cast<int32_t*>(w + pl.j_off);
@@ -484,7 +488,7 @@ static hipError_t launch_kl_t(const KlPlan& pl, const KlLaunch& x, void* ws, hip
   a.dk_idx = x.dk_idx;
   for (int64_t r0 = 0; r0 < pl.rows_bound; r0 += pl.window) {
     const int64_t r1 = r0 + pl.window < pl.rows_bound ? r0 + pl.window : pl.rows_bound;
-    hipError_t e = build_edge_lists(x.attn, pl.nb_max, r0, r1, counts, offsets, chunks, cursor, edges, true, st);
+    hipError_t e = build_edge_lists(x.attn, pl.nb_max, r0, r1, counts, offsets, chunks, cbucket, cursor, edges, true, st);
     if (e != hipSuccess) return e;
     a.row_lo = r0;
     a.row_hi = r1;

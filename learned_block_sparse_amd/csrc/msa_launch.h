@@ -87,10 +87,11 @@ constexpr int kEdgeChunk = 64;
 // selection slot), the entries of bucket i are edges[offsets[i] ..
 // offsets[i + 1]), ascending when `sorted`, else in the order the placing
 // atomics handed out.  counts, chunk_start and cursor are scratch of
-// batch * G * nb_max (+1) ints each.
+// batch * G * nb_max (+1) ints each; chunk_bucket (or null) receives the
+// bucket of every chunk of kEdgeChunk edges.
 hipError_t build_edge_lists(const AttnArgs& x, int nb_max, int64_t row_lo, int64_t row_hi, int32_t* counts,
-                            int32_t* offsets, int32_t* chunk_start, int32_t* cursor, int32_t* edges, bool sorted,
-                            hipStream_t st);
+                            int32_t* offsets, int32_t* chunk_start, int32_t* chunk_bucket, int32_t* cursor,
+                            int32_t* edges, bool sorted, hipStream_t st);
 
 // Backward of the main branch (bf16 inputs, fp32 gradients).
 struct BwdPlan {
@@ -124,6 +125,7 @@ struct KlPlan {
   int64_t rows_bound = 0;
   int64_t window = 0;        // query rows per edge-list window
   size_t counts_off = 0, offsets_off = 0, chunks_off = 0, cursor_off = 0, edges_off = 0;
+  size_t cbucket_off = 0;                    // bucket of each edge chunk
   size_t s_off = 0, j_off = 0, pos_off = 0;  // per selection slot of a window: score, argmax, edge position
   size_t key_off = 0, ds_off = 0;            // per edge-list position: edge key, dS
   size_t workspace_bytes = 0;

@@ -851,7 +851,7 @@ hipError_t launch_sparse_attn_bwd(const BwdPlan& pl, const BwdArgs& x, void* ws,
   hipLaunchKernelGGL(bwd_delta, dim3((unsigned)((pl.rows_bound * a.Hq + 7) / 8)), dim3(256), 0, st, a);
   for (int64_t r0 = 0; r0 < pl.rows_bound; r0 += pl.window) {
     const int64_t r1 = r0 + pl.window < pl.rows_bound ? r0 + pl.window : pl.rows_bound;
-    hipError_t e = build_edge_lists(x.fwd, pl.nb_max, r0, r1, counts, offsets, chunks, cursor, a.edges, true, st);
+    hipError_t e = build_edge_lists(x.fwd, pl.nb_max, r0, r1, counts, offsets, chunks, nullptr, cursor, a.edges, true, st);
     if (e != hipSuccess) return e;
     a.row_lo = r0;
     if (r0 == 0) hipLaunchKernelGGL(bwd_zero, dim3((unsigned)pl.nbuckets), dim3(256), 0, st, a);

@@ -564,8 +564,8 @@ static void launch_edge_lists(const KvoArgs& a, int nbk, hipStream_t st) {
 }
 
 hipError_t build_edge_lists(const AttnArgs& x, int nb_max, int64_t row_lo, int64_t row_hi, int32_t* counts,
-                            int32_t* offsets, int32_t* chunk_start, int32_t* cursor, int32_t* edges, bool sorted,
-                            hipStream_t st) {
+                            int32_t* offsets, int32_t* chunk_start, int32_t* chunk_bucket, int32_t* cursor,
+                            int32_t* edges, bool sorted, hipStream_t st) {
   if (row_hi - row_lo > kSortCap) return hipErrorInvalidValue;
   KvoArgs a{};
   a.block_idx = x.block_idx;
@@ -581,6 +581,7 @@ hipError_t build_edge_lists(const AttnArgs& x, int nb_max, int64_t row_lo, int64
   a.counts = counts;
   a.offsets = offsets;
   a.chunk_start = chunk_start;
+  a.chunk_bucket = chunk_bucket;
   a.cursor = cursor;
   a.edges = edges;
   const int nbk = x.batch * x.Hkv * nb_max;
