@@ -376,6 +376,30 @@ def test_decode_beyond_one_round_of_blocks(msa, synth, oracle_lib):
     _decode_check(msa, oracle_lib, synth, wl, ctx, "decode >1M", seed=13)
 
 
+def test_fullsize_ids_1m_three_tiles(msa, synth, oracle_lib):
+    """L=1048576, 256 planted blocks, the bench's 8192-query calls: block ids
+    of the first and last 8 rows and 8 random rows of the first, the 64th and
+    the last call, all 4 groups, against the oracle (index branch only)."""
+    wl = synth.WORKLOADS["prefill_1m"]
+    inp = synth.prefill_inputs(wl, device="cuda", seed=0, with_main=False)
+    T = wl.q_tile
+    rng = np.random.default_rng(2)
+    got, rows = [], []
+    for lo in (0, 63 * T, wl.seq_len - T):
+        hi = lo + T
+        say(f"[parity] 1M ids, call [{lo}, {hi})")
+        cu_q = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+        cu_k = torch.tensor([0, hi], dtype=torch.int32, device="cuda")
+        ids = msa.msa_index_topk(inp["q_idx"][lo:hi], inp["k_idx"], cu_q, cu_k, T, hi, wl.block_size, wl.topk)
+        r = np.array(sorted(set(range(8)) | set(range(T - 8, T)) | set(int(x) for x in rng.integers(0, T, 8))))
+        got.append(ids[torch.as_tensor(r, device="cuda")].cpu())
+        rows.append(lo + r)
+    rows = np.concatenate(rows).astype(np.int64)
+    ref = oracle_lib.index_topk(host(inp["q_idx"]), host(inp["k_idx"]), np.zeros(len(rows), dtype=np.int64),
+                                rows.copy(), rows, wl.block_size, wl.topk)
+    compare_ids(torch.cat(got), ref, "1M three calls")
+
+
 def test_fullsize_prefill_1m_last_tile(msa, synth, oracle_lib):
     """L=1048576, 256 planted blocks: the last 8192-query tile against the whole
     1M prefix (8191 earlier blocks per query); sampled rows."""
