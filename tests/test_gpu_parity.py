@@ -359,11 +359,16 @@ def test_fullsize_prefill_128k_tiles(msa, synth, oracle_lib, tile):
 
 
 def test_fullsize_decode_1m(msa, synth, oracle_lib):
-    """32 sequences, contexts uniform in [64K, 1M]: sampled sequences."""
+    """32 sequences, contexts uniform in [64K, 1M]: outputs of sampled
+    sequences, block ids of every sequence."""
     wl = synth.WORKLOADS["decode_1m"]
     ctx = synth.decode_ctx_lens(wl, 0)
     seqs = [int(np.argmin(ctx)), int(np.argmax(ctx)), 3, 11, 20, 31]
-    _decode_check(msa, oracle_lib, synth, wl, ctx, "decode 1M", seed=0, seqs=sorted(set(seqs)))
+    inp, ids, _, _ = _decode_check(msa, oracle_lib, synth, wl, ctx, "decode 1M", seed=0, seqs=sorted(set(seqs)))
+    _, kstart, pos = oracle_lib.rows_decode(inp["k_offsets_host"], ctx)
+    ref = oracle_lib.index_topk(host(inp["q_idx"]), host(inp["k_idx"]), kstart, pos, np.arange(len(ctx)),
+                                wl.block_size, wl.topk)
+    compare_ids(ids, ref, "decode 1M, every sequence")
 
 
 def test_decode_beyond_one_round_of_blocks(msa, synth, oracle_lib):
