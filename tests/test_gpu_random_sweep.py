@@ -8,6 +8,7 @@ planted blocks and the split count, then runs the index call and the prefill
 call and one decode step on the same caches, and compares with the CPU oracle:
 block ids exactly, outputs and LSEs within the tolerances of parity_helpers.
 The draws come from a fixed numpy seed, so the cases are the same on every run.
+A second set of cases packs long ragged sequences and compares block ids only.
 """
 import dataclasses
 
@@ -91,3 +92,39 @@ def test_random_shapes(msa, synth, oracle_lib, case):
                                             host(d["v"]), d["k_offsets_host"], kv, wl.block_size, wl.topk)
     compare_ids(dids, r_ids, what + " decode ids")
     compare_outputs(dout, dlse, r_out, r_lse, wl.dtype, what + " decode")
+
+
+def _long_cases(n=4, seed=4242):
+    """Packed batches of 2-5 long ragged sequences (2,000-24,000 keys): scans
+    with several key chunks and, for the larger batches, two rounds of items
+    (each workgroup then scores an item and its mirror); selections over up to
+    187 earlier blocks."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        hq, g = HEADS[(2 * i + 1) % len(HEADS)]
+        d_idx = int(rng.choice([64, 128]))
+        topk = int(rng.choice([3, 8, 16]))
+        planted = int(rng.integers(0, 9))
+        batch = int(rng.integers(2, 6))
+        kv = [int(rng.integers(2000, 24000)) for _ in range(batch)]
+        ql = [n if rng.random() < 0.7 else int(rng.integers(1, n + 1)) for n in kv]
+        cases.append(dict(id=i, hq=hq, g=g, d_idx=d_idx, topk=topk, planted=planted, kv=kv, ql=ql))
+    return cases
+
+
+@pytest.mark.parametrize("case", _long_cases(), ids=lambda c: f"long{c['id']}")
+def test_long_ragged_batch_ids(msa, synth, oracle_lib, case):
+    wl = dataclasses.replace(synth.WORKLOADS["prefill_32k"], num_heads=case["hq"], num_kv_heads=case["g"],
+                             index_dim=case["d_idx"], topk=case["topk"], planted=case["planted"])
+    kv, ql = case["kv"], case["ql"]
+    what = (f"long{case['id']} heads {wl.num_heads}/{wl.num_kv_heads} d_idx {wl.index_dim} k {wl.topk} "
+            f"kv={kv} q={ql}")
+    say(f"[sweep] {what}")
+    inp = synth.prefill_inputs(wl, device="cuda", seed=5000 + case["id"], seq_lens=kv, q_lens=ql, with_main=False)
+    ids = msa.msa_index_topk(inp["q_idx"], inp["k_idx"], inp["cu_seqlens_q"], inp["cu_seqlens_k"], max(ql),
+                             max(kv), wl.block_size, wl.topk)
+    torch.cuda.synchronize()
+    rows, kstart, pos = oracle_lib.rows_prefill(inp["cu_q_host"], inp["cu_k_host"])
+    ref = oracle_lib.index_topk(host(inp["q_idx"]), host(inp["k_idx"]), kstart, pos, rows, wl.block_size, wl.topk)
+    compare_ids(ids, ref, what + " ids")
