@@ -9,7 +9,10 @@ own 8 bytes inside the tile, and under a model of gfx950's LDS (64 banks of 4
 bytes, an 8-byte access served 32 lanes at a time, or 16 lanes at a time) the
 writes of the V waves and the transposed reads of the dQ product take the
 fewest cycles their 512 bytes allow, as they did with the earlier 160-element
-rows; an unswizzled tile of the same pitch would not.
+rows; an unswizzled tile of the same pitch would not.  (On the GPU the
+transposed reads measure as modelled; the 8-byte writes of this pattern count
+twice the minimum cycles, so the model is a necessary check for the writes,
+not a sufficient one.)
 
 A selection slot's partial output holds 16 heads x 128 dims in bf16, stored
 run-major: the 16-byte run of dims 8r .. 8r + 7 of head h at element
