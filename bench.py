@@ -636,6 +636,20 @@ def main():
     torch.cuda.synchronize()
     result["roofline"]["copy_GBs"] = round(2 * (1 << 30) * 10 / (c0.elapsed_time(c1) / 1e3) / 1e9, 1)
     del src, dst
+    # and what the vendor GEMM library reaches on a large dense bf16 product on this GPU (a calibration of the
+    # MFMA rate under its sustained clock, for comparison with the index scan's fraction of peak)
+    ga = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    gb = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    gc = torch.matmul(ga, gb)
+    c0.record(stream)
+    for _ in range(20):
+        torch.matmul(ga, gb, out=gc)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    gemm_tf = 2 * 8192 ** 3 * 20 / (c0.elapsed_time(c1) / 1e3) / 1e12
+    result["roofline"]["library_gemm_bf16"] = {"shape": "8192x8192x8192", "tflops": round(gemm_tf, 1),
+                                               "frac": round(gemm_tf / PEAK_BF16_TFLOPS, 4)}
+    del ga, gb, gc
 
     # ------------------------------------------------------------ CPU baseline
     if not args.no_cpu_baseline:
