@@ -118,12 +118,11 @@ __device__ __forceinline__ unsigned kvo_row_mask(const int32_t* sel, int topk, i
 // their local block, so this removes most same-address global atomics), then
 // issues one global atomic per non-empty bucket; in the placing pass that
 // atomic reserves the workgroup's range of the bucket's list.
-constexpr int kLdsBuckets = 8192;
+constexpr int kLdsBuckets = 32768;  // 128 KB: one workgroup per CU, and a window's 8192 rows need <= 32 G of them
 
 template <bool kScatter>
 __global__ __launch_bounds__(256) void kvo_bucket(KvoArgs a, int nbk) {
-  __shared__ int s_cnt[kLdsBuckets];
-  __shared__ int s_base[kScatter ? kLdsBuckets : 1];
+  __shared__ int s_cnt[kLdsBuckets];  // counts; in the placing pass then each bucket's base in the list
   const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
   int64_t t = a.row_lo + item / a.G;
   const int g = (int)(item % a.G);
@@ -157,14 +156,14 @@ __global__ __launch_bounds__(256) void kvo_bucket(KvoArgs a, int nbk) {
   for (int j = threadIdx.x; j < nbk; j += 256) {
     const int n = s_cnt[j];
     if (n == 0) continue;
-    if (kScatter) s_base[j] = atomicAdd(&a.cursor[j], n);
+    if (kScatter) s_cnt[j] = atomicAdd(&a.cursor[j], n);
     else atomicAdd(&a.counts[j], n);
   }
   if (!kScatter) return;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 16; ++i)
-    if (mask & (1u << i)) a.edges[s_base[base + c[i]] + rk[i]] = code0 | i;
+    if (mask & (1u << i)) a.edges[s_cnt[base + c[i]] + rk[i]] = code0 | i;
 }
 
 // Exclusive scans of the edge counts and of the chunk counts, one workgroup.
