@@ -227,6 +227,31 @@ def test_prefill_attention_handmade_selection(msa, synth, oracle_lib, splits):
     compare_outputs(out, lse, ref_out, ref_lse, wl.dtype, "prefill hand-made")
 
 
+@pytest.mark.parametrize("max_kv_len", [2100, 1 << 18, 1 << 20])
+def test_prefill_attention_bucket_table_sizes(msa, synth, oracle_lib, max_kv_len):
+    """KV-outer edge lists with (sequence, group, block) bucket counts below,
+    well above the 8,192 an older table held, and above the 32,768 the LDS table
+    holds (one global atomic per entry there): a ragged batch of three with
+    hand-made selections, max_kv_len passed as a loose upper bound."""
+    wl = synth.WORKLOADS["prefill_32k"]
+    lens = [1500, 700, 2100]
+    nbk = len(lens) * wl.num_kv_heads * -(-max_kv_len // wl.block_size)
+    say(f"[parity] prefill buckets: lens={lens} max_kv_len={max_kv_len} buckets={nbk}")
+    inp = synth.prefill_inputs(wl, device="cuda", seed=13, seq_lens=lens)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    pos = np.concatenate([np.arange(n) for n in lens]).astype(np.int64)
+    kstart = np.concatenate([np.full(n, s) for n, s in zip(lens, starts)]).astype(np.int64)
+    sel = _handmade_selection(np.random.default_rng(13), pos, wl.num_kv_heads, wl.topk, wl.block_size)
+    ids = torch.as_tensor(sel, device="cuda")
+    out, lse = msa.msa_sparse_attn_prefill(inp["q"], inp["k"], inp["v"], ids, inp["cu_seqlens_q"],
+                                           inp["cu_seqlens_k"], max(lens), max_kv_len, wl.block_size, wl.topk)
+    torch.cuda.synchronize()
+    rows = np.arange(sum(lens), dtype=np.int64)
+    ref_out, ref_lse = oracle_lib.sparse_attn(host(inp["q"]), host(inp["k"]), host(inp["v"]), sel, kstart, pos,
+                                              rows, wl.block_size, wl.topk)
+    compare_outputs(out, lse, ref_out, ref_lse, wl.dtype, f"prefill buckets max_kv_len={max_kv_len}")
+
+
 def test_decode_tie_dense_index_inputs(msa, synth, oracle_lib):
     """Decode rows whose index values lie in {-1/8, 0, 1/8}: block scores tie
     often, so the decode selection's search over the high words of the thread
