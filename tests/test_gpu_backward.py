@@ -88,6 +88,27 @@ def test_backward_vs_oracle(msa, synth, oracle_lib):
     _check_vs_oracle(oracle_lib, inp, ids, dout, grads, wl, "bwd")
 
 
+@pytest.mark.parametrize("max_kv_len", [1 << 18, 1 << 20])
+def test_backward_loose_kv_bound(msa, synth, oracle_lib, max_kv_len):
+    """max_kv_len passed as a loose upper bound, so the edge lists hold 2 x 4 x
+    2048 or 2 x 4 x 8192 (sequence, group, block) buckets: the second is past
+    the LDS table and places edges by one global atomic each."""
+    wl = dataclasses.replace(synth.WORKLOADS["prefill_32k"], planted=8)
+    kv, ql = [1000, 300], [1000, 129]
+    say(f"[bwd] kv={kv} q={ql} max_kv_len={max_kv_len}")
+    inp = synth.prefill_inputs(wl, device="cuda", seed=43, seq_lens=kv, q_lens=ql)
+    mq = max(ql)
+    ids = msa.msa_index_topk(inp["q_idx"], inp["k_idx"], inp["cu_seqlens_q"], inp["cu_seqlens_k"], mq, max(kv),
+                             wl.block_size, wl.topk)
+    out, lse = msa.msa_sparse_attn_prefill(inp["q"], inp["k"], inp["v"], ids, inp["cu_seqlens_q"],
+                                           inp["cu_seqlens_k"], mq, max_kv_len, wl.block_size, wl.topk)
+    dout = synth.normal(inp["q"].shape, torch.bfloat16, "cuda", 43, "dout")
+    grads = msa.msa_sparse_attn_backward(inp["q"], inp["k"], inp["v"], out, dout, lse, ids, inp["cu_seqlens_q"],
+                                         inp["cu_seqlens_k"], mq, max_kv_len, wl.block_size, wl.topk)
+    torch.cuda.synchronize()
+    _check_vs_oracle(oracle_lib, inp, ids, dout, grads, wl, f"bwd max_kv_len={max_kv_len}")
+
+
 def test_backward_is_deterministic(msa, synth):
     wl = dataclasses.replace(synth.WORKLOADS["prefill_32k"], planted=8)
     kv, ql = [2100, 700], [2100, 700]
