@@ -90,11 +90,12 @@ def test_block_lse_decode_vs_oracle(msa, synth, oracle_lib):
     _compare_blse(blse, ref, 1e-3, "decode")
 
 
-def _kl_check(msa, synth, oracle_lib, wl, kv, ql, seed, what):
+def _kl_check(msa, synth, oracle_lib, wl, kv, ql, seed, what, max_kv_len=None):
     inp = synth.prefill_inputs(wl, device="cuda", seed=seed, seq_lens=kv, q_lens=ql)
     ids, _, lse, blse = _forward(msa, inp, wl, kv, ql)
     loss, dq, dk = msa.msa_index_kl_backward(inp["q_idx"], inp["k_idx"], ids, lse, blse, inp["cu_seqlens_q"],
-                                             inp["cu_seqlens_k"], max(ql), max(kv), wl.block_size, wl.topk)
+                                             inp["cu_seqlens_k"], max(ql), max_kv_len or max(kv), wl.block_size,
+                                             wl.topk)
     torch.cuda.synchronize()
     rows, kstart, pos = oracle_lib.rows_prefill(inp["cu_q_host"], inp["cu_k_host"])
     rl, rdq, rdk = oracle_lib.index_kl(host(inp["q_idx"]), host(inp["k_idx"]), host(inp["q"]), host(inp["k"]),
@@ -119,6 +120,17 @@ def test_index_kl_vs_oracle(msa, synth, oracle_lib):
     kv, ql = [1000, 300], [1000, 129]
     say(f"[kl] loss kv={kv} q={ql}")
     _kl_check(msa, synth, oracle_lib, wl, kv, ql, 53, "kl")
+
+
+@pytest.mark.parametrize("max_kv_len", [1 << 18, 1 << 20])
+def test_index_kl_loose_kv_bound(msa, synth, oracle_lib, max_kv_len):
+    """max_kv_len a loose upper bound: 2 x 4 x 2048 or 2 x 4 x 8192 (sequence,
+    group, block) buckets in the loss's edge lists, the second past the LDS
+    table (edges placed by one global atomic each)."""
+    wl = dataclasses.replace(synth.WORKLOADS["prefill_32k"], planted=8)
+    kv, ql = [1000, 300], [1000, 129]
+    say(f"[kl] loss kv={kv} q={ql} max_kv_len={max_kv_len}")
+    _kl_check(msa, synth, oracle_lib, wl, kv, ql, 54, f"kl max_kv_len={max_kv_len}", max_kv_len)
 
 
 def test_index_kl_fp32_and_deterministic(msa, synth, oracle_lib):
